@@ -1,0 +1,335 @@
+/*
+ * gpuos.h - C ABI of the persistent small-op runtime for AMD Instinct MI355X
+ * (gfx950).
+ *
+ * One resident HIP kernel stays on the GPU and drains a queue of small tensor
+ * operations that the host publishes through a ring of descriptors, so that a
+ * stream of tiny ops costs one launch instead of one launch per op.  The
+ * method is the one described in "GPUOS: A GPU Operating System Primitive for
+ * Transparent Operation Fusion" (section "The Paper": a long-lived worker
+ * kernel fed by a host-managed work queue with atomic task queues, micro-ops
+ * batched into unified submissions, operators over a generic tensor view).
+ * The host-to-device hand-off follows the launch path described in "Kernel
+ * Launch and Host-Device Interaction" (section "The launch path": commands are
+ * written into a pinned ring in host memory and a doorbell write tells the GPU
+ * front end to fetch them), moved into user space and paid once per flush.
+ * Elementwise chains such as y = relu(a*x + b) are merged into one
+ * register-resident pass as in "Launch Overhead and Fusion" (section
+ * "Fusion").
+ *
+ * Conventions shared by every entry point:
+ *  - Every function returns a gpuos_status (0 on success, a negative code on
+ *    failure) unless stated otherwise.  On failure a message is available from
+ *    gpuos_last_error() in the calling thread.
+ *  - Pointers inside a gpuos_op are DEVICE addresses owned by the caller
+ *    (typically torch tensors' data_ptr()).  They must stay allocated, and no
+ *    other agent may write them, until the op that uses them has completed.
+ *  - Plain host pointers to gpuos_op / gpuos_config / gpuos_stats arrays are
+ *    read or written during the call only; the library keeps no reference.
+ *  - A context is single-producer: calls on one context must not overlap in
+ *    time (like calls on one stream).  Different contexts are independent.
+ *  - While a context is alive its resident kernel occupies part of every
+ *    compute unit.  A device-wide synchronisation (hipDeviceSynchronize,
+ *    torch.cuda.synchronize) waits for that kernel and therefore only returns
+ *    after gpuos_destroy().  Synchronise on the caller's own streams instead.
+ */
+#ifndef GPUOS_H
+#define GPUOS_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define GPUOS_ABI_VERSION 1
+
+/* Status codes. */
+typedef enum gpuos_status {
+  GPUOS_OK = 0,
+  GPUOS_EINVAL = -1,    /* a malformed argument or op descriptor */
+  GPUOS_ENOMEM = -2,    /* device or pinned host allocation failed */
+  GPUOS_EAGAIN = -3,    /* ring full and the context does not block */
+  GPUOS_ETIMEDOUT = -4, /* gpuos_sync gave up before the ops completed */
+  GPUOS_EDEVICE = -5,   /* HIP error, or the device raised its error word;
+                           the context is poisoned and must be destroyed */
+  GPUOS_ESTATE = -6     /* call not allowed in the context's current state */
+} gpuos_status;
+
+/*
+ * Opcodes accepted by gpuos_submit.  Operand roles: in[0] and in[1] are the
+ * data operands, in[2] the auxiliary operand (weight matrix, gain vector,
+ * rotary table or index vector).  "x[k mod len]" means that a source whose
+ * src_len is shorter than the op's extent is read cyclically; a longer one is
+ * read as a prefix.  Element type: dtype applies to in[0], in[1] and out unless
+ * the row says otherwise; BF16 operands are widened exactly to fp32, computed
+ * in fp32 and rounded to bf16 with round-to-nearest-even.
+ *
+ *  NOP          nothing; completes once its dependencies have completed.
+ *  COPY         out[k] = in0[k mod src_len0], k < n.  Bit copy.
+ *  GATHER       out[k] = in0[idx[k]], idx = (int32*)in[2], k < n; an index
+ *               outside [0, src_len0) sets the device error word.
+ *  ADD          out[k] = in0[k] + in1[k]
+ *  MUL          out[k] = in0[k] * in1[k]
+ *  SCALE        out[k] = alpha * in0[k]
+ *  RELU         out[k] = in0[k] > 0 ? in0[k] : +0   (-0 and NaN give +0)
+ *  EXP          out[k] = exp(in0[k])
+ *  ROW_SUM      out[r] = sum_j in0[r*row_len + j], r < rows; out has rows
+ *               elements, n must equal rows*row_len.
+ *  ROW_SOFTMAX  m = max_j x[r,j]; out[r,j] = exp(x[r,j]-m) / sum_j exp(x[r,j]-m)
+ *  RMSNORM      out[r,j] = x[r,j] / sqrt(mean_j(x[r,j]^2) + eps) * g[j],
+ *               g = in[2] (row_len elements of dtype).
+ *  ROPE         rotate-half rotary embedding of rows = heads rows of row_len =
+ *               head_dim (even): with c = in[2][0..h/2), s = in[2][h/2..h)
+ *               (fp32 table for the token's position, h = head_dim):
+ *               y[i] = x[i]*c[i] - x[i+h/2]*s[i],
+ *               y[i+h/2] = x[i+h/2]*c[i] + x[i]*s[i],  i < h/2.
+ *  GEMV         out[i] = sum_k W[i*K + k] * x[k], i < M; W = (bf16*)in[2] row
+ *               major, x = in0 (dtype), aux[0] = M, aux[1] = K, n = M.
+ *  ATTN_SCORE   out[h*S + j] = alpha * sum_d q[h*D + d] * Kc[j*(H*D) + h*D + d]
+ *               q = in0 (dtype), Kc = (bf16*)in[2], out fp32;
+ *               aux = {H, D, S}, n = H*S.
+ *  ATTN_AV      out[h*D + d] = sum_j p[h*S + j] * Vc[j*(H*D) + h*D + d]
+ *               p = (float*)in0, Vc = (bf16*)in[2], out dtype;
+ *               aux = {H, D, S}, n = H*D.
+ *  SILU_MUL     out[k] = g[k] / (1 + exp(-g[k])) * u[k], g = in0, u = in1.
+ *  SPIN         debug op: the claiming wave spins for aux[0] nanoseconds
+ *               (bounded to 10 ms) and completes; used to test time-outs.
+ *
+ * Ops whose result is rounded once from an exact formula (COPY, GATHER, ADD,
+ * MUL, SCALE, RELU, ROPE) give bit-identical results however the queue is
+ * scheduled or fused.  Reductions and transcendentals (EXP, ROW_SUM,
+ * ROW_SOFTMAX, RMSNORM, GEMV, ATTN_*, SILU_MUL) accumulate in fp32 and match
+ * an exact evaluation to within rounding.
+ */
+typedef enum gpuos_opcode {
+  GPUOS_OP_NOP = 0,
+  GPUOS_OP_COPY = 1,
+  GPUOS_OP_GATHER = 2,
+  GPUOS_OP_ADD = 3,
+  GPUOS_OP_MUL = 4,
+  GPUOS_OP_SCALE = 5,
+  GPUOS_OP_RELU = 6,
+  GPUOS_OP_EXP = 7,
+  GPUOS_OP_ROW_SUM = 8,
+  GPUOS_OP_ROW_SOFTMAX = 9,
+  GPUOS_OP_RMSNORM = 10,
+  GPUOS_OP_ROPE = 11,
+  GPUOS_OP_GEMV = 12,
+  GPUOS_OP_ATTN_SCORE = 13,
+  GPUOS_OP_ATTN_AV = 14,
+  GPUOS_OP_SILU_MUL = 15,
+  GPUOS_OP_SPIN = 16,
+  GPUOS_OP_COUNT = 17
+} gpuos_opcode;
+
+typedef enum gpuos_dtype {
+  GPUOS_F32 = 0,
+  GPUOS_BF16 = 1,
+  GPUOS_I32 = 2 /* COPY and GATHER only (bit moves) */
+} gpuos_dtype;
+
+/* Op flags. */
+#define GPUOS_FLAG_TRANSIENT 0x1u   /* the output is scratch: when the fusion
+                                       pass merges this op with its consumer
+                                       and no other queued op reads it, the
+                                       store is elided and its contents are
+                                       left undefined */
+#define GPUOS_FLAG_LC 0x2u          /* latency-critical: goes to the priority
+                                       ring, whose work is claimed before any
+                                       best-effort tile; LC ops may depend
+                                       only on LC ops */
+#define GPUOS_FLAG_NONTEMPORAL 0x4u /* streaming output hint */
+
+/*
+ * User op descriptor (128 bytes).  Fields not used by an opcode must be zero.
+ *  n        extent of the op: number of output elements for elementwise ops,
+ *           rows*row_len for row ops, M for GEMV, H*S / H*D for attention.
+ *  src_len  length in elements of in[0] / in[1]; 0 means "same as the op's
+ *           extent".  A shorter source is read cyclically (elementwise ops,
+ *           COPY, ROW_* inputs); GATHER uses src_len[0] as the bound check.
+ *  deps     up to four ops this op must wait for: a value > 0 is an id
+ *           returned by an earlier gpuos_submit; a value < 0 names the op
+ *           -deps[i] positions earlier in the same gpuos_submit array; 0 is
+ *           unused.  Read-after-write, write-after-read and write-after-write
+ *           hazards between the byte ranges of queued ops are added
+ *           automatically unless the context was created with auto_deps = 0.
+ * All device pointers must be aligned to their element size; 16-byte aligned
+ * operands take the 128-bit load path.
+ */
+typedef struct gpuos_op {
+  uint16_t opcode;   /* gpuos_opcode */
+  uint8_t dtype;     /* gpuos_dtype */
+  uint8_t flags;     /* GPUOS_FLAG_* */
+  uint32_t n;
+  uint32_t rows;
+  uint32_t row_len;
+  void* out;
+  const void* in[3];
+  uint64_t src_len[2];
+  float alpha;
+  float beta;
+  float eps;
+  int32_t aux[4];
+  int32_t _pad;
+  int64_t deps[4];
+} gpuos_op;
+
+/*
+ * Context configuration.  gpuos_config_default() fills the defaults; zero in
+ * a field of a config passed to gpuos_create also selects the default.
+ */
+typedef struct gpuos_config {
+  uint32_t ring_slots;    /* descriptors per ring, power of two in
+                             [64, 1<<20]; default 65536 */
+  uint32_t waves_per_cu;  /* resident waves per compute unit, multiple of 4
+                             in [4, 32]; default 8 */
+  uint32_t tile_elems;    /* elementwise tile in elements, multiple of 256;
+                             default 4096 */
+  uint32_t be_tile_elems; /* tile for ops of 1<<24 elements or more (bounds
+                             how long a priority op waits for a free wave);
+                             default 16384 */
+  uint32_t fusion;        /* 1 = merge adjacent elementwise ops (default),
+                             2 = off */
+  uint32_t auto_deps;     /* 1 = add hazard dependencies (default), 2 = off */
+  uint32_t trace;         /* 1 = record per-op device timestamps, 2 = off
+                             (default) */
+  uint32_t block_on_full; /* 1 = submit/flush wait for ring space (default),
+                             2 = return GPUOS_EAGAIN */
+  uint32_t max_fuse;      /* longest fused chain, 2..8; default 8 */
+  uint32_t reserved[7];
+} gpuos_config;
+
+/* Counters returned by gpuos_get_stats. */
+typedef struct gpuos_stats {
+  uint64_t ops_submitted;      /* user ops accepted by gpuos_submit */
+  uint64_t ops_fused;          /* user ops merged into a preceding descriptor */
+  uint64_t descs_published;    /* device descriptors published (all rings) */
+  uint64_t descs_completed;    /* device descriptors retired (all rings) */
+  uint64_t flushes;
+  uint64_t ring_full_waits;    /* times publishing had to wait for space */
+  uint64_t deps_explicit;      /* dependencies given by the caller */
+  uint64_t deps_auto;          /* hazard dependencies added by the runtime */
+  uint64_t device_error;       /* device error word (0 = none) */
+  uint64_t error_desc;         /* descriptor sequence that raised it */
+  uint64_t worker_waves;       /* resident worker waves */
+  uint64_t compute_units;
+  uint64_t reserved[4];
+} gpuos_stats;
+
+/* Per-descriptor device timing, recorded when config.trace == 1. */
+typedef struct gpuos_trace_rec {
+  uint64_t seq;       /* device descriptor sequence (1-based, per ring) */
+  uint64_t t_claim;   /* s_memrealtime at the first tile's start */
+  uint64_t t_done;    /* s_memrealtime when the last tile finished */
+  uint32_t opcode;    /* opcode executed (FUSED_EW = 32) */
+  uint32_t ntiles;
+  uint32_t ring;      /* 0 = best-effort ring, 1 = latency-critical ring */
+  uint32_t first_ops; /* user ops folded into this descriptor */
+} gpuos_trace_rec;
+
+typedef struct gpuos_ctx gpuos_ctx;
+
+/* Fills *cfg with the defaults. */
+void gpuos_config_default(gpuos_config* cfg);
+
+/*
+ * Creates a context on HIP device `device`: allocates the descriptor rings
+ * (pinned host memory), the scheduler state (device memory) and launches the
+ * resident kernel on a library-owned non-blocking stream ("The Paper": one
+ * long-lived kernel instead of one launch per op).  cfg may be NULL for the
+ * defaults.  *out receives the context (NULL on failure).
+ * Errors: EINVAL (bad device or config), ENOMEM, EDEVICE (HIP failure).
+ */
+int gpuos_create(int device, const gpuos_config* cfg, gpuos_ctx** out);
+
+/*
+ * Validates and copies n ops into the context's staging area; the caller's
+ * array may be reused on return.  ids_out (nullable, n entries) receives the
+ * ids assigned to the ops: consecutive, monotone, starting at 1 for a new
+ * context.  Nothing reaches the device before gpuos_flush (the "unified
+ * submission" of "The Paper").  Dependencies are resolved here (explicit ones
+ * plus byte-range hazards).
+ * Errors: EINVAL (bad opcode, dtype, size, alignment, or a dependency on an
+ * id not yet submitted); nothing from the call is staged then.  ESTATE if the
+ * context is poisoned.
+ */
+int gpuos_submit(gpuos_ctx* ctx, const gpuos_op* ops, uint32_t n,
+                 uint64_t* ids_out);
+
+/*
+ * Runs the fusion pass over the staged ops, writes the resulting device
+ * descriptors into the ring and rings the doorbell (a release store of the
+ * ring tail the resident kernel polls).  Returns without waiting for the ops
+ * to run, like a kernel launch.  If the ring is full it waits for space when
+ * block_on_full = 1, else returns EAGAIN with the unpublished ops still
+ * staged.  Errors: EDEVICE (context poisoned), EAGAIN.
+ */
+int gpuos_flush(gpuos_ctx* ctx);
+
+/*
+ * Flushes, then blocks until every op with id <= upto has completed
+ * (upto = 0: every op submitted so far).  timeout_ns < 0 waits forever.
+ * Completion of an op implies its outputs are visible to later work on any
+ * stream of the device and to device-to-host copies.  ("Synchronization
+ * primitives": the blocking form of stream/event synchronisation.)
+ * Errors: ETIMEDOUT, EDEVICE (device error word set or HIP failure).
+ */
+int gpuos_sync(gpuos_ctx* ctx, uint64_t upto, int64_t timeout_ns);
+
+/*
+ * Non-blocking completion test for op `id` (the event.query form of
+ * "Synchronization primitives"): returns 1 if done, 0 if pending, or a
+ * negative status (EINVAL for an id never submitted, EDEVICE if poisoned).
+ * Does not flush.
+ */
+int gpuos_query(gpuos_ctx* ctx, uint64_t id);
+
+/* Copies the context's counters into *out. */
+int gpuos_get_stats(gpuos_ctx* ctx, gpuos_stats* out);
+
+/*
+ * Copies up to max trace records of the most recently retired descriptors
+ * (oldest first, at most ring_slots of them) into out and stores the count
+ * in *n_out.  Requires config.trace == 1 (else ESTATE).  Waits for no op.
+ */
+int gpuos_trace_read(gpuos_ctx* ctx, gpuos_trace_rec* out, uint32_t max,
+                     uint32_t* n_out);
+
+/*
+ * Drains every submitted op (or abandons unflushed ones when the context is
+ * poisoned), tells the resident kernel to exit, waits for it (bounded by
+ * timeout_ns, < 0 = forever) and frees all library memory.  The context
+ * pointer is invalid afterwards, also when an error is returned.
+ * Errors: ETIMEDOUT (kernel did not exit; its memory is then leaked, not
+ * freed under it), EDEVICE.
+ */
+int gpuos_destroy(gpuos_ctx* ctx, int64_t timeout_ns);
+
+/*
+ * Message describing the last failing call made by this thread (on any
+ * context); "" if none.  The pointer stays valid until the thread's next
+ * failing call.
+ */
+const char* gpuos_last_error(void);
+
+/*
+ * Per-op launch comparator: runs the n ops on HIP stream `stream` (NULL = the
+ * legacy default stream) as one kernel launch each, in order, with the same
+ * tile code as the resident kernel; stream order provides every dependency
+ * ("Under the hood": blocks of different kernels on one stream never
+ * overlap).  With fuse = 1 the fusion pass runs first and each fused chain is
+ * one launch (a stand-alone fused kernel).  Does not synchronise.
+ * deps are ignored.  Errors: EINVAL, EDEVICE.
+ */
+int gpuos_baseline_run(int device, const gpuos_op* ops, uint32_t n, int fuse,
+                       void* stream);
+
+/* ABI version of the loaded library (GPUOS_ABI_VERSION). */
+int gpuos_abi_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+#endif

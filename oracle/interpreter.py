@@ -1,0 +1,305 @@
+"""CPU oracle for queues of small tensor ops.
+
+TEST INFRASTRUCTURE ONLY.  Nothing on the product path may import this
+module: it is used by ``tests/``, by ``__graft_entry__.smoke()`` to check the
+GPU result and by ``bench.py`` to time the CPU baseline.  It shares no code,
+constant or helper with the HIP runtime; both read the same seeded
+:class:`persistent_fusion_amd.workloads.Workload`.
+
+What it computes.  The method ("GPUOS: A GPU Operating System Primitive for
+Transparent Operation Fusion", section "The Paper") only removes launch
+overhead: the result of a queue of small ops is the result of running the ops
+one after another in submission order.  The oracle is that definition written
+out: one op at a time, in order, every output written (also the ones the
+runtime may keep in registers), no fusion.  Fusion itself ("Launch Overhead and
+Fusion", section "Fusion") must not change the result; the pins in
+``tests/test_oracle_pins.py`` check this interpreter against an independent
+per-element evaluator.
+
+Per-op definitions (the readings taken where the pages are silent are listed
+in the design doc):
+
+* fp32 ADD / MUL / SCALE are single IEEE operations rounded to nearest even
+  (numpy float32 arithmetic, no fused multiply-add); RELU is
+  ``x > 0 ? x : +0``; bf16 operands are widened exactly to fp32 and every bf16
+  result is the fp32 result rounded to bf16 with round-to-nearest-even.
+* EXP, ROW_SUM, ROW_SOFTMAX, RMSNORM, GEMV, ATTN_SCORE, ATTN_AV, SILU_MUL are
+  evaluated in fp64 and rounded once to fp32 (then to bf16 for bf16 outputs).
+* ROPE is the rotate-half rotation evaluated in fp32 with each product and each
+  sum rounded, as written: ``y_i = x_i c_i - x_{i+h/2} s_i``,
+  ``y_{i+h/2} = x_{i+h/2} c_i + x_i s_i``.
+* A data operand whose readable length is shorter than the op's extent is read
+  cyclically (index ``k mod len``); a longer one is read as a prefix.
+
+``run`` also returns, for every element written by a reduction or a
+transcendental, the error scale the tolerance test uses: the sum of absolute
+values of the terms for sums and dot products, ``|result|`` otherwise.
+"""
+
+from __future__ import annotations
+
+from typing import Dict, List, Optional, Tuple
+
+import numpy as np
+
+from persistent_fusion_amd.workloads import Op, Ref, Workload
+
+EXACT_KINDS = frozenset({"nop", "spin", "copy", "gather", "add", "mul", "scale", "relu", "rope"})
+TOL_KINDS = frozenset({"exp", "row_sum", "row_softmax", "rmsnorm", "gemv", "attn_score",
+                       "attn_av", "silu_mul"})
+
+
+class OracleError(RuntimeError):
+    """An op the definition rejects (for example a GATHER index out of range)."""
+
+
+# ----------------------------------------------------------------------------
+# bf16 <-> fp32, written from the format's definition: bf16 is the top half of
+# an IEEE binary32 word.  Narrowing rounds to nearest, ties to even; NaN stays
+# a quiet NaN with its sign.
+
+
+def bf16_to_f32(u: np.ndarray) -> np.ndarray:
+    return (np.asarray(u, dtype=np.uint16).astype(np.uint32) << np.uint32(16)).view(np.float32)
+
+
+def f32_to_bf16(x: np.ndarray) -> np.ndarray:
+    bits = np.ascontiguousarray(x, dtype=np.float32).view(np.uint32).astype(np.uint64)
+    upper = bits >> np.uint64(16)
+    lower = bits & np.uint64(0xFFFF)
+    half = np.uint64(0x8000)
+    round_up = (lower > half) | ((lower == half) & ((upper & np.uint64(1)) == np.uint64(1)))
+    out = upper + round_up.astype(np.uint64)
+    is_nan = np.isnan(np.asarray(x, dtype=np.float32))
+    out = np.where(is_nan, upper | np.uint64(0x0040), out)
+    return out.astype(np.uint16)
+
+
+def _to_f32(arr: np.ndarray, dtype: str) -> np.ndarray:
+    if dtype == "bf16":
+        return bf16_to_f32(arr)
+    return np.asarray(arr, dtype=np.float32)
+
+
+def _store_from_f32(vals32: np.ndarray, dtype: str) -> np.ndarray:
+    if dtype == "bf16":
+        return f32_to_bf16(vals32)
+    return np.asarray(vals32, dtype=np.float32)
+
+
+def _store_from_f64(vals64: np.ndarray, dtype: str) -> np.ndarray:
+    with np.errstate(over="ignore", invalid="ignore"):
+        vals32 = np.asarray(vals64, dtype=np.float64).astype(np.float32)
+    return _store_from_f32(vals32, dtype)
+
+
+# ----------------------------------------------------------------------------
+# operand access
+
+
+def _elem_count(bufs: Dict[str, np.ndarray], ref: Ref) -> int:
+    return bufs[ref.buf].shape[0] - ref.off
+
+
+def _read_cyclic(bufs: Dict[str, np.ndarray], ref: Ref, src_len: int, extent: int) -> np.ndarray:
+    """Elements k mod src_len (k < extent) of the operand starting at ref."""
+    if src_len == 0:
+        src_len = extent
+    if ref.off + src_len > bufs[ref.buf].shape[0]:
+        raise OracleError(f"operand {ref} of length {src_len} overruns its buffer")
+    base = bufs[ref.buf][ref.off:ref.off + src_len]
+    if src_len >= extent:
+        return base[:extent].copy()
+    reps = -(-extent // src_len)
+    return np.tile(base, reps)[:extent].copy()
+
+
+def _read(bufs: Dict[str, np.ndarray], ref: Ref, count: int) -> np.ndarray:
+    if ref.off + count > bufs[ref.buf].shape[0]:
+        raise OracleError(f"operand {ref} of length {count} overruns its buffer")
+    return bufs[ref.buf][ref.off:ref.off + count].copy()
+
+
+def _write(bufs: Dict[str, np.ndarray], ref: Ref, vals: np.ndarray) -> None:
+    dst = bufs[ref.buf]
+    if ref.off + vals.shape[0] > dst.shape[0]:
+        raise OracleError(f"output {ref} of length {vals.shape[0]} overruns its buffer")
+    dst[ref.off:ref.off + vals.shape[0]] = vals.astype(dst.dtype, copy=False)
+
+
+# ----------------------------------------------------------------------------
+# one op
+
+
+def out_len(op: Op) -> int:
+    """Number of elements an op writes."""
+    if op.kind in ("nop", "spin"):
+        return 0
+    if op.kind == "row_sum":
+        return op.rows
+    return op.n
+
+
+def apply_op(op: Op, bufs: Dict[str, np.ndarray], dtypes: Dict[str, str]) -> Optional[np.ndarray]:
+    """Executes one op on ``bufs`` in place.
+
+    Returns the error-scale array of the elements written (tolerance class),
+    or None for ops whose result is exact.
+    """
+    k = op.kind
+    dt = op.dtype
+    n = op.n
+    if k in ("nop", "spin"):
+        return None
+
+    if k == "copy":
+        _write(bufs, op.out, _read_cyclic(bufs, op.ins[0], op.src_len[0], n))
+        return None
+
+    if k == "gather":
+        idx = _read(bufs, op.aux, n).astype(np.int64)
+        src_n = op.src_len[0] or _elem_count(bufs, op.ins[0])
+        if np.any(idx < 0) or np.any(idx >= src_n):
+            raise OracleError("gather index out of range")
+        src = _read(bufs, op.ins[0], src_n)
+        _write(bufs, op.out, src[idx])
+        return None
+
+    if k in ("add", "mul", "scale", "relu", "exp", "silu_mul"):
+        x = _to_f32(_read_cyclic(bufs, op.ins[0], op.src_len[0], n), dt)
+        if k in ("add", "mul", "silu_mul"):
+            y = _to_f32(_read_cyclic(bufs, op.ins[1], op.src_len[1], n), dt)
+        if k == "add":
+            r32 = x + y
+        elif k == "mul":
+            r32 = x * y
+        elif k == "scale":
+            r32 = np.float32(op.alpha) * x
+        elif k == "relu":
+            r32 = np.where(x > np.float32(0.0), x, np.float32(0.0)).astype(np.float32)
+        elif k == "exp":
+            with np.errstate(over="ignore"):
+                r64 = np.exp(x.astype(np.float64))
+            vals = _store_from_f64(r64, dt)
+            _write(bufs, op.out, vals)
+            return np.abs(r64)
+        else:  # silu_mul: g / (1 + exp(-g)) * u in fp64
+            g = x.astype(np.float64)
+            u = y.astype(np.float64)
+            with np.errstate(over="ignore", invalid="ignore"):
+                r64 = g / (1.0 + np.exp(-g)) * u
+            _write(bufs, op.out, _store_from_f64(r64, dt))
+            return np.abs(r64)
+        _write(bufs, op.out, _store_from_f32(r32.astype(np.float32), dt))
+        return None
+
+    if k in ("row_sum", "row_softmax", "rmsnorm"):
+        rows, L = op.rows, op.row_len
+        if rows * L != n:
+            raise OracleError("row op with n != rows * row_len")
+        x64 = _to_f32(_read_cyclic(bufs, op.ins[0], op.src_len[0], n), dt).astype(np.float64)
+        x64 = x64.reshape(rows, L)
+        if k == "row_sum":
+            s = x64.sum(axis=1)
+            _write(bufs, op.out, _store_from_f64(s, dt))
+            return np.abs(x64).sum(axis=1)
+        if k == "row_softmax":
+            m = x64.max(axis=1, keepdims=True)  # NaN propagates through max
+            with np.errstate(invalid="ignore", over="ignore"):
+                e = np.exp(x64 - m)
+                y = e / e.sum(axis=1, keepdims=True)
+            _write(bufs, op.out, _store_from_f64(y.reshape(-1), dt))
+            return np.abs(y).reshape(-1)
+        g = _to_f32(_read(bufs, op.aux, L), dt).astype(np.float64)
+        ms = (x64 * x64).sum(axis=1) / L
+        inv = 1.0 / np.sqrt(ms + float(np.float32(op.eps)))
+        y = x64 * inv[:, None] * g[None, :]
+        _write(bufs, op.out, _store_from_f64(y.reshape(-1), dt))
+        return np.abs(y).reshape(-1)
+
+    if k == "rope":
+        heads, hd = op.rows, op.row_len
+        if heads * hd != n or hd % 2:
+            raise OracleError("rope needs n = heads * head_dim with an even head_dim")
+        half = hd // 2
+        x = _to_f32(_read(bufs, op.ins[0], n), dt).reshape(heads, hd)
+        tab = _read(bufs, op.aux, hd).astype(np.float32)
+        c, s = tab[:half], tab[half:]
+        x1, x2 = x[:, :half], x[:, half:]
+        y1 = (x1 * c) - (x2 * s)
+        y2 = (x2 * c) + (x1 * s)
+        y = np.concatenate([y1, y2], axis=1).astype(np.float32).reshape(-1)
+        _write(bufs, op.out, _store_from_f32(y, dt))
+        return None
+
+    if k == "gemv":
+        M, K = op.dims[0], op.dims[1]
+        if M != n:
+            raise OracleError("gemv needs n == M")
+        W = bf16_to_f32(_read(bufs, op.aux, M * K)).astype(np.float64).reshape(M, K)
+        x = _to_f32(_read(bufs, op.ins[0], K), dt).astype(np.float64)
+        y = W @ x
+        _write(bufs, op.out, _store_from_f64(y, dt))
+        return np.abs(W) @ np.abs(x)
+
+    if k == "attn_score":
+        H, Dh, S = op.dims[0], op.dims[1], op.dims[2]
+        if H * S != n:
+            raise OracleError("attn_score needs n == H * S")
+        q = _to_f32(_read(bufs, op.ins[0], H * Dh), dt).astype(np.float64).reshape(H, Dh)
+        Kc = bf16_to_f32(_read(bufs, op.aux, S * H * Dh)).astype(np.float64).reshape(S, H, Dh)
+        a = float(np.float32(op.alpha))
+        sc = np.empty((H, S))
+        scale = np.empty((H, S))
+        for h in range(H):
+            sc[h] = a * (Kc[:, h, :] @ q[h])
+            scale[h] = abs(a) * (np.abs(Kc[:, h, :]) @ np.abs(q[h]))
+        _write(bufs, op.out, _store_from_f64(sc.reshape(-1), "f32"))
+        return scale.reshape(-1)
+
+    if k == "attn_av":
+        H, Dh, S = op.dims[0], op.dims[1], op.dims[2]
+        if H * Dh != n:
+            raise OracleError("attn_av needs n == H * D")
+        p = _read(bufs, op.ins[0], H * S).astype(np.float64).reshape(H, S)
+        Vc = bf16_to_f32(_read(bufs, op.aux, S * H * Dh)).astype(np.float64).reshape(S, H, Dh)
+        o = np.empty((H, Dh))
+        scale = np.empty((H, Dh))
+        for h in range(H):
+            o[h] = Vc[:, h, :].T @ p[h]
+            scale[h] = np.abs(Vc[:, h, :]).T @ np.abs(p[h])
+        _write(bufs, op.out, _store_from_f64(o.reshape(-1), dt))
+        return scale.reshape(-1)
+
+    raise OracleError(f"unknown op kind {k!r}")
+
+
+# ----------------------------------------------------------------------------
+# a whole queue
+
+
+def run(wl: Workload, upto: Optional[int] = None, scales: bool = False,
+        buffers: Optional[Dict[str, np.ndarray]] = None):
+    """Runs ops [0, upto) of the workload in submission order.
+
+    Returns the final buffers (copies; the workload is not modified).  With
+    ``scales=True`` also returns ``{buffer: scale array or None}``: for every
+    buffer, an fp64 array of error scales where the last writer of an element
+    was a tolerance-class op, NaN where it was an exact op or the initial
+    contents.
+    """
+    bufs = {k: v.copy() for k, v in (buffers or wl.buffers).items()}
+    sc: Dict[str, np.ndarray] = {}
+    ops = wl.ops if upto is None else wl.ops[:upto]
+    for op in ops:
+        s = apply_op(op, bufs, wl.dtypes)
+        if not scales or op.kind in ("nop", "spin"):
+            continue
+        name = op.out.buf
+        if name not in sc:
+            sc[name] = np.full(bufs[name].shape[0], np.nan)
+        cnt = out_len(op)
+        sc[name][op.out.off:op.out.off + cnt] = np.nan if s is None else s
+    if scales:
+        return bufs, sc
+    return bufs

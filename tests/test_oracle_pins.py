@@ -1,0 +1,676 @@
+"""Pins of the CPU oracle against facts that do not come from the oracle itself.
+
+Each test checks one op definition against a worked example printed on a page,
+a closed form, an invariant, exact rational arithmetic on tiny inputs, or an
+independent library routine.  They run on the CPU (``-m "not gpu"``).
+"""
+
+import itertools
+import math
+import os
+import struct
+from fractions import Fraction
+
+import numpy as np
+import pytest
+
+import oracle
+from oracle import bf16_to_f32, compare, f32_to_bf16
+from oracle.interpreter import apply_op, out_len
+from persistent_fusion_amd import traffic
+from persistent_fusion_amd.workloads import (Op, Ref, Workload, gen_decode, gen_dynamic_dag,
+                                             gen_elementwise_queue, gen_fused_chain,
+                                             gen_priority_mix, rope_table)
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+def f32(v: float) -> float:
+    """Python double rounded to the nearest fp32 (C cast semantics)."""
+    try:
+        return struct.unpack("<f", struct.pack("<f", v))[0]
+    except OverflowError:
+        return math.copysign(math.inf, v)
+
+
+def bits32(v) -> int:
+    return int(np.float32(v).view(np.uint32))
+
+
+def wl_of(bufs, ops, dtypes=None):
+    dts = dtypes or {k: ("bf16" if v.dtype == np.uint16 else "i32" if v.dtype == np.int32 else "f32")
+                     for k, v in bufs.items()}
+    return Workload("t", {k: np.asarray(v) for k, v in bufs.items()}, dts, ops)
+
+
+# ----------------------------------------------------------------------------
+# worked example from the pages
+
+
+def _read_golden():
+    rows, consts, nbytes = [], None, {}
+    with open(os.path.join(GOLDEN, "relu_axb_constants.txt")) as f:
+        for line in f:
+            t = line.split()
+            if not t or t[0].startswith("#"):
+                continue
+            if t[0] == "const":
+                consts = (float(t[1]), float(t[2]))
+            elif t[0] == "row":
+                rows.append((int(t[1]), float(t[2]), float(t[3])))
+            else:
+                nbytes[t[0]] = int(t[1])
+    return consts, rows, nbytes
+
+
+def test_golden_relu_axb_page_constants():
+    (a, b), rows, _ = _read_golden()
+    n = 200
+    x = (np.arange(n) % 100 - 50).astype(np.float32)
+    bufs = {"x": x, "bv": np.full(n, b, np.float32), "av": np.full(n, a, np.float32),
+            "t1": np.zeros(n, np.float32), "t2": np.zeros(n, np.float32),
+            "y": np.zeros(n, np.float32), "y2": np.zeros(n, np.float32)}
+    ops = [
+        # scalar a as SCALE's alpha, scalar b as a constant vector
+        Op("scale", Ref("t1"), (Ref("x"),), n=n, alpha=a),
+        Op("add", Ref("t2"), (Ref("t1"), Ref("bv")), n=n),
+        Op("relu", Ref("y"), (Ref("t2"),), n=n),
+        # the same chain with a as a vector operand
+        Op("mul", Ref("t1"), (Ref("av"), Ref("x")), n=n),
+        Op("add", Ref("t2"), (Ref("t1"), Ref("bv")), n=n),
+        Op("relu", Ref("y2"), (Ref("t2"),), n=n),
+    ]
+    out = oracle.run(wl_of(bufs, ops))
+    for i, xi, yi in rows:
+        assert out["x"][i] == xi
+        assert out["y"][i] == np.float32(yi), (i, out["y"][i], yi)
+        assert out["y2"][i] == np.float32(yi)
+        assert bits32(out["y"][i]) == bits32(yi)  # +0, never -0
+
+
+def test_golden_traffic_model_page_bytes():
+    _, _, nbytes = _read_golden()
+    n = 1000
+    chain = [Op("mul", Ref("t1"), (Ref("a"), Ref("x")), n=n, transient=True),
+             Op("add", Ref("t2"), (Ref("t1"), Ref("b")), n=n, transient=True),
+             Op("relu", Ref("y"), (Ref("t2"),), n=n)]
+    scal = {"a", "b"}
+    assert traffic.unfused_bytes(chain, scal) == nbytes["bytes_unfused"] * n
+    assert traffic.fused_chain_bytes(chain, scal) == nbytes["bytes_fused"] * n
+    # vector a, b (the 16M-element workload): 32 vs 16 bytes per element
+    assert traffic.unfused_bytes(chain) == 32 * n
+    assert traffic.fused_chain_bytes(chain) == 16 * n
+    wl = gen_fused_chain(n=4096)
+    assert traffic.fused_chain_bytes(wl.ops) == wl.meta["fused_bytes"] // wl.meta["n"] * 4096
+
+
+# ----------------------------------------------------------------------------
+# closed forms on constants
+
+
+@pytest.mark.parametrize("a,x,b,want", [(2.0, 3.0, -7.0, 0.0), (0.5, 3.0, 0.25, 1.75),
+                                        (1.5, -50.0, 0.5, 0.0), (1.5, 49.0, 0.5, 74.0)])
+def test_relu_axb_closed_form(a, x, b, want):
+    n = 5
+    bufs = {"a": np.full(n, a, np.float32), "x": np.full(n, x, np.float32),
+            "b": np.full(n, b, np.float32), "t": np.zeros(n, np.float32),
+            "u": np.zeros(n, np.float32), "y": np.zeros(n, np.float32)}
+    ops = [Op("mul", Ref("t"), (Ref("a"), Ref("x")), n=n),
+           Op("add", Ref("u"), (Ref("t"), Ref("b")), n=n),
+           Op("relu", Ref("y"), (Ref("u"),), n=n)]
+    out = oracle.run(wl_of(bufs, ops))
+    assert np.all(out["y"] == np.float32(want))
+    assert np.all(out["y"].view(np.uint32) == bits32(want))
+
+
+def test_relu_signed_zero_nan_and_denormals():
+    vals = np.array([-0.0, 0.0, np.nan, -np.nan, np.inf, -np.inf, 1e-45, -1e-45, 3.0, -3.0],
+                    np.float32)
+    n = vals.size
+    bufs = {"x": vals, "y": np.zeros(n, np.float32)}
+    out = oracle.run(wl_of(bufs, [Op("relu", Ref("y"), (Ref("x"),), n=n)]))
+    want = [0.0, 0.0, 0.0, 0.0, math.inf, 0.0, 1e-45, 0.0, 3.0, 0.0]
+    for g, w in zip(out["y"], want):
+        assert bits32(g) == bits32(w)
+
+
+def test_denormals_are_preserved():
+    d = np.float32(2.0 ** -140)  # subnormal in fp32
+    n = 4
+    bufs = {"a": np.full(n, d, np.float32), "b": np.full(n, d, np.float32),
+            "h": np.full(n, 2.0 ** -10, np.float32),
+            "s": np.zeros(n, np.float32), "p": np.zeros(n, np.float32)}
+    ops = [Op("add", Ref("s"), (Ref("a"), Ref("b")), n=n),
+           Op("mul", Ref("p"), (Ref("a"), Ref("h")), n=n)]
+    out = oracle.run(wl_of(bufs, ops))
+    assert np.all(out["s"] == np.float32(2.0 ** -139))
+    # 2^-150 is exactly half the smallest subnormal: ties-to-even rounds it to +0
+    assert np.all(out["p"].view(np.uint32) == 0)
+    bufs["h"] = np.full(n, 2.0 ** -3, np.float32)
+    out = oracle.run(wl_of(bufs, ops))
+    assert np.all(out["p"] == np.float32(2.0 ** -143))
+
+
+# ----------------------------------------------------------------------------
+# brute force on tiny queues: an independent per-element evaluator
+
+
+def _eval_queue_elementwise(wl: Workload):
+    """Recursive per-element evaluation of a fp32 elementwise queue.
+
+    The value of buffer b at element k just before op p runs is the output of
+    the last earlier op that wrote that element, evaluated element-wise in
+    Python doubles and rounded to fp32 after each operation (double rounding
+    is innocuous for one fp32 add or multiply), or the initial contents.
+    """
+    memo = {}
+
+    def value(buf, k, pos):
+        key = (buf, k, pos)
+        if key in memo:
+            return memo[key]
+        v = None
+        for j in range(pos - 1, -1, -1):
+            op = wl.ops[j]
+            if op.out.buf == buf and op.out.off <= k < op.out.off + op.n:
+                v = op_elem(j, k - op.out.off)
+                break
+        if v is None:
+            v = float(wl.buffers[buf][k])
+        memo[key] = v
+        return v
+
+    def op_elem(j, e):
+        op = wl.ops[j]
+        srcs = []
+        for i, r in enumerate(op.ins):
+            L = op.src_len[i] or op.n
+            srcs.append(value(r.buf, r.off + (e % L), j))
+        if op.kind == "add":
+            return f32(srcs[0] + srcs[1])
+        if op.kind == "mul":
+            return f32(srcs[0] * srcs[1])
+        if op.kind == "scale":
+            return f32(float(np.float32(op.alpha)) * srcs[0])
+        if op.kind == "relu":
+            return srcs[0] if srcs[0] > 0 else 0.0
+        if op.kind == "copy":
+            return srcs[0]
+        raise AssertionError(op.kind)
+
+    final = {}
+    for name, arr in wl.buffers.items():
+        final[name] = np.array([value(name, k, len(wl.ops)) for k in range(arr.shape[0])],
+                               np.float32)
+    return final
+
+
+def _same_bits(a, b):
+    a = np.asarray(a, np.float32)
+    b = np.asarray(b, np.float32)
+    both_nan = np.isnan(a) & np.isnan(b)
+    return bool(np.all((a.view(np.uint32) == b.view(np.uint32)) | both_nan))
+
+
+@pytest.mark.parametrize("seed", [0, 1, 2])
+def test_elementwise_queue_matches_per_element_evaluation(seed):
+    wl = gen_elementwise_queue(seed=seed, n_ops=60, n=16)
+    got = oracle.run(wl)
+    want = _eval_queue_elementwise(wl)
+    for name in wl.buffers:
+        assert _same_bits(got[name], want[name]), name
+
+
+def test_reuse_and_cyclic_queue_matches_per_element_evaluation():
+    rng = np.random.default_rng(5)
+    bufs = {"A": rng.standard_normal(12).astype(np.float32),
+            "B": rng.standard_normal(5).astype(np.float32),
+            "C": np.zeros(12, np.float32)}
+    ops = [
+        Op("mul", Ref("C"), (Ref("A"), Ref("B")), n=12, src_len=(12, 5)),      # cyclic B
+        Op("add", Ref("A", 2), (Ref("C", 1), Ref("A")), n=9, src_len=(0, 3)),  # overlap + cyclic
+        Op("relu", Ref("C"), (Ref("C"),), n=12),                               # in place
+        Op("scale", Ref("B"), (Ref("C", 3),), n=5, alpha=-0.75),
+        Op("copy", Ref("A"), (Ref("B"),), n=7, src_len=(5, 0)),
+        Op("add", Ref("C", 4), (Ref("A", 1), Ref("C")), n=8),
+    ]
+    wl = wl_of(bufs, ops)
+    got = oracle.run(wl)
+    want = _eval_queue_elementwise(wl)
+    for name in bufs:
+        assert _same_bits(got[name], want[name]), name
+
+
+def _hazard(a: Op, b: Op) -> bool:
+    def rng_(r, cnt):
+        return (r.buf, r.off, r.off + cnt)
+
+    def ov(x, y):
+        return x[0] == y[0] and x[1] < y[2] and y[1] < x[2]
+
+    wa = rng_(a.out, out_len(a))
+    wb = rng_(b.out, out_len(b))
+    ra = [rng_(r, a.src_len[i] or a.n) for i, r in enumerate(a.ins)]
+    rb = [rng_(r, b.src_len[i] or b.n) for i, r in enumerate(b.ins)]
+    return ov(wa, wb) or any(ov(wa, r) for r in rb) or any(ov(wb, r) for r in ra)
+
+
+def test_every_topological_order_gives_identical_buffers():
+    rng = np.random.default_rng(11)
+    n = 6
+    bufs = {k: rng.standard_normal(n).astype(np.float32) for k in "ABCD"}
+    ops = [Op("mul", Ref("C"), (Ref("A"), Ref("B")), n=n),
+           Op("add", Ref("D"), (Ref("A"), Ref("A")), n=n),
+           Op("relu", Ref("A"), (Ref("C"),), n=n),
+           Op("scale", Ref("B"), (Ref("D"),), n=n, alpha=1.25),
+           Op("add", Ref("D"), (Ref("B"), Ref("C")), n=n),
+           Op("exp", Ref("C"), (Ref("D"),), n=n)]
+    base = oracle.run(wl_of(bufs, ops))
+    orders = 0
+    for perm in itertools.permutations(range(len(ops))):
+        pos = {p: i for i, p in enumerate(perm)}
+        if any(pos[i] > pos[j] for i in range(len(ops)) for j in range(i + 1, len(ops))
+               if _hazard(ops[i], ops[j])):
+            continue
+        orders += 1
+        out = oracle.run(wl_of(bufs, [ops[p] for p in perm]))
+        for k in bufs:
+            assert _same_bits(out[k], base[k])
+    assert orders > 1
+
+
+# ----------------------------------------------------------------------------
+# bf16 conversion
+
+
+def test_bf16_rounding_edge_cases():
+    cases = [
+        (1.0, 0x3F80),
+        (1.0 + 2.0 ** -8, 0x3F80),            # exact tie: rounds to even (down)
+        (1.0 + 3 * 2.0 ** -8, 0x3F82),        # tie between 0x3F81 and 0x3F82: to even (up)
+        (1.0 + 2.0 ** -8 + 2.0 ** -20, 0x3F81),  # just above the tie: up
+        (-2.5, 0xC020),
+        (0.0, 0x0000), (-0.0, 0x8000),
+        (math.inf, 0x7F80), (-math.inf, 0xFF80),
+        (3.3895313892515355e38, 0x7F7F),     # largest finite bf16
+        (3.4e38, 0x7F80),                     # rounds up past the largest finite: inf
+        (2.0 ** -133, 0x0001),                # smallest bf16 subnormal
+    ]
+    x = np.array([c[0] for c in cases], np.float32)
+    got = f32_to_bf16(x)
+    for (v, want), g in zip(cases, got):
+        assert int(g) == want, (v, hex(int(g)), hex(want))
+    nan = f32_to_bf16(np.array([np.nan, -np.nan], np.float32))
+    assert np.all(np.isnan(bf16_to_f32(nan)))
+    assert np.all((nan & 0x7FC0) == 0x7FC0)
+
+
+def test_bf16_matches_torch_rne():
+    torch = pytest.importorskip("torch")
+    rng = np.random.default_rng(3)
+    x = np.concatenate([rng.standard_normal(20000).astype(np.float32) * 1e3,
+                        (rng.integers(0, 2 ** 32, 20000, dtype=np.uint64)).astype(np.uint32).view(np.float32)])
+    x = x[~np.isnan(x)]
+    want = torch.from_numpy(x).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+    assert np.array_equal(f32_to_bf16(x), want)
+    back = bf16_to_f32(want)
+    assert np.array_equal(back, torch.from_numpy(want.view(np.int16)).view(torch.bfloat16).float().numpy())
+
+
+def test_bf16_elementwise_is_fp32_then_rne():
+    rng = np.random.default_rng(4)
+    n = 64
+    a = f32_to_bf16(rng.standard_normal(n).astype(np.float32))
+    b = f32_to_bf16(rng.standard_normal(n).astype(np.float32))
+    bufs = {"a": a, "b": b, "y": np.zeros(n, np.uint16)}
+    out = oracle.run(wl_of(bufs, [Op("add", Ref("y"), (Ref("a"), Ref("b")), n=n, dtype="bf16")]))
+    torch = pytest.importorskip("torch")
+    ta = torch.from_numpy(bf16_to_f32(a))
+    tb = torch.from_numpy(bf16_to_f32(b))
+    want = (ta + tb).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+    assert np.array_equal(out["y"], want)
+
+
+# ----------------------------------------------------------------------------
+# EXP
+
+
+def test_exp_special_values_and_library():
+    x = np.array([0.0, -0.0, 1.0, -1.0, 10.5, -20.25, 88.7, 88.8, -100.0, -np.inf, np.inf, np.nan],
+                 np.float32)
+    n = x.size
+    out = oracle.run(wl_of({"x": x, "y": np.zeros(n, np.float32)},
+                           [Op("exp", Ref("y"), (Ref("x"),), n=n)]))["y"]
+    assert out[0] == 1.0 and out[1] == 1.0
+    for xi, yi in zip(x[2:8], out[2:8]):
+        assert bits32(yi) == bits32(f32(math.exp(float(xi))))
+    assert out[7] == np.inf           # exp(88.8) overflows fp32
+    assert out[8] > 0 and out[8] < 2.0 ** -126  # subnormal result is kept
+    assert out[9] == 0.0 and out[10] == np.inf and np.isnan(out[11])
+
+
+# ----------------------------------------------------------------------------
+# row reductions
+
+
+def test_row_sum_exact_cases_and_rational_sum():
+    L = 256
+    bufs = {"x": np.full(4 * L, 2.0 ** -3, np.float32), "y": np.zeros(4, np.float32)}
+    bufs["x"][L:2 * L] = 2.0 ** 5
+    bufs["x"][2 * L:3 * L] = -(2.0 ** -20)
+    bufs["x"][3 * L:] = np.arange(L, dtype=np.float32)
+    out = oracle.run(wl_of(bufs, [Op("row_sum", Ref("y"), (Ref("x"),), n=4 * L, rows=4, row_len=L)]))
+    assert list(out["y"]) == [L * 2.0 ** -3, L * 2.0 ** 5, -L * 2.0 ** -20, L * (L - 1) / 2]
+    rng = np.random.default_rng(7)
+    R, L = 20, 333
+    x = (rng.standard_normal(R * L) * np.exp(rng.uniform(-8, 8, R * L))).astype(np.float32)
+    bufs = {"x": x, "y": np.zeros(R, np.float32)}
+    wl = wl_of(bufs, [Op("row_sum", Ref("y"), (Ref("x"),), n=R * L, rows=R, row_len=L)])
+    out, sc = oracle.run(wl, scales=True)
+    for r in range(R):
+        exact = sum(Fraction(float(v)) for v in x[r * L:(r + 1) * L])
+        want = f32(float(exact))
+        assert abs(float(out["y"][r]) - want) <= abs(want) * 2.0 ** -23 + 1e-300
+        assert sc["y"][r] == pytest.approx(float(np.abs(x[r * L:(r + 1) * L].astype(np.float64)).sum()))
+
+
+def test_row_sum_permutation_invariant():
+    rng = np.random.default_rng(8)
+    L = 1000
+    x = rng.standard_normal(L).astype(np.float32)
+    xp = rng.permutation(x)
+    bufs = {"x": np.concatenate([x, xp]), "y": np.zeros(2, np.float32)}
+    out, sc = oracle.run(wl_of(bufs, [Op("row_sum", Ref("y"), (Ref("x"),), n=2 * L, rows=2, row_len=L)]),
+                         scales=True)
+    assert abs(out["y"][0] - out["y"][1]) <= 1e-7 * sc["y"][0]
+
+
+def _softmax(x, R, L):
+    bufs = {"x": np.asarray(x, np.float32), "y": np.zeros(R * L, np.float32)}
+    return oracle.run(wl_of(bufs, [Op("row_softmax", Ref("y"), (Ref("x"),), n=R * L, rows=R,
+                                      row_len=L)]))["y"].reshape(R, L)
+
+
+def test_softmax_invariants():
+    rng = np.random.default_rng(9)
+    R, L = 16, 512
+    x = (rng.standard_normal(R * L) * 4).astype(np.float32)
+    y = _softmax(x, R, L)
+    s = y.astype(np.float64).sum(axis=1)
+    assert np.all(np.abs(s - 1.0) <= L * 2.0 ** -24)
+    assert np.all(np.argmax(y, axis=1) == np.argmax(x.reshape(R, L), axis=1))
+    # shifting a row by a constant leaves it unchanged (within rounding of the shift)
+    y2 = _softmax(x + np.float32(3.0), R, L)
+    assert np.allclose(y2, y, rtol=1e-5, atol=0)
+    # constant rows of power-of-two length give exactly 1/L
+    for L2 in (128, 1024, 4096):
+        yc = _softmax(np.full(L2, -7.25, np.float32), 1, L2)
+        assert np.all(yc == np.float32(1.0 / L2))
+
+
+def test_softmax_brute_force_and_special_rows():
+    rng = np.random.default_rng(10)
+    L = 7
+    x = rng.standard_normal(3 * L).astype(np.float32)
+    y = _softmax(x, 3, L)
+    for r in range(3):
+        row = [float(v) for v in x[r * L:(r + 1) * L]]
+        m = max(row)
+        e = [math.exp(v - m) for v in row]
+        tot = math.fsum(e)
+        for j in range(L):
+            assert abs(float(y[r, j]) - e[j] / tot) <= 2.0 ** -23 * (e[j] / tot)
+    special = np.array([0, 1, np.nan, 2, 3, np.inf, -np.inf, -np.inf, -np.inf], np.float32)
+    ys = _softmax(special, 3, 3)
+    assert np.all(np.isnan(ys))
+
+
+def test_rmsnorm_invariants_and_brute_force():
+    rng = np.random.default_rng(12)
+    R, L = 6, 896
+    x = rng.standard_normal(R * L).astype(np.float32) * 3
+    g = (rng.standard_normal(L) * 0.5 + 1).astype(np.float32)
+    eps = float(np.float32(1e-6))
+    bufs = {"x": x, "g": g, "y": np.zeros(R * L, np.float32)}
+    y = oracle.run(wl_of(bufs, [Op("rmsnorm", Ref("y"), (Ref("x"),), Ref("g"), n=R * L, rows=R,
+                                   row_len=L, eps=eps)]))["y"].reshape(R, L)
+    z = y.astype(np.float64) / g.astype(np.float64)
+    rms = np.sqrt((z * z).mean(axis=1))
+    assert np.all(np.abs(rms - 1.0) <= 1e-5)
+    for r in range(R):
+        row = x[r * L:(r + 1) * L]
+        ss = sum(Fraction(float(v)) ** 2 for v in row)
+        inv = 1.0 / math.sqrt(float(ss / L) + eps)
+        for j in (0, 1, 17, L - 1):
+            want = float(row[j]) * inv * float(g[j])
+            assert abs(float(y[r, j]) - want) <= 2.0 ** -22 * abs(want)
+    # rows whose mean square is comparable to eps: catches eps outside the root
+    xs = (rng.standard_normal(L) * 1e-3).astype(np.float32)
+    bufs = {"x": xs, "g": g, "y": np.zeros(L, np.float32)}
+    y = oracle.run(wl_of(bufs, [Op("rmsnorm", Ref("y"), (Ref("x"),), Ref("g"), n=L, rows=1,
+                                   row_len=L, eps=eps)]))["y"]
+    ss = sum(Fraction(float(v)) ** 2 for v in xs)
+    inv = 1.0 / math.sqrt(float(ss / L) + eps)
+    for j in (0, 5, L - 1):
+        want = float(xs[j]) * inv * float(g[j])
+        assert abs(float(y[j]) - want) <= 2.0 ** -22 * abs(want)
+    # constant row c: y = sign(c) * g up to the eps term
+    bufs = {"x": np.full(L, -2.0, np.float32), "g": g, "y": np.zeros(L, np.float32)}
+    y = oracle.run(wl_of(bufs, [Op("rmsnorm", Ref("y"), (Ref("x"),), Ref("g"), n=L, rows=1,
+                                   row_len=L, eps=eps)]))["y"]
+    assert np.allclose(y, -g, rtol=1e-6)
+
+
+# ----------------------------------------------------------------------------
+# rotary
+
+
+def _rope(x, tab, heads, hd, dtype="f32"):
+    bufs = {"x": x, "t": np.asarray(tab, np.float32),
+            "y": np.zeros(heads * hd, np.uint16 if dtype == "bf16" else np.float32)}
+    return oracle.run(wl_of(bufs, [Op("rope", Ref("y"), (Ref("x"),), Ref("t"), n=heads * hd,
+                                      dtype=dtype, rows=heads, row_len=hd, dims=(heads, hd))]))["y"]
+
+
+def test_rope_position_zero_is_identity_and_quarter_turn_swaps():
+    rng = np.random.default_rng(13)
+    H, hd = 3, 8
+    x = rng.standard_normal(H * hd).astype(np.float32)
+    tab0 = rope_table([0], hd)[0]
+    assert np.all(tab0[:hd // 2] == 1) and np.all(tab0[hd // 2:] == 0)
+    assert _same_bits(_rope(x, tab0, H, hd), x)
+    quarter = np.concatenate([np.zeros(hd // 2), np.ones(hd // 2)]).astype(np.float32)
+    y = _rope(x, quarter, H, hd).reshape(H, hd)
+    xr = x.reshape(H, hd)
+    assert np.array_equal(y[:, :hd // 2], -xr[:, hd // 2:])
+    assert np.array_equal(y[:, hd // 2:], xr[:, :hd // 2])
+
+
+def test_rope_brute_force_and_norm():
+    rng = np.random.default_rng(14)
+    H, hd = 4, 64
+    x = rng.standard_normal(H * hd).astype(np.float32)
+    tab = rope_table([531], hd)[0]
+    y = _rope(x, tab, H, hd)
+    half = hd // 2
+    for h in range(H):
+        for i in range(half):
+            a, b = float(x[h * hd + i]), float(x[h * hd + half + i])
+            c, s = float(tab[i]), float(tab[half + i])
+            assert bits32(y[h * hd + i]) == bits32(f32(f32(a * c) - f32(b * s)))
+            assert bits32(y[h * hd + half + i]) == bits32(f32(f32(b * c) + f32(a * s)))
+            n0 = math.hypot(a, b)
+            n1 = math.hypot(float(y[h * hd + i]), float(y[h * hd + half + i]))
+            assert abs(n1 - n0) <= 4 * 2.0 ** -24 * n0
+    # bf16 output is the fp32 rotation rounded with RNE
+    yb = _rope(f32_to_bf16(x), tab, H, hd, "bf16")
+    yf = _rope(bf16_to_f32(f32_to_bf16(x)), tab, H, hd)
+    assert np.array_equal(yb, f32_to_bf16(yf))
+
+
+# ----------------------------------------------------------------------------
+# GEMV and attention
+
+
+def _exact_dot(a, b):
+    return float(sum(Fraction(float(p)) * Fraction(float(q)) for p, q in zip(a, b)))
+
+
+def test_gemv_identity_onehot_and_rational_dot():
+    rng = np.random.default_rng(15)
+    K = 8
+    x = f32_to_bf16(rng.standard_normal(K).astype(np.float32))
+    eye = f32_to_bf16(np.eye(K, dtype=np.float32).reshape(-1))
+    bufs = {"W": eye, "x": x, "y": np.zeros(K, np.uint16)}
+    y = oracle.run(wl_of(bufs, [Op("gemv", Ref("y"), (Ref("x"),), Ref("W"), n=K, dtype="bf16",
+                                   dims=(K, K))]))["y"]
+    assert np.array_equal(y, x)
+    # one-hot rows act as a gather
+    M = 5
+    idx = [3, 0, 7, 7, 2]
+    W = np.zeros((M, K), np.float32)
+    W[np.arange(M), idx] = 1.0
+    bufs = {"W": f32_to_bf16(W.reshape(-1)), "x": x, "y": np.zeros(M, np.uint16)}
+    y = oracle.run(wl_of(bufs, [Op("gemv", Ref("y"), (Ref("x"),), Ref("W"), n=M, dtype="bf16",
+                                   dims=(M, K))]))["y"]
+    assert np.array_equal(y, x[idx])
+    # non-square, fp32 output, against an exact rational dot product
+    M, K = 5, 7
+    W = f32_to_bf16(rng.standard_normal(M * K).astype(np.float32))
+    xf = rng.standard_normal(K).astype(np.float32)
+    bufs = {"W": W, "x": xf, "y": np.zeros(M, np.float32)}
+    y = oracle.run(wl_of(bufs, [Op("gemv", Ref("y"), (Ref("x"),), Ref("W"), n=M, dims=(M, K))]))["y"]
+    Wf = bf16_to_f32(W).reshape(M, K)
+    for i in range(M):
+        assert bits32(y[i]) == bits32(f32(_exact_dot(Wf[i], xf)))
+
+
+def test_attention_brute_force():
+    rng = np.random.default_rng(16)
+    H, D, S = 3, 4, 5
+    q = f32_to_bf16(rng.standard_normal(H * D).astype(np.float32))
+    Kc = f32_to_bf16(rng.standard_normal(S * H * D).astype(np.float32))
+    Vc = f32_to_bf16(rng.standard_normal(S * H * D).astype(np.float32))
+    p = rng.uniform(0, 1, H * S).astype(np.float32)
+    bufs = {"q": q, "K": Kc, "V": Vc, "p": p, "s": np.zeros(H * S, np.float32),
+            "o": np.zeros(H * D, np.float32)}
+    ops = [Op("attn_score", Ref("s"), (Ref("q"),), Ref("K"), n=H * S, dtype="bf16", alpha=0.5,
+              dims=(H, D, S)),
+           Op("attn_av", Ref("o"), (Ref("p"),), Ref("V"), n=H * D, dtype="f32", dims=(H, D, S))]
+    wl = wl_of(bufs, ops)
+    wl.dtypes["o"] = "f32"
+    out = oracle.run(wl)
+    qf, Kf, Vf = bf16_to_f32(q), bf16_to_f32(Kc), bf16_to_f32(Vc)
+    for h in range(H):
+        for j in range(S):
+            ex = 0.5 * _exact_dot(qf[h * D:(h + 1) * D], Kf[j * H * D + h * D: j * H * D + (h + 1) * D])
+            assert bits32(out["s"][h * S + j]) == bits32(f32(ex))
+        for d in range(D):
+            ex = _exact_dot(p[h * S:(h + 1) * S], [Vf[j * H * D + h * D + d] for j in range(S)])
+            assert bits32(out["o"][h * D + d]) == bits32(f32(ex))
+
+
+def test_attention_zero_query_gives_column_mean():
+    rng = np.random.default_rng(17)
+    H, D, S = 2, 8, 512
+    Kc = f32_to_bf16(rng.standard_normal(S * H * D).astype(np.float32))
+    Vc = f32_to_bf16(rng.standard_normal(S * H * D).astype(np.float32))
+    bufs = {"q": np.zeros(H * D, np.uint16), "K": Kc, "V": Vc, "s": np.zeros(H * S, np.float32),
+            "p": np.zeros(H * S, np.float32), "o": np.zeros(H * D, np.float32)}
+    ops = [Op("attn_score", Ref("s"), (Ref("q"),), Ref("K"), n=H * S, dtype="bf16", alpha=0.125,
+              dims=(H, D, S)),
+           Op("row_softmax", Ref("p"), (Ref("s"),), n=H * S, rows=H, row_len=S),
+           Op("attn_av", Ref("o"), (Ref("p"),), Ref("V"), n=H * D, dtype="f32", dims=(H, D, S))]
+    out = oracle.run(wl_of(bufs, ops))
+    assert np.all(out["s"] == 0)
+    assert np.all(out["p"] == np.float32(1.0 / S))
+    Vf = bf16_to_f32(Vc).reshape(S, H * D)
+    for c in range(H * D):
+        want = f32(float(sum(Fraction(float(v)) for v in Vf[:, c]) / S))
+        assert bits32(out["o"][c]) == bits32(want)
+
+
+def test_silu_mul_limits():
+    g = np.array([0.0, 30.0, -30.0, 1.0, -1.0, 200.0, -200.0], np.float32)
+    u = np.array([5.0, 2.0, 2.0, 3.0, 3.0, 1.0, 1.0], np.float32)
+    n = g.size
+    bufs = {"g": g, "u": u, "y": np.zeros(n, np.float32)}
+    y = oracle.run(wl_of(bufs, [Op("silu_mul", Ref("y"), (Ref("g"), Ref("u")), n=n)]))["y"]
+    assert y[0] == 0.0
+    assert y[1] == np.float32(60.0)
+    assert 0 > float(y[2]) > -1e-11
+    assert bits32(y[3]) == bits32(f32(1.0 / (1.0 + math.exp(-1.0)) * 3.0))
+    assert bits32(y[4]) == bits32(f32(-1.0 / (1.0 + math.exp(1.0)) * 3.0))
+    assert y[5] == 200.0 and float(y[6]) <= 0 and float(y[6]) > -1e-80
+
+
+def test_gather_and_copy():
+    x = np.arange(10, dtype=np.float32) * 1.5
+    idx = np.array([9, 0, 3, 3, 7], np.int32)
+    bufs = {"x": x, "i": idx, "y": np.zeros(5, np.float32), "z": np.zeros(23, np.float32)}
+    out = oracle.run(wl_of(bufs, [Op("gather", Ref("y"), (Ref("x"),), Ref("i"), n=5, src_len=(10, 0)),
+                                  Op("copy", Ref("z"), (Ref("x", 2),), n=23, src_len=(4, 0))]))
+    assert list(out["y"]) == [x[9], x[0], x[3], x[3], x[7]]
+    assert list(out["z"]) == [x[2 + (k % 4)] for k in range(23)]
+    bufs["i"] = np.array([0, 10, 1, 1, 1], np.int32)
+    with pytest.raises(oracle.OracleError):
+        oracle.run(wl_of(bufs, [Op("gather", Ref("y"), (Ref("x"),), Ref("i"), n=5, src_len=(10, 0))]))
+
+
+# ----------------------------------------------------------------------------
+# the comparison rule
+
+
+def test_compare_flags_one_ulp_in_exact_class_and_accepts_within_tolerance():
+    rng = np.random.default_rng(18)
+    want = rng.standard_normal(1000).astype(np.float32)
+    got = want.copy()
+    assert compare(got, want, "f32").ok
+    got.view(np.uint32)[123] += 1
+    r = compare(got, want, "f32")
+    assert r.count == 1 and r.first_index == 123
+    scale = np.abs(want).astype(np.float64)
+    assert compare(got, want, "f32", scale).ok  # 1 ulp is inside 1e-5 relative
+    got[5] = want[5] * (1 + 3e-5)
+    assert not compare(got, want, "f32", scale).ok
+    # NaN matches NaN in both classes; inf must match by class
+    w = np.array([np.nan, np.inf, 1.0], np.float32)
+    assert compare(np.array([np.nan, np.inf, 1.0], np.float32), w, "f32").ok
+    assert not compare(np.array([np.nan, 3e38, 1.0], np.float32), w, "f32", np.ones(3)).ok
+    # -0 differs from +0 in the exact class
+    assert not compare(np.array([-0.0], np.float32), np.array([0.0], np.float32), "f32").ok
+
+
+# ----------------------------------------------------------------------------
+# generators
+
+
+def test_generators_are_deterministic_and_shaped():
+    a = gen_elementwise_queue(seed=0, n_ops=100, n=64)
+    b = gen_elementwise_queue(seed=0, n_ops=100, n=64)
+    assert [o.kind for o in a.ops] == [o.kind for o in b.ops]
+    assert all(np.array_equal(a.buffers[k], b.buffers[k]) for k in a.buffers)
+    assert {o.kind for o in a.ops} == {"add", "mul", "relu", "scale"}
+    assert np.all(np.abs(a.buffers["S0"]) <= 1)
+    dec = gen_decode(layers=2, tokens=3, kv_len=16)
+    assert len(dec.ops) == 2 * 3 * 15 and len(dec.groups) == 3
+    dag = gen_dynamic_dag(n_ops=500, n_max=1 << 14, pool_len=1 << 14)
+    for i, op in enumerate(dag.ops):
+        assert all(i - 8 <= d < i for d in op.deps)
+        if op.kind in ("row_sum", "row_softmax"):
+            # rows = max(1, n // L): a draw shorter than its row becomes one row
+            assert op.n == op.rows * op.row_len and 128 <= op.row_len <= 4096
+            assert 128 <= op.n <= 1 << 14
+        else:
+            assert 256 <= op.n <= 1 << 14
+    mix = gen_priority_mix(rounds=3, be_n=1024, lc_n=256)
+    assert sum(o.lc for o in mix.ops) == 30 and len(mix.ops) == 33
+
+
+def test_small_decode_runs_and_feeds_back():
+    wl = gen_decode(layers=2, tokens=2, kv_len=32)
+    out = oracle.run(wl)
+    assert not np.array_equal(out["x"], wl.buffers["x"])
+    # token t wrote its cache slot t
+    assert not np.array_equal(out["K0"][:896], wl.buffers["K0"][:896])
+    assert np.array_equal(out["K0"][2 * 896:], wl.buffers["K0"][2 * 896:])
