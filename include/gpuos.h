@@ -215,7 +215,10 @@ typedef struct gpuos_stats {
   uint64_t error_desc;         /* descriptor sequence that raised it */
   uint64_t worker_waves;       /* resident worker waves */
   uint64_t compute_units;
-  uint64_t reserved[4];
+  uint64_t kernel_ns;          /* lifetime of the resident kernel from HIP
+                                  events recorded on its stream around the
+                                  launch and its exit; 0 until gpuos_stop */
+  uint64_t reserved[3];
 } gpuos_stats;
 
 /* Per-descriptor device timing, recorded when config.trace == 1. */
@@ -296,6 +299,18 @@ int gpuos_get_stats(gpuos_ctx* ctx, gpuos_stats* out);
  */
 int gpuos_trace_read(gpuos_ctx* ctx, gpuos_trace_rec* out, uint32_t max,
                      uint32_t* n_out);
+
+/*
+ * Drains every submitted op, tells the resident kernel to exit (a STOP
+ * descriptor with one tile per worker wave) and waits for it, bounded by
+ * timeout_ns (< 0 = forever).  Afterwards the context accepts only
+ * gpuos_get_stats, gpuos_trace_read, gpuos_query, gpuos_sync (which returns
+ * at once) and gpuos_destroy; gpuos_stats.kernel_ns then holds the kernel's
+ * lifetime.  Calling it twice is harmless.
+ * Errors: ETIMEDOUT (ops did not drain or the kernel did not exit),
+ * EDEVICE (device error word set or HIP failure; the kernel is still stopped).
+ */
+int gpuos_stop(gpuos_ctx* ctx, int64_t timeout_ns);
 
 /*
  * Drains every submitted op (or abandons unflushed ones when the context is

@@ -13,8 +13,8 @@ pinned only through its individual ops) and GPUOS's own scheduling semantics
 """
 
 from .interpreter import (EXACT_KINDS, TOL_KINDS, OracleError, apply_op, bf16_to_f32,
-                          f32_to_bf16, out_len, run)
+                          f32_to_bf16, local_check, out_len, run)
 from .compare import RTOL, Mismatch, compare
 
 __all__ = ["EXACT_KINDS", "TOL_KINDS", "OracleError", "apply_op", "bf16_to_f32",
-           "f32_to_bf16", "out_len", "run", "RTOL", "Mismatch", "compare"]
+           "f32_to_bf16", "local_check", "out_len", "run", "RTOL", "Mismatch", "compare"]

@@ -303,3 +303,30 @@ def run(wl: Workload, upto: Optional[int] = None, scales: bool = False,
     if scales:
         return bufs, sc
     return bufs
+
+
+def local_check(wl: Workload, gpu: Dict[str, np.ndarray], compare_fn):
+    """Checks each op on the GPU's own inputs.
+
+    Requires a workload in which every element is written at most once (its
+    verification form), so the GPU's final buffers hold every op's output.
+    The state before op i is the initial buffers with the GPU outputs of ops
+    0..i-1 written into their ranges; op i is re-run by the oracle on that
+    state and its output compared with the GPU's.  Returns a list of
+    (op index, buffer, Mismatch) for every op whose output differs.
+    """
+    state = {k: v.copy() for k, v in wl.buffers.items()}
+    bad = []
+    for i, op in enumerate(wl.ops):
+        cnt = out_len(op)
+        if cnt == 0:
+            continue
+        name, off = op.out.buf, op.out.off
+        s = apply_op(op, state, wl.dtypes)
+        want = state[name][off:off + cnt].copy()
+        got = gpu[name][off:off + cnt]
+        r = compare_fn(got, want, wl.dtypes[name], s)
+        if not r.ok:
+            bad.append((i, name, r))
+        state[name][off:off + cnt] = got
+    return bad

@@ -1,0 +1,168 @@
+// Internal layouts shared by the host runtime and the device kernels.
+//
+// Queue structure ("GPUOS: A GPU Operating System Primitive for Transparent
+// Operation Fusion", section "The Paper": a host-managed work queue drained by
+// one long-lived kernel with atomic task queues).  The hand-off mirrors the
+// driver path of "Kernel Launch and Host-Device Interaction" (section "The
+// launch path": packets written into a pinned ring in host memory, then a
+// doorbell): here the host writes 256-byte descriptors into a pinned ring and
+// the doorbell is a release store of the ring tail that one device wave polls.
+//
+// Tiles of every published descriptor form one dense ticket space per ring:
+// descriptor `seq` owns tickets [ends[seq-1], ends[seq]).  Workers claim
+// tickets in increasing order, so claims follow op order (every tile a wave
+// waits on is already held by a running wave) and each tile runs exactly once.
+#pragma once
+
+#include <stddef.h>
+#include <stdint.h>
+
+namespace gpuos {
+
+// Internal opcodes beyond the public ones (gpuos_opcode).
+enum : uint8_t {
+  OP_FUSED_EW = 32,  // register-resident elementwise chain
+  OP_STOP = 33,      // one tile per worker wave; a wave that claims one exits
+};
+
+// Elementwise step codes inside a FUSED_EW micro-program.
+enum : uint8_t {
+  FS_ADD = 1,
+  FS_MUL = 2,
+  FS_SCALE = 3,
+  FS_RELU = 4,
+  FS_EXP = 5,
+  FS_COPY = 6,  // identity (a COPY folded into a chain)
+};
+
+// Step flag bits.  Bits 4..5 hold the index (1..3) of the fused input pointer
+// that supplies a binary step's second operand.
+enum : uint8_t {
+  FSF_OPERAND = 0x1,   // binary step: second operand is fused input in[idx]
+  FSF_SELF = 0x2,      // binary step whose second operand is the accumulator
+  FSF_STORE = 0x4,     // write the accumulator to out[s] after the step
+};
+
+constexpr int kMaxSteps = 8;
+constexpr int kMaxFusedInputs = 4;
+constexpr int kRings = 2;      // 0 = best effort (default), 1 = latency critical
+constexpr uint32_t kDescBytes = 256;
+constexpr uint32_t kDescMagic = 0x9e3779b9u;
+
+// Device descriptor: 256 bytes = 64 dwords; lane i of a wave fetches dword i.
+struct alignas(16) DevDesc {
+  uint8_t opcode;     // dword 0: public opcode or OP_FUSED_EW / OP_STOP
+  uint8_t dtype;      //          gpuos_dtype
+  uint8_t flags;      //          GPUOS_FLAG_*
+  uint8_t nsteps;     //          FUSED_EW program length
+  uint32_t n;         // 1: extent (see gpuos.h)
+  uint32_t rows;      // 2
+  uint32_t row_len;   // 3
+  uint64_t seq;       // 4-5: 1-based sequence in its ring
+  uint32_t ntiles;    // 6
+  uint32_t tile;      // 7: units per tile (elements, rows, key rows, chunks)
+  uint64_t deps[4];   // 8-15: sequences in the same ring to wait for
+  uint64_t wait_retired;  // 16-17: wait until the ring's in-order retire
+                          // cursor reaches this sequence (0 = none)
+  union {
+    struct {
+      uint64_t ptr[4];      // 18-25: out, in0, in1, in2
+      uint32_t src_len[2];  // 26-27: readable length of in0 / in1 (0 = n)
+      float alpha;          // 28
+      float eps;            // 29
+      int32_t aux[4];       // 30-33
+      uint8_t _pad[104];
+    } p;
+    struct {
+      uint64_t in[4];       // 18-25: in[0] = chain input, in[1..3] operands
+      uint64_t out[8];      // 26-41: output pointer of step s (FSF_STORE)
+      uint8_t step_op[8];   // 42-43
+      uint8_t step_fl[8];   // 44-45
+      float fscal[8];       // 46-53: SCALE factor of step s
+      uint8_t _pad[24];
+    } f;
+  };
+  uint64_t tstart;      // 60-61: first ticket of this descriptor
+  uint32_t user_ops;    // 62: user ops folded into this descriptor
+  uint32_t check;       // 63: (uint32)seq ^ kDescMagic
+};
+static_assert(sizeof(DevDesc) == kDescBytes, "descriptor must be 256 bytes");
+static_assert(offsetof(DevDesc, deps) == 8 * 4, "deps at dword 8");
+static_assert(offsetof(DevDesc, wait_retired) == 16 * 4, "wait_retired at dword 16");
+static_assert(offsetof(DevDesc, p.ptr) == 18 * 4, "ptr at dword 18");
+static_assert(offsetof(DevDesc, p.src_len) == 26 * 4, "src_len at dword 26");
+static_assert(offsetof(DevDesc, p.alpha) == 28 * 4, "alpha at dword 28");
+static_assert(offsetof(DevDesc, p.aux) == 30 * 4, "aux at dword 30");
+static_assert(offsetof(DevDesc, f.out) == 26 * 4, "fused out at dword 26");
+static_assert(offsetof(DevDesc, f.step_op) == 42 * 4, "step_op at dword 42");
+static_assert(offsetof(DevDesc, f.step_fl) == 44 * 4, "step_fl at dword 44");
+static_assert(offsetof(DevDesc, f.fscal) == 46 * 4, "fscal at dword 46");
+static_assert(offsetof(DevDesc, tstart) == 60 * 4, "tstart at dword 60");
+static_assert(offsetof(DevDesc, user_ops) == 62 * 4, "user_ops at dword 62");
+static_assert(offsetof(DevDesc, check) == 63 * 4, "check word is dword 63");
+
+// Device-side scheduler state of one ring (device memory).  Hot words sit on
+// their own 256-byte lines.
+struct alignas(256) DevRing {
+  uint64_t next;        // ticket counter (ring 0: fetch-add; ring 1: CAS)
+  uint64_t _p0[31];
+  uint64_t avail_ops;   // descriptors made visible by the doorbell wave
+  uint64_t avail_tiles; // tickets below this value are claimable
+  uint64_t _p1[30];
+  uint64_t retired;     // in-order retire cursor
+  uint64_t _p2[31];
+};
+
+struct alignas(256) DevCtl {
+  DevRing ring[kRings];
+  uint32_t stop;        // set by the doorbell wave when the host asks to stop
+  uint32_t _p0[63];
+};
+
+// Host-visible control block (pinned host memory, fine-grained).
+struct alignas(256) HostCtl {
+  uint64_t tail[kRings];      // host: last published sequence per ring
+  uint64_t _p0[30];
+  uint64_t completed[kRings]; // device: retire cursor per ring
+  uint64_t heartbeat;         // device: doorbell loop iterations
+  uint64_t _p1[29];
+  uint64_t stop_seq;          // host: ring-0 sequence of the STOP descriptor
+  uint64_t error;             // device: first error code (0 = none)
+  uint64_t error_seq;         // device: (ring << 62) | sequence that raised it
+  uint64_t _p2[29];
+};
+
+// Per-descriptor trace record (device memory), one per ring slot.
+struct TraceRec {
+  uint64_t seq;
+  uint64_t t_claim;
+  uint64_t t_done;
+  uint32_t opcode;
+  uint32_t ntiles;
+};
+
+// Device error codes (HostCtl::error).
+enum : uint64_t {
+  DERR_BAD_OPCODE = 1,
+  DERR_GATHER_RANGE = 2,
+  DERR_DESC_CHECK = 3,
+};
+
+// Everything the resident kernel needs, passed by value.
+struct KArgs {
+  const DevDesc* hdesc[kRings];   // pinned host ring (device-visible address)
+  const uint64_t* hends[kRings];  // pinned host: ends[slot] per descriptor
+  HostCtl* hctl;                  // pinned host control block
+  DevCtl* dctl;                   // device control block
+  uint64_t* dends[kRings];        // device copy of ends[], 2 * ring_slots
+                                  // entries indexed by (seq - 1) mod 2*slots
+  uint64_t* done_id[kRings];      // device: last completed sequence per slot
+  uint32_t* tiles_done[kRings];   // device: tiles finished per slot
+  TraceRec* trace[kRings];        // device trace ring (nullable)
+  uint32_t cap_mask;              // ring_slots - 1
+  uint32_t ends_mask;             // 2 * ring_slots - 1
+  uint32_t workers;               // worker waves (all waves but the doorbell)
+  uint32_t lc_enabled;            // poll the latency-critical ring
+};
+
+}  // namespace gpuos

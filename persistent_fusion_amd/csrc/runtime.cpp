@@ -1,0 +1,1438 @@
+// Host runtime of the persistent small-op queue: contexts, validation, hazard
+// dependencies, the fusion pass, ring publication (the doorbell), completion
+// tracking, and the per-op launch comparator.
+//
+// The queue is the "host-managed work queue" of "GPUOS: A GPU Operating
+// System Primitive for Transparent Operation Fusion" (section "The Paper"),
+// fed in "unified submissions" (one flush publishes many ops).  The hand-off
+// follows "Kernel Launch and Host-Device Interaction" (section "The launch
+// path"): descriptors go into a pinned ring in host memory and a single store
+// of the ring tail acts as the doorbell; the GPU side polls it.  Pinned memory
+// is what lets the device read the ring directly (same page, section "Memory
+// transfers").
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <atomic>
+#include <cstdarg>
+#include <chrono>
+#include <cstdio>
+#include <cstdlib>
+#include <cstring>
+#include <deque>
+#include <map>
+#include <mutex>
+#include <string>
+#include <thread>
+#include <vector>
+
+#include "../../include/gpuos.h"
+#include "../../include/gpuos_debug.h"
+#include "gpuos_internal.h"
+#include "kernels.h"
+
+using namespace gpuos;
+
+namespace {
+
+thread_local std::string g_last_error;
+
+int fail(int code, const char* fmt, ...) __attribute__((format(printf, 2, 3)));
+int fail(int code, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof buf, fmt, ap);
+  va_end(ap);
+  g_last_error = buf;
+  if (getenv("GPUOS_LOG")) fprintf(stderr, "gpuos: %s\n", buf);
+  return code;
+}
+
+#define HIP_TRY(expr)                                                              \
+  do {                                                                             \
+    hipError_t e_ = (expr);                                                        \
+    if (e_ != hipSuccess)                                                          \
+      return fail(GPUOS_EDEVICE, "%s failed: %s", #expr, hipGetErrorString(e_));   \
+  } while (0)
+
+inline uint64_t load_acq(const uint64_t* p) {
+  return __atomic_load_n(p, __ATOMIC_ACQUIRE);
+}
+inline void store_rel(uint64_t* p, uint64_t v) { __atomic_store_n(p, v, __ATOMIC_RELEASE); }
+
+inline void cpu_relax() {
+#if defined(__x86_64__)
+  __builtin_ia32_pause();
+#endif
+}
+
+uint32_t elem_size(uint32_t dt) { return dt == GPUOS_BF16 ? 2u : 4u; }
+
+bool is_elementwise(uint32_t op) {
+  switch (op) {
+    case GPUOS_OP_COPY: case GPUOS_OP_GATHER: case GPUOS_OP_ADD: case GPUOS_OP_MUL:
+    case GPUOS_OP_SCALE: case GPUOS_OP_RELU: case GPUOS_OP_EXP: case GPUOS_OP_SILU_MUL:
+      return true;
+    default:
+      return false;
+  }
+}
+
+bool is_binary(uint32_t op) {
+  return op == GPUOS_OP_ADD || op == GPUOS_OP_MUL || op == GPUOS_OP_SILU_MUL;
+}
+
+// ---------------------------------------------------------------------------
+// byte ranges an op reads and writes (used by validation and hazards)
+
+struct Range {
+  uint64_t lo, hi;
+};
+
+struct OpRanges {
+  Range w{0, 0};
+  Range r[3]{};
+  int nr = 0;
+};
+
+uint64_t src_extent(uint64_t src_len, uint64_t extent) {
+  if (src_len == 0 || src_len >= extent) return extent;
+  return src_len;
+}
+
+OpRanges op_ranges(const gpuos_op& o) {
+  OpRanges R;
+  const uint64_t es = elem_size(o.dtype);
+  auto rd = [&](const void* p, uint64_t bytes) {
+    if (p && bytes) R.r[R.nr++] = Range{(uint64_t)p, (uint64_t)p + bytes};
+  };
+  auto wr = [&](void* p, uint64_t bytes) {
+    if (p && bytes) R.w = Range{(uint64_t)p, (uint64_t)p + bytes};
+  };
+  const uint64_t n = o.n;
+  switch (o.opcode) {
+    case GPUOS_OP_COPY: case GPUOS_OP_ADD: case GPUOS_OP_MUL: case GPUOS_OP_SCALE:
+    case GPUOS_OP_RELU: case GPUOS_OP_EXP: case GPUOS_OP_SILU_MUL:
+      wr(o.out, n * es);
+      rd(o.in[0], src_extent(o.src_len[0], n) * es);
+      if (is_binary(o.opcode)) rd(o.in[1], src_extent(o.src_len[1], n) * es);
+      break;
+    case GPUOS_OP_GATHER:
+      wr(o.out, n * es);
+      rd(o.in[0], o.src_len[0] * es);
+      rd(o.in[2], n * 4);
+      break;
+    case GPUOS_OP_ROW_SUM:
+      wr(o.out, (uint64_t)o.rows * es);
+      rd(o.in[0], src_extent(o.src_len[0], n) * es);
+      break;
+    case GPUOS_OP_ROW_SOFTMAX:
+      wr(o.out, n * es);
+      rd(o.in[0], src_extent(o.src_len[0], n) * es);
+      break;
+    case GPUOS_OP_RMSNORM:
+      wr(o.out, n * es);
+      rd(o.in[0], src_extent(o.src_len[0], n) * es);
+      rd(o.in[2], (uint64_t)o.row_len * es);
+      break;
+    case GPUOS_OP_ROPE:
+      wr(o.out, n * es);
+      rd(o.in[0], n * es);
+      rd(o.in[2], (uint64_t)o.row_len * 4);
+      break;
+    case GPUOS_OP_GEMV:
+      wr(o.out, (uint64_t)o.aux[0] * es);
+      rd(o.in[0], (uint64_t)o.aux[1] * es);
+      rd(o.in[2], (uint64_t)o.aux[0] * (uint64_t)o.aux[1] * 2);
+      break;
+    case GPUOS_OP_ATTN_SCORE: {
+      const uint64_t H = o.aux[0], D = o.aux[1], S = o.aux[2];
+      wr(o.out, H * S * 4);
+      rd(o.in[0], H * D * es);
+      rd(o.in[2], S * H * D * 2);
+      break;
+    }
+    case GPUOS_OP_ATTN_AV: {
+      const uint64_t H = o.aux[0], D = o.aux[1], S = o.aux[2];
+      wr(o.out, H * D * es);
+      rd(o.in[0], H * S * 4);
+      rd(o.in[2], S * H * D * 2);
+      break;
+    }
+    default:
+      break;
+  }
+  return R;
+}
+
+bool overlaps(const Range& a, const Range& b) {
+  return a.lo < b.hi && b.lo < a.hi && a.hi > a.lo && b.hi > b.lo;
+}
+
+// ---------------------------------------------------------------------------
+// validation
+
+int validate(const gpuos_op& o, uint32_t index) {
+  const uint32_t op = o.opcode;
+  if (op >= GPUOS_OP_COUNT) return fail(GPUOS_EINVAL, "op %u: unknown opcode %u", index, op);
+  if (o.dtype > GPUOS_I32) return fail(GPUOS_EINVAL, "op %u: unknown dtype %u", index, o.dtype);
+  if (o.flags & ~0x7u) return fail(GPUOS_EINVAL, "op %u: unknown flag bits 0x%x", index, o.flags);
+  if (o.dtype == GPUOS_I32 && op != GPUOS_OP_COPY && op != GPUOS_OP_GATHER)
+    return fail(GPUOS_EINVAL, "op %u: int32 is only for COPY and GATHER", index);
+  const uint64_t es = elem_size(o.dtype);
+  auto need = [&](const void* p, const char* what) -> int {
+    if (!p) return fail(GPUOS_EINVAL, "op %u: %s pointer is null", index, what);
+    return 0;
+  };
+  auto align = [&](const void* p, uint64_t a, const char* what) -> int {
+    if (p && ((uintptr_t)p % a)) return fail(GPUOS_EINVAL, "op %u: %s not %llu-byte aligned",
+                                             index, what, (unsigned long long)a);
+    return 0;
+  };
+  int rc;
+  if (op == GPUOS_OP_NOP) return 0;
+  if (op == GPUOS_OP_SPIN) {
+    if (o.aux[0] < 0) return fail(GPUOS_EINVAL, "op %u: negative spin time", index);
+    return 0;
+  }
+  if (o.n == 0) return fail(GPUOS_EINVAL, "op %u: n must be > 0", index);
+  if ((rc = need(o.out, "out"))) return rc;
+  if ((rc = need(o.in[0], "in[0]"))) return rc;
+  if ((rc = align(o.out, es, "out"))) return rc;
+  if ((rc = align(o.in[0], es, "in[0]"))) return rc;
+  if (o.src_len[0] > 0xffffffffull || o.src_len[1] > 0xffffffffull)
+    return fail(GPUOS_EINVAL, "op %u: src_len beyond 2^32", index);
+  if (is_binary(op)) {
+    if ((rc = need(o.in[1], "in[1]"))) return rc;
+    if ((rc = align(o.in[1], es, "in[1]"))) return rc;
+  }
+  switch (op) {
+    case GPUOS_OP_GATHER:
+      if ((rc = need(o.in[2], "index"))) return rc;
+      if ((rc = align(o.in[2], 4, "index"))) return rc;
+      if (o.src_len[0] == 0) return fail(GPUOS_EINVAL, "op %u: GATHER needs src_len[0]", index);
+      break;
+    case GPUOS_OP_ROW_SUM: case GPUOS_OP_ROW_SOFTMAX: case GPUOS_OP_RMSNORM:
+      if (o.rows == 0 || o.row_len == 0 || (uint64_t)o.rows * o.row_len != o.n)
+        return fail(GPUOS_EINVAL, "op %u: row op needs n == rows * row_len", index);
+      if (o.row_len > 4096) return fail(GPUOS_EINVAL, "op %u: row_len > 4096", index);
+      if (op == GPUOS_OP_RMSNORM) {
+        if ((rc = need(o.in[2], "gain"))) return rc;
+        if ((rc = align(o.in[2], es, "gain"))) return rc;
+        if (!(o.eps >= 0.0f)) return fail(GPUOS_EINVAL, "op %u: eps must be >= 0", index);
+      }
+      break;
+    case GPUOS_OP_ROPE:
+      if (o.rows == 0 || o.row_len == 0 || (o.row_len & 1) ||
+          (uint64_t)o.rows * o.row_len != o.n)
+        return fail(GPUOS_EINVAL, "op %u: ROPE needs n == heads * head_dim, even head_dim", index);
+      if ((rc = need(o.in[2], "table"))) return rc;
+      if ((rc = align(o.in[2], 4, "table"))) return rc;
+      break;
+    case GPUOS_OP_GEMV:
+      if (o.aux[0] <= 0 || o.aux[1] <= 0 || (uint32_t)o.aux[0] != o.n)
+        return fail(GPUOS_EINVAL, "op %u: GEMV needs aux = {M, K} with n == M", index);
+      if ((rc = need(o.in[2], "weight"))) return rc;
+      if ((rc = align(o.in[2], 2, "weight"))) return rc;
+      break;
+    case GPUOS_OP_ATTN_SCORE: case GPUOS_OP_ATTN_AV: {
+      if (o.aux[0] <= 0 || o.aux[1] <= 0 || o.aux[2] <= 0)
+        return fail(GPUOS_EINVAL, "op %u: attention needs aux = {H, D, S}", index);
+      const uint64_t H = o.aux[0], D = o.aux[1], S = o.aux[2];
+      if (op == GPUOS_OP_ATTN_SCORE && H * S != o.n)
+        return fail(GPUOS_EINVAL, "op %u: ATTN_SCORE needs n == H * S", index);
+      if (op == GPUOS_OP_ATTN_AV && H * D != o.n)
+        return fail(GPUOS_EINVAL, "op %u: ATTN_AV needs n == H * D", index);
+      if ((rc = need(o.in[2], "cache"))) return rc;
+      if ((rc = align(o.in[2], 2, "cache"))) return rc;
+      if (op == GPUOS_OP_ATTN_AV && ((uintptr_t)o.in[0] % 4))
+        return fail(GPUOS_EINVAL, "op %u: probabilities must be fp32 aligned", index);
+      break;
+    }
+    default:
+      break;
+  }
+  return 0;
+}
+
+// ---------------------------------------------------------------------------
+// hazard map: non-overlapping byte segments, each with its last writer and
+// the readers since that write (user op ids).
+
+struct Seg {
+  uint64_t hi;
+  uint64_t writer;
+  std::vector<uint64_t> readers;
+};
+
+class HazardMap {
+ public:
+  template <class Retired>
+  void access(const Range& rg, uint64_t id, bool write, std::vector<uint64_t>& deps,
+              Retired retired) {
+    if (rg.hi <= rg.lo) return;
+    split(rg.lo);
+    split(rg.hi);
+    auto it = segs_.lower_bound(rg.lo);
+    uint64_t cur = rg.lo;
+    std::vector<std::pair<uint64_t, uint64_t>> gaps;
+    while (it != segs_.end() && it->first < rg.hi) {
+      if (it->first > cur) gaps.push_back({cur, it->first});
+      Seg& s = it->second;
+      if (s.writer && !retired(s.writer)) deps.push_back(s.writer);
+      if (write)
+        for (uint64_t r : s.readers)
+          if (!retired(r)) deps.push_back(r);
+      cur = s.hi;
+      ++it;
+    }
+    if (cur < rg.hi) gaps.push_back({cur, rg.hi});
+    if (write) {
+      segs_.erase(segs_.lower_bound(rg.lo), segs_.lower_bound(rg.hi));
+      segs_[rg.lo] = Seg{rg.hi, id, {}};
+    } else {
+      for (auto g : gaps) segs_[g.first] = Seg{g.second, 0, {}};
+      for (auto i2 = segs_.lower_bound(rg.lo); i2 != segs_.end() && i2->first < rg.hi; ++i2) {
+        auto& rd = i2->second.readers;
+        if (rd.empty() || rd.back() != id) rd.push_back(id);
+        if (rd.size() > 32) prune_vec(rd, retired);
+      }
+    }
+  }
+
+  template <class Retired>
+  void prune(Retired retired) {
+    for (auto it = segs_.begin(); it != segs_.end();) {
+      Seg& s = it->second;
+      if (s.writer && retired(s.writer)) s.writer = 0;
+      prune_vec(s.readers, retired);
+      if (!s.writer && s.readers.empty())
+        it = segs_.erase(it);
+      else
+        ++it;
+    }
+  }
+
+  size_t size() const { return segs_.size(); }
+  void clear() { segs_.clear(); }
+
+ private:
+  template <class Retired>
+  static void prune_vec(std::vector<uint64_t>& v, Retired retired) {
+    v.erase(std::remove_if(v.begin(), v.end(), [&](uint64_t x) { return retired(x); }), v.end());
+  }
+
+  void split(uint64_t x) {
+    auto it = segs_.upper_bound(x);
+    if (it == segs_.begin()) return;
+    --it;
+    if (it->first < x && x < it->second.hi) {
+      Seg tail = it->second;
+      it->second.hi = x;
+      segs_[x] = std::move(tail);
+    }
+  }
+
+  std::map<uint64_t, Seg> segs_;
+};
+
+}  // namespace
+
+// ---------------------------------------------------------------------------
+// context
+
+struct Staged {
+  gpuos_op op;
+  uint64_t id;
+  uint32_t ring;
+  std::vector<uint64_t> deps;  // user ids
+};
+
+// A device op after the fusion pass: one descriptor built from user ops
+// [first, first + count) of the staged list.
+struct Planned {
+  size_t first;
+  uint32_t count;
+  DevDesc desc;
+  std::vector<uint64_t> deps;  // user ids outside the group
+  uint32_t ring;
+};
+
+struct gpuos_ctx {
+  int device = GPUOS_DEVICE_NONE;
+  bool host_only = true;
+  gpuos_config cfg{};
+  hipStream_t stream = nullptr;
+  uint32_t cap = 0, cus = 0, blocks = 0, workers = 0;
+
+  // pinned host memory (malloc'd in host-only mode)
+  HostCtl* hctl = nullptr;
+  DevDesc* hdesc[kRings] = {nullptr, nullptr};
+  uint64_t* hends[kRings] = {nullptr, nullptr};
+  // device memory
+  DevCtl* dctl = nullptr;
+  uint64_t* dends[kRings] = {nullptr, nullptr};
+  uint64_t* done_id[kRings] = {nullptr, nullptr};
+  uint32_t* tiles_done[kRings] = {nullptr, nullptr};
+  TraceRec* trace[kRings] = {nullptr, nullptr};
+
+  // host bookkeeping
+  uint64_t next_id = 1;
+  uint64_t id_base = 1;            // ids below are retired and forgotten
+  std::deque<uint64_t> idseq;      // (ring << 63) | seq, 0 = staged
+  std::vector<Staged> staged;
+  uint64_t pub_seq[kRings] = {0, 0};
+  uint64_t pub_tiles[kRings] = {0, 0};
+  uint64_t tail_written[kRings] = {0, 0};
+  HazardMap hazards;
+  uint64_t since_prune = 0;
+  bool poisoned = false;
+  bool stopped = false;     // STOP published; no more submissions
+  bool exited = false;      // resident kernel has exited
+  bool leaked = false;      // kernel did not exit: memory must not be freed
+  hipEvent_t ev_start = nullptr, ev_end = nullptr;
+  gpuos_stats st{};
+};
+
+namespace {
+
+uint64_t completed_of(gpuos_ctx* c, uint32_t ring) { return load_acq(&c->hctl->completed[ring]); }
+
+bool check_device_error(gpuos_ctx* c) {
+  if (c->poisoned) return true;
+  const uint64_t e = load_acq(&c->hctl->error);
+  if (e) {
+    c->poisoned = true;
+    c->st.device_error = e;
+    c->st.error_desc = c->hctl->error_seq;
+    fail(GPUOS_EDEVICE, "device error %llu at ring %llu seq %llu", (unsigned long long)e,
+         (unsigned long long)(c->hctl->error_seq >> 62),
+         (unsigned long long)(c->hctl->error_seq & ((1ull << 62) - 1)));
+    return true;
+  }
+  return false;
+}
+
+// Is user op `id` known to have completed?
+bool id_retired(gpuos_ctx* c, uint64_t id) {
+  if (id < c->id_base) return true;
+  const uint64_t idx = id - c->id_base;
+  if (idx >= c->idseq.size()) return false;
+  const uint64_t v = c->idseq[idx];
+  if (!v) return false;
+  return (v & ((1ull << 63) - 1)) <= completed_of(c, (uint32_t)(v >> 63));
+}
+
+void prune_ids(gpuos_ctx* c) {
+  while (!c->idseq.empty()) {
+    const uint64_t v = c->idseq.front();
+    if (!v) break;
+    if ((v & ((1ull << 63) - 1)) > completed_of(c, (uint32_t)(v >> 63))) break;
+    c->idseq.pop_front();
+    ++c->id_base;
+  }
+}
+
+uint32_t ring_of_id(gpuos_ctx* c, uint64_t id, bool* known) {
+  *known = false;
+  if (id < c->id_base) return 0;
+  const uint64_t idx = id - c->id_base;
+  if (idx >= c->idseq.size()) return 0;
+  const uint64_t v = c->idseq[idx];
+  if (v) {
+    *known = true;
+    return (uint32_t)(v >> 63);
+  }
+  for (const Staged& s : c->staged)
+    if (s.id == id) {
+      *known = true;
+      return s.ring;
+    }
+  return 0;
+}
+
+// ---------------------------------------------------------------------------
+// descriptor encoding
+
+uint32_t ceil_div(uint64_t a, uint64_t b) { return (uint32_t)((a + b - 1) / b); }
+
+// Elementwise tile: cfg.tile_elems, or be_tile_elems for very large ops.
+// Large ops get a tile count that is a multiple of the worker count so the
+// last round of tiles does not leave most waves idle.
+uint32_t ew_tile_elems(const gpuos_config& cfg, uint32_t workers, uint64_t n) {
+  uint64_t tile = n >= (1ull << 24) ? cfg.be_tile_elems : cfg.tile_elems;
+  const uint64_t nt = (n + tile - 1) / tile;
+  if (workers && nt > workers) {
+    const uint64_t rounds = (nt + workers - 1) / workers;
+    uint64_t t2 = (n + rounds * workers - 1) / (rounds * workers);
+    t2 = (t2 + 255) / 256 * 256;
+    if (t2 >= 256 && t2 <= tile) tile = t2;
+  }
+  return (uint32_t)tile;
+}
+
+void set_tiling(const gpuos_config& cfg, uint32_t workers, DevDesc& d) {
+  switch (d.opcode) {
+    case GPUOS_OP_NOP: case GPUOS_OP_SPIN: case GPUOS_OP_ROPE:
+      d.tile = 1;
+      d.ntiles = 1;
+      break;
+    case GPUOS_OP_ROW_SUM: case GPUOS_OP_ROW_SOFTMAX: case GPUOS_OP_RMSNORM: {
+      uint32_t rpt = std::max<uint32_t>(1, 4096 / d.row_len);
+      const uint32_t by_waves = ceil_div(d.rows, std::max<uint32_t>(1, workers));
+      rpt = std::min(rpt, std::max<uint32_t>(1, by_waves));
+      d.tile = rpt;
+      d.ntiles = ceil_div(d.rows, rpt);
+      break;
+    }
+    case GPUOS_OP_GEMV: {
+      const uint32_t M = (uint32_t)d.p.aux[0];
+      uint32_t r = ceil_div(M, std::max<uint32_t>(1, workers));
+      r = std::min<uint32_t>(std::max<uint32_t>(r, 1), 16);
+      d.tile = r;
+      d.ntiles = ceil_div(M, r);
+      break;
+    }
+    case GPUOS_OP_ATTN_SCORE: {
+      const uint32_t S = (uint32_t)d.p.aux[2];
+      uint32_t r = ceil_div(S, std::max<uint32_t>(1, workers));
+      r = std::max<uint32_t>(r, 1);
+      d.tile = r;
+      d.ntiles = ceil_div(S, r);
+      break;
+    }
+    case GPUOS_OP_ATTN_AV: {
+      const uint32_t H = (uint32_t)d.p.aux[0], D = (uint32_t)d.p.aux[1];
+      if (D % 8 == 0) {
+        d.tile = 1;
+        d.ntiles = H * D / 8;
+      } else {
+        d.tile = 8;
+        d.ntiles = ceil_div((uint64_t)H * D, 8);
+      }
+      break;
+    }
+    default: {  // elementwise and fused
+      d.tile = ew_tile_elems(cfg, workers, d.n);
+      d.ntiles = ceil_div(d.n, d.tile);
+      break;
+    }
+  }
+}
+
+void encode_plain(const gpuos_op& o, const gpuos_config& cfg, uint32_t workers, DevDesc& d) {
+  memset(&d, 0, sizeof d);
+  d.opcode = (uint8_t)o.opcode;
+  d.dtype = o.dtype;
+  d.flags = o.flags;
+  d.n = o.n;
+  d.rows = o.rows;
+  d.row_len = o.row_len;
+  if (o.opcode == GPUOS_OP_GATHER || o.opcode == GPUOS_OP_NOP || o.opcode == GPUOS_OP_SPIN) {
+    // nothing to normalise
+  }
+  d.p.ptr[0] = (uint64_t)o.out;
+  d.p.ptr[1] = (uint64_t)o.in[0];
+  d.p.ptr[2] = (uint64_t)o.in[1];
+  d.p.ptr[3] = (uint64_t)o.in[2];
+  for (int i = 0; i < 2; ++i) {
+    uint64_t sl = o.src_len[i];
+    if (o.opcode != GPUOS_OP_GATHER && sl >= o.n) sl = 0;  // a longer source is read as a prefix
+    d.p.src_len[i] = (uint32_t)sl;
+  }
+  d.p.alpha = o.alpha;
+  d.p.eps = o.eps;
+  for (int i = 0; i < 4; ++i) d.p.aux[i] = o.aux[i];
+  if (o.opcode == GPUOS_OP_ROPE) {
+    d.rows = o.rows;
+    d.row_len = o.row_len;
+  }
+  d.user_ops = 1;
+  set_tiling(cfg, workers, d);
+}
+
+// ---------------------------------------------------------------------------
+// fusion pass: merges maximal runs of adjacent elementwise ops in which each
+// op consumes its predecessor's output element for element into one
+// FUSED_EW descriptor ("Launch Overhead and Fusion", section "Fusion": one
+// pass, intermediates kept in registers).  Results stay bit-identical: every
+// step is the same single IEEE operation, rounded to the storage type after
+// each step, and stores of intermediates are kept unless the op is marked
+// transient and no later queued op reads it.
+
+uint8_t fuse_code(uint32_t op) {
+  switch (op) {
+    case GPUOS_OP_ADD: return FS_ADD;
+    case GPUOS_OP_MUL: return FS_MUL;
+    case GPUOS_OP_SCALE: return FS_SCALE;
+    case GPUOS_OP_RELU: return FS_RELU;
+    case GPUOS_OP_EXP: return FS_EXP;
+    case GPUOS_OP_COPY: return FS_COPY;
+    default: return 0;
+  }
+}
+
+bool fusable(const gpuos_op& o) {
+  if (!fuse_code(o.opcode)) return false;
+  if (o.dtype == GPUOS_I32) return false;
+  if (o.src_len[0] && o.src_len[0] < o.n) return false;
+  if (is_binary(o.opcode) && o.src_len[1] && o.src_len[1] < o.n) return false;
+  return true;
+}
+
+struct ChainState {
+  uint64_t chain_in = 0;           // pointer loaded into the accumulator
+  uint64_t operands[3] = {0, 0, 0};
+  int nops = 0;
+  std::vector<Range> outs;         // output ranges written so far (in order)
+  std::vector<Range> reads;        // every range read by the chain
+  uint64_t last_out = 0;
+};
+
+// Can op `o` extend the chain whose previous op wrote `st.last_out`?
+// On success fills the step encoding.
+bool try_extend(const gpuos_op& o, ChainState& st, uint8_t& code, uint8_t& fl) {
+  const uint64_t es = elem_size(o.dtype);
+  const uint64_t bytes = (uint64_t)o.n * es;
+  const uint64_t P = st.last_out;
+  const uint64_t i0 = (uint64_t)o.in[0], i1 = (uint64_t)o.in[1];
+  code = fuse_code(o.opcode);
+  fl = 0;
+  uint64_t operand = 0;
+  if (is_binary(o.opcode)) {
+    if (i0 == P && i1 == P)
+      fl = FSF_SELF;
+    else if (i0 == P)
+      operand = i1;
+    else if (i1 == P)
+      operand = i0;
+    else
+      return false;
+  } else {
+    if (i0 != P) return false;
+  }
+  const Range out{(uint64_t)o.out, (uint64_t)o.out + bytes};
+  if (operand) {
+    const Range orng{operand, operand + bytes};
+    // the operand is loaded before any step runs: it must not depend on a
+    // value written earlier in the chain
+    for (const Range& w : st.outs)
+      if (overlaps(w, orng)) return false;
+  }
+  // the new output must not clobber, at another element, anything the chain
+  // reads; in place (same base) is fine because loads precede stores
+  auto ok_against = [&](const Range& r) {
+    return !overlaps(r, out) || r.lo == out.lo;
+  };
+  for (const Range& r : st.reads)
+    if (!ok_against(r)) return false;
+  for (const Range& w : st.outs)
+    if (overlaps(w, out) && w.lo != out.lo) return false;
+  if (operand) {
+    const Range orng{operand, operand + bytes};
+    if (!ok_against(orng)) return false;
+    int idx = -1;
+    for (int k = 0; k < st.nops; ++k)
+      if (st.operands[k] == operand) idx = k;
+    if (idx < 0) {
+      if (st.nops == 3) return false;
+      idx = st.nops;
+      st.operands[st.nops++] = operand;
+    }
+    fl |= (uint8_t)(FSF_OPERAND | ((idx + 1) << 4));
+    st.reads.push_back(orng);
+  }
+  st.outs.push_back(out);
+  st.last_out = (uint64_t)o.out;
+  return true;
+}
+
+void plan_ops(gpuos_ctx* c, size_t begin, size_t end, std::vector<Planned>& plan) {
+  const gpuos_config& cfg = c->cfg;
+  const bool fuse = cfg.fusion == 1;
+  size_t i = begin;
+  while (i < end) {
+    const Staged& s0 = c->staged[i];
+    Planned pl;
+    pl.first = i;
+    pl.count = 1;
+    pl.ring = s0.ring;
+    size_t j = i + 1;
+    if (fuse && fusable(s0.op)) {
+      ChainState st;
+      const gpuos_op& o0 = s0.op;
+      const uint64_t es = elem_size(o0.dtype);
+      const uint64_t bytes = (uint64_t)o0.n * es;
+      st.chain_in = (uint64_t)o0.in[0];
+      st.reads.push_back(Range{st.chain_in, st.chain_in + bytes});
+      uint8_t fl0 = 0;
+      if (is_binary(o0.opcode)) {
+        if (o0.in[1] == o0.in[0]) {
+          fl0 = FSF_SELF;
+        } else {
+          st.operands[0] = (uint64_t)o0.in[1];
+          st.nops = 1;
+          fl0 = (uint8_t)(FSF_OPERAND | (1 << 4));
+          st.reads.push_back(Range{st.operands[0], st.operands[0] + bytes});
+        }
+      }
+      const Range out0{(uint64_t)o0.out, (uint64_t)o0.out + bytes};
+      bool first_ok = true;
+      for (const Range& r : st.reads)
+        if (overlaps(r, out0) && r.lo != out0.lo) first_ok = false;
+      if (first_ok) {
+        st.outs.push_back(out0);
+        st.last_out = (uint64_t)o0.out;
+        uint8_t codes[kMaxSteps], fls[kMaxSteps];
+        codes[0] = fuse_code(o0.opcode);
+        fls[0] = fl0;
+        uint32_t n_steps = 1;
+        const uint32_t max_steps = std::min<uint32_t>(cfg.max_fuse, kMaxSteps);
+        while (j < end && n_steps < max_steps) {
+          const Staged& sj = c->staged[j];
+          if (sj.ring != s0.ring || !fusable(sj.op) || sj.op.dtype != o0.dtype ||
+              sj.op.n != o0.n)
+            break;
+          ChainState trial = st;
+          uint8_t code, fl;
+          if (!try_extend(sj.op, trial, code, fl)) break;
+          st = trial;
+          codes[n_steps] = code;
+          fls[n_steps] = fl;
+          ++n_steps;
+          ++j;
+        }
+        if (n_steps > 1) {
+          DevDesc& d = pl.desc;
+          memset(&d, 0, sizeof d);
+          d.opcode = OP_FUSED_EW;
+          d.dtype = o0.dtype;
+          d.n = o0.n;
+          d.nsteps = (uint8_t)n_steps;
+          d.f.in[0] = st.chain_in;
+          for (int k = 0; k < 3; ++k) d.f.in[k + 1] = st.operands[k];
+          for (uint32_t s = 0; s < n_steps; ++s) {
+            const gpuos_op& os = c->staged[i + s].op;
+            d.f.step_op[s] = codes[s];
+            d.f.fscal[s] = os.alpha;
+            // keep the store unless the op is transient and nothing queued
+            // after the chain reads its output
+            bool keep = !(os.flags & GPUOS_FLAG_TRANSIENT);
+            if (!keep) {
+              const Range w{(uint64_t)os.out, (uint64_t)os.out + bytes};
+              for (size_t k = j; k < c->staged.size() && !keep; ++k) {
+                const OpRanges R = op_ranges(c->staged[k].op);
+                for (int q = 0; q < R.nr; ++q)
+                  if (overlaps(R.r[q], w)) keep = true;
+              }
+            }
+            d.f.out[s] = keep ? (uint64_t)os.out : 0;
+            d.f.step_fl[s] = (uint8_t)(fls[s] | (keep ? FSF_STORE : 0));
+          }
+          d.user_ops = n_steps;
+          set_tiling(cfg, c->workers, d);
+          pl.count = n_steps;
+          c->st.ops_fused += n_steps - 1;
+        }
+      }
+    }
+    if (pl.count == 1) {
+      encode_plain(s0.op, cfg, c->workers, pl.desc);
+      j = i + 1;
+    }
+    // dependencies: union of the members' deps that point outside the group
+    const uint64_t gfirst = c->staged[i].id, glast = c->staged[i + pl.count - 1].id;
+    for (uint32_t k = 0; k < pl.count; ++k)
+      for (uint64_t dep : c->staged[i + k].deps)
+        if (dep < gfirst || dep > glast) pl.deps.push_back(dep);
+    std::sort(pl.deps.begin(), pl.deps.end());
+    pl.deps.erase(std::unique(pl.deps.begin(), pl.deps.end()), pl.deps.end());
+    plan.push_back(std::move(pl));
+    i = i + plan.back().count;
+  }
+}
+
+// Waits until ring slot for `seq` is free; returns 0, EAGAIN or EDEVICE.
+int wait_ring_space(gpuos_ctx* c, uint32_t ring, uint64_t seq) {
+  if (seq <= (uint64_t)c->cap || seq - c->cap <= completed_of(c, ring)) return 0;
+  if (c->host_only || c->cfg.block_on_full == 2)
+    return fail(GPUOS_EAGAIN, "ring %u full (%u slots)", ring, c->cap);
+  ++c->st.ring_full_waits;
+  // make what is already written visible so the device can drain it
+  if (c->tail_written[ring] != c->pub_seq[ring]) {
+    store_rel(&c->hctl->tail[ring], c->pub_seq[ring]);
+    c->tail_written[ring] = c->pub_seq[ring];
+  }
+  uint32_t spins = 0;
+  while (seq - c->cap > completed_of(c, ring)) {
+    if (check_device_error(c)) return GPUOS_EDEVICE;
+    if (++spins > 256) {
+      std::this_thread::yield();
+      if ((spins & 0xffff) == 0 && hipStreamQuery(c->stream) != hipErrorNotReady) {
+        c->poisoned = true;
+        return fail(GPUOS_EDEVICE, "resident kernel is no longer running");
+      }
+    } else {
+      cpu_relax();
+    }
+  }
+  return 0;
+}
+
+void publish_tail(gpuos_ctx* c, uint32_t ring) {
+  if (c->tail_written[ring] == c->pub_seq[ring]) return;
+  std::atomic_thread_fence(std::memory_order_release);
+  store_rel(&c->hctl->tail[ring], c->pub_seq[ring]);
+  c->tail_written[ring] = c->pub_seq[ring];
+}
+
+// Writes one planned descriptor into its ring and records the id -> seq map.
+int publish_one(gpuos_ctx* c, Planned& pl) {
+  const uint32_t ring = pl.ring;
+  const uint64_t seq = c->pub_seq[ring] + 1;
+  int rc = wait_ring_space(c, ring, seq);
+  if (rc) return rc;
+  DevDesc& d = pl.desc;
+  d.seq = seq;
+  d.check = (uint32_t)seq ^ kDescMagic;
+  d.tstart = c->pub_tiles[ring];
+  // dependencies -> sequences of the same ring; drop completed ones
+  std::vector<uint64_t> dseq;
+  for (uint64_t dep : pl.deps) {
+    if (id_retired(c, dep)) continue;
+    const uint64_t v = c->idseq[dep - c->id_base];
+    const uint32_t dring = (uint32_t)(v >> 63);
+    const uint64_t s = v & ((1ull << 63) - 1);
+    if (dring != ring) {
+      // a dependency across rings is honoured on the host: wait for it
+      publish_tail(c, dring);
+      publish_tail(c, ring);
+      while (s > completed_of(c, dring)) {
+        if (check_device_error(c)) return GPUOS_EDEVICE;
+        if (c->host_only) return fail(GPUOS_EAGAIN, "cross-ring dependency pending");
+        std::this_thread::yield();
+      }
+      continue;
+    }
+    dseq.push_back(s);
+  }
+  std::sort(dseq.begin(), dseq.end());
+  dseq.erase(std::unique(dseq.begin(), dseq.end()), dseq.end());
+  if (dseq.size() <= 4) {
+    for (size_t k = 0; k < dseq.size(); ++k) d.deps[k] = dseq[k];
+  } else {
+    d.wait_retired = dseq.back();  // retire order covers every dependency
+  }
+  DevDesc* slot = &c->hdesc[ring][(seq - 1) & (c->cap - 1)];
+  memcpy(slot, &d, sizeof d);
+  c->hends[ring][(seq - 1) & (c->cap - 1)] = c->pub_tiles[ring] + d.ntiles;
+  c->pub_tiles[ring] += d.ntiles;
+  c->pub_seq[ring] = seq;
+  for (uint32_t k = 0; k < pl.count; ++k) {
+    const uint64_t id = c->staged[pl.first + k].id;
+    c->idseq[id - c->id_base] = ((uint64_t)ring << 63) | seq;
+  }
+  ++c->st.descs_published;
+  if ((seq & 63) == 0) publish_tail(c, ring);
+  return 0;
+}
+
+int flush_impl(gpuos_ctx* c) {
+  if (check_device_error(c)) return GPUOS_EDEVICE;
+  if (c->staged.empty()) return 0;
+  ++c->st.flushes;
+  std::vector<Planned> plan;
+  plan_ops(c, 0, c->staged.size(), plan);
+  size_t done_ops = 0;
+  int rc = 0;
+  for (Planned& pl : plan) {
+    rc = publish_one(c, pl);
+    if (rc) break;
+    done_ops += pl.count;
+  }
+  publish_tail(c, 0);
+  publish_tail(c, 1);
+  c->staged.erase(c->staged.begin(), c->staged.begin() + done_ops);
+  return rc;
+}
+
+int alloc_host(gpuos_ctx* c, void** p, size_t bytes) {
+  if (c->host_only) {
+    *p = aligned_alloc(256, (bytes + 255) / 256 * 256);
+    if (!*p) return fail(GPUOS_ENOMEM, "host allocation of %zu bytes failed", bytes);
+    memset(*p, 0, bytes);
+    return 0;
+  }
+  hipError_t e = hipHostMalloc(p, bytes, hipHostMallocCoherent | hipHostMallocMapped);
+  if (e != hipSuccess) return fail(GPUOS_ENOMEM, "hipHostMalloc(%zu): %s", bytes, hipGetErrorString(e));
+  memset(*p, 0, bytes);
+  return 0;
+}
+
+void free_host(gpuos_ctx* c, void* p) {
+  if (!p) return;
+  if (c->host_only)
+    free(p);
+  else
+    (void)hipHostFree(p);
+}
+
+void free_all(gpuos_ctx* c) {
+  free_host(c, c->hctl);
+  for (int r = 0; r < kRings; ++r) {
+    free_host(c, c->hdesc[r]);
+    free_host(c, c->hends[r]);
+  }
+  if (!c->host_only) {
+    (void)hipFree(c->dctl);
+    for (int r = 0; r < kRings; ++r) {
+      (void)hipFree(c->dends[r]);
+      (void)hipFree(c->done_id[r]);
+      (void)hipFree(c->tiles_done[r]);
+      (void)hipFree(c->trace[r]);
+    }
+    if (c->ev_start) (void)hipEventDestroy(c->ev_start);
+    if (c->ev_end) (void)hipEventDestroy(c->ev_end);
+    if (c->stream) (void)hipStreamDestroy(c->stream);
+  }
+}
+
+void* dev_ptr(void* host) {
+  void* d = nullptr;
+  if (hipHostGetDevicePointer(&d, host, 0) != hipSuccess) return host;
+  return d;
+}
+
+int apply_config(const gpuos_config* in, gpuos_config& out) {
+  gpuos_config_default(&out);
+  if (!in) return 0;
+  if (in->ring_slots) out.ring_slots = in->ring_slots;
+  if (in->waves_per_cu) out.waves_per_cu = in->waves_per_cu;
+  if (in->tile_elems) out.tile_elems = in->tile_elems;
+  if (in->be_tile_elems) out.be_tile_elems = in->be_tile_elems;
+  if (in->fusion) out.fusion = in->fusion;
+  if (in->auto_deps) out.auto_deps = in->auto_deps;
+  if (in->trace) out.trace = in->trace;
+  if (in->block_on_full) out.block_on_full = in->block_on_full;
+  if (in->max_fuse) out.max_fuse = in->max_fuse;
+  const uint32_t rs = out.ring_slots;
+  if (rs < 64 || rs > (1u << 18) || (rs & (rs - 1)))
+    return fail(GPUOS_EINVAL, "ring_slots must be a power of two in [64, 2^18]");
+  if (out.waves_per_cu < 4 || out.waves_per_cu > 32 || out.waves_per_cu % 4)
+    return fail(GPUOS_EINVAL, "waves_per_cu must be a multiple of 4 in [4, 32]");
+  if (out.tile_elems < 256 || out.tile_elems % 256 || out.tile_elems > (1u << 22))
+    return fail(GPUOS_EINVAL, "tile_elems must be a multiple of 256 in [256, 2^22]");
+  if (out.be_tile_elems < 256 || out.be_tile_elems % 256 || out.be_tile_elems > (1u << 22))
+    return fail(GPUOS_EINVAL, "be_tile_elems must be a multiple of 256 in [256, 2^22]");
+  if (out.fusion > 2 || out.auto_deps > 2 || out.trace > 2 || out.block_on_full > 2)
+    return fail(GPUOS_EINVAL, "switch fields take 1 (on) or 2 (off)");
+  if (out.max_fuse < 2 || out.max_fuse > (uint32_t)kMaxSteps)
+    return fail(GPUOS_EINVAL, "max_fuse must be in [2, 8]");
+  return 0;
+}
+
+int sync_impl(gpuos_ctx* c, uint64_t upto, int64_t timeout_ns) {
+  uint64_t target[kRings] = {c->pub_seq[0], c->pub_seq[1]};
+  if (upto) {
+    if (upto >= c->next_id) return fail(GPUOS_EINVAL, "sync: id %llu was never submitted",
+                                        (unsigned long long)upto);
+    target[0] = target[1] = 0;
+    bool found[kRings] = {false, false};
+    for (uint64_t id = upto; id >= c->id_base && !(found[0] && found[1]); --id) {
+      const uint64_t v = c->idseq[id - c->id_base];
+      const uint32_t r = (uint32_t)(v >> 63);
+      if (!found[r]) {
+        target[r] = v & ((1ull << 63) - 1);
+        found[r] = true;
+      }
+      if (id == c->id_base) break;
+    }
+  }
+  const auto t0 = std::chrono::steady_clock::now();
+  uint32_t spins = 0;
+  for (int r = 0; r < kRings; ++r) {
+    while (completed_of(c, r) < target[r]) {
+      if (check_device_error(c)) return GPUOS_EDEVICE;
+      if (c->host_only) return fail(GPUOS_ETIMEDOUT, "host-only context: ops never complete");
+      ++spins;
+      if (spins < 2048) {
+        cpu_relax();
+        continue;
+      }
+      if ((spins & 1023) == 0) {
+        if (timeout_ns >= 0) {
+          const auto el = std::chrono::duration_cast<std::chrono::nanoseconds>(
+                              std::chrono::steady_clock::now() - t0)
+                              .count();
+          if (el > timeout_ns)
+            return fail(GPUOS_ETIMEDOUT, "sync timed out: ring %d at %llu of %llu", r,
+                        (unsigned long long)completed_of(c, r), (unsigned long long)target[r]);
+        }
+        if (hipStreamQuery(c->stream) != hipErrorNotReady) {
+          c->poisoned = true;
+          return fail(GPUOS_EDEVICE, "resident kernel is no longer running");
+        }
+      }
+      std::this_thread::yield();
+    }
+  }
+  if (check_device_error(c)) return GPUOS_EDEVICE;
+  prune_ids(c);
+  return 0;
+}
+
+}  // namespace
+
+// ===========================================================================
+// C ABI
+
+extern "C" {
+
+int gpuos_abi_version(void) { return GPUOS_ABI_VERSION; }
+
+const char* gpuos_last_error(void) { return g_last_error.c_str(); }
+
+void gpuos_config_default(gpuos_config* cfg) {
+  if (!cfg) return;
+  memset(cfg, 0, sizeof *cfg);
+  cfg->ring_slots = 65536;
+  cfg->waves_per_cu = 8;
+  cfg->tile_elems = 4096;
+  cfg->be_tile_elems = 16384;
+  cfg->fusion = 1;
+  cfg->auto_deps = 1;
+  cfg->trace = 2;
+  cfg->block_on_full = 1;
+  cfg->max_fuse = 8;
+}
+
+int gpuos_create(int device, const gpuos_config* cfg_in, gpuos_ctx** out) {
+  if (!out) return fail(GPUOS_EINVAL, "out is null");
+  *out = nullptr;
+  gpuos_config cfg;
+  int rc = apply_config(cfg_in, cfg);
+  if (rc) return rc;
+  auto* c = new gpuos_ctx();
+  c->cfg = cfg;
+  c->cap = cfg.ring_slots;
+  c->device = device;
+  c->host_only = device == GPUOS_DEVICE_NONE;
+  if (!c->host_only) {
+    int ndev = 0;
+    if (hipGetDeviceCount(&ndev) != hipSuccess || device < 0 || device >= ndev) {
+      delete c;
+      return fail(GPUOS_EINVAL, "no HIP device %d (%d visible)", device, ndev);
+    }
+    hipError_t e = hipSetDevice(device);
+    hipDeviceProp_t prop;
+    if (e == hipSuccess) e = hipGetDeviceProperties(&prop, device);
+    if (e != hipSuccess) {
+      delete c;
+      return fail(GPUOS_EDEVICE, "device %d: %s", device, hipGetErrorString(e));
+    }
+    c->cus = (uint32_t)prop.multiProcessorCount;
+    int nb = 0;
+    e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&nb, resident_kernel(), 256, 0);
+    if (e != hipSuccess || nb <= 0) {
+      delete c;
+      return fail(GPUOS_EDEVICE, "occupancy query failed: %s", hipGetErrorString(e));
+    }
+    uint32_t bpc = cfg.waves_per_cu / 4;
+    if (bpc > (uint32_t)nb) {
+      delete c;
+      return fail(GPUOS_EINVAL, "waves_per_cu %u exceeds the kernel's occupancy (%d blocks of 4 waves)",
+                  cfg.waves_per_cu, nb);
+    }
+    c->blocks = c->cus * bpc;
+  } else {
+    c->cus = 256;
+    c->blocks = c->cus * (cfg.waves_per_cu / 4);
+  }
+  c->workers = c->blocks * 4 - 1;
+  c->st.worker_waves = c->workers;
+  c->st.compute_units = c->cus;
+
+  rc = alloc_host(c, (void**)&c->hctl, sizeof(HostCtl));
+  for (int r = 0; r < kRings && !rc; ++r) {
+    rc = alloc_host(c, (void**)&c->hdesc[r], (size_t)c->cap * sizeof(DevDesc));
+    if (!rc) rc = alloc_host(c, (void**)&c->hends[r], (size_t)c->cap * sizeof(uint64_t));
+  }
+  if (rc) {
+    free_all(c);
+    delete c;
+    return rc;
+  }
+  if (!c->host_only) {
+    auto dalloc = [&](void** p, size_t bytes) -> int {
+      hipError_t e = hipMalloc(p, bytes);
+      if (e != hipSuccess) return fail(GPUOS_ENOMEM, "hipMalloc(%zu): %s", bytes, hipGetErrorString(e));
+      return 0;
+    };
+    rc = dalloc((void**)&c->dctl, sizeof(DevCtl));
+    for (int r = 0; r < kRings && !rc; ++r) {
+      rc = dalloc((void**)&c->dends[r], (size_t)2 * c->cap * sizeof(uint64_t));
+      if (!rc) rc = dalloc((void**)&c->done_id[r], (size_t)c->cap * sizeof(uint64_t));
+      if (!rc) rc = dalloc((void**)&c->tiles_done[r], (size_t)c->cap * sizeof(uint32_t));
+      if (!rc && cfg.trace == 1) rc = dalloc((void**)&c->trace[r], (size_t)c->cap * sizeof(TraceRec));
+    }
+    hipError_t e = hipSuccess;
+    if (!rc) e = hipStreamCreateWithFlags(&c->stream, hipStreamNonBlocking);
+    if (!rc && e == hipSuccess) {
+      e = hipMemsetAsync(c->dctl, 0, sizeof(DevCtl), c->stream);
+      for (int r = 0; r < kRings && e == hipSuccess; ++r) {
+        e = hipMemsetAsync(c->dends[r], 0, (size_t)2 * c->cap * sizeof(uint64_t), c->stream);
+        if (e == hipSuccess) e = hipMemsetAsync(c->done_id[r], 0, (size_t)c->cap * 8, c->stream);
+        if (e == hipSuccess) e = hipMemsetAsync(c->tiles_done[r], 0, (size_t)c->cap * 4, c->stream);
+        if (e == hipSuccess && c->trace[r])
+          e = hipMemsetAsync(c->trace[r], 0, (size_t)c->cap * sizeof(TraceRec), c->stream);
+      }
+    }
+    if (!rc && e == hipSuccess) {
+      KArgs a{};
+      for (int r = 0; r < kRings; ++r) {
+        a.hdesc[r] = (const DevDesc*)dev_ptr(c->hdesc[r]);
+        a.hends[r] = (const uint64_t*)dev_ptr(c->hends[r]);
+        a.dends[r] = c->dends[r];
+        a.done_id[r] = c->done_id[r];
+        a.tiles_done[r] = c->tiles_done[r];
+        a.trace[r] = c->trace[r];
+      }
+      a.hctl = (HostCtl*)dev_ptr(c->hctl);
+      a.dctl = c->dctl;
+      a.cap_mask = c->cap - 1;
+      a.ends_mask = 2 * c->cap - 1;
+      a.workers = c->workers;
+      a.lc_enabled = 1;
+      e = hipEventCreate(&c->ev_start);
+      if (e == hipSuccess) e = hipEventCreate(&c->ev_end);
+      if (e == hipSuccess) e = hipEventRecord(c->ev_start, c->stream);
+      if (e == hipSuccess) e = launch_resident(a, c->blocks, c->stream);
+    }
+    if (!rc && e != hipSuccess) rc = fail(GPUOS_EDEVICE, "create: %s", hipGetErrorString(e));
+    if (rc) {
+      if (c->stream) (void)hipStreamSynchronize(c->stream);
+      free_all(c);
+      delete c;
+      return rc;
+    }
+  }
+  *out = c;
+  return 0;
+}
+
+int gpuos_submit(gpuos_ctx* c, const gpuos_op* ops, uint32_t n, uint64_t* ids_out) {
+  if (!c) return fail(GPUOS_EINVAL, "null context");
+  if (c->stopped) return fail(GPUOS_ESTATE, "context is stopped");
+  if (check_device_error(c)) return fail(GPUOS_ESTATE, "context is poisoned: %s", g_last_error.c_str());
+  if (n && !ops) return fail(GPUOS_EINVAL, "ops is null");
+  const uint64_t first = c->next_id;
+  // validate everything before staging anything
+  for (uint32_t i = 0; i < n; ++i) {
+    int rc = validate(ops[i], i);
+    if (rc) return rc;
+    for (int k = 0; k < 4; ++k) {
+      const int64_t dv = ops[i].deps[k];
+      if (dv > 0 && (uint64_t)dv >= first + i)
+        return fail(GPUOS_EINVAL, "op %u: dependency on id %lld, not yet submitted", i, (long long)dv);
+      if (dv < 0 && (uint64_t)(-dv) > i)
+        return fail(GPUOS_EINVAL, "op %u: relative dependency %lld points before this call", i,
+                    (long long)dv);
+    }
+    // explicit dependencies must stay in the op's ring
+    const uint32_t ring = (ops[i].flags & GPUOS_FLAG_LC) ? 1 : 0;
+    for (int k = 0; k < 4; ++k) {
+      const int64_t dv = ops[i].deps[k];
+      if (dv < 0) {
+        const uint32_t r2 = (ops[i + dv].flags & GPUOS_FLAG_LC) ? 1 : 0;
+        if (r2 != ring) return fail(GPUOS_EINVAL, "op %u: explicit dependency across priority rings", i);
+      } else if (dv > 0 && !id_retired(c, (uint64_t)dv)) {
+        bool known = false;
+        const uint32_t r2 = ring_of_id(c, (uint64_t)dv, &known);
+        if (known && r2 != ring)
+          return fail(GPUOS_EINVAL, "op %u: explicit dependency across priority rings", i);
+      }
+    }
+  }
+  auto retired = [c](uint64_t id) { return id_retired(c, id); };
+  for (uint32_t i = 0; i < n; ++i) {
+    Staged s;
+    s.op = ops[i];
+    s.id = c->next_id++;
+    s.ring = (ops[i].flags & GPUOS_FLAG_LC) ? 1 : 0;
+    for (int k = 0; k < 4; ++k) {
+      const int64_t dv = ops[i].deps[k];
+      if (dv > 0) {
+        if (!id_retired(c, (uint64_t)dv)) s.deps.push_back((uint64_t)dv);
+        ++c->st.deps_explicit;
+      } else if (dv < 0) {
+        s.deps.push_back(s.id - (uint64_t)(-dv));
+        ++c->st.deps_explicit;
+      }
+    }
+    if (c->cfg.auto_deps == 1) {
+      const size_t before = s.deps.size();
+      const OpRanges R = op_ranges(ops[i]);
+      for (int q = 0; q < R.nr; ++q) c->hazards.access(R.r[q], s.id, false, s.deps, retired);
+      c->hazards.access(R.w, s.id, true, s.deps, retired);
+      // reads recorded above also list this op as a reader of its own output
+      // range when it runs in place; drop self-dependencies
+      s.deps.erase(std::remove(s.deps.begin(), s.deps.end(), s.id), s.deps.end());
+      c->st.deps_auto += s.deps.size() - before;
+    }
+    std::sort(s.deps.begin(), s.deps.end());
+    s.deps.erase(std::unique(s.deps.begin(), s.deps.end()), s.deps.end());
+    c->idseq.push_back(0);
+    if (ids_out) ids_out[i] = s.id;
+    c->staged.push_back(std::move(s));
+  }
+  c->st.ops_submitted += n;
+  if ((c->since_prune += n) >= 4096) {
+    c->since_prune = 0;
+    prune_ids(c);
+    c->hazards.prune(retired);
+  }
+  return 0;
+}
+
+int gpuos_flush(gpuos_ctx* c) {
+  if (!c) return fail(GPUOS_EINVAL, "null context");
+  if (c->stopped) return fail(GPUOS_ESTATE, "context is stopped");
+  return flush_impl(c);
+}
+
+int gpuos_sync(gpuos_ctx* c, uint64_t upto, int64_t timeout_ns) {
+  if (!c) return fail(GPUOS_EINVAL, "null context");
+  if (c->exited) return check_device_error(c) ? GPUOS_EDEVICE : 0;
+  int rc = flush_impl(c);
+  if (rc) return rc;
+  if (!c->staged.empty()) return fail(GPUOS_EAGAIN, "sync: ops still staged");
+  return sync_impl(c, upto, timeout_ns);
+}
+
+int gpuos_query(gpuos_ctx* c, uint64_t id) {
+  if (!c) return fail(GPUOS_EINVAL, "null context");
+  if (id == 0 || id >= c->next_id) return fail(GPUOS_EINVAL, "query: unknown id");
+  if (check_device_error(c)) return GPUOS_EDEVICE;
+  return id_retired(c, id) ? 1 : 0;
+}
+
+int gpuos_get_stats(gpuos_ctx* c, gpuos_stats* out) {
+  if (!c || !out) return fail(GPUOS_EINVAL, "null argument");
+  c->st.descs_completed = completed_of(c, 0) + completed_of(c, 1);
+  c->st.device_error = c->hctl->error;
+  c->st.error_desc = c->hctl->error_seq;
+  *out = c->st;
+  return 0;
+}
+
+int gpuos_trace_read(gpuos_ctx* c, gpuos_trace_rec* out, uint32_t max, uint32_t* n_out) {
+  if (!c || !n_out) return fail(GPUOS_EINVAL, "null argument");
+  *n_out = 0;
+  if (c->cfg.trace != 1 || c->host_only) return fail(GPUOS_ESTATE, "tracing is off");
+  std::vector<TraceRec> tr((size_t)c->cap * kRings);
+  hipStream_t s = nullptr;
+  hipError_t e = hipStreamCreateWithFlags(&s, hipStreamNonBlocking);
+  for (int r = 0; r < kRings && e == hipSuccess; ++r)
+    e = hipMemcpyAsync(tr.data() + (size_t)r * c->cap, c->trace[r], (size_t)c->cap * sizeof(TraceRec),
+                       hipMemcpyDeviceToHost, s);
+  if (e == hipSuccess) e = hipStreamSynchronize(s);
+  if (s) (void)hipStreamDestroy(s);
+  if (e != hipSuccess) return fail(GPUOS_EDEVICE, "trace copy: %s", hipGetErrorString(e));
+  std::vector<gpuos_trace_rec> recs;
+  for (int r = 0; r < kRings; ++r) {
+    const uint64_t done = completed_of(c, r);
+    const uint64_t lo = done > c->cap ? done - c->cap + 1 : 1;
+    for (uint64_t sq = lo; sq <= done; ++sq) {
+      const TraceRec& t = tr[(size_t)r * c->cap + ((sq - 1) & (c->cap - 1))];
+      if (t.seq != sq) continue;
+      gpuos_trace_rec o;
+      o.seq = sq;
+      o.t_claim = t.t_claim;
+      o.t_done = t.t_done;
+      o.opcode = t.opcode;
+      o.ntiles = t.ntiles;
+      o.ring = (uint32_t)r;
+      o.first_ops = c->hdesc[r][(sq - 1) & (c->cap - 1)].seq == sq
+                        ? c->hdesc[r][(sq - 1) & (c->cap - 1)].user_ops
+                        : 0;
+      recs.push_back(o);
+    }
+  }
+  const size_t k = std::min<size_t>(recs.size(), max);
+  if (out) memcpy(out, recs.data() + (recs.size() - k), k * sizeof(gpuos_trace_rec));
+  *n_out = (uint32_t)k;
+  return 0;
+}
+
+int gpuos_stop(gpuos_ctx* c, int64_t timeout_ns) {
+  if (!c) return fail(GPUOS_EINVAL, "null context");
+  if (c->host_only || c->exited) return 0;
+  if (c->leaked) return fail(GPUOS_ETIMEDOUT, "resident kernel did not exit");
+  int rc = 0;
+  if (!c->stopped) {
+    if (!c->poisoned) {
+      int r2 = flush_impl(c);
+      if (!r2) r2 = sync_impl(c, 0, timeout_ns);
+      if (r2) rc = r2;
+    }
+    c->staged.clear();
+    c->stopped = true;
+    // STOP: one tile per worker wave; each wave that claims one exits
+    const uint64_t seq = c->pub_seq[0] + 1;
+    const auto t0 = std::chrono::steady_clock::now();
+    while (seq > c->cap && seq - c->cap > completed_of(c, 0)) {
+      // only reachable after a timed-out drain: wait, bounded, for a slot
+      std::this_thread::yield();
+      if (timeout_ns >= 0 &&
+          std::chrono::steady_clock::now() - t0 > std::chrono::nanoseconds(timeout_ns)) {
+        c->leaked = true;
+        return fail(GPUOS_ETIMEDOUT, "ring never drained; resident kernel left running");
+      }
+    }
+    DevDesc d;
+    memset(&d, 0, sizeof d);
+    d.opcode = OP_STOP;
+    d.ntiles = c->workers;
+    d.tile = 1;
+    d.seq = seq;
+    d.check = (uint32_t)seq ^ kDescMagic;
+    d.tstart = c->pub_tiles[0];
+    memcpy(&c->hdesc[0][(seq - 1) & (c->cap - 1)], &d, sizeof d);
+    c->hends[0][(seq - 1) & (c->cap - 1)] = c->pub_tiles[0] + d.ntiles;
+    c->pub_tiles[0] += d.ntiles;
+    c->pub_seq[0] = seq;
+    std::atomic_thread_fence(std::memory_order_release);
+    store_rel(&c->hctl->stop_seq, seq);
+    publish_tail(c, 0);
+  }
+  // wait for the kernel to exit
+  const auto t0 = std::chrono::steady_clock::now();
+  for (;;) {
+    hipError_t e = hipStreamQuery(c->stream);
+    if (e == hipSuccess) break;
+    if (e != hipErrorNotReady) {
+      c->exited = true;
+      c->poisoned = true;
+      return fail(GPUOS_EDEVICE, "resident kernel failed: %s", hipGetErrorString(e));
+    }
+    if (timeout_ns >= 0 &&
+        std::chrono::steady_clock::now() - t0 > std::chrono::nanoseconds(timeout_ns)) {
+      c->leaked = true;
+      return fail(GPUOS_ETIMEDOUT, "resident kernel did not exit");
+    }
+    std::this_thread::sleep_for(std::chrono::microseconds(20));
+  }
+  c->exited = true;
+  if (c->ev_end && hipEventRecord(c->ev_end, c->stream) == hipSuccess &&
+      hipEventSynchronize(c->ev_end) == hipSuccess) {
+    float ms = 0.0f;
+    if (hipEventElapsedTime(&ms, c->ev_start, c->ev_end) == hipSuccess)
+      c->st.kernel_ns = (uint64_t)((double)ms * 1e6);
+  }
+  if (check_device_error(c)) return GPUOS_EDEVICE;
+  return rc;
+}
+
+int gpuos_destroy(gpuos_ctx* c, int64_t timeout_ns) {
+  if (!c) return fail(GPUOS_EINVAL, "null context");
+  int rc = 0;
+  if (!c->host_only) {
+    rc = gpuos_stop(c, timeout_ns);
+    if (c->leaked) {
+      // never free memory a running kernel may still touch
+      rc = fail(GPUOS_ETIMEDOUT, "resident kernel did not exit; its memory is leaked");
+      delete c;
+      return rc;
+    }
+  }
+  free_all(c);
+  delete c;
+  return rc;
+}
+
+// ---------------------------------------------------------------------------
+// per-op launch comparator
+
+int gpuos_baseline_run(int device, const gpuos_op* ops, uint32_t n, int fuse, void* stream) {
+  if (n && !ops) return fail(GPUOS_EINVAL, "ops is null");
+  for (uint32_t i = 0; i < n; ++i) {
+    int rc = validate(ops[i], i);
+    if (rc) return rc;
+  }
+  static thread_local int cached_dev = -2;
+  static thread_local uint32_t cached_cus = 0;
+  if (cached_dev != device) {
+    hipDeviceProp_t prop;
+    HIP_TRY(hipGetDeviceProperties(&prop, device));
+    cached_cus = (uint32_t)prop.multiProcessorCount;
+    cached_dev = device;
+  }
+  HIP_TRY(hipSetDevice(device));
+  gpuos_ctx tmp;  // host-side planning state only
+  tmp.host_only = true;
+  gpuos_config_default(&tmp.cfg);
+  tmp.cfg.fusion = fuse ? 1 : 2;
+  tmp.workers = cached_cus * 8;
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  if (!fuse) {
+    DevDesc d;
+    for (uint32_t i = 0; i < n; ++i) {
+      encode_plain(ops[i], tmp.cfg, tmp.workers, d);
+      if (ops[i].opcode == GPUOS_OP_NOP) continue;
+      HIP_TRY(launch_single(d, nullptr, s));
+    }
+    return 0;
+  }
+  tmp.staged.reserve(n);
+  for (uint32_t i = 0; i < n; ++i) {
+    Staged st;
+    st.op = ops[i];
+    st.id = i + 1;
+    st.ring = 0;
+    tmp.staged.push_back(std::move(st));
+  }
+  std::vector<Planned> plan;
+  plan_ops(&tmp, 0, tmp.staged.size(), plan);
+  for (Planned& pl : plan) {
+    if (pl.desc.opcode == GPUOS_OP_NOP) continue;
+    HIP_TRY(launch_single(pl.desc, nullptr, s));
+  }
+  return 0;
+}
+
+// ---------------------------------------------------------------------------
+// debug hooks
+
+int gpuos_debug_read_desc(gpuos_ctx* c, int ring, uint64_t seq, void* out) {
+  if (!c || !out || ring < 0 || ring >= kRings) return fail(GPUOS_EINVAL, "bad argument");
+  if (seq == 0 || seq > c->pub_seq[ring] || (c->pub_seq[ring] >= c->cap && seq <= c->pub_seq[ring] - c->cap))
+    return fail(GPUOS_EINVAL, "sequence %llu not in the ring", (unsigned long long)seq);
+  memcpy(out, &c->hdesc[ring][(seq - 1) & (c->cap - 1)], sizeof(DevDesc));
+  return 0;
+}
+
+uint64_t gpuos_debug_published(gpuos_ctx* c, int ring) {
+  if (!c || ring < 0 || ring >= kRings) return 0;
+  return c->pub_seq[ring];
+}
+
+int gpuos_debug_seq_of(gpuos_ctx* c, uint64_t id, int* ring_out, uint64_t* seq_out) {
+  if (!c || !ring_out || !seq_out) return fail(GPUOS_EINVAL, "bad argument");
+  if (id == 0 || id >= c->next_id || id < c->id_base) return fail(GPUOS_EINVAL, "unknown id");
+  const uint64_t v = c->idseq[id - c->id_base];
+  if (!v) return fail(GPUOS_EAGAIN, "id still staged");
+  *ring_out = (int)(v >> 63);
+  *seq_out = v & ((1ull << 63) - 1);
+  return 0;
+}
+
+int gpuos_debug_retire(gpuos_ctx* c, int ring, uint64_t upto) {
+  if (!c || ring < 0 || ring >= kRings) return fail(GPUOS_EINVAL, "bad argument");
+  if (!c->host_only) return fail(GPUOS_ESTATE, "only host-only contexts are retired by hand");
+  if (upto > c->pub_seq[ring]) return fail(GPUOS_EINVAL, "beyond the last published sequence");
+  if (upto > c->hctl->completed[ring]) store_rel(&c->hctl->completed[ring], upto);
+  return 0;
+}
+
+}  // extern "C"

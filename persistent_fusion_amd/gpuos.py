@@ -1,0 +1,288 @@
+"""ctypes binding of the gpuos C ABI (``include/gpuos.h``).
+
+Argument marshalling only: every op runs in the HIP kernels of ``libgpuos.so``.
+Device buffers come from the caller (typically torch tensors, passed by
+``data_ptr()``); torch does no compute on this path.  Importing this module
+fails loudly when the native library has not been built.
+"""
+
+from __future__ import annotations
+
+import ctypes as C
+import os
+from typing import Callable, Dict, Iterable, List, Optional, Sequence
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libgpuos.so")
+
+# status codes
+OK, EINVAL, ENOMEM, EAGAIN, ETIMEDOUT, EDEVICE, ESTATE = 0, -1, -2, -3, -4, -5, -6
+STATUS_NAMES = {0: "OK", -1: "EINVAL", -2: "ENOMEM", -3: "EAGAIN", -4: "ETIMEDOUT",
+                -5: "EDEVICE", -6: "ESTATE"}
+
+OPCODES = {
+    "nop": 0, "copy": 1, "gather": 2, "add": 3, "mul": 4, "scale": 5, "relu": 6, "exp": 7,
+    "row_sum": 8, "row_softmax": 9, "rmsnorm": 10, "rope": 11, "gemv": 12,
+    "attn_score": 13, "attn_av": 14, "silu_mul": 15, "spin": 16,
+}
+DTYPES = {"f32": 0, "bf16": 1, "i32": 2}
+ELEM_BYTES = {"f32": 4, "bf16": 2, "i32": 4}
+FLAG_TRANSIENT, FLAG_LC, FLAG_NONTEMPORAL = 0x1, 0x2, 0x4
+DEVICE_NONE = -1
+
+
+class GpuosOp(C.Structure):
+    _fields_ = [
+        ("opcode", C.c_uint16), ("dtype", C.c_uint8), ("flags", C.c_uint8),
+        ("n", C.c_uint32), ("rows", C.c_uint32), ("row_len", C.c_uint32),
+        ("out", C.c_void_p), ("in_", C.c_void_p * 3), ("src_len", C.c_uint64 * 2),
+        ("alpha", C.c_float), ("beta", C.c_float), ("eps", C.c_float),
+        ("aux", C.c_int32 * 4), ("_pad", C.c_int32), ("deps", C.c_int64 * 4),
+    ]
+
+
+class GpuosConfig(C.Structure):
+    _fields_ = [(name, C.c_uint32) for name in (
+        "ring_slots", "waves_per_cu", "tile_elems", "be_tile_elems", "fusion", "auto_deps",
+        "trace", "block_on_full", "max_fuse")] + [("reserved", C.c_uint32 * 7)]
+
+
+class GpuosStats(C.Structure):
+    _fields_ = [(name, C.c_uint64) for name in (
+        "ops_submitted", "ops_fused", "descs_published", "descs_completed", "flushes",
+        "ring_full_waits", "deps_explicit", "deps_auto", "device_error", "error_desc",
+        "worker_waves", "compute_units", "kernel_ns")] + [("reserved", C.c_uint64 * 3)]
+
+
+class GpuosTraceRec(C.Structure):
+    _fields_ = [("seq", C.c_uint64), ("t_claim", C.c_uint64), ("t_done", C.c_uint64),
+                ("opcode", C.c_uint32), ("ntiles", C.c_uint32), ("ring", C.c_uint32),
+                ("first_ops", C.c_uint32)]
+
+
+assert C.sizeof(GpuosOp) == 128
+assert C.sizeof(GpuosConfig) == 64
+assert C.sizeof(GpuosStats) == 128
+assert C.sizeof(GpuosTraceRec) == 40
+
+# Every symbol declared in include/gpuos.h and include/gpuos_debug.h.
+EXPORTS = (
+    "gpuos_abi_version", "gpuos_last_error", "gpuos_config_default", "gpuos_create",
+    "gpuos_submit", "gpuos_flush", "gpuos_sync", "gpuos_query", "gpuos_get_stats",
+    "gpuos_trace_read", "gpuos_stop", "gpuos_destroy", "gpuos_baseline_run",
+    "gpuos_debug_read_desc", "gpuos_debug_published", "gpuos_debug_seq_of", "gpuos_debug_retire",
+)
+
+_lib = None
+
+
+def lib() -> C.CDLL:
+    """Loads libgpuos.so (built in-tree by ``__graft_entry__.build()``)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise RuntimeError(f"native library {LIB_PATH} is missing: run __graft_entry__.build() first")
+    L = C.CDLL(LIB_PATH)
+    P = C.c_void_p
+    sig = {
+        "gpuos_abi_version": (C.c_int, []),
+        "gpuos_last_error": (C.c_char_p, []),
+        "gpuos_config_default": (None, [C.POINTER(GpuosConfig)]),
+        "gpuos_create": (C.c_int, [C.c_int, C.POINTER(GpuosConfig), C.POINTER(P)]),
+        "gpuos_submit": (C.c_int, [P, C.POINTER(GpuosOp), C.c_uint32, C.POINTER(C.c_uint64)]),
+        "gpuos_flush": (C.c_int, [P]),
+        "gpuos_sync": (C.c_int, [P, C.c_uint64, C.c_int64]),
+        "gpuos_query": (C.c_int, [P, C.c_uint64]),
+        "gpuos_get_stats": (C.c_int, [P, C.POINTER(GpuosStats)]),
+        "gpuos_trace_read": (C.c_int, [P, C.POINTER(GpuosTraceRec), C.c_uint32, C.POINTER(C.c_uint32)]),
+        "gpuos_stop": (C.c_int, [P, C.c_int64]),
+        "gpuos_destroy": (C.c_int, [P, C.c_int64]),
+        "gpuos_baseline_run": (C.c_int, [C.c_int, C.POINTER(GpuosOp), C.c_uint32, C.c_int, P]),
+        "gpuos_debug_read_desc": (C.c_int, [P, C.c_int, C.c_uint64, P]),
+        "gpuos_debug_published": (C.c_uint64, [P, C.c_int]),
+        "gpuos_debug_seq_of": (C.c_int, [P, C.c_uint64, C.POINTER(C.c_int), C.POINTER(C.c_uint64)]),
+        "gpuos_debug_retire": (C.c_int, [P, C.c_int, C.c_uint64]),
+    }
+    for name, (res, args) in sig.items():
+        fn = getattr(L, name)
+        fn.restype = res
+        fn.argtypes = args
+    _lib = L
+    return L
+
+
+class GpuosError(RuntimeError):
+    def __init__(self, status: int, where: str):
+        msg = lib().gpuos_last_error().decode(errors="replace")
+        super().__init__(f"{where}: {STATUS_NAMES.get(status, status)}: {msg}")
+        self.status = status
+
+
+def _check(rc: int, where: str) -> int:
+    if rc < 0:
+        raise GpuosError(rc, where)
+    return rc
+
+
+def config(**kw) -> GpuosConfig:
+    cfg = GpuosConfig()
+    lib().gpuos_config_default(C.byref(cfg))
+    for k, v in kw.items():
+        if not hasattr(cfg, k):
+            raise TypeError(f"unknown config field {k}")
+        setattr(cfg, k, int(v))
+    return cfg
+
+
+def make_op(kind: str, out: int, ins: Sequence[int] = (), aux: int = 0, n: int = 0,
+            dtype: str = "f32", rows: int = 0, row_len: int = 0, src_len=(0, 0),
+            alpha: float = 0.0, eps: float = 0.0, dims: Sequence[int] = (),
+            deps: Sequence[int] = (), flags: int = 0) -> GpuosOp:
+    """Fills one gpuos_op from raw device addresses."""
+    o = GpuosOp()
+    o.opcode = OPCODES[kind]
+    o.dtype = DTYPES[dtype]
+    o.flags = flags
+    o.n, o.rows, o.row_len = n, rows, row_len
+    o.out = out or None
+    for i, p in enumerate(ins):
+        o.in_[i] = p or None
+    o.in_[2] = aux or None
+    o.src_len[0], o.src_len[1] = int(src_len[0]), int(src_len[1])
+    o.alpha, o.eps = alpha, eps
+    for i, v in enumerate(dims):
+        o.aux[i] = int(v)
+    for i, v in enumerate(deps):
+        o.deps[i] = int(v)
+    return o
+
+
+def encode_ops(ops, start: int, end: int, addr: Callable, id_of: Dict[int, int]):
+    """Encodes workload ops [start, end) as a gpuos_op array.
+
+    ``addr(ref, dtype)`` returns the device address of a workload ``Ref``;
+    ``id_of`` maps earlier op indices to the ids gpuos_submit returned.  A
+    dependency inside [start, end) becomes a relative one (negative), an
+    earlier one an absolute id.
+    """
+    arr = (GpuosOp * (end - start))()
+    for k, i in enumerate(range(start, end)):
+        op = ops[i]
+        deps = []
+        for d in op.deps:
+            deps.append(-(i - d) if d >= start else id_of[d])
+        if len(deps) > 4:
+            raise ValueError("at most 4 explicit dependencies")
+        in_dt = "f32" if op.kind == "attn_av" else op.dtype
+        aux_dt = {"rmsnorm": op.dtype, "rope": "f32", "gather": "i32"}.get(op.kind, "bf16")
+        out_dt = "f32" if op.kind == "attn_score" else op.dtype
+        flags = (FLAG_TRANSIENT if op.transient else 0) | (FLAG_LC if op.lc else 0)
+        arr[k] = make_op(op.kind, addr(op.out, out_dt), [addr(r, in_dt) for r in op.ins],
+                         addr(op.aux, aux_dt) if op.aux is not None else 0, n=op.n,
+                         dtype=op.dtype, rows=op.rows, row_len=op.row_len, src_len=op.src_len,
+                         alpha=op.alpha, eps=op.eps, dims=op.dims, deps=deps, flags=flags)
+    return arr
+
+
+class Context:
+    """One resident-kernel context (``gpuos_create`` ... ``gpuos_destroy``)."""
+
+    def __init__(self, device: int = 0, **cfg):
+        self._lib = lib()
+        self._cfg = config(**cfg)
+        h = C.c_void_p()
+        _check(self._lib.gpuos_create(device, C.byref(self._cfg), C.byref(h)), "gpuos_create")
+        self.handle = h
+        self.device = device
+
+    def submit(self, ops, n: Optional[int] = None) -> List[int]:
+        if isinstance(ops, GpuosOp):
+            ops = (GpuosOp * 1)(ops)
+        n = len(ops) if n is None else n
+        ids = (C.c_uint64 * max(n, 1))()
+        _check(self._lib.gpuos_submit(self.handle, ops, n, ids), "gpuos_submit")
+        return list(ids[:n])
+
+    def submit_noids(self, ops, n: int) -> None:
+        _check(self._lib.gpuos_submit(self.handle, ops, n, None), "gpuos_submit")
+
+    def flush(self) -> None:
+        _check(self._lib.gpuos_flush(self.handle), "gpuos_flush")
+
+    def sync(self, upto: int = 0, timeout_s: float = -1.0) -> None:
+        t = -1 if timeout_s < 0 else int(timeout_s * 1e9)
+        _check(self._lib.gpuos_sync(self.handle, upto, t), "gpuos_sync")
+
+    def query(self, op_id: int) -> bool:
+        return _check(self._lib.gpuos_query(self.handle, op_id), "gpuos_query") == 1
+
+    def stats(self) -> dict:
+        s = GpuosStats()
+        _check(self._lib.gpuos_get_stats(self.handle, C.byref(s)), "gpuos_get_stats")
+        return {name: getattr(s, name) for name, _ in GpuosStats._fields_ if name != "reserved"}
+
+    def trace(self, max_records: int = 1 << 16) -> List[dict]:
+        buf = (GpuosTraceRec * max_records)()
+        n = C.c_uint32()
+        _check(self._lib.gpuos_trace_read(self.handle, buf, max_records, C.byref(n)), "gpuos_trace_read")
+        return [{k: getattr(buf[i], k) for k, _ in GpuosTraceRec._fields_} for i in range(n.value)]
+
+    def read_desc(self, ring: int, seq: int) -> bytes:
+        out = C.create_string_buffer(256)
+        _check(self._lib.gpuos_debug_read_desc(self.handle, ring, seq, out), "gpuos_debug_read_desc")
+        return out.raw
+
+    def published(self, ring: int = 0) -> int:
+        return self._lib.gpuos_debug_published(self.handle, ring)
+
+    def seq_of(self, op_id: int):
+        r, s = C.c_int(), C.c_uint64()
+        _check(self._lib.gpuos_debug_seq_of(self.handle, op_id, C.byref(r), C.byref(s)), "gpuos_debug_seq_of")
+        return r.value, s.value
+
+    def retire(self, ring: int, upto: int) -> None:
+        _check(self._lib.gpuos_debug_retire(self.handle, ring, upto), "gpuos_debug_retire")
+
+    def stop(self, timeout_s: float = 30.0) -> None:
+        _check(self._lib.gpuos_stop(self.handle, int(timeout_s * 1e9)), "gpuos_stop")
+
+    def destroy(self, timeout_s: float = 30.0) -> None:
+        if self.handle:
+            h, self.handle = self.handle, None
+            _check(self._lib.gpuos_destroy(h, int(timeout_s * 1e9)), "gpuos_destroy")
+
+    def __enter__(self):
+        return self
+
+    def __exit__(self, *exc):
+        self.destroy()
+        return False
+
+
+def baseline_run(device: int, ops, n: Optional[int] = None, fuse: bool = False,
+                 stream: int = 0) -> None:
+    """One kernel launch per op (or per fused chain) on `stream` (0 = default)."""
+    n = len(ops) if n is None else n
+    _check(lib().gpuos_baseline_run(device, ops, n, 1 if fuse else 0, stream or None),
+           "gpuos_baseline_run")
+
+
+def decode_desc(raw: bytes) -> dict:
+    """Splits a 256-byte device descriptor into named fields (debug/tests)."""
+    import struct
+    w = struct.unpack("<64I", raw)
+    q = lambda i: w[i] | (w[i + 1] << 32)
+    d = {
+        "opcode": w[0] & 0xFF, "dtype": (w[0] >> 8) & 0xFF, "flags": (w[0] >> 16) & 0xFF,
+        "nsteps": w[0] >> 24, "n": w[1], "rows": w[2], "row_len": w[3], "seq": q(4),
+        "ntiles": w[6], "tile": w[7], "deps": [q(8 + 2 * i) for i in range(4)],
+        "wait_retired": q(16), "ptr": [q(18 + 2 * i) for i in range(4)],
+        "src_len": [w[26], w[27]], "tstart": q(60), "user_ops": w[62], "check": w[63],
+    }
+    d["fused_out"] = [q(26 + 2 * s) for s in range(8)]
+    d["step_op"] = [(w[42 + s // 4] >> (8 * (s % 4))) & 0xFF for s in range(8)]
+    d["step_fl"] = [(w[44 + s // 4] >> (8 * (s % 4))) & 0xFF for s in range(8)]
+    d["fscal"] = list(struct.unpack("<8f", raw[46 * 4:54 * 4]))
+    d["alpha"] = struct.unpack("<f", raw[28 * 4:29 * 4])[0]
+    return d

@@ -219,7 +219,7 @@ DECODE_OPS_PER_LAYER = 15
 
 def gen_decode(seed: int = 0, layers: int = 24, hidden: int = 896, heads: int = 14,
                head_dim: int = 64, ffn: int = 4864, kv_len: int = 512, tokens: int = 64,
-               eps: float = 1e-6, weight_std: float = 0.02) -> Workload:
+               eps: float = 1e-6, weight_std: float = 0.02, distinct: bool = False) -> Workload:
     """Synthetic batch-1 decode of a decoder with random N(0, 0.02) bf16 weights.
 
     Per layer, 15 ops: RMSNORM, GEMV(qkv), ROPE(q), ROPE(k -> K cache slot),
@@ -229,6 +229,11 @@ def gen_decode(seed: int = 0, layers: int = 24, hidden: int = 896, heads: int = 
     kv_len slots (a sliding window over a random N(0, 1) cache).  The hidden
     state after the last layer of token t is the input of token t + 1.  Each
     token's ops form one submission group (flush per token).
+
+    With ``distinct`` every activation of every (token, layer) gets its own
+    buffer and the residual adds write a new hidden-state buffer, so each
+    element is written at most once (verification mode: every intermediate
+    survives to the end and each op can be re-checked on its own inputs).
     """
     assert hidden == heads * head_dim
     rng = np.random.default_rng(seed)
@@ -260,48 +265,71 @@ def gen_decode(seed: int = 0, layers: int = 24, hidden: int = 896, heads: int = 
     eps32 = float(np.float32(eps))
     ops: List[Op] = []
     groups = []
+    sizes = {"h": (D, "bf16"), "qkv": (3 * D, "bf16"), "q": (D, "bf16"),
+             "scores": (H * S, "f32"), "probs": (H * S, "f32"), "attn": (D, "bf16"),
+             "o": (D, "bf16"), "gu": (2 * F, "bf16"), "act": (F, "bf16"), "down": (D, "bf16"),
+             "x": (D, "bf16")}
+    cur_x = "x"
     for t in range(tokens):
         g0 = len(ops)
         slot = t % S
         tab = Ref("rope", t * Dh)
         for l in range(layers):
+            if distinct:
+                def nm(base, tag=""):
+                    name = f"{base}{tag}.{t}.{l}"
+                    cnt, dt = sizes[base]
+                    if name not in bufs:
+                        add(name, np.zeros(cnt, NP_DTYPE[dt]), dt)
+                    return name
+                h1, qkv, q, sc, pr = nm("h", "a"), nm("qkv"), nm("q"), nm("scores"), nm("probs")
+                at, o, h2, gu, act, dn = nm("attn"), nm("o"), nm("h", "b"), nm("gu"), nm("act"), nm("down")
+                x_in, x_mid, x_out = cur_x, nm("x", "a"), nm("x", "b")
+            else:
+                h1 = h2 = "h"
+                qkv, q, sc, pr, at, o, gu, act, dn = ("qkv", "q", "scores", "probs", "attn", "o",
+                                                      "gu", "act", "down")
+                x_in = x_mid = x_out = "x"
             ops += [
-                Op("rmsnorm", Ref("h"), (Ref("x"),), Ref(f"gin{l}"), n=D, dtype="bf16",
+                Op("rmsnorm", Ref(h1), (Ref(x_in),), Ref(f"gin{l}"), n=D, dtype="bf16",
                    rows=1, row_len=D, eps=eps32),
-                Op("gemv", Ref("qkv"), (Ref("h"),), Ref(f"Wqkv{l}"), n=3 * D, dtype="bf16",
+                Op("gemv", Ref(qkv), (Ref(h1),), Ref(f"Wqkv{l}"), n=3 * D, dtype="bf16",
                    dims=(3 * D, D)),
-                Op("rope", Ref("q"), (Ref("qkv", 0),), tab, n=D, dtype="bf16",
+                Op("rope", Ref(q), (Ref(qkv, 0),), tab, n=D, dtype="bf16",
                    rows=H, row_len=Dh, dims=(H, Dh)),
-                Op("rope", Ref(f"K{l}", slot * D), (Ref("qkv", D),), tab, n=D, dtype="bf16",
+                Op("rope", Ref(f"K{l}", slot * D), (Ref(qkv, D),), tab, n=D, dtype="bf16",
                    rows=H, row_len=Dh, dims=(H, Dh)),
-                Op("copy", Ref(f"V{l}", slot * D), (Ref("qkv", 2 * D),), n=D, dtype="bf16"),
-                Op("attn_score", Ref("scores"), (Ref("q"),), Ref(f"K{l}"), n=H * S,
+                Op("copy", Ref(f"V{l}", slot * D), (Ref(qkv, 2 * D),), n=D, dtype="bf16"),
+                Op("attn_score", Ref(sc), (Ref(q),), Ref(f"K{l}"), n=H * S,
                    dtype="bf16", alpha=1.0 / math.sqrt(Dh), dims=(H, Dh, S)),
-                Op("row_softmax", Ref("probs"), (Ref("scores"),), n=H * S, dtype="f32",
+                Op("row_softmax", Ref(pr), (Ref(sc),), n=H * S, dtype="f32",
                    rows=H, row_len=S),
-                Op("attn_av", Ref("attn"), (Ref("probs"),), Ref(f"V{l}"), n=D, dtype="bf16",
+                Op("attn_av", Ref(at), (Ref(pr),), Ref(f"V{l}"), n=D, dtype="bf16",
                    dims=(H, Dh, S)),
-                Op("gemv", Ref("o"), (Ref("attn"),), Ref(f"Wo{l}"), n=D, dtype="bf16",
+                Op("gemv", Ref(o), (Ref(at),), Ref(f"Wo{l}"), n=D, dtype="bf16",
                    dims=(D, D)),
-                Op("add", Ref("x"), (Ref("x"), Ref("o")), n=D, dtype="bf16"),
-                Op("rmsnorm", Ref("h"), (Ref("x"),), Ref(f"gpost{l}"), n=D, dtype="bf16",
+                Op("add", Ref(x_mid), (Ref(x_in), Ref(o)), n=D, dtype="bf16"),
+                Op("rmsnorm", Ref(h2), (Ref(x_mid),), Ref(f"gpost{l}"), n=D, dtype="bf16",
                    rows=1, row_len=D, eps=eps32),
-                Op("gemv", Ref("gu"), (Ref("h"),), Ref(f"Wgu{l}"), n=2 * F, dtype="bf16",
+                Op("gemv", Ref(gu), (Ref(h2),), Ref(f"Wgu{l}"), n=2 * F, dtype="bf16",
                    dims=(2 * F, D)),
-                Op("silu_mul", Ref("act"), (Ref("gu", 0), Ref("gu", F)), n=F, dtype="bf16"),
-                Op("gemv", Ref("down"), (Ref("act"),), Ref(f"Wdown{l}"), n=D, dtype="bf16",
+                Op("silu_mul", Ref(act), (Ref(gu, 0), Ref(gu, F)), n=F, dtype="bf16"),
+                Op("gemv", Ref(dn), (Ref(act),), Ref(f"Wdown{l}"), n=D, dtype="bf16",
                    dims=(D, F)),
-                Op("add", Ref("x"), (Ref("x"), Ref("down")), n=D, dtype="bf16"),
+                Op("add", Ref(x_out), (Ref(x_mid), Ref(dn)), n=D, dtype="bf16"),
             ]
+            cur_x = x_out
         groups.append((g0, len(ops)))
     weight_bytes = 2 * layers * (3 * D * D + D * D + 2 * F * D + D * F + 2 * D)
     kv_bytes = 2 * layers * 2 * S * D
-    return Workload("decode", bufs, dts, ops, groups=groups,
-                    outputs=["x"] + [f"K{l}" for l in range(layers)] + [f"V{l}" for l in range(layers)],
+    outs = [cur_x] + [f"K{l}" for l in range(layers)] + [f"V{l}" for l in range(layers)]
+    if distinct:
+        outs = sorted({op.out.buf for op in ops})
+    return Workload("decode", bufs, dts, ops, groups=groups, outputs=outs,
                     meta={"layers": layers, "tokens": tokens, "hidden": D, "heads": H,
                           "head_dim": Dh, "ffn": F, "kv_len": S,
                           "weight_bytes": weight_bytes, "kv_bytes": kv_bytes,
-                          "ops_per_token": layers * DECODE_OPS_PER_LAYER})
+                          "ops_per_token": layers * DECODE_OPS_PER_LAYER, "final_x": cur_x})
 
 
 # ----------------------------------------------------------------------------

@@ -1,0 +1,288 @@
+"""GPU parity: the resident kernel (and the per-op comparator) against the oracle.
+
+Every test runs seeded workloads through libgpuos.so on cuda:0 and compares
+the outputs with the CPU oracle element by element: bit-exact for COPY,
+GATHER, ADD, MUL, SCALE, RELU and ROPE, within 1e-5 (fp32) / 1e-2 (bf16)
+relative to the oracle's error scale for reductions and transcendentals.
+"""
+
+import math
+
+import numpy as np
+import pytest
+
+import oracle
+from persistent_fusion_amd import gpuos, runner, workloads
+from persistent_fusion_amd.workloads import Op, Ref, Workload
+
+pytestmark = pytest.mark.gpu
+
+
+def _need_gpu():
+    import torch
+
+    assert torch.cuda.is_available(), "GPU tests need a GPU"
+    gpuos.lib()  # fails loudly when the native library is missing
+
+
+def say(msg):
+    print(msg, flush=True)
+
+
+def check(wl, got, outputs=None, upto=None):
+    want, scales = oracle.run(wl, upto=upto, scales=True)
+    for name in outputs or wl.outputs:
+        r = oracle.compare(got[name], want[name], wl.dtypes[name], scales.get(name))
+        assert r.ok, f"{wl.name}/{name}: {r}"
+
+
+# ----------------------------------------------------------------------------
+# the fused chain y = relu(a*x + b)
+
+
+@pytest.mark.parametrize("n", [1, 63, 1000, 4097, 1_000_003])
+@pytest.mark.parametrize("fusion", [1, 2])
+def test_fused_chain_resident(n, fusion):
+    _need_gpu()
+    say(f"fused chain n={n} fusion={fusion}")
+    wl = workloads.gen_fused_chain(seed=1, n=n)
+    got = runner.run_resident(wl, outputs=["y"], fusion=fusion)
+    check(wl, got, ["y"])
+
+
+@pytest.mark.parametrize("fuse", [False, True])
+def test_fused_chain_per_op_launches(fuse):
+    _need_gpu()
+    say(f"fused chain per-op fuse={fuse}")
+    wl = workloads.gen_fused_chain(seed=2, n=1_000_003)
+    got = runner.run_per_op(wl, outputs=["y"], fuse=fuse)
+    check(wl, got, ["y"])
+
+
+def test_fused_chain_full_size():
+    _need_gpu()
+    say("fused chain n=16777216")
+    wl = workloads.gen_fused_chain(seed=0)
+    got = runner.run_resident(wl, outputs=["y"])
+    check(wl, got, ["y"])
+
+
+# ----------------------------------------------------------------------------
+# queue of 1,000 elementwise ops on 4,096-element vectors
+
+
+@pytest.mark.parametrize("fusion", [1, 2])
+def test_elementwise_queue_full(fusion):
+    _need_gpu()
+    say(f"elementwise queue 1000x4096 fusion={fusion}")
+    wl = workloads.gen_elementwise_queue(seed=0)
+    got = runner.run_resident(wl, fusion=fusion)
+    check(wl, got)
+
+
+@pytest.mark.parametrize("auto_deps", [1, 2])
+def test_elementwise_queue_explicit_or_auto_deps(auto_deps):
+    _need_gpu()
+    say(f"elementwise queue auto_deps={auto_deps}")
+    wl = workloads.gen_elementwise_queue(seed=3, n_ops=600, n=4097)
+    got = runner.run_resident(wl, auto_deps=auto_deps)
+    check(wl, got)
+
+
+def test_elementwise_queue_per_op():
+    _need_gpu()
+    say("elementwise queue per-op")
+    wl = workloads.gen_elementwise_queue(seed=0)
+    got = runner.run_per_op(wl)
+    check(wl, got)
+
+
+def test_elementwise_queue_small_ring_wraps():
+    _need_gpu()
+    say("elementwise queue ring_slots=64")
+    wl = workloads.gen_elementwise_queue(seed=4, n_ops=1000, n=1024)
+    got = runner.run_resident(wl, ring_slots=64)
+    check(wl, got)
+
+
+# ----------------------------------------------------------------------------
+# every opcode on ragged sizes
+
+
+def _ew_workload(kind, dtype, n, seed, src_len=(0, 0)):
+    rng = np.random.default_rng(seed)
+    conv = (lambda a: workloads.f32_to_bf16_trunc(a)) if dtype == "bf16" else (lambda a: a)
+    npdt = np.uint16 if dtype == "bf16" else np.float32
+    la = src_len[0] or n
+    lb = src_len[1] or n
+    bufs = {"a": conv((rng.standard_normal(la) * 3).astype(np.float32)),
+            "b": conv((rng.standard_normal(lb) * 3).astype(np.float32)),
+            "y": np.zeros(n, npdt)}
+    dts = {k: dtype for k in bufs}
+    ar = 2 if kind in ("add", "mul", "silu_mul") else 1
+    ins = (Ref("a"), Ref("b"))[:ar]
+    op = Op(kind, Ref("y"), ins, n=n, dtype=dtype, alpha=-0.6875, src_len=src_len[:2])
+    return Workload(f"{kind}-{dtype}-{n}", bufs, dts, [op], outputs=["y"])
+
+
+@pytest.mark.parametrize("kind", ["add", "mul", "scale", "relu", "exp", "copy", "silu_mul"])
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_elementwise_ops_ragged(kind, dtype):
+    _need_gpu()
+    for n in (1, 63, 64, 65, 4095, 4096, 4097, (1 << 20) + 3):
+        say(f"{kind} {dtype} n={n}")
+        wl = _ew_workload(kind, dtype, n, seed=n)
+        got = runner.run_resident(wl)
+        check(wl, got)
+
+
+@pytest.mark.parametrize("kind", ["add", "relu", "copy"])
+def test_cyclic_sources(kind):
+    _need_gpu()
+    say(f"cyclic {kind}")
+    wl = _ew_workload(kind, "f32", 10_000, seed=5, src_len=(777, 4096))
+    got = runner.run_resident(wl)
+    check(wl, got)
+    got = runner.run_per_op(wl)
+    check(wl, got)
+
+
+def test_special_values_bit_exact():
+    _need_gpu()
+    say("special values")
+    vals = np.array([0.0, -0.0, np.nan, np.inf, -np.inf, 1e-45, -1e-45, 2.0 ** -140, 3.4e38,
+                     -3.4e38, 1.0, -1.0], np.float32)
+    n = vals.size * 100
+    a = np.tile(vals, 100)
+    b = np.roll(a, 7)
+    bufs = {"a": a, "b": b}
+    ops = []
+    for i, kind in enumerate(("add", "mul", "relu", "scale")):
+        bufs[f"y{i}"] = np.zeros(n, np.float32)
+        ins = (Ref("a"), Ref("b")) if kind in ("add", "mul") else (Ref("a"),)
+        ops.append(Op(kind, Ref(f"y{i}"), ins, n=n, alpha=3.0))
+    wl = Workload("special", bufs, {k: "f32" for k in bufs}, ops, outputs=[f"y{i}" for i in range(4)])
+    got = runner.run_resident(wl)
+    check(wl, got)
+
+
+@pytest.mark.parametrize("kind", ["row_sum", "row_softmax", "rmsnorm"])
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_row_ops(kind, dtype):
+    _need_gpu()
+    rng = np.random.default_rng(7)
+    conv = (lambda a: workloads.f32_to_bf16_trunc(a)) if dtype == "bf16" else (lambda a: a)
+    npdt = np.uint16 if dtype == "bf16" else np.float32
+    for rows, L in ((1, 1), (3, 63), (14, 512), (5, 896), (2, 4096), (300, 129), (1, 4095)):
+        say(f"{kind} {dtype} rows={rows} L={L}")
+        n = rows * L
+        bufs = {"x": conv((rng.standard_normal(n) * 2).astype(np.float32)),
+                "g": conv(rng.standard_normal(L).astype(np.float32)),
+                "y": np.zeros(rows if kind == "row_sum" else n, npdt)}
+        op = Op(kind, Ref("y"), (Ref("x"),), Ref("g") if kind == "rmsnorm" else None, n=n,
+                dtype=dtype, rows=rows, row_len=L, eps=float(np.float32(1e-6)))
+        wl = Workload(kind, bufs, {k: dtype for k in bufs}, [op], outputs=["y"])
+        check(wl, runner.run_resident(wl))
+
+
+def test_softmax_special_rows():
+    _need_gpu()
+    say("softmax special rows")
+    L = 64
+    x = np.random.default_rng(8).standard_normal(5 * L).astype(np.float32)
+    x[3] = np.nan
+    x[L + 5] = np.inf
+    x[2 * L:3 * L] = -np.inf
+    x[3 * L + 1] = -np.inf
+    x[4 * L:] = 88.0
+    bufs = {"x": x, "y": np.zeros(5 * L, np.float32)}
+    wl = Workload("softmax-special", bufs, {"x": "f32", "y": "f32"},
+                  [Op("row_softmax", Ref("y"), (Ref("x"),), n=5 * L, rows=5, row_len=L)], outputs=["y"])
+    check(wl, runner.run_resident(wl))
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_rope(dtype):
+    _need_gpu()
+    rng = np.random.default_rng(9)
+    for heads, hd in ((14, 64), (3, 10), (1, 128)):
+        say(f"rope {dtype} heads={heads} hd={hd}")
+        n = heads * hd
+        conv = (lambda a: workloads.f32_to_bf16_trunc(a)) if dtype == "bf16" else (lambda a: a)
+        bufs = {"x": conv(rng.standard_normal(n).astype(np.float32)),
+                "t": workloads.rope_table([537], hd)[0],
+                "y": np.zeros(n, np.uint16 if dtype == "bf16" else np.float32)}
+        ops = [Op("rope", Ref("y"), (Ref("x"),), Ref("t"), n=n, dtype=dtype, rows=heads, row_len=hd,
+                  dims=(heads, hd)),
+               Op("rope", Ref("x"), (Ref("x"),), Ref("t"), n=n, dtype=dtype, rows=heads, row_len=hd,
+                  dims=(heads, hd))]  # in place
+        wl = Workload("rope", bufs, {"x": dtype, "t": "f32", "y": dtype}, ops, outputs=["y", "x"])
+        check(wl, runner.run_resident(wl))
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_gemv(dtype):
+    _need_gpu()
+    rng = np.random.default_rng(10)
+    for M, K in ((1, 8), (5, 7), (2688, 896), (896, 4864), (9728, 896), (33, 100)):
+        say(f"gemv {dtype} M={M} K={K}")
+        conv = (lambda a: workloads.f32_to_bf16_trunc(a)) if dtype == "bf16" else (lambda a: a)
+        bufs = {"W": workloads.f32_to_bf16_trunc((rng.standard_normal(M * K) * 0.05).astype(np.float32)),
+                "x": conv(rng.standard_normal(K).astype(np.float32)),
+                "y": np.zeros(M, np.uint16 if dtype == "bf16" else np.float32)}
+        wl = Workload("gemv", bufs, {"W": "bf16", "x": dtype, "y": dtype},
+                      [Op("gemv", Ref("y"), (Ref("x"),), Ref("W"), n=M, dtype=dtype, dims=(M, K))],
+                      outputs=["y"])
+        check(wl, runner.run_resident(wl))
+
+
+@pytest.mark.parametrize("H,D,S", [(14, 64, 512), (2, 8, 5), (3, 10, 70), (4, 128, 64)])
+def test_attention(H, D, S):
+    _need_gpu()
+    say(f"attention H={H} D={D} S={S}")
+    rng = np.random.default_rng(11)
+    bf = workloads.f32_to_bf16_trunc
+    bufs = {"q": bf(rng.standard_normal(H * D).astype(np.float32)),
+            "K": bf(rng.standard_normal(S * H * D).astype(np.float32)),
+            "V": bf(rng.standard_normal(S * H * D).astype(np.float32)),
+            "s": np.zeros(H * S, np.float32), "p": np.zeros(H * S, np.float32),
+            "o": np.zeros(H * D, np.uint16)}
+    ops = [Op("attn_score", Ref("s"), (Ref("q"),), Ref("K"), n=H * S, dtype="bf16",
+              alpha=1 / math.sqrt(D), dims=(H, D, S)),
+           Op("row_softmax", Ref("p"), (Ref("s"),), n=H * S, rows=H, row_len=S),
+           Op("attn_av", Ref("o"), (Ref("p"),), Ref("V"), n=H * D, dtype="bf16", dims=(H, D, S))]
+    wl = Workload("attn", bufs, {"q": "bf16", "K": "bf16", "V": "bf16", "s": "f32", "p": "f32",
+                                 "o": "bf16"}, ops, outputs=["s", "p", "o"])
+    got = runner.run_resident(wl)
+    # local check: each op against the oracle run on the GPU's own inputs
+    want, sc = oracle.run(wl, upto=1, scales=True)
+    assert oracle.compare(got["s"], want["s"], "f32", sc["s"]).ok
+    b2 = dict(wl.buffers, s=got["s"])
+    want, sc = oracle.run(Workload("attn", b2, wl.dtypes, ops[1:2]), scales=True)
+    assert oracle.compare(got["p"], want["p"], "f32", sc["p"]).ok
+    b3 = dict(wl.buffers, p=got["p"])
+    want, sc = oracle.run(Workload("attn", b3, wl.dtypes, ops[2:3]), scales=True)
+    r = oracle.compare(got["o"], want["o"], "bf16", sc["o"])
+    assert r.ok, str(r)
+
+
+def test_gather():
+    _need_gpu()
+    say("gather")
+    rng = np.random.default_rng(12)
+    x = rng.standard_normal(1000).astype(np.float32)
+    idx = rng.integers(0, 1000, 5000).astype(np.int32)
+    bufs = {"x": x, "i": idx, "y": np.zeros(5000, np.float32)}
+    wl = Workload("gather", bufs, {"x": "f32", "i": "i32", "y": "f32"},
+                  [Op("gather", Ref("y"), (Ref("x"),), Ref("i"), n=5000, src_len=(1000, 0))],
+                  outputs=["y"])
+    check(wl, runner.run_resident(wl))
+
+
+def test_small_decode_local_check():
+    _need_gpu()
+    say("decode 2 layers x 3 tokens, verification form")
+    wl = workloads.gen_decode(seed=0, layers=2, tokens=3, distinct=True)
+    got = runner.run_resident(wl)
+    bad = oracle.local_check(wl, got, oracle.compare)
+    assert not bad, [(i, wl.ops[i].kind, n, str(r)) for i, n, r in bad[:5]]

@@ -1,0 +1,322 @@
+"""Host half of the runtime, exercised without a GPU.
+
+A context created on GPUOS_DEVICE_NONE keeps its rings in ordinary memory and
+launches nothing; these tests inspect the descriptors it publishes (fusion
+pass, hazard dependencies, ticket ranges, ring wraparound and back-pressure)
+and the validation errors.  Device pointers here are opaque addresses that are
+never dereferenced.
+"""
+
+import os
+import re
+
+import pytest
+
+from persistent_fusion_amd import gpuos
+from persistent_fusion_amd.gpuos import Context, DEVICE_NONE, GpuosError, decode_desc, make_op
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+BASE = 0x7F0000000000
+MB = 1 << 26
+
+
+def buf(i):
+    """Opaque device address number i (64 MiB apart)."""
+    return BASE + i * MB
+
+
+def ctx(**kw):
+    kw.setdefault("ring_slots", 1024)
+    return Context(DEVICE_NONE, **kw)
+
+
+def desc(c, seq, ring=0):
+    return decode_desc(c.read_desc(ring, seq))
+
+
+def test_library_exports_every_declared_symbol():
+    declared = set()
+    for h in ("gpuos.h", "gpuos_debug.h"):
+        text = open(os.path.join(ROOT, "include", h)).read()
+        declared |= set(re.findall(r"^(?:int|void|uint64_t|const char\*)\s+(gpuos_[a-z_]+)\(",
+                                   text, re.M))
+    lib = gpuos.lib()
+    missing = [s for s in sorted(declared) if not hasattr(lib, s)]
+    assert not missing, missing
+    assert set(gpuos.EXPORTS) == declared
+    assert lib.gpuos_abi_version() == 1
+
+
+def test_fused_chain_becomes_one_descriptor():
+    n = 1 << 20
+    a, x, b, t1, t2, y = (buf(i) for i in range(6))
+    ops = (gpuos.GpuosOp * 3)(
+        make_op("mul", t1, [a, x], n=n, flags=gpuos.FLAG_TRANSIENT),
+        make_op("add", t2, [t1, b], n=n, flags=gpuos.FLAG_TRANSIENT, deps=[-1]),
+        make_op("relu", y, [t2], n=n, deps=[-1]),
+    )
+    with ctx() as c:
+        ids = c.submit(ops)
+        assert ids == [1, 2, 3]
+        c.flush()
+        assert c.published(0) == 1
+        d = desc(c, 1)
+        assert d["opcode"] == 32 and d["nsteps"] == 3 and d["user_ops"] == 3
+        assert d["ptr"][0] == a  # chain input
+        assert d["step_op"][:3] == [2, 1, 4]  # MUL, ADD, RELU
+        # operands: x as fused input 1, b as fused input 2; only y is stored
+        assert d["ptr"][1] == x and d["ptr"][2] == b
+        assert [(f >> 4) & 3 for f in d["step_fl"][:3]] == [1, 2, 0]
+        assert [bool(f & 4) for f in d["step_fl"][:3]] == [False, False, True]
+        assert d["fused_out"][:3] == [0, 0, y]
+        assert d["deps"] == [0, 0, 0, 0]
+        assert d["ntiles"] * d["tile"] >= n and d["tstart"] == 0
+        assert all(c.seq_of(i) == (0, 1) for i in ids)
+        assert c.stats()["ops_fused"] == 2
+
+
+def test_fusion_off_and_transient_output_read_later_is_kept():
+    n = 4096
+    a, x, b, t1, t2, y, z = (buf(i) for i in range(7))
+    ops = (gpuos.GpuosOp * 4)(
+        make_op("mul", t1, [a, x], n=n, flags=gpuos.FLAG_TRANSIENT),
+        make_op("add", t2, [t1, b], n=n, flags=gpuos.FLAG_TRANSIENT),
+        make_op("relu", y, [t2], n=n),
+        make_op("copy", z, [t1], n=n),  # reads the transient t1 after the chain
+    )
+    with ctx(fusion=2) as c:
+        c.submit(ops)
+        c.flush()
+        assert c.published(0) == 4
+        assert [desc(c, s)["opcode"] for s in (1, 2, 3, 4)] == [4, 3, 6, 1]
+        # auto deps: add waits for mul, relu for add, copy for mul
+        assert desc(c, 2)["deps"][0] == 1 and desc(c, 3)["deps"][0] == 2
+        assert desc(c, 4)["deps"][0] == 1
+    with ctx() as c:
+        c.submit(ops)
+        c.flush()
+        assert c.published(0) == 2  # chain of 3, then the copy
+        d = desc(c, 1)
+        assert d["fused_out"][:3] == [t1, 0, y]
+        assert desc(c, 2)["deps"][0] == 1
+
+
+def test_fusion_rejects_unsafe_chains():
+    n = 4096
+    p = [buf(i) for i in range(8)]
+    with ctx() as c:
+        # second op's other operand is the first op's own output at another
+        # offset: the chain must not be fused
+        ops = (gpuos.GpuosOp * 2)(
+            make_op("add", p[2], [p[0], p[1]], n=n),
+            make_op("mul", p[3], [p[2], p[2] + 64], n=n),
+        )
+        c.submit(ops)
+        c.flush()
+        assert c.published(0) == 2
+    with ctx() as c:
+        # different n: not fused
+        ops = (gpuos.GpuosOp * 2)(
+            make_op("add", p[2], [p[0], p[1]], n=n),
+            make_op("relu", p[3], [p[2]], n=n // 2),
+        )
+        c.submit(ops)
+        c.flush()
+        assert c.published(0) == 2
+    with ctx() as c:
+        # in place chain x = relu(x * x) fuses (same base, loads before stores)
+        ops = (gpuos.GpuosOp * 2)(
+            make_op("mul", p[0], [p[0], p[0]], n=n),
+            make_op("relu", p[0], [p[0]], n=n),
+        )
+        c.submit(ops)
+        c.flush()
+        assert c.published(0) == 1
+        d = desc(c, 1)
+        assert d["step_fl"][0] & 2  # FSF_SELF
+        assert d["fused_out"][:2] == [p[0], p[0]]
+
+
+def test_hazard_dependencies_raw_war_waw():
+    n = 1024
+    A, B, C_, D = (buf(i) for i in range(4))
+    ops = (gpuos.GpuosOp * 4)(
+        make_op("relu", B, [A], n=n),          # 1: reads A, writes B
+        make_op("exp", C_, [A], n=n),          # 2: reads A, writes C
+        make_op("scale", A, [D], n=n, alpha=2.0),  # 3: writes A (WAR on 1, 2)
+        make_op("exp", B, [C_], n=n),          # 4: RAW on 2, WAW on 1
+    )
+    with ctx(fusion=2) as c:
+        c.submit(ops)
+        c.flush()
+        deps = [sorted(x for x in desc(c, s)["deps"] if x) for s in (1, 2, 3, 4)]
+        assert deps == [[], [], [1, 2], [1, 2]]
+    with ctx(fusion=2, auto_deps=2) as c:
+        c.submit(ops)
+        c.flush()
+        assert all(desc(c, s)["deps"] == [0, 0, 0, 0] for s in (1, 2, 3, 4))
+
+
+def test_partial_overlap_is_a_hazard_and_disjoint_is_not():
+    A = buf(0)
+    ops = (gpuos.GpuosOp * 3)(
+        make_op("relu", A, [buf(1)], n=1000),            # writes A[0:1000]
+        make_op("relu", A + 4000, [buf(2)], n=1000),     # writes A[1000:2000], disjoint
+        make_op("exp", buf(3), [A + 3996], n=2),          # reads A[999:1001]: both
+    )
+    with ctx(fusion=2) as c:
+        c.submit(ops)
+        c.flush()
+        assert desc(c, 2)["deps"] == [0, 0, 0, 0]
+        assert sorted(x for x in desc(c, 3)["deps"] if x) == [1, 2]
+
+
+def test_many_dependencies_fall_back_to_retire_order():
+    n = 256
+    ops = (gpuos.GpuosOp * 7)(*[make_op("relu", buf(10 + i), [buf(0)], n=n) for i in range(6)],
+                              make_op("scale", buf(0), [buf(1)], n=n, alpha=1.0))
+    with ctx(fusion=2) as c:
+        c.submit(ops)
+        c.flush()
+        d = desc(c, 7)
+        assert d["deps"] == [0, 0, 0, 0] and d["wait_retired"] == 6
+
+
+def test_ticket_ranges_are_contiguous_and_tiles_cover_ops():
+    ops = (gpuos.GpuosOp * 5)(
+        make_op("add", buf(0), [buf(1), buf(2)], n=10_000),
+        make_op("row_softmax", buf(3), [buf(4)], n=14 * 512, rows=14, row_len=512),
+        make_op("gemv", buf(5), [buf(6)], aux=buf(7), n=2688, dtype="bf16", dims=(2688, 896)),
+        make_op("attn_av", buf(8), [buf(9)], aux=buf(10), n=896, dtype="bf16", dims=(14, 64, 512)),
+        make_op("rope", buf(11), [buf(12)], aux=buf(13), n=896, dtype="bf16", rows=14, row_len=64),
+    )
+    with ctx(fusion=2) as c:
+        c.submit(ops)
+        c.flush()
+        ds = [desc(c, s) for s in range(1, 6)]
+        start = 0
+        for d in ds:
+            assert d["tstart"] == start
+            start += d["ntiles"]
+        assert ds[0]["ntiles"] * ds[0]["tile"] >= 10_000 and ds[0]["tile"] % 256 == 0
+        assert ds[1]["ntiles"] * ds[1]["tile"] >= 14
+        assert ds[2]["ntiles"] * ds[2]["tile"] >= 2688
+        assert ds[3]["ntiles"] == 896 // 8
+        assert ds[4]["ntiles"] == 1
+
+
+def test_ring_wraparound_and_back_pressure():
+    n = 256
+    with ctx(fusion=2, auto_deps=2, ring_slots=64) as c:
+        ops = (gpuos.GpuosOp * 150)(*[make_op("relu", buf(i % 7), [buf(100)], n=n) for i in range(150)])
+        ids = c.submit(ops)
+        with pytest.raises(GpuosError) as e:
+            c.flush()
+        assert e.value.status == gpuos.EAGAIN
+        assert c.published(0) == 64
+        with pytest.raises(GpuosError):
+            c.read_desc(0, 65)
+        c.retire(0, 40)
+        with pytest.raises(GpuosError):
+            c.flush()
+        assert c.published(0) == 104
+        # slot of seq 1 now holds seq 65
+        with pytest.raises(GpuosError):
+            c.read_desc(0, 1)
+        d = desc(c, 65)
+        assert d["seq"] == 65 and d["check"] == (65 ^ 0x9E3779B9)
+        c.retire(0, 104)
+        c.flush()
+        assert c.published(0) == 150
+        assert c.seq_of(ids[-1]) == (0, 150)
+        c.retire(0, 150)
+        assert c.query(ids[-1])
+
+
+def test_priority_ring_and_cross_ring_rules():
+    n = 4096
+    with ctx(fusion=2) as c:
+        ops = (gpuos.GpuosOp * 3)(
+            make_op("add", buf(0), [buf(1), buf(2)], n=n),
+            make_op("relu", buf(3), [buf(4)], n=n, dtype="bf16", flags=gpuos.FLAG_LC),
+            make_op("scale", buf(5), [buf(3)], n=n, dtype="bf16", flags=gpuos.FLAG_LC, alpha=0.5),
+        )
+        ids = c.submit(ops)
+        c.flush()
+        assert c.published(0) == 1 and c.published(1) == 2
+        assert c.seq_of(ids[1]) == (1, 1) and c.seq_of(ids[2]) == (1, 2)
+        assert desc(c, 2, ring=1)["deps"][0] == 1
+        bad = (gpuos.GpuosOp * 2)(
+            make_op("add", buf(0), [buf(1), buf(2)], n=n),
+            make_op("relu", buf(6), [buf(7)], n=n, flags=gpuos.FLAG_LC, deps=[-1]),
+        )
+        with pytest.raises(GpuosError) as e:
+            c.submit(bad)
+        assert e.value.status == gpuos.EINVAL
+
+
+@pytest.mark.parametrize("op,msg", [
+    (lambda: make_op("add", buf(0), [buf(1), 0], n=10), "in[1]"),
+    (lambda: make_op("add", buf(0) + 2, [buf(1), buf(2)], n=10), "aligned"),
+    (lambda: make_op("relu", buf(0), [buf(1)], n=0), "n must be"),
+    (lambda: make_op("row_sum", buf(0), [buf(1)], n=100, rows=3, row_len=33), "rows"),
+    (lambda: make_op("row_softmax", buf(0), [buf(1)], n=8192, rows=1, row_len=8192), "4096"),
+    (lambda: make_op("gemv", buf(0), [buf(1)], aux=buf(2), n=10, dims=(11, 4)), "GEMV"),
+    (lambda: make_op("rope", buf(0), [buf(1)], aux=buf(2), n=21, rows=3, row_len=7), "ROPE"),
+    (lambda: make_op("gather", buf(0), [buf(1)], aux=buf(2), n=10), "src_len"),
+    (lambda: make_op("relu", buf(0), [buf(1)], n=10, dtype="i32"), "int32"),
+])
+def test_validation_errors_stage_nothing(op, msg):
+    with ctx() as c:
+        good = make_op("relu", buf(5), [buf(6)], n=16)
+        arr = (gpuos.GpuosOp * 2)(good, op())
+        with pytest.raises(GpuosError) as e:
+            c.submit(arr)
+        assert e.value.status == gpuos.EINVAL and msg in str(e.value)
+        c.flush()
+        assert c.published(0) == 0
+
+
+def test_dependency_on_future_or_outside_ids_is_rejected():
+    with ctx() as c:
+        arr = (gpuos.GpuosOp * 1)(make_op("relu", buf(0), [buf(1)], n=16, deps=[5]))
+        with pytest.raises(GpuosError):
+            c.submit(arr)
+        arr = (gpuos.GpuosOp * 1)(make_op("relu", buf(0), [buf(1)], n=16, deps=[-1]))
+        with pytest.raises(GpuosError):
+            c.submit(arr)
+        ok = c.submit((gpuos.GpuosOp * 1)(make_op("relu", buf(0), [buf(1)], n=16)))
+        arr = (gpuos.GpuosOp * 1)(make_op("exp", buf(2), [buf(3)], n=16, deps=[ok[0]]))
+        c.submit(arr)
+        c.flush()
+        assert desc(c, 2)["deps"][0] == 1
+
+
+def test_host_only_sync_reports_timeout_and_config_errors():
+    with ctx() as c:
+        c.submit((gpuos.GpuosOp * 1)(make_op("relu", buf(0), [buf(1)], n=16)))
+        with pytest.raises(GpuosError) as e:
+            c.sync(0, 0.01)
+        assert e.value.status == gpuos.ETIMEDOUT
+    for bad in ({"ring_slots": 100}, {"waves_per_cu": 6}, {"tile_elems": 100}, {"max_fuse": 9}):
+        with pytest.raises(GpuosError):
+            Context(DEVICE_NONE, **bad)
+
+
+def test_elementwise_queue_encoding_matches_workload():
+    from persistent_fusion_amd.workloads import gen_elementwise_queue
+
+    wl = gen_elementwise_queue(n_ops=50, n=4096)
+    names = sorted(wl.buffers)
+    base = {k: buf(i) for i, k in enumerate(names)}
+    addr = lambda ref, dt: base[ref.buf] + ref.off * 4
+    arr = gpuos.encode_ops(wl.ops, 0, 50, addr, {})
+    with ctx(fusion=2) as c:
+        c.submit(arr)
+        c.flush()
+        assert c.published(0) == 50
+        for i, op in enumerate(wl.ops):
+            d = desc(c, i + 1)
+            assert d["ptr"][0] == base[op.out.buf]
+            got = sorted(x for x in d["deps"] if x)
+            assert got == sorted({j + 1 for j in op.deps})
