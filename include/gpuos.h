@@ -156,7 +156,9 @@ typedef enum gpuos_dtype {
  *           hazards between the byte ranges of queued ops are added
  *           automatically unless the context was created with auto_deps = 0.
  * All device pointers must be aligned to their element size; 16-byte aligned
- * operands take the 128-bit load path.
+ * operands take the 128-bit load path.  n, rows * row_len and src_len are at
+ * most 2^30, and no operand may span more than 0xFFF00000 bytes (4 GiB minus
+ * 1 MiB: kernels address an operand with 32-bit byte offsets).
  */
 typedef struct gpuos_op {
   uint16_t opcode;   /* gpuos_opcode */
@@ -198,7 +200,11 @@ typedef struct gpuos_config {
   uint32_t block_on_full; /* 1 = submit/flush wait for ring space (default),
                              2 = return GPUOS_EAGAIN */
   uint32_t max_fuse;      /* longest fused chain, 2..8; default 8 */
-  uint32_t reserved[7];
+  uint32_t priority;      /* 1 = workers also serve the latency-critical
+                             ring between their own tiles (default), 2 = no
+                             priority ring: GPUOS_FLAG_LC ops are rejected
+                             and workers skip the per-tile check */
+  uint32_t reserved[6];
 } gpuos_config;
 
 /* Counters returned by gpuos_get_stats. */

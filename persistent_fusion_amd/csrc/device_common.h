@@ -100,20 +100,71 @@ __device__ __forceinline__ float group_sum(float v) {
 
 __device__ __forceinline__ bool aligned16(uint64_t p) { return (p & 15u) == 0; }
 
-// Global-memory accessors.  Pointers carried in descriptors are plain 64-bit
-// addresses; casting them to the global address space gives global_load /
-// global_store instructions instead of flat ones.  16-byte accesses use a
-// native 4 x u32 vector so values stay in registers.
+// Buffer-resource memory access.  Every tile body reads and writes through a
+// raw buffer resource (base address in SGPRs, 32-bit byte offset per lane) so
+// that the cache policy of each access is explicit:
+//   CP_DEFAULT  ordinary loads / stores (kernel boundaries order them);
+//   CP_DEVICE   device-scope coherent (`sc1`): loads read the device
+//               coherence point, stores write through to it.  The resident
+//               kernel uses it for all tensor data, so results become visible
+//               to waves on other XCDs once the stores are acknowledged, with
+//               no L2 writeback or invalidate in the op path.
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
-#define GPUOS_GLOBAL __attribute__((address_space(1)))
+typedef __amdgpu_buffer_rsrc_t rsrc_t;
 
-template <typename T>
-__device__ __forceinline__ T ldg(uint64_t addr) {
-  return *reinterpret_cast<const GPUOS_GLOBAL T*>(addr);
+enum : int { CP_DEFAULT = 0, CP_DEVICE = 16, CP_SYSTEM = 17 };
+
+// 0x00020000: raw (untyped) 32-bit data format word of the gfx9 resource.
+__device__ __forceinline__ rsrc_t make_rsrc(uint64_t base) {
+  return __builtin_amdgcn_make_buffer_rsrc(reinterpret_cast<void*>(base), 0, -1, 0x00020000);
 }
-template <typename T>
-__device__ __forceinline__ void stg(uint64_t addr, T v) {
-  *reinterpret_cast<GPUOS_GLOBAL T*>(addr) = v;
+// A resource covering exactly `bytes` bytes (0 for a null pointer): accesses
+// at offsets past the end are dropped by the hardware range check (loads
+// return zero), so vector loops need no per-lane bounds tests.
+__device__ __forceinline__ rsrc_t make_rsrc_n(uint64_t base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(reinterpret_cast<void*>(base), 0,
+                                           base ? (int)bytes : 0, 0x00020000);
 }
+// Byte offset of 16-byte vector q, saturated (operand extents are at most
+// 0xFFF00000 bytes, checked on the host) so an index past the end stays out of
+// range instead of wrapping.
+__device__ __forceinline__ uint32_t vec_off(uint32_t q) {
+  return q < 0x0FFF0000u ? q * 16u : 0xFFF00000u;
+}
+
+template <int CP>
+__device__ __forceinline__ u32x4 ld128(rsrc_t r, uint32_t off) {
+  return __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, CP);
+}
+template <int CP>
+__device__ __forceinline__ uint32_t ld32(rsrc_t r, uint32_t off) {
+  return __builtin_amdgcn_raw_buffer_load_b32(r, off, 0, CP);
+}
+template <int CP>
+__device__ __forceinline__ uint16_t ld16(rsrc_t r, uint32_t off) {
+  return __builtin_amdgcn_raw_buffer_load_b16(r, off, 0, CP);
+}
+template <int CP>
+__device__ __forceinline__ void st128(rsrc_t r, uint32_t off, u32x4 v) {
+  __builtin_amdgcn_raw_buffer_store_b128(v, r, off, 0, CP);
+}
+template <int CP>
+__device__ __forceinline__ void st32(rsrc_t r, uint32_t off, uint32_t v) {
+  __builtin_amdgcn_raw_buffer_store_b32(v, r, off, 0, CP);
+}
+template <int CP>
+__device__ __forceinline__ void st16(rsrc_t r, uint32_t off, uint16_t v) {
+  __builtin_amdgcn_raw_buffer_store_b16(v, r, off, 0, CP);
+}
+
+// Waits until every memory access this wave issued has completed (stores
+// acknowledged by their scope's coherence point).  The compiler fences keep
+// the surrounding memory operations on their side of the wait.
+__device__ __forceinline__ void wait_mem() {
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);
+  __builtin_amdgcn_s_waitcnt(0);
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);
+}
+__device__ __forceinline__ void compiler_fence() { __atomic_signal_fence(__ATOMIC_SEQ_CST); }
 
 }  // namespace gpuos

@@ -9,9 +9,13 @@
 // the doorbell is a release store of the ring tail that one device wave polls.
 //
 // Tiles of every published descriptor form one dense ticket space per ring:
-// descriptor `seq` owns tickets [ends[seq-1], ends[seq]).  Workers claim
-// tickets in increasing order, so claims follow op order (every tile a wave
-// waits on is already held by a running wave) and each tile runs exactly once.
+// descriptor `seq` owns tickets [ends[seq-1], ends[seq]).  In the best-effort
+// ring, worker wave w runs tickets w, w + W, w + 2W, ... in increasing order
+// (W = worker waves), so each tile runs exactly once without a shared claim
+// counter, and the wave holding the smallest unfinished ticket can always
+// proceed: every tile its op waits on has a smaller ticket and is finished.
+// The latency-critical ring is claimed dynamically (compare-and-swap), so any
+// wave can pick up priority work between its own tiles.
 #pragma once
 
 #include <stddef.h>
@@ -22,8 +26,16 @@ namespace gpuos {
 // Internal opcodes beyond the public ones (gpuos_opcode).
 enum : uint8_t {
   OP_FUSED_EW = 32,  // register-resident elementwise chain
-  OP_STOP = 33,      // one tile per worker wave; a wave that claims one exits
 };
+
+// Completion counting: descriptors with more than kSubCounters tiles count
+// tile t in sub-counter t % kSubCounters; the wave that fills a sub-counter
+// bumps the second-level counter, which completes the descriptor at
+// kSubCounters.  Spreading the increments over 16 addresses keeps one hot
+// address from serialising the end of a large op.
+constexpr uint32_t kSubCounters = 16;
+// Replicas of the published-work words; wave w polls replica w % kReplicas.
+constexpr uint32_t kReplicas = 16;
 
 // Elementwise step codes inside a FUSED_EW micro-program.
 enum : uint8_t {
@@ -47,11 +59,16 @@ constexpr int kMaxSteps = 8;
 constexpr int kMaxFusedInputs = 4;
 constexpr int kRings = 2;      // 0 = best effort (default), 1 = latency critical
 constexpr uint32_t kDescBytes = 256;
+// Largest byte extent of one operand.  Tile bodies address tensors through
+// buffer resources with 32-bit byte offsets; offsets of vectors past the end
+// saturate at this value, which stays out of every resource's range with room
+// for a 16-byte access.
+constexpr uint64_t kMaxExtentBytes = 0xFFF00000ull;
 constexpr uint32_t kDescMagic = 0x9e3779b9u;
 
 // Device descriptor: 256 bytes = 64 dwords; lane i of a wave fetches dword i.
 struct alignas(16) DevDesc {
-  uint8_t opcode;     // dword 0: public opcode or OP_FUSED_EW / OP_STOP
+  uint8_t opcode;     // dword 0: public opcode or OP_FUSED_EW
   uint8_t dtype;      //          gpuos_dtype
   uint8_t flags;      //          GPUOS_FLAG_*
   uint8_t nsteps;     //          FUSED_EW program length
@@ -101,22 +118,28 @@ static_assert(offsetof(DevDesc, tstart) == 60 * 4, "tstart at dword 60");
 static_assert(offsetof(DevDesc, user_ops) == 62 * 4, "user_ops at dword 62");
 static_assert(offsetof(DevDesc, check) == 63 * 4, "check word is dword 63");
 
-// Device-side scheduler state of one ring (device memory).  Hot words sit on
-// their own 256-byte lines.
+// Device-side scheduler state (device memory).  Hot words sit on their own
+// 256-byte lines.
 struct alignas(256) DevRing {
-  uint64_t next;        // ticket counter (ring 0: fetch-add; ring 1: CAS)
+  uint64_t next;        // latency-critical ring: next ticket to claim (CAS)
   uint64_t _p0[31];
-  uint64_t avail_ops;   // descriptors made visible by the doorbell wave
-  uint64_t avail_tiles; // tickets below this value are claimable
-  uint64_t _p1[30];
   uint64_t retired;     // in-order retire cursor
-  uint64_t _p2[31];
+  uint64_t _p1[31];
+};
+
+// One replica of what the doorbell wave has published for a ring.  The
+// doorbell stores avail_ops before avail_tiles; readers load avail_tiles
+// first, so the descriptors below avail_tiles are always within avail_ops.
+struct alignas(256) AvailLine {
+  uint64_t avail_tiles;  // tickets below this value are runnable
+  uint64_t avail_ops;    // descriptors made visible
+  uint64_t stop_ticket;  // ring 0: waves whose next ticket is >= this exit
+  uint64_t _p[29];
 };
 
 struct alignas(256) DevCtl {
   DevRing ring[kRings];
-  uint32_t stop;        // set by the doorbell wave when the host asks to stop
-  uint32_t _p0[63];
+  AvailLine avail[kRings][kReplicas];
 };
 
 // Host-visible control block (pinned host memory, fine-grained).
@@ -126,7 +149,8 @@ struct alignas(256) HostCtl {
   uint64_t completed[kRings]; // device: retire cursor per ring
   uint64_t heartbeat;         // device: doorbell loop iterations
   uint64_t _p1[29];
-  uint64_t stop_seq;          // host: ring-0 sequence of the STOP descriptor
+  uint64_t stop_req;          // host: nonzero asks the kernel to exit once
+                              // every published descriptor has retired
   uint64_t error;             // device: first error code (0 = none)
   uint64_t error_seq;         // device: (ring << 62) | sequence that raised it
   uint64_t _p2[29];
@@ -151,13 +175,18 @@ enum : uint64_t {
 // Everything the resident kernel needs, passed by value.
 struct KArgs {
   const DevDesc* hdesc[kRings];   // pinned host ring (device-visible address)
+  DevDesc* ddesc[kRings];         // device copy of the ring, filled by the
+                                  // doorbell wave before it publishes
   const uint64_t* hends[kRings];  // pinned host: ends[slot] per descriptor
   HostCtl* hctl;                  // pinned host control block
   DevCtl* dctl;                   // device control block
   uint64_t* dends[kRings];        // device copy of ends[], 2 * ring_slots
                                   // entries indexed by (seq - 1) mod 2*slots
   uint64_t* done_id[kRings];      // device: last completed sequence per slot
-  uint32_t* tiles_done[kRings];   // device: tiles finished per slot
+  uint32_t* tiles_done[kRings];   // device: kSubCounters x ring_slots tile
+                                  // counters, sub-counter s of slot at
+                                  // [s * ring_slots + slot]
+  uint32_t* subs_done[kRings];    // device: filled sub-counters per slot
   TraceRec* trace[kRings];        // device trace ring (nullable)
   uint32_t cap_mask;              // ring_slots - 1
   uint32_t ends_mask;             // 2 * ring_slots - 1

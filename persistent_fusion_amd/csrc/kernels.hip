@@ -20,7 +20,21 @@
 
 namespace gpuos {
 
-// Descriptor held in one VGPR: lane i keeps dword i.
+// Cache policies of tensor data in the resident kernel.  Results must be
+// visible to waves on other XCDs once an op completes: stores write through
+// to the device coherence point and loads read it (see device_common.h).
+constexpr int kResidentLoadCP = CP_DEVICE;
+constexpr int kResidentStoreCP = CP_DEVICE;
+// Acquire: invalidate this XCD's L2 before a wave reads a new descriptor's
+// inputs (needed only when loads use the default policy).
+constexpr bool kAcquireInvalidate = false;
+// Release: write back this XCD's L2 after each tile (needed only when stores
+// use the default policy).
+constexpr bool kReleaseWriteback = false;
+
+// Descriptor as just loaded, one dword per lane (lane i keeps dword i).  Read
+// with readlane only where every lane is active (right after the load);
+// everything after that reads the wave's LDS copy.
 struct VDesc {
   uint32_t v;
   __device__ __forceinline__ uint32_t operator()(int i) const {
@@ -31,13 +45,15 @@ struct VDesc {
   }
 };
 
-// Per-wave cache of the descriptor the wave last worked on, per ring.
+// Per-wave cache of the descriptor the wave last worked on, per ring; the
+// descriptor itself is in the wave's LDS slot for that ring.
 struct Cached {
   uint64_t seq;    // 0 = none
   uint64_t start;  // first ticket
   uint64_t end;    // one past the last ticket
-  uint32_t dw;     // this lane's descriptor dword
+  lds_u32* slot;   // 64 dwords
   uint32_t deps_ok;
+  __device__ __forceinline__ SDesc desc() const { return SDesc{slot}; }
 };
 
 __device__ __forceinline__ uint32_t slot_of(uint64_t seq, uint32_t mask) {
@@ -85,65 +101,98 @@ __device__ uint64_t find_seq(const KArgs& a, uint64_t ticket, uint64_t lo, uint6
   return hi;
 }
 
+// Loads descriptor `seq` from the device ring (lane i gets dword i).  The
+// ring slot is read through the caches first; a copy left over from the
+// slot's previous occupant is recognised by its sequence words (the seq field
+// in the first 128-byte line, the check word in the second) and re-read from
+// the device coherence point.
 template <int RING>
 __device__ void fetch_desc(const KArgs& a, uint64_t seq, Cached& c) {
-  const uint32_t* src = reinterpret_cast<const uint32_t*>(&a.hdesc[RING][slot_of(seq, a.cap_mask)]);
-  c.dw = ld_rlx_sys(src + lane_id());
-  VDesc d{c.dw};
+  const rsrc_t r = make_rsrc(reinterpret_cast<uint64_t>(&a.ddesc[RING][slot_of(seq, a.cap_mask)]));
+  const uint32_t off = 4u * lane_id();
+  uint32_t dw = ld32<CP_DEFAULT>(r, off);
+  const VDesc d{dw};
+  if (d.q(4) != seq || d(63) != ((uint32_t)seq ^ kDescMagic)) {
+    dw = ld32<CP_DEVICE>(r, off);
+    const VDesc f{dw};
+    if (f.q(4) != seq || f(63) != ((uint32_t)seq ^ kDescMagic)) report_error(a, RING, seq, DERR_DESC_CHECK);
+  }
+  const VDesc e{dw};
+  c.slot[lane_id()] = dw;
   c.seq = seq;
-  c.start = d.q(60);
-  c.end = c.start + d(6);
+  c.start = e.q(60);
+  c.end = c.start + e(6);
   c.deps_ok = 0;
-  if (d(63) != ((uint32_t)seq ^ kDescMagic)) report_error(a, RING, seq, DERR_DESC_CHECK);
 }
 
+// Waits until every dependency of the cached descriptor has completed.
+// Polls are device-scope loads (coherent without invalidating L2); tensor data
+// is read with device-coherent loads, so no acquire fence is needed after.
 template <int RING>
 __device__ void wait_deps(const KArgs& a, const Cached& c) {
-  VDesc d{c.dw};
+  const SDesc d = c.desc();
   const uint32_t mask = a.cap_mask;
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
     const uint64_t dep = d.q(8 + 2 * i);
     if (dep) {
       const uint64_t* w = &a.done_id[RING][slot_of(dep, mask)];
-      while (bcast64(ld_rlx_agent(w)) < dep) __builtin_amdgcn_s_sleep(2);
+      while (bcast64(ld_rlx_agent(w)) < dep) __builtin_amdgcn_s_sleep(1);
     }
   }
   const uint64_t wr = d.q(16);
   if (wr) {
-    while (bcast64(ld_rlx_agent(&a.dctl->ring[RING].retired)) < wr) __builtin_amdgcn_s_sleep(4);
+    while (bcast64(ld_rlx_agent(&a.dctl->ring[RING].retired)) < wr) __builtin_amdgcn_s_sleep(2);
   }
-  fence_acq_agent();
+  if constexpr (kAcquireInvalidate) fence_acq_agent();
+  compiler_fence();
 }
 
-// Counts one tile done; the wave finishing the last tile publishes the
-// descriptor's completion (done_id) for dependents and the doorbell wave.
+// Counts one tile done; the wave completing the descriptor publishes
+// done_id for dependents and the doorbell wave.  The tile's stores are
+// device-coherent write-through stores, so waiting for their acknowledgement
+// makes them visible on every XCD before the count moves (no L2 writeback).
 template <int RING>
-__device__ void finish_tile(const KArgs& a, const Cached& c, uint64_t t_start) {
+__device__ void finish_tile(const KArgs& a, const Cached& c, uint32_t tile) {
   const uint32_t slot = slot_of(c.seq, a.cap_mask);
-  VDesc d{c.dw};
+  const uint32_t cap = a.cap_mask + 1;
+  const SDesc d = c.desc();
   const uint32_t ntiles = d(6);
-  fence_rel_agent();
-  uint32_t old = 0;
-  if (lane_id() == 0)
-    old = __hip_atomic_fetch_add(&a.tiles_done[RING][slot], 1u, __ATOMIC_RELAXED,
-                                 __HIP_MEMORY_SCOPE_AGENT);
-  old = bcast(old);
-  if (old + 1 == ntiles) {
-    fence_acq_agent();
-    if (lane_id() == 0) {
-      a.tiles_done[RING][slot] = 0;
-      if (a.trace[RING]) {
-        TraceRec* tr = &a.trace[RING][slot];
-        tr->seq = c.seq;
-        tr->t_done = now_ticks();
-        tr->opcode = d(0) & 0xffu;
-        tr->ntiles = ntiles;
-      }
+  if constexpr (kReleaseWriteback) fence_rel_agent();
+  wait_mem();
+  if (lane_id() != 0) return;
+  bool complete;
+  if (ntiles <= kSubCounters) {
+    uint32_t* ctr = &a.tiles_done[RING][slot];
+    const uint32_t old = __hip_atomic_fetch_add(ctr, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    complete = old + 1 == ntiles;
+    if (complete) st_rlx_agent(ctr, 0u);
+  } else {
+    const uint32_t sub = tile % kSubCounters;
+    const uint32_t need = ntiles / kSubCounters + (sub < ntiles % kSubCounters ? 1u : 0u);
+    uint32_t* ctr = &a.tiles_done[RING][sub * cap + slot];
+    const uint32_t old = __hip_atomic_fetch_add(ctr, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    complete = false;
+    if (old + 1 == need) {
+      st_rlx_agent(ctr, 0u);
+      wait_mem();
+      uint32_t* top = &a.subs_done[RING][slot];
+      const uint32_t o2 = __hip_atomic_fetch_add(top, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      complete = o2 + 1 == kSubCounters;
+      if (complete) st_rlx_agent(top, 0u);
     }
-    if (lane_id() == 0) st_rel_agent(&a.done_id[RING][slot], c.seq);
   }
-  (void)t_start;
+  if (complete) {
+    if (a.trace[RING]) {
+      TraceRec* tr = &a.trace[RING][slot];
+      st_rlx_agent(&tr->seq, c.seq);
+      st_rlx_agent(&tr->t_done, now_ticks());
+      st_rlx_agent(&tr->opcode, d(0) & 0xffu);
+      st_rlx_agent(&tr->ntiles, ntiles);
+    }
+    wait_mem();
+    st_rlx_agent(&a.done_id[RING][slot], c.seq);
+  }
 }
 
 template <int RING>
@@ -153,15 +202,15 @@ __device__ void run_ticket(const KArgs& a, uint64_t ticket, Cached& c) {
     c.deps_ok = 1;
   }
   const uint32_t tile = (uint32_t)(ticket - c.start);
-  VDesc d{c.dw};
+  const SDesc d = c.desc();
   if (a.trace[RING] && tile == 0 && lane_id() == 0)
-    a.trace[RING][slot_of(c.seq, a.cap_mask)].t_claim = now_ticks();
-  const uint32_t err = exec_tile(d, tile);
+    st_rlx_agent(&a.trace[RING][slot_of(c.seq, a.cap_mask)].t_claim, now_ticks());
+  const uint32_t err = exec_tile<kResidentLoadCP, kResidentStoreCP>(d, tile);
   if (err) report_error(a, RING, c.seq, err);
-  finish_tile<RING>(a, c, 0);
+  finish_tile<RING>(a, c, tile);
 }
 
-// Maps a claimable ticket to its descriptor (refreshing the cache if needed).
+// Maps a runnable ticket to its descriptor (refreshing the cache if needed).
 template <int RING>
 __device__ void map_ticket(const KArgs& a, uint64_t ticket, uint64_t avail_ops, Cached& c) {
   if (c.seq != 0 && ticket < c.end) return;
@@ -169,20 +218,37 @@ __device__ void map_ticket(const KArgs& a, uint64_t ticket, uint64_t avail_ops, 
   fetch_desc<RING>(a, seq, c);
 }
 
-// Latency-critical ring: claims with compare-and-swap so a wave never holds a
-// priority ticket that has no work behind it.  Priority tiles are drained
-// before the wave returns to its best-effort ticket.
-__device__ void service_lc(const KArgs& a, Cached& c) {
+// Reads a ring's published-work replica: avail_tiles first, then (after the
+// first load has returned) avail_ops, which was stored before it.
+__device__ __forceinline__ void read_avail(const AvailLine* l, uint64_t& tiles, uint64_t& ops) {
+  uint64_t t = 0, o = 0;
+  if (lane_id() == 0) {
+    t = ld_rlx_agent(&l->avail_tiles);
+    wait_mem();
+    o = ld_rlx_agent(&l->avail_ops);
+  }
+  tiles = bcast64(t);
+  ops = bcast64(o);
+}
+
+// Latency-critical ring: tiles are claimed with compare-and-swap so a wave
+// never holds a priority ticket with no work behind it, and every wave drains
+// priority tiles before returning to its own best-effort ticket.  `seen` is
+// the published count at which this wave last found the ring empty.
+__device__ void service_lc(const KArgs& a, const AvailLine* line, Cached& c, uint64_t& seen) {
   DevRing* R = &a.dctl->ring[1];
   for (;;) {
-    uint64_t nxt = 0, av = 0, avops = 0;
-    if (lane_id() == 0) {
-      av = ld_acq_agent(&R->avail_tiles);
-      nxt = ld_rlx_agent(&R->next);
-    }
+    uint64_t av = 0;
+    if (lane_id() == 0) av = ld_rlx_agent(&line->avail_tiles);
     av = bcast64(av);
+    if (av == seen) return;
+    uint64_t nxt = 0;
+    if (lane_id() == 0) nxt = ld_rlx_agent(&R->next);
     nxt = bcast64(nxt);
-    if (nxt >= av) return;
+    if (nxt >= av) {
+      seen = av;
+      return;
+    }
     uint32_t ok = 0;
     if (lane_id() == 0) {
       uint64_t expect = nxt;
@@ -190,81 +256,96 @@ __device__ void service_lc(const KArgs& a, Cached& c) {
                                                 __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)
                ? 1u
                : 0u;
-      avops = ld_acq_agent(&R->avail_ops);
     }
-    ok = bcast(ok);
-    avops = bcast64(avops);
-    if (!ok) continue;
-    map_ticket<1>(a, nxt, avops, c);
+    if (!bcast(ok)) continue;
+    uint64_t tiles, ops;
+    read_avail(line, tiles, ops);
+    map_ticket<1>(a, nxt, ops, c);
     run_ticket<1>(a, nxt, c);
   }
 }
 
-__device__ void worker_loop(const KArgs& a) {
-  DevRing* R = &a.dctl->ring[0];
-  Cached c0{0, 0, 0, 0, 0}, c1{0, 0, 0, 0, 0};
-  uint64_t avail = 0, avail_ops = 0;
+__device__ void worker_loop(const KArgs& a, uint32_t w, lds_u32* slot0, lds_u32* slot1) {
+  const AvailLine* line0 = &a.dctl->avail[0][w % kReplicas];
+  const AvailLine* line1 = &a.dctl->avail[1][w % kReplicas];
+  Cached c0{0, 0, 0, slot0, 0}, c1{0, 0, 0, slot1, 0};
+  uint64_t avail = 0, avail_ops = 0, lc_seen = 0;
   uint32_t idle = 0;
-  uint64_t ticket = 0;
-  if (lane_id() == 0)
-    ticket = __hip_atomic_fetch_add(&R->next, (uint64_t)1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-  ticket = bcast64(ticket);
+  uint64_t ticket = w;
   for (;;) {
-    if (a.lc_enabled) service_lc(a, c1);
+    if (a.lc_enabled) service_lc(a, line1, c1, lc_seen);
     if (ticket >= avail) {
-      uint64_t av = 0, ao = 0;
-      if (lane_id() == 0) {
-        av = ld_acq_agent(&R->avail_tiles);
-        ao = ld_acq_agent(&R->avail_ops);
-      }
-      avail = bcast64(av);
-      avail_ops = bcast64(ao);
+      read_avail(line0, avail, avail_ops);
       if (ticket >= avail) {
+        uint64_t stop = 0;
+        if (lane_id() == 0) stop = ld_rlx_agent(&line0->stop_ticket);
+        if (ticket >= bcast64(stop)) return;
         // nothing published for this ticket yet: back off
-        if (idle < 64) {
+        if (idle < 32) {
           ++idle;
           __builtin_amdgcn_s_sleep(2);
         } else {
-          __builtin_amdgcn_s_sleep(16);
+          __builtin_amdgcn_s_sleep(20);
         }
         continue;
       }
     }
     idle = 0;
     map_ticket<0>(a, ticket, avail_ops, c0);
-    if ((VDesc{c0.dw}(0) & 0xffu) == OP_STOP) {
-      finish_tile<0>(a, c0, 0);
-      return;
-    }
     run_ticket<0>(a, ticket, c0);
-    if (lane_id() == 0)
-      ticket = __hip_atomic_fetch_add(&R->next, (uint64_t)1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    ticket = bcast64(ticket);
+    ticket += a.workers;
   }
 }
 
 // ---------------------------------------------------------------------------
 // doorbell / tracker wave
 
+// Copies descriptors (from, to] from the pinned host ring into the device
+// ring: 16-byte system-scope loads, four descriptors per wave-wide load and
+// up to 32 in flight, written through to the device coherence point.
 template <int RING>
-__device__ bool publish_ring(const KArgs& a, uint64_t tail, uint64_t& avail) {
+__device__ void copy_descs(const KArgs& a, uint64_t from, uint64_t to) {
+  const uint32_t mask = a.cap_mask;
+  const uint32_t lane = lane_id();
+  const rsrc_t hr = make_rsrc(reinterpret_cast<uint64_t>(a.hdesc[RING]));
+  const rsrc_t dr = make_rsrc(reinterpret_cast<uint64_t>(a.ddesc[RING]));
+  const uint32_t sub = lane / 16, part = lane % 16;  // descriptor in group, 16-byte part
+  for (uint64_t s0 = from + 1; s0 <= to; s0 += 32) {
+    u32x4 v[8];
+#pragma unroll
+    for (int g = 0; g < 8; ++g) {
+      const uint64_t s = s0 + 4 * g + sub;
+      if (s <= to) v[g] = ld128<CP_SYSTEM>(hr, slot_of(s, mask) * kDescBytes + 16u * part);
+    }
+#pragma unroll
+    for (int g = 0; g < 8; ++g) {
+      const uint64_t s = s0 + 4 * g + sub;
+      if (s <= to) st128<CP_DEVICE>(dr, slot_of(s, mask) * kDescBytes + 16u * part, v[g]);
+    }
+  }
+}
+
+template <int RING>
+__device__ bool publish_ring(const KArgs& a, uint64_t tail, uint64_t& avail, uint64_t& avail_tiles) {
   if (tail <= avail) return false;
   const uint32_t mask = a.cap_mask;
   const uint32_t lane = lane_id();
+  copy_descs<RING>(a, avail, tail);
   for (uint64_t s0 = avail + 1; s0 <= tail; s0 += 64) {
     const uint64_t s = s0 + lane;
     if (s <= tail)
-      a.dends[RING][slot_of(s, a.ends_mask)] = ld_rlx_sys(&a.hends[RING][slot_of(s, mask)]);
+      st_rlx_agent(&a.dends[RING][slot_of(s, a.ends_mask)], ld_rlx_sys(&a.hends[RING][slot_of(s, mask)]));
   }
   uint64_t end_tiles = 0;
   if (lane == 0) end_tiles = ld_rlx_sys(&a.hends[RING][slot_of(tail, mask)]);
   end_tiles = bcast64(end_tiles);
-  fence_rel_agent();
-  if (lane == 0) {
-    st_rlx_agent(&a.dctl->ring[RING].avail_ops, tail);
-    st_rel_agent(&a.dctl->ring[RING].avail_tiles, end_tiles);
-  }
+  wait_mem();
+  // every replica: avail_ops, then avail_tiles (one replica per lane)
+  if (lane < kReplicas) st_rlx_agent(&a.dctl->avail[RING][lane].avail_ops, tail);
+  wait_mem();
+  if (lane < kReplicas) st_rlx_agent(&a.dctl->avail[RING][lane].avail_tiles, end_tiles);
   avail = tail;
+  avail_tiles = end_tiles;
   return true;
 }
 
@@ -284,41 +365,38 @@ __device__ bool retire_ring(const KArgs& a, uint64_t avail, uint64_t& retired) {
     retired += adv;
     moved = true;
   }
-  if (moved) {
-    fence_acq_agent();
-    if (lane == 0) {
-      st_rel_agent(&a.dctl->ring[RING].retired, retired);
-      st_rel_sys(&a.hctl->completed[RING], retired);
-    }
+  if (moved && lane == 0) {
+    st_rlx_agent(&a.dctl->ring[RING].retired, retired);
+    st_rlx_sys(&a.hctl->completed[RING], retired);
   }
   return moved;
 }
 
 __device__ void doorbell_loop(const KArgs& a) {
-  uint64_t avail0 = 0, avail1 = 0, ret0 = 0, ret1 = 0;
+  uint64_t avail0 = 0, avail1 = 0, ret0 = 0, ret1 = 0, tiles0 = 0, tiles1 = 0;
   uint64_t beats = 0;
   for (;;) {
     uint64_t t0 = 0, t1 = 0, stop = 0;
     if (lane_id() == 0) {
       t0 = ld_rlx_sys(&a.hctl->tail[0]);
       t1 = ld_rlx_sys(&a.hctl->tail[1]);
-      stop = ld_rlx_sys(&a.hctl->stop_seq);
+      stop = ld_rlx_sys(&a.hctl->stop_req);
     }
     t0 = bcast64(t0);
     t1 = bcast64(t1);
     stop = bcast64(stop);
-    fence_acq_sys();
-    bool work = publish_ring<0>(a, t0, avail0);
-    work |= publish_ring<1>(a, t1, avail1);
+    compiler_fence();
+    bool work = publish_ring<0>(a, t0, avail0, tiles0);
+    work |= publish_ring<1>(a, t1, avail1, tiles1);
     work |= retire_ring<0>(a, avail0, ret0);
     work |= retire_ring<1>(a, avail1, ret1);
     ++beats;
     if ((beats & 1023) == 0 && lane_id() == 0) st_rlx_sys(&a.hctl->heartbeat, beats);
-    if (stop && ret0 >= stop) {
-      if (lane_id() == 0) {
-        st_rel_agent(&a.dctl->stop, 1u);
-        st_rel_sys(&a.hctl->heartbeat, beats);
-      }
+    if (stop && ret0 == t0 && ret1 == t1) {
+      // every published descriptor has retired: release the workers
+      if (lane_id() < kReplicas) st_rlx_agent(&a.dctl->avail[0][lane_id()].stop_ticket, tiles0);
+      if (lane_id() == 0) st_rlx_sys(&a.hctl->heartbeat, beats);
+      wait_mem();
       return;
     }
     if (!work) __builtin_amdgcn_s_sleep(1);
@@ -326,11 +404,14 @@ __device__ void doorbell_loop(const KArgs& a) {
 }
 
 __global__ __launch_bounds__(256) void gpuos_resident(KArgs a) {
+  // one descriptor slot per wave and ring
+  __shared__ uint32_t sdesc[4][2][64];
   const uint32_t wave = (blockIdx.x * blockDim.x + threadIdx.x) / 64;
+  const uint32_t wib = threadIdx.x / 64;
   if (wave == 0)
     doorbell_loop(a);
   else
-    worker_loop(a);
+    worker_loop(a, wave - 1, (lds_u32*)&sdesc[wib][0][0], (lds_u32*)&sdesc[wib][1][0]);
 }
 
 // ---------------------------------------------------------------------------
@@ -340,11 +421,14 @@ __global__ __launch_bounds__(256) void gpuos_resident(KArgs a) {
 __global__ __launch_bounds__(256) void gpuos_single(DevDesc d, uint32_t* err) {
   const uint32_t wave = (blockIdx.x * blockDim.x + threadIdx.x) / 64;
   const uint32_t waves = gridDim.x * blockDim.x / 64;
-  // same register layout as the resident kernel: lane i holds dword i
-  const VDesc v{reinterpret_cast<const uint32_t*>(&d)[lane_id()]};
+  // the descriptor goes to this wave's LDS slot, as in the resident kernel
+  __shared__ uint32_t sdesc[4][64];
+  lds_u32* slot = (lds_u32*)&sdesc[threadIdx.x / 64][0];
+  slot[lane_id()] = reinterpret_cast<const uint32_t*>(&d)[lane_id()];
+  const SDesc v{slot};
   const uint32_t ntiles = v(6);
   for (uint32_t t = wave; t < ntiles; t += waves) {
-    const uint32_t e = exec_tile(v, t);
+    const uint32_t e = exec_tile<CP_DEFAULT, CP_DEFAULT>(v, t);
     if (e && lane_id() == 0 && err) *err = e;
   }
 }
@@ -357,7 +441,7 @@ hipError_t launch_resident(const KArgs& a, uint32_t blocks, hipStream_t s) {
 hipError_t launch_single(const DevDesc& d, uint32_t* err, hipStream_t s) {
   uint32_t waves = d.ntiles;
   uint32_t blocks = (waves + 3) / 4;
-  if (blocks > 8192) blocks = 8192;
+  if (blocks > 16384) blocks = 16384;
   if (blocks == 0) blocks = 1;
   hipLaunchKernelGGL(gpuos_single, dim3(blocks), dim3(256), 0, s, d, err);
   return hipGetLastError();

@@ -201,8 +201,8 @@ int validate(const gpuos_op& o, uint32_t index) {
   if ((rc = need(o.in[0], "in[0]"))) return rc;
   if ((rc = align(o.out, es, "out"))) return rc;
   if ((rc = align(o.in[0], es, "in[0]"))) return rc;
-  if (o.src_len[0] > 0xffffffffull || o.src_len[1] > 0xffffffffull)
-    return fail(GPUOS_EINVAL, "op %u: src_len beyond 2^32", index);
+  if (o.src_len[0] > (1ull << 30) || o.src_len[1] > (1ull << 30) || o.n > (1u << 30))
+    return fail(GPUOS_EINVAL, "op %u: n and src_len are limited to 2^30 elements", index);
   if (is_binary(op)) {
     if ((rc = need(o.in[1], "in[1]"))) return rc;
     if ((rc = align(o.in[1], es, "in[1]"))) return rc;
@@ -253,6 +253,13 @@ int validate(const gpuos_op& o, uint32_t index) {
     default:
       break;
   }
+  // the kernels address every operand with 32-bit byte offsets
+  const OpRanges R = op_ranges(o);
+  if (R.w.hi - R.w.lo > kMaxExtentBytes)
+    return fail(GPUOS_EINVAL, "op %u: output spans more than 4 GiB - 1 MiB", index);
+  for (int q = 0; q < R.nr; ++q)
+    if (R.r[q].hi - R.r[q].lo > kMaxExtentBytes)
+      return fail(GPUOS_EINVAL, "op %u: an operand spans more than 4 GiB - 1 MiB", index);
   return 0;
 }
 
@@ -372,9 +379,11 @@ struct gpuos_ctx {
   uint64_t* hends[kRings] = {nullptr, nullptr};
   // device memory
   DevCtl* dctl = nullptr;
+  DevDesc* ddesc[kRings] = {nullptr, nullptr};
   uint64_t* dends[kRings] = {nullptr, nullptr};
   uint64_t* done_id[kRings] = {nullptr, nullptr};
   uint32_t* tiles_done[kRings] = {nullptr, nullptr};
+  uint32_t* subs_done[kRings] = {nullptr, nullptr};
   TraceRec* trace[kRings] = {nullptr, nullptr};
 
   // host bookkeeping
@@ -457,17 +466,23 @@ uint32_t ring_of_id(gpuos_ctx* c, uint64_t id, bool* known) {
 
 uint32_t ceil_div(uint64_t a, uint64_t b) { return (uint32_t)((a + b - 1) / b); }
 
-// Elementwise tile: cfg.tile_elems, or be_tile_elems for very large ops.
-// Large ops get a tile count that is a multiple of the worker count so the
-// last round of tiles does not leave most waves idle.
+// Elementwise tile: cfg.tile_elems, or be_tile_elems for ops of 2^24
+// elements or more.  Large ops are cut into whole rounds over the worker
+// waves (every wave gets the same number of tiles) and an op big enough to
+// give every wave 1024 elements is spread over all of them.  Tiles stay a
+// multiple of 64 elements so every tile starts 16-byte aligned.
 uint32_t ew_tile_elems(const gpuos_config& cfg, uint32_t workers, uint64_t n) {
   uint64_t tile = n >= (1ull << 24) ? cfg.be_tile_elems : cfg.tile_elems;
-  const uint64_t nt = (n + tile - 1) / tile;
-  if (workers && nt > workers) {
-    const uint64_t rounds = (nt + workers - 1) / workers;
-    uint64_t t2 = (n + rounds * workers - 1) / (rounds * workers);
-    t2 = (t2 + 255) / 256 * 256;
-    if (t2 >= 256 && t2 <= tile) tile = t2;
+  uint64_t nt = (n + tile - 1) / tile;
+  if (workers) {
+    if (nt < workers) {
+      if (n >= (uint64_t)workers * 1024) nt = workers;
+    } else {
+      nt = (nt + workers - 1) / workers * workers;
+    }
+    uint64_t t2 = (n + nt - 1) / nt;
+    t2 = (t2 + 63) / 64 * 64;
+    if (t2 >= 64) tile = t2;
   }
   return (uint32_t)tile;
 }
@@ -575,7 +590,10 @@ uint8_t fuse_code(uint32_t op) {
 
 bool fusable(const gpuos_op& o) {
   if (!fuse_code(o.opcode)) return false;
-  if (o.dtype == GPUOS_I32) return false;
+  // fp32 chains only: a bf16 chain would re-round after every step in
+  // registers, and its register footprint would cap the resident kernel's
+  // occupancy for every other op
+  if (o.dtype != GPUOS_F32) return false;
   if (o.src_len[0] && o.src_len[0] < o.n) return false;
   if (is_binary(o.opcode) && o.src_len[1] && o.src_len[1] < o.n) return false;
   return true;
@@ -887,9 +905,11 @@ void free_all(gpuos_ctx* c) {
   if (!c->host_only) {
     (void)hipFree(c->dctl);
     for (int r = 0; r < kRings; ++r) {
+      (void)hipFree(c->ddesc[r]);
       (void)hipFree(c->dends[r]);
       (void)hipFree(c->done_id[r]);
       (void)hipFree(c->tiles_done[r]);
+      (void)hipFree(c->subs_done[r]);
       (void)hipFree(c->trace[r]);
     }
     if (c->ev_start) (void)hipEventDestroy(c->ev_start);
@@ -916,6 +936,7 @@ int apply_config(const gpuos_config* in, gpuos_config& out) {
   if (in->trace) out.trace = in->trace;
   if (in->block_on_full) out.block_on_full = in->block_on_full;
   if (in->max_fuse) out.max_fuse = in->max_fuse;
+  if (in->priority) out.priority = in->priority;
   const uint32_t rs = out.ring_slots;
   if (rs < 64 || rs > (1u << 18) || (rs & (rs - 1)))
     return fail(GPUOS_EINVAL, "ring_slots must be a power of two in [64, 2^18]");
@@ -925,7 +946,8 @@ int apply_config(const gpuos_config* in, gpuos_config& out) {
     return fail(GPUOS_EINVAL, "tile_elems must be a multiple of 256 in [256, 2^22]");
   if (out.be_tile_elems < 256 || out.be_tile_elems % 256 || out.be_tile_elems > (1u << 22))
     return fail(GPUOS_EINVAL, "be_tile_elems must be a multiple of 256 in [256, 2^22]");
-  if (out.fusion > 2 || out.auto_deps > 2 || out.trace > 2 || out.block_on_full > 2)
+  if (out.fusion > 2 || out.auto_deps > 2 || out.trace > 2 || out.block_on_full > 2 ||
+      out.priority > 2)
     return fail(GPUOS_EINVAL, "switch fields take 1 (on) or 2 (off)");
   if (out.max_fuse < 2 || out.max_fuse > (uint32_t)kMaxSteps)
     return fail(GPUOS_EINVAL, "max_fuse must be in [2, 8]");
@@ -1005,6 +1027,7 @@ void gpuos_config_default(gpuos_config* cfg) {
   cfg->trace = 2;
   cfg->block_on_full = 1;
   cfg->max_fuse = 8;
+  cfg->priority = 1;
 }
 
 int gpuos_create(int device, const gpuos_config* cfg_in, gpuos_ctx** out) {
@@ -1071,19 +1094,30 @@ int gpuos_create(int device, const gpuos_config* cfg_in, gpuos_ctx** out) {
     };
     rc = dalloc((void**)&c->dctl, sizeof(DevCtl));
     for (int r = 0; r < kRings && !rc; ++r) {
-      rc = dalloc((void**)&c->dends[r], (size_t)2 * c->cap * sizeof(uint64_t));
+      rc = dalloc((void**)&c->ddesc[r], (size_t)c->cap * sizeof(DevDesc));
+      if (!rc) rc = dalloc((void**)&c->dends[r], (size_t)2 * c->cap * sizeof(uint64_t));
       if (!rc) rc = dalloc((void**)&c->done_id[r], (size_t)c->cap * sizeof(uint64_t));
-      if (!rc) rc = dalloc((void**)&c->tiles_done[r], (size_t)c->cap * sizeof(uint32_t));
+      if (!rc) rc = dalloc((void**)&c->tiles_done[r], (size_t)kSubCounters * c->cap * sizeof(uint32_t));
+      if (!rc) rc = dalloc((void**)&c->subs_done[r], (size_t)c->cap * sizeof(uint32_t));
       if (!rc && cfg.trace == 1) rc = dalloc((void**)&c->trace[r], (size_t)c->cap * sizeof(TraceRec));
     }
     hipError_t e = hipSuccess;
     if (!rc) e = hipStreamCreateWithFlags(&c->stream, hipStreamNonBlocking);
     if (!rc && e == hipSuccess) {
-      e = hipMemsetAsync(c->dctl, 0, sizeof(DevCtl), c->stream);
+      // control block: zeros, except that no wave may stop yet
+      auto* img = new DevCtl();
+      memset(img, 0, sizeof *img);
+      for (int r = 0; r < kRings; ++r)
+        for (uint32_t k = 0; k < kReplicas; ++k) img->avail[r][k].stop_ticket = ~0ull;
+      e = hipMemcpy(c->dctl, img, sizeof(DevCtl), hipMemcpyHostToDevice);
+      delete img;
       for (int r = 0; r < kRings && e == hipSuccess; ++r) {
         e = hipMemsetAsync(c->dends[r], 0, (size_t)2 * c->cap * sizeof(uint64_t), c->stream);
+        if (e == hipSuccess) e = hipMemsetAsync(c->ddesc[r], 0, (size_t)c->cap * sizeof(DevDesc), c->stream);
         if (e == hipSuccess) e = hipMemsetAsync(c->done_id[r], 0, (size_t)c->cap * 8, c->stream);
-        if (e == hipSuccess) e = hipMemsetAsync(c->tiles_done[r], 0, (size_t)c->cap * 4, c->stream);
+        if (e == hipSuccess)
+          e = hipMemsetAsync(c->tiles_done[r], 0, (size_t)kSubCounters * c->cap * 4, c->stream);
+        if (e == hipSuccess) e = hipMemsetAsync(c->subs_done[r], 0, (size_t)c->cap * 4, c->stream);
         if (e == hipSuccess && c->trace[r])
           e = hipMemsetAsync(c->trace[r], 0, (size_t)c->cap * sizeof(TraceRec), c->stream);
       }
@@ -1093,9 +1127,11 @@ int gpuos_create(int device, const gpuos_config* cfg_in, gpuos_ctx** out) {
       for (int r = 0; r < kRings; ++r) {
         a.hdesc[r] = (const DevDesc*)dev_ptr(c->hdesc[r]);
         a.hends[r] = (const uint64_t*)dev_ptr(c->hends[r]);
+        a.ddesc[r] = c->ddesc[r];
         a.dends[r] = c->dends[r];
         a.done_id[r] = c->done_id[r];
         a.tiles_done[r] = c->tiles_done[r];
+        a.subs_done[r] = c->subs_done[r];
         a.trace[r] = c->trace[r];
       }
       a.hctl = (HostCtl*)dev_ptr(c->hctl);
@@ -1103,7 +1139,7 @@ int gpuos_create(int device, const gpuos_config* cfg_in, gpuos_ctx** out) {
       a.cap_mask = c->cap - 1;
       a.ends_mask = 2 * c->cap - 1;
       a.workers = c->workers;
-      a.lc_enabled = 1;
+      a.lc_enabled = cfg.priority == 1 ? 1u : 0u;
       e = hipEventCreate(&c->ev_start);
       if (e == hipSuccess) e = hipEventCreate(&c->ev_end);
       if (e == hipSuccess) e = hipEventRecord(c->ev_start, c->stream);
@@ -1141,6 +1177,8 @@ int gpuos_submit(gpuos_ctx* c, const gpuos_op* ops, uint32_t n, uint64_t* ids_ou
     }
     // explicit dependencies must stay in the op's ring
     const uint32_t ring = (ops[i].flags & GPUOS_FLAG_LC) ? 1 : 0;
+    if (ring == 1 && c->cfg.priority != 1)
+      return fail(GPUOS_EINVAL, "op %u: latency-critical op on a context without the priority ring", i);
     for (int k = 0; k < 4; ++k) {
       const int64_t dv = ops[i].deps[k];
       if (dv < 0) {
@@ -1278,33 +1316,9 @@ int gpuos_stop(gpuos_ctx* c, int64_t timeout_ns) {
     }
     c->staged.clear();
     c->stopped = true;
-    // STOP: one tile per worker wave; each wave that claims one exits
-    const uint64_t seq = c->pub_seq[0] + 1;
-    const auto t0 = std::chrono::steady_clock::now();
-    while (seq > c->cap && seq - c->cap > completed_of(c, 0)) {
-      // only reachable after a timed-out drain: wait, bounded, for a slot
-      std::this_thread::yield();
-      if (timeout_ns >= 0 &&
-          std::chrono::steady_clock::now() - t0 > std::chrono::nanoseconds(timeout_ns)) {
-        c->leaked = true;
-        return fail(GPUOS_ETIMEDOUT, "ring never drained; resident kernel left running");
-      }
-    }
-    DevDesc d;
-    memset(&d, 0, sizeof d);
-    d.opcode = OP_STOP;
-    d.ntiles = c->workers;
-    d.tile = 1;
-    d.seq = seq;
-    d.check = (uint32_t)seq ^ kDescMagic;
-    d.tstart = c->pub_tiles[0];
-    memcpy(&c->hdesc[0][(seq - 1) & (c->cap - 1)], &d, sizeof d);
-    c->hends[0][(seq - 1) & (c->cap - 1)] = c->pub_tiles[0] + d.ntiles;
-    c->pub_tiles[0] += d.ntiles;
-    c->pub_seq[0] = seq;
+    // every published descriptor retires before the kernel lets its waves go
     std::atomic_thread_fence(std::memory_order_release);
-    store_rel(&c->hctl->stop_seq, seq);
-    publish_tail(c, 0);
+    store_rel(&c->hctl->stop_req, 1);
   }
   // wait for the kernel to exit
   const auto t0 = std::chrono::steady_clock::now();
@@ -1373,7 +1387,7 @@ int gpuos_baseline_run(int device, const gpuos_op* ops, uint32_t n, int fuse, vo
   tmp.host_only = true;
   gpuos_config_default(&tmp.cfg);
   tmp.cfg.fusion = fuse ? 1 : 2;
-  tmp.workers = cached_cus * 8;
+  tmp.workers = cached_cus * 16;
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
   if (!fuse) {
     DevDesc d;

@@ -1,14 +1,22 @@
 // Tile bodies of the op table, shared by the resident kernel and the per-op
 // launch comparator.  A body runs on one wave64 and processes one tile of one
 // descriptor; `d(i)` returns dword i of the descriptor (uniform), `d.q(i)` the
-// 64-bit value at dwords i, i+1.
+// 64-bit value at dwords i, i+1.  The descriptor sits in the wave's LDS slot
+// and every field read is an LDS load made uniform with readfirstlane, which
+// is correct under any set of active lanes (a lane-indexed register copy read
+// with readlane is not: inside a divergent region the inactive lanes of a
+// reloaded register hold stale values).  CPL / CPS are the cache policies of tensor
+// access: CPL for loads, CPS for stores (device-coherent in the resident
+// kernel, default in the comparator).
 //
-// Memory-bound ops stream with 128-bit loads and stores (4 fp32 or 8 bf16 per
-// lane); reductions keep a row in registers and reduce across the wave.  No op
-// here is a dense contraction (batch-1 GEMV moves ~2 bytes per flop), so
-// nothing uses MFMA.  Exact-class ops (COPY, GATHER, ADD, MUL, SCALE, RELU,
-// ROPE) are single IEEE operations per element; the library is compiled with
-// contraction off so a*b+c is never fused into an FMA.
+// Memory-bound ops stream with 128-bit accesses (4 fp32 or 8 bf16 per lane)
+// and keep several loads in flight per lane; reductions sweep a row with the
+// whole wave and reduce across lanes.  No op here is a dense contraction
+// (batch-1 GEMV moves ~2 bytes per flop), so nothing uses MFMA.  Exact-class
+// ops (COPY, GATHER, ADD, MUL, SCALE, RELU, ROPE) are single IEEE operations
+// per element; the library is compiled with contraction off so a*b+c is never
+// fused into an FMA.  Tensor byte offsets fit in 32 bits (checked on the
+// host).
 #pragma once
 
 #include "device_common.h"
@@ -17,31 +25,57 @@
 
 namespace gpuos {
 
+typedef __attribute__((address_space(3))) uint32_t lds_u32;
+
+// The 64 dwords of a descriptor in LDS.
+struct SDesc {
+  const lds_u32* p;
+  __device__ __forceinline__ uint32_t operator()(int i) const {
+    return (uint32_t)__builtin_amdgcn_readfirstlane((int)p[i]);
+  }
+  __device__ __forceinline__ uint64_t q(int i) const {
+    return (uint64_t)(*this)(i) | ((uint64_t)(*this)(i + 1) << 32);
+  }
+};
+
 // ---------------------------------------------------------------------------
 // element types
 
-template <int DT>
+template <int DT, int CPL, int CPS>
 struct DTr;
 
-template <>
-struct DTr<GPUOS_F32> {
-  static constexpr int V = 4;  // elements per 16-byte access
-  __device__ static __forceinline__ float ld(uint64_t p, uint32_t i) {
-    return ldg<float>(p + 4ull * i);
+template <int CPL, int CPS>
+struct DTr<GPUOS_F32, CPL, CPS> {
+  static constexpr int V = 4;   // elements per 16-byte access
+  static constexpr int ES = 4;  // bytes per element
+  __device__ static __forceinline__ float ld(rsrc_t r, uint32_t i) {
+    return __uint_as_float(ld32<CPL>(r, 4u * i));
   }
-  __device__ static __forceinline__ void st(uint64_t p, uint32_t i, float v) {
-    stg<float>(p + 4ull * i, v);
+  __device__ static __forceinline__ void st(rsrc_t r, uint32_t i, float v) {
+    st32<CPS>(r, 4u * i, __float_as_uint(v));
   }
-  __device__ static __forceinline__ void ldv(uint64_t p, uint32_t i, float (&x)[4]) {
-    const u32x4 t = ldg<u32x4>(p + 4ull * i);
+  __device__ static __forceinline__ void ldv(rsrc_t r, uint32_t i, float (&x)[4]) {
+    const u32x4 t = ld128<CPL>(r, 4u * i);
     x[0] = __uint_as_float(t.x); x[1] = __uint_as_float(t.y);
     x[2] = __uint_as_float(t.z); x[3] = __uint_as_float(t.w);
   }
-  __device__ static __forceinline__ void stv(uint64_t p, uint32_t i, const float (&x)[4]) {
+  __device__ static __forceinline__ void stv(rsrc_t r, uint32_t i, const float (&x)[4]) {
     u32x4 t;
     t.x = __float_as_uint(x[0]); t.y = __float_as_uint(x[1]);
     t.z = __float_as_uint(x[2]); t.w = __float_as_uint(x[3]);
-    stg<u32x4>(p + 4ull * i, t);
+    st128<CPS>(r, 4u * i, t);
+  }
+  // 16-byte vector q (elements 4q .. 4q + 3)
+  __device__ static __forceinline__ void ldq(rsrc_t r, uint32_t q, float (&x)[4]) {
+    const u32x4 t = ld128<CPL>(r, vec_off(q));
+    x[0] = __uint_as_float(t.x); x[1] = __uint_as_float(t.y);
+    x[2] = __uint_as_float(t.z); x[3] = __uint_as_float(t.w);
+  }
+  __device__ static __forceinline__ void stq(rsrc_t r, uint32_t q, const float (&x)[4]) {
+    u32x4 t;
+    t.x = __float_as_uint(x[0]); t.y = __float_as_uint(x[1]);
+    t.z = __float_as_uint(x[2]); t.w = __float_as_uint(x[3]);
+    st128<CPS>(r, vec_off(q), t);
   }
   __device__ static __forceinline__ float round(float v) { return v; }
 };
@@ -53,25 +87,38 @@ __device__ __forceinline__ void unpack_bf16x8(const u32x4& t, float (&w)[8]) {
   w[6] = bf2f(t.w & 0xffffu); w[7] = bf2f(t.w >> 16);
 }
 
-template <>
-struct DTr<GPUOS_BF16> {
+template <int CPL, int CPS>
+struct DTr<GPUOS_BF16, CPL, CPS> {
   static constexpr int V = 8;
-  __device__ static __forceinline__ float ld(uint64_t p, uint32_t i) {
-    return bf2f(ldg<uint16_t>(p + 2ull * i));
+  static constexpr int ES = 2;
+  __device__ static __forceinline__ float ld(rsrc_t r, uint32_t i) {
+    return bf2f(ld16<CPL>(r, 2u * i));
   }
-  __device__ static __forceinline__ void st(uint64_t p, uint32_t i, float v) {
-    stg<uint16_t>(p + 2ull * i, (uint16_t)f2bf(v));
+  __device__ static __forceinline__ void st(rsrc_t r, uint32_t i, float v) {
+    st16<CPS>(r, 2u * i, (uint16_t)f2bf(v));
   }
-  __device__ static __forceinline__ void ldv(uint64_t p, uint32_t i, float (&x)[8]) {
-    unpack_bf16x8(ldg<u32x4>(p + 2ull * i), x);
+  __device__ static __forceinline__ void ldv(rsrc_t r, uint32_t i, float (&x)[8]) {
+    unpack_bf16x8(ld128<CPL>(r, 2u * i), x);
   }
-  __device__ static __forceinline__ void stv(uint64_t p, uint32_t i, const float (&x)[8]) {
+  __device__ static __forceinline__ void stv(rsrc_t r, uint32_t i, const float (&x)[8]) {
     u32x4 t;
     t.x = f2bf(x[0]) | (f2bf(x[1]) << 16);
     t.y = f2bf(x[2]) | (f2bf(x[3]) << 16);
     t.z = f2bf(x[4]) | (f2bf(x[5]) << 16);
     t.w = f2bf(x[6]) | (f2bf(x[7]) << 16);
-    stg<u32x4>(p + 2ull * i, t);
+    st128<CPS>(r, 2u * i, t);
+  }
+  // 16-byte vector q (elements 8q .. 8q + 7)
+  __device__ static __forceinline__ void ldq(rsrc_t r, uint32_t q, float (&x)[8]) {
+    unpack_bf16x8(ld128<CPL>(r, vec_off(q)), x);
+  }
+  __device__ static __forceinline__ void stq(rsrc_t r, uint32_t q, const float (&x)[8]) {
+    u32x4 t;
+    t.x = f2bf(x[0]) | (f2bf(x[1]) << 16);
+    t.y = f2bf(x[2]) | (f2bf(x[3]) << 16);
+    t.z = f2bf(x[4]) | (f2bf(x[5]) << 16);
+    t.w = f2bf(x[6]) | (f2bf(x[7]) << 16);
+    st128<CPS>(r, vec_off(q), t);
   }
   // value after a round trip through bf16 storage
   __device__ static __forceinline__ float round(float v) { return bf2f(f2bf(v)); }
@@ -98,115 +145,112 @@ constexpr bool ew_binary() {
   return OP == GPUOS_OP_ADD || OP == GPUOS_OP_MUL || OP == GPUOS_OP_SILU_MUL;
 }
 
-// Elements [lo, hi) of tile t of an elementwise op.
-template <class D>
-__device__ __forceinline__ void tile_range(const D& d, uint32_t t, uint32_t& lo, uint32_t& hi) {
-  const uint32_t n = d(1), tile = d(7);
-  lo = t * tile;
-  hi = lo + tile < n ? lo + tile : n;
-}
-
-template <int OP, int DT, class D>
-__device__ __forceinline__ void ew_tile(const D& d, uint32_t t) {
-  using T = DTr<DT>;
+// Elementwise tiles are interleaved: the op's whole 16-byte vectors form
+// rows of 64 (one per lane), and tile t of T takes rows t, t + T, t + 2T, ...
+// so at any moment the waves of a large op sweep adjacent memory together
+// (DRAM-friendly, like a grid-stride loop), U rows per wave in flight.  The
+// n % V leftover elements belong to the last tile.  A source read
+// cyclically, or a misaligned operand, uses the per-element path with the
+// same interleaving.
+template <int OP, int DT, int CPL, int CPS, class D>
+__device__ __attribute__((noinline)) void ew_tile(D d, uint32_t t) {
+  using T = DTr<DT, CPL, CPS>;
   constexpr int V = T::V;
   constexpr bool BIN = ew_binary<OP>();
   constexpr int U = DT == GPUOS_F32 ? 4 : 2;
-  uint32_t lo, hi;
-  tile_range(d, t, lo, hi);
-  const uint64_t out = d.q(18), a = d.q(20), b = d.q(22);
+  const uint32_t n = d(1), ntiles = d(6);
+  const rsrc_t out = make_rsrc(d.q(18)), a = make_rsrc(d.q(20)), b = make_rsrc(d.q(22));
   const uint32_t ca = d(26), cb = d(27);
   const float alpha = __uint_as_float(d(28));
   const uint32_t lane = lane_id();
-  const bool fast = ca == 0 && (!BIN || cb == 0) && aligned16(out) && aligned16(a) &&
-                    (!BIN || aligned16(b));
-  uint32_t vend = lo;
+  const bool fast = ca == 0 && (!BIN || cb == 0) && aligned16(d.q(18)) && aligned16(d.q(20)) &&
+                    (!BIN || aligned16(d.q(22)));
   if (fast) {
-    vend = lo + ((hi - lo) / V) * V;
-    for (uint32_t base = lo; base < vend; base += 64 * V * U) {
+    // whole vectors only; rows past the end fall outside the resources
+    const uint32_t nv = n / V, nrows = (nv + 63) / 64;
+    const rsrc_t vo = make_rsrc_n(d.q(18), nv * 16u), va = make_rsrc_n(d.q(20), nv * 16u);
+    const rsrc_t vb = make_rsrc_n(BIN ? d.q(22) : 0, nv * 16u);
+    for (uint32_t row = t; row < nrows; row += U * ntiles) {
       float x[U][V], y[U][V];
 #pragma unroll
       for (int u = 0; u < U; ++u) {
-        const uint32_t i = base + (u * 64 + lane) * V;
-        if (i < vend) {
-          T::ldv(a, i, x[u]);
-          if constexpr (BIN) T::ldv(b, i, y[u]);
-        }
+        const uint32_t q = (row + u * ntiles) * 64 + lane;
+        T::ldq(va, q, x[u]);
+        if constexpr (BIN) T::ldq(vb, q, y[u]);
       }
 #pragma unroll
       for (int u = 0; u < U; ++u) {
-        const uint32_t i = base + (u * 64 + lane) * V;
-        if (i < vend) {
-          float r[V];
+        const uint32_t q = (row + u * ntiles) * 64 + lane;
+        float r[V];
 #pragma unroll
-          for (int e = 0; e < V; ++e) r[e] = ew_apply<OP>(x[u][e], BIN ? y[u][e] : 0.0f, alpha);
-          T::stv(out, i, r);
-        }
+        for (int e = 0; e < V; ++e) r[e] = ew_apply<OP>(x[u][e], BIN ? y[u][e] : 0.0f, alpha);
+        T::stq(vo, q, r);
       }
     }
+    if (t + 1 == ntiles) {
+      for (uint32_t i = nv * V + lane; i < n; i += 64) {
+        const float y = BIN ? T::ld(b, i) : 0.0f;
+        T::st(out, i, ew_apply<OP>(T::ld(a, i), y, alpha));
+      }
+    }
+    return;
   }
-  for (uint32_t i = vend + lane; i < hi; i += 64) {
+  for (uint32_t i = t * 64 + lane; i < n; i += 64 * ntiles) {
     const float x = T::ld(a, ca ? i % ca : i);
     const float y = BIN ? T::ld(b, cb ? i % cb : i) : 0.0f;
     T::st(out, i, ew_apply<OP>(x, y, alpha));
   }
 }
 
-template <int ES>
-__device__ __forceinline__ void copy_elem(uint64_t dst, uint64_t src) {
+template <int ES, int CPL, int CPS>
+__device__ __forceinline__ void copy_elem(rsrc_t dst, uint32_t i, rsrc_t src, uint32_t j) {
   if constexpr (ES == 4)
-    stg<uint32_t>(dst, ldg<uint32_t>(src));
+    st32<CPS>(dst, 4u * i, ld32<CPL>(src, 4u * j));
   else
-    stg<uint16_t>(dst, ldg<uint16_t>(src));
+    st16<CPS>(dst, 2u * i, ld16<CPL>(src, 2u * j));
 }
 
-// Bit copy of elements of ES bytes, with cyclic source.
-template <int ES, class D>
-__device__ __forceinline__ void copy_tile(const D& d, uint32_t t) {
-  uint32_t lo, hi;
-  tile_range(d, t, lo, hi);
-  const uint64_t out = d.q(18), a = d.q(20);
+// Bit copy of elements of ES bytes, with cyclic source (interleaved tiles).
+template <int ES, int CPL, int CPS, class D>
+__device__ __attribute__((noinline)) void copy_tile(D d, uint32_t t) {
+  const uint32_t n = d(1), ntiles = d(6);
+  const rsrc_t out = make_rsrc(d.q(18)), a = make_rsrc(d.q(20));
   const uint32_t ca = d(26);
   const uint32_t lane = lane_id();
   constexpr int V = 16 / ES;
-  uint32_t vend = lo;
-  if (ca == 0 && aligned16(out) && aligned16(a)) {
-    vend = lo + ((hi - lo) / V) * V;
-    for (uint32_t base = lo; base < vend; base += 64 * V * 4) {
-      u32x4 v[4];
+  constexpr int U = 4;
+  if (ca == 0 && aligned16(d.q(18)) && aligned16(d.q(20))) {
+    const uint32_t nv = n / V, nrows = (nv + 63) / 64;
+    const rsrc_t vo = make_rsrc_n(d.q(18), nv * 16u), va = make_rsrc_n(d.q(20), nv * 16u);
+    for (uint32_t row = t; row < nrows; row += U * ntiles) {
+      u32x4 v[U];
 #pragma unroll
-      for (int u = 0; u < 4; ++u) {
-        const uint32_t i = base + (u * 64 + lane) * V;
-        if (i < vend) v[u] = ldg<u32x4>(a + (uint64_t)i * ES);
-      }
+      for (int u = 0; u < U; ++u) v[u] = ld128<CPL>(va, vec_off((row + u * ntiles) * 64 + lane));
 #pragma unroll
-      for (int u = 0; u < 4; ++u) {
-        const uint32_t i = base + (u * 64 + lane) * V;
-        if (i < vend) stg<u32x4>(out + (uint64_t)i * ES, v[u]);
-      }
+      for (int u = 0; u < U; ++u) st128<CPS>(vo, vec_off((row + u * ntiles) * 64 + lane), v[u]);
     }
+    if (t + 1 == ntiles)
+      for (uint32_t i = nv * V + lane; i < n; i += 64) copy_elem<ES, CPL, CPS>(out, i, a, i);
+    return;
   }
-  for (uint32_t i = vend + lane; i < hi; i += 64) {
-    const uint32_t j = ca ? i % ca : i;
-    copy_elem<ES>(out + (uint64_t)i * ES, a + (uint64_t)j * ES);
-  }
+  for (uint32_t i = t * 64 + lane; i < n; i += 64 * ntiles)
+    copy_elem<ES, CPL, CPS>(out, i, a, ca ? i % ca : i);
 }
 
 // out[k] = x[idx[k]]; returns an error code if any index is out of range.
-template <int ES, class D>
-__device__ __forceinline__ uint32_t gather_tile(const D& d, uint32_t t) {
-  uint32_t lo, hi;
-  tile_range(d, t, lo, hi);
-  const uint64_t out = d.q(18), x = d.q(20), idx = d.q(24);
+template <int ES, int CPL, int CPS, class D>
+__device__ __attribute__((noinline)) uint32_t gather_tile(D d, uint32_t t) {
+  const uint32_t n = d(1), ntiles = d(6);
+  const rsrc_t out = make_rsrc(d.q(18)), x = make_rsrc(d.q(20)), idx = make_rsrc(d.q(24));
   const int64_t bound = (int64_t)d(26);
   bool bad = false;
-  for (uint32_t i = lo + lane_id(); i < hi; i += 64) {
-    const int32_t j = ldg<int32_t>(idx + 4ull * i);
+  for (uint32_t i = t * 64 + lane_id(); i < n; i += 64 * ntiles) {
+    const int32_t j = (int32_t)ld32<CPL>(idx, 4u * i);
     if (j < 0 || (int64_t)j >= bound) {
       bad = true;
       continue;
     }
-    copy_elem<ES>(out + (uint64_t)i * ES, x + (uint64_t)j * ES);
+    copy_elem<ES, CPL, CPS>(out, i, x, (uint32_t)j);
   }
   return ballot(bad) ? (uint32_t)DERR_GATHER_RANGE : 0u;
 }
@@ -245,75 +289,110 @@ __device__ __forceinline__ void fused_step(uint32_t op, uint32_t fl, float scal,
   }
 }
 
-template <int DT, class D>
-__device__ __forceinline__ void fused_tile(const D& d, uint32_t t) {
-  using T = DTr<DT>;
-  constexpr int V = T::V;
-  constexpr int U = DT == GPUOS_F32 ? 2 : 1;
-  uint32_t lo, hi;
-  tile_range(d, t, lo, hi);
-  const uint32_t nsteps = d(0) >> 24;
-  const uint64_t in0 = d.q(18), in1 = d.q(20), in2 = d.q(22), in3 = d.q(24);
-  bool fast = aligned16(in0) && aligned16(in1) && aligned16(in2) && aligned16(in3);
+// The step program of a fused descriptor, read once per tile.
+struct FusedProg {
+  uint32_t nsteps;
+  uint32_t ops[2], fls[2];  // one byte per step
+  uint32_t scal[kMaxSteps];
+  uint64_t out[kMaxSteps];
+  __device__ __forceinline__ uint32_t op(int s) const { return (ops[s / 4] >> (8 * (s % 4))) & 0xffu; }
+  __device__ __forceinline__ uint32_t fl(int s) const { return (fls[s / 4] >> (8 * (s % 4))) & 0xffu; }
+};
+
+template <class D>
+__device__ __forceinline__ FusedProg fused_prog(D d) {
+  FusedProg p;
+  p.nsteps = d(0) >> 24;
+  p.ops[0] = d(42); p.ops[1] = d(43);
+  p.fls[0] = d(44); p.fls[1] = d(45);
 #pragma unroll
-  for (int s = 0; s < kMaxSteps; ++s) fast = fast && aligned16(d.q(26 + 2 * s));
+  for (int s = 0; s < kMaxSteps; ++s) {
+    p.scal[s] = d(46 + s);
+    p.out[s] = d.q(26 + 2 * s);
+  }
+  return p;
+}
+
+// Applies step s of the program to V values; returns the step's flags.
+template <int V>
+__device__ __forceinline__ uint32_t fused_apply(const FusedProg& P, int s, float (&acc)[V],
+                                                const float (&v1)[V], const float (&v2)[V],
+                                                const float (&v3)[V]) {
+  const uint32_t sfl = P.fl(s);
+  const uint32_t which = (sfl >> 4) & 3u;
+  // operand = fused input `which`, selected with uniform bit masks (a select
+  // between arrays would be lowered to a scratch-memory load)
+  const uint32_t m1 = which == 1 ? ~0u : 0u, m2 = which == 2 ? ~0u : 0u, m3 = which == 3 ? ~0u : 0u;
+  float opnd[V];
+#pragma unroll
+  for (int e = 0; e < V; ++e)
+    opnd[e] = __uint_as_float((__float_as_uint(v1[e]) & m1) | (__float_as_uint(v2[e]) & m2) |
+                              (__float_as_uint(v3[e]) & m3));
+  fused_step<V>(P.op(s), sfl, __uint_as_float(P.scal[s]), acc, opnd);
+  return sfl;
+}
+
+template <int DT, int CPL, int CPS, class D>
+__device__ __attribute__((noinline)) void fused_tile(D d, uint32_t t) {
+  static_assert(DT == GPUOS_F32, "fused chains are fp32");
+  using T = DTr<DT, CPL, CPS>;
+  constexpr int V = T::V;
+  constexpr int U = 2;
+  const uint32_t n = d(1), ntiles = d(6);
+  const uint64_t p0 = d.q(18), p1 = d.q(20), p2 = d.q(22), p3 = d.q(24);
+  const FusedProg P = fused_prog(d);
+  bool fast = aligned16(p0) && aligned16(p1) && aligned16(p2) && aligned16(p3);
+#pragma unroll
+  for (int s = 0; s < kMaxSteps; ++s) fast = fast && aligned16(P.out[s]);
   const uint32_t lane = lane_id();
-  uint32_t vend = lo;
+  uint32_t scalar_from = t * 64, scalar_step = 64 * ntiles;  // per-element path
   if (fast) {
-    vend = lo + ((hi - lo) / V) * V;
-    for (uint32_t base = lo; base < vend; base += 64 * V * U) {
+    // whole vectors only; unused inputs have empty resources and rows past
+    // the end fall outside them, so every load and store is unconditional
+    const uint32_t nv = n / V, nrows = (nv + 63) / 64;
+    const uint32_t vb = nv * 16u;
+    const rsrc_t r0 = make_rsrc_n(p0, vb), r1 = make_rsrc_n(p1, vb), r2 = make_rsrc_n(p2, vb),
+                 r3 = make_rsrc_n(p3, vb);
+    for (uint32_t row = t; row < nrows; row += U * ntiles) {
       float acc[U][V], v1[U][V], v2[U][V], v3[U][V];
 #pragma unroll
       for (int u = 0; u < U; ++u) {
-        const uint32_t i = base + (u * 64 + lane) * V;
-        if (i < vend) {
-          T::ldv(in0, i, acc[u]);
-          if (in1) T::ldv(in1, i, v1[u]);
-          if (in2) T::ldv(in2, i, v2[u]);
-          if (in3) T::ldv(in3, i, v3[u]);
-        }
+        const uint32_t q = (row + u * ntiles) * 64 + lane;
+        T::ldq(r0, q, acc[u]);
+        T::ldq(r1, q, v1[u]);
+        T::ldq(r2, q, v2[u]);
+        T::ldq(r3, q, v3[u]);
       }
 #pragma unroll
-      for (int u = 0; u < U; ++u) {
-        const uint32_t i = base + (u * 64 + lane) * V;
-        if (i < vend) {
+      for (int s = 0; s < kMaxSteps; ++s) {
+        if ((uint32_t)s < P.nsteps) {
+          uint32_t sfl = 0;
 #pragma unroll
-          for (int s = 0; s < kMaxSteps; ++s) {
-            if ((uint32_t)s < nsteps) {
-              const uint32_t sop = (d(42 + s / 4) >> (8 * (s % 4))) & 0xffu;
-              const uint32_t sfl = (d(44 + s / 4) >> (8 * (s % 4))) & 0xffu;
-              const uint32_t which = (sfl >> 4) & 3u;
-              float opnd[V];
+          for (int u = 0; u < U; ++u) sfl = fused_apply<V>(P, s, acc[u], v1[u], v2[u], v3[u]);
+          if (sfl & FSF_STORE) {
+            const rsrc_t o = make_rsrc_n(P.out[s], vb);
 #pragma unroll
-              for (int e = 0; e < V; ++e)
-                opnd[e] = which == 1 ? v1[u][e] : (which == 2 ? v2[u][e] : v3[u][e]);
-              fused_step<V>(sop, sfl, __uint_as_float(d(46 + s)), acc[u], opnd);
-              if constexpr (DT == GPUOS_BF16) {
-#pragma unroll
-                for (int e = 0; e < V; ++e) acc[u][e] = T::round(acc[u][e]);
-              }
-              if (sfl & FSF_STORE) T::stv(d.q(26 + 2 * s), i, acc[u]);
-            }
+            for (int u = 0; u < U; ++u) T::stq(o, (row + u * ntiles) * 64 + lane, acc[u]);
           }
         }
       }
     }
+    if (t + 1 != ntiles) return;
+    scalar_from = nv * V;  // leftover elements, last tile only
+    scalar_step = 64;
   }
-  for (uint32_t i = vend + lane; i < hi; i += 64) {
+  const rsrc_t in0 = make_rsrc(p0), in1 = make_rsrc_n(p1, n * 4u), in2 = make_rsrc_n(p2, n * 4u),
+               in3 = make_rsrc_n(p3, n * 4u);
+  for (uint32_t i = scalar_from + lane; i < n; i += scalar_step) {
     float acc[1] = {T::ld(in0, i)};
-    const float v1s = in1 ? T::ld(in1, i) : 0.0f;
-    const float v2s = in2 ? T::ld(in2, i) : 0.0f;
-    const float v3s = in3 ? T::ld(in3, i) : 0.0f;
+    const float v1s[1] = {T::ld(in1, i)};
+    const float v2s[1] = {T::ld(in2, i)};
+    const float v3s[1] = {T::ld(in3, i)};
 #pragma unroll
     for (int s = 0; s < kMaxSteps; ++s) {
-      if ((uint32_t)s < nsteps) {
-        const uint32_t sop = (d(42 + s / 4) >> (8 * (s % 4))) & 0xffu;
-        const uint32_t sfl = (d(44 + s / 4) >> (8 * (s % 4))) & 0xffu;
-        const uint32_t which = (sfl >> 4) & 3u;
-        const float opnd[1] = {which == 1 ? v1s : (which == 2 ? v2s : v3s)};
-        fused_step<1>(sop, sfl, __uint_as_float(d(46 + s)), acc, opnd);
-        acc[0] = T::round(acc[0]);
-        if (sfl & FSF_STORE) T::st(d.q(26 + 2 * s), i, acc[0]);
+      if ((uint32_t)s < P.nsteps) {
+        const uint32_t sfl = fused_apply<1>(P, s, acc, v1s, v2s, v3s);
+        if (sfl & FSF_STORE) T::st(make_rsrc(P.out[s]), i, acc[0]);
       }
     }
   }
@@ -323,30 +402,30 @@ __device__ __forceinline__ void fused_tile(const D& d, uint32_t t) {
 // row reductions: one row at a time per wave.  A pass over the row is a
 // coalesced sweep (lane j reads elements j, j + 64, ...); multi-pass ops
 // (softmax: max, sum of exponentials, write; RMSNORM: sum of squares, write)
-// re-read the row while it is still in L2.
+// read the row again.
 
-template <int DT>
+template <int DT, int CPL, int CPS>
 struct RowReader {
-  uint64_t in;
+  rsrc_t in;
   uint32_t base, ca;
   __device__ __forceinline__ float operator()(uint32_t j) const {
     const uint32_t e = base + j;
-    return DTr<DT>::ld(in, ca ? e % ca : e);
+    return DTr<DT, CPL, CPS>::ld(in, ca ? e % ca : e);
   }
 };
 
-template <int OP, int DT, class D>
-__device__ __forceinline__ void row_tile(const D& d, uint32_t t) {
-  using T = DTr<DT>;
+template <int OP, int DT, int CPL, int CPS, class D>
+__device__ __attribute__((noinline)) void row_tile(D d, uint32_t t) {
+  using T = DTr<DT, CPL, CPS>;
   const uint32_t rows = d(2), L = d(3), tile = d(7);
   const uint32_t r0 = t * tile;
   const uint32_t r1 = r0 + tile < rows ? r0 + tile : rows;
-  const uint64_t out = d.q(18), in = d.q(20), g = d.q(24);
+  const rsrc_t out = make_rsrc(d.q(18)), in = make_rsrc(d.q(20)), g = make_rsrc(d.q(24));
   const uint32_t ca = d(26);
   const float eps = __uint_as_float(d(29));
   const uint32_t lane = lane_id();
   for (uint32_t r = r0; r < r1; ++r) {
-    const RowReader<DT> x{in, r * L, ca};
+    const RowReader<DT, CPL, CPS> x{in, r * L, ca};
     if constexpr (OP == GPUOS_OP_ROW_SUM) {
       float s0 = 0.0f, s1 = 0.0f, s2 = 0.0f, s3 = 0.0f;
       uint32_t j = lane;
@@ -393,17 +472,18 @@ __device__ __forceinline__ void row_tile(const D& d, uint32_t t) {
 // rotate-half rotary embedding, rows = heads of row_len = head_dim; each lane
 // owns whole (i, i + h/2) pairs, so the op may run in place.
 
-template <int DT, class D>
-__device__ __forceinline__ void rope_tile(const D& d, uint32_t) {
-  using T = DTr<DT>;
+template <int DT, int CPL, int CPS, class D>
+__device__ __attribute__((noinline)) void rope_tile(D d, uint32_t) {
+  using T = DTr<DT, CPL, CPS>;
   const uint32_t heads = d(2), hd = d(3), half = hd / 2;
-  const uint64_t out = d.q(18), in = d.q(20), tab = d.q(24);
+  const rsrc_t out = make_rsrc(d.q(18)), in = make_rsrc(d.q(20)), tab = make_rsrc(d.q(24));
   const uint32_t pairs = heads * half;
   for (uint32_t p = lane_id(); p < pairs; p += 64) {
     const uint32_t h = p / half, i = p - h * half;
     const float x1 = T::ld(in, h * hd + i);
     const float x2 = T::ld(in, h * hd + half + i);
-    const float c = ldg<float>(tab + 4ull * i), s = ldg<float>(tab + 4ull * (half + i));
+    const float c = __uint_as_float(ld32<CPL>(tab, 4u * i));
+    const float s = __uint_as_float(ld32<CPL>(tab, 4u * (half + i)));
     const float a1 = x1 * c, b1 = x2 * s;
     const float a2 = x2 * c, b2 = x1 * s;
     T::st(out, h * hd + i, a1 - b1);
@@ -415,12 +495,12 @@ __device__ __forceinline__ void rope_tile(const D& d, uint32_t) {
 // GEMV: out[i] = sum_k W[i, k] x[k]; `tile` rows per tile, up to 4 rows in
 // flight per wave; lanes split K in 16-byte chunks of W (8 bf16).
 
-template <int DT>
-__device__ __forceinline__ void load_x8(uint64_t x, uint32_t k, float (&v)[8]) {
+template <int DT, int CPL>
+__device__ __forceinline__ void load_x8(rsrc_t x, uint32_t k, float (&v)[8]) {
   if constexpr (DT == GPUOS_BF16) {
-    unpack_bf16x8(ldg<u32x4>(x + 2ull * k), v);
+    unpack_bf16x8(ld128<CPL>(x, 2u * k), v);
   } else {
-    const u32x4 a = ldg<u32x4>(x + 4ull * k), b = ldg<u32x4>(x + 4ull * k + 16);
+    const u32x4 a = ld128<CPL>(x, 4u * k), b = ld128<CPL>(x, 4u * k + 16u);
     v[0] = __uint_as_float(a.x); v[1] = __uint_as_float(a.y);
     v[2] = __uint_as_float(a.z); v[3] = __uint_as_float(a.w);
     v[4] = __uint_as_float(b.x); v[5] = __uint_as_float(b.y);
@@ -428,15 +508,15 @@ __device__ __forceinline__ void load_x8(uint64_t x, uint32_t k, float (&v)[8]) {
   }
 }
 
-template <int DT, class D>
-__device__ __forceinline__ void gemv_tile(const D& d, uint32_t t) {
-  using T = DTr<DT>;
+template <int DT, int CPL, int CPS, class D>
+__device__ __attribute__((noinline)) void gemv_tile(D d, uint32_t t) {
+  using T = DTr<DT, CPL, CPS>;
   const uint32_t M = d(30), K = d(31), tile = d(7);
-  const uint64_t out = d.q(18), x = d.q(20), W = d.q(24);
+  const rsrc_t out = make_rsrc(d.q(18)), x = make_rsrc(d.q(20)), W = make_rsrc(d.q(24));
   const uint32_t i0 = t * tile;
   const uint32_t i1 = i0 + tile < M ? i0 + tile : M;
   const uint32_t lane = lane_id();
-  const bool fast = (K % 8 == 0) && aligned16(x) && aligned16(W);
+  const bool fast = (K % 8 == 0) && aligned16(d.q(20)) && aligned16(d.q(24));
   if (fast) {
     const uint32_t chunks = K / 8;
     constexpr int R = 4;
@@ -444,11 +524,11 @@ __device__ __forceinline__ void gemv_tile(const D& d, uint32_t t) {
       float acc[R] = {0.0f, 0.0f, 0.0f, 0.0f};
       for (uint32_t c = lane; c < chunks; c += 64) {
         float xv[8];
-        load_x8<DT>(x, c * 8, xv);
+        load_x8<DT, CPL>(x, c * 8, xv);
         u32x4 wr[R];
 #pragma unroll
         for (int r = 0; r < R; ++r)
-          if (i + r < i1) wr[r] = ldg<u32x4>(W + 2ull * ((uint64_t)(i + r) * K + c * 8));
+          if (i + r < i1) wr[r] = ld128<CPL>(W, 2u * ((i + r) * K + c * 8));
 #pragma unroll
         for (int r = 0; r < R; ++r) {
           if (i + r < i1) {
@@ -471,7 +551,7 @@ __device__ __forceinline__ void gemv_tile(const D& d, uint32_t t) {
     for (uint32_t i = i0; i < i1; ++i) {
       float acc = 0.0f;
       for (uint32_t k = lane; k < K; k += 64)
-        acc = __builtin_fmaf(bf2f(ldg<uint16_t>(W + 2ull * ((uint64_t)i * K + k))), T::ld(x, k), acc);
+        acc = __builtin_fmaf(bf2f(ld16<CPL>(W, 2u * (i * K + k))), T::ld(x, k), acc);
       acc = wave_sum(acc);
       if (lane == 0) T::st(out, i, acc);
     }
@@ -483,11 +563,11 @@ __device__ __forceinline__ void gemv_tile(const D& d, uint32_t t) {
 // tile.  Lanes walk the key rows in 16-byte chunks; the Dh/8 lanes holding
 // one (j, h) pair reduce together.
 
-template <int DT, int CPH, class D>
-__device__ __forceinline__ void score_rows_fast(const D& d, uint32_t j0, uint32_t j1) {
+template <int DT, int CPL, int CPS, int CPH, class D>
+__device__ __forceinline__ void score_rows_fast(D d, uint32_t j0, uint32_t j1) {
   const uint32_t H = d(30), Dh = d(31), S = d(32);
   const uint32_t HD = H * Dh, cpr = HD / 8;  // 16-byte chunks per key row
-  const uint64_t out = d.q(18), q = d.q(20), Kc = d.q(24);
+  const rsrc_t out = make_rsrc(d.q(18)), q = make_rsrc(d.q(20)), Kc = make_rsrc(d.q(24));
   const float alpha = __uint_as_float(d(28));
   const uint32_t lane = lane_id();
   const uint32_t total = (j1 - j0) * cpr;
@@ -500,34 +580,34 @@ __device__ __forceinline__ void score_rows_fast(const D& d, uint32_t j0, uint32_
       c = f - (j - j0) * cpr;
       h = c / CPH;
       float qv[8], kv[8];
-      load_x8<DT>(q, c * 8, qv);
-      unpack_bf16x8(ldg<u32x4>(Kc + 2ull * ((uint64_t)j * HD + c * 8)), kv);
+      load_x8<DT, CPL>(q, c * 8, qv);
+      unpack_bf16x8(ld128<CPL>(Kc, 2u * (j * HD + c * 8)), kv);
 #pragma unroll
       for (int e = 0; e < 8; ++e) part = __builtin_fmaf(qv[e], kv[e], part);
     }
     part = group_sum<CPH>(part);
-    if (f < total && (c % CPH) == 0) stg<float>(out + 4ull * ((uint64_t)h * S + j), alpha * part);
+    if (f < total && (c % CPH) == 0) st32<CPS>(out, 4u * (h * S + j), __float_as_uint(alpha * part));
     (void)Dh;
   }
 }
 
-template <int DT, class D>
-__device__ __forceinline__ void attn_score_tile(const D& d, uint32_t t) {
-  using T = DTr<DT>;
+template <int DT, int CPL, int CPS, class D>
+__device__ __attribute__((noinline)) void attn_score_tile(D d, uint32_t t) {
+  using T = DTr<DT, CPL, CPS>;
   const uint32_t H = d(30), Dh = d(31), S = d(32), tile = d(7);
   const uint32_t j0 = t * tile;
   const uint32_t j1 = j0 + tile < S ? j0 + tile : S;
   const bool aligned = aligned16(d.q(20)) && aligned16(d.q(24));
   if (aligned && Dh == 64) {
-    score_rows_fast<DT, 8>(d, j0, j1);
+    score_rows_fast<DT, CPL, CPS, 8>(d, j0, j1);
     return;
   }
   if (aligned && Dh == 128) {
-    score_rows_fast<DT, 16>(d, j0, j1);
+    score_rows_fast<DT, CPL, CPS, 16>(d, j0, j1);
     return;
   }
   // general head size: one (j, h) pair per lane
-  const uint64_t out = d.q(18), q = d.q(20), Kc = d.q(24);
+  const rsrc_t out = make_rsrc(d.q(18)), q = make_rsrc(d.q(20)), Kc = make_rsrc(d.q(24));
   const float alpha = __uint_as_float(d(28));
   const uint32_t HD = H * Dh;
   const uint32_t pairs = (j1 - j0) * H;
@@ -535,22 +615,21 @@ __device__ __forceinline__ void attn_score_tile(const D& d, uint32_t t) {
     const uint32_t j = j0 + p / H, h = p % H;
     float acc = 0.0f;
     for (uint32_t e = 0; e < Dh; ++e)
-      acc = __builtin_fmaf(T::ld(q, h * Dh + e),
-                           bf2f(ldg<uint16_t>(Kc + 2ull * ((uint64_t)j * HD + h * Dh + e))), acc);
-    stg<float>(out + 4ull * ((uint64_t)h * S + j), alpha * acc);
+      acc = __builtin_fmaf(T::ld(q, h * Dh + e), bf2f(ld16<CPL>(Kc, 2u * (j * HD + h * Dh + e))), acc);
+    st32<CPS>(out, 4u * (h * S + j), __float_as_uint(alpha * acc));
   }
 }
 
 // attention output: out[h*Dh + c] = sum_j p[h, j] V[j, h*Dh + c]; a tile is
 // `tile` 8-column chunks; lanes split the key positions.
-template <int DT, class D>
-__device__ __forceinline__ void attn_av_tile(const D& d, uint32_t t) {
-  using T = DTr<DT>;
+template <int DT, int CPL, int CPS, class D>
+__device__ __attribute__((noinline)) void attn_av_tile(D d, uint32_t t) {
+  using T = DTr<DT, CPL, CPS>;
   const uint32_t H = d(30), Dh = d(31), S = d(32), tile = d(7);
   const uint32_t HD = H * Dh;
-  const uint64_t out = d.q(18), p = d.q(20), Vc = d.q(24);
+  const rsrc_t out = make_rsrc(d.q(18)), p = make_rsrc(d.q(20)), Vc = make_rsrc(d.q(24));
   const uint32_t lane = lane_id();
-  if ((Dh % 8) == 0 && aligned16(Vc)) {
+  if ((Dh % 8) == 0 && aligned16(d.q(24))) {
     const uint32_t nchunks = HD / 8;
     const uint32_t c0 = t * tile;
     const uint32_t c1 = c0 + tile < nchunks ? c0 + tile : nchunks;
@@ -558,9 +637,9 @@ __device__ __forceinline__ void attn_av_tile(const D& d, uint32_t t) {
       const uint32_t h = (c * 8) / Dh;
       float acc[8] = {0, 0, 0, 0, 0, 0, 0, 0};
       for (uint32_t j = lane; j < S; j += 64) {
-        const float w = ldg<float>(p + 4ull * ((uint64_t)h * S + j));
+        const float w = __uint_as_float(ld32<CPL>(p, 4u * (h * S + j)));
         float v[8];
-        unpack_bf16x8(ldg<u32x4>(Vc + 2ull * ((uint64_t)j * HD + c * 8)), v);
+        unpack_bf16x8(ld128<CPL>(Vc, 2u * (j * HD + c * 8)), v);
 #pragma unroll
         for (int e = 0; e < 8; ++e) acc[e] = __builtin_fmaf(w, v[e], acc[e]);
       }
@@ -582,8 +661,8 @@ __device__ __forceinline__ void attn_av_tile(const D& d, uint32_t t) {
       const uint32_t h = c / Dh;
       float acc = 0.0f;
       for (uint32_t j = lane; j < S; j += 64)
-        acc = __builtin_fmaf(ldg<float>(p + 4ull * ((uint64_t)h * S + j)),
-                             bf2f(ldg<uint16_t>(Vc + 2ull * ((uint64_t)j * HD + c))), acc);
+        acc = __builtin_fmaf(__uint_as_float(ld32<CPL>(p, 4u * (h * S + j))),
+                             bf2f(ld16<CPL>(Vc, 2u * (j * HD + c))), acc);
       acc = wave_sum(acc);
       if (lane == 0) T::st(out, c, acc);
     }
@@ -594,7 +673,7 @@ __device__ __forceinline__ void attn_av_tile(const D& d, uint32_t t) {
 // debug op: spin for aux[0] nanoseconds (s_memrealtime ticks at 100 MHz),
 // bounded to 10 ms.
 template <class D>
-__device__ __forceinline__ void spin_tile(const D& d, uint32_t) {
+__device__ __forceinline__ void spin_tile(D d, uint32_t) {
   uint64_t ns = d(30);
   if (ns > 10000000u) ns = 10000000u;
   const uint64_t t0 = now_ticks();
@@ -606,67 +685,66 @@ __device__ __forceinline__ void spin_tile(const D& d, uint32_t) {
 // opcode switch over the fixed op table (uniform per wave: a scalar branch,
 // no indirect call).  Returns a device error code, 0 on success.
 
-template <class D>
-__device__ uint32_t exec_tile(const D& d, uint32_t t) {
+template <int CPL, int CPS, class D>
+__device__ uint32_t exec_tile(D d, uint32_t t) {
   const uint32_t w0 = d(0);
   const uint32_t op = w0 & 0xffu, dt = (w0 >> 8) & 0xffu;
   const bool bf = dt == GPUOS_BF16;
+  constexpr int F = GPUOS_F32, B = GPUOS_BF16;
   switch (op) {
     case GPUOS_OP_NOP:
       return 0;
     case GPUOS_OP_COPY:
-      if (bf) copy_tile<2>(d, t); else copy_tile<4>(d, t);
+      if (bf) copy_tile<2, CPL, CPS>(d, t); else copy_tile<4, CPL, CPS>(d, t);
       return 0;
     case GPUOS_OP_GATHER:
-      return bf ? gather_tile<2>(d, t) : gather_tile<4>(d, t);
+      return bf ? gather_tile<2, CPL, CPS>(d, t) : gather_tile<4, CPL, CPS>(d, t);
     case GPUOS_OP_ADD:
-      if (bf) ew_tile<GPUOS_OP_ADD, GPUOS_BF16>(d, t); else ew_tile<GPUOS_OP_ADD, GPUOS_F32>(d, t);
+      if (bf) ew_tile<GPUOS_OP_ADD, B, CPL, CPS>(d, t); else ew_tile<GPUOS_OP_ADD, F, CPL, CPS>(d, t);
       return 0;
     case GPUOS_OP_MUL:
-      if (bf) ew_tile<GPUOS_OP_MUL, GPUOS_BF16>(d, t); else ew_tile<GPUOS_OP_MUL, GPUOS_F32>(d, t);
+      if (bf) ew_tile<GPUOS_OP_MUL, B, CPL, CPS>(d, t); else ew_tile<GPUOS_OP_MUL, F, CPL, CPS>(d, t);
       return 0;
     case GPUOS_OP_SCALE:
-      if (bf) ew_tile<GPUOS_OP_SCALE, GPUOS_BF16>(d, t); else ew_tile<GPUOS_OP_SCALE, GPUOS_F32>(d, t);
+      if (bf) ew_tile<GPUOS_OP_SCALE, B, CPL, CPS>(d, t); else ew_tile<GPUOS_OP_SCALE, F, CPL, CPS>(d, t);
       return 0;
     case GPUOS_OP_RELU:
-      if (bf) ew_tile<GPUOS_OP_RELU, GPUOS_BF16>(d, t); else ew_tile<GPUOS_OP_RELU, GPUOS_F32>(d, t);
+      if (bf) ew_tile<GPUOS_OP_RELU, B, CPL, CPS>(d, t); else ew_tile<GPUOS_OP_RELU, F, CPL, CPS>(d, t);
       return 0;
     case GPUOS_OP_EXP:
-      if (bf) ew_tile<GPUOS_OP_EXP, GPUOS_BF16>(d, t); else ew_tile<GPUOS_OP_EXP, GPUOS_F32>(d, t);
+      if (bf) ew_tile<GPUOS_OP_EXP, B, CPL, CPS>(d, t); else ew_tile<GPUOS_OP_EXP, F, CPL, CPS>(d, t);
       return 0;
     case GPUOS_OP_SILU_MUL:
-      if (bf) ew_tile<GPUOS_OP_SILU_MUL, GPUOS_BF16>(d, t);
-      else ew_tile<GPUOS_OP_SILU_MUL, GPUOS_F32>(d, t);
+      if (bf) ew_tile<GPUOS_OP_SILU_MUL, B, CPL, CPS>(d, t); else ew_tile<GPUOS_OP_SILU_MUL, F, CPL, CPS>(d, t);
       return 0;
     case GPUOS_OP_ROW_SUM:
-      if (bf) row_tile<GPUOS_OP_ROW_SUM, GPUOS_BF16>(d, t);
-      else row_tile<GPUOS_OP_ROW_SUM, GPUOS_F32>(d, t);
+      if (bf) row_tile<GPUOS_OP_ROW_SUM, B, CPL, CPS>(d, t); else row_tile<GPUOS_OP_ROW_SUM, F, CPL, CPS>(d, t);
       return 0;
     case GPUOS_OP_ROW_SOFTMAX:
-      if (bf) row_tile<GPUOS_OP_ROW_SOFTMAX, GPUOS_BF16>(d, t);
-      else row_tile<GPUOS_OP_ROW_SOFTMAX, GPUOS_F32>(d, t);
+      if (bf) row_tile<GPUOS_OP_ROW_SOFTMAX, B, CPL, CPS>(d, t);
+      else row_tile<GPUOS_OP_ROW_SOFTMAX, F, CPL, CPS>(d, t);
       return 0;
     case GPUOS_OP_RMSNORM:
-      if (bf) row_tile<GPUOS_OP_RMSNORM, GPUOS_BF16>(d, t);
-      else row_tile<GPUOS_OP_RMSNORM, GPUOS_F32>(d, t);
+      if (bf) row_tile<GPUOS_OP_RMSNORM, B, CPL, CPS>(d, t); else row_tile<GPUOS_OP_RMSNORM, F, CPL, CPS>(d, t);
       return 0;
     case GPUOS_OP_ROPE:
-      if (bf) rope_tile<GPUOS_BF16>(d, t); else rope_tile<GPUOS_F32>(d, t);
+      if (bf) rope_tile<B, CPL, CPS>(d, t); else rope_tile<F, CPL, CPS>(d, t);
       return 0;
     case GPUOS_OP_GEMV:
-      if (bf) gemv_tile<GPUOS_BF16>(d, t); else gemv_tile<GPUOS_F32>(d, t);
+      if (bf) gemv_tile<B, CPL, CPS>(d, t); else gemv_tile<F, CPL, CPS>(d, t);
       return 0;
     case GPUOS_OP_ATTN_SCORE:
-      if (bf) attn_score_tile<GPUOS_BF16>(d, t); else attn_score_tile<GPUOS_F32>(d, t);
+      if (bf) attn_score_tile<B, CPL, CPS>(d, t); else attn_score_tile<F, CPL, CPS>(d, t);
       return 0;
     case GPUOS_OP_ATTN_AV:
-      if (bf) attn_av_tile<GPUOS_BF16>(d, t); else attn_av_tile<GPUOS_F32>(d, t);
+      if (bf) attn_av_tile<B, CPL, CPS>(d, t); else attn_av_tile<F, CPL, CPS>(d, t);
       return 0;
     case GPUOS_OP_SPIN:
       spin_tile(d, t);
       return 0;
-    case OP_FUSED_EW:
-      if (bf) fused_tile<GPUOS_BF16>(d, t); else fused_tile<GPUOS_F32>(d, t);
+    case OP_FUSED_EW:  // fp32 chains only (the fusion pass leaves bf16 ops unfused)
+      if (bf) return (uint32_t)DERR_BAD_OPCODE;
+      fused_tile<F, CPL, CPS>(d, t);
       return 0;
     default:
       return (uint32_t)DERR_BAD_OPCODE;

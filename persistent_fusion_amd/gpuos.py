@@ -44,7 +44,7 @@ class GpuosOp(C.Structure):
 class GpuosConfig(C.Structure):
     _fields_ = [(name, C.c_uint32) for name in (
         "ring_slots", "waves_per_cu", "tile_elems", "be_tile_elems", "fusion", "auto_deps",
-        "trace", "block_on_full", "max_fuse")] + [("reserved", C.c_uint32 * 7)]
+        "trace", "block_on_full", "max_fuse", "priority")] + [("reserved", C.c_uint32 * 6)]
 
 
 class GpuosStats(C.Structure):

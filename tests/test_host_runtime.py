@@ -198,7 +198,7 @@ def test_ticket_ranges_are_contiguous_and_tiles_cover_ops():
         for d in ds:
             assert d["tstart"] == start
             start += d["ntiles"]
-        assert ds[0]["ntiles"] * ds[0]["tile"] >= 10_000 and ds[0]["tile"] % 256 == 0
+        assert ds[0]["ntiles"] * ds[0]["tile"] >= 10_000 and ds[0]["tile"] % 64 == 0
         assert ds[1]["ntiles"] * ds[1]["tile"] >= 14
         assert ds[2]["ntiles"] * ds[2]["tile"] >= 2688
         assert ds[3]["ntiles"] == 896 // 8
