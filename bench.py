@@ -9,6 +9,8 @@ three descriptors, gpuos_flush (fusion pass, ring publication, doorbell), the
 resident kernel's claim/dispatch/completion, and (once, after the last step)
 gpuos_sync.  Four independent replicas of x, a, b, y (1 GiB) rotate across
 steps so the 256 MB infinity cache cannot serve a pass from the previous one.
+The warm-up and timed passes run in one launch of the resident kernel, whose
+duration (HIP events on its stream) gives the roofline's achieved bandwidth.
 
 Prints one JSON line (rank 0).  Only one GPU is supported.
 """
@@ -29,6 +31,8 @@ N_ELEMS = 16_777_216
 REPLICAS = 4
 HBM_PEAK_GBS = 8000.0
 METRIC = "small ops/sec and effective HBM GB/s vs per-op launch, 1× MI355X"
+# sources whose change invalidates the committed HBM byte counts
+KERNEL_SOURCES = ("kernels.hip", "tile_ops.h", "device_common.h", "gpuos_internal.h")
 
 
 def log(msg):
@@ -36,6 +40,7 @@ def log(msg):
 
 
 def fused_chain_leg(steps, warmup, device=0):
+    """One resident launch: `warmup` passes, then `steps` timed passes."""
     import torch
 
     from persistent_fusion_amd import gpuos, runner, traffic, workloads
@@ -52,24 +57,17 @@ def fused_chain_leg(steps, warmup, device=0):
         arrs.append(gpuos.encode_ops(wl.ops, 0, 3, addr, {}))
     torch.cuda.synchronize()
 
-    # warm-up session (kernel launch, first touches)
-    log(f"bench: fused chain warm-up ({warmup} passes)")
-    ctx = gpuos.Context(device)
+    # the launch covers the warm-up passes and the timed passes; the HIP events
+    # recorded around it on its stream give the kernel's duration
+    log(f"bench: fused chain, one resident launch: {warmup} warm-up + {steps} timed passes")
+    ctx = gpuos.Context(device, trace=1)
     for k in range(warmup):
         ctx.submit_noids(arrs[k % REPLICAS], 3)
         ctx.flush()
     ctx.sync(0, 60.0)
-    ctx.destroy()
-    torch.cuda.synchronize()
-
-    # timed session: the kernel is launched, then `steps` passes are queued
-    # back to back and drained; the resident kernel's HIP-event lifetime covers
-    # the same passes
-    log(f"bench: fused chain timed ({steps} passes)")
-    ctx = gpuos.Context(device, trace=1)
     t0 = time.perf_counter()
     for k in range(steps):
-        ctx.submit_noids(arrs[k % REPLICAS], 3)
+        ctx.submit_noids(arrs[(warmup + k) % REPLICAS], 3)
         ctx.flush()
     ctx.sync(0, 120.0)
     t1 = time.perf_counter()
@@ -79,16 +77,18 @@ def fused_chain_leg(steps, warmup, device=0):
     ctx.destroy()
     torch.cuda.synchronize()
     wall = t1 - t0
+    if st["launches"] != 1:
+        raise RuntimeError(f"the resident kernel was launched {st['launches']} times in one session")
     kernel_s = st["kernel_ns"] * 1e-9
-    # device-side busy span of the passes from the in-kernel trace (100 MHz)
-    fused = [r for r in tr if r["opcode"] == 32]
+    # device-side busy span of the timed passes from the in-kernel trace (100 MHz)
+    fused = sorted((r for r in tr if r["opcode"] == 32), key=lambda r: r["seq"])[-steps:]
     dev_span = None
     if fused:
         dev_span = (max(r["t_done"] for r in fused) - min(r["t_claim"] for r in fused)) * 1e-8
-    per_pass_dev = [(r["t_done"] - r["t_claim"]) * 1e-8 for r in fused]
+    per_pass_dev = sorted((r["t_done"] - r["t_claim"]) * 1e-8 for r in fused)
 
     # output of the last pass (checked against the oracle in the CPU leg)
-    y = reps[(steps - 1) % REPLICAS]["y"].cpu().numpy()
+    y = reps[(warmup + steps - 1) % REPLICAS]["y"].cpu().numpy()
 
     # per-op launches (3 kernels per pass) and one stand-alone fused kernel
     stream = torch.cuda.current_stream(device)
@@ -118,9 +118,34 @@ def fused_chain_leg(steps, warmup, device=0):
     return {
         "wall_s": wall, "kernel_s": kernel_s, "dev_span_s": dev_span, "y": y,
         "fused_bytes": fused_bytes, "unfused_bytes": unfused_bytes,
-        "per_pass_dev_us": (sorted(per_pass_dev)[len(per_pass_dev) // 2] * 1e6) if per_pass_dev else None,
+        "per_pass_dev_us": per_pass_dev[len(per_pass_dev) // 2] * 1e6 if per_pass_dev else None,
         "stats": st, "baselines": res,
     }
+
+
+def copy_leg(device=0, reps=10):
+    """A plain device copy of 1 GiB (torch's copy kernel): the bandwidth a
+    simple streaming kernel reaches on this GPU, and the known-size kernel the
+    HBM byte counters are calibrated with."""
+    import torch
+
+    n = 1 << 28  # 268,435,456 fp32 = 1 GiB
+    src = torch.empty(n, dtype=torch.float32, device=f"cuda:{device}").uniform_()
+    dst = torch.empty_like(src)
+    dst.copy_(src)
+    torch.cuda.synchronize()
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(reps):
+        dst.copy_(src)
+    e1.record()
+    torch.cuda.synchronize()
+    s = e0.elapsed_time(e1) * 1e-3 / reps
+    del src, dst
+    torch.cuda.empty_cache()
+    return {"bytes_per_launch": 2 * 4 * n, "gb_per_s": round(2 * 4 * n / s / 1e9, 1),
+            "kernel": "torch copy_ (1 GiB -> 1 GiB)"}
 
 
 def queue_leg(reps_n, device=0):
@@ -177,20 +202,48 @@ def cpu_baseline_leg(budget_s=10.0, gpu_y=None):
     wl = workloads.gen_fused_chain(seed=0, n=N_ELEMS)
     fused_bytes = traffic.fused_chain_bytes(wl.ops)
     passes = 0
-    parity = None
+    first = None
     t0 = time.perf_counter()
     while True:
         out = oracle.run(wl)
-        if passes == 0 and gpu_y is not None:
-            parity = oracle.compare(gpu_y, out["y"], "f32").ok
+        if first is None:
+            first = out["y"]
         passes += 1
         el = time.perf_counter() - t0
         if el >= budget_s or passes >= 200:
             break
+    parity = oracle.compare(gpu_y, first, "f32").ok if gpu_y is not None else None
     return {"value": round(passes * fused_bytes / el / 1e9, 3), "unit": "GB/s", "cores": 1,
             "kind": "oracle",
             "sample": f"{passes} passes of the 16,777,216-element relu(a*x+b) chain, op by op "
                       f"(3 numpy passes each), {el:.1f} s, single thread"}, parity
+
+
+def traffic_per_launch(passes):
+    """HBM bytes of one fused-chain launch from the committed counter summary,
+    or None when the kernel sources have changed since the counters were
+    taken (or none were taken)."""
+    import hashlib
+
+    path = os.path.join(ROOT, "profiles", "gpuos_resident_fused_chain_16M_traffic.md")
+    if not os.path.exists(path):
+        return None
+    fields = {}
+    with open(path) as f:
+        for line in f:
+            if line.startswith("- ") and ": " in line:
+                k, v = line[2:].strip().split(": ", 1)
+                fields[k.strip("`")] = v.strip().strip("`")
+    h = hashlib.sha256()
+    for name in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, "persistent_fusion_amd", "csrc", name), "rb") as f:
+            h.update(f.read())
+    if fields.get("kernel_sources_sha256") != h.hexdigest():
+        return None
+    try:
+        return int(round(float(fields["hbm_bytes_per_pass"]) * passes))
+    except (KeyError, ValueError):
+        return None
 
 
 def main():
@@ -213,11 +266,14 @@ def main():
     torch.cuda.synchronize()
     fc = fused_chain_leg(args.steps, args.warmup)
     q = queue_leg(args.queue_reps)
+    cp = copy_leg()
     cpu, parity = (None, None) if args.no_cpu else cpu_baseline_leg(args.cpu_budget, fc["y"])
 
     steps = args.steps
     value = steps * fc["fused_bytes"] / fc["wall_s"] / 1e9
-    achieved = steps * fc["fused_bytes"] / fc["kernel_s"] / 1e9
+    launch_bytes = (args.warmup + steps) * fc["fused_bytes"]
+    achieved = launch_bytes / fc["kernel_s"] / 1e9
+    tr = traffic_per_launch(args.warmup + steps)
     line = {
         "metric": METRIC,
         "value": round(value, 1),
@@ -235,8 +291,10 @@ def main():
                                "fused into 1 pass, 4 rotating replicas",
                    "elements": N_ELEMS, "descriptors_per_step": 3},
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
-                     "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
-                     "kernel": "gpuos_resident", "bytes_per_launch": steps * fc["fused_bytes"],
+                     "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
+                     "traffic": tr,
+                     "kernel": "gpuos_resident", "passes_per_launch": args.warmup + steps,
+                     "bytes_per_launch": launch_bytes,
                      "launch_s_hip_events": round(fc["kernel_s"], 6)},
         "ops_per_s": round(3 * steps / fc["wall_s"]),
         "parity_last_pass_bit_exact": parity,
@@ -246,6 +304,7 @@ def main():
         "per_op_launch": fc["baselines"]["per_op_launch"],
         "standalone_fused_kernel": fc["baselines"]["standalone_fused_kernel"],
         "elementwise_queue_1000x4096": q,
+        "plain_copy_kernel": cp,
         "cpu_baseline": cpu,
     }
     print(json.dumps(line), flush=True)

@@ -140,7 +140,12 @@ typedef enum gpuos_dtype {
                                        ring, whose work is claimed before any
                                        best-effort tile; LC ops may depend
                                        only on LC ops */
-#define GPUOS_FLAG_NONTEMPORAL 0x4u /* streaming output hint */
+#define GPUOS_FLAG_NONTEMPORAL 0x4u /* stream the op's operands: loads and
+                                       stores are marked non-temporal so
+                                       their cache lines are evicted first.
+                                       Set automatically on elementwise,
+                                       COPY and fused ops whose operands
+                                       total config.stream_min_kib or more */
 
 /*
  * User op descriptor (128 bytes).  Fields not used by an opcode must be zero.
@@ -184,7 +189,7 @@ typedef struct gpuos_op {
  */
 typedef struct gpuos_config {
   uint32_t ring_slots;    /* descriptors per ring, power of two in
-                             [64, 1<<20]; default 65536 */
+                             [64, 1<<18]; default 65536 */
   uint32_t waves_per_cu;  /* resident waves per compute unit, multiple of 4
                              in [4, 32]; default 8 */
   uint32_t tile_elems;    /* elementwise tile in elements, multiple of 256;
@@ -204,7 +209,16 @@ typedef struct gpuos_config {
                              ring between their own tiles (default), 2 = no
                              priority ring: GPUOS_FLAG_LC ops are rejected
                              and workers skip the per-tile check */
-  uint32_t reserved[6];
+  uint32_t idle_exit_ms;  /* the resident kernel exits after this many
+                             milliseconds with every published op retired and
+                             nothing new, giving its compute units back; the
+                             next flush (or a wait that finds work pending)
+                             relaunches it.  Default 200; 0xFFFFFFFF = never */
+  uint32_t stream_min_kib; /* elementwise / COPY / fused ops moving at least
+                              this many KiB are streamed (non-temporal).
+                              Default 32768 (32 MiB); 0xFFFFFFFF = only ops
+                              flagged GPUOS_FLAG_NONTEMPORAL */
+  uint32_t reserved[4];
 } gpuos_config;
 
 /* Counters returned by gpuos_get_stats. */
@@ -221,10 +235,13 @@ typedef struct gpuos_stats {
   uint64_t error_desc;         /* descriptor sequence that raised it */
   uint64_t worker_waves;       /* resident worker waves */
   uint64_t compute_units;
-  uint64_t kernel_ns;          /* lifetime of the resident kernel from HIP
-                                  events recorded on its stream around the
-                                  launch and its exit; 0 until gpuos_stop */
-  uint64_t reserved[3];
+  uint64_t kernel_ns;          /* summed duration of the resident kernel's
+                                  launches, from HIP events recorded on its
+                                  stream just before and just after each
+                                  launch; counts launches that have ended */
+  uint64_t launches;           /* resident kernel launches (1 + relaunches
+                                  after idle exits) */
+  uint64_t reserved[2];
 } gpuos_stats;
 
 /* Per-descriptor device timing, recorded when config.trace == 1. */

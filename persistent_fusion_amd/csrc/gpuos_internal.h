@@ -133,8 +133,10 @@ struct alignas(256) DevRing {
 struct alignas(256) AvailLine {
   uint64_t avail_tiles;  // tickets below this value are runnable
   uint64_t avail_ops;    // descriptors made visible
-  uint64_t stop_ticket;  // ring 0: waves whose next ticket is >= this exit
-  uint64_t _p[29];
+  uint64_t stop_ticket;  // ring 0: once stop_epoch is the running launch's
+  uint64_t stop_epoch;   // epoch, waves whose next ticket is >= stop_ticket
+                         // exit (stop_ticket is stored first)
+  uint64_t _p[28];
 };
 
 struct alignas(256) DevCtl {
@@ -148,7 +150,14 @@ struct alignas(256) HostCtl {
   uint64_t _p0[30];
   uint64_t completed[kRings]; // device: retire cursor per ring
   uint64_t heartbeat;         // device: doorbell loop iterations
-  uint64_t _p1[29];
+  uint64_t exit_tiles;        // device: ring-0 tickets published when the
+                              // kernel last exited (stored first)
+  uint64_t exit_epoch;        // device: epoch of the launch that exited
+  uint64_t exit_req;          // device: epoch of a launch about to leave
+                              // after idling (0 = cancelled); between this
+                              // store and the exit, the doorbell re-reads
+                              // the tails and cancels if any moved
+  uint64_t _p1[26];
   uint64_t stop_req;          // host: nonzero asks the kernel to exit once
                               // every published descriptor has retired
   uint64_t error;             // device: first error code (0 = none)
@@ -192,6 +201,12 @@ struct KArgs {
   uint32_t ends_mask;             // 2 * ring_slots - 1
   uint32_t workers;               // worker waves (all waves but the doorbell)
   uint32_t lc_enabled;            // poll the latency-critical ring
+  uint32_t epoch;                 // launch number of this context, from 1
+  uint32_t _pad;
+  uint64_t ticket_base;           // ring-0 tickets below this ran in earlier
+                                  // launches
+  uint64_t idle_exit_ticks;       // exit after this long (100 MHz ticks) with
+                                  // nothing queued; 0 = never
 };
 
 }  // namespace gpuos

@@ -271,15 +271,23 @@ __device__ void worker_loop(const KArgs& a, uint32_t w, lds_u32* slot0, lds_u32*
   Cached c0{0, 0, 0, slot0, 0}, c1{0, 0, 0, slot1, 0};
   uint64_t avail = 0, avail_ops = 0, lc_seen = 0;
   uint32_t idle = 0;
-  uint64_t ticket = w;
+  // tickets are dealt round-robin: this wave owns those = w (mod workers),
+  // from the first one this launch has not inherited as done
+  const uint64_t base = a.ticket_base;
+  uint64_t ticket = base - base % a.workers + w;
+  if (ticket < base) ticket += a.workers;
   for (;;) {
     if (a.lc_enabled) service_lc(a, line1, c1, lc_seen);
     if (ticket >= avail) {
       read_avail(line0, avail, avail_ops);
       if (ticket >= avail) {
-        uint64_t stop = 0;
-        if (lane_id() == 0) stop = ld_rlx_agent(&line0->stop_ticket);
-        if (ticket >= bcast64(stop)) return;
+        uint64_t se = 0, stop = 0;
+        if (lane_id() == 0) {
+          se = ld_rlx_agent(&line0->stop_epoch);
+          wait_mem();
+          stop = ld_rlx_agent(&line0->stop_ticket);
+        }
+        if (bcast64(se) == a.epoch && ticket >= bcast64(stop)) return;
         // nothing published for this ticket yet: back off
         if (idle < 32) {
           ++idle;
@@ -372,9 +380,35 @@ __device__ bool retire_ring(const KArgs& a, uint64_t avail, uint64_t& retired) {
   return moved;
 }
 
+// Releases the workers (every ticket below `tiles0` has run) and reports the
+// exit to the host.
+__device__ void release_workers(const KArgs& a, uint64_t tiles0) {
+  const uint32_t lane = lane_id();
+  if (lane < kReplicas) st_rlx_agent(&a.dctl->avail[0][lane].stop_ticket, tiles0);
+  wait_mem();
+  if (lane < kReplicas) st_rlx_agent(&a.dctl->avail[0][lane].stop_epoch, (uint64_t)a.epoch);
+  if (lane == 0) st_rlx_sys(&a.hctl->exit_tiles, tiles0);
+  wait_mem();
+  if (lane == 0) st_rlx_sys(&a.hctl->exit_epoch, (uint64_t)a.epoch);
+  wait_mem();
+}
+
 __device__ void doorbell_loop(const KArgs& a) {
+  // resume from what earlier launches published and retired
   uint64_t avail0 = 0, avail1 = 0, ret0 = 0, ret1 = 0, tiles0 = 0, tiles1 = 0;
+  if (lane_id() == 0) {
+    avail0 = ld_rlx_agent(&a.dctl->avail[0][0].avail_ops);
+    avail1 = ld_rlx_agent(&a.dctl->avail[1][0].avail_ops);
+    tiles0 = ld_rlx_agent(&a.dctl->avail[0][0].avail_tiles);
+    tiles1 = ld_rlx_agent(&a.dctl->avail[1][0].avail_tiles);
+    ret0 = ld_rlx_agent(&a.dctl->ring[0].retired);
+    ret1 = ld_rlx_agent(&a.dctl->ring[1].retired);
+  }
+  avail0 = bcast64(avail0); avail1 = bcast64(avail1);
+  tiles0 = bcast64(tiles0); tiles1 = bcast64(tiles1);
+  ret0 = bcast64(ret0); ret1 = bcast64(ret1);
   uint64_t beats = 0;
+  uint64_t last_work = now_ticks();
   for (;;) {
     uint64_t t0 = 0, t1 = 0, stop = 0;
     if (lane_id() == 0) {
@@ -392,12 +426,38 @@ __device__ void doorbell_loop(const KArgs& a) {
     work |= retire_ring<1>(a, avail1, ret1);
     ++beats;
     if ((beats & 1023) == 0 && lane_id() == 0) st_rlx_sys(&a.hctl->heartbeat, beats);
-    if (stop && ret0 == t0 && ret1 == t1) {
+    const bool drained = ret0 == t0 && ret1 == t1 && avail0 == t0 && avail1 == t1;
+    if (work) last_work = now_ticks();
+    if (drained && stop) {
       // every published descriptor has retired: release the workers
-      if (lane_id() < kReplicas) st_rlx_agent(&a.dctl->avail[0][lane_id()].stop_ticket, tiles0);
       if (lane_id() == 0) st_rlx_sys(&a.hctl->heartbeat, beats);
-      wait_mem();
+      release_workers(a, tiles0);
       return;
+    }
+    if (drained && a.idle_exit_ticks && now_ticks() - last_work > a.idle_exit_ticks) {
+      // idle for too long: announce the exit, then look at the tails again.
+      // The re-read cannot overtake the announcement on its way to host
+      // memory, and the host reads the announcement after storing a tail, so
+      // either the host sees the announcement (and relaunches after the exit)
+      // or this wave sees the new tail (and cancels).
+      uint64_t n0 = 0, n1 = 0;
+      if (lane_id() == 0) {
+        st_rlx_sys(&a.hctl->exit_req, (uint64_t)a.epoch);
+        wait_mem();
+        n0 = ld_rlx_sys(&a.hctl->tail[0]);
+        n1 = ld_rlx_sys(&a.hctl->tail[1]);
+      }
+      n0 = bcast64(n0);
+      n1 = bcast64(n1);
+      if (n0 == t0 && n1 == t1) {
+        if (lane_id() == 0) st_rlx_sys(&a.hctl->heartbeat, beats);
+        release_workers(a, tiles0);
+        return;
+      }
+      if (lane_id() == 0) st_rlx_sys(&a.hctl->exit_req, (uint64_t)0);
+      wait_mem();
+      last_work = now_ticks();
+      continue;
     }
     if (!work) __builtin_amdgcn_s_sleep(1);
   }

@@ -90,6 +90,63 @@ struct Range {
   uint64_t lo, hi;
 };
 
+// A vector with N elements of inline storage (no heap allocation until it
+// holds more than N).
+template <class T, unsigned N>
+class SmallVec {
+ public:
+  T* begin() { return n_ <= N ? inl_ : ext_.data(); }
+  T* end() { return begin() + n_; }
+  const T* begin() const { return n_ <= N ? inl_ : ext_.data(); }
+  const T* end() const { return begin() + n_; }
+  size_t size() const { return n_; }
+  bool empty() const { return n_ == 0; }
+  T& operator[](size_t i) { return begin()[i]; }
+  const T& operator[](size_t i) const { return begin()[i]; }
+  T& back() { return begin()[n_ - 1]; }
+  void clear() {
+    n_ = 0;
+    ext_.clear();
+  }
+  void push_back(const T& x) {
+    if (n_ < N) {
+      inl_[n_++] = x;
+      return;
+    }
+    if (n_ == N) ext_.assign(inl_, inl_ + N);
+    ext_.push_back(x);
+    ++n_;
+  }
+  // keeps the first k elements
+  void truncate(size_t k) {
+    if (k >= n_) return;
+    if (n_ > N) {
+      if (k <= N) {
+        std::copy(ext_.begin(), ext_.begin() + k, inl_);
+        ext_.clear();
+      } else {
+        ext_.resize(k);
+      }
+    }
+    n_ = (uint32_t)k;
+  }
+  template <class Pred>
+  void remove_if(Pred p) {
+    truncate((size_t)(std::remove_if(begin(), end(), p) - begin()));
+  }
+  void sort_unique() {
+    std::sort(begin(), end());
+    truncate((size_t)(std::unique(begin(), end()) - begin()));
+  }
+
+ private:
+  T inl_[N];
+  uint32_t n_ = 0;
+  std::vector<T> ext_;
+};
+
+typedef SmallVec<uint64_t, 8> DepVec;
+
 struct OpRanges {
   Range w{0, 0};
   Range r[3]{};
@@ -270,28 +327,43 @@ int validate(const gpuos_op& o, uint32_t index) {
 struct Seg {
   uint64_t hi;
   uint64_t writer;
-  std::vector<uint64_t> readers;
+  SmallVec<uint64_t, 4> readers;
 };
 
 class HazardMap {
  public:
   template <class Retired>
-  void access(const Range& rg, uint64_t id, bool write, std::vector<uint64_t>& deps,
-              Retired retired) {
+  void access(const Range& rg, uint64_t id, bool write, DepVec& deps, Retired retired) {
     if (rg.hi <= rg.lo) return;
+    auto it = segs_.lower_bound(rg.lo);
+    if (it != segs_.end() && it->first == rg.lo && it->second.hi == rg.hi) {
+      // the range is exactly one segment (segments never overlap)
+      touch(it->second, id, write, deps, retired);
+      return;
+    }
+    const bool clear_after = it == segs_.end() || it->first >= rg.hi;
+    bool clear_before = true;
+    if (it != segs_.begin()) clear_before = std::prev(it)->second.hi <= rg.lo;
+    if (clear_after && clear_before) {
+      // nothing recorded inside the range yet
+      Seg sg{rg.hi, write ? id : 0, {}};
+      if (!write) sg.readers.push_back(id);
+      segs_.emplace_hint(it, rg.lo, std::move(sg));
+      return;
+    }
     split(rg.lo);
     split(rg.hi);
-    auto it = segs_.lower_bound(rg.lo);
+    it = segs_.lower_bound(rg.lo);
     uint64_t cur = rg.lo;
-    std::vector<std::pair<uint64_t, uint64_t>> gaps;
+    SmallVec<std::pair<uint64_t, uint64_t>, 4> gaps;
     while (it != segs_.end() && it->first < rg.hi) {
       if (it->first > cur) gaps.push_back({cur, it->first});
-      Seg& s = it->second;
-      if (s.writer && !retired(s.writer)) deps.push_back(s.writer);
+      Seg& sg = it->second;
+      if (sg.writer && !retired(sg.writer)) deps.push_back(sg.writer);
       if (write)
-        for (uint64_t r : s.readers)
+        for (uint64_t r : sg.readers)
           if (!retired(r)) deps.push_back(r);
-      cur = s.hi;
+      cur = sg.hi;
       ++it;
     }
     if (cur < rg.hi) gaps.push_back({cur, rg.hi});
@@ -300,21 +372,18 @@ class HazardMap {
       segs_[rg.lo] = Seg{rg.hi, id, {}};
     } else {
       for (auto g : gaps) segs_[g.first] = Seg{g.second, 0, {}};
-      for (auto i2 = segs_.lower_bound(rg.lo); i2 != segs_.end() && i2->first < rg.hi; ++i2) {
-        auto& rd = i2->second.readers;
-        if (rd.empty() || rd.back() != id) rd.push_back(id);
-        if (rd.size() > 32) prune_vec(rd, retired);
-      }
+      for (auto i2 = segs_.lower_bound(rg.lo); i2 != segs_.end() && i2->first < rg.hi; ++i2)
+        add_reader(i2->second, id, retired);
     }
   }
 
   template <class Retired>
   void prune(Retired retired) {
     for (auto it = segs_.begin(); it != segs_.end();) {
-      Seg& s = it->second;
-      if (s.writer && retired(s.writer)) s.writer = 0;
-      prune_vec(s.readers, retired);
-      if (!s.writer && s.readers.empty())
+      Seg& sg = it->second;
+      if (sg.writer && retired(sg.writer)) sg.writer = 0;
+      sg.readers.remove_if(retired);
+      if (!sg.writer && sg.readers.empty())
         it = segs_.erase(it);
       else
         ++it;
@@ -326,8 +395,22 @@ class HazardMap {
 
  private:
   template <class Retired>
-  static void prune_vec(std::vector<uint64_t>& v, Retired retired) {
-    v.erase(std::remove_if(v.begin(), v.end(), [&](uint64_t x) { return retired(x); }), v.end());
+  static void add_reader(Seg& sg, uint64_t id, Retired retired) {
+    if (sg.readers.empty() || sg.readers.back() != id) sg.readers.push_back(id);
+    if (sg.readers.size() > 32) sg.readers.remove_if(retired);
+  }
+
+  template <class Retired>
+  static void touch(Seg& sg, uint64_t id, bool write, DepVec& deps, Retired retired) {
+    if (sg.writer && !retired(sg.writer)) deps.push_back(sg.writer);
+    if (write) {
+      for (uint64_t r : sg.readers)
+        if (!retired(r)) deps.push_back(r);
+      sg.readers.clear();
+      sg.writer = id;
+    } else {
+      add_reader(sg, id, retired);
+    }
   }
 
   void split(uint64_t x) {
@@ -353,7 +436,7 @@ struct Staged {
   gpuos_op op;
   uint64_t id;
   uint32_t ring;
-  std::vector<uint64_t> deps;  // user ids
+  DepVec deps;  // user ids
 };
 
 // A device op after the fusion pass: one descriptor built from user ops
@@ -362,7 +445,7 @@ struct Planned {
   size_t first;
   uint32_t count;
   DevDesc desc;
-  std::vector<uint64_t> deps;  // user ids outside the group
+  DepVec deps;  // user ids outside the group
   uint32_t ring;
 };
 
@@ -400,6 +483,9 @@ struct gpuos_ctx {
   bool stopped = false;     // STOP published; no more submissions
   bool exited = false;      // resident kernel has exited
   bool leaked = false;      // kernel did not exit: memory must not be freed
+  bool timing = false;      // ev_start/ev_end bracket a launch not yet counted
+  uint32_t epoch = 0;       // launches so far
+  KArgs kargs{};
   hipEvent_t ev_start = nullptr, ev_end = nullptr;
   gpuos_stats st{};
 };
@@ -603,8 +689,8 @@ struct ChainState {
   uint64_t chain_in = 0;           // pointer loaded into the accumulator
   uint64_t operands[3] = {0, 0, 0};
   int nops = 0;
-  std::vector<Range> outs;         // output ranges written so far (in order)
-  std::vector<Range> reads;        // every range read by the chain
+  SmallVec<Range, kMaxSteps> outs;   // output ranges written so far (in order)
+  SmallVec<Range, 4> reads;          // every range read by the chain
   uint64_t last_out = 0;
 };
 
@@ -666,6 +752,28 @@ bool try_extend(const gpuos_op& o, ChainState& st, uint8_t& code, uint8_t& fl) {
   return true;
 }
 
+// Streams (non-temporal) elementwise, COPY and fused descriptors whose
+// operands total at least stream_min_kib.
+void mark_streaming(const gpuos_config& cfg, DevDesc& d) {
+  if (cfg.stream_min_kib == 0xFFFFFFFFu) return;
+  const uint64_t es = elem_size(d.dtype);
+  uint64_t bytes = 0;
+  if (d.opcode == OP_FUSED_EW) {
+    uint32_t k = 0;
+    for (int i = 0; i < 4; ++i) k += d.f.in[i] != 0;
+    for (int i = 0; i < kMaxSteps; ++i) k += d.f.out[i] != 0;
+    bytes = (uint64_t)k * d.n * es;
+  } else if (is_elementwise(d.opcode) && d.opcode != GPUOS_OP_GATHER) {
+    const uint64_t ext = (uint64_t)d.n * es;
+    const uint64_t l0 = d.p.src_len[0] ? std::min<uint64_t>(d.p.src_len[0], d.n) * es : ext;
+    const uint64_t l1 = d.p.src_len[1] ? std::min<uint64_t>(d.p.src_len[1], d.n) * es : ext;
+    bytes = ext + (d.p.ptr[1] ? l0 : 0) + (d.p.ptr[2] && is_binary(d.opcode) ? l1 : 0);
+  } else {
+    return;
+  }
+  if (bytes >= (uint64_t)cfg.stream_min_kib * 1024) d.flags |= GPUOS_FLAG_NONTEMPORAL;
+}
+
 void plan_ops(gpuos_ctx* c, size_t begin, size_t end, std::vector<Planned>& plan) {
   const gpuos_config& cfg = c->cfg;
   const bool fuse = cfg.fusion == 1;
@@ -677,7 +785,15 @@ void plan_ops(gpuos_ctx* c, size_t begin, size_t end, std::vector<Planned>& plan
     pl.count = 1;
     pl.ring = s0.ring;
     size_t j = i + 1;
-    if (fuse && fusable(s0.op)) {
+    // a chain needs a next op of the same ring, dtype and size that reads
+    // this op's output
+    bool chain_possible = false;
+    if (fuse && j < end && fusable(s0.op)) {
+      const gpuos_op& nx = c->staged[j].op;
+      chain_possible = c->staged[j].ring == s0.ring && fusable(nx) && nx.dtype == s0.op.dtype &&
+                       nx.n == s0.op.n && (nx.in[0] == s0.op.out || nx.in[1] == s0.op.out);
+    }
+    if (chain_possible) {
       ChainState st;
       const gpuos_op& o0 = s0.op;
       const uint64_t es = elem_size(o0.dtype);
@@ -734,6 +850,7 @@ void plan_ops(gpuos_ctx* c, size_t begin, size_t end, std::vector<Planned>& plan
             const gpuos_op& os = c->staged[i + s].op;
             d.f.step_op[s] = codes[s];
             d.f.fscal[s] = os.alpha;
+            d.flags |= (uint8_t)(os.flags & GPUOS_FLAG_NONTEMPORAL);
             // keep the store unless the op is transient and nothing queued
             // after the chain reads its output
             bool keep = !(os.flags & GPUOS_FLAG_TRANSIENT);
@@ -759,16 +876,107 @@ void plan_ops(gpuos_ctx* c, size_t begin, size_t end, std::vector<Planned>& plan
       encode_plain(s0.op, cfg, c->workers, pl.desc);
       j = i + 1;
     }
+    mark_streaming(cfg, pl.desc);
     // dependencies: union of the members' deps that point outside the group
     const uint64_t gfirst = c->staged[i].id, glast = c->staged[i + pl.count - 1].id;
     for (uint32_t k = 0; k < pl.count; ++k)
       for (uint64_t dep : c->staged[i + k].deps)
         if (dep < gfirst || dep > glast) pl.deps.push_back(dep);
-    std::sort(pl.deps.begin(), pl.deps.end());
-    pl.deps.erase(std::unique(pl.deps.begin(), pl.deps.end()), pl.deps.end());
+    pl.deps.sort_unique();
     plan.push_back(std::move(pl));
     i = i + plan.back().count;
   }
+}
+
+// Launches the resident kernel (epoch + 1), its first ring-0 ticket `base`.
+// HIP events recorded just before and just after the launch on its stream
+// bracket exactly that launch.
+int launch_kernel(gpuos_ctx* c, uint64_t base) {
+  c->kargs.epoch = ++c->epoch;
+  c->kargs.ticket_base = base;
+  hipError_t e = hipEventRecord(c->ev_start, c->stream);
+  if (e == hipSuccess) e = launch_resident(c->kargs, c->blocks, c->stream);
+  if (e == hipSuccess) e = hipEventRecord(c->ev_end, c->stream);
+  if (e != hipSuccess) {
+    c->poisoned = true;
+    c->exited = true;
+    return fail(GPUOS_EDEVICE, "resident launch: %s", hipGetErrorString(e));
+  }
+  c->timing = true;
+  ++c->st.launches;
+  return 0;
+}
+
+// Adds the duration of the last launch, which has ended, to kernel_ns.
+void account_launch(gpuos_ctx* c) {
+  if (!c->timing) return;
+  c->timing = false;
+  float ms = 0.0f;
+  if (hipEventSynchronize(c->ev_end) == hipSuccess &&
+      hipEventElapsedTime(&ms, c->ev_start, c->ev_end) == hipSuccess)
+    c->st.kernel_ns += (uint64_t)((double)ms * 1e6);
+}
+
+// Waits (bounded) for the resident kernel's launch to end.
+int wait_kernel_end(gpuos_ctx* c, int64_t timeout_ns) {
+  const auto t0 = std::chrono::steady_clock::now();
+  for (;;) {
+    const hipError_t e = hipStreamQuery(c->stream);
+    if (e == hipSuccess) return 0;
+    if (e != hipErrorNotReady) {
+      c->exited = true;
+      c->poisoned = true;
+      return fail(GPUOS_EDEVICE, "resident kernel failed: %s", hipGetErrorString(e));
+    }
+    if (timeout_ns >= 0 &&
+        std::chrono::steady_clock::now() - t0 > std::chrono::nanoseconds(timeout_ns)) {
+      c->leaked = true;
+      return fail(GPUOS_ETIMEDOUT, "resident kernel did not exit");
+    }
+    std::this_thread::sleep_for(std::chrono::microseconds(20));
+  }
+}
+
+// Called from every host wait and after every flush: if the kernel has left
+// after an idle period, waits for its launch to end and launches it again.
+// A kernel that ended without announcing an exit has failed.
+int keep_running(gpuos_ctx* c, bool query_stream) {
+  if (c->host_only || c->exited) return 0;
+  bool gone = load_acq(&c->hctl->exit_epoch) == c->epoch;
+  if (!gone && load_acq(&c->hctl->exit_req) == c->epoch) {
+    // the doorbell is deciding whether to leave: it either completes the exit
+    // or withdraws the announcement within microseconds
+    const auto t0 = std::chrono::steady_clock::now();
+    for (;;) {
+      gone = load_acq(&c->hctl->exit_epoch) == c->epoch;
+      if (gone || load_acq(&c->hctl->exit_req) != c->epoch) break;
+      if (std::chrono::steady_clock::now() - t0 > std::chrono::seconds(10)) {
+        c->poisoned = true;
+        return fail(GPUOS_EDEVICE, "resident kernel neither left nor resumed");
+      }
+      cpu_relax();
+    }
+  }
+  if (!gone && query_stream) {
+    const hipError_t e = hipStreamQuery(c->stream);
+    if (e == hipErrorNotReady) return 0;
+    // the exit announcement precedes the end of the launch
+    gone = load_acq(&c->hctl->exit_epoch) == c->epoch;
+    if (!gone || e != hipSuccess) {
+      c->poisoned = true;
+      c->exited = true;
+      return fail(GPUOS_EDEVICE, "resident kernel is no longer running: %s", hipGetErrorString(e));
+    }
+  }
+  if (!gone) return 0;
+  int rc = wait_kernel_end(c, 10ll * 1000 * 1000 * 1000);
+  if (rc) return rc;
+  account_launch(c);
+  if (c->stopped) {
+    c->exited = true;
+    return 0;
+  }
+  return launch_kernel(c, load_acq(&c->hctl->exit_tiles));
 }
 
 // Waits until ring slot for `seq` is free; returns 0, EAGAIN or EDEVICE.
@@ -787,9 +995,9 @@ int wait_ring_space(gpuos_ctx* c, uint32_t ring, uint64_t seq) {
     if (check_device_error(c)) return GPUOS_EDEVICE;
     if (++spins > 256) {
       std::this_thread::yield();
-      if ((spins & 0xffff) == 0 && hipStreamQuery(c->stream) != hipErrorNotReady) {
-        c->poisoned = true;
-        return fail(GPUOS_EDEVICE, "resident kernel is no longer running");
+      if ((spins & 1023) == 0) {
+        const int rc = keep_running(c, (spins & 0xffff) == 0);
+        if (rc) return rc;
       }
     } else {
       cpu_relax();
@@ -816,7 +1024,7 @@ int publish_one(gpuos_ctx* c, Planned& pl) {
   d.check = (uint32_t)seq ^ kDescMagic;
   d.tstart = c->pub_tiles[ring];
   // dependencies -> sequences of the same ring; drop completed ones
-  std::vector<uint64_t> dseq;
+  DepVec dseq;
   for (uint64_t dep : pl.deps) {
     if (id_retired(c, dep)) continue;
     const uint64_t v = c->idseq[dep - c->id_base];
@@ -826,17 +1034,21 @@ int publish_one(gpuos_ctx* c, Planned& pl) {
       // a dependency across rings is honoured on the host: wait for it
       publish_tail(c, dring);
       publish_tail(c, ring);
+      uint32_t spins = 0;
       while (s > completed_of(c, dring)) {
         if (check_device_error(c)) return GPUOS_EDEVICE;
         if (c->host_only) return fail(GPUOS_EAGAIN, "cross-ring dependency pending");
+        if ((++spins & 1023) == 0) {
+          const int rc2 = keep_running(c, (spins & 0xffff) == 0);
+          if (rc2) return rc2;
+        }
         std::this_thread::yield();
       }
       continue;
     }
     dseq.push_back(s);
   }
-  std::sort(dseq.begin(), dseq.end());
-  dseq.erase(std::unique(dseq.begin(), dseq.end()), dseq.end());
+  dseq.sort_unique();
   if (dseq.size() <= 4) {
     for (size_t k = 0; k < dseq.size(); ++k) d.deps[k] = dseq[k];
   } else {
@@ -872,6 +1084,9 @@ int flush_impl(gpuos_ctx* c) {
   publish_tail(c, 0);
   publish_tail(c, 1);
   c->staged.erase(c->staged.begin(), c->staged.begin() + done_ops);
+  // the tail stores above come before the look at the exit announcement
+  std::atomic_thread_fence(std::memory_order_seq_cst);
+  if (!rc) rc = keep_running(c, false);
   return rc;
 }
 
@@ -937,6 +1152,8 @@ int apply_config(const gpuos_config* in, gpuos_config& out) {
   if (in->block_on_full) out.block_on_full = in->block_on_full;
   if (in->max_fuse) out.max_fuse = in->max_fuse;
   if (in->priority) out.priority = in->priority;
+  if (in->idle_exit_ms) out.idle_exit_ms = in->idle_exit_ms;
+  if (in->stream_min_kib) out.stream_min_kib = in->stream_min_kib;
   const uint32_t rs = out.ring_slots;
   if (rs < 64 || rs > (1u << 18) || (rs & (rs - 1)))
     return fail(GPUOS_EINVAL, "ring_slots must be a power of two in [64, 2^18]");
@@ -991,10 +1208,8 @@ int sync_impl(gpuos_ctx* c, uint64_t upto, int64_t timeout_ns) {
             return fail(GPUOS_ETIMEDOUT, "sync timed out: ring %d at %llu of %llu", r,
                         (unsigned long long)completed_of(c, r), (unsigned long long)target[r]);
         }
-        if (hipStreamQuery(c->stream) != hipErrorNotReady) {
-          c->poisoned = true;
-          return fail(GPUOS_EDEVICE, "resident kernel is no longer running");
-        }
+        const int rc = keep_running(c, (spins & 0xffff) == 0);
+        if (rc) return rc;
       }
       std::this_thread::yield();
     }
@@ -1028,6 +1243,8 @@ void gpuos_config_default(gpuos_config* cfg) {
   cfg->block_on_full = 1;
   cfg->max_fuse = 8;
   cfg->priority = 1;
+  cfg->idle_exit_ms = 200;
+  cfg->stream_min_kib = 32768;
 }
 
 int gpuos_create(int device, const gpuos_config* cfg_in, gpuos_ctx** out) {
@@ -1108,7 +1325,7 @@ int gpuos_create(int device, const gpuos_config* cfg_in, gpuos_ctx** out) {
       auto* img = new DevCtl();
       memset(img, 0, sizeof *img);
       for (int r = 0; r < kRings; ++r)
-        for (uint32_t k = 0; k < kReplicas; ++k) img->avail[r][k].stop_ticket = ~0ull;
+        for (uint32_t k = 0; k < kReplicas; ++k) img->avail[r][k].stop_ticket = ~0ull;  // epoch 0
       e = hipMemcpy(c->dctl, img, sizeof(DevCtl), hipMemcpyHostToDevice);
       delete img;
       for (int r = 0; r < kRings && e == hipSuccess; ++r) {
@@ -1123,7 +1340,7 @@ int gpuos_create(int device, const gpuos_config* cfg_in, gpuos_ctx** out) {
       }
     }
     if (!rc && e == hipSuccess) {
-      KArgs a{};
+      KArgs& a = c->kargs;
       for (int r = 0; r < kRings; ++r) {
         a.hdesc[r] = (const DevDesc*)dev_ptr(c->hdesc[r]);
         a.hends[r] = (const uint64_t*)dev_ptr(c->hends[r]);
@@ -1140,10 +1357,11 @@ int gpuos_create(int device, const gpuos_config* cfg_in, gpuos_ctx** out) {
       a.ends_mask = 2 * c->cap - 1;
       a.workers = c->workers;
       a.lc_enabled = cfg.priority == 1 ? 1u : 0u;
+      // s_memrealtime counts at 100 MHz
+      a.idle_exit_ticks = cfg.idle_exit_ms == 0xFFFFFFFFu ? 0 : (uint64_t)cfg.idle_exit_ms * 100000u;
       e = hipEventCreate(&c->ev_start);
       if (e == hipSuccess) e = hipEventCreate(&c->ev_end);
-      if (e == hipSuccess) e = hipEventRecord(c->ev_start, c->stream);
-      if (e == hipSuccess) e = launch_resident(a, c->blocks, c->stream);
+      if (e == hipSuccess) rc = launch_kernel(c, 0);
     }
     if (!rc && e != hipSuccess) rc = fail(GPUOS_EDEVICE, "create: %s", hipGetErrorString(e));
     if (rc) {
@@ -1215,11 +1433,11 @@ int gpuos_submit(gpuos_ctx* c, const gpuos_op* ops, uint32_t n, uint64_t* ids_ou
       c->hazards.access(R.w, s.id, true, s.deps, retired);
       // reads recorded above also list this op as a reader of its own output
       // range when it runs in place; drop self-dependencies
-      s.deps.erase(std::remove(s.deps.begin(), s.deps.end(), s.id), s.deps.end());
+      const uint64_t self = s.id;
+      s.deps.remove_if([self](uint64_t x) { return x == self; });
       c->st.deps_auto += s.deps.size() - before;
     }
-    std::sort(s.deps.begin(), s.deps.end());
-    s.deps.erase(std::unique(s.deps.begin(), s.deps.end()), s.deps.end());
+    s.deps.sort_unique();
     c->idseq.push_back(0);
     if (ids_out) ids_out[i] = s.id;
     c->staged.push_back(std::move(s));
@@ -1252,7 +1470,9 @@ int gpuos_query(gpuos_ctx* c, uint64_t id) {
   if (!c) return fail(GPUOS_EINVAL, "null context");
   if (id == 0 || id >= c->next_id) return fail(GPUOS_EINVAL, "query: unknown id");
   if (check_device_error(c)) return GPUOS_EDEVICE;
-  return id_retired(c, id) ? 1 : 0;
+  if (id_retired(c, id)) return 1;
+  const int rc = keep_running(c, false);
+  return rc ? rc : 0;
 }
 
 int gpuos_get_stats(gpuos_ctx* c, gpuos_stats* out) {
@@ -1320,30 +1540,11 @@ int gpuos_stop(gpuos_ctx* c, int64_t timeout_ns) {
     std::atomic_thread_fence(std::memory_order_release);
     store_rel(&c->hctl->stop_req, 1);
   }
-  // wait for the kernel to exit
-  const auto t0 = std::chrono::steady_clock::now();
-  for (;;) {
-    hipError_t e = hipStreamQuery(c->stream);
-    if (e == hipSuccess) break;
-    if (e != hipErrorNotReady) {
-      c->exited = true;
-      c->poisoned = true;
-      return fail(GPUOS_EDEVICE, "resident kernel failed: %s", hipGetErrorString(e));
-    }
-    if (timeout_ns >= 0 &&
-        std::chrono::steady_clock::now() - t0 > std::chrono::nanoseconds(timeout_ns)) {
-      c->leaked = true;
-      return fail(GPUOS_ETIMEDOUT, "resident kernel did not exit");
-    }
-    std::this_thread::sleep_for(std::chrono::microseconds(20));
-  }
+  // wait for the kernel to exit (it may already have left after idling)
+  const int r3 = wait_kernel_end(c, timeout_ns);
+  if (r3) return r3;
   c->exited = true;
-  if (c->ev_end && hipEventRecord(c->ev_end, c->stream) == hipSuccess &&
-      hipEventSynchronize(c->ev_end) == hipSuccess) {
-    float ms = 0.0f;
-    if (hipEventElapsedTime(&ms, c->ev_start, c->ev_end) == hipSuccess)
-      c->st.kernel_ns = (uint64_t)((double)ms * 1e6);
-  }
+  account_launch(c);
   if (check_device_error(c)) return GPUOS_EDEVICE;
   return rc;
 }

@@ -685,38 +685,63 @@ __device__ __forceinline__ void spin_tile(D d, uint32_t) {
 // opcode switch over the fixed op table (uniform per wave: a scalar branch,
 // no indirect call).  Returns a device error code, 0 on success.
 
+// Streaming ops (elementwise, copy, fused chains) under cache policies CPL /
+// CPS; returns false for any other opcode.
+template <int CPL, int CPS, class D>
+__device__ __forceinline__ bool exec_stream(uint32_t op, bool bf, D d, uint32_t t, uint32_t& err) {
+  constexpr int F = GPUOS_F32, B = GPUOS_BF16;
+  err = 0;
+  switch (op) {
+    case GPUOS_OP_COPY:
+      if (bf) copy_tile<2, CPL, CPS>(d, t); else copy_tile<4, CPL, CPS>(d, t);
+      return true;
+    case GPUOS_OP_ADD:
+      if (bf) ew_tile<GPUOS_OP_ADD, B, CPL, CPS>(d, t); else ew_tile<GPUOS_OP_ADD, F, CPL, CPS>(d, t);
+      return true;
+    case GPUOS_OP_MUL:
+      if (bf) ew_tile<GPUOS_OP_MUL, B, CPL, CPS>(d, t); else ew_tile<GPUOS_OP_MUL, F, CPL, CPS>(d, t);
+      return true;
+    case GPUOS_OP_SCALE:
+      if (bf) ew_tile<GPUOS_OP_SCALE, B, CPL, CPS>(d, t); else ew_tile<GPUOS_OP_SCALE, F, CPL, CPS>(d, t);
+      return true;
+    case GPUOS_OP_RELU:
+      if (bf) ew_tile<GPUOS_OP_RELU, B, CPL, CPS>(d, t); else ew_tile<GPUOS_OP_RELU, F, CPL, CPS>(d, t);
+      return true;
+    case GPUOS_OP_EXP:
+      if (bf) ew_tile<GPUOS_OP_EXP, B, CPL, CPS>(d, t); else ew_tile<GPUOS_OP_EXP, F, CPL, CPS>(d, t);
+      return true;
+    case GPUOS_OP_SILU_MUL:
+      if (bf) ew_tile<GPUOS_OP_SILU_MUL, B, CPL, CPS>(d, t); else ew_tile<GPUOS_OP_SILU_MUL, F, CPL, CPS>(d, t);
+      return true;
+    case OP_FUSED_EW:  // fp32 chains only (the fusion pass leaves bf16 ops unfused)
+      if (bf) err = (uint32_t)DERR_BAD_OPCODE; else fused_tile<F, CPL, CPS>(d, t);
+      return true;
+    default:
+      return false;
+  }
+}
+
+// Cache-policy bit that marks an access non-temporal (streamed: its lines
+// are the first to be evicted).
+constexpr int CP_NT = 2;
+
 template <int CPL, int CPS, class D>
 __device__ uint32_t exec_tile(D d, uint32_t t) {
   const uint32_t w0 = d(0);
-  const uint32_t op = w0 & 0xffu, dt = (w0 >> 8) & 0xffu;
+  const uint32_t op = w0 & 0xffu, dt = (w0 >> 8) & 0xffu, fl = (w0 >> 16) & 0xffu;
   const bool bf = dt == GPUOS_BF16;
   constexpr int F = GPUOS_F32, B = GPUOS_BF16;
+  uint32_t err = 0;
+  if (fl & GPUOS_FLAG_NONTEMPORAL) {
+    if (exec_stream<CPL | CP_NT, CPS | CP_NT>(op, bf, d, t, err)) return err;
+  } else {
+    if (exec_stream<CPL, CPS>(op, bf, d, t, err)) return err;
+  }
   switch (op) {
     case GPUOS_OP_NOP:
       return 0;
-    case GPUOS_OP_COPY:
-      if (bf) copy_tile<2, CPL, CPS>(d, t); else copy_tile<4, CPL, CPS>(d, t);
-      return 0;
     case GPUOS_OP_GATHER:
       return bf ? gather_tile<2, CPL, CPS>(d, t) : gather_tile<4, CPL, CPS>(d, t);
-    case GPUOS_OP_ADD:
-      if (bf) ew_tile<GPUOS_OP_ADD, B, CPL, CPS>(d, t); else ew_tile<GPUOS_OP_ADD, F, CPL, CPS>(d, t);
-      return 0;
-    case GPUOS_OP_MUL:
-      if (bf) ew_tile<GPUOS_OP_MUL, B, CPL, CPS>(d, t); else ew_tile<GPUOS_OP_MUL, F, CPL, CPS>(d, t);
-      return 0;
-    case GPUOS_OP_SCALE:
-      if (bf) ew_tile<GPUOS_OP_SCALE, B, CPL, CPS>(d, t); else ew_tile<GPUOS_OP_SCALE, F, CPL, CPS>(d, t);
-      return 0;
-    case GPUOS_OP_RELU:
-      if (bf) ew_tile<GPUOS_OP_RELU, B, CPL, CPS>(d, t); else ew_tile<GPUOS_OP_RELU, F, CPL, CPS>(d, t);
-      return 0;
-    case GPUOS_OP_EXP:
-      if (bf) ew_tile<GPUOS_OP_EXP, B, CPL, CPS>(d, t); else ew_tile<GPUOS_OP_EXP, F, CPL, CPS>(d, t);
-      return 0;
-    case GPUOS_OP_SILU_MUL:
-      if (bf) ew_tile<GPUOS_OP_SILU_MUL, B, CPL, CPS>(d, t); else ew_tile<GPUOS_OP_SILU_MUL, F, CPL, CPS>(d, t);
-      return 0;
     case GPUOS_OP_ROW_SUM:
       if (bf) row_tile<GPUOS_OP_ROW_SUM, B, CPL, CPS>(d, t); else row_tile<GPUOS_OP_ROW_SUM, F, CPL, CPS>(d, t);
       return 0;
@@ -741,10 +766,6 @@ __device__ uint32_t exec_tile(D d, uint32_t t) {
       return 0;
     case GPUOS_OP_SPIN:
       spin_tile(d, t);
-      return 0;
-    case OP_FUSED_EW:  // fp32 chains only (the fusion pass leaves bf16 ops unfused)
-      if (bf) return (uint32_t)DERR_BAD_OPCODE;
-      fused_tile<F, CPL, CPS>(d, t);
       return 0;
     default:
       return (uint32_t)DERR_BAD_OPCODE;

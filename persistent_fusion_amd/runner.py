@@ -2,9 +2,10 @@
 
 Device memory for the workload's buffers comes from torch (allocation and
 host<->device copies only); every op runs in the HIP kernels behind
-:mod:`persistent_fusion_amd.gpuos`.  The resident context must be destroyed
-before anything waits on the whole device (``torch.cuda.synchronize()``),
-because the resident kernel only exits in ``gpuos_destroy``.
+:mod:`persistent_fusion_amd.gpuos`.  A wait on the whole device
+(``torch.cuda.synchronize()``) while a context is open also waits for the
+resident kernel, which leaves only after its idle period (or in
+``gpuos_stop`` / ``gpuos_destroy``); destroy contexts first.
 """
 
 from __future__ import annotations

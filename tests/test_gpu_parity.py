@@ -136,6 +136,27 @@ def test_elementwise_ops_ragged(kind, dtype):
         check(wl, got)
 
 
+@pytest.mark.parametrize("kind", ["add", "mul", "scale", "relu", "exp", "copy", "silu_mul"])
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_elementwise_ops_streamed(kind, dtype):
+    """The non-temporal (streamed) variants of the elementwise bodies."""
+    _need_gpu()
+    for n in (1, 4097, (1 << 20) + 3):
+        say(f"streamed {kind} {dtype} n={n}")
+        wl = _ew_workload(kind, dtype, n, seed=n + 1)
+        got = runner.run_resident(wl, stream_min_kib=1)
+        check(wl, got)
+
+
+@pytest.mark.parametrize("n", [63, 1_000_003])
+def test_fused_chain_streamed(n):
+    _need_gpu()
+    say(f"streamed fused chain n={n}")
+    wl = workloads.gen_fused_chain(seed=3, n=n)
+    got = runner.run_resident(wl, outputs=["y"], stream_min_kib=1)
+    check(wl, got, ["y"])
+
+
 @pytest.mark.parametrize("kind", ["add", "relu", "copy"])
 def test_cyclic_sources(kind):
     _need_gpu()
