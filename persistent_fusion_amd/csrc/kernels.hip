@@ -60,7 +60,7 @@ __device__ __forceinline__ uint32_t slot_of(uint64_t seq, uint32_t mask) {
   return (uint32_t)((seq - 1) & mask);
 }
 
-__device__ void report_error(const KArgs& a, uint32_t ring, uint64_t seq, uint64_t code) {
+__device__ __forceinline__ void report_error(const KArgs& a, uint32_t ring, uint64_t seq, uint64_t code) {
   if (lane_id() == 0) {
     st_rlx_sys(&a.hctl->error_seq, ((uint64_t)ring << 62) | seq);
     st_rel_sys(&a.hctl->error, code);
@@ -80,7 +80,7 @@ __device__ void report_error(const KArgs& a, uint32_t ring, uint64_t seq, uint64
 // hi <= retired + C at publication) cannot retire before this wave runs it, so
 // the host can publish at most up to X - 1 + C < s + 2C for any probed s.
 template <int RING>
-__device__ uint64_t find_seq(const KArgs& a, uint64_t ticket, uint64_t lo, uint64_t hi) {
+__device__ __forceinline__ uint64_t find_seq(const KArgs& a, uint64_t ticket, uint64_t lo, uint64_t hi) {
   const uint32_t lane = lane_id();
   const uint32_t mask = a.cap_mask;
   if (hi > (uint64_t)mask + 1 && lo < hi - mask - 1) lo = hi - mask - 1;
@@ -107,7 +107,7 @@ __device__ uint64_t find_seq(const KArgs& a, uint64_t ticket, uint64_t lo, uint6
 // in the first 128-byte line, the check word in the second) and re-read from
 // the device coherence point.
 template <int RING>
-__device__ void fetch_desc(const KArgs& a, uint64_t seq, Cached& c) {
+__device__ __forceinline__ void fetch_desc(const KArgs& a, uint64_t seq, Cached& c) {
   const rsrc_t r = make_rsrc(reinterpret_cast<uint64_t>(&a.ddesc[RING][slot_of(seq, a.cap_mask)]));
   const uint32_t off = 4u * lane_id();
   uint32_t dw = ld32<CP_DEFAULT>(r, off);
@@ -129,7 +129,7 @@ __device__ void fetch_desc(const KArgs& a, uint64_t seq, Cached& c) {
 // Polls are device-scope loads (coherent without invalidating L2); tensor data
 // is read with device-coherent loads, so no acquire fence is needed after.
 template <int RING>
-__device__ void wait_deps(const KArgs& a, const Cached& c) {
+__device__ __forceinline__ void wait_deps(const KArgs& a, const Cached& c) {
   const SDesc d = c.desc();
   const uint32_t mask = a.cap_mask;
 #pragma unroll
@@ -153,7 +153,7 @@ __device__ void wait_deps(const KArgs& a, const Cached& c) {
 // device-coherent write-through stores, so waiting for their acknowledgement
 // makes them visible on every XCD before the count moves (no L2 writeback).
 template <int RING>
-__device__ void finish_tile(const KArgs& a, const Cached& c, uint32_t tile) {
+__device__ __forceinline__ void finish_tile(const KArgs& a, const Cached& c, uint32_t tile) {
   const uint32_t slot = slot_of(c.seq, a.cap_mask);
   const uint32_t cap = a.cap_mask + 1;
   const SDesc d = c.desc();
@@ -196,7 +196,7 @@ __device__ void finish_tile(const KArgs& a, const Cached& c, uint32_t tile) {
 }
 
 template <int RING>
-__device__ void run_ticket(const KArgs& a, uint64_t ticket, Cached& c) {
+__device__ __forceinline__ void run_ticket(const KArgs& a, uint64_t ticket, Cached& c) {
   if (!c.deps_ok) {
     wait_deps<RING>(a, c);
     c.deps_ok = 1;
@@ -212,7 +212,7 @@ __device__ void run_ticket(const KArgs& a, uint64_t ticket, Cached& c) {
 
 // Maps a runnable ticket to its descriptor (refreshing the cache if needed).
 template <int RING>
-__device__ void map_ticket(const KArgs& a, uint64_t ticket, uint64_t avail_ops, Cached& c) {
+__device__ __forceinline__ void map_ticket(const KArgs& a, uint64_t ticket, uint64_t avail_ops, Cached& c) {
   if (c.seq != 0 && ticket < c.end) return;
   const uint64_t seq = find_seq<RING>(a, ticket, c.seq, avail_ops);
   fetch_desc<RING>(a, seq, c);
@@ -235,7 +235,7 @@ __device__ __forceinline__ void read_avail(const AvailLine* l, uint64_t& tiles, 
 // never holds a priority ticket with no work behind it, and every wave drains
 // priority tiles before returning to its own best-effort ticket.  `seen` is
 // the published count at which this wave last found the ring empty.
-__device__ void service_lc(const KArgs& a, const AvailLine* line, Cached& c, uint64_t& seen) {
+__device__ __forceinline__ void service_lc(const KArgs& a, const AvailLine* line, Cached& c, uint64_t& seen) {
   DevRing* R = &a.dctl->ring[1];
   for (;;) {
     uint64_t av = 0;
@@ -265,7 +265,7 @@ __device__ void service_lc(const KArgs& a, const AvailLine* line, Cached& c, uin
   }
 }
 
-__device__ void worker_loop(const KArgs& a, uint32_t w, lds_u32* slot0, lds_u32* slot1) {
+__device__ __forceinline__ void worker_loop(const KArgs& a, uint32_t w, lds_u32* slot0, lds_u32* slot1) {
   const AvailLine* line0 = &a.dctl->avail[0][w % kReplicas];
   const AvailLine* line1 = &a.dctl->avail[1][w % kReplicas];
   Cached c0{0, 0, 0, slot0, 0}, c1{0, 0, 0, slot1, 0};
@@ -312,7 +312,7 @@ __device__ void worker_loop(const KArgs& a, uint32_t w, lds_u32* slot0, lds_u32*
 // ring: 16-byte system-scope loads, four descriptors per wave-wide load and
 // up to 32 in flight, written through to the device coherence point.
 template <int RING>
-__device__ void copy_descs(const KArgs& a, uint64_t from, uint64_t to) {
+__device__ __forceinline__ void copy_descs(const KArgs& a, uint64_t from, uint64_t to) {
   const uint32_t mask = a.cap_mask;
   const uint32_t lane = lane_id();
   const rsrc_t hr = make_rsrc(reinterpret_cast<uint64_t>(a.hdesc[RING]));
@@ -334,7 +334,7 @@ __device__ void copy_descs(const KArgs& a, uint64_t from, uint64_t to) {
 }
 
 template <int RING>
-__device__ bool publish_ring(const KArgs& a, uint64_t tail, uint64_t& avail, uint64_t& avail_tiles) {
+__device__ __forceinline__ bool publish_ring(const KArgs& a, uint64_t tail, uint64_t& avail, uint64_t& avail_tiles) {
   if (tail <= avail) return false;
   const uint32_t mask = a.cap_mask;
   const uint32_t lane = lane_id();
@@ -358,7 +358,7 @@ __device__ bool publish_ring(const KArgs& a, uint64_t tail, uint64_t& avail, uin
 }
 
 template <int RING>
-__device__ bool retire_ring(const KArgs& a, uint64_t avail, uint64_t& retired) {
+__device__ __forceinline__ bool retire_ring(const KArgs& a, uint64_t avail, uint64_t& retired) {
   const uint32_t mask = a.cap_mask;
   const uint32_t lane = lane_id();
   bool moved = false;
@@ -382,7 +382,7 @@ __device__ bool retire_ring(const KArgs& a, uint64_t avail, uint64_t& retired) {
 
 // Releases the workers (every ticket below `tiles0` has run) and reports the
 // exit to the host.
-__device__ void release_workers(const KArgs& a, uint64_t tiles0) {
+__device__ __forceinline__ void release_workers(const KArgs& a, uint64_t tiles0) {
   const uint32_t lane = lane_id();
   if (lane < kReplicas) st_rlx_agent(&a.dctl->avail[0][lane].stop_ticket, tiles0);
   wait_mem();
@@ -393,7 +393,7 @@ __device__ void release_workers(const KArgs& a, uint64_t tiles0) {
   wait_mem();
 }
 
-__device__ void doorbell_loop(const KArgs& a) {
+__device__ __forceinline__ void doorbell_loop(const KArgs& a) {
   // resume from what earlier launches published and retired
   uint64_t avail0 = 0, avail1 = 0, ret0 = 0, ret1 = 0, tiles0 = 0, tiles1 = 0;
   if (lane_id() == 0) {

@@ -153,7 +153,7 @@ constexpr bool ew_binary() {
 // cyclically, or a misaligned operand, uses the per-element path with the
 // same interleaving.
 template <int OP, int DT, int CPL, int CPS, class D>
-__device__ __attribute__((noinline)) void ew_tile(D d, uint32_t t) {
+__device__ __forceinline__ void ew_tile(D d, uint32_t t) {
   using T = DTr<DT, CPL, CPS>;
   constexpr int V = T::V;
   constexpr bool BIN = ew_binary<OP>();
@@ -212,7 +212,7 @@ __device__ __forceinline__ void copy_elem(rsrc_t dst, uint32_t i, rsrc_t src, ui
 
 // Bit copy of elements of ES bytes, with cyclic source (interleaved tiles).
 template <int ES, int CPL, int CPS, class D>
-__device__ __attribute__((noinline)) void copy_tile(D d, uint32_t t) {
+__device__ __forceinline__ void copy_tile(D d, uint32_t t) {
   const uint32_t n = d(1), ntiles = d(6);
   const rsrc_t out = make_rsrc(d.q(18)), a = make_rsrc(d.q(20));
   const uint32_t ca = d(26);
@@ -239,7 +239,7 @@ __device__ __attribute__((noinline)) void copy_tile(D d, uint32_t t) {
 
 // out[k] = x[idx[k]]; returns an error code if any index is out of range.
 template <int ES, int CPL, int CPS, class D>
-__device__ __attribute__((noinline)) uint32_t gather_tile(D d, uint32_t t) {
+__device__ __forceinline__ uint32_t gather_tile(D d, uint32_t t) {
   const uint32_t n = d(1), ntiles = d(6);
   const rsrc_t out = make_rsrc(d.q(18)), x = make_rsrc(d.q(20)), idx = make_rsrc(d.q(24));
   const int64_t bound = (int64_t)d(26);
@@ -333,7 +333,7 @@ __device__ __forceinline__ uint32_t fused_apply(const FusedProg& P, int s, float
 }
 
 template <int DT, int CPL, int CPS, class D>
-__device__ __attribute__((noinline)) void fused_tile(D d, uint32_t t) {
+__device__ __forceinline__ void fused_tile(D d, uint32_t t) {
   static_assert(DT == GPUOS_F32, "fused chains are fp32");
   using T = DTr<DT, CPL, CPS>;
   constexpr int V = T::V;
@@ -415,7 +415,7 @@ struct RowReader {
 };
 
 template <int OP, int DT, int CPL, int CPS, class D>
-__device__ __attribute__((noinline)) void row_tile(D d, uint32_t t) {
+__device__ __forceinline__ void row_tile(D d, uint32_t t) {
   using T = DTr<DT, CPL, CPS>;
   const uint32_t rows = d(2), L = d(3), tile = d(7);
   const uint32_t r0 = t * tile;
@@ -473,7 +473,7 @@ __device__ __attribute__((noinline)) void row_tile(D d, uint32_t t) {
 // owns whole (i, i + h/2) pairs, so the op may run in place.
 
 template <int DT, int CPL, int CPS, class D>
-__device__ __attribute__((noinline)) void rope_tile(D d, uint32_t) {
+__device__ __forceinline__ void rope_tile(D d, uint32_t) {
   using T = DTr<DT, CPL, CPS>;
   const uint32_t heads = d(2), hd = d(3), half = hd / 2;
   const rsrc_t out = make_rsrc(d.q(18)), in = make_rsrc(d.q(20)), tab = make_rsrc(d.q(24));
@@ -509,7 +509,7 @@ __device__ __forceinline__ void load_x8(rsrc_t x, uint32_t k, float (&v)[8]) {
 }
 
 template <int DT, int CPL, int CPS, class D>
-__device__ __attribute__((noinline)) void gemv_tile(D d, uint32_t t) {
+__device__ __forceinline__ void gemv_tile(D d, uint32_t t) {
   using T = DTr<DT, CPL, CPS>;
   const uint32_t M = d(30), K = d(31), tile = d(7);
   const rsrc_t out = make_rsrc(d.q(18)), x = make_rsrc(d.q(20)), W = make_rsrc(d.q(24));
@@ -592,7 +592,7 @@ __device__ __forceinline__ void score_rows_fast(D d, uint32_t j0, uint32_t j1) {
 }
 
 template <int DT, int CPL, int CPS, class D>
-__device__ __attribute__((noinline)) void attn_score_tile(D d, uint32_t t) {
+__device__ __forceinline__ void attn_score_tile(D d, uint32_t t) {
   using T = DTr<DT, CPL, CPS>;
   const uint32_t H = d(30), Dh = d(31), S = d(32), tile = d(7);
   const uint32_t j0 = t * tile;
@@ -623,7 +623,7 @@ __device__ __attribute__((noinline)) void attn_score_tile(D d, uint32_t t) {
 // attention output: out[h*Dh + c] = sum_j p[h, j] V[j, h*Dh + c]; a tile is
 // `tile` 8-column chunks; lanes split the key positions.
 template <int DT, int CPL, int CPS, class D>
-__device__ __attribute__((noinline)) void attn_av_tile(D d, uint32_t t) {
+__device__ __forceinline__ void attn_av_tile(D d, uint32_t t) {
   using T = DTr<DT, CPL, CPS>;
   const uint32_t H = d(30), Dh = d(31), S = d(32), tile = d(7);
   const uint32_t HD = H * Dh;
@@ -726,7 +726,7 @@ __device__ __forceinline__ bool exec_stream(uint32_t op, bool bf, D d, uint32_t 
 constexpr int CP_NT = 2;
 
 template <int CPL, int CPS, class D>
-__device__ uint32_t exec_tile(D d, uint32_t t) {
+__device__ __forceinline__ uint32_t exec_tile(D d, uint32_t t) {
   const uint32_t w0 = d(0);
   const uint32_t op = w0 & 0xffu, dt = (w0 >> 8) & 0xffu, fl = (w0 >> 16) & 0xffu;
   const bool bf = dt == GPUOS_BF16;
