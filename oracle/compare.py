@@ -9,9 +9,13 @@ Matching rule:
   must be equal, except that any NaN matches any NaN;
 * tolerance class (EXP, reductions, dot products, SILU_MUL): both values must
   have the same class (NaN, +inf, -inf, finite) and finite values must satisfy
-  ``|g - o| <= rtol * max(|o|, s)`` where ``s`` is the oracle's error scale for
-  the element (sum of |terms| for sums and dot products) and ``rtol`` is 1e-5
-  for fp32 outputs and 1e-2 for bf16 outputs.
+  ``|g - o| <= max(rtol * max(|o|, s), 2 * u)`` where ``s`` is the oracle's
+  error scale for the element (sum of |terms| for sums and dot products),
+  ``rtol`` is 1e-5 for fp32 outputs and 1e-2 for bf16 outputs, and ``u`` is
+  the spacing of the output type's subnormal numbers (2**-149 for fp32,
+  2**-133 for bf16).  Below the normal range a format keeps a fixed absolute
+  spacing and ever fewer significant bits, so no relative bound is reachable
+  there; a result within two subnormal steps of the exact value is accepted.
 """
 
 from __future__ import annotations
@@ -24,6 +28,8 @@ import numpy as np
 from .interpreter import bf16_to_f32
 
 RTOL = {"f32": 1e-5, "bf16": 1e-2}
+# spacing of the subnormal numbers of each output type
+SUBNORMAL_STEP = {"f32": 2.0 ** -149, "bf16": 2.0 ** -133}
 
 
 @dataclass
@@ -92,6 +98,7 @@ def compare(got: np.ndarray, want: np.ndarray, dtype: str,
         err = np.zeros_like(gf)
         with np.errstate(invalid="ignore"):
             bound = rtol * np.maximum(np.abs(wf), np.where(np.isfinite(s), s, 0.0))
+            bound = np.maximum(bound, 2.0 * SUBNORMAL_STEP.get(dtype, 0.0))
             err[fin] = np.abs(gf[fin] - wf[fin])
             rel = np.where(bound > 0, err / np.where(bound > 0, bound, 1.0), np.where(err > 0, np.inf, 0.0))
         b = (cls_g != cls_w) | (fin & (err > bound))

@@ -641,6 +641,37 @@ def test_compare_flags_one_ulp_in_exact_class_and_accepts_within_tolerance():
     assert not compare(np.array([-0.0], np.float32), np.array([0.0], np.float32), "f32").ok
 
 
+def test_compare_uses_the_subnormal_spacing_below_the_normal_range():
+    # fp32 subnormals are multiples of 2**-149: a relative bound means nothing
+    # there, so the tolerance class accepts two steps of that spacing
+    want = np.array([3.377129299022809e-43, 2.0 ** -149, 1e-40, 1.0], np.float32)
+    scale = np.abs(want).astype(np.float64)
+    for steps, ok in ((1, True), (2, True), (3, False)):
+        got = want.copy()
+        got.view(np.uint32)[0] += steps
+        assert compare(got, want, "f32", scale).ok is ok, steps
+    got = want.copy()
+    got[1] = 0.0  # one step below the smallest subnormal
+    assert compare(got, want, "f32", scale).ok
+    got = want.copy()
+    got[2] = 0.0  # a subnormal of 1e-40 flushed to zero is far more than two steps
+    assert not compare(got, want, "f32", scale).ok
+    got = want.copy()
+    got.view(np.uint32)[3] += 3  # normal range: the relative bound is unchanged
+    assert compare(got, want, "f32", scale).ok
+    got[3] = np.float32(1.0 + 3e-5)
+    assert not compare(got, want, "f32", scale).ok
+    # the exact class still needs equal bits
+    got = want.copy()
+    got.view(np.uint32)[0] += 1
+    assert not compare(got, want, "f32").ok
+    # bf16 subnormals are multiples of 2**-133
+    wb = np.array([0x0005, 0x3F80], np.uint16)
+    sb = np.abs(bf16_to_f32(wb)).astype(np.float64)
+    assert compare(np.array([0x0007, 0x3F80], np.uint16), wb, "bf16", sb).ok
+    assert not compare(np.array([0x0008, 0x3F80], np.uint16), wb, "bf16", sb).ok
+
+
 # ----------------------------------------------------------------------------
 # generators
 
