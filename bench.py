@@ -191,6 +191,215 @@ def queue_leg(reps_n, device=0):
             "effective_gb_per_s": round(wl.meta["bytes"] / med / 1e9, 1)}
 
 
+class _NoIds(dict):
+    """Ids of earlier groups for per-op launches: none (stream order already
+    covers every dependency)."""
+
+    def __missing__(self, key):
+        return 0
+
+
+def _time_per_op(device, groups_encoded, sizes):
+    """The same submission groups as one launch per op on one stream."""
+    import torch
+
+    from persistent_fusion_amd import gpuos
+
+    stream = torch.cuda.current_stream(device)
+    stream.synchronize()
+    t0 = time.perf_counter()
+    for arr, k in zip(groups_encoded, sizes):
+        gpuos.baseline_run(device, arr, k, stream=stream.cuda_stream)
+    stream.synchronize()
+    return time.perf_counter() - t0
+
+
+def decode_leg(device=0, reps=3):
+    """Batch-1 decode: 24 layers, 64 tokens, 360 ops per token, one flush per
+    token, one sync at the end."""
+    import torch
+
+    from persistent_fusion_amd import gpuos, runner, workloads
+
+    wl = workloads.gen_decode(seed=0)
+    t = runner.to_device(wl, device)
+    addr = runner.addr_fn(t, wl)
+    enc = [gpuos.encode_ops(wl.ops, g0, g1, addr, {}) for g0, g1 in wl.groups]
+    sizes = [g1 - g0 for g0, g1 in wl.groups]
+    torch.cuda.synchronize()
+    ctx = gpuos.Context(device, trace=1)
+    times = []
+    for r in range(reps + 1):
+        t0 = time.perf_counter()
+        for arr, k in zip(enc, sizes):
+            ctx.submit_noids(arr, k)
+            ctx.flush()
+        ctx.sync(0, 120.0)
+        if r:
+            times.append(time.perf_counter() - t0)
+    tr = ctx.trace(1 << 16)
+    ctx.destroy()
+    torch.cuda.synchronize()
+    per_op = []
+    for r in range(reps + 1):
+        w = _time_per_op(device, enc, sizes)
+        if r:
+            per_op.append(w)
+    tokens = wl.meta["tokens"]
+    ops = len(wl.ops)
+    byt = (wl.meta["weight_bytes"] + wl.meta["kv_bytes"]) * tokens
+    best, best_b = min(times), min(per_op)
+    # device-side time per token from the trace of the last run
+    recs = sorted(tr, key=lambda x: x["seq"])[-ops:]
+    dev_s = (max(x["t_done"] for x in recs) - min(x["t_claim"] for x in recs)) * 1e-8 if recs else None
+    del t
+    torch.cuda.empty_cache()
+    return {"workload": "decode 24 layers, hidden 896, 14x64 heads, FFN 4864, KV 512, 64 tokens",
+            "ops": ops, "tokens": tokens,
+            "resident_tok_per_s": round(tokens / best, 1),
+            "resident_ops_per_s": round(ops / best),
+            "resident_gb_per_s": round(byt / best / 1e9, 1),
+            "resident_device_span_ms": round(dev_s * 1e3, 3) if dev_s else None,
+            "per_op_launch_tok_per_s": round(tokens / best_b, 1),
+            "per_op_launch_ops_per_s": round(ops / best_b),
+            "speedup_vs_per_op_launch": round(best_b / best, 2),
+            "bytes_per_token": byt // tokens}
+
+
+def dag_leg(device=0, reps=2):
+    """100,000 ops, log-uniform sizes, random DAG, 64-slot output ring;
+    submitted in groups of 1,000 with a flush each, one sync at the end."""
+    import torch
+
+    from persistent_fusion_amd import gpuos, runner, workloads
+
+    wl = workloads.gen_dynamic_dag(seed=0, group=1000)
+    t = runner.to_device(wl, device)
+    addr = runner.addr_fn(t, wl)
+    n = len(wl.ops)
+    # a context numbers ops 1, 2, 3, ... in submission order, so pass r's op i
+    # gets id r * n + i + 1: encode every pass beforehand
+    passes = []
+    for r in range(reps + 1):
+        ids = {i: r * n + i + 1 for i in range(n)}
+        passes.append([(gpuos.encode_ops(wl.ops, g0, g1, addr, ids), g1 - g0) for g0, g1 in wl.groups])
+    torch.cuda.synchronize()
+    ctx = gpuos.Context(device)
+    times = []
+    for r in range(reps + 1):
+        t0 = time.perf_counter()
+        first = None
+        for arr, k in passes[r]:
+            got = ctx.submit(arr, k)
+            first = got[0] if first is None else first
+            ctx.flush()
+        ctx.sync(0, 300.0)
+        if first != r * n + 1:
+            raise RuntimeError("unexpected op ids")
+        if r:
+            times.append(time.perf_counter() - t0)
+    ctx.destroy()
+    torch.cuda.synchronize()
+    # per-op launches: stream order covers every dependency
+    enc_b = [gpuos.encode_ops(wl.ops, g0, g1, addr, _NoIds()) for g0, g1 in wl.groups]
+    sizes = [g1 - g0 for g0, g1 in wl.groups]
+    per_op = [_time_per_op(device, enc_b, sizes) for _ in range(reps)]
+    best, best_b = min(times), min(per_op)
+    del t
+    torch.cuda.empty_cache()
+    return {"workload": "dynamic DAG: 100,000 ops, n log-uniform 256..1,048,576, add/mul/relu/exp/"
+                        "row_sum/row_softmax, 0-2 deps among the previous 8, 64-slot output ring",
+            "ops": n, "algorithmic_bytes": wl.meta["bytes"],
+            "resident_ops_per_s": round(n / best),
+            "resident_gb_per_s": round(wl.meta["bytes"] / best / 1e9, 1),
+            "per_op_launch_ops_per_s": round(n / best_b),
+            "per_op_launch_gb_per_s": round(wl.meta["bytes"] / best_b / 1e9, 1),
+            "speedup_vs_per_op_launch": round(best_b / best, 2)}
+
+
+def priority_leg(device=0, rounds=200):
+    """Two-priority mix: per round one 64M-element fp32 best-effort op (no
+    wait), then ten bf16 4,096-element latency-critical ops, each submitted,
+    flushed and waited for (closed loop)."""
+    import torch
+
+    from persistent_fusion_amd import gpuos, runner, workloads, traffic
+
+    wl = workloads.gen_priority_mix(seed=0, rounds=rounds)
+    t = runner.to_device(wl, device)
+    addr = runner.addr_fn(t, wl)
+    enc = [gpuos.encode_ops(wl.ops, i, i + 1, addr, {}) for i in range(len(wl.ops))]
+    be_bytes = sum(traffic.op_bytes(op) for op in wl.ops if not op.lc)
+    lc_bytes = sum(traffic.op_bytes(op) for op in wl.ops if op.lc)
+    torch.cuda.synchronize()
+    res = {}
+    for label, prio in (("priority_ring", 1), ("single_ring", 2)):
+        ctx = gpuos.Context(device, priority=prio)
+        lat = []
+        t0 = time.perf_counter()
+        for i, op in enumerate(wl.ops):
+            if not op.lc:
+                ctx.submit_noids(enc[i], 1)
+                ctx.flush()
+                continue
+            a = enc[i]
+            if prio == 2:
+                a[0].flags &= ~gpuos.FLAG_LC
+            s0 = time.perf_counter()
+            oid = ctx.submit(a, 1)[0]
+            ctx.flush()
+            while not ctx.query(oid):
+                pass
+            lat.append(time.perf_counter() - s0)
+            if prio == 2:
+                a[0].flags |= gpuos.FLAG_LC
+        ctx.sync(0, 120.0)
+        wall = time.perf_counter() - t0
+        ctx.destroy()
+        lat.sort()
+        res[label] = {"lc_p50_us": round(lat[len(lat) // 2] * 1e6, 1),
+                      "lc_p99_us": round(lat[int(len(lat) * 0.99)] * 1e6, 1),
+                      "lc_max_us": round(lat[-1] * 1e6, 1),
+                      "aggregate_gb_per_s": round((be_bytes + lc_bytes) / wall / 1e9, 1)}
+    torch.cuda.synchronize()
+    # best-effort ops alone, back to back
+    ctx = gpuos.Context(device)
+    t0 = time.perf_counter()
+    for i, op in enumerate(wl.ops):
+        if not op.lc:
+            ctx.submit_noids(enc[i], 1)
+            ctx.flush()
+    ctx.sync(0, 120.0)
+    res["best_effort_alone_gb_per_s"] = round(be_bytes / (time.perf_counter() - t0) / 1e9, 1)
+    ctx.destroy()
+    # per-op launches: best-effort ops on one stream, latency-critical ops on a
+    # second stream (both at the default priority), each LC op waited for
+    s_be = torch.cuda.Stream(device)
+    s_lc = torch.cuda.Stream(device)
+    lat = []
+    t0 = time.perf_counter()
+    for i, op in enumerate(wl.ops):
+        if not op.lc:
+            gpuos.baseline_run(device, enc[i], 1, stream=s_be.cuda_stream)
+            continue
+        s0 = time.perf_counter()
+        gpuos.baseline_run(device, enc[i], 1, stream=s_lc.cuda_stream)
+        s_lc.synchronize()
+        lat.append(time.perf_counter() - s0)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    lat.sort()
+    res["per_op_launch_two_streams"] = {"lc_p50_us": round(lat[len(lat) // 2] * 1e6, 1),
+                                        "lc_p99_us": round(lat[int(len(lat) * 0.99)] * 1e6, 1),
+                                        "lc_max_us": round(lat[-1] * 1e6, 1),
+                                        "aggregate_gb_per_s": round((be_bytes + lc_bytes) / wall / 1e9, 1)}
+    del t
+    torch.cuda.empty_cache()
+    res["workload"] = (f"{rounds} rounds of one fp32[67,108,864] best-effort op and ten "
+                       "bf16[4096] latency-critical ops (closed loop)")
+    return res
+
+
 def cpu_baseline_leg(budget_s=10.0, gpu_y=None):
     """The oracle, untuned, on a bounded sample of the same workload.
 
@@ -254,6 +463,8 @@ def main():
     ap.add_argument("--queue-reps", type=int, default=50)
     ap.add_argument("--cpu-budget", type=float, default=10.0)
     ap.add_argument("--no-cpu", action="store_true")
+    ap.add_argument("--extra", default="",
+                    help="comma-separated extra legs: decode, dag, priority (or all)")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
         print("bench.py: this build measures one GPU only (the resident kernel runs on one "
@@ -267,6 +478,12 @@ def main():
     fc = fused_chain_leg(args.steps, args.warmup)
     q = queue_leg(args.queue_reps)
     cp = copy_leg()
+    extra_names = ("decode", "dag", "priority") if args.extra == "all" else \
+        tuple(x for x in args.extra.split(",") if x)
+    extra = {}
+    for name in extra_names:
+        log(f"bench: extra leg {name}")
+        extra[name] = {"decode": decode_leg, "dag": dag_leg, "priority": priority_leg}[name]()
     cpu, parity = (None, None) if args.no_cpu else cpu_baseline_leg(args.cpu_budget, fc["y"])
 
     steps = args.steps
@@ -305,6 +522,7 @@ def main():
         "standalone_fused_kernel": fc["baselines"]["standalone_fused_kernel"],
         "elementwise_queue_1000x4096": q,
         "plain_copy_kernel": cp,
+        **({"extra_configs": extra} if extra else {}),
         "cpu_baseline": cpu,
     }
     print(json.dumps(line), flush=True)

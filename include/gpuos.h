@@ -193,7 +193,7 @@ typedef struct gpuos_config {
   uint32_t waves_per_cu;  /* resident waves per compute unit, multiple of 4
                              in [4, 32]; default 8 */
   uint32_t tile_elems;    /* elementwise tile in elements, multiple of 256;
-                             default 4096 */
+                             default 1024 (one memory round trip per wave) */
   uint32_t be_tile_elems; /* tile for ops of 1<<24 elements or more (bounds
                              how long a priority op waits for a free wave);
                              default 16384 */

@@ -56,6 +56,12 @@ enum : uint8_t {
 };
 
 constexpr int kMaxSteps = 8;
+// Descriptor flag set by the runtime (user flags use the low bits): in[2]
+// (GEMV weights) has no queued writer, so the kernel may read it before the
+// op's dependencies have completed.
+constexpr uint8_t DF_AUX_READY = 0x80;
+constexpr int kMaxDeps = 14;  // dependencies a descriptor carries (more: wait
+                              // for the retire cursor instead)
 constexpr int kMaxFusedInputs = 4;
 constexpr int kRings = 2;      // 0 = best effort (default), 1 = latency critical
 constexpr uint32_t kDescBytes = 256;
@@ -78,7 +84,8 @@ struct alignas(16) DevDesc {
   uint64_t seq;       // 4-5: 1-based sequence in its ring
   uint32_t ntiles;    // 6
   uint32_t tile;      // 7: units per tile (elements, rows, key rows, chunks)
-  uint64_t deps[4];   // 8-15: sequences in the same ring to wait for
+  uint32_t deps_lo[8];  // 8-15: dependencies 0..7 as seq - dep_seq (same
+                        // ring; 0 = none); 8..13 are dwords 54-59
   uint64_t wait_retired;  // 16-17: wait until the ring's in-order retire
                           // cursor reaches this sequence (0 = none)
   union {
@@ -88,7 +95,7 @@ struct alignas(16) DevDesc {
       float alpha;          // 28
       float eps;            // 29
       int32_t aux[4];       // 30-33
-      uint8_t _pad[104];
+      uint8_t _pad[80];
     } p;
     struct {
       uint64_t in[4];       // 18-25: in[0] = chain input, in[1..3] operands
@@ -96,15 +103,16 @@ struct alignas(16) DevDesc {
       uint8_t step_op[8];   // 42-43
       uint8_t step_fl[8];   // 44-45
       float fscal[8];       // 46-53: SCALE factor of step s
-      uint8_t _pad[24];
     } f;
   };
+  uint32_t deps_hi[6];  // 54-59: dependencies 8..13 (as deps_lo)
   uint64_t tstart;      // 60-61: first ticket of this descriptor
   uint32_t user_ops;    // 62: user ops folded into this descriptor
   uint32_t check;       // 63: (uint32)seq ^ kDescMagic
 };
 static_assert(sizeof(DevDesc) == kDescBytes, "descriptor must be 256 bytes");
-static_assert(offsetof(DevDesc, deps) == 8 * 4, "deps at dword 8");
+static_assert(offsetof(DevDesc, deps_lo) == 8 * 4, "deps_lo at dword 8");
+static_assert(offsetof(DevDesc, deps_hi) == 54 * 4, "deps_hi at dword 54");
 static_assert(offsetof(DevDesc, wait_retired) == 16 * 4, "wait_retired at dword 16");
 static_assert(offsetof(DevDesc, p.ptr) == 18 * 4, "ptr at dword 18");
 static_assert(offsetof(DevDesc, p.src_len) == 26 * 4, "src_len at dword 26");

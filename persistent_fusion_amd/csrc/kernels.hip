@@ -132,10 +132,10 @@ template <int RING>
 __device__ __forceinline__ void wait_deps(const KArgs& a, const Cached& c) {
   const SDesc d = c.desc();
   const uint32_t mask = a.cap_mask;
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const uint64_t dep = d.q(8 + 2 * i);
-    if (dep) {
+  for (int i = 0; i < kMaxDeps; ++i) {
+    const uint32_t delta = d(i < 8 ? 8 + i : 54 + (i - 8));
+    if (delta) {
+      const uint64_t dep = c.seq - delta;
       const uint64_t* w = &a.done_id[RING][slot_of(dep, mask)];
       while (bcast64(ld_rlx_agent(w)) < dep) __builtin_amdgcn_s_sleep(1);
     }
@@ -162,7 +162,9 @@ __device__ __forceinline__ void finish_tile(const KArgs& a, const Cached& c, uin
   wait_mem();
   if (lane_id() != 0) return;
   bool complete;
-  if (ntiles <= kSubCounters) {
+  if (ntiles == 1) {
+    complete = true;  // the only tile: no count needed
+  } else if (ntiles <= kSubCounters) {
     uint32_t* ctr = &a.tiles_done[RING][slot];
     const uint32_t old = __hip_atomic_fetch_add(ctr, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     complete = old + 1 == ntiles;
@@ -197,14 +199,32 @@ __device__ __forceinline__ void finish_tile(const KArgs& a, const Cached& c, uin
 
 template <int RING>
 __device__ __forceinline__ void run_ticket(const KArgs& a, uint64_t ticket, Cached& c) {
+  const uint32_t tile = (uint32_t)(ticket - c.start);
+  const SDesc d = c.desc();
+  auto claimed = [&]() {
+    if (a.trace[RING] && tile == 0 && lane_id() == 0)
+      st_rlx_agent(&a.trace[RING][slot_of(c.seq, a.cap_mask)].t_claim, now_ticks());
+  };
   if (!c.deps_ok) {
+    const uint32_t w0 = d(0);
+    if ((w0 & 0xffu) == GPUOS_OP_GEMV && ((w0 >> 16) & DF_AUX_READY)) {
+      // the weights are final: start streaming them, then wait for x
+      auto ready = [&]() {
+        wait_deps<RING>(a, c);
+        c.deps_ok = 1;
+        claimed();
+      };
+      if (((w0 >> 8) & 0xffu) == GPUOS_BF16)
+        gemv_tile<GPUOS_BF16, kResidentLoadCP, kResidentStoreCP>(d, tile, ready);
+      else
+        gemv_tile<GPUOS_F32, kResidentLoadCP, kResidentStoreCP>(d, tile, ready);
+      finish_tile<RING>(a, c, tile);
+      return;
+    }
     wait_deps<RING>(a, c);
     c.deps_ok = 1;
   }
-  const uint32_t tile = (uint32_t)(ticket - c.start);
-  const SDesc d = c.desc();
-  if (a.trace[RING] && tile == 0 && lane_id() == 0)
-    st_rlx_agent(&a.trace[RING][slot_of(c.seq, a.cap_mask)].t_claim, now_ticks());
+  claimed();
   const uint32_t err = exec_tile<kResidentLoadCP, kResidentStoreCP>(d, tile);
   if (err) report_error(a, RING, c.seq, err);
   finish_tile<RING>(a, c, tile);
@@ -466,12 +486,16 @@ __device__ __forceinline__ void doorbell_loop(const KArgs& a) {
 __global__ __launch_bounds__(256) void gpuos_resident(KArgs a) {
   // one descriptor slot per wave and ring
   __shared__ uint32_t sdesc[4][2][64];
-  const uint32_t wave = (blockIdx.x * blockDim.x + threadIdx.x) / 64;
+  // Waves are numbered across workgroups first (wave j of workgroup b is
+  // j * blocks + b), so consecutive tickets, dealt round-robin, land on
+  // different CUs and XCDs (workgroups are dispatched round-robin over the
+  // XCDs).  Number 0 is the doorbell wave.
   const uint32_t wib = threadIdx.x / 64;
-  if (wave == 0)
+  const uint32_t num = wib * gridDim.x + blockIdx.x;
+  if (num == 0)
     doorbell_loop(a);
   else
-    worker_loop(a, wave - 1, (lds_u32*)&sdesc[wib][0][0], (lds_u32*)&sdesc[wib][1][0]);
+    worker_loop(a, num - 1, (lds_u32*)&sdesc[wib][0][0], (lds_u32*)&sdesc[wib][1][0]);
 }
 
 // ---------------------------------------------------------------------------

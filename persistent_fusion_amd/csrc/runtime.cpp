@@ -321,13 +321,25 @@ int validate(const gpuos_op& o, uint32_t index) {
 }
 
 // ---------------------------------------------------------------------------
-// hazard map: non-overlapping byte segments, each with its last writer and
-// the readers since that write (user op ids).
+// hazard map.  Writes keep exact non-overlapping byte segments, each with its
+// last writer (user op id) and the readers of that write.  A read never splits
+// a segment: it is recorded as a reader of every segment it touches, which can
+// only add write-after-read orderings.  Reads of bytes no queued op has
+// written (inputs uploaded before the queue) go to merged read spans, so
+// reading many different prefixes of one buffer costs no segments.  A write
+// depends on the writers and readers of every segment and span it overlaps.
 
-struct Seg {
+typedef SmallVec<uint64_t, 4> Readers;
+
+struct WSeg {
   uint64_t hi;
   uint64_t writer;
-  SmallVec<uint64_t, 4> readers;
+  Readers readers;
+};
+
+struct RSpan {
+  uint64_t hi;
+  Readers readers;
 };
 
 class HazardMap {
@@ -335,96 +347,145 @@ class HazardMap {
   template <class Retired>
   void access(const Range& rg, uint64_t id, bool write, DepVec& deps, Retired retired) {
     if (rg.hi <= rg.lo) return;
-    auto it = segs_.lower_bound(rg.lo);
-    if (it != segs_.end() && it->first == rg.lo && it->second.hi == rg.hi) {
-      // the range is exactly one segment (segments never overlap)
-      touch(it->second, id, write, deps, retired);
-      return;
-    }
-    const bool clear_after = it == segs_.end() || it->first >= rg.hi;
-    bool clear_before = true;
-    if (it != segs_.begin()) clear_before = std::prev(it)->second.hi <= rg.lo;
-    if (clear_after && clear_before) {
-      // nothing recorded inside the range yet
-      Seg sg{rg.hi, write ? id : 0, {}};
-      if (!write) sg.readers.push_back(id);
-      segs_.emplace_hint(it, rg.lo, std::move(sg));
-      return;
-    }
-    split(rg.lo);
-    split(rg.hi);
-    it = segs_.lower_bound(rg.lo);
-    uint64_t cur = rg.lo;
-    SmallVec<std::pair<uint64_t, uint64_t>, 4> gaps;
-    while (it != segs_.end() && it->first < rg.hi) {
-      if (it->first > cur) gaps.push_back({cur, it->first});
-      Seg& sg = it->second;
-      if (sg.writer && !retired(sg.writer)) deps.push_back(sg.writer);
-      if (write)
-        for (uint64_t r : sg.readers)
-          if (!retired(r)) deps.push_back(r);
-      cur = sg.hi;
-      ++it;
-    }
-    if (cur < rg.hi) gaps.push_back({cur, rg.hi});
-    if (write) {
-      segs_.erase(segs_.lower_bound(rg.lo), segs_.lower_bound(rg.hi));
-      segs_[rg.lo] = Seg{rg.hi, id, {}};
-    } else {
-      for (auto g : gaps) segs_[g.first] = Seg{g.second, 0, {}};
-      for (auto i2 = segs_.lower_bound(rg.lo); i2 != segs_.end() && i2->first < rg.hi; ++i2)
-        add_reader(i2->second, id, retired);
-    }
+    if (write)
+      do_write(rg, id, deps, retired);
+    else
+      do_read(rg, id, deps, retired);
   }
 
   template <class Retired>
   void prune(Retired retired) {
-    for (auto it = segs_.begin(); it != segs_.end();) {
-      Seg& sg = it->second;
+    for (auto it = w_.begin(); it != w_.end();) {
+      WSeg& sg = it->second;
       if (sg.writer && retired(sg.writer)) sg.writer = 0;
       sg.readers.remove_if(retired);
       if (!sg.writer && sg.readers.empty())
-        it = segs_.erase(it);
+        it = w_.erase(it);
+      else
+        ++it;
+    }
+    for (auto it = r_.begin(); it != r_.end();) {
+      it->second.readers.remove_if(retired);
+      if (it->second.readers.empty())
+        it = r_.erase(it);
       else
         ++it;
     }
   }
 
-  size_t size() const { return segs_.size(); }
-  void clear() { segs_.clear(); }
+  size_t size() const { return w_.size() + r_.size(); }
+  void clear() {
+    w_.clear();
+    r_.clear();
+  }
 
  private:
-  template <class Retired>
-  static void add_reader(Seg& sg, uint64_t id, Retired retired) {
-    if (sg.readers.empty() || sg.readers.back() != id) sg.readers.push_back(id);
-    if (sg.readers.size() > 32) sg.readers.remove_if(retired);
+  // first element whose range may overlap [lo, ...)
+  template <class M>
+  static typename M::iterator first_overlap(M& m, uint64_t lo) {
+    auto it = m.upper_bound(lo);
+    if (it != m.begin()) {
+      auto p = std::prev(it);
+      if (p->second.hi > lo) return p;
+    }
+    return it;
   }
 
   template <class Retired>
-  static void touch(Seg& sg, uint64_t id, bool write, DepVec& deps, Retired retired) {
-    if (sg.writer && !retired(sg.writer)) deps.push_back(sg.writer);
-    if (write) {
-      for (uint64_t r : sg.readers)
-        if (!retired(r)) deps.push_back(r);
-      sg.readers.clear();
-      sg.writer = id;
-    } else {
-      add_reader(sg, id, retired);
+  static void add_reader(Readers& rd, uint64_t id, Retired retired) {
+    if (!rd.empty() && rd.back() == id) return;
+    rd.push_back(id);
+    const size_t n = rd.size();
+    if (n >= 32 && (n & (n - 1)) == 0) rd.remove_if(retired);  // amortised
+  }
+
+  template <class Retired>
+  void do_read(const Range& rg, uint64_t id, DepVec& deps, Retired retired) {
+    uint64_t cur = rg.lo;
+    bool gap = false;
+    for (auto it = first_overlap(w_, rg.lo); it != w_.end() && it->first < rg.hi; ++it) {
+      if (it->first > cur) gap = true;
+      WSeg& sg = it->second;
+      if (sg.writer && !retired(sg.writer)) deps.push_back(sg.writer);
+      add_reader(sg.readers, id, retired);
+      cur = sg.hi;
     }
+    if (gap || cur < rg.hi) add_span(rg, id, retired);
+  }
+
+  // records a read of never-written bytes (conservatively the whole range)
+  template <class Retired>
+  void add_span(const Range& rg, uint64_t id, Retired retired) {
+    auto it = first_overlap(r_, rg.lo);
+    if (it != r_.end() && it->first <= rg.lo && it->second.hi >= rg.hi) {
+      add_reader(it->second.readers, id, retired);  // inside one span
+      return;
+    }
+    // merge every span that overlaps or touches the range into one
+    uint64_t lo = rg.lo, hi = rg.hi;
+    Readers rd;
+    auto j = r_.upper_bound(lo);
+    if (j != r_.begin() && std::prev(j)->second.hi >= lo) --j;
+    while (j != r_.end() && j->first <= hi) {
+      lo = std::min(lo, j->first);
+      hi = std::max(hi, j->second.hi);
+      for (uint64_t x : j->second.readers) rd.push_back(x);
+      j = r_.erase(j);
+    }
+    rd.remove_if(retired);
+    rd.sort_unique();
+    add_reader(rd, id, retired);
+    r_.emplace(lo, RSpan{hi, std::move(rd)});
+  }
+
+  template <class Retired>
+  void do_write(const Range& rg, uint64_t id, DepVec& deps, Retired retired) {
+    // read spans: every reader of an overlapping span must read first
+    for (auto it = first_overlap(r_, rg.lo); it != r_.end() && it->first < rg.hi;) {
+      for (uint64_t x : it->second.readers)
+        if (!retired(x)) deps.push_back(x);
+      if (it->first >= rg.lo && it->second.hi <= rg.hi)
+        it = r_.erase(it);  // wholly overwritten
+      else
+        ++it;
+    }
+    auto it = w_.lower_bound(rg.lo);
+    if (it != w_.end() && it->first == rg.lo && it->second.hi == rg.hi) {
+      // exactly one segment (segments never overlap)
+      WSeg& sg = it->second;
+      collect(sg, deps, retired);
+      sg.writer = id;
+      sg.readers.clear();
+      return;
+    }
+    for (auto j = first_overlap(w_, rg.lo); j != w_.end() && j->first < rg.hi; ++j)
+      collect(j->second, deps, retired);
+    split(rg.lo);
+    split(rg.hi);
+    w_.erase(w_.lower_bound(rg.lo), w_.lower_bound(rg.hi));
+    w_.emplace(rg.lo, WSeg{rg.hi, id, {}});
+  }
+
+  template <class Retired>
+  static void collect(const WSeg& sg, DepVec& deps, Retired retired) {
+    if (sg.writer && !retired(sg.writer)) deps.push_back(sg.writer);
+    for (uint64_t r : sg.readers)
+      if (!retired(r)) deps.push_back(r);
   }
 
   void split(uint64_t x) {
-    auto it = segs_.upper_bound(x);
-    if (it == segs_.begin()) return;
+    auto it = w_.upper_bound(x);
+    if (it == w_.begin()) return;
     --it;
     if (it->first < x && x < it->second.hi) {
-      Seg tail = it->second;
+      WSeg tail = it->second;
       it->second.hi = x;
-      segs_[x] = std::move(tail);
+      w_.emplace(x, std::move(tail));
     }
   }
 
-  std::map<uint64_t, Seg> segs_;
+  std::map<uint64_t, WSeg> w_;
+  std::map<uint64_t, RSpan> r_;
 };
 
 }  // namespace
@@ -1049,8 +1110,15 @@ int publish_one(gpuos_ctx* c, Planned& pl) {
     dseq.push_back(s);
   }
   dseq.sort_unique();
-  if (dseq.size() <= 4) {
-    for (size_t k = 0; k < dseq.size(); ++k) d.deps[k] = dseq[k];
+  if (dseq.size() <= (size_t)kMaxDeps) {
+    // seq - dep fits 32 bits: a live dependency is less than a ring behind
+    for (size_t k = 0; k < dseq.size(); ++k) {
+      const uint32_t delta = (uint32_t)(seq - dseq[k]);
+      if (k < 8)
+        d.deps_lo[k] = delta;
+      else
+        d.deps_hi[k - 8] = delta;
+    }
   } else {
     d.wait_retired = dseq.back();  // retire order covers every dependency
   }
@@ -1235,7 +1303,7 @@ void gpuos_config_default(gpuos_config* cfg) {
   memset(cfg, 0, sizeof *cfg);
   cfg->ring_slots = 65536;
   cfg->waves_per_cu = 8;
-  cfg->tile_elems = 4096;
+  cfg->tile_elems = 1024;
   cfg->be_tile_elems = 16384;
   cfg->fusion = 1;
   cfg->auto_deps = 1;
@@ -1429,7 +1497,14 @@ int gpuos_submit(gpuos_ctx* c, const gpuos_op* ops, uint32_t n, uint64_t* ids_ou
     if (c->cfg.auto_deps == 1) {
       const size_t before = s.deps.size();
       const OpRanges R = op_ranges(ops[i]);
-      for (int q = 0; q < R.nr; ++q) c->hazards.access(R.r[q], s.id, false, s.deps, retired);
+      for (int q = 0; q < R.nr; ++q) {
+        const size_t k0 = s.deps.size();
+        c->hazards.access(R.r[q], s.id, false, s.deps, retired);
+        // GEMV weights (second read range) with no queued writer may be
+        // streamed before the op's dependencies complete
+        if (ops[i].opcode == GPUOS_OP_GEMV && q == 1 && s.deps.size() == k0)
+          s.op.flags |= DF_AUX_READY;
+      }
       c->hazards.access(R.w, s.id, true, s.deps, retired);
       // reads recorded above also list this op as a reader of its own output
       // range when it runs in place; drop self-dependencies

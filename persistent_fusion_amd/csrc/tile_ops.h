@@ -399,10 +399,15 @@ __device__ __forceinline__ void fused_tile(D d, uint32_t t) {
 }
 
 // ---------------------------------------------------------------------------
-// row reductions: one row at a time per wave.  A pass over the row is a
-// coalesced sweep (lane j reads elements j, j + 64, ...); multi-pass ops
-// (softmax: max, sum of exponentials, write; RMSNORM: sum of squares, write)
-// read the row again.
+// row reductions: one row at a time per wave.
+//
+// Vector path (16-byte aligned rows of whole vectors, no cyclic source): a
+// row of up to 128 vectors (2 per lane) is loaded once and kept in
+// registers; a longer row is swept in blocks of 16 values per lane with all
+// of a block's loads issued before any is used.  Softmax keeps a running
+// maximum and a sum rescaled to it (two sweeps: reduce, then write), RMSNORM
+// a sum of squares (two sweeps), ROW_SUM a sum (one sweep).  Other rows take
+// the per-element path (lane j reads elements j, j + 64, ...).
 
 template <int DT, int CPL, int CPS>
 struct RowReader {
@@ -414,16 +419,177 @@ struct RowReader {
   }
 };
 
+// Running softmax state of one lane: maximum m and sum of exp(x - m).  A
+// -inf element adds nothing; NaN and +inf make the row NaN (as a
+// max-subtracted softmax does).
+struct SoftAcc {
+  float m = -__builtin_inff();
+  float s = 0.0f;
+  __device__ __forceinline__ void add(float x) {
+    if (x != x) {
+      m = x;
+      s = x;
+      return;
+    }
+    if (x == -__builtin_inff()) return;
+    if (x > m) {
+      s = s * expf(m - x) + 1.0f;
+      m = x;
+    } else {
+      s += expf(x - m);
+    }
+  }
+};
+
+// Combines the lanes' (m, s) into the row's maximum and sum.
+__device__ __forceinline__ void soft_combine(SoftAcc a, float& M, float& S) {
+  M = wave_max_nan(a.m);
+  float part = a.s;
+  if (a.m == -__builtin_inff())
+    part = M == -__builtin_inff() ? __builtin_nanf("") : 0.0f;  // all -inf row: NaN
+  else
+    part = a.s * expf(a.m - M);
+  S = wave_sum(part);
+  if (M != M) S = M;
+}
+
+// One row on the vector path.  `in` / `out` cover exactly this row (whole
+// vectors), so a lane's vectors past the row read as zeros and its stores are
+// dropped; `g` covers the gain; ROW_SUM writes element r of `out`.
+template <int OP, int DT, int CPL, int CPS>
+__device__ __forceinline__ void row_vec(rsrc_t in, rsrc_t out, rsrc_t g, uint32_t r, uint32_t L,
+                                        float eps) {
+  using T = DTr<DT, CPL, CPS>;
+  constexpr int V = T::V;
+  const uint32_t lane = lane_id();
+  const uint32_t nv = L / V;
+  if (nv <= 128) {
+    // the whole row in registers: 2 vectors per lane
+    float x[2][V];
+    const bool v0 = lane < nv, v1 = lane + 64 < nv;
+    T::ldq(in, lane, x[0]);
+    T::ldq(in, lane + 64, x[1]);
+    if constexpr (OP == GPUOS_OP_ROW_SUM) {
+      float s = 0.0f;
+#pragma unroll
+      for (int e = 0; e < V; ++e) s += x[0][e];
+#pragma unroll
+      for (int e = 0; e < V; ++e) s += x[1][e];
+      s = wave_sum(s);
+      if (lane == 0) T::st(out, r, s);
+    } else if constexpr (OP == GPUOS_OP_ROW_SOFTMAX) {
+      SoftAcc acc;
+#pragma unroll
+      for (int e = 0; e < V; ++e)
+        if (v0) acc.add(x[0][e]);
+#pragma unroll
+      for (int e = 0; e < V; ++e)
+        if (v1) acc.add(x[1][e]);
+      float M, S;
+      soft_combine(acc, M, S);
+      float y[2][V];
+#pragma unroll
+      for (int e = 0; e < V; ++e) {
+        y[0][e] = expf(x[0][e] - M) / S;
+        y[1][e] = expf(x[1][e] - M) / S;
+      }
+      T::stq(out, lane, y[0]);
+      T::stq(out, lane + 64, y[1]);
+    } else {  // RMSNORM
+      float q = 0.0f;
+#pragma unroll
+      for (int e = 0; e < V; ++e) q += x[0][e] * x[0][e];
+#pragma unroll
+      for (int e = 0; e < V; ++e) q += x[1][e] * x[1][e];
+      const float ss = wave_sum(q);
+      const float inv = 1.0f / sqrtf(ss / (float)L + eps);
+      float w[2][V], y[2][V];
+      T::ldq(g, lane, w[0]);
+      T::ldq(g, lane + 64, w[1]);
+#pragma unroll
+      for (int e = 0; e < V; ++e) {
+        y[0][e] = x[0][e] * inv * w[0][e];
+        y[1][e] = x[1][e] * inv * w[1][e];
+      }
+      T::stq(out, lane, y[0]);
+      T::stq(out, lane + 64, y[1]);
+    }
+    return;
+  }
+  // long row: blocks of 16 values per lane (4 fp32 / 2 bf16 vectors)
+  constexpr int B = 16 / V;
+  float s = 0.0f;
+  SoftAcc acc;
+  for (uint32_t j0 = 0; j0 < nv; j0 += 64 * B) {
+    float x[B][V];
+#pragma unroll
+    for (int u = 0; u < B; ++u) T::ldq(in, j0 + lane + 64 * u, x[u]);
+#pragma unroll
+    for (int u = 0; u < B; ++u) {
+      const bool v = j0 + lane + 64 * u < nv;
+#pragma unroll
+      for (int e = 0; e < V; ++e) {
+        if constexpr (OP == GPUOS_OP_ROW_SUM) s += x[u][e];
+        else if constexpr (OP == GPUOS_OP_RMSNORM) s += x[u][e] * x[u][e];
+        else if (v) acc.add(x[u][e]);
+      }
+    }
+  }
+  if constexpr (OP == GPUOS_OP_ROW_SUM) {
+    s = wave_sum(s);
+    if (lane == 0) T::st(out, r, s);
+    return;
+  }
+  float M = 0.0f, S = 0.0f, inv = 0.0f;
+  if constexpr (OP == GPUOS_OP_ROW_SOFTMAX) soft_combine(acc, M, S);
+  else inv = 1.0f / sqrtf(wave_sum(s) / (float)L + eps);
+  for (uint32_t j0 = 0; j0 < nv; j0 += 64 * B) {
+    float x[B][V], w[B][V];
+#pragma unroll
+    for (int u = 0; u < B; ++u) {
+      T::ldq(in, j0 + lane + 64 * u, x[u]);
+      if constexpr (OP == GPUOS_OP_RMSNORM) T::ldq(g, j0 + lane + 64 * u, w[u]);
+    }
+#pragma unroll
+    for (int u = 0; u < B; ++u) {
+      float y[V];
+#pragma unroll
+      for (int e = 0; e < V; ++e) {
+        if constexpr (OP == GPUOS_OP_ROW_SOFTMAX) y[e] = expf(x[u][e] - M) / S;
+        else y[e] = x[u][e] * inv * w[u][e];
+      }
+      T::stq(out, j0 + lane + 64 * u, y);
+    }
+  }
+}
+
 template <int OP, int DT, int CPL, int CPS, class D>
 __device__ __forceinline__ void row_tile(D d, uint32_t t) {
   using T = DTr<DT, CPL, CPS>;
+  constexpr int V = T::V;
   const uint32_t rows = d(2), L = d(3), tile = d(7);
   const uint32_t r0 = t * tile;
   const uint32_t r1 = r0 + tile < rows ? r0 + tile : rows;
-  const rsrc_t out = make_rsrc(d.q(18)), in = make_rsrc(d.q(20)), g = make_rsrc(d.q(24));
+  const uint64_t pout = d.q(18), pin = d.q(20), pg = d.q(24);
   const uint32_t ca = d(26);
   const float eps = __uint_as_float(d(29));
   const uint32_t lane = lane_id();
+  const bool vec = ca == 0 && L % V == 0 && aligned16(pin) &&
+                   (OP == GPUOS_OP_ROW_SUM || aligned16(pout)) &&
+                   (OP != GPUOS_OP_RMSNORM || aligned16(pg));
+  if (vec) {
+    const uint32_t rowbytes = L / V * 16u;
+    const rsrc_t vg = make_rsrc_n(OP == GPUOS_OP_RMSNORM ? pg : 0, rowbytes);
+    const rsrc_t sums = make_rsrc(pout);
+    for (uint32_t r = r0; r < r1; ++r) {
+      const uint64_t off = (uint64_t)r * rowbytes;
+      const rsrc_t vin = make_rsrc_n(pin + off, rowbytes);
+      const rsrc_t vout = OP == GPUOS_OP_ROW_SUM ? sums : make_rsrc_n(pout + off, rowbytes);
+      row_vec<OP, DT, CPL, CPS>(vin, vout, vg, r, L, eps);
+    }
+    return;
+  }
+  const rsrc_t out = make_rsrc(pout), in = make_rsrc(pin), g = make_rsrc(pg);
   for (uint32_t r = r0; r < r1; ++r) {
     const RowReader<DT, CPL, CPS> x{in, r * L, ca};
     if constexpr (OP == GPUOS_OP_ROW_SUM) {
@@ -436,18 +602,11 @@ __device__ __forceinline__ void row_tile(D d, uint32_t t) {
       const float s = wave_sum((s0 + s1) + (s2 + s3));
       if (lane == 0) T::st(out, r, s);
     } else if constexpr (OP == GPUOS_OP_ROW_SOFTMAX) {
-      float m = -__builtin_inff();
-      for (uint32_t j = lane; j < L; j += 64) m = nan_max(m, x(j));
-      m = wave_max_nan(m);
-      float s0 = 0.0f, s1 = 0.0f;
-      uint32_t j = lane;
-      for (; j + 64 < L; j += 128) {
-        s0 += expf(x(j) - m);
-        s1 += expf(x(j + 64) - m);
-      }
-      for (; j < L; j += 64) s0 += expf(x(j) - m);
-      const float s = wave_sum(s0 + s1);
-      for (uint32_t jj = lane; jj < L; jj += 64) T::st(out, r * L + jj, expf(x(jj) - m) / s);
+      SoftAcc acc;
+      for (uint32_t j = lane; j < L; j += 64) acc.add(x(j));
+      float M, S;
+      soft_combine(acc, M, S);
+      for (uint32_t jj = lane; jj < L; jj += 64) T::st(out, r * L + jj, expf(x(jj) - M) / S);
     } else {  // RMSNORM
       float q0 = 0.0f, q1 = 0.0f;
       uint32_t j = lane;
@@ -461,8 +620,7 @@ __device__ __forceinline__ void row_tile(D d, uint32_t t) {
         q0 += a * a;
       }
       const float ss = wave_sum(q0 + q1);
-      const float ms = ss / (float)L;
-      const float inv = 1.0f / sqrtf(ms + eps);
+      const float inv = 1.0f / sqrtf(ss / (float)L + eps);
       for (uint32_t jj = lane; jj < L; jj += 64) T::st(out, r * L + jj, x(jj) * inv * T::ld(g, jj));
     }
   }
@@ -470,15 +628,72 @@ __device__ __forceinline__ void row_tile(D d, uint32_t t) {
 
 // ---------------------------------------------------------------------------
 // rotate-half rotary embedding, rows = heads of row_len = head_dim; each lane
-// owns whole (i, i + h/2) pairs, so the op may run in place.
+// owns whole (i, i + h/2) pairs, so the op may run in place.  With 16-byte
+// aligned operands and h/2 a multiple of 8, a lane takes 8 consecutive pairs
+// with 128-bit loads (all of its loads in flight at once).
 
 template <int DT, int CPL, int CPS, class D>
 __device__ __forceinline__ void rope_tile(D d, uint32_t) {
   using T = DTr<DT, CPL, CPS>;
   const uint32_t heads = d(2), hd = d(3), half = hd / 2;
-  const rsrc_t out = make_rsrc(d.q(18)), in = make_rsrc(d.q(20)), tab = make_rsrc(d.q(24));
+  const uint64_t pout = d.q(18), pin = d.q(20), ptab = d.q(24);
+  const rsrc_t out = make_rsrc(pout), in = make_rsrc(pin), tab = make_rsrc(ptab);
+  const uint32_t lane = lane_id();
+  if (half % 8 == 0 && aligned16(pout) && aligned16(pin) && aligned16(ptab)) {
+    const uint32_t per_head = half / 8, units = heads * per_head;
+    for (uint32_t u = lane; u < units; u += 64) {
+      const uint32_t h = u / per_head, i0 = (u - h * per_head) * 8;
+      const uint32_t e1 = h * hd + i0, e2 = e1 + half;
+      float x1[8], x2[8], c[8], s[8];
+      if constexpr (DT == GPUOS_BF16) {
+        unpack_bf16x8(ld128<CPL>(in, 2u * e1), x1);
+        unpack_bf16x8(ld128<CPL>(in, 2u * e2), x2);
+      } else {
+#pragma unroll
+        for (int k = 0; k < 2; ++k) {
+          const u32x4 a = ld128<CPL>(in, 4u * (e1 + 4 * k)), b = ld128<CPL>(in, 4u * (e2 + 4 * k));
+          x1[4 * k] = __uint_as_float(a.x); x1[4 * k + 1] = __uint_as_float(a.y);
+          x1[4 * k + 2] = __uint_as_float(a.z); x1[4 * k + 3] = __uint_as_float(a.w);
+          x2[4 * k] = __uint_as_float(b.x); x2[4 * k + 1] = __uint_as_float(b.y);
+          x2[4 * k + 2] = __uint_as_float(b.z); x2[4 * k + 3] = __uint_as_float(b.w);
+        }
+      }
+#pragma unroll
+      for (int k = 0; k < 2; ++k) {
+        const u32x4 a = ld128<CPL>(tab, 4u * (i0 + 4 * k)), b = ld128<CPL>(tab, 4u * (half + i0 + 4 * k));
+        c[4 * k] = __uint_as_float(a.x); c[4 * k + 1] = __uint_as_float(a.y);
+        c[4 * k + 2] = __uint_as_float(a.z); c[4 * k + 3] = __uint_as_float(a.w);
+        s[4 * k] = __uint_as_float(b.x); s[4 * k + 1] = __uint_as_float(b.y);
+        s[4 * k + 2] = __uint_as_float(b.z); s[4 * k + 3] = __uint_as_float(b.w);
+      }
+      float y1[8], y2[8];
+#pragma unroll
+      for (int k = 0; k < 8; ++k) {
+        const float a1 = x1[k] * c[k], b1 = x2[k] * s[k];
+        const float a2 = x2[k] * c[k], b2 = x1[k] * s[k];
+        y1[k] = a1 - b1;
+        y2[k] = a2 + b2;
+      }
+      if constexpr (DT == GPUOS_BF16) {
+        T::stv(out, e1, y1);
+        T::stv(out, e2, y2);
+      } else {
+#pragma unroll
+        for (int k = 0; k < 2; ++k) {
+          u32x4 a, b;
+          a.x = __float_as_uint(y1[4 * k]); a.y = __float_as_uint(y1[4 * k + 1]);
+          a.z = __float_as_uint(y1[4 * k + 2]); a.w = __float_as_uint(y1[4 * k + 3]);
+          b.x = __float_as_uint(y2[4 * k]); b.y = __float_as_uint(y2[4 * k + 1]);
+          b.z = __float_as_uint(y2[4 * k + 2]); b.w = __float_as_uint(y2[4 * k + 3]);
+          st128<CPS>(out, 4u * (e1 + 4 * k), a);
+          st128<CPS>(out, 4u * (e2 + 4 * k), b);
+        }
+      }
+    }
+    return;
+  }
   const uint32_t pairs = heads * half;
-  for (uint32_t p = lane_id(); p < pairs; p += 64) {
+  for (uint32_t p = lane; p < pairs; p += 64) {
     const uint32_t h = p / half, i = p - h * half;
     const float x1 = T::ld(in, h * hd + i);
     const float x2 = T::ld(in, h * hd + half + i);
@@ -492,8 +707,9 @@ __device__ __forceinline__ void rope_tile(D d, uint32_t) {
 }
 
 // ---------------------------------------------------------------------------
-// GEMV: out[i] = sum_k W[i, k] x[k]; `tile` rows per tile, up to 4 rows in
-// flight per wave; lanes split K in 16-byte chunks of W (8 bf16).
+// GEMV: out[i] = sum_k W[i, k] x[k]; `tile` rows per tile.  Lanes split K in
+// 16-byte chunks of W (8 bf16); a step loads several chunks per lane (and up
+// to 4 rows) with every load issued before the first FMA.
 
 template <int DT, int CPL>
 __device__ __forceinline__ void load_x8(rsrc_t x, uint32_t k, float (&v)[8]) {
@@ -508,53 +724,107 @@ __device__ __forceinline__ void load_x8(rsrc_t x, uint32_t k, float (&v)[8]) {
   }
 }
 
-template <int DT, int CPL, int CPS, class D>
-__device__ __forceinline__ void gemv_tile(D d, uint32_t t) {
+// Called where a GEMV tile may start reading x; the default does nothing.
+struct NoWait {
+  __device__ __forceinline__ void operator()() const {}
+};
+
+// R rows at a time, C chunks per lane per step (x kept packed until used).
+// `ready()` runs once, after the first step's weight loads are issued and
+// before any load of x: a tile whose weights are already final can stream
+// them while it waits for the op that produces x.
+template <int R, int C, int DT, int CPL, int CPS, class Ready>
+__device__ __forceinline__ void gemv_rows(rsrc_t out, uint64_t px, uint64_t pw, uint32_t K,
+                                          uint32_t i0, uint32_t i1, Ready& ready) {
+  using T = DTr<DT, CPL, CPS>;
+  const uint32_t lane = lane_id();
+  const uint32_t chunks = K / 8;
+  // x and W clipped to whole chunks / the step's rows: anything past reads zeros
+  const rsrc_t xv = make_rsrc_n(px, chunks * 8u * T::ES);
+  bool waiting = true;
+  for (uint32_t i = i0; i < i1; i += R) {
+    float acc[R];
+#pragma unroll
+    for (int r = 0; r < R; ++r) acc[r] = 0.0f;
+    const uint32_t nr = i1 - i < (uint32_t)R ? i1 - i : (uint32_t)R;
+    const rsrc_t Wr = make_rsrc_n(pw + (uint64_t)i * K * 2u, nr * K * 2u);
+    for (uint32_t c0 = 0; c0 < chunks; c0 += 64 * C) {
+      u32x4 wr[R][C];
+      u32x4 xp[C][T::ES / 2];  // 8 elements: one (bf16) or two (fp32) vectors
+#pragma unroll
+      for (int c = 0; c < C; ++c) {
+        const uint32_t ch = c0 + lane + 64 * c;
+#pragma unroll
+        for (int r = 0; r < R; ++r)
+          wr[r][c] = ld128<CPL>(Wr, ch < chunks ? 2u * (r * K + ch * 8) : 0xFFF00000u);
+      }
+      if (waiting) {
+        compiler_fence();
+        ready();
+        compiler_fence();
+        waiting = false;
+      }
+#pragma unroll
+      for (int c = 0; c < C; ++c) {
+        const uint32_t ch = c0 + lane + 64 * c;
+        const uint32_t xo = ch < chunks ? ch * 8u * T::ES : 0xFFF00000u;
+#pragma unroll
+        for (int k = 0; k < T::ES / 2; ++k) xp[c][k] = ld128<CPL>(xv, xo + 16u * k);
+      }
+#pragma unroll
+      for (int c = 0; c < C; ++c) {
+        float xf[8];
+        if constexpr (DT == GPUOS_BF16) {
+          unpack_bf16x8(xp[c][0], xf);
+        } else {
+          xf[0] = __uint_as_float(xp[c][0].x); xf[1] = __uint_as_float(xp[c][0].y);
+          xf[2] = __uint_as_float(xp[c][0].z); xf[3] = __uint_as_float(xp[c][0].w);
+          xf[4] = __uint_as_float(xp[c][1].x); xf[5] = __uint_as_float(xp[c][1].y);
+          xf[6] = __uint_as_float(xp[c][1].z); xf[7] = __uint_as_float(xp[c][1].w);
+        }
+#pragma unroll
+        for (int r = 0; r < R; ++r) {
+          float w[8];
+          unpack_bf16x8(wr[r][c], w);
+#pragma unroll
+          for (int e = 0; e < 8; ++e) acc[r] = __builtin_fmaf(w[e], xf[e], acc[r]);
+        }
+      }
+    }
+#pragma unroll
+    for (int r = 0; r < R; ++r) {
+      const float s = wave_sum(acc[r]);
+      if (lane == 0 && (uint32_t)r < nr) T::st(out, i + r, s);
+    }
+  }
+  if (waiting) ready();
+}
+
+template <int DT, int CPL, int CPS, class D, class Ready = NoWait>
+__device__ __forceinline__ void gemv_tile(D d, uint32_t t, Ready ready = Ready()) {
   using T = DTr<DT, CPL, CPS>;
   const uint32_t M = d(30), K = d(31), tile = d(7);
-  const rsrc_t out = make_rsrc(d.q(18)), x = make_rsrc(d.q(20)), W = make_rsrc(d.q(24));
+  const uint64_t px = d.q(20), pw = d.q(24);
+  const rsrc_t out = make_rsrc(d.q(18)), x = make_rsrc(px), W = make_rsrc(pw);
   const uint32_t i0 = t * tile;
   const uint32_t i1 = i0 + tile < M ? i0 + tile : M;
   const uint32_t lane = lane_id();
-  const bool fast = (K % 8 == 0) && aligned16(d.q(20)) && aligned16(d.q(24));
-  if (fast) {
-    const uint32_t chunks = K / 8;
-    constexpr int R = 4;
-    for (uint32_t i = i0; i < i1; i += R) {
-      float acc[R] = {0.0f, 0.0f, 0.0f, 0.0f};
-      for (uint32_t c = lane; c < chunks; c += 64) {
-        float xv[8];
-        load_x8<DT, CPL>(x, c * 8, xv);
-        u32x4 wr[R];
-#pragma unroll
-        for (int r = 0; r < R; ++r)
-          if (i + r < i1) wr[r] = ld128<CPL>(W, 2u * ((i + r) * K + c * 8));
-#pragma unroll
-        for (int r = 0; r < R; ++r) {
-          if (i + r < i1) {
-            float w[8];
-            unpack_bf16x8(wr[r], w);
-#pragma unroll
-            for (int e = 0; e < 8; ++e) acc[r] = __builtin_fmaf(w[e], xv[e], acc[r]);
-          }
-        }
-      }
-#pragma unroll
-      for (int r = 0; r < R; ++r) {
-        if (i + r < i1) {
-          const float s = wave_sum(acc[r]);
-          if (lane == 0) T::st(out, i + r, s);
-        }
-      }
-    }
-  } else {
-    for (uint32_t i = i0; i < i1; ++i) {
-      float acc = 0.0f;
-      for (uint32_t k = lane; k < K; k += 64)
-        acc = __builtin_fmaf(bf2f(ld16<CPL>(W, 2u * (i * K + k))), T::ld(x, k), acc);
-      acc = wave_sum(acc);
-      if (lane == 0) T::st(out, i, acc);
-    }
+  if ((K % 8 == 0) && aligned16(px) && aligned16(pw)) {
+    // short rows: 4 rows per step, K <= 1,024 in one step; long rows: one row
+    // per step, 4,096 (bf16 x) or 2,048 (fp32 x) of K per step
+    if (K <= 1024)
+      gemv_rows<4, 2, DT, CPL, CPS>(out, px, pw, K, i0, i1, ready);
+    else
+      gemv_rows<1, DT == GPUOS_F32 ? 4 : 8, DT, CPL, CPS>(out, px, pw, K, i0, i1, ready);
+    return;
+  }
+  ready();
+  for (uint32_t i = i0; i < i1; ++i) {
+    float acc = 0.0f;
+    for (uint32_t k = lane; k < K; k += 64)
+      acc = __builtin_fmaf(bf2f(ld16<CPL>(W, 2u * (i * K + k))), T::ld(x, k), acc);
+    acc = wave_sum(acc);
+    if (lane == 0) T::st(out, i, acc);
   }
 }
 
@@ -571,22 +841,33 @@ __device__ __forceinline__ void score_rows_fast(D d, uint32_t j0, uint32_t j1) {
   const float alpha = __uint_as_float(d(28));
   const uint32_t lane = lane_id();
   const uint32_t total = (j1 - j0) * cpr;
-  for (uint32_t f0 = 0; f0 < total; f0 += 64) {
-    const uint32_t f = f0 + lane;
-    float part = 0.0f;
-    uint32_t j = 0, h = 0, c = 0;
-    if (f < total) {
-      j = j0 + f / cpr;
-      c = f - (j - j0) * cpr;
-      h = c / CPH;
-      float qv[8], kv[8];
-      load_x8<DT, CPL>(q, c * 8, qv);
-      unpack_bf16x8(ld128<CPL>(Kc, 2u * (j * HD + c * 8)), kv);
+  // two 64-chunk groups per step, both groups' loads issued first
+  for (uint32_t f0 = 0; f0 < total; f0 += 128) {
+    float qv[2][8];
+    u32x4 kv[2];
+    uint32_t j[2], c[2];
 #pragma unroll
-      for (int e = 0; e < 8; ++e) part = __builtin_fmaf(qv[e], kv[e], part);
+    for (int u = 0; u < 2; ++u) {
+      const uint32_t f = f0 + 64 * u + lane;
+      const uint32_t fc = f < total ? f : 0;
+      j[u] = j0 + fc / cpr;
+      c[u] = fc - (j[u] - j0) * cpr;
+      load_x8<DT, CPL>(q, c[u] * 8, qv[u]);
+      kv[u] = ld128<CPL>(Kc, 2u * (j[u] * HD + c[u] * 8));
     }
-    part = group_sum<CPH>(part);
-    if (f < total && (c % CPH) == 0) st32<CPS>(out, 4u * (h * S + j), __float_as_uint(alpha * part));
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+      const uint32_t f = f0 + 64 * u + lane;
+      float k8[8];
+      unpack_bf16x8(kv[u], k8);
+      float part = 0.0f;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) part = __builtin_fmaf(qv[u][e], k8[e], part);
+      part = group_sum<CPH>(part);
+      const uint32_t h = c[u] / CPH;
+      if (f < total && (c[u] % CPH) == 0)
+        st32<CPS>(out, 4u * (h * S + j[u]), __float_as_uint(alpha * part));
+    }
     (void)Dh;
   }
 }
@@ -633,15 +914,30 @@ __device__ __forceinline__ void attn_av_tile(D d, uint32_t t) {
     const uint32_t nchunks = HD / 8;
     const uint32_t c0 = t * tile;
     const uint32_t c1 = c0 + tile < nchunks ? c0 + tile : nchunks;
+    // p and V clipped to the S key positions: positions past S read zeros
+    const rsrc_t pv = make_rsrc_n(d.q(20), H * S * 4u);
+    const rsrc_t Vv = make_rsrc_n(d.q(24), S * HD * 2u);
     for (uint32_t c = c0; c < c1; ++c) {
       const uint32_t h = (c * 8) / Dh;
       float acc[8] = {0, 0, 0, 0, 0, 0, 0, 0};
-      for (uint32_t j = lane; j < S; j += 64) {
-        const float w = __uint_as_float(ld32<CPL>(p, 4u * (h * S + j)));
-        float v[8];
-        unpack_bf16x8(ld128<CPL>(Vc, 2u * (j * HD + c * 8)), v);
+      // 8 key positions per lane per step, every load of a step issued first
+      for (uint32_t jb = 0; jb < S; jb += 64 * 8) {
+        float w[8];
+        u32x4 vr[8];
 #pragma unroll
-        for (int e = 0; e < 8; ++e) acc[e] = __builtin_fmaf(w, v[e], acc[e]);
+        for (int u = 0; u < 8; ++u) {
+          const uint32_t j = jb + 64 * u + lane;
+          const bool ok = j < S;
+          w[u] = __uint_as_float(ld32<CPL>(pv, ok ? 4u * (h * S + j) : 0xFFF00000u));
+          vr[u] = ld128<CPL>(Vv, ok ? 2u * (j * HD + c * 8) : 0xFFF00000u);
+        }
+#pragma unroll
+        for (int u = 0; u < 8; ++u) {
+          float v[8];
+          unpack_bf16x8(vr[u], v);
+#pragma unroll
+          for (int e = 0; e < 8; ++e) acc[e] = __builtin_fmaf(w[u], v[e], acc[e]);
+        }
       }
 #pragma unroll
       for (int e = 0; e < 8; ++e) acc[e] = wave_sum(acc[e]);

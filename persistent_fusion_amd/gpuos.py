@@ -277,7 +277,8 @@ def decode_desc(raw: bytes) -> dict:
     d = {
         "opcode": w[0] & 0xFF, "dtype": (w[0] >> 8) & 0xFF, "flags": (w[0] >> 16) & 0xFF,
         "nsteps": w[0] >> 24, "n": w[1], "rows": w[2], "row_len": w[3], "seq": q(4),
-        "ntiles": w[6], "tile": w[7], "deps": [q(8 + 2 * i) for i in range(4)],
+        "ntiles": w[6], "tile": w[7],
+        "deps": [q(4) - x if x else 0 for x in list(w[8:16]) + list(w[54:60])],
         "wait_retired": q(16), "ptr": [q(18 + 2 * i) for i in range(4)],
         "src_len": [w[26], w[27]], "tstart": q(60), "user_ops": w[62], "check": w[63],
     }

@@ -206,19 +206,23 @@ def test_row_ops(kind, dtype):
         check(wl, runner.run_resident(wl))
 
 
-def test_softmax_special_rows():
+@pytest.mark.parametrize("L", [63, 64, 512, 4096])
+def test_softmax_special_rows(L):
+    """NaN, +inf, all -inf, a single -inf and a constant row, on the
+    per-element path (63), the in-register path (64, 512) and the long-row
+    path (4096)."""
     _need_gpu()
-    say("softmax special rows")
-    L = 64
-    x = np.random.default_rng(8).standard_normal(5 * L).astype(np.float32)
+    say(f"softmax special rows L={L}")
+    x = np.random.default_rng(8).standard_normal(6 * L).astype(np.float32)
     x[3] = np.nan
     x[L + 5] = np.inf
     x[2 * L:3 * L] = -np.inf
     x[3 * L + 1] = -np.inf
-    x[4 * L:] = 88.0
-    bufs = {"x": x, "y": np.zeros(5 * L, np.float32)}
+    x[4 * L:5 * L] = 88.0
+    x[5 * L + L // 2] = 1e4  # one element far above the rest: every other is exp(-inf-ish) = 0
+    bufs = {"x": x, "y": np.zeros(6 * L, np.float32)}
     wl = Workload("softmax-special", bufs, {"x": "f32", "y": "f32"},
-                  [Op("row_softmax", Ref("y"), (Ref("x"),), n=5 * L, rows=5, row_len=L)], outputs=["y"])
+                  [Op("row_softmax", Ref("y"), (Ref("x"),), n=6 * L, rows=6, row_len=L)], outputs=["y"])
     check(wl, runner.run_resident(wl))
 
 

@@ -69,7 +69,7 @@ def test_fused_chain_becomes_one_descriptor():
         assert [(f >> 4) & 3 for f in d["step_fl"][:3]] == [1, 2, 0]
         assert [bool(f & 4) for f in d["step_fl"][:3]] == [False, False, True]
         assert d["fused_out"][:3] == [0, 0, y]
-        assert d["deps"] == [0, 0, 0, 0]
+        assert d["deps"] == [0] * 14
         assert d["ntiles"] * d["tile"] >= n and d["tstart"] == 0
         assert all(c.seq_of(i) == (0, 1) for i in ids)
         assert c.stats()["ops_fused"] == 2
@@ -154,7 +154,7 @@ def test_hazard_dependencies_raw_war_waw():
     with ctx(fusion=2, auto_deps=2) as c:
         c.submit(ops)
         c.flush()
-        assert all(desc(c, s)["deps"] == [0, 0, 0, 0] for s in (1, 2, 3, 4))
+        assert all(desc(c, s)["deps"] == [0] * 14 for s in (1, 2, 3, 4))
 
 
 def test_partial_overlap_is_a_hazard_and_disjoint_is_not():
@@ -167,19 +167,26 @@ def test_partial_overlap_is_a_hazard_and_disjoint_is_not():
     with ctx(fusion=2) as c:
         c.submit(ops)
         c.flush()
-        assert desc(c, 2)["deps"] == [0, 0, 0, 0]
+        assert desc(c, 2)["deps"] == [0] * 14
         assert sorted(x for x in desc(c, 3)["deps"] if x) == [1, 2]
 
 
 def test_many_dependencies_fall_back_to_retire_order():
+    # 14 readers fit in the descriptor; 15 fall back to the retire cursor
     n = 256
-    ops = (gpuos.GpuosOp * 7)(*[make_op("relu", buf(10 + i), [buf(0)], n=n) for i in range(6)],
-                              make_op("scale", buf(0), [buf(1)], n=n, alpha=1.0))
-    with ctx(fusion=2) as c:
-        c.submit(ops)
-        c.flush()
-        d = desc(c, 7)
-        assert d["deps"] == [0, 0, 0, 0] and d["wait_retired"] == 6
+    for readers, fallback in ((14, False), (15, True)):
+        ops = (gpuos.GpuosOp * (readers + 1))(
+            *[make_op("relu", buf(10 + i), [buf(0)], n=n) for i in range(readers)],
+            make_op("scale", buf(0), [buf(1)], n=n, alpha=1.0))
+        with ctx(fusion=2) as c:
+            c.submit(ops)
+            c.flush()
+            d = desc(c, readers + 1)
+            if fallback:
+                assert d["deps"] == [0] * 14 and d["wait_retired"] == readers
+            else:
+                assert sorted(x for x in d["deps"] if x) == list(range(1, readers + 1))
+                assert d["wait_retired"] == 0
 
 
 def test_ticket_ranges_are_contiguous_and_tiles_cover_ops():
