@@ -205,10 +205,10 @@ typedef struct gpuos_config {
   uint32_t block_on_full; /* 1 = submit/flush wait for ring space (default),
                              2 = return GPUOS_EAGAIN */
   uint32_t max_fuse;      /* longest fused chain, 2..8; default 8 */
-  uint32_t priority;      /* 1 = workers also serve the latency-critical
-                             ring between their own tiles (default), 2 = no
+  uint32_t priority;      /* 1 = a latency-critical ring served by
+                             lc_waves reserved waves (default), 2 = no
                              priority ring: GPUOS_FLAG_LC ops are rejected
-                             and workers skip the per-tile check */
+                             and every wave runs best-effort tiles */
   uint32_t idle_exit_ms;  /* the resident kernel exits after this many
                              milliseconds with every published op retired and
                              nothing new, giving its compute units back; the
@@ -218,7 +218,12 @@ typedef struct gpuos_config {
                               this many KiB are streamed (non-temporal).
                               Default 32768 (32 MiB); 0xFFFFFFFF = only ops
                               flagged GPUOS_FLAG_NONTEMPORAL */
-  uint32_t reserved[4];
+  uint32_t lc_waves;      /* waves reserved for the latency-critical ring
+                             when priority == 1, in [1, 64]; default 8 (one
+                             per XCD).  They never run best-effort tiles, so
+                             a latency-critical op waits for no best-effort
+                             tile */
+  uint32_t reserved[3];
 } gpuos_config;
 
 /* Counters returned by gpuos_get_stats. */
@@ -233,7 +238,7 @@ typedef struct gpuos_stats {
   uint64_t deps_auto;          /* hazard dependencies added by the runtime */
   uint64_t device_error;       /* device error word (0 = none) */
   uint64_t error_desc;         /* descriptor sequence that raised it */
-  uint64_t worker_waves;       /* resident worker waves */
+  uint64_t worker_waves;       /* resident best-effort worker waves */
   uint64_t compute_units;
   uint64_t kernel_ns;          /* summed duration of the resident kernel's
                                   launches, from HIP events recorded on its
@@ -241,7 +246,8 @@ typedef struct gpuos_stats {
                                   launch; counts launches that have ended */
   uint64_t launches;           /* resident kernel launches (1 + relaunches
                                   after idle exits) */
-  uint64_t reserved[2];
+  uint64_t lc_waves;           /* waves serving the latency-critical ring */
+  uint64_t reserved[1];
 } gpuos_stats;
 
 /* Per-descriptor device timing, recorded when config.trace == 1. */

@@ -207,8 +207,9 @@ struct KArgs {
   TraceRec* trace[kRings];        // device trace ring (nullable)
   uint32_t cap_mask;              // ring_slots - 1
   uint32_t ends_mask;             // 2 * ring_slots - 1
-  uint32_t workers;               // worker waves (all waves but the doorbell)
-  uint32_t lc_enabled;            // poll the latency-critical ring
+  uint32_t workers;               // best-effort worker waves
+  uint32_t lc_waves;              // waves reserved for the latency-critical
+                                  // ring (0 = no priority ring)
   uint32_t epoch;                 // launch number of this context, from 1
   uint32_t _pad;
   uint64_t ticket_base;           // ring-0 tickets below this ran in earlier

@@ -251,10 +251,10 @@ __device__ __forceinline__ void read_avail(const AvailLine* l, uint64_t& tiles, 
   ops = bcast64(o);
 }
 
-// Latency-critical ring: tiles are claimed with compare-and-swap so a wave
-// never holds a priority ticket with no work behind it, and every wave drains
-// priority tiles before returning to its own best-effort ticket.  `seen` is
-// the published count at which this wave last found the ring empty.
+// Latency-critical ring: served only by the reserved waves, which claim its
+// tiles with compare-and-swap (a wave never holds a priority ticket with no
+// work behind it).  Drains the ring; `seen` is the published count at which
+// this wave last found it empty.
 __device__ __forceinline__ void service_lc(const KArgs& a, const AvailLine* line, Cached& c, uint64_t& seen) {
   DevRing* R = &a.dctl->ring[1];
   for (;;) {
@@ -285,11 +285,27 @@ __device__ __forceinline__ void service_lc(const KArgs& a, const AvailLine* line
   }
 }
 
-__device__ __forceinline__ void worker_loop(const KArgs& a, uint32_t w, lds_u32* slot0, lds_u32* slot1) {
+// A reserved wave: serves the latency-critical ring until the launch ends
+// (at which point every published descriptor has retired).
+__device__ __forceinline__ void lc_loop(const KArgs& a, uint32_t w, lds_u32* slot1) {
   const AvailLine* line0 = &a.dctl->avail[0][w % kReplicas];
   const AvailLine* line1 = &a.dctl->avail[1][w % kReplicas];
-  Cached c0{0, 0, 0, slot0, 0}, c1{0, 0, 0, slot1, 0};
-  uint64_t avail = 0, avail_ops = 0, lc_seen = 0;
+  Cached c1{0, 0, 0, slot1, 0};
+  uint64_t seen = 0;
+  for (;;) {
+    service_lc(a, line1, c1, seen);
+    uint64_t se = 0;
+    if (lane_id() == 0) se = ld_rlx_agent(&line0->stop_epoch);
+    if (bcast64(se) == a.epoch) return;
+    __builtin_amdgcn_s_sleep(1);
+  }
+}
+
+// A best-effort wave: runs its round-robin share of the ring-0 tickets.
+__device__ __forceinline__ void worker_loop(const KArgs& a, uint32_t w, lds_u32* slot0) {
+  const AvailLine* line0 = &a.dctl->avail[0][w % kReplicas];
+  Cached c0{0, 0, 0, slot0, 0};
+  uint64_t avail = 0, avail_ops = 0;
   uint32_t idle = 0;
   // tickets are dealt round-robin: this wave owns those = w (mod workers),
   // from the first one this launch has not inherited as done
@@ -297,7 +313,6 @@ __device__ __forceinline__ void worker_loop(const KArgs& a, uint32_t w, lds_u32*
   uint64_t ticket = base - base % a.workers + w;
   if (ticket < base) ticket += a.workers;
   for (;;) {
-    if (a.lc_enabled) service_lc(a, line1, c1, lc_seen);
     if (ticket >= avail) {
       read_avail(line0, avail, avail_ops);
       if (ticket >= avail) {
@@ -489,13 +504,16 @@ __global__ __launch_bounds__(256) void gpuos_resident(KArgs a) {
   // Waves are numbered across workgroups first (wave j of workgroup b is
   // j * blocks + b), so consecutive tickets, dealt round-robin, land on
   // different CUs and XCDs (workgroups are dispatched round-robin over the
-  // XCDs).  Number 0 is the doorbell wave.
+  // XCDs).  Number 0 is the doorbell wave; the next lc_waves (one per XCD for
+  // up to 8) serve the latency-critical ring; the rest run best-effort tiles.
   const uint32_t wib = threadIdx.x / 64;
   const uint32_t num = wib * gridDim.x + blockIdx.x;
   if (num == 0)
     doorbell_loop(a);
+  else if (num - 1 < a.lc_waves)
+    lc_loop(a, num - 1, (lds_u32*)&sdesc[wib][1][0]);
   else
-    worker_loop(a, num - 1, (lds_u32*)&sdesc[wib][0][0], (lds_u32*)&sdesc[wib][1][0]);
+    worker_loop(a, num - 1 - a.lc_waves, (lds_u32*)&sdesc[wib][0][0]);
 }
 
 // ---------------------------------------------------------------------------

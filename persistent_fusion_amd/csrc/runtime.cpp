@@ -515,7 +515,7 @@ struct gpuos_ctx {
   bool host_only = true;
   gpuos_config cfg{};
   hipStream_t stream = nullptr;
-  uint32_t cap = 0, cus = 0, blocks = 0, workers = 0;
+  uint32_t cap = 0, cus = 0, blocks = 0, workers = 0, lc_waves = 0;
 
   // pinned host memory (malloc'd in host-only mode)
   HostCtl* hctl = nullptr;
@@ -1222,6 +1222,7 @@ int apply_config(const gpuos_config* in, gpuos_config& out) {
   if (in->priority) out.priority = in->priority;
   if (in->idle_exit_ms) out.idle_exit_ms = in->idle_exit_ms;
   if (in->stream_min_kib) out.stream_min_kib = in->stream_min_kib;
+  if (in->lc_waves) out.lc_waves = in->lc_waves;
   const uint32_t rs = out.ring_slots;
   if (rs < 64 || rs > (1u << 18) || (rs & (rs - 1)))
     return fail(GPUOS_EINVAL, "ring_slots must be a power of two in [64, 2^18]");
@@ -1234,6 +1235,8 @@ int apply_config(const gpuos_config* in, gpuos_config& out) {
   if (out.fusion > 2 || out.auto_deps > 2 || out.trace > 2 || out.block_on_full > 2 ||
       out.priority > 2)
     return fail(GPUOS_EINVAL, "switch fields take 1 (on) or 2 (off)");
+  if (out.lc_waves < 1 || out.lc_waves > 64)
+    return fail(GPUOS_EINVAL, "lc_waves must be in [1, 64]");
   if (out.max_fuse < 2 || out.max_fuse > (uint32_t)kMaxSteps)
     return fail(GPUOS_EINVAL, "max_fuse must be in [2, 8]");
   return 0;
@@ -1313,6 +1316,7 @@ void gpuos_config_default(gpuos_config* cfg) {
   cfg->priority = 1;
   cfg->idle_exit_ms = 200;
   cfg->stream_min_kib = 32768;
+  cfg->lc_waves = 8;
 }
 
 int gpuos_create(int device, const gpuos_config* cfg_in, gpuos_ctx** out) {
@@ -1357,8 +1361,14 @@ int gpuos_create(int device, const gpuos_config* cfg_in, gpuos_ctx** out) {
     c->cus = 256;
     c->blocks = c->cus * (cfg.waves_per_cu / 4);
   }
-  c->workers = c->blocks * 4 - 1;
+  c->lc_waves = cfg.priority == 1 ? cfg.lc_waves : 0;
+  if (c->lc_waves + 64 > c->blocks * 4) {
+    delete c;
+    return fail(GPUOS_EINVAL, "lc_waves %u leaves too few best-effort waves", cfg.lc_waves);
+  }
+  c->workers = c->blocks * 4 - 1 - c->lc_waves;
   c->st.worker_waves = c->workers;
+  c->st.lc_waves = c->lc_waves;
   c->st.compute_units = c->cus;
 
   rc = alloc_host(c, (void**)&c->hctl, sizeof(HostCtl));
@@ -1424,7 +1434,7 @@ int gpuos_create(int device, const gpuos_config* cfg_in, gpuos_ctx** out) {
       a.cap_mask = c->cap - 1;
       a.ends_mask = 2 * c->cap - 1;
       a.workers = c->workers;
-      a.lc_enabled = cfg.priority == 1 ? 1u : 0u;
+      a.lc_waves = c->lc_waves;
       // s_memrealtime counts at 100 MHz
       a.idle_exit_ticks = cfg.idle_exit_ms == 0xFFFFFFFFu ? 0 : (uint64_t)cfg.idle_exit_ms * 100000u;
       e = hipEventCreate(&c->ev_start);

@@ -44,15 +44,16 @@ class GpuosOp(C.Structure):
 class GpuosConfig(C.Structure):
     _fields_ = [(name, C.c_uint32) for name in (
         "ring_slots", "waves_per_cu", "tile_elems", "be_tile_elems", "fusion", "auto_deps",
-        "trace", "block_on_full", "max_fuse", "priority", "idle_exit_ms", "stream_min_kib")] + [
-            ("reserved", C.c_uint32 * 4)]
+        "trace", "block_on_full", "max_fuse", "priority", "idle_exit_ms", "stream_min_kib",
+        "lc_waves")] + [("reserved", C.c_uint32 * 3)]
 
 
 class GpuosStats(C.Structure):
     _fields_ = [(name, C.c_uint64) for name in (
         "ops_submitted", "ops_fused", "descs_published", "descs_completed", "flushes",
         "ring_full_waits", "deps_explicit", "deps_auto", "device_error", "error_desc",
-        "worker_waves", "compute_units", "kernel_ns", "launches")] + [("reserved", C.c_uint64 * 2)]
+        "worker_waves", "compute_units", "kernel_ns", "launches", "lc_waves")] + [
+            ("reserved", C.c_uint64 * 1)]
 
 
 class GpuosTraceRec(C.Structure):

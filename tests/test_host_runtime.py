@@ -305,7 +305,8 @@ def test_host_only_sync_reports_timeout_and_config_errors():
         with pytest.raises(GpuosError) as e:
             c.sync(0, 0.01)
         assert e.value.status == gpuos.ETIMEDOUT
-    for bad in ({"ring_slots": 100}, {"waves_per_cu": 6}, {"tile_elems": 100}, {"max_fuse": 9}):
+    for bad in ({"ring_slots": 100}, {"waves_per_cu": 6}, {"tile_elems": 100}, {"max_fuse": 9},
+                {"lc_waves": 65}):
         with pytest.raises(GpuosError):
             Context(DEVICE_NONE, **bad)
 
