@@ -238,6 +238,7 @@ def decode_leg(device=0, reps=3):
         if r:
             times.append(time.perf_counter() - t0)
     tr = ctx.trace(1 << 16)
+    descs_per_run = ctx.stats()["descs_published"] // (reps + 1)
     ctx.destroy()
     torch.cuda.synchronize()
     per_op = []
@@ -249,8 +250,9 @@ def decode_leg(device=0, reps=3):
     ops = len(wl.ops)
     byt = (wl.meta["weight_bytes"] + wl.meta["kv_bytes"]) * tokens
     best, best_b = min(times), min(per_op)
-    # device-side time per token from the trace of the last run
-    recs = sorted(tr, key=lambda x: x["seq"])[-ops:]
+    # device-side span of the last run from the trace (fused descriptors
+    # carry several ops, so count descriptors, not ops)
+    recs = sorted(tr, key=lambda x: x["seq"])[-descs_per_run:]
     dev_s = (max(x["t_done"] for x in recs) - min(x["t_claim"] for x in recs)) * 1e-8 if recs else None
     del t
     torch.cuda.empty_cache()

@@ -25,7 +25,11 @@ namespace gpuos {
 
 // Internal opcodes beyond the public ones (gpuos_opcode).
 enum : uint8_t {
-  OP_FUSED_EW = 32,  // register-resident elementwise chain
+  OP_FUSED_EW = 32,   // register-resident elementwise chain
+  OP_NORM_GEMV = 33,  // RMSNORM -> GEMV (-> SILU_MUL): every GEMV tile
+                      // normalises the input row itself (tile 0 also stores
+                      // it); with the SiLU gate a tile computes gate row i
+                      // and up row F + i together
 };
 
 // Completion counting: descriptors with more than kSubCounters tiles count
@@ -98,6 +102,19 @@ struct alignas(16) DevDesc {
       uint8_t _pad[80];
     } p;
     struct {
+      uint64_t W;           // 18-19: GEMV weights [M x K] bf16
+      uint64_t out;         // 20-21: GEMV output [M] (0 = not stored)
+      uint64_t x;           // 22-23: RMSNORM input [K]
+      uint64_t g;           // 24-25: RMSNORM gain [K]
+      uint64_t h;           // 26-27: RMSNORM output [K] (0 = not stored)
+      uint64_t act;         // 28-29: SILU_MUL output [F] (0 = no SiLU gate)
+      uint32_t M;           // 30
+      uint32_t K;           // 31
+      float eps;            // 32
+      uint32_t F;           // 33: gate rows (M == 2F) when act != 0
+      uint8_t _pad[80];
+    } ng;
+    struct {
       uint64_t in[4];       // 18-25: in[0] = chain input, in[1..3] operands
       uint64_t out[8];      // 26-41: output pointer of step s (FSF_STORE)
       uint8_t step_op[8];   // 42-43
@@ -119,6 +136,7 @@ static_assert(offsetof(DevDesc, p.src_len) == 26 * 4, "src_len at dword 26");
 static_assert(offsetof(DevDesc, p.alpha) == 28 * 4, "alpha at dword 28");
 static_assert(offsetof(DevDesc, p.aux) == 30 * 4, "aux at dword 30");
 static_assert(offsetof(DevDesc, f.out) == 26 * 4, "fused out at dword 26");
+static_assert(offsetof(DevDesc, ng.M) == 30 * 4, "norm-GEMV M at dword 30");
 static_assert(offsetof(DevDesc, f.step_op) == 42 * 4, "step_op at dword 42");
 static_assert(offsetof(DevDesc, f.step_fl) == 44 * 4, "step_fl at dword 44");
 static_assert(offsetof(DevDesc, f.fscal) == 46 * 4, "fscal at dword 46");

@@ -207,17 +207,23 @@ __device__ __forceinline__ void run_ticket(const KArgs& a, uint64_t ticket, Cach
   };
   if (!c.deps_ok) {
     const uint32_t w0 = d(0);
-    if ((w0 & 0xffu) == GPUOS_OP_GEMV && ((w0 >> 16) & DF_AUX_READY)) {
+    const uint32_t op = w0 & 0xffu;
+    if ((op == GPUOS_OP_GEMV || op == OP_NORM_GEMV) && ((w0 >> 16) & DF_AUX_READY)) {
       // the weights are final: start streaming them, then wait for x
       auto ready = [&]() {
         wait_deps<RING>(a, c);
         c.deps_ok = 1;
         claimed();
       };
-      if (((w0 >> 8) & 0xffu) == GPUOS_BF16)
+      const bool bf = ((w0 >> 8) & 0xffu) == GPUOS_BF16;
+      if (op == OP_NORM_GEMV && bf)
+        norm_gemv_tile<kResidentLoadCP, kResidentStoreCP>(d, tile, ready);
+      else if (op == GPUOS_OP_GEMV && bf)
         gemv_tile<GPUOS_BF16, kResidentLoadCP, kResidentStoreCP>(d, tile, ready);
-      else
+      else if (op == GPUOS_OP_GEMV)
         gemv_tile<GPUOS_F32, kResidentLoadCP, kResidentStoreCP>(d, tile, ready);
+      else
+        report_error(a, RING, c.seq, DERR_BAD_OPCODE);
       finish_tile<RING>(a, c, tile);
       return;
     }

@@ -135,8 +135,19 @@ class SmallVec {
     truncate((size_t)(std::remove_if(begin(), end(), p) - begin()));
   }
   void sort_unique() {
-    std::sort(begin(), end());
-    truncate((size_t)(std::unique(begin(), end()) - begin()));
+    if (n_ <= 1) return;
+    T* a = begin();
+    if (n_ <= 16) {
+      for (uint32_t i = 1; i < n_; ++i) {  // insertion sort: lists are short
+        const T v = a[i];
+        uint32_t j = i;
+        for (; j > 0 && v < a[j - 1]; --j) a[j] = a[j - 1];
+        a[j] = v;
+      }
+    } else {
+      std::sort(a, a + n_);
+    }
+    truncate((size_t)(std::unique(a, a + n_) - a));
   }
 
  private:
@@ -535,6 +546,7 @@ struct gpuos_ctx {
   uint64_t id_base = 1;            // ids below are retired and forgotten
   std::deque<uint64_t> idseq;      // (ring << 63) | seq, 0 = staged
   std::vector<Staged> staged;
+  std::vector<Planned> plan;       // fusion pass output, reused across flushes
   uint64_t pub_seq[kRings] = {0, 0};
   uint64_t pub_tiles[kRings] = {0, 0};
   uint64_t tail_written[kRings] = {0, 0};
@@ -646,6 +658,14 @@ void set_tiling(const gpuos_config& cfg, uint32_t workers, DevDesc& d) {
       rpt = std::min(rpt, std::max<uint32_t>(1, by_waves));
       d.tile = rpt;
       d.ntiles = ceil_div(d.rows, rpt);
+      break;
+    }
+    case OP_NORM_GEMV: {
+      const uint32_t units = d.ng.act ? d.ng.F : d.ng.M;
+      uint32_t r = ceil_div(units, std::max<uint32_t>(1, workers));
+      r = std::min<uint32_t>(std::max<uint32_t>(r, 1), 16);
+      d.tile = r;
+      d.ntiles = ceil_div(units, r);
       break;
     }
     case GPUOS_OP_GEMV: {
@@ -835,21 +855,109 @@ void mark_streaming(const gpuos_config& cfg, DevDesc& d) {
   if (bytes >= (uint64_t)cfg.stream_min_kib * 1024) d.flags |= GPUOS_FLAG_NONTEMPORAL;
 }
 
+// Is output range `w` of staged op `from` - 1 read by any op staged after it?
+bool read_later(gpuos_ctx* c, size_t from, const Range& w) {
+  for (size_t k = from; k < c->staged.size(); ++k) {
+    const OpRanges R = op_ranges(c->staged[k].op);
+    for (int q = 0; q < R.nr; ++q)
+      if (overlaps(R.r[q], w)) return true;
+  }
+  return false;
+}
+
+// RMSNORM (one bf16 row of K) -> GEMV on that row (K <= 1,024) -> optionally
+// SILU_MUL on the two halves of the GEMV output: fused into one descriptor
+// when the ops are adjacent, in one ring, 16-byte aligned, and no output
+// overlaps an input of the group (tiles run concurrently).  Returns the
+// number of user ops fused (0 = none).
+uint32_t try_norm_gemv(gpuos_ctx* c, size_t i, size_t end, DevDesc& d) {
+  if (i + 1 >= end) return 0;
+  const Staged& sa = c->staged[i];
+  const Staged& sb = c->staged[i + 1];
+  const gpuos_op& A = sa.op;
+  const gpuos_op& B = sb.op;
+  if (A.opcode != GPUOS_OP_RMSNORM || B.opcode != GPUOS_OP_GEMV) return 0;
+  if (A.dtype != GPUOS_BF16 || B.dtype != GPUOS_BF16 || sa.ring != sb.ring) return 0;
+  const uint32_t K = A.row_len, M = (uint32_t)B.aux[0];
+  if (A.rows != 1 || (uint32_t)B.aux[1] != K || K % 8 || K > 1024 || B.in[0] != A.out) return 0;
+  if (A.src_len[0] && A.src_len[0] < K) return 0;
+  const uint64_t x = (uint64_t)A.in[0], g = (uint64_t)A.in[2], h = (uint64_t)A.out;
+  const uint64_t W = (uint64_t)B.in[2], y = (uint64_t)B.out;
+  for (uint64_t p : {x, g, h, W, y})
+    if (p % 16) return 0;
+  const Range rx{x, x + 2ull * K}, rg{g, g + 2ull * K}, rh{h, h + 2ull * K};
+  const Range rW{W, W + 2ull * M * K}, ry{y, y + 2ull * M};
+  for (const Range& o : {rh, ry})
+    for (const Range& in : {rx, rg, rW})
+      if (overlaps(o, in)) return 0;
+  if (overlaps(rh, ry)) return 0;
+  uint32_t count = 2;
+  uint64_t act = 0;
+  uint32_t F = 0;
+  if (i + 2 < end) {
+    const Staged& sc = c->staged[i + 2];
+    const gpuos_op& C = sc.op;
+    const uint32_t f = M / 2;
+    if (C.opcode == GPUOS_OP_SILU_MUL && C.dtype == GPUOS_BF16 && sc.ring == sa.ring &&
+        M % 2 == 0 && C.n == f && (uint64_t)C.in[0] == y && (uint64_t)C.in[1] == y + 2ull * f &&
+        (!C.src_len[0] || C.src_len[0] >= f) && (!C.src_len[1] || C.src_len[1] >= f)) {
+      const Range ra{(uint64_t)C.out, (uint64_t)C.out + 2ull * f};
+      bool clear = !overlaps(ra, ry);
+      for (const Range& in : {rx, rg, rW, rh})
+        if (overlaps(ra, in)) clear = false;
+      if (clear) {
+        act = (uint64_t)C.out;
+        F = f;
+        count = 3;
+      }
+    }
+  }
+  memset(&d, 0, sizeof d);
+  d.opcode = OP_NORM_GEMV;
+  d.dtype = GPUOS_BF16;
+  d.flags = (uint8_t)((B.flags & DF_AUX_READY) | ((A.flags | B.flags) & GPUOS_FLAG_NONTEMPORAL));
+  d.n = F ? F : M;
+  d.ng.W = W;
+  d.ng.x = x;
+  d.ng.g = g;
+  // intermediates are stored unless transient and unread by later ops
+  const bool keep_h = !(A.flags & GPUOS_FLAG_TRANSIENT) || read_later(c, i + count, rh);
+  const bool keep_y = !F || !(B.flags & GPUOS_FLAG_TRANSIENT) || read_later(c, i + count, ry);
+  d.ng.h = keep_h ? h : 0;
+  d.ng.out = keep_y ? y : 0;
+  d.ng.act = act;
+  d.ng.M = M;
+  d.ng.K = K;
+  d.ng.eps = A.eps;
+  d.ng.F = F;
+  d.user_ops = count;
+  set_tiling(c->cfg, c->workers, d);
+  return count;
+}
+
 void plan_ops(gpuos_ctx* c, size_t begin, size_t end, std::vector<Planned>& plan) {
   const gpuos_config& cfg = c->cfg;
   const bool fuse = cfg.fusion == 1;
   size_t i = begin;
   while (i < end) {
     const Staged& s0 = c->staged[i];
-    Planned pl;
+    Planned& pl = plan.emplace_back();
     pl.first = i;
     pl.count = 1;
     pl.ring = s0.ring;
+    pl.deps.clear();
     size_t j = i + 1;
+    if (fuse) {
+      const uint32_t k = try_norm_gemv(c, i, end, pl.desc);
+      if (k) {
+        pl.count = k;
+        c->st.ops_fused += k - 1;
+      }
+    }
     // a chain needs a next op of the same ring, dtype and size that reads
     // this op's output
     bool chain_possible = false;
-    if (fuse && j < end && fusable(s0.op)) {
+    if (pl.count == 1 && fuse && j < end && fusable(s0.op)) {
       const gpuos_op& nx = c->staged[j].op;
       chain_possible = c->staged[j].ring == s0.ring && fusable(nx) && nx.dtype == s0.op.dtype &&
                        nx.n == s0.op.n && (nx.in[0] == s0.op.out || nx.in[1] == s0.op.out);
@@ -944,8 +1052,7 @@ void plan_ops(gpuos_ctx* c, size_t begin, size_t end, std::vector<Planned>& plan
       for (uint64_t dep : c->staged[i + k].deps)
         if (dep < gfirst || dep > glast) pl.deps.push_back(dep);
     pl.deps.sort_unique();
-    plan.push_back(std::move(pl));
-    i = i + plan.back().count;
+    i = i + pl.count;
   }
 }
 
@@ -1140,7 +1247,9 @@ int flush_impl(gpuos_ctx* c) {
   if (check_device_error(c)) return GPUOS_EDEVICE;
   if (c->staged.empty()) return 0;
   ++c->st.flushes;
-  std::vector<Planned> plan;
+  std::vector<Planned>& plan = c->plan;
+  plan.clear();
+  plan.reserve(c->staged.size());
   plan_ops(c, 0, c->staged.size(), plan);
   size_t done_ops = 0;
   int rc = 0;
@@ -1489,8 +1598,9 @@ int gpuos_submit(gpuos_ctx* c, const gpuos_op* ops, uint32_t n, uint64_t* ids_ou
     }
   }
   auto retired = [c](uint64_t id) { return id_retired(c, id); };
+  c->staged.reserve(c->staged.size() + n);
   for (uint32_t i = 0; i < n; ++i) {
-    Staged s;
+    Staged& s = c->staged.emplace_back();
     s.op = ops[i];
     s.id = c->next_id++;
     s.ring = (ops[i].flags & GPUOS_FLAG_LC) ? 1 : 0;
@@ -1525,7 +1635,6 @@ int gpuos_submit(gpuos_ctx* c, const gpuos_op* ops, uint32_t n, uint64_t* ids_ou
     s.deps.sort_unique();
     c->idseq.push_back(0);
     if (ids_out) ids_out[i] = s.id;
-    c->staged.push_back(std::move(s));
   }
   c->st.ops_submitted += n;
   if ((c->since_prune += n) >= 4096) {

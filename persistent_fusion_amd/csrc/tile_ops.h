@@ -828,6 +828,109 @@ __device__ __forceinline__ void gemv_tile(D d, uint32_t t, Ready ready = Ready()
   }
 }
 
+// RMSNORM -> GEMV (-> SILU_MUL), bf16, K <= 1,024 (the normalised row is two
+// 16-byte vectors per lane, in the GEMV's chunk layout).  Each value is the
+// one the separate ops would store: the norm is summed in the same order as
+// RMSNORM's in-register path and rounded to bf16, the GEMV accumulates in
+// the same order as gemv_rows<4, 2>, its outputs are rounded to bf16, and the
+// gate is applied to those rounded values.  Up to 4 output rows per step (2
+// gate/up pairs with the epilogue); the first step's weights are requested
+// before `ready()`.
+template <int CPL, int CPS, class D, class Ready = NoWait>
+__device__ __forceinline__ void norm_gemv_tile(D d, uint32_t t, Ready ready = Ready()) {
+  using T = DTr<GPUOS_BF16, CPL, CPS>;
+  const uint64_t pW = d.q(18), pout = d.q(20), px = d.q(22), pg = d.q(24), ph = d.q(26),
+                 pact = d.q(28);
+  const uint32_t M = d(30), K = d(31), F = d(33), tile = d(7);
+  const float eps = __uint_as_float(d(32));
+  const bool gate = pact != 0;
+  const uint32_t units = gate ? F : M;
+  const uint32_t u0 = t * tile;
+  const uint32_t u1 = u0 + tile < units ? u0 + tile : units;
+  const uint32_t lane = lane_id();
+  const uint32_t chunks = K / 8;
+  const rsrc_t xr = make_rsrc_n(px, chunks * 16u), gr = make_rsrc_n(pg, chunks * 16u);
+  const rsrc_t W = make_rsrc_n(pW, M * K * 2u);
+  const rsrc_t out = make_rsrc(pout), act = make_rsrc(pact);
+  constexpr int R = 4;
+  const uint32_t step = gate ? 2u : 4u;  // units per step
+  float hx[2][8];
+  bool waiting = true;
+  for (uint32_t i = u0; i < u1; i += step) {
+    // the step's rows: i .. i + 3, or gate rows i, i + 1 and up rows F + i, F + i + 1
+    uint32_t row[R];
+    bool ok[R];
+#pragma unroll
+    for (int r = 0; r < R; ++r) {
+      const uint32_t k = gate ? (uint32_t)(r & 1) : (uint32_t)r;
+      ok[r] = i + k < u1;
+      row[r] = (gate && r >= 2 ? F : 0u) + i + k;
+    }
+    u32x4 wr[R][2];
+#pragma unroll
+    for (int c = 0; c < 2; ++c) {
+      const uint32_t ch = lane + 64 * c;
+#pragma unroll
+      for (int r = 0; r < R; ++r)
+        wr[r][c] = ld128<CPL>(W, ok[r] && ch < chunks ? 2u * (row[r] * K + ch * 8) : 0xFFF00000u);
+    }
+    if (waiting) {
+      compiler_fence();
+      ready();
+      compiler_fence();
+      waiting = false;
+      // the normalised row, as RMSNORM computes and stores it
+      float xv[2][8], gv[2][8];
+      T::ldq(xr, lane, xv[0]);
+      T::ldq(xr, lane + 64, xv[1]);
+      T::ldq(gr, lane, gv[0]);
+      T::ldq(gr, lane + 64, gv[1]);
+      float q = 0.0f;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) q += xv[0][e] * xv[0][e];
+#pragma unroll
+      for (int e = 0; e < 8; ++e) q += xv[1][e] * xv[1][e];
+      const float ss = wave_sum(q);
+      const float inv = 1.0f / sqrtf(ss / (float)K + eps);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        hx[0][e] = T::round(xv[0][e] * inv * gv[0][e]);
+        hx[1][e] = T::round(xv[1][e] * inv * gv[1][e]);
+      }
+      if (t == 0 && ph) {
+        const rsrc_t hr = make_rsrc_n(ph, chunks * 16u);
+        T::stq(hr, lane, hx[0]);
+        T::stq(hr, lane + 64, hx[1]);
+      }
+    }
+    float acc[R] = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+    for (int c = 0; c < 2; ++c) {
+#pragma unroll
+      for (int r = 0; r < R; ++r) {
+        float w[8];
+        unpack_bf16x8(wr[r][c], w);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) acc[r] = __builtin_fmaf(w[e], hx[c][e], acc[r]);
+      }
+    }
+    float v[R];
+#pragma unroll
+    for (int r = 0; r < R; ++r) v[r] = T::round(wave_sum(acc[r]));
+    if (lane == 0) {
+#pragma unroll
+      for (int r = 0; r < R; ++r)
+        if (ok[r] && pout) T::st(out, row[r], v[r]);
+      if (gate) {
+#pragma unroll
+        for (int k = 0; k < 2; ++k)
+          if (ok[k]) T::st(act, i + k, ew_apply<GPUOS_OP_SILU_MUL>(v[k], v[k + 2], 0.0f));
+      }
+    }
+  }
+  if (waiting) ready();
+}
+
 // ---------------------------------------------------------------------------
 // attention scores: out[h*S + j] = alpha * <q_h, K[j, h]>, `tile` key rows per
 // tile.  Lanes walk the key rows in 16-byte chunks; the Dh/8 lanes holding
@@ -1062,6 +1165,10 @@ __device__ __forceinline__ uint32_t exec_tile(D d, uint32_t t) {
       return 0;
     case GPUOS_OP_SPIN:
       spin_tile(d, t);
+      return 0;
+    case OP_NORM_GEMV:
+      if (!bf) return (uint32_t)DERR_BAD_OPCODE;
+      norm_gemv_tile<CPL, CPS>(d, t);
       return 0;
     default:
       return (uint32_t)DERR_BAD_OPCODE;

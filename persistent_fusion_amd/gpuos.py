@@ -288,4 +288,8 @@ def decode_desc(raw: bytes) -> dict:
     d["step_fl"] = [(w[44 + s // 4] >> (8 * (s % 4))) & 0xFF for s in range(8)]
     d["fscal"] = list(struct.unpack("<8f", raw[46 * 4:54 * 4]))
     d["alpha"] = struct.unpack("<f", raw[28 * 4:29 * 4])[0]
+    # RMSNORM -> GEMV (-> SILU_MUL) descriptors
+    d["ng"] = {"W": q(18), "out": q(20), "x": q(22), "g": q(24), "h": q(26), "act": q(28),
+               "M": w[30], "K": w[31], "eps": struct.unpack("<f", raw[32 * 4:33 * 4])[0],
+               "F": w[33]}
     return d

@@ -311,3 +311,18 @@ def test_small_decode_local_check():
     got = runner.run_resident(wl)
     bad = oracle.local_check(wl, got, oracle.compare)
     assert not bad, [(i, wl.ops[i].kind, n, str(r)) for i, n, r in bad[:5]]
+
+
+def test_decode_norm_gemv_fusion_is_bit_identical():
+    """RMSNORM -> GEMV -> SILU_MUL fused into one descriptor stores exactly the
+    values the three separate ops store (same sums in the same order, same
+    bf16 roundings)."""
+    _need_gpu()
+    say("decode 3 layers x 3 tokens, fusion on vs off")
+    outs = {}
+    for fusion in (1, 2):
+        wl = workloads.gen_decode(seed=4, layers=3, tokens=3)
+        names = ["x", "h", "qkv", "gu", "act"] + [f"K{l}" for l in range(3)] + [f"V{l}" for l in range(3)]
+        outs[fusion] = runner.run_resident(wl, outputs=names, fusion=fusion)
+    for name, v in outs[1].items():
+        assert np.array_equal(v, outs[2][name]), name

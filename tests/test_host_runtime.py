@@ -328,3 +328,64 @@ def test_elementwise_queue_encoding_matches_workload():
             assert d["ptr"][0] == base[op.out.buf]
             got = sorted(x for x in d["deps"] if x)
             assert got == sorted({j + 1 for j in op.deps})
+
+
+# ----------------------------------------------------------------------------
+# RMSNORM -> GEMV (-> SILU_MUL) fusion
+
+
+def _norm_gemv_ops(K=896, F=4864, with_gate=True, h_is_x=False, transient_h=False):
+    x, g, h, W, gu, act = (buf(i) for i in range(6))
+    h = x if h_is_x else h
+    M = 2 * F
+    ops = [make_op("rmsnorm", h, [x], aux=g, n=K, dtype="bf16", rows=1, row_len=K, eps=1e-6,
+                   flags=gpuos.FLAG_TRANSIENT if transient_h else 0),
+           make_op("gemv", gu, [h], aux=W, n=M, dtype="bf16", dims=(M, K))]
+    if with_gate:
+        ops.append(make_op("silu_mul", act, [gu, gu + 2 * F], n=F, dtype="bf16"))
+    return (gpuos.GpuosOp * len(ops))(*ops), (x, g, h, W, gu, act)
+
+
+def test_norm_gemv_gate_fuses_into_one_descriptor():
+    ops, (x, g, h, W, gu, act) = _norm_gemv_ops()
+    with ctx() as c:
+        c.submit(ops)
+        c.flush()
+        assert c.published(0) == 1
+        d = desc(c, 1)
+        assert d["opcode"] == 33 and d["user_ops"] == 3
+        ng = d["ng"]
+        assert (ng["x"], ng["g"], ng["h"], ng["W"], ng["out"], ng["act"]) == (x, g, h, W, gu, act)
+        assert (ng["M"], ng["K"], ng["F"]) == (2 * 4864, 896, 4864)
+        assert abs(ng["eps"] - 1e-6) < 1e-12
+        assert d["n"] == 4864 and d["ntiles"] * d["tile"] >= 4864
+        # the weights have no queued writer: the kernel may stream them early
+        assert d["flags"] & 0x80
+
+
+def test_norm_gemv_without_gate_and_refusals():
+    ops, _ = _norm_gemv_ops(with_gate=False)
+    with ctx() as c:
+        c.submit(ops)
+        c.flush()
+        assert c.published(0) == 1 and desc(c, 1)["user_ops"] == 2
+    # a norm written over its own input would race with the other tiles
+    ops, _ = _norm_gemv_ops(h_is_x=True)
+    with ctx() as c:
+        c.submit(ops)
+        c.flush()
+        assert c.published(0) == 3
+    # fusion off: three descriptors
+    ops, _ = _norm_gemv_ops()
+    with ctx(fusion=2) as c:
+        c.submit(ops)
+        c.flush()
+        assert c.published(0) == 3
+
+
+def test_norm_gemv_drops_unread_transient_norm_output():
+    ops, _ = _norm_gemv_ops(transient_h=True)
+    with ctx() as c:
+        c.submit(ops)
+        c.flush()
+        assert desc(c, 1)["ng"]["h"] == 0
