@@ -158,11 +158,13 @@ struct alignas(256) DevRing {
 // first, so the descriptors below avail_tiles are always within avail_ops.
 struct alignas(256) AvailLine {
   uint64_t avail_tiles;  // tickets below this value are runnable
-  uint64_t avail_ops;    // descriptors made visible
+  uint64_t avail_ops;    // descriptors whose ticket ranges are published
   uint64_t stop_ticket;  // ring 0: once stop_epoch is the running launch's
   uint64_t stop_epoch;   // epoch, waves whose next ticket is >= stop_ticket
                          // exit (stop_ticket is stored first)
-  uint64_t _p[28];
+  uint64_t copied_ops;   // descriptors (retired, copied_ops] are in the
+                         // device ring; later ones are read from the host
+  uint64_t _p[27];
 };
 
 struct alignas(256) DevCtl {

@@ -101,19 +101,30 @@ __device__ __forceinline__ uint64_t find_seq(const KArgs& a, uint64_t ticket, ui
   return hi;
 }
 
-// Loads descriptor `seq` from the device ring (lane i gets dword i).  The
-// ring slot is read through the caches first; a copy left over from the
-// slot's previous occupant is recognised by its sequence words (the seq field
-// in the first 128-byte line, the check word in the second) and re-read from
-// the device coherence point.
+// Loads descriptor `seq` (lane i gets dword i).  A descriptor the doorbell
+// wave has already copied (seq <= `copied`) comes from the device ring: read
+// through the caches first, and if that copy is the slot's previous occupant
+// (recognised by the seq field in the first 128-byte line and the check word
+// in the second) again from the device coherence point.  A newer one comes
+// straight from the pinned host ring, whose slot does not change before the
+// descriptor retires.
 template <int RING>
-__device__ __forceinline__ void fetch_desc(const KArgs& a, uint64_t seq, Cached& c) {
-  const rsrc_t r = make_rsrc(reinterpret_cast<uint64_t>(&a.ddesc[RING][slot_of(seq, a.cap_mask)]));
+__device__ __forceinline__ void fetch_desc(const KArgs& a, uint64_t seq, uint64_t copied, Cached& c) {
+  const uint32_t slot = slot_of(seq, a.cap_mask);
   const uint32_t off = 4u * lane_id();
-  uint32_t dw = ld32<CP_DEFAULT>(r, off);
-  const VDesc d{dw};
-  if (d.q(4) != seq || d(63) != ((uint32_t)seq ^ kDescMagic)) {
-    dw = ld32<CP_DEVICE>(r, off);
+  uint32_t dw;
+  if (seq <= copied) {
+    const rsrc_t r = make_rsrc(reinterpret_cast<uint64_t>(&a.ddesc[RING][slot]));
+    dw = ld32<CP_DEFAULT>(r, off);
+    const VDesc d{dw};
+    if (d.q(4) != seq || d(63) != ((uint32_t)seq ^ kDescMagic)) {
+      dw = ld32<CP_DEVICE>(r, off);
+      const VDesc f{dw};
+      if (f.q(4) != seq || f(63) != ((uint32_t)seq ^ kDescMagic)) report_error(a, RING, seq, DERR_DESC_CHECK);
+    }
+  } else {
+    const rsrc_t r = make_rsrc(reinterpret_cast<uint64_t>(&a.hdesc[RING][slot]));
+    dw = ld32<CP_SYSTEM>(r, off);
     const VDesc f{dw};
     if (f.q(4) != seq || f(63) != ((uint32_t)seq ^ kDescMagic)) report_error(a, RING, seq, DERR_DESC_CHECK);
   }
@@ -238,23 +249,28 @@ __device__ __forceinline__ void run_ticket(const KArgs& a, uint64_t ticket, Cach
 
 // Maps a runnable ticket to its descriptor (refreshing the cache if needed).
 template <int RING>
-__device__ __forceinline__ void map_ticket(const KArgs& a, uint64_t ticket, uint64_t avail_ops, Cached& c) {
+__device__ __forceinline__ void map_ticket(const KArgs& a, uint64_t ticket, uint64_t avail_ops,
+                                           uint64_t copied, Cached& c) {
   if (c.seq != 0 && ticket < c.end) return;
   const uint64_t seq = find_seq<RING>(a, ticket, c.seq, avail_ops);
-  fetch_desc<RING>(a, seq, c);
+  fetch_desc<RING>(a, seq, copied, c);
 }
 
 // Reads a ring's published-work replica: avail_tiles first, then (after the
-// first load has returned) avail_ops, which was stored before it.
-__device__ __forceinline__ void read_avail(const AvailLine* l, uint64_t& tiles, uint64_t& ops) {
-  uint64_t t = 0, o = 0;
+// first load has returned) avail_ops, which was stored before it, and the
+// copied frontier (any value it held is a valid lower bound).
+__device__ __forceinline__ void read_avail(const AvailLine* l, uint64_t& tiles, uint64_t& ops,
+                                           uint64_t& copied) {
+  uint64_t t = 0, o = 0, k = 0;
   if (lane_id() == 0) {
     t = ld_rlx_agent(&l->avail_tiles);
     wait_mem();
     o = ld_rlx_agent(&l->avail_ops);
+    k = ld_rlx_agent(&l->copied_ops);
   }
   tiles = bcast64(t);
   ops = bcast64(o);
+  copied = bcast64(k);
 }
 
 // Latency-critical ring: served only by the reserved waves, which claim its
@@ -284,9 +300,9 @@ __device__ __forceinline__ void service_lc(const KArgs& a, const AvailLine* line
                : 0u;
     }
     if (!bcast(ok)) continue;
-    uint64_t tiles, ops;
-    read_avail(line, tiles, ops);
-    map_ticket<1>(a, nxt, ops, c);
+    uint64_t tiles, ops, copied;
+    read_avail(line, tiles, ops, copied);
+    map_ticket<1>(a, nxt, ops, copied, c);
     run_ticket<1>(a, nxt, c);
   }
 }
@@ -311,7 +327,7 @@ __device__ __forceinline__ void lc_loop(const KArgs& a, uint32_t w, lds_u32* slo
 __device__ __forceinline__ void worker_loop(const KArgs& a, uint32_t w, lds_u32* slot0) {
   const AvailLine* line0 = &a.dctl->avail[0][w % kReplicas];
   Cached c0{0, 0, 0, slot0, 0};
-  uint64_t avail = 0, avail_ops = 0;
+  uint64_t avail = 0, avail_ops = 0, copied = 0;
   uint32_t idle = 0;
   // tickets are dealt round-robin: this wave owns those = w (mod workers),
   // from the first one this launch has not inherited as done
@@ -320,7 +336,7 @@ __device__ __forceinline__ void worker_loop(const KArgs& a, uint32_t w, lds_u32*
   if (ticket < base) ticket += a.workers;
   for (;;) {
     if (ticket >= avail) {
-      read_avail(line0, avail, avail_ops);
+      read_avail(line0, avail, avail_ops, copied);
       if (ticket >= avail) {
         uint64_t se = 0, stop = 0;
         if (lane_id() == 0) {
@@ -340,7 +356,7 @@ __device__ __forceinline__ void worker_loop(const KArgs& a, uint32_t w, lds_u32*
       }
     }
     idle = 0;
-    map_ticket<0>(a, ticket, avail_ops, c0);
+    map_ticket<0>(a, ticket, avail_ops, copied, c0);
     run_ticket<0>(a, ticket, c0);
     ticket += a.workers;
   }
@@ -349,45 +365,37 @@ __device__ __forceinline__ void worker_loop(const KArgs& a, uint32_t w, lds_u32*
 // ---------------------------------------------------------------------------
 // doorbell / tracker wave
 
-// Copies descriptors (from, to] from the pinned host ring into the device
-// ring: 16-byte system-scope loads, four descriptors per wave-wide load and
-// up to 32 in flight, written through to the device coherence point.
+// Publishes the ticket ranges of descriptors (avail, tail]: their ends are
+// copied from the pinned host ring into the device ring of ends (8 loads of
+// 8 bytes per lane in flight, 512 descriptors per round trip over the host
+// link), then every replica gets avail_ops and, after it, avail_tiles.
 template <int RING>
-__device__ __forceinline__ void copy_descs(const KArgs& a, uint64_t from, uint64_t to) {
-  const uint32_t mask = a.cap_mask;
-  const uint32_t lane = lane_id();
-  const rsrc_t hr = make_rsrc(reinterpret_cast<uint64_t>(a.hdesc[RING]));
-  const rsrc_t dr = make_rsrc(reinterpret_cast<uint64_t>(a.ddesc[RING]));
-  const uint32_t sub = lane / 16, part = lane % 16;  // descriptor in group, 16-byte part
-  for (uint64_t s0 = from + 1; s0 <= to; s0 += 32) {
-    u32x4 v[8];
-#pragma unroll
-    for (int g = 0; g < 8; ++g) {
-      const uint64_t s = s0 + 4 * g + sub;
-      if (s <= to) v[g] = ld128<CP_SYSTEM>(hr, slot_of(s, mask) * kDescBytes + 16u * part);
-    }
-#pragma unroll
-    for (int g = 0; g < 8; ++g) {
-      const uint64_t s = s0 + 4 * g + sub;
-      if (s <= to) st128<CP_DEVICE>(dr, slot_of(s, mask) * kDescBytes + 16u * part, v[g]);
-    }
-  }
-}
-
-template <int RING>
-__device__ __forceinline__ bool publish_ring(const KArgs& a, uint64_t tail, uint64_t& avail, uint64_t& avail_tiles) {
+__device__ __forceinline__ bool publish_ends(const KArgs& a, uint64_t tail, uint64_t& avail,
+                                             uint64_t& avail_tiles) {
   if (tail <= avail) return false;
   const uint32_t mask = a.cap_mask;
   const uint32_t lane = lane_id();
-  copy_descs<RING>(a, avail, tail);
-  for (uint64_t s0 = avail + 1; s0 <= tail; s0 += 64) {
-    const uint64_t s = s0 + lane;
-    if (s <= tail)
-      st_rlx_agent(&a.dends[RING][slot_of(s, a.ends_mask)], ld_rlx_sys(&a.hends[RING][slot_of(s, mask)]));
+  constexpr int B = 8;
+  uint64_t last = 0;
+  for (uint64_t s0 = avail + 1; s0 <= tail; s0 += 64 * B) {
+    uint64_t e[B];
+#pragma unroll
+    for (int k = 0; k < B; ++k) {
+      const uint64_t s = s0 + 64 * k + lane;
+      e[k] = s <= tail ? ld_rlx_sys(&a.hends[RING][slot_of(s, mask)]) : 0;
+    }
+#pragma unroll
+    for (int k = 0; k < B; ++k) {
+      const uint64_t s = s0 + 64 * k + lane;
+      if (s <= tail) st_rlx_agent(&a.dends[RING][slot_of(s, a.ends_mask)], e[k]);
+      if (s == tail) last = e[k];
+    }
   }
-  uint64_t end_tiles = 0;
-  if (lane == 0) end_tiles = ld_rlx_sys(&a.hends[RING][slot_of(tail, mask)]);
-  end_tiles = bcast64(end_tiles);
+  // the lane that loaded ends(tail) shares it
+  const uint64_t holder = ballot((tail - avail - 1) % 64 == lane);
+  const uint32_t src = (uint32_t)__builtin_ctzll(holder);
+  const uint64_t end_tiles = (uint64_t)(uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)last, src) |
+                             ((uint64_t)(uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)(last >> 32), src) << 32);
   wait_mem();
   // every replica: avail_ops, then avail_tiles (one replica per lane)
   if (lane < kReplicas) st_rlx_agent(&a.dctl->avail[RING][lane].avail_ops, tail);
@@ -395,6 +403,43 @@ __device__ __forceinline__ bool publish_ring(const KArgs& a, uint64_t tail, uint
   if (lane < kReplicas) st_rlx_agent(&a.dctl->avail[RING][lane].avail_tiles, end_tiles);
   avail = tail;
   avail_tiles = end_tiles;
+  return true;
+}
+
+// Copies the next (at most kCopyChunk) published descriptors into the device
+// ring: every 16-byte system-scope load of the chunk (four descriptors per
+// wave-wide load) is issued before the first store; the stores write
+// through to the device coherence point, and once they are acknowledged the
+// copied frontier moves.  Retired descriptors are never copied.
+constexpr uint32_t kCopyChunk = 128;
+
+template <int RING>
+__device__ __forceinline__ bool copy_some(const KArgs& a, uint64_t avail, uint64_t retired,
+                                          uint64_t& copied) {
+  if (copied < retired) copied = retired;
+  if (copied >= avail) return false;
+  const uint64_t from = copied;
+  const uint64_t to = avail - from > kCopyChunk ? from + kCopyChunk : avail;
+  constexpr int G = kCopyChunk / 4;  // wave-wide loads of 4 descriptors
+  const uint32_t mask = a.cap_mask;
+  const uint32_t lane = lane_id();
+  const rsrc_t hr = make_rsrc(reinterpret_cast<uint64_t>(a.hdesc[RING]));
+  const rsrc_t dr = make_rsrc(reinterpret_cast<uint64_t>(a.ddesc[RING]));
+  const uint32_t sub = lane / 16, part = lane % 16;  // descriptor in group, 16-byte part
+  u32x4 v[G];
+#pragma unroll
+  for (int g = 0; g < G; ++g) {
+    const uint64_t s = from + 1 + 4 * g + sub;
+    if (s <= to) v[g] = ld128<CP_SYSTEM>(hr, slot_of(s, mask) * kDescBytes + 16u * part);
+  }
+#pragma unroll
+  for (int g = 0; g < G; ++g) {
+    const uint64_t s = from + 1 + 4 * g + sub;
+    if (s <= to) st128<CP_DEVICE>(dr, slot_of(s, mask) * kDescBytes + 16u * part, v[g]);
+  }
+  wait_mem();
+  if (lane < kReplicas) st_rlx_agent(&a.dctl->avail[RING][lane].copied_ops, to);
+  copied = to;
   return true;
 }
 
@@ -436,17 +481,20 @@ __device__ __forceinline__ void release_workers(const KArgs& a, uint64_t tiles0)
 
 __device__ __forceinline__ void doorbell_loop(const KArgs& a) {
   // resume from what earlier launches published and retired
-  uint64_t avail0 = 0, avail1 = 0, ret0 = 0, ret1 = 0, tiles0 = 0, tiles1 = 0;
+  uint64_t avail0 = 0, avail1 = 0, ret0 = 0, ret1 = 0, tiles0 = 0, tiles1 = 0, cp0 = 0, cp1 = 0;
   if (lane_id() == 0) {
     avail0 = ld_rlx_agent(&a.dctl->avail[0][0].avail_ops);
     avail1 = ld_rlx_agent(&a.dctl->avail[1][0].avail_ops);
     tiles0 = ld_rlx_agent(&a.dctl->avail[0][0].avail_tiles);
     tiles1 = ld_rlx_agent(&a.dctl->avail[1][0].avail_tiles);
+    cp0 = ld_rlx_agent(&a.dctl->avail[0][0].copied_ops);
+    cp1 = ld_rlx_agent(&a.dctl->avail[1][0].copied_ops);
     ret0 = ld_rlx_agent(&a.dctl->ring[0].retired);
     ret1 = ld_rlx_agent(&a.dctl->ring[1].retired);
   }
   avail0 = bcast64(avail0); avail1 = bcast64(avail1);
   tiles0 = bcast64(tiles0); tiles1 = bcast64(tiles1);
+  cp0 = bcast64(cp0); cp1 = bcast64(cp1);
   ret0 = bcast64(ret0); ret1 = bcast64(ret1);
   uint64_t beats = 0;
   uint64_t last_work = now_ticks();
@@ -461,8 +509,11 @@ __device__ __forceinline__ void doorbell_loop(const KArgs& a) {
     t1 = bcast64(t1);
     stop = bcast64(stop);
     compiler_fence();
-    bool work = publish_ring<0>(a, t0, avail0, tiles0);
-    work |= publish_ring<1>(a, t1, avail1, tiles1);
+    // ticket ranges first (cheap), then one chunk of descriptor copies
+    bool work = publish_ends<1>(a, t1, avail1, tiles1);
+    work |= publish_ends<0>(a, t0, avail0, tiles0);
+    work |= copy_some<1>(a, avail1, ret1, cp1);
+    work |= copy_some<0>(a, avail0, ret0, cp0);
     work |= retire_ring<0>(a, avail0, ret0);
     work |= retire_ring<1>(a, avail1, ret1);
     ++beats;
