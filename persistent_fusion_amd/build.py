@@ -3,6 +3,7 @@
 from __future__ import annotations
 
 import os
+import re
 import subprocess
 import sys
 
@@ -33,17 +34,52 @@ def hipcc() -> str:
     raise RuntimeError("hipcc not found")
 
 
+# The resident kernel is launched with 8 waves per CU by default (2 per
+# SIMD): it must keep that occupancy and use no scratch memory.
+MIN_WAVES_PER_SIMD = 2
+
+
+def kernel_resources(stderr: str) -> dict:
+    """Per-kernel resource usage from the compiler's resource-usage remarks."""
+    res, cur = {}, None
+    pat = re.compile(r"remark:\s+(.*?):\s+(\S+) \[-Rpass-analysis=kernel-resource-usage\]")
+    for line in stderr.splitlines():
+        m = pat.search(line)
+        if not m:
+            continue
+        key, val = m.group(1).strip(), m.group(2)
+        if key == "Function Name":
+            cur = res.setdefault(val, {})
+        elif cur is not None:
+            cur[key] = val
+    return res
+
+
 def build(verbose: bool = False) -> str:
     tmp = LIB + ".tmp"
-    cmd = [hipcc(), *FLAGS, "-o", tmp] + [os.path.join(CSRC, s) for s in SOURCES]
+    cmd = [hipcc(), *FLAGS, "-Rpass-analysis=kernel-resource-usage", "-o", tmp] + \
+        [os.path.join(CSRC, s) for s in SOURCES]
     if verbose:
         print(" ".join(cmd), flush=True)
     r = subprocess.run(cmd, cwd=CSRC, capture_output=True, text=True)
-    errs = [l for l in r.stderr.splitlines() if "packed-fp32-ops" not in l and l.strip()]
+    errs = [l for l in r.stderr.splitlines()
+            if "packed-fp32-ops" not in l and "kernel-resource-usage" not in l and l.strip()
+            and not l.strip().startswith(("|", "^")) and not l[:8].strip().isdigit()]
     if r.returncode != 0:
         raise RuntimeError("hipcc failed:\n" + "\n".join(errs))
-    if verbose and errs:
-        print("\n".join(errs), file=sys.stderr)
+    res = kernel_resources(r.stderr)
+    for name, k in res.items():
+        if "gpuos_resident" not in name and "gpuos_single" not in name:
+            continue
+        waves = int(k.get("Occupancy [waves/SIMD]", "0"))
+        scratch = int(k.get("ScratchSize [bytes/lane]", "0"))
+        if verbose:
+            print(f"{name}: VGPRs {k.get('VGPRs')} occupancy {waves} waves/SIMD scratch {scratch}",
+                  flush=True)
+        if waves < MIN_WAVES_PER_SIMD or scratch:
+            raise RuntimeError(f"{name}: {k.get('VGPRs')} VGPRs, {waves} waves/SIMD, "
+                               f"{scratch} B scratch: below {MIN_WAVES_PER_SIMD} waves/SIMD "
+                               "or using scratch")
     os.replace(tmp, LIB)
     return LIB
 

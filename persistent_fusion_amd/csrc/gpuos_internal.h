@@ -32,12 +32,14 @@ enum : uint8_t {
                       // and up row F + i together
 };
 
-// Completion counting: descriptors with more than kSubCounters tiles count
-// tile t in sub-counter t % kSubCounters; the wave that fills a sub-counter
-// bumps the second-level counter, which completes the descriptor at
-// kSubCounters.  Spreading the increments over 16 addresses keeps one hot
-// address from serialising the end of a large op.
-constexpr uint32_t kSubCounters = 16;
+// Completion counting: a descriptor of up to 8 tiles counts its tiles in one
+// counter.  A larger one spreads them over S = min(64, ceil(tiles / 8))
+// sub-counters (tile t in sub-counter t % S); the wave that fills a
+// sub-counter bumps the second-level counter, which completes the descriptor
+// at S.  Same-address atomics serialise, so no address takes more than
+// about 8 (sub-counters) or 64 (second level) increments.
+constexpr uint32_t kSubCounters = 64;
+constexpr uint32_t kTilesPerSub = 8;
 // Replicas of the published-work words; wave w polls replica w % kReplicas.
 constexpr uint32_t kReplicas = 16;
 

@@ -101,17 +101,38 @@ __device__ __forceinline__ uint64_t find_seq(const KArgs& a, uint64_t ticket, ui
   return hi;
 }
 
+// Descriptors of at most this many tiles may be read from the pinned host
+// ring before the doorbell wave has copied them; larger ones wait for the
+// copy (so that one op's many waves never read it over the host link).
+constexpr uint64_t kHostReadMaxTiles = 4;
+
 // Loads descriptor `seq` (lane i gets dword i).  A descriptor the doorbell
 // wave has already copied (seq <= `copied`) comes from the device ring: read
 // through the caches first, and if that copy is the slot's previous occupant
 // (recognised by the seq field in the first 128-byte line and the check word
-// in the second) again from the device coherence point.  A newer one comes
-// straight from the pinned host ring, whose slot does not change before the
-// descriptor retires.
+// in the second) again from the device coherence point.  A newer small one
+// comes straight from the pinned host ring, whose slot does not change before
+// the descriptor retires; a newer large one is waited for.
 template <int RING>
-__device__ __forceinline__ void fetch_desc(const KArgs& a, uint64_t seq, uint64_t copied, Cached& c) {
+__device__ __forceinline__ void fetch_desc(const KArgs& a, uint64_t seq, uint64_t copied,
+                                           const AvailLine* line, Cached& c) {
   const uint32_t slot = slot_of(seq, a.cap_mask);
   const uint32_t off = 4u * lane_id();
+  if (seq > copied) {
+    uint64_t lo = 0, hi = 0;
+    if (lane_id() == 0) {
+      lo = ld_rlx_agent(&a.dends[RING][slot_of(seq - 1, a.ends_mask)]);
+      hi = ld_rlx_agent(&a.dends[RING][slot_of(seq, a.ends_mask)]);
+    }
+    if (bcast64(hi) - bcast64(lo) > kHostReadMaxTiles) {
+      while (seq > copied) {
+        __builtin_amdgcn_s_sleep(1);
+        uint64_t k = 0;
+        if (lane_id() == 0) k = ld_rlx_agent(&line->copied_ops);
+        copied = bcast64(k);
+      }
+    }
+  }
   uint32_t dw;
   if (seq <= copied) {
     const rsrc_t r = make_rsrc(reinterpret_cast<uint64_t>(&a.ddesc[RING][slot]));
@@ -173,38 +194,41 @@ __device__ __forceinline__ void finish_tile(const KArgs& a, const Cached& c, uin
   wait_mem();
   if (lane_id() != 0) return;
   bool complete;
+  const uint32_t S = ntiles <= kTilesPerSub ? 1u
+                     : ((ntiles + kTilesPerSub - 1) / kTilesPerSub < kSubCounters
+                            ? (ntiles + kTilesPerSub - 1) / kTilesPerSub : kSubCounters);
   if (ntiles == 1) {
     complete = true;  // the only tile: no count needed
-  } else if (ntiles <= kSubCounters) {
+  } else if (S == 1) {
     uint32_t* ctr = &a.tiles_done[RING][slot];
     const uint32_t old = __hip_atomic_fetch_add(ctr, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     complete = old + 1 == ntiles;
     if (complete) st_rlx_agent(ctr, 0u);
   } else {
-    const uint32_t sub = tile % kSubCounters;
-    const uint32_t need = ntiles / kSubCounters + (sub < ntiles % kSubCounters ? 1u : 0u);
+    const uint32_t sub = tile % S;
+    const uint32_t need = ntiles / S + (sub < ntiles % S ? 1u : 0u);
     uint32_t* ctr = &a.tiles_done[RING][sub * cap + slot];
     const uint32_t old = __hip_atomic_fetch_add(ctr, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     complete = false;
     if (old + 1 == need) {
       st_rlx_agent(ctr, 0u);
-      wait_mem();
       uint32_t* top = &a.subs_done[RING][slot];
       const uint32_t o2 = __hip_atomic_fetch_add(top, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      complete = o2 + 1 == kSubCounters;
+      complete = o2 + 1 == S;
       if (complete) st_rlx_agent(top, 0u);
     }
   }
   if (complete) {
+    // every tile's stores were acknowledged before its count: publish at once
+    const uint64_t t_done = now_ticks();
+    st_rlx_agent(&a.done_id[RING][slot], c.seq);
     if (a.trace[RING]) {
       TraceRec* tr = &a.trace[RING][slot];
       st_rlx_agent(&tr->seq, c.seq);
-      st_rlx_agent(&tr->t_done, now_ticks());
+      st_rlx_agent(&tr->t_done, t_done);
       st_rlx_agent(&tr->opcode, d(0) & 0xffu);
       st_rlx_agent(&tr->ntiles, ntiles);
     }
-    wait_mem();
-    st_rlx_agent(&a.done_id[RING][slot], c.seq);
   }
 }
 
@@ -250,10 +274,10 @@ __device__ __forceinline__ void run_ticket(const KArgs& a, uint64_t ticket, Cach
 // Maps a runnable ticket to its descriptor (refreshing the cache if needed).
 template <int RING>
 __device__ __forceinline__ void map_ticket(const KArgs& a, uint64_t ticket, uint64_t avail_ops,
-                                           uint64_t copied, Cached& c) {
+                                           uint64_t copied, const AvailLine* line, Cached& c) {
   if (c.seq != 0 && ticket < c.end) return;
   const uint64_t seq = find_seq<RING>(a, ticket, c.seq, avail_ops);
-  fetch_desc<RING>(a, seq, copied, c);
+  fetch_desc<RING>(a, seq, copied, line, c);
 }
 
 // Reads a ring's published-work replica: avail_tiles first, then (after the
@@ -302,7 +326,7 @@ __device__ __forceinline__ void service_lc(const KArgs& a, const AvailLine* line
     if (!bcast(ok)) continue;
     uint64_t tiles, ops, copied;
     read_avail(line, tiles, ops, copied);
-    map_ticket<1>(a, nxt, ops, copied, c);
+    map_ticket<1>(a, nxt, ops, copied, line, c);
     run_ticket<1>(a, nxt, c);
   }
 }
@@ -356,7 +380,7 @@ __device__ __forceinline__ void worker_loop(const KArgs& a, uint32_t w, lds_u32*
       }
     }
     idle = 0;
-    map_ticket<0>(a, ticket, avail_ops, copied, c0);
+    map_ticket<0>(a, ticket, avail_ops, copied, line0, c0);
     run_ticket<0>(a, ticket, c0);
     ticket += a.workers;
   }
@@ -411,7 +435,7 @@ __device__ __forceinline__ bool publish_ends(const KArgs& a, uint64_t tail, uint
 // wave-wide load) is issued before the first store; the stores write
 // through to the device coherence point, and once they are acknowledged the
 // copied frontier moves.  Retired descriptors are never copied.
-constexpr uint32_t kCopyChunk = 128;
+constexpr uint32_t kCopyChunk = 64;
 
 template <int RING>
 __device__ __forceinline__ bool copy_some(const KArgs& a, uint64_t avail, uint64_t retired,

@@ -810,10 +810,13 @@ __device__ __forceinline__ void gemv_tile(D d, uint32_t t, Ready ready = Ready()
   const uint32_t i1 = i0 + tile < M ? i0 + tile : M;
   const uint32_t lane = lane_id();
   if ((K % 8 == 0) && aligned16(px) && aligned16(pw)) {
-    // short rows: 4 rows per step, K <= 1,024 in one step; long rows: one row
-    // per step, 4,096 (bf16 x) or 2,048 (fp32 x) of K per step
+    // short rows: 4 rows per step, K <= 1,024 in one step; bf16 rows up to
+    // 5,120: one row, all of K in one step; longer rows: one row per step,
+    // 4,096 (bf16 x) or 2,048 (fp32 x) of K per step
     if (K <= 1024)
       gemv_rows<4, 2, DT, CPL, CPS>(out, px, pw, K, i0, i1, ready);
+    else if (DT == GPUOS_BF16 && K <= 5120)
+      gemv_rows<1, 10, DT, CPL, CPS>(out, px, pw, K, i0, i1, ready);  // one step
     else
       gemv_rows<1, DT == GPUOS_F32 ? 4 : 8, DT, CPL, CPS>(out, px, pw, K, i0, i1, ready);
     return;
@@ -834,8 +837,8 @@ __device__ __forceinline__ void gemv_tile(D d, uint32_t t, Ready ready = Ready()
 // RMSNORM's in-register path and rounded to bf16, the GEMV accumulates in
 // the same order as gemv_rows<4, 2>, its outputs are rounded to bf16, and the
 // gate is applied to those rounded values.  Up to 4 output rows per step (2
-// gate/up pairs with the epilogue); the first step's weights are requested
-// before `ready()`.
+// gate/up pairs with the epilogue), two steps' weights requested together
+// (the tile's first two before `ready()`).
 template <int CPL, int CPS, class D, class Ready = NoWait>
 __device__ __forceinline__ void norm_gemv_tile(D d, uint32_t t, Ready ready = Ready()) {
   using T = DTr<GPUOS_BF16, CPL, CPS>;
@@ -854,19 +857,16 @@ __device__ __forceinline__ void norm_gemv_tile(D d, uint32_t t, Ready ready = Re
   const rsrc_t out = make_rsrc(pout), act = make_rsrc(pact);
   constexpr int R = 4;
   const uint32_t step = gate ? 2u : 4u;  // units per step
-  float hx[2][8];
-  bool waiting = true;
-  for (uint32_t i = u0; i < u1; i += step) {
-    // the step's rows: i .. i + 3, or gate rows i, i + 1 and up rows F + i, F + i + 1
-    uint32_t row[R];
-    bool ok[R];
+  // a step's rows: i .. i + 3, or gate rows i, i + 1 and up rows F + i, F + i + 1
+  auto rows_of = [&](uint32_t i, uint32_t (&row)[R], bool (&ok)[R]) {
 #pragma unroll
     for (int r = 0; r < R; ++r) {
       const uint32_t k = gate ? (uint32_t)(r & 1) : (uint32_t)r;
       ok[r] = i + k < u1;
       row[r] = (gate && r >= 2 ? F : 0u) + i + k;
     }
-    u32x4 wr[R][2];
+  };
+  auto load_w = [&](const uint32_t (&row)[R], const bool (&ok)[R], u32x4 (&wr)[R][2]) {
 #pragma unroll
     for (int c = 0; c < 2; ++c) {
       const uint32_t ch = lane + 64 * c;
@@ -874,6 +874,45 @@ __device__ __forceinline__ void norm_gemv_tile(D d, uint32_t t, Ready ready = Re
       for (int r = 0; r < R; ++r)
         wr[r][c] = ld128<CPL>(W, ok[r] && ch < chunks ? 2u * (row[r] * K + ch * 8) : 0xFFF00000u);
     }
+  };
+  float hx[2][8];
+  auto finish = [&](uint32_t i, const uint32_t (&row)[R], const bool (&ok)[R], const u32x4 (&wr)[R][2]) {
+    float acc[R] = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+    for (int c = 0; c < 2; ++c) {
+#pragma unroll
+      for (int r = 0; r < R; ++r) {
+        float w[8];
+        unpack_bf16x8(wr[r][c], w);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) acc[r] = __builtin_fmaf(w[e], hx[c][e], acc[r]);
+      }
+    }
+    float v[R];
+#pragma unroll
+    for (int r = 0; r < R; ++r) v[r] = T::round(wave_sum(acc[r]));
+    if (lane == 0) {
+#pragma unroll
+      for (int r = 0; r < R; ++r)
+        if (ok[r] && pout) T::st(out, row[r], v[r]);
+      if (gate) {
+#pragma unroll
+        for (int k = 0; k < 2; ++k)
+          if (ok[k]) T::st(act, i + k, ew_apply<GPUOS_OP_SILU_MUL>(v[k], v[k + 2], 0.0f));
+      }
+    }
+  };
+  bool waiting = true;
+  // two steps at a time: both steps' weights are requested before the first
+  // use (and, for the tile's first pair, before `ready()`)
+  for (uint32_t i = u0; i < u1; i += 2 * step) {
+    uint32_t rowA[R], rowB[R];
+    bool okA[R], okB[R];
+    rows_of(i, rowA, okA);
+    rows_of(i + step, rowB, okB);
+    u32x4 wA[R][2], wB[R][2];
+    load_w(rowA, okA, wA);
+    load_w(rowB, okB, wB);
     if (waiting) {
       compiler_fence();
       ready();
@@ -903,30 +942,8 @@ __device__ __forceinline__ void norm_gemv_tile(D d, uint32_t t, Ready ready = Re
         T::stq(hr, lane + 64, hx[1]);
       }
     }
-    float acc[R] = {0.0f, 0.0f, 0.0f, 0.0f};
-#pragma unroll
-    for (int c = 0; c < 2; ++c) {
-#pragma unroll
-      for (int r = 0; r < R; ++r) {
-        float w[8];
-        unpack_bf16x8(wr[r][c], w);
-#pragma unroll
-        for (int e = 0; e < 8; ++e) acc[r] = __builtin_fmaf(w[e], hx[c][e], acc[r]);
-      }
-    }
-    float v[R];
-#pragma unroll
-    for (int r = 0; r < R; ++r) v[r] = T::round(wave_sum(acc[r]));
-    if (lane == 0) {
-#pragma unroll
-      for (int r = 0; r < R; ++r)
-        if (ok[r] && pout) T::st(out, row[r], v[r]);
-      if (gate) {
-#pragma unroll
-        for (int k = 0; k < 2; ++k)
-          if (ok[k]) T::st(act, i + k, ew_apply<GPUOS_OP_SILU_MUL>(v[k], v[k + 2], 0.0f));
-      }
-    }
+    finish(i, rowA, okA, wA);
+    if (i + step < u1) finish(i + step, rowB, okB, wB);
   }
   if (waiting) ready();
 }
