@@ -113,6 +113,25 @@ def fused_chain_leg(steps, warmup, device=0):
                       "launches_per_step": 1 if fuse else 3,
                       "avg_kernel_us_events": round(gpu_s / launches * 1e6, 2),
                       "hbm_bytes_per_step": fused_bytes if fuse else unfused_bytes}
+    # the same launches captured once per buffer replica as HIP graphs
+    for label, fuse in (("graph_replay", False), ("graph_replay_fused", True)):
+        graphs = [gpuos.Graph(device, a, 3, fuse=fuse) for a in arrs]
+        try:
+            for k in range(warmup):
+                graphs[k % REPLICAS].launch(stream.cuda_stream)
+            stream.synchronize()
+            t0 = time.perf_counter()
+            for k in range(steps):
+                graphs[k % REPLICAS].launch(stream.cuda_stream)
+            stream.synchronize()
+            w = time.perf_counter() - t0
+        finally:
+            for g in graphs:
+                g.destroy()
+        res[label] = {"gb_per_s": round(steps * fused_bytes / w / 1e9, 1),
+                      "ms_per_step": round(w / steps * 1e3, 4),
+                      "launches_per_step": 1 if fuse else 3,
+                      "hbm_bytes_per_step": fused_bytes if fuse else unfused_bytes}
     del reps
     torch.cuda.empty_cache()
     return {
@@ -182,10 +201,16 @@ def queue_leg(reps_n, device=0):
         btimes.append(time.perf_counter() - t0)
     med = sorted(times)[len(times) // 2]
     bmed = sorted(btimes)[len(btimes) // 2]
+    gtimes, gbuild = _time_graph(device, arr, n_ops, False, reps_n)
+    gmed = sorted(gtimes)[len(gtimes) // 2]
     del t
     return {"ops": n_ops, "elems": 4096, "resident_ops_per_s": round(n_ops / med),
             "per_op_launch_ops_per_s": round(n_ops / bmed),
             "speedup_vs_per_op_launch": round(bmed / med, 2),
+            "graph_replay_ops_per_s": round(n_ops / gmed),
+            "speedup_vs_graph_replay": round(gmed / med, 2),
+            "graph_replay_us_per_queue_median": round(gmed * 1e6, 1),
+            "graph_capture_and_instantiate_ms": round(gbuild * 1e3, 2),
             "resident_us_per_queue_median": round(med * 1e6, 1),
             "per_op_launch_us_per_queue_median": round(bmed * 1e6, 1),
             "effective_gb_per_s": round(wl.meta["bytes"] / med / 1e9, 1)}
@@ -212,6 +237,32 @@ def _time_per_op(device, groups_encoded, sizes):
         gpuos.baseline_run(device, arr, k, stream=stream.cuda_stream)
     stream.synchronize()
     return time.perf_counter() - t0
+
+
+def _time_graph(device, arr, n, fuse, reps):
+    """The per-op launches of arr[0, n) captured once as a HIP graph: one
+    untimed replay, then `reps` replays each timed from launch to the end of a
+    stream synchronisation."""
+    import torch
+
+    from persistent_fusion_amd import gpuos
+
+    stream = torch.cuda.current_stream(device)
+    t0 = time.perf_counter()
+    g = gpuos.Graph(device, arr, n, fuse=fuse)
+    build_s = time.perf_counter() - t0
+    try:
+        g.launch(stream.cuda_stream)
+        stream.synchronize()
+        times = []
+        for _ in range(reps):
+            t0 = time.perf_counter()
+            g.launch(stream.cuda_stream)
+            stream.synchronize()
+            times.append(time.perf_counter() - t0)
+    finally:
+        g.destroy()
+    return times, build_s
 
 
 def decode_leg(device=0, reps=3):
@@ -246,6 +297,13 @@ def decode_leg(device=0, reps=3):
         w = _time_per_op(device, enc, sizes)
         if r:
             per_op.append(w)
+    # the whole 64-token run (every group, in order) captured as one graph:
+    # the most favourable case for replay, since no launch is issued per token
+    whole = gpuos.encode_ops(wl.ops, 0, len(wl.ops), addr, {})
+    graph = {}
+    for label, fuse in (("graph_replay", False), ("graph_replay_fused", True)):
+        gt, gb = _time_graph(device, whole, len(wl.ops), fuse, reps)
+        graph[label] = (min(gt), gb)
     tokens = wl.meta["tokens"]
     ops = len(wl.ops)
     byt = (wl.meta["weight_bytes"] + wl.meta["kv_bytes"]) * tokens
@@ -265,6 +323,11 @@ def decode_leg(device=0, reps=3):
             "per_op_launch_tok_per_s": round(tokens / best_b, 1),
             "per_op_launch_ops_per_s": round(ops / best_b),
             "speedup_vs_per_op_launch": round(best_b / best, 2),
+            "graph_replay_tok_per_s": round(tokens / graph["graph_replay"][0], 1),
+            "graph_replay_fused_tok_per_s": round(tokens / graph["graph_replay_fused"][0], 1),
+            "speedup_vs_graph_replay": round(graph["graph_replay"][0] / best, 2),
+            "speedup_vs_graph_replay_fused": round(graph["graph_replay_fused"][0] / best, 2),
+            "graph_capture_and_instantiate_ms": round(graph["graph_replay"][1] * 1e3, 1),
             "bytes_per_token": byt // tokens}
 
 
@@ -522,6 +585,8 @@ def main():
         "median_pass_device_us": (round(fc["per_pass_dev_us"], 2) if fc["per_pass_dev_us"] else None),
         "per_op_launch": fc["baselines"]["per_op_launch"],
         "standalone_fused_kernel": fc["baselines"]["standalone_fused_kernel"],
+        "graph_replay": fc["baselines"]["graph_replay"],
+        "graph_replay_fused": fc["baselines"]["graph_replay_fused"],
         "elementwise_queue_1000x4096": q,
         "plain_copy_kernel": cp,
         **({"extra_configs": extra} if extra else {}),

@@ -370,6 +370,24 @@ const char* gpuos_last_error(void);
 int gpuos_baseline_run(int device, const gpuos_op* ops, uint32_t n, int fuse,
                        void* stream);
 
+/*
+ * Graph-replay comparator ("Launch Overhead and Fusion", section "Graph
+ * capture": a fixed sequence of launches recorded once and replayed with a
+ * single submission).  gpuos_graph_create captures into a HIP graph the
+ * launches gpuos_baseline_run would issue for ops[0, n) (same tile code; with
+ * fuse = 1 the same fusion pass), on device `device`; the ops' pointers,
+ * sizes and scalars are fixed in the graph, the caller's array may be freed
+ * on return.  gpuos_graph_launch replays the whole graph on HIP stream
+ * `stream` (NULL = the legacy default stream) without synchronising; the
+ * buffers must stay allocated while a replay may run.  gpuos_graph_destroy
+ * frees the graph (no replay may be pending).  Errors: EINVAL (bad op, null
+ * argument), EDEVICE (HIP failure).
+ */
+typedef struct gpuos_graph gpuos_graph;
+int gpuos_graph_create(int device, const gpuos_op* ops, uint32_t n, int fuse, gpuos_graph** out);
+int gpuos_graph_launch(gpuos_graph* g, void* stream);
+int gpuos_graph_destroy(gpuos_graph* g);
+
 /* ABI version of the loaded library (GPUOS_ABI_VERSION). */
 int gpuos_abi_version(void);
 

@@ -1763,7 +1763,13 @@ int gpuos_destroy(gpuos_ctx* c, int64_t timeout_ns) {
 // ---------------------------------------------------------------------------
 // per-op launch comparator
 
-int gpuos_baseline_run(int device, const gpuos_op* ops, uint32_t n, int fuse, void* stream) {
+}  // extern "C"
+
+namespace {
+
+// Checks ops[0, n) and returns the compute-unit count of `device`.  Makes no
+// stream call, so it may run before a capture begins.
+int per_op_prepare(int device, const gpuos_op* ops, uint32_t n, uint32_t* cus) {
   if (n && !ops) return fail(GPUOS_EINVAL, "ops is null");
   for (uint32_t i = 0; i < n; ++i) {
     int rc = validate(ops[i], i);
@@ -1777,17 +1783,24 @@ int gpuos_baseline_run(int device, const gpuos_op* ops, uint32_t n, int fuse, vo
     cached_cus = (uint32_t)prop.multiProcessorCount;
     cached_dev = device;
   }
+  *cus = cached_cus;
   HIP_TRY(hipSetDevice(device));
+  return 0;
+}
+
+// Issues the per-op launches of ops[0, n) (already checked by per_op_prepare)
+// on stream s: one gpuos_single launch per op, or per fused group if fuse.
+int issue_per_op(const gpuos_op* ops, uint32_t n, int fuse, uint32_t cus, hipStream_t s) {
   gpuos_ctx tmp;  // host-side planning state only
   tmp.host_only = true;
   gpuos_config_default(&tmp.cfg);
   tmp.cfg.fusion = fuse ? 1 : 2;
-  tmp.workers = cached_cus * 16;
-  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  tmp.workers = cus * 16;
   if (!fuse) {
     DevDesc d;
     for (uint32_t i = 0; i < n; ++i) {
       encode_plain(ops[i], tmp.cfg, tmp.workers, d);
+      mark_streaming(tmp.cfg, d);
       if (ops[i].opcode == GPUOS_OP_NOP) continue;
       HIP_TRY(launch_single(d, nullptr, s));
     }
@@ -1795,19 +1808,81 @@ int gpuos_baseline_run(int device, const gpuos_op* ops, uint32_t n, int fuse, vo
   }
   tmp.staged.reserve(n);
   for (uint32_t i = 0; i < n; ++i) {
-    Staged st;
+    Staged& st = tmp.staged.emplace_back();
     st.op = ops[i];
     st.id = i + 1;
     st.ring = 0;
-    tmp.staged.push_back(std::move(st));
   }
   std::vector<Planned> plan;
+  plan.reserve(n);
   plan_ops(&tmp, 0, tmp.staged.size(), plan);
   for (Planned& pl : plan) {
     if (pl.desc.opcode == GPUOS_OP_NOP) continue;
     HIP_TRY(launch_single(pl.desc, nullptr, s));
   }
   return 0;
+}
+
+}  // namespace
+
+struct gpuos_graph {
+  int device = 0;
+  hipGraph_t graph = nullptr;
+  hipGraphExec_t exec = nullptr;
+};
+
+extern "C" {
+
+int gpuos_baseline_run(int device, const gpuos_op* ops, uint32_t n, int fuse, void* stream) {
+  uint32_t cus = 0;
+  int rc = per_op_prepare(device, ops, n, &cus);
+  if (rc) return rc;
+  return issue_per_op(ops, n, fuse, cus, reinterpret_cast<hipStream_t>(stream));
+}
+
+int gpuos_graph_create(int device, const gpuos_op* ops, uint32_t n, int fuse, gpuos_graph** out) {
+  if (!out) return fail(GPUOS_EINVAL, "out is null");
+  *out = nullptr;
+  uint32_t cus = 0;
+  int rc = per_op_prepare(device, ops, n, &cus);
+  if (rc) return rc;
+  hipStream_t s = nullptr;
+  HIP_TRY(hipStreamCreateWithFlags(&s, hipStreamNonBlocking));
+  auto* g = new gpuos_graph();
+  g->device = device;
+  hipError_t e = hipStreamBeginCapture(s, hipStreamCaptureModeThreadLocal);
+  if (e == hipSuccess) {
+    rc = issue_per_op(ops, n, fuse, cus, s);
+    const hipError_t e2 = hipStreamEndCapture(s, &g->graph);
+    if (!rc && e2 != hipSuccess) e = e2;
+  }
+  if (!rc && e == hipSuccess) e = hipGraphInstantiate(&g->exec, g->graph, nullptr, nullptr, 0);
+  (void)hipStreamDestroy(s);
+  if (rc || e != hipSuccess) {
+    if (!rc) rc = fail(GPUOS_EDEVICE, "graph capture: %s", hipGetErrorString(e));
+    if (g->exec) (void)hipGraphExecDestroy(g->exec);
+    if (g->graph) (void)hipGraphDestroy(g->graph);
+    delete g;
+    return rc;
+  }
+  *out = g;
+  return 0;
+}
+
+int gpuos_graph_launch(gpuos_graph* g, void* stream) {
+  if (!g) return fail(GPUOS_EINVAL, "null graph");
+  HIP_TRY(hipSetDevice(g->device));
+  HIP_TRY(hipGraphLaunch(g->exec, reinterpret_cast<hipStream_t>(stream)));
+  return 0;
+}
+
+int gpuos_graph_destroy(gpuos_graph* g) {
+  if (!g) return fail(GPUOS_EINVAL, "null graph");
+  int rc = 0;
+  if (g->exec && hipGraphExecDestroy(g->exec) != hipSuccess) rc = fail(GPUOS_EDEVICE, "graph exec destroy");
+  if (g->graph && hipGraphDestroy(g->graph) != hipSuccess) rc = fail(GPUOS_EDEVICE, "graph destroy");
+  delete g;
+  return rc;
 }
 
 // ---------------------------------------------------------------------------

@@ -72,6 +72,7 @@ EXPORTS = (
     "gpuos_abi_version", "gpuos_last_error", "gpuos_config_default", "gpuos_create",
     "gpuos_submit", "gpuos_flush", "gpuos_sync", "gpuos_query", "gpuos_get_stats",
     "gpuos_trace_read", "gpuos_stop", "gpuos_destroy", "gpuos_baseline_run",
+    "gpuos_graph_create", "gpuos_graph_launch", "gpuos_graph_destroy",
     "gpuos_debug_read_desc", "gpuos_debug_published", "gpuos_debug_seq_of", "gpuos_debug_retire",
 )
 
@@ -101,6 +102,9 @@ def lib() -> C.CDLL:
         "gpuos_stop": (C.c_int, [P, C.c_int64]),
         "gpuos_destroy": (C.c_int, [P, C.c_int64]),
         "gpuos_baseline_run": (C.c_int, [C.c_int, C.POINTER(GpuosOp), C.c_uint32, C.c_int, P]),
+        "gpuos_graph_create": (C.c_int, [C.c_int, C.POINTER(GpuosOp), C.c_uint32, C.c_int, C.POINTER(P)]),
+        "gpuos_graph_launch": (C.c_int, [P, P]),
+        "gpuos_graph_destroy": (C.c_int, [P]),
         "gpuos_debug_read_desc": (C.c_int, [P, C.c_int, C.c_uint64, P]),
         "gpuos_debug_published": (C.c_uint64, [P, C.c_int]),
         "gpuos_debug_seq_of": (C.c_int, [P, C.c_uint64, C.POINTER(C.c_int), C.POINTER(C.c_uint64)]),
@@ -268,6 +272,36 @@ def baseline_run(device: int, ops, n: Optional[int] = None, fuse: bool = False,
     n = len(ops) if n is None else n
     _check(lib().gpuos_baseline_run(device, ops, n, 1 if fuse else 0, stream or None),
            "gpuos_baseline_run")
+
+
+class Graph:
+    """The per-op launches of a fixed op list, captured once as a HIP graph.
+
+    ``launch`` replays every launch with one submission on `stream`; the
+    buffers the ops name must stay allocated while the graph exists.
+    """
+
+    def __init__(self, device: int, ops, n: Optional[int] = None, fuse: bool = False):
+        n = len(ops) if n is None else n
+        h = C.c_void_p()
+        _check(lib().gpuos_graph_create(device, ops, n, 1 if fuse else 0, C.byref(h)),
+               "gpuos_graph_create")
+        self.handle = h
+
+    def launch(self, stream: int = 0) -> None:
+        _check(lib().gpuos_graph_launch(self.handle, stream or None), "gpuos_graph_launch")
+
+    def destroy(self) -> None:
+        if self.handle:
+            h, self.handle = self.handle, None
+            _check(lib().gpuos_graph_destroy(h), "gpuos_graph_destroy")
+
+    def __enter__(self):
+        return self
+
+    def __exit__(self, *exc):
+        self.destroy()
+        return False
 
 
 def decode_desc(raw: bytes) -> dict:

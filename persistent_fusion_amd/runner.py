@@ -96,3 +96,77 @@ def run_per_op(wl: Workload, device: int = 0, outputs: Optional[Iterable[str]] =
         gpuos.baseline_run(device, arr, g1 - g0, fuse=fuse, stream=stream)
     torch.cuda.current_stream(device).synchronize()
     return download(tensors, wl, outputs or wl.outputs)
+
+
+def _out_elems(op) -> int:
+    """Number of output elements an op writes."""
+    if op.kind == "row_sum":
+        return op.rows
+    if op.kind == "gemv":
+        return op.dims[0]
+    if op.kind == "attn_score":
+        H, _, S = op.dims
+        return H * S
+    if op.kind == "attn_av":
+        H, D, _ = op.dims
+        return H * D
+    return op.n
+
+
+def poisonable(wl: Workload, outputs: Iterable[str]) -> List[str]:
+    """The `outputs` whose first use in op order is a write of the whole buffer
+    (so no op can observe their contents before the workload sets them)."""
+    first = {}
+    for op in wl.ops:
+        reads = {r.buf for r in op.ins}
+        if op.aux is not None:
+            reads.add(op.aux.buf)
+        for b in reads:
+            first.setdefault(b, False)
+        if op.out.buf not in first:
+            whole = op.out.off == 0 and _out_elems(op) >= len(wl.buffers[op.out.buf])
+            first[op.out.buf] = whole
+    return [b for b in outputs if first.get(b, False)]
+
+
+def restore(tensors: Dict[str, "object"], wl: Workload, outputs: Iterable[str]) -> None:
+    """Re-uploads every buffer's initial contents, then fills the outputs that
+    the workload overwrites whole before any read (see `poisonable`) with NaN
+    (all-ones words for bf16 and i32), on torch's current stream."""
+    import torch
+
+    for name, t in tensors.items():
+        arr = wl.buffers[name]
+        host = arr.view(np.int16) if wl.dtypes[name] == "bf16" else arr
+        t.copy_(torch.from_numpy(np.ascontiguousarray(host)))
+    for name in poisonable(wl, outputs):
+        t = tensors[name]
+        t.fill_(float("nan") if wl.dtypes[name] == "f32" else -1)
+
+
+def capture_graph(wl: Workload, tensors, device: int = 0, fuse: bool = False) -> gpuos.Graph:
+    """Captures the workload's per-op launches (all groups, in order) as one graph."""
+    addr = addr_fn(tensors, wl)
+    arr = gpuos.encode_ops(wl.ops, 0, len(wl.ops), addr, {})
+    return gpuos.Graph(device, arr, len(wl.ops), fuse=fuse)
+
+
+def run_graph(wl: Workload, device: int = 0, outputs: Optional[Iterable[str]] = None,
+              fuse: bool = False, replays: int = 3) -> List[Dict[str, np.ndarray]]:
+    """Replays the captured per-op launches `replays` times; before each replay
+    the buffers are restored and the outputs poisoned by ordinary torch work,
+    and after it the device is synchronised.  Returns each replay's outputs."""
+    import torch
+
+    outputs = list(outputs or wl.outputs)
+    tensors = to_device(wl, device)
+    stream = torch.cuda.current_stream(device)
+    res = []
+    with capture_graph(wl, tensors, device, fuse) as g:
+        for _ in range(replays):
+            restore(tensors, wl, outputs)
+            torch.cuda.synchronize(device)
+            g.launch(stream.cuda_stream)
+            torch.cuda.synchronize(device)
+            res.append(download(tensors, wl, outputs))
+    return res

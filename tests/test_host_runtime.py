@@ -389,3 +389,19 @@ def test_norm_gemv_drops_unread_transient_norm_output():
         c.submit(ops)
         c.flush()
         assert desc(c, 1)["ng"]["h"] == 0
+
+
+def test_graph_replay_poisons_only_buffers_written_whole_first():
+    """Between graph replays the tests fill outputs with NaN; only buffers
+    whose first use is a whole write may be poisoned (a KV cache written at
+    one slot and a fed-back hidden state keep their contents)."""
+    from persistent_fusion_amd import runner, workloads
+
+    wl = workloads.gen_decode(seed=7, layers=2, tokens=3, distinct=True)
+    p = set(runner.poisonable(wl, wl.outputs))
+    assert {"K0", "K1", "V0", "V1"}.isdisjoint(p)
+    assert {"qkv.0.0", "scores.1.1", "probs.2.0", "act.0.1", "xb.2.1"} <= p
+    wl = workloads.gen_decode(seed=7, layers=2, tokens=3)
+    assert runner.poisonable(wl, wl.outputs) == []
+    wl = workloads.gen_fused_chain(seed=5, n=1000)
+    assert runner.poisonable(wl, ["y"]) == ["y"]
