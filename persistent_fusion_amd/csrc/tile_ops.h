@@ -146,12 +146,13 @@ constexpr bool ew_binary() {
 }
 
 // Elementwise tiles are interleaved: the op's whole 16-byte vectors form
-// rows of 64 (one per lane), and tile t of T takes rows t, t + T, t + 2T, ...
-// so at any moment the waves of a large op sweep adjacent memory together
-// (DRAM-friendly, like a grid-stride loop), U rows per wave in flight.  The
-// n % V leftover elements belong to the last tile.  A source read
-// cyclically, or a misaligned operand, uses the per-element path with the
-// same interleaving.
+// rows of 64 (one per lane), U adjacent rows form a group, and tile t of T
+// takes groups t, t + T, t + 2T, ...  At any moment the waves of a large op
+// sweep adjacent memory together (like a grid-stride loop), and each wave's
+// U rows in flight are one contiguous U KiB (fp32) block per operand, which
+// keeps fewer DRAM pages open than U rows spread T rows apart.  The n % V
+// leftover elements belong to the last tile.  A source read cyclically, or
+// a misaligned operand, uses the per-element path interleaved by lanes.
 template <int OP, int DT, int CPL, int CPS, class D>
 __device__ __forceinline__ void ew_tile(D d, uint32_t t) {
   using T = DTr<DT, CPL, CPS>;
@@ -170,20 +171,34 @@ __device__ __forceinline__ void ew_tile(D d, uint32_t t) {
     const uint32_t nv = n / V, nrows = (nv + 63) / 64;
     const rsrc_t vo = make_rsrc_n(d.q(18), nv * 16u), va = make_rsrc_n(d.q(20), nv * 16u);
     const rsrc_t vb = make_rsrc_n(BIN ? d.q(22) : 0, nv * 16u);
-    for (uint32_t row = t; row < nrows; row += U * ntiles) {
-      float x[U][V], y[U][V];
+    const uint32_t ngroups = (nrows + U - 1) / U;
+    float x[U][V], y[U][V];
+    auto load = [&](uint32_t g) {
 #pragma unroll
       for (int u = 0; u < U; ++u) {
-        const uint32_t q = (row + u * ntiles) * 64 + lane;
+        const uint32_t q = (g * U + u) * 64 + lane;
         T::ldq(va, q, x[u]);
         if constexpr (BIN) T::ldq(vb, q, y[u]);
       }
+    };
+    // software pipeline: group g + T is requested before group g is computed
+    if (t < ngroups) load(t);
+    for (uint32_t g = t; g < ngroups; g += ntiles) {
+      float cx[U][V], cy[U][V];
+#pragma unroll
+      for (int u = 0; u < U; ++u)
+#pragma unroll
+        for (int e = 0; e < V; ++e) {
+          cx[u][e] = x[u][e];
+          cy[u][e] = BIN ? y[u][e] : 0.0f;
+        }
+      if (g + ntiles < ngroups) load(g + ntiles);
 #pragma unroll
       for (int u = 0; u < U; ++u) {
-        const uint32_t q = (row + u * ntiles) * 64 + lane;
+        const uint32_t q = (g * U + u) * 64 + lane;
         float r[V];
 #pragma unroll
-        for (int e = 0; e < V; ++e) r[e] = ew_apply<OP>(x[u][e], BIN ? y[u][e] : 0.0f, alpha);
+        for (int e = 0; e < V; ++e) r[e] = ew_apply<OP>(cx[u][e], cy[u][e], alpha);
         T::stq(vo, q, r);
       }
     }
@@ -222,12 +237,20 @@ __device__ __forceinline__ void copy_tile(D d, uint32_t t) {
   if (ca == 0 && aligned16(d.q(18)) && aligned16(d.q(20))) {
     const uint32_t nv = n / V, nrows = (nv + 63) / 64;
     const rsrc_t vo = make_rsrc_n(d.q(18), nv * 16u), va = make_rsrc_n(d.q(20), nv * 16u);
-    for (uint32_t row = t; row < nrows; row += U * ntiles) {
-      u32x4 v[U];
+    const uint32_t ngroups = (nrows + U - 1) / U;
+    u32x4 v[U];
+    auto load = [&](uint32_t g) {
 #pragma unroll
-      for (int u = 0; u < U; ++u) v[u] = ld128<CPL>(va, vec_off((row + u * ntiles) * 64 + lane));
+      for (int u = 0; u < U; ++u) v[u] = ld128<CPL>(va, vec_off((g * U + u) * 64 + lane));
+    };
+    if (t < ngroups) load(t);
+    for (uint32_t g = t; g < ngroups; g += ntiles) {
+      u32x4 c[U];
 #pragma unroll
-      for (int u = 0; u < U; ++u) st128<CPS>(vo, vec_off((row + u * ntiles) * 64 + lane), v[u]);
+      for (int u = 0; u < U; ++u) c[u] = v[u];
+      if (g + ntiles < ngroups) load(g + ntiles);
+#pragma unroll
+      for (int u = 0; u < U; ++u) st128<CPS>(vo, vec_off((g * U + u) * 64 + lane), c[u]);
     }
     if (t + 1 == ntiles)
       for (uint32_t i = nv * V + lane; i < n; i += 64) copy_elem<ES, CPL, CPS>(out, i, a, i);
@@ -347,32 +370,57 @@ __device__ __forceinline__ void fused_tile(D d, uint32_t t) {
   const uint32_t lane = lane_id();
   uint32_t scalar_from = t * 64, scalar_step = 64 * ntiles;  // per-element path
   if (fast) {
-    // whole vectors only; unused inputs have empty resources and rows past
-    // the end fall outside them, so every load and store is unconditional
+    // whole vectors only; rows past the end fall outside the resources, so
+    // no load or store needs a bounds test; unused (null) inputs are not read
     const uint32_t nv = n / V, nrows = (nv + 63) / 64;
     const uint32_t vb = nv * 16u;
     const rsrc_t r0 = make_rsrc_n(p0, vb), r1 = make_rsrc_n(p1, vb), r2 = make_rsrc_n(p2, vb),
                  r3 = make_rsrc_n(p3, vb);
-    for (uint32_t row = t; row < nrows; row += U * ntiles) {
-      float acc[U][V], v1[U][V], v2[U][V], v3[U][V];
+    const bool has1 = p1 != 0, has2 = p2 != 0, has3 = p3 != 0;
+    const uint32_t ngroups = (nrows + U - 1) / U;
+    float acc[U][V], v1[U][V], v2[U][V], v3[U][V];
+#pragma unroll
+    for (int u = 0; u < U; ++u)
+#pragma unroll
+      for (int e = 0; e < V; ++e) {
+        v1[u][e] = 0.0f;
+        v2[u][e] = 0.0f;
+        v3[u][e] = 0.0f;
+      }
+    auto load = [&](uint32_t g) {
 #pragma unroll
       for (int u = 0; u < U; ++u) {
-        const uint32_t q = (row + u * ntiles) * 64 + lane;
+        const uint32_t q = (g * U + u) * 64 + lane;
         T::ldq(r0, q, acc[u]);
-        T::ldq(r1, q, v1[u]);
-        T::ldq(r2, q, v2[u]);
-        T::ldq(r3, q, v3[u]);
+        if (has1) T::ldq(r1, q, v1[u]);
+        if (has2) T::ldq(r2, q, v2[u]);
+        if (has3) T::ldq(r3, q, v3[u]);
       }
+    };
+    // software pipeline: group g + T is requested before group g is computed
+    if (t < ngroups) load(t);
+    for (uint32_t g = t; g < ngroups; g += ntiles) {
+      float a[U][V], b1[U][V], b2[U][V], b3[U][V];
+#pragma unroll
+      for (int u = 0; u < U; ++u)
+#pragma unroll
+        for (int e = 0; e < V; ++e) {
+          a[u][e] = acc[u][e];
+          b1[u][e] = v1[u][e];
+          b2[u][e] = v2[u][e];
+          b3[u][e] = v3[u][e];
+        }
+      if (g + ntiles < ngroups) load(g + ntiles);
 #pragma unroll
       for (int s = 0; s < kMaxSteps; ++s) {
         if ((uint32_t)s < P.nsteps) {
           uint32_t sfl = 0;
 #pragma unroll
-          for (int u = 0; u < U; ++u) sfl = fused_apply<V>(P, s, acc[u], v1[u], v2[u], v3[u]);
+          for (int u = 0; u < U; ++u) sfl = fused_apply<V>(P, s, a[u], b1[u], b2[u], b3[u]);
           if (sfl & FSF_STORE) {
             const rsrc_t o = make_rsrc_n(P.out[s], vb);
 #pragma unroll
-            for (int u = 0; u < U; ++u) T::stq(o, (row + u * ntiles) * 64 + lane, acc[u]);
+            for (int u = 0; u < U; ++u) T::stq(o, (g * U + u) * 64 + lane, a[u]);
           }
         }
       }
