@@ -73,7 +73,10 @@ __device__ __forceinline__ void report_error(const KArgs& a, uint32_t ring, uint
 // Finds the descriptor owning `ticket` among sequences (lo, hi]:
 // ends(s) = dends[(s - 1) mod 2C] is the first ticket after descriptor s
 // (C = ring slots).  A 64-way search: every lane probes one sequence, a ballot
-// picks the first probe past the ticket; each round shrinks the range 64-fold.
+// picks the first probe past the ticket, and the range shrinks to the gap
+// before it.  On a wide first round, lanes 0-31 probe the 32 sequences right
+// after lo (where a wave's next ticket lies when the ops are large, so one
+// round finds it exactly) and lanes 32-63 split the rest of the range.
 //
 // Probes stay inside (hi - C, hi], and no probed entry can be overwritten
 // while the search runs: the ticket's own descriptor X (>= retired + 1, with
@@ -84,19 +87,32 @@ __device__ __forceinline__ uint64_t find_seq(const KArgs& a, uint64_t ticket, ui
   const uint32_t lane = lane_id();
   const uint32_t mask = a.cap_mask;
   if (hi > (uint64_t)mask + 1 && lo < hi - mask - 1) lo = hi - mask - 1;
+  bool first = true;
   while (hi - lo > 1) {
     const uint64_t span = hi - lo;
-    const uint64_t step = (span + 63) / 64;
-    uint64_t s = lo + step * (lane + 1);
-    if (s > hi) s = hi;
+    uint64_t s;
+    if (first && span > 64) {
+      const uint64_t step = (span - 32 + 31) / 32;
+      s = lane < 32 ? lo + 1 + lane : lo + 32 + step * (lane - 31);
+    } else {
+      const uint64_t step = (span + 63) / 64;
+      s = lo + step * (lane + 1);
+    }
+    if (s > hi) s = hi;  // probes are non-decreasing and the last one is hi
     const uint64_t e = ld_rlx_agent(&a.dends[RING][slot_of(s, a.ends_mask)]);
     const uint64_t past = ballot(e > ticket);
-    // the probe at hi is always past the ticket, so `past` is non-empty
+    // the probe at hi is always past the ticket, so `past` is non-empty; the
+    // probe before the first past one is not past, hence strictly smaller
     const uint32_t f = (uint32_t)__builtin_ctzll(past);
-    const uint64_t nhi = lo + step * (f + 1) > hi ? hi : lo + step * (f + 1);
-    const uint64_t nlo = f == 0 ? lo : lo + step * f;
+    const uint64_t nhi = ((uint64_t)(uint32_t)__builtin_amdgcn_readlane((int)(s >> 32), f) << 32) |
+                         (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)s, f);
+    uint64_t nlo = lo;
+    if (f > 0)
+      nlo = ((uint64_t)(uint32_t)__builtin_amdgcn_readlane((int)(s >> 32), f - 1) << 32) |
+            (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)s, f - 1);
     lo = nlo;
     hi = nhi;
+    first = false;
   }
   return hi;
 }
@@ -113,6 +129,16 @@ constexpr uint64_t kHostReadMaxTiles = 4;
 // in the second) again from the device coherence point.  A newer small one
 // comes straight from the pinned host ring, whose slot does not change before
 // the descriptor retires; a newer large one is waited for.
+// Makes descriptor `seq` (lane i holds dword i in dw) the wave's cached one.
+__device__ __forceinline__ void install_desc(Cached& c, uint64_t seq, uint32_t dw) {
+  const VDesc e{dw};
+  c.slot[lane_id()] = dw;
+  c.seq = seq;
+  c.start = e.q(60);
+  c.end = c.start + e(6);
+  c.deps_ok = 0;
+}
+
 template <int RING>
 __device__ __forceinline__ void fetch_desc(const KArgs& a, uint64_t seq, uint64_t copied,
                                            const AvailLine* line, Cached& c) {
@@ -149,12 +175,7 @@ __device__ __forceinline__ void fetch_desc(const KArgs& a, uint64_t seq, uint64_
     const VDesc f{dw};
     if (f.q(4) != seq || f(63) != ((uint32_t)seq ^ kDescMagic)) report_error(a, RING, seq, DERR_DESC_CHECK);
   }
-  const VDesc e{dw};
-  c.slot[lane_id()] = dw;
-  c.seq = seq;
-  c.start = e.q(60);
-  c.end = c.start + e(6);
-  c.deps_ok = 0;
+  install_desc(c, seq, dw);
 }
 
 // Waits until every dependency of the cached descriptor has completed.
@@ -276,7 +297,25 @@ template <int RING>
 __device__ __forceinline__ void map_ticket(const KArgs& a, uint64_t ticket, uint64_t avail_ops,
                                            uint64_t copied, const AvailLine* line, Cached& c) {
   if (c.seq != 0 && ticket < c.end) return;
+  // When ops are large the next descriptor usually owns the ticket: its copy
+  // in the device ring is requested before the search, so both share one
+  // round trip.  It is used only if the search agrees and it is the current
+  // occupant of its slot (seq field and check word).
+  const uint64_t nx = c.seq + 1;
+  const bool spec = c.seq != 0 && nx <= copied && nx <= avail_ops;
+  uint32_t sdw = 0;
+  if (spec) {
+    const rsrc_t r = make_rsrc(reinterpret_cast<uint64_t>(&a.ddesc[RING][slot_of(nx, a.cap_mask)]));
+    sdw = ld32<CP_DEFAULT>(r, 4u * lane_id());
+  }
   const uint64_t seq = find_seq<RING>(a, ticket, c.seq, avail_ops);
+  if (spec && seq == nx) {
+    const VDesc d{sdw};
+    if (d.q(4) == nx && d(63) == ((uint32_t)nx ^ kDescMagic)) {
+      install_desc(c, nx, sdw);
+      return;
+    }
+  }
   fetch_desc<RING>(a, seq, copied, line, c);
 }
 
