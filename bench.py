@@ -189,6 +189,12 @@ def queue_leg(reps_n, device=0):
         ctx.sync(0, 60.0)
         times.append(time.perf_counter() - t0)
     ctx.destroy()
+    # one more queue with the in-kernel trace on (not timed), for the gaps
+    ctx = gpuos.Context(device, trace=1)
+    ctx.submit_noids(arr, n_ops)
+    ctx.sync(0, 60.0)
+    gaps = handoff_gaps(ctx, ctx.trace())
+    ctx.destroy()
     torch.cuda.synchronize()
     stream = torch.cuda.current_stream(device)
     gpuos.baseline_run(device, arr, n_ops, stream=stream.cuda_stream)
@@ -211,6 +217,8 @@ def queue_leg(reps_n, device=0):
             "speedup_vs_graph_replay": round(gmed / med, 2),
             "graph_replay_us_per_queue_median": round(gmed * 1e6, 1),
             "graph_capture_and_instantiate_ms": round(gbuild * 1e3, 2),
+            "per_op_launch_us_per_op": round(bmed / n_ops * 1e6, 2),
+            "resident_trace": gaps,
             "resident_us_per_queue_median": round(med * 1e6, 1),
             "per_op_launch_us_per_queue_median": round(bmed * 1e6, 1),
             "effective_gb_per_s": round(wl.meta["bytes"] / med / 1e9, 1)}
@@ -265,6 +273,29 @@ def _time_graph(device, arr, n, fuse, reps):
     return times, build_s
 
 
+def handoff_gaps(ctx, recs):
+    """Idle gaps between dependent ops inside the resident kernel, from its
+    trace (100 MHz timestamps): for every descriptor whose dependencies are all
+    in `recs`, the time from the last dependency's completion to the claim of
+    the descriptor's first tile; and each descriptor's own claim-to-done time."""
+    from persistent_fusion_amd import gpuos
+
+    by_seq = {r["seq"]: r for r in recs if r["ring"] == 0}
+    gaps, busy = [], []
+    for seq, r in by_seq.items():
+        busy.append((r["t_done"] - r["t_claim"]) * 1e-2)
+        deps = [x for x in gpuos.decode_desc(ctx.read_desc(0, seq))["deps"] if x]
+        if not deps or any(x not in by_seq for x in deps):
+            continue
+        gaps.append((r["t_claim"] - max(by_seq[x]["t_done"] for x in deps)) * 1e-2)
+    gaps.sort()
+    busy.sort()
+    pick = lambda v, q: round(v[min(len(v) - 1, int(q * len(v)))], 2) if v else None
+    return {"descriptors": len(by_seq), "with_deps": len(gaps),
+            "handoff_us_p50": pick(gaps, 0.5), "handoff_us_p90": pick(gaps, 0.9),
+            "busy_us_p50": pick(busy, 0.5), "busy_us_p90": pick(busy, 0.9)}
+
+
 def decode_leg(device=0, reps=3):
     """Batch-1 decode: 24 layers, 64 tokens, 360 ops per token, one flush per
     token, one sync at the end."""
@@ -290,6 +321,8 @@ def decode_leg(device=0, reps=3):
             times.append(time.perf_counter() - t0)
     tr = ctx.trace(1 << 16)
     descs_per_run = ctx.stats()["descs_published"] // (reps + 1)
+    last_run = sorted(tr, key=lambda x: x["seq"])[-descs_per_run:]
+    gaps = handoff_gaps(ctx, last_run)
     ctx.destroy()
     torch.cuda.synchronize()
     per_op = []
@@ -328,6 +361,8 @@ def decode_leg(device=0, reps=3):
             "speedup_vs_graph_replay": round(graph["graph_replay"][0] / best, 2),
             "speedup_vs_graph_replay_fused": round(graph["graph_replay_fused"][0] / best, 2),
             "graph_capture_and_instantiate_ms": round(graph["graph_replay"][1] * 1e3, 1),
+            "per_op_launch_us_per_op": round(best_b / ops * 1e6, 2),
+            "resident_trace_last_run": gaps,
             "bytes_per_token": byt // tokens}
 
 

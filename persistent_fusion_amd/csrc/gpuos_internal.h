@@ -30,7 +30,14 @@ enum : uint8_t {
                       // normalises the input row itself (tile 0 also stores
                       // it); with the SiLU gate a tile computes gate row i
                       // and up row F + i together
+  OP_GEMV_ADD = 34,   // GEMV -> ADD of a residual: each output row, rounded
+                      // as the GEMV stores it, is added to the residual
+                      // element and stored to the ADD's output
+  OP_SOFTMAX_AV = 35, // ROW_SOFTMAX -> ATTN_AV: each AV tile computes the
+                      // softmax of its head's score row itself
 };
+// Per-wave LDS scratch of the tile bodies, in floats.
+constexpr uint32_t kWaveScratch = 512;
 
 // Completion counting: a descriptor of up to 8 tiles counts its tiles in one
 // counter.  A larger one spreads them over S = min(64, ceil(tiles / 8))
@@ -117,6 +124,18 @@ struct alignas(16) DevDesc {
       uint8_t _pad[80];
     } ng;
     struct {
+      uint64_t out;         // 18-19: GEMV output [M] (0 = not stored)
+      uint64_t x;           // 20-21: GEMV input [K]
+      uint64_t res;         // 22-23: residual [M]
+      uint64_t W;           // 24-25: weights [M x K] bf16
+      uint32_t res_first;   // 26: 1 = the ADD reads the residual as in[0]
+      uint32_t _u[3];       // 27-29
+      uint32_t M;           // 30
+      uint32_t K;           // 31
+      uint64_t sum;         // 32-33: ADD output [M]
+      uint8_t _pad[80];
+    } ga;
+    struct {
       uint64_t in[4];       // 18-25: in[0] = chain input, in[1..3] operands
       uint64_t out[8];      // 26-41: output pointer of step s (FSF_STORE)
       uint8_t step_op[8];   // 42-43
@@ -139,6 +158,9 @@ static_assert(offsetof(DevDesc, p.alpha) == 28 * 4, "alpha at dword 28");
 static_assert(offsetof(DevDesc, p.aux) == 30 * 4, "aux at dword 30");
 static_assert(offsetof(DevDesc, f.out) == 26 * 4, "fused out at dword 26");
 static_assert(offsetof(DevDesc, ng.M) == 30 * 4, "norm-GEMV M at dword 30");
+static_assert(offsetof(DevDesc, ga.W) == 24 * 4 && offsetof(DevDesc, ga.M) == 30 * 4 &&
+                  offsetof(DevDesc, ga.sum) == 32 * 4,
+              "GEMV-ADD keeps the GEMV fields where a GEMV descriptor has them");
 static_assert(offsetof(DevDesc, f.step_op) == 42 * 4, "step_op at dword 42");
 static_assert(offsetof(DevDesc, f.step_fl) == 44 * 4, "step_fl at dword 44");
 static_assert(offsetof(DevDesc, f.fscal) == 46 * 4, "fscal at dword 46");

@@ -53,6 +53,7 @@ struct Cached {
   uint64_t end;    // one past the last ticket
   lds_u32* slot;   // 64 dwords
   uint32_t deps_ok;
+  lds_f32* scr;    // the wave's tile scratch (kWaveScratch floats)
   __device__ __forceinline__ SDesc desc() const { return SDesc{slot}; }
 };
 
@@ -264,7 +265,8 @@ __device__ __forceinline__ void run_ticket(const KArgs& a, uint64_t ticket, Cach
   if (!c.deps_ok) {
     const uint32_t w0 = d(0);
     const uint32_t op = w0 & 0xffu;
-    if ((op == GPUOS_OP_GEMV || op == OP_NORM_GEMV) && ((w0 >> 16) & DF_AUX_READY)) {
+    if ((op == GPUOS_OP_GEMV || op == OP_NORM_GEMV || op == OP_GEMV_ADD) &&
+        ((w0 >> 16) & DF_AUX_READY)) {
       // the weights are final: start streaming them, then wait for x
       auto ready = [&]() {
         wait_deps<RING>(a, c);
@@ -278,6 +280,10 @@ __device__ __forceinline__ void run_ticket(const KArgs& a, uint64_t ticket, Cach
         gemv_tile<GPUOS_BF16, kResidentLoadCP, kResidentStoreCP>(d, tile, ready);
       else if (op == GPUOS_OP_GEMV)
         gemv_tile<GPUOS_F32, kResidentLoadCP, kResidentStoreCP>(d, tile, ready);
+      else if (op == OP_GEMV_ADD && bf)
+        gemv_tile<GPUOS_BF16, kResidentLoadCP, kResidentStoreCP>(d, tile, ready, true);
+      else if (op == OP_GEMV_ADD)
+        gemv_tile<GPUOS_F32, kResidentLoadCP, kResidentStoreCP>(d, tile, ready, true);
       else
         report_error(a, RING, c.seq, DERR_BAD_OPCODE);
       finish_tile<RING>(a, c, tile);
@@ -287,7 +293,7 @@ __device__ __forceinline__ void run_ticket(const KArgs& a, uint64_t ticket, Cach
     c.deps_ok = 1;
   }
   claimed();
-  const uint32_t err = exec_tile<kResidentLoadCP, kResidentStoreCP>(d, tile);
+  const uint32_t err = exec_tile<kResidentLoadCP, kResidentStoreCP>(d, tile, c.scr);
   if (err) report_error(a, RING, c.seq, err);
   finish_tile<RING>(a, c, tile);
 }
@@ -372,10 +378,10 @@ __device__ __forceinline__ void service_lc(const KArgs& a, const AvailLine* line
 
 // A reserved wave: serves the latency-critical ring until the launch ends
 // (at which point every published descriptor has retired).
-__device__ __forceinline__ void lc_loop(const KArgs& a, uint32_t w, lds_u32* slot1) {
+__device__ __forceinline__ void lc_loop(const KArgs& a, uint32_t w, lds_u32* slot1, lds_f32* scr) {
   const AvailLine* line0 = &a.dctl->avail[0][w % kReplicas];
   const AvailLine* line1 = &a.dctl->avail[1][w % kReplicas];
-  Cached c1{0, 0, 0, slot1, 0};
+  Cached c1{0, 0, 0, slot1, 0, scr};
   uint64_t seen = 0;
   for (;;) {
     service_lc(a, line1, c1, seen);
@@ -387,9 +393,9 @@ __device__ __forceinline__ void lc_loop(const KArgs& a, uint32_t w, lds_u32* slo
 }
 
 // A best-effort wave: runs its round-robin share of the ring-0 tickets.
-__device__ __forceinline__ void worker_loop(const KArgs& a, uint32_t w, lds_u32* slot0) {
+__device__ __forceinline__ void worker_loop(const KArgs& a, uint32_t w, lds_u32* slot0, lds_f32* scr) {
   const AvailLine* line0 = &a.dctl->avail[0][w % kReplicas];
-  Cached c0{0, 0, 0, slot0, 0};
+  Cached c0{0, 0, 0, slot0, 0, scr};
   uint64_t avail = 0, avail_ops = 0, copied = 0;
   uint32_t idle = 0;
   // tickets are dealt round-robin: this wave owns those = w (mod workers),
@@ -399,22 +405,34 @@ __device__ __forceinline__ void worker_loop(const KArgs& a, uint32_t w, lds_u32*
   if (ticket < base) ticket += a.workers;
   for (;;) {
     if (ticket >= avail) {
-      read_avail(line0, avail, avail_ops, copied);
+      if (idle > 0) {
+        // idle: watch avail_tiles alone until it moves past this ticket
+        uint64_t t = 0;
+        if (lane_id() == 0) t = ld_rlx_agent(&line0->avail_tiles);
+        if (bcast64(t) > ticket) read_avail(line0, avail, avail_ops, copied);
+      } else {
+        read_avail(line0, avail, avail_ops, copied);
+      }
       if (ticket >= avail) {
-        uint64_t se = 0, stop = 0;
-        if (lane_id() == 0) {
-          se = ld_rlx_agent(&line0->stop_epoch);
-          wait_mem();
-          stop = ld_rlx_agent(&line0->stop_ticket);
+        if (idle >= 32 || (idle & 7) == 7) {
+          uint64_t se = 0, stop = 0;
+          if (lane_id() == 0) {
+            se = ld_rlx_agent(&line0->stop_epoch);
+            wait_mem();
+            stop = ld_rlx_agent(&line0->stop_ticket);
+          }
+          if (bcast64(se) == a.epoch && ticket >= bcast64(stop)) return;
         }
-        if (bcast64(se) == a.epoch && ticket >= bcast64(stop)) return;
-        // nothing published for this ticket yet: back off
+        // nothing published for this ticket yet: back off, further the
+        // longer the queue stays empty (about 0.03, 0.6, then 3.5 us)
         if (idle < 32) {
-          ++idle;
           __builtin_amdgcn_s_sleep(2);
-        } else {
+        } else if (idle < 4096) {
           __builtin_amdgcn_s_sleep(20);
+        } else {
+          __builtin_amdgcn_s_sleep(127);
         }
+        if (idle < 4096) ++idle;
         continue;
       }
     }
@@ -619,8 +637,9 @@ __device__ __forceinline__ void doorbell_loop(const KArgs& a) {
 }
 
 __global__ __launch_bounds__(256) void gpuos_resident(KArgs a) {
-  // one descriptor slot per wave and ring
+  // one descriptor slot per wave and ring, and each wave's tile scratch
   __shared__ uint32_t sdesc[4][2][64];
+  __shared__ float sscr[4][kWaveScratch];
   // Waves are numbered across workgroups first (wave j of workgroup b is
   // j * blocks + b), so consecutive tickets, dealt round-robin, land on
   // different CUs and XCDs (workgroups are dispatched round-robin over the
@@ -631,9 +650,9 @@ __global__ __launch_bounds__(256) void gpuos_resident(KArgs a) {
   if (num == 0)
     doorbell_loop(a);
   else if (num - 1 < a.lc_waves)
-    lc_loop(a, num - 1, (lds_u32*)&sdesc[wib][1][0]);
+    lc_loop(a, num - 1, (lds_u32*)&sdesc[wib][1][0], (lds_f32*)&sscr[wib][0]);
   else
-    worker_loop(a, num - 1 - a.lc_waves, (lds_u32*)&sdesc[wib][0][0]);
+    worker_loop(a, num - 1 - a.lc_waves, (lds_u32*)&sdesc[wib][0][0], (lds_f32*)&sscr[wib][0]);
 }
 
 // ---------------------------------------------------------------------------
@@ -645,12 +664,14 @@ __global__ __launch_bounds__(256) void gpuos_single(DevDesc d, uint32_t* err) {
   const uint32_t waves = gridDim.x * blockDim.x / 64;
   // the descriptor goes to this wave's LDS slot, as in the resident kernel
   __shared__ uint32_t sdesc[4][64];
+  __shared__ float sscr[4][kWaveScratch];
   lds_u32* slot = (lds_u32*)&sdesc[threadIdx.x / 64][0];
+  lds_f32* scr = (lds_f32*)&sscr[threadIdx.x / 64][0];
   slot[lane_id()] = reinterpret_cast<const uint32_t*>(&d)[lane_id()];
   const SDesc v{slot};
   const uint32_t ntiles = v(6);
   for (uint32_t t = wave; t < ntiles; t += waves) {
-    const uint32_t e = exec_tile<CP_DEFAULT, CP_DEFAULT>(v, t);
+    const uint32_t e = exec_tile<CP_DEFAULT, CP_DEFAULT>(v, t, scr);
     if (e && lane_id() == 0 && err) *err = e;
   }
 }

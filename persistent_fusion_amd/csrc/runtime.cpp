@@ -668,7 +668,8 @@ void set_tiling(const gpuos_config& cfg, uint32_t workers, DevDesc& d) {
       d.ntiles = ceil_div(units, r);
       break;
     }
-    case GPUOS_OP_GEMV: {
+    case GPUOS_OP_GEMV:
+    case OP_GEMV_ADD: {
       const uint32_t M = (uint32_t)d.p.aux[0];
       uint32_t r = ceil_div(M, std::max<uint32_t>(1, workers));
       r = std::min<uint32_t>(std::max<uint32_t>(r, 1), 16);
@@ -684,6 +685,10 @@ void set_tiling(const gpuos_config& cfg, uint32_t workers, DevDesc& d) {
       d.ntiles = ceil_div(S, r);
       break;
     }
+    case OP_SOFTMAX_AV:  // one 8-column chunk per tile
+      d.tile = 1;
+      d.ntiles = (uint32_t)d.p.aux[0] * (uint32_t)d.p.aux[1] / 8;
+      break;
     case GPUOS_OP_ATTN_AV: {
       const uint32_t H = (uint32_t)d.p.aux[0], D = (uint32_t)d.p.aux[1];
       if (D % 8 == 0) {
@@ -935,6 +940,105 @@ uint32_t try_norm_gemv(gpuos_ctx* c, size_t i, size_t end, DevDesc& d) {
   return count;
 }
 
+// GEMV -> ADD of that GEMV's output (read at the same index) and a residual,
+// same dtype, n == M: one descriptor whose tiles finish each output row with
+// the add.  The ADD may write the residual in place (each element is read
+// and written by the wave that owns its row) but its output may not overlap
+// any other operand, and the GEMV output may not overlap x, W or the
+// residual.  Returns the number of user ops fused (0 = none).
+uint32_t try_gemv_add(gpuos_ctx* c, size_t i, size_t end, DevDesc& d) {
+  if (i + 1 >= end) return 0;
+  const Staged& sa = c->staged[i];
+  const Staged& sb = c->staged[i + 1];
+  const gpuos_op& A = sa.op;
+  const gpuos_op& B = sb.op;
+  if (A.opcode != GPUOS_OP_GEMV || B.opcode != GPUOS_OP_ADD || sa.ring != sb.ring) return 0;
+  if (A.dtype != B.dtype || (A.dtype != GPUOS_F32 && A.dtype != GPUOS_BF16)) return 0;
+  const uint32_t M = (uint32_t)A.aux[0], K = (uint32_t)A.aux[1];
+  if (B.n != M) return 0;
+  const uint64_t y = (uint64_t)A.out;
+  bool res_first;
+  if ((uint64_t)B.in[1] == y && (uint64_t)B.in[0] != y)
+    res_first = true;
+  else if ((uint64_t)B.in[0] == y && (uint64_t)B.in[1] != y)
+    res_first = false;
+  else
+    return 0;
+  for (int q = 0; q < 2; ++q)
+    if (B.src_len[q] && B.src_len[q] < M) return 0;  // cyclic reads stay unfused
+  const uint64_t es = elem_size(A.dtype);
+  const uint64_t x = (uint64_t)A.in[0], W = (uint64_t)A.in[2];
+  const uint64_t r = (uint64_t)(res_first ? B.in[0] : B.in[1]), z = (uint64_t)B.out;
+  const Range rx{x, x + es * K}, rW{W, W + 2ull * M * K}, ry{y, y + es * M};
+  const Range rr{r, r + es * M}, rz{z, z + es * M};
+  for (const Range& in : {rx, rW, rr})
+    if (overlaps(ry, in)) return 0;
+  for (const Range& in : {rx, rW, ry})
+    if (overlaps(rz, in)) return 0;
+  if (overlaps(rz, rr) && z != r) return 0;
+  memset(&d, 0, sizeof d);
+  d.opcode = OP_GEMV_ADD;
+  d.dtype = A.dtype;
+  d.flags = (uint8_t)((A.flags & DF_AUX_READY) | ((A.flags | B.flags) & GPUOS_FLAG_NONTEMPORAL));
+  d.n = M;
+  // the GEMV output is stored unless transient and unread by later ops
+  const bool keep_y = !(A.flags & GPUOS_FLAG_TRANSIENT) || read_later(c, i + 2, ry);
+  d.ga.out = keep_y ? y : 0;
+  d.ga.x = x;
+  d.ga.res = r;
+  d.ga.W = W;
+  d.ga.res_first = res_first ? 1u : 0u;
+  d.ga.M = M;
+  d.ga.K = K;
+  d.ga.sum = z;
+  d.user_ops = 2;
+  set_tiling(c->cfg, c->workers, d);
+  return 2;
+}
+
+// ROW_SOFTMAX over fp32 score rows -> ATTN_AV reading those probabilities:
+// one descriptor whose AV tiles each compute their head's softmax row (rows
+// of at most 512 elements, a multiple of 4; head size a multiple of 8;
+// scores, probabilities and V 16-byte aligned; no output overlapping an
+// input).  The probabilities are stored unless transient and unread later.
+uint32_t try_softmax_av(gpuos_ctx* c, size_t i, size_t end, DevDesc& d) {
+  if (i + 1 >= end) return 0;
+  const Staged& sa = c->staged[i];
+  const Staged& sb = c->staged[i + 1];
+  const gpuos_op& A = sa.op;
+  const gpuos_op& B = sb.op;
+  if (A.opcode != GPUOS_OP_ROW_SOFTMAX || B.opcode != GPUOS_OP_ATTN_AV || sa.ring != sb.ring) return 0;
+  if (A.dtype != GPUOS_F32 || (B.dtype != GPUOS_F32 && B.dtype != GPUOS_BF16)) return 0;
+  const uint32_t H = (uint32_t)B.aux[0], Dh = (uint32_t)B.aux[1], S = (uint32_t)B.aux[2];
+  if (A.rows != H || A.row_len != S || S % 4 || S > 4 * 128 || Dh % 8) return 0;
+  if (A.src_len[0] && A.src_len[0] < A.n) return 0;
+  const uint64_t x = (uint64_t)A.in[0], p = (uint64_t)A.out, V = (uint64_t)B.in[2];
+  const uint64_t o = (uint64_t)B.out;
+  if ((uint64_t)B.in[0] != p || x % 16 || p % 16 || V % 16) return 0;
+  const uint64_t rowsb = 4ull * H * S;
+  const Range rx{x, x + rowsb}, rp{p, p + rowsb}, rV{V, V + 2ull * S * H * Dh};
+  const Range ro{o, o + elem_size(B.dtype) * H * Dh};
+  for (const Range& in : {rx, rV})
+    if (overlaps(rp, in) || overlaps(ro, in)) return 0;
+  if (overlaps(rp, ro)) return 0;
+  memset(&d, 0, sizeof d);
+  d.opcode = OP_SOFTMAX_AV;
+  d.dtype = B.dtype;
+  d.flags = (uint8_t)((A.flags | B.flags) & GPUOS_FLAG_NONTEMPORAL);
+  d.n = H * Dh;
+  const bool keep_p = !(A.flags & GPUOS_FLAG_TRANSIENT) || read_later(c, i + 2, rp);
+  d.p.ptr[0] = o;
+  d.p.ptr[1] = keep_p ? p : 0;
+  d.p.ptr[2] = x;
+  d.p.ptr[3] = V;
+  d.p.aux[0] = (int32_t)H;
+  d.p.aux[1] = (int32_t)Dh;
+  d.p.aux[2] = (int32_t)S;
+  d.user_ops = 2;
+  set_tiling(c->cfg, c->workers, d);
+  return 2;
+}
+
 void plan_ops(gpuos_ctx* c, size_t begin, size_t end, std::vector<Planned>& plan) {
   const gpuos_config& cfg = c->cfg;
   const bool fuse = cfg.fusion == 1;
@@ -948,7 +1052,9 @@ void plan_ops(gpuos_ctx* c, size_t begin, size_t end, std::vector<Planned>& plan
     pl.deps.clear();
     size_t j = i + 1;
     if (fuse) {
-      const uint32_t k = try_norm_gemv(c, i, end, pl.desc);
+      uint32_t k = try_norm_gemv(c, i, end, pl.desc);
+      if (!k) k = try_gemv_add(c, i, end, pl.desc);
+      if (!k) k = try_softmax_av(c, i, end, pl.desc);
       if (k) {
         pl.count = k;
         c->st.ops_fused += k - 1;

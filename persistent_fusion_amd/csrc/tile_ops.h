@@ -26,6 +26,7 @@
 namespace gpuos {
 
 typedef __attribute__((address_space(3))) uint32_t lds_u32;
+typedef __attribute__((address_space(3))) float lds_f32;
 
 // The 64 dwords of a descriptor in LDS.
 struct SDesc {
@@ -777,12 +778,42 @@ struct NoWait {
   __device__ __forceinline__ void operator()() const {}
 };
 
+// GEMV epilogues: `load(i, nr)` runs on every lane once per step of rows
+// i .. i + nr - 1, after the step's x loads (so after `ready()`);
+// `store(i, r, s)` runs on lane 0 with the wave sum s of row i (= step row r).
+template <int DT, int CPL, int CPS>
+struct GemvStore {  // the plain op: round and store the row
+  rsrc_t out;
+  __device__ __forceinline__ void load(uint32_t, uint32_t) {}
+  __device__ __forceinline__ void store(uint32_t i, int, float s) { DTr<DT, CPL, CPS>::st(out, i, s); }
+};
+
+// GEMV followed by ADD with a residual: the row is rounded as the GEMV stores
+// it (and stored if the GEMV output is kept), then added to the residual
+// element in the ADD's operand order and rounded as the ADD stores it.
+template <int DT, int CPL, int CPS, int R>
+struct GemvResAdd {
+  using T = DTr<DT, CPL, CPS>;
+  rsrc_t out, res, sum;
+  bool keep, res_first;
+  float rv[R];
+  __device__ __forceinline__ void load(uint32_t i, uint32_t nr) {
+#pragma unroll
+    for (int r = 0; r < R; ++r) rv[r] = (uint32_t)r < nr ? T::ld(res, i + r) : 0.0f;
+  }
+  __device__ __forceinline__ void store(uint32_t i, int r, float s) {
+    const float v = T::round(s);
+    if (keep) T::st(out, i, v);
+    T::st(sum, i, res_first ? rv[r] + v : v + rv[r]);
+  }
+};
+
 // R rows at a time, C chunks per lane per step (x kept packed until used).
 // `ready()` runs once, after the first step's weight loads are issued and
 // before any load of x: a tile whose weights are already final can stream
 // them while it waits for the op that produces x.
-template <int R, int C, int DT, int CPL, int CPS, class Ready>
-__device__ __forceinline__ void gemv_rows(rsrc_t out, uint64_t px, uint64_t pw, uint32_t K,
+template <int R, int C, int DT, int CPL, int CPS, class Ready, class Epi>
+__device__ __forceinline__ void gemv_rows(Epi& epi, uint64_t px, uint64_t pw, uint32_t K,
                                           uint32_t i0, uint32_t i1, Ready& ready) {
   using T = DTr<DT, CPL, CPS>;
   const uint32_t lane = lane_id();
@@ -819,6 +850,7 @@ __device__ __forceinline__ void gemv_rows(rsrc_t out, uint64_t px, uint64_t pw, 
 #pragma unroll
         for (int k = 0; k < T::ES / 2; ++k) xp[c][k] = ld128<CPL>(xv, xo + 16u * k);
       }
+      if (c0 == 0) epi.load(i, nr);
 #pragma unroll
       for (int c = 0; c < C; ++c) {
         float xf[8];
@@ -842,40 +874,56 @@ __device__ __forceinline__ void gemv_rows(rsrc_t out, uint64_t px, uint64_t pw, 
 #pragma unroll
     for (int r = 0; r < R; ++r) {
       const float s = wave_sum(acc[r]);
-      if (lane == 0 && (uint32_t)r < nr) T::st(out, i + r, s);
+      if (lane == 0 && (uint32_t)r < nr) epi.store(i + r, r, s);
     }
   }
   if (waiting) ready();
 }
 
+// Rows [t * tile, (t + 1) * tile) of a GEMV (or of a GEMV-ADD: `fused`).
 template <int DT, int CPL, int CPS, class D, class Ready = NoWait>
-__device__ __forceinline__ void gemv_tile(D d, uint32_t t, Ready ready = Ready()) {
+__device__ __forceinline__ void gemv_tile(D d, uint32_t t, Ready ready = Ready(), bool fused = false) {
   using T = DTr<DT, CPL, CPS>;
   const uint32_t M = d(30), K = d(31), tile = d(7);
   const uint64_t px = d.q(20), pw = d.q(24);
-  const rsrc_t out = make_rsrc(d.q(18)), x = make_rsrc(px), W = make_rsrc(pw);
+  const rsrc_t x = make_rsrc(px), W = make_rsrc(pw);
   const uint32_t i0 = t * tile;
   const uint32_t i1 = i0 + tile < M ? i0 + tile : M;
   const uint32_t lane = lane_id();
-  if ((K % 8 == 0) && aligned16(px) && aligned16(pw)) {
-    // short rows: 4 rows per step, K <= 1,024 in one step; bf16 rows up to
-    // 5,120: one row, all of K in one step; longer rows: one row per step,
-    // 4,096 (bf16 x) or 2,048 (fp32 x) of K per step
-    if (K <= 1024)
-      gemv_rows<4, 2, DT, CPL, CPS>(out, px, pw, K, i0, i1, ready);
-    else if (DT == GPUOS_BF16 && K <= 5120)
-      gemv_rows<1, 10, DT, CPL, CPS>(out, px, pw, K, i0, i1, ready);  // one step
-    else
-      gemv_rows<1, DT == GPUOS_F32 ? 4 : 8, DT, CPL, CPS>(out, px, pw, K, i0, i1, ready);
-    return;
-  }
-  ready();
-  for (uint32_t i = i0; i < i1; ++i) {
-    float acc = 0.0f;
-    for (uint32_t k = lane; k < K; k += 64)
-      acc = __builtin_fmaf(bf2f(ld16<CPL>(W, 2u * (i * K + k))), T::ld(x, k), acc);
-    acc = wave_sum(acc);
-    if (lane == 0) T::st(out, i, acc);
+  auto run = [&](auto& epi) {
+    if ((K % 8 == 0) && aligned16(px) && aligned16(pw)) {
+      // short rows: 4 rows per step, K <= 1,024 in one step; bf16 rows up to
+      // 5,120: one row, all of K in one step; longer rows: one row per step,
+      // 4,096 (bf16 x) or 2,048 (fp32 x) of K per step
+      if (K <= 1024)
+        gemv_rows<4, 2, DT, CPL, CPS>(epi, px, pw, K, i0, i1, ready);
+      else if (DT == GPUOS_BF16 && K <= 5120)
+        gemv_rows<1, 10, DT, CPL, CPS>(epi, px, pw, K, i0, i1, ready);  // one step
+      else
+        gemv_rows<1, DT == GPUOS_F32 ? 4 : 8, DT, CPL, CPS>(epi, px, pw, K, i0, i1, ready);
+      return;
+    }
+    ready();
+    for (uint32_t i = i0; i < i1; ++i) {
+      float acc = 0.0f;
+      for (uint32_t k = lane; k < K; k += 64)
+        acc = __builtin_fmaf(bf2f(ld16<CPL>(W, 2u * (i * K + k))), T::ld(x, k), acc);
+      acc = wave_sum(acc);
+      epi.load(i, 1);
+      if (lane == 0) epi.store(i, 0, acc);
+    }
+  };
+  if (!fused) {
+    GemvStore<DT, CPL, CPS> epi{make_rsrc(d.q(18))};
+    run(epi);
+  } else {
+    GemvResAdd<DT, CPL, CPS, 4> epi;
+    epi.out = make_rsrc(d.q(18));
+    epi.res = make_rsrc(d.q(22));
+    epi.sum = make_rsrc(d.q(32));
+    epi.keep = d.q(18) != 0;
+    epi.res_first = d(26) != 0;
+    run(epi);
   }
 }
 
@@ -1133,6 +1181,90 @@ __device__ __forceinline__ void attn_av_tile(D d, uint32_t t) {
   }
 }
 
+// ROW_SOFTMAX -> ATTN_AV (fp32 score rows of S <= 512 elements, Dh % 8 == 0,
+// 16-byte aligned scores, probabilities and V).  Tile t is AV chunk t (8
+// output columns of head h).  The wave computes the softmax of score row h
+// itself, with ROW_SOFTMAX's in-register arithmetic (the head's first chunk
+// also stores the row when it is kept), hands the probabilities to the AV
+// lanes through its LDS scratch (`kWaveScratch` floats) and sums them against
+// V in attn_av_tile's order, so every stored value matches the separate ops.
+// V and the score row are requested together.
+template <int DT, int CPL, int CPS, class D>
+__device__ __forceinline__ void softmax_av_tile(D d, uint32_t t, lds_f32* scr) {
+  using T = DTr<DT, CPL, CPS>;
+  using F = DTr<GPUOS_F32, CPL, CPS>;
+  const uint32_t H = d(30), Dh = d(31), S = d(32);
+  const uint32_t HD = H * Dh;
+  const uint64_t pout = d.q(18), pp = d.q(20), px = d.q(22), pV = d.q(24);
+  const uint32_t lane = lane_id();
+  const uint32_t c = t;
+  const uint32_t h = (c * 8) / Dh;
+  const uint32_t rowbytes = S * 4u;
+  const rsrc_t Vv = make_rsrc_n(pV, S * HD * 2u);
+  u32x4 vr[8];
+#pragma unroll
+  for (int u = 0; u < 8; ++u) {
+    const uint32_t j = 64 * u + lane;
+    vr[u] = ld128<CPL>(Vv, j < S ? 2u * (j * HD + c * 8) : 0xFFF00000u);
+  }
+  const rsrc_t vin = make_rsrc_n(px + (uint64_t)h * rowbytes, rowbytes);
+  float x[2][4];
+  F::ldq(vin, lane, x[0]);
+  F::ldq(vin, lane + 64, x[1]);
+  const uint32_t nv = S / 4;
+  const bool v0 = lane < nv, v1 = lane + 64 < nv;
+  SoftAcc acc;
+#pragma unroll
+  for (int e = 0; e < 4; ++e)
+    if (v0) acc.add(x[0][e]);
+#pragma unroll
+  for (int e = 0; e < 4; ++e)
+    if (v1) acc.add(x[1][e]);
+  float M, Ssum;
+  soft_combine(acc, M, Ssum);
+  float y[2][4];
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    y[0][e] = expf(x[0][e] - M) / Ssum;
+    y[1][e] = expf(x[1][e] - M) / Ssum;
+  }
+  if (pp && (c * 8) % Dh == 0) {
+    const rsrc_t vout = make_rsrc_n(pp + (uint64_t)h * rowbytes, rowbytes);
+    F::stq(vout, lane, y[0]);
+    F::stq(vout, lane + 64, y[1]);
+  }
+  // element 4k + e of the row sits in lane k (k < 64) or k - 64 (k >= 64);
+  // a wave's LDS accesses complete in issue order
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    scr[4 * lane + e] = y[0][e];
+    scr[256 + 4 * lane + e] = y[1][e];
+  }
+  float w[8];
+#pragma unroll
+  for (int u = 0; u < 8; ++u) {
+    const uint32_t j = 64 * u + lane;
+    w[u] = j < S ? scr[j] : 0.0f;
+  }
+  float a8[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+#pragma unroll
+  for (int u = 0; u < 8; ++u) {
+    float v[8];
+    unpack_bf16x8(vr[u], v);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) a8[e] = __builtin_fmaf(w[u], v[e], a8[e]);
+  }
+#pragma unroll
+  for (int e = 0; e < 8; ++e) a8[e] = wave_sum(a8[e]);
+  if (lane < 8) {
+    float mine = a8[0];
+#pragma unroll
+    for (int e = 1; e < 8; ++e)
+      if (lane == (uint32_t)e) mine = a8[e];
+    T::st(make_rsrc(pout), c * 8 + lane, mine);
+  }
+}
+
 // ---------------------------------------------------------------------------
 // debug op: spin for aux[0] nanoseconds (s_memrealtime ticks at 100 MHz),
 // bounded to 10 ms.
@@ -1190,7 +1322,7 @@ __device__ __forceinline__ bool exec_stream(uint32_t op, bool bf, D d, uint32_t 
 constexpr int CP_NT = 2;
 
 template <int CPL, int CPS, class D>
-__device__ __forceinline__ uint32_t exec_tile(D d, uint32_t t) {
+__device__ __forceinline__ uint32_t exec_tile(D d, uint32_t t, lds_f32* scr) {
   const uint32_t w0 = d(0);
   const uint32_t op = w0 & 0xffu, dt = (w0 >> 8) & 0xffu, fl = (w0 >> 16) & 0xffu;
   const bool bf = dt == GPUOS_BF16;
@@ -1234,6 +1366,13 @@ __device__ __forceinline__ uint32_t exec_tile(D d, uint32_t t) {
     case OP_NORM_GEMV:
       if (!bf) return (uint32_t)DERR_BAD_OPCODE;
       norm_gemv_tile<CPL, CPS>(d, t);
+      return 0;
+    case OP_GEMV_ADD:
+      if (bf) gemv_tile<B, CPL, CPS>(d, t, NoWait(), true);
+      else gemv_tile<F, CPL, CPS>(d, t, NoWait(), true);
+      return 0;
+    case OP_SOFTMAX_AV:
+      if (bf) softmax_av_tile<B, CPL, CPS>(d, t, scr); else softmax_av_tile<F, CPL, CPS>(d, t, scr);
       return 0;
     default:
       return (uint32_t)DERR_BAD_OPCODE;

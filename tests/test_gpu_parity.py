@@ -261,7 +261,46 @@ def test_gemv(dtype):
         check(wl, runner.run_resident(wl))
 
 
-@pytest.mark.parametrize("H,D,S", [(14, 64, 512), (2, 8, 5), (3, 10, 70), (4, 128, 64)])
+def _gemv_add_workload(dtype, M, K, res_first, in_place, seed):
+    rng = np.random.default_rng(seed)
+    conv = (lambda a: workloads.f32_to_bf16_trunc(a)) if dtype == "bf16" else (lambda a: a)
+    npdt = np.uint16 if dtype == "bf16" else np.float32
+    bufs = {"W": workloads.f32_to_bf16_trunc((rng.standard_normal(M * K) * 0.05).astype(np.float32)),
+            "x": conv(rng.standard_normal(K).astype(np.float32)),
+            "r": conv(rng.standard_normal(M).astype(np.float32)),
+            "y": np.zeros(M, npdt), "z": np.zeros(M, npdt)}
+    z = "r" if in_place else "z"
+    ins = (Ref("r"), Ref("y")) if res_first else (Ref("y"), Ref("r"))
+    ops = [Op("gemv", Ref("y"), (Ref("x"),), Ref("W"), n=M, dtype=dtype, dims=(M, K)),
+           Op("add", Ref(z), ins, n=M, dtype=dtype)]
+    dts = {"W": "bf16", "x": dtype, "r": dtype, "y": dtype, "z": dtype}
+    return Workload("gemv_add", bufs, dts, ops, outputs=["y", z])
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_gemv_add_fused(dtype):
+    """GEMV followed by a residual ADD runs as one descriptor; each op is
+    checked on the GPU's own inputs, and the fused run stores exactly what
+    the two separate ops store (also when the ADD writes the residual in
+    place)."""
+    _need_gpu()
+    for M, K, res_first in ((896, 896, True), (896, 4864, False), (1000, 6000, True),
+                            (33, 100, False), (1, 8, True)):
+        say(f"gemv+add {dtype} M={M} K={K} res_first={res_first}")
+        wl = _gemv_add_workload(dtype, M, K, res_first, False, 20 + M)
+        got = runner.run_resident(wl)
+        bad = oracle.local_check(wl, got, oracle.compare)
+        assert not bad, [(i, n, str(r)) for i, n, r in bad]
+        for in_place in (False, True):
+            wl = _gemv_add_workload(dtype, M, K, res_first, in_place, 20 + M)
+            fused = runner.run_resident(wl, fusion=1)
+            plain = runner.run_resident(wl, fusion=2)
+            for name in wl.outputs:
+                assert np.array_equal(fused[name].view(np.uint8), plain[name].view(np.uint8)), name
+
+
+@pytest.mark.parametrize("H,D,S", [(14, 64, 512), (2, 8, 5), (3, 10, 70), (4, 128, 64),
+                                   (2, 16, 100), (1, 8, 4)])
 def test_attention(H, D, S):
     _need_gpu()
     say(f"attention H={H} D={D} S={S}")
@@ -289,6 +328,11 @@ def test_attention(H, D, S):
     want, sc = oracle.run(Workload("attn", b3, wl.dtypes, ops[2:3]), scales=True)
     r = oracle.compare(got["o"], want["o"], "bf16", sc["o"])
     assert r.ok, str(r)
+    # softmax and AV fused into one descriptor (when the shape allows) store
+    # exactly what the separate ops store
+    plain = runner.run_resident(wl, fusion=2)
+    for name in ("s", "p", "o"):
+        assert np.array_equal(got[name].view(np.uint8), plain[name].view(np.uint8)), name
 
 
 def test_gather():

@@ -391,6 +391,103 @@ def test_norm_gemv_drops_unread_transient_norm_output():
         assert desc(c, 1)["ng"]["h"] == 0
 
 
+# ----------------------------------------------------------------------------
+# GEMV -> residual ADD fusion
+
+
+def _gemv_add_ops(M=896, K=4864, res_first=True, z_is=None, src_len=0, dtype="bf16"):
+    x, W, y, r, z = (buf(i) for i in range(5))
+    z = {None: z, "r": r, "x": x, "y": y}[z_is]
+    ins = [r, y] if res_first else [y, r]
+    ops = [make_op("gemv", y, [x], aux=W, n=M, dtype=dtype, dims=(M, K)),
+           make_op("add", z, ins, n=M, dtype=dtype, src_len=(src_len, 0))]
+    return (gpuos.GpuosOp * 2)(*ops), (x, W, y, r, z)
+
+
+def test_gemv_add_fuses_into_one_descriptor():
+    for res_first in (True, False):
+        for z_is in (None, "r"):
+            ops, (x, W, y, r, z) = _gemv_add_ops(res_first=res_first, z_is=z_is)
+            with ctx() as c:
+                c.submit(ops)
+                c.flush()
+                assert c.published(0) == 1
+                d = desc(c, 1)
+                assert d["opcode"] == 34 and d["user_ops"] == 2 and d["n"] == 896
+                ga = d["ga"]
+                assert (ga["out"], ga["x"], ga["res"], ga["W"], ga["sum"]) == (y, x, r, W, z)
+                assert (ga["M"], ga["K"], ga["res_first"]) == (896, 4864, int(res_first))
+                assert d["ntiles"] * d["tile"] >= 896 and d["flags"] & 0x80
+    # fp32 works the same way
+    ops, _ = _gemv_add_ops(dtype="f32")
+    with ctx() as c:
+        c.submit(ops)
+        c.flush()
+        assert c.published(0) == 1 and desc(c, 1)["opcode"] == 34
+
+
+def test_gemv_add_refusals():
+    # the sum written over the GEMV input or output would race with other rows
+    for z_is in ("x", "y"):
+        ops, _ = _gemv_add_ops(z_is=z_is)
+        with ctx() as c:
+            c.submit(ops)
+            c.flush()
+            assert c.published(0) == 2
+    # a residual read cyclically stays unfused
+    ops, _ = _gemv_add_ops(src_len=448)
+    with ctx() as c:
+        c.submit(ops)
+        c.flush()
+        assert c.published(0) == 2
+    # fusion off
+    ops, _ = _gemv_add_ops()
+    with ctx(fusion=2) as c:
+        c.submit(ops)
+        c.flush()
+        assert c.published(0) == 2
+
+
+# ----------------------------------------------------------------------------
+# ROW_SOFTMAX -> ATTN_AV fusion
+
+
+def _softmax_av_ops(H=14, D=64, S=512, p_is=None, transient=False, out_dtype="bf16"):
+    x, p, V, o = (buf(i) for i in range(4))
+    p = {None: p, "x": x, "V": V}[p_is]
+    ops = [make_op("row_softmax", p, [x], n=H * S, rows=H, row_len=S,
+                   flags=gpuos.FLAG_TRANSIENT if transient else 0),
+           make_op("attn_av", o, [p], aux=V, n=H * D, dtype=out_dtype, dims=(H, D, S))]
+    return (gpuos.GpuosOp * 2)(*ops), (x, p, V, o)
+
+
+def test_softmax_av_fuses_into_one_descriptor():
+    for transient in (False, True):
+        ops, (x, p, V, o) = _softmax_av_ops(transient=transient)
+        with ctx() as c:
+            c.submit(ops)
+            c.flush()
+            assert c.published(0) == 1
+            d = desc(c, 1)
+            assert d["opcode"] == 35 and d["user_ops"] == 2
+            assert d["ptr"] == [o, 0 if transient else p, x, V]
+            assert d["ntiles"] == 14 * 64 // 8 and d["tile"] == 1 and d["n"] == 14 * 64
+
+
+def test_softmax_av_refusals():
+    for kw in (dict(S=516), dict(S=70), dict(D=12), dict(p_is="x")):
+        ops, _ = _softmax_av_ops(**kw)
+        with ctx() as c:
+            c.submit(ops)
+            c.flush()
+            assert c.published(0) == 2, kw
+    ops, _ = _softmax_av_ops()
+    with ctx(fusion=2) as c:
+        c.submit(ops)
+        c.flush()
+        assert c.published(0) == 2
+
+
 def test_graph_replay_poisons_only_buffers_written_whole_first():
     """Between graph replays the tests fill outputs with NaN; only buffers
     whose first use is a whole write may be poisoned (a KV cache written at
