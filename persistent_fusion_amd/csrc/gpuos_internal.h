@@ -26,10 +26,12 @@ namespace gpuos {
 // Internal opcodes beyond the public ones (gpuos_opcode).
 enum : uint8_t {
   OP_FUSED_EW = 32,   // register-resident elementwise chain
-  OP_NORM_GEMV = 33,  // RMSNORM -> GEMV (-> SILU_MUL): every GEMV tile
-                      // normalises the input row itself (tile 0 also stores
-                      // it); with the SiLU gate a tile computes gate row i
-                      // and up row F + i together
+  OP_NORM_GEMV = 33,  // RMSNORM -> GEMV (-> SILU_MUL, or -> ROPE q, ROPE k,
+                      // COPY v): every GEMV tile normalises the input row
+                      // itself (tile 0 also stores it); with the SiLU gate
+                      // a tile computes gate row i and up row F + i
+                      // together, in rotary mode the two rows a rotation
+                      // pairs
   OP_GEMV_ADD = 34,   // GEMV -> ADD of a residual: each output row, rounded
                       // as the GEMV stores it, is added to the residual
                       // element and stored to the ADD's output
@@ -121,7 +123,15 @@ struct alignas(16) DevDesc {
       uint32_t K;           // 31
       float eps;            // 32
       uint32_t F;           // 33: gate rows (M == 2F) when act != 0
-      uint8_t _pad[80];
+      // rotary mode (q != 0): the GEMV output is q | k | v, D = M / 3 rows
+      // each, heads of hd rows; ROPE of q and k and COPY of v follow
+      uint64_t q;           // 34-35: rotated q [D]
+      uint64_t k;           // 36-37: rotated k [D] (e.g. a K-cache slot)
+      uint64_t v;           // 38-39: copy of v [D] (e.g. a V-cache slot)
+      uint64_t tabq;        // 40-41: rotary table of q (fp32 cos[hd/2] | sin[hd/2])
+      uint64_t tabk;        // 42-43: rotary table of k
+      uint32_t hd;          // 44: head size (even)
+      uint8_t _pad[36];
     } ng;
     struct {
       uint64_t out;         // 18-19: GEMV output [M] (0 = not stored)
@@ -158,6 +168,8 @@ static_assert(offsetof(DevDesc, p.alpha) == 28 * 4, "alpha at dword 28");
 static_assert(offsetof(DevDesc, p.aux) == 30 * 4, "aux at dword 30");
 static_assert(offsetof(DevDesc, f.out) == 26 * 4, "fused out at dword 26");
 static_assert(offsetof(DevDesc, ng.M) == 30 * 4, "norm-GEMV M at dword 30");
+static_assert(offsetof(DevDesc, ng.q) == 34 * 4 && offsetof(DevDesc, ng.hd) == 44 * 4,
+              "norm-GEMV rotary fields at dwords 34-44");
 static_assert(offsetof(DevDesc, ga.W) == 24 * 4 && offsetof(DevDesc, ga.M) == 30 * 4 &&
                   offsetof(DevDesc, ga.sum) == 32 * 4,
               "GEMV-ADD keeps the GEMV fields where a GEMV descriptor has them");

@@ -661,7 +661,7 @@ void set_tiling(const gpuos_config& cfg, uint32_t workers, DevDesc& d) {
       break;
     }
     case OP_NORM_GEMV: {
-      const uint32_t units = d.ng.act ? d.ng.F : d.ng.M;
+      const uint32_t units = d.ng.act ? d.ng.F : d.ng.q ? d.ng.M / 2 : d.ng.M;
       uint32_t r = ceil_div(units, std::max<uint32_t>(1, workers));
       r = std::min<uint32_t>(std::max<uint32_t>(r, 1), 16);
       d.tile = r;
@@ -917,6 +917,45 @@ uint32_t try_norm_gemv(gpuos_ctx* c, size_t i, size_t end, DevDesc& d) {
       }
     }
   }
+  // rotary mode: ROPE of the q third, ROPE of the k third, COPY of the v third
+  uint64_t rq = 0, rk = 0, rv = 0, tq = 0, tk = 0;
+  uint32_t hd = 0;
+  if (!F && i + 4 < end) {
+    const gpuos_op& Q = c->staged[i + 2].op;
+    const gpuos_op& Kr = c->staged[i + 3].op;
+    const gpuos_op& Cv = c->staged[i + 4].op;
+    bool ok = c->staged[i + 2].ring == sa.ring && c->staged[i + 3].ring == sa.ring &&
+              c->staged[i + 4].ring == sa.ring && Q.opcode == GPUOS_OP_ROPE &&
+              Kr.opcode == GPUOS_OP_ROPE && Cv.opcode == GPUOS_OP_COPY && Q.dtype == GPUOS_BF16 &&
+              Kr.dtype == GPUOS_BF16 && Cv.dtype == GPUOS_BF16;
+    const uint32_t H = Q.rows, h = Q.row_len, Dq = H * h;
+    ok = ok && h >= 2 && h % 2 == 0 && Kr.rows == H && Kr.row_len == h && Cv.n == Dq &&
+         M == 3 * Dq && (uint64_t)Q.in[0] == y && (uint64_t)Kr.in[0] == y + 2ull * Dq &&
+         (uint64_t)Cv.in[0] == y + 4ull * Dq;
+    for (const gpuos_op* o : {&Q, &Kr, &Cv})
+      ok = ok && (!o->src_len[0] || o->src_len[0] >= o->n);
+    if (ok) {
+      const Range oq{(uint64_t)Q.out, (uint64_t)Q.out + 2ull * Dq};
+      const Range ok_{(uint64_t)Kr.out, (uint64_t)Kr.out + 2ull * Dq};
+      const Range ov{(uint64_t)Cv.out, (uint64_t)Cv.out + 2ull * Dq};
+      const Range rtq{(uint64_t)Q.in[2], (uint64_t)Q.in[2] + 4ull * h};
+      const Range rtk{(uint64_t)Kr.in[2], (uint64_t)Kr.in[2] + 4ull * h};
+      for (const Range& o : {oq, ok_, ov}) {
+        for (const Range& in : {rx, rg, rW, rh, ry, rtq, rtk})
+          if (overlaps(o, in)) ok = false;
+      }
+      if (overlaps(oq, ok_) || overlaps(oq, ov) || overlaps(ok_, ov)) ok = false;
+      if (ok) {
+        rq = (uint64_t)Q.out;
+        rk = (uint64_t)Kr.out;
+        rv = (uint64_t)Cv.out;
+        tq = (uint64_t)Q.in[2];
+        tk = (uint64_t)Kr.in[2];
+        hd = h;
+        count = 5;
+      }
+    }
+  }
   memset(&d, 0, sizeof d);
   d.opcode = OP_NORM_GEMV;
   d.dtype = GPUOS_BF16;
@@ -927,7 +966,7 @@ uint32_t try_norm_gemv(gpuos_ctx* c, size_t i, size_t end, DevDesc& d) {
   d.ng.g = g;
   // intermediates are stored unless transient and unread by later ops
   const bool keep_h = !(A.flags & GPUOS_FLAG_TRANSIENT) || read_later(c, i + count, rh);
-  const bool keep_y = !F || !(B.flags & GPUOS_FLAG_TRANSIENT) || read_later(c, i + count, ry);
+  const bool keep_y = (!F && !rq) || !(B.flags & GPUOS_FLAG_TRANSIENT) || read_later(c, i + count, ry);
   d.ng.h = keep_h ? h : 0;
   d.ng.out = keep_y ? y : 0;
   d.ng.act = act;
@@ -935,6 +974,12 @@ uint32_t try_norm_gemv(gpuos_ctx* c, size_t i, size_t end, DevDesc& d) {
   d.ng.K = K;
   d.ng.eps = A.eps;
   d.ng.F = F;
+  d.ng.q = rq;
+  d.ng.k = rk;
+  d.ng.v = rv;
+  d.ng.tabq = tq;
+  d.ng.tabk = tk;
+  d.ng.hd = hd;
   d.user_ops = count;
   set_tiling(c->cfg, c->workers, d);
   return count;

@@ -927,14 +927,17 @@ __device__ __forceinline__ void gemv_tile(D d, uint32_t t, Ready ready = Ready()
   }
 }
 
-// RMSNORM -> GEMV (-> SILU_MUL), bf16, K <= 1,024 (the normalised row is two
-// 16-byte vectors per lane, in the GEMV's chunk layout).  Each value is the
-// one the separate ops would store: the norm is summed in the same order as
-// RMSNORM's in-register path and rounded to bf16, the GEMV accumulates in
-// the same order as gemv_rows<4, 2>, its outputs are rounded to bf16, and the
-// gate is applied to those rounded values.  Up to 4 output rows per step (2
-// gate/up pairs with the epilogue), two steps' weights requested together
-// (the tile's first two before `ready()`).
+// RMSNORM -> GEMV (-> SILU_MUL, or -> ROPE q, ROPE k, COPY v), bf16,
+// K <= 1,024 (the normalised row is two 16-byte vectors per lane, in the
+// GEMV's chunk layout).  Each value is the one the separate ops would store:
+// the norm is summed in the same order as RMSNORM's in-register path and
+// rounded to bf16, the GEMV accumulates in the same order as gemv_rows<4, 2>,
+// its outputs are rounded to bf16, and the gate, or the rotation (with
+// rope_tile's products and sums) and the copy, are applied to those rounded
+// values.  A unit is one output row, a gate/up pair, or in rotary mode a
+// pair of rows (i, i + hd/2) of one q or k head or two adjacent v rows.  Up
+// to 4 output rows per step, two steps' weights requested together (the
+// tile's first two before `ready()`).
 template <int CPL, int CPS, class D, class Ready = NoWait>
 __device__ __forceinline__ void norm_gemv_tile(D d, uint32_t t, Ready ready = Ready()) {
   using T = DTr<GPUOS_BF16, CPL, CPS>;
@@ -943,7 +946,11 @@ __device__ __forceinline__ void norm_gemv_tile(D d, uint32_t t, Ready ready = Re
   const uint32_t M = d(30), K = d(31), F = d(33), tile = d(7);
   const float eps = __uint_as_float(d(32));
   const bool gate = pact != 0;
-  const uint32_t units = gate ? F : M;
+  const uint64_t prq = d.q(34), prk = d.q(36), prv = d.q(38), ptq = d.q(40), ptk = d.q(42);
+  const bool rope = prq != 0;
+  const uint32_t hd = rope ? d(44) : 2u, half = hd / 2;
+  const uint32_t Dq = M / 3, hh = Dq / 2;  // rotary mode: rows per section, units per section
+  const uint32_t units = gate ? F : rope ? M / 2 : M;
   const uint32_t u0 = t * tile;
   const uint32_t u1 = u0 + tile < units ? u0 + tile : units;
   const uint32_t lane = lane_id();
@@ -952,14 +959,42 @@ __device__ __forceinline__ void norm_gemv_tile(D d, uint32_t t, Ready ready = Re
   const rsrc_t W = make_rsrc_n(pW, M * K * 2u);
   const rsrc_t out = make_rsrc(pout), act = make_rsrc(pact);
   constexpr int R = 4;
-  const uint32_t step = gate ? 2u : 4u;  // units per step
-  // a step's rows: i .. i + 3, or gate rows i, i + 1 and up rows F + i, F + i + 1
+  const bool paired = gate || rope;
+  const uint32_t step = paired ? 2u : 4u;  // units per step
+  // row `which` (0, 1) of rotary unit u
+  auto pair_row = [&](uint32_t u, uint32_t which) -> uint32_t {
+    const uint32_t sec = u / hh, w = u - sec * hh;
+    if (sec >= 2) return 2 * Dq + 2 * w + which;
+    const uint32_t h = w / half, p = w - h * half;
+    return sec * Dq + h * hd + p + which * half;
+  };
+  // a step's rows: i .. i + 3; or units i, i + 1 as rows 0, 1 and their
+  // partners (up rows F + i, F + i + 1, or the rotation partners) as rows 2, 3
   auto rows_of = [&](uint32_t i, uint32_t (&row)[R], bool (&ok)[R]) {
 #pragma unroll
     for (int r = 0; r < R; ++r) {
-      const uint32_t k = gate ? (uint32_t)(r & 1) : (uint32_t)r;
+      const uint32_t k = paired ? (uint32_t)(r & 1) : (uint32_t)r;
       ok[r] = i + k < u1;
-      row[r] = (gate && r >= 2 ? F : 0u) + i + k;
+      if (rope)
+        row[r] = ok[r] ? pair_row(i + k, (uint32_t)r >> 1) : 0u;
+      else
+        row[r] = (gate && r >= 2 ? F : 0u) + i + k;
+    }
+  };
+  // rotary mode: cos / sin of the 4 units from i on (0 for v units)
+  float tc[4], ts[4];
+  auto load_tab = [&](uint32_t i) {
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      tc[k] = 0.0f;
+      ts[k] = 0.0f;
+      const uint32_t u = i + k, sec = u / hh;
+      if (u < u1 && sec < 2) {
+        const uint32_t w = u - sec * hh, p = w - (w / half) * half;
+        const rsrc_t tab = make_rsrc(sec == 0 ? ptq : ptk);
+        tc[k] = __uint_as_float(ld32<CPL>(tab, 4u * p));
+        ts[k] = __uint_as_float(ld32<CPL>(tab, 4u * (half + p)));
+      }
     }
   };
   auto load_w = [&](const uint32_t (&row)[R], const bool (&ok)[R], u32x4 (&wr)[R][2]) {
@@ -972,7 +1007,8 @@ __device__ __forceinline__ void norm_gemv_tile(D d, uint32_t t, Ready ready = Re
     }
   };
   float hx[2][8];
-  auto finish = [&](uint32_t i, const uint32_t (&row)[R], const bool (&ok)[R], const u32x4 (&wr)[R][2]) {
+  auto finish = [&](uint32_t i, uint32_t toff, const uint32_t (&row)[R], const bool (&ok)[R],
+                    const u32x4 (&wr)[R][2]) {
     float acc[R] = {0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
     for (int c = 0; c < 2; ++c) {
@@ -995,6 +1031,27 @@ __device__ __forceinline__ void norm_gemv_tile(D d, uint32_t t, Ready ready = Re
 #pragma unroll
         for (int k = 0; k < 2; ++k)
           if (ok[k]) T::st(act, i + k, ew_apply<GPUOS_OP_SILU_MUL>(v[k], v[k + 2], 0.0f));
+      }
+      if (rope) {
+#pragma unroll
+        for (int k = 0; k < 2; ++k) {
+          if (!ok[k]) continue;
+          const uint32_t u = i + k, sec = u / hh, w = u - sec * hh;
+          const float x1 = v[k], x2 = v[k + 2];
+          if (sec < 2) {
+            const float c = tc[toff + k], sn = ts[toff + k];
+            const float a1 = x1 * c, b1 = x2 * sn;
+            const float a2 = x2 * c, b2 = x1 * sn;
+            const uint32_t h = w / half, e1 = h * hd + (w - h * half);
+            const rsrc_t dst = make_rsrc(sec == 0 ? prq : prk);
+            T::st(dst, e1, a1 - b1);
+            T::st(dst, e1 + half, a2 + b2);
+          } else {
+            const rsrc_t dst = make_rsrc(prv);
+            T::st(dst, 2 * w, x1);
+            T::st(dst, 2 * w + 1, x2);
+          }
+        }
       }
     }
   };
@@ -1038,8 +1095,9 @@ __device__ __forceinline__ void norm_gemv_tile(D d, uint32_t t, Ready ready = Re
         T::stq(hr, lane + 64, hx[1]);
       }
     }
-    finish(i, rowA, okA, wA);
-    if (i + step < u1) finish(i + step, rowB, okB, wB);
+    if (rope) load_tab(i);
+    finish(i, 0, rowA, okA, wA);
+    if (i + step < u1) finish(i + step, 2, rowB, okB, wB);
   }
   if (waiting) ready();
 }

@@ -325,7 +325,8 @@ def decode_desc(raw: bytes) -> dict:
     # RMSNORM -> GEMV (-> SILU_MUL) descriptors
     d["ng"] = {"W": q(18), "out": q(20), "x": q(22), "g": q(24), "h": q(26), "act": q(28),
                "M": w[30], "K": w[31], "eps": struct.unpack("<f", raw[32 * 4:33 * 4])[0],
-               "F": w[33]}
+               "F": w[33], "q": q(34), "k": q(36), "v": q(38), "tabq": q(40), "tabk": q(42),
+               "hd": w[44]}
     # GEMV -> residual ADD descriptors
     d["ga"] = {"out": q(18), "x": q(20), "res": q(22), "W": q(24), "res_first": w[26],
                "M": w[30], "K": w[31], "sum": q(32)}

@@ -357,16 +357,56 @@ def test_small_decode_local_check():
     assert not bad, [(i, wl.ops[i].kind, n, str(r)) for i, n, r in bad[:5]]
 
 
-def test_decode_norm_gemv_fusion_is_bit_identical():
-    """RMSNORM -> GEMV -> SILU_MUL fused into one descriptor stores exactly the
-    values the three separate ops store (same sums in the same order, same
-    bf16 roundings)."""
+@pytest.mark.parametrize("H,hd", [(14, 64), (3, 16), (2, 128), (5, 8)])
+def test_norm_gemv_rotary_fused(H, hd):
+    """RMSNORM -> GEMV(q|k|v) -> ROPE q, ROPE k (into a cache slot), COPY v
+    (into a cache slot) as one descriptor: each op checked on the GPU's own
+    inputs, and the fused run stores exactly what the five separate ops
+    store."""
+    _need_gpu()
+    say(f"norm-gemv rotary H={H} hd={hd}")
+    D, S, slot = H * hd, 4, 2
+    rng = np.random.default_rng(30 + H)
+    bf = workloads.f32_to_bf16_trunc
+    tab = workloads.rope_table([17], hd).reshape(-1)
+    bufs = {"x": bf(rng.standard_normal(D).astype(np.float32)),
+            "g": bf((rng.standard_normal(D) * 0.5).astype(np.float32)),
+            "W": bf((rng.standard_normal(3 * D * D) * 0.05).astype(np.float32)),
+            "tab": tab.astype(np.float32),
+            "h": np.zeros(D, np.uint16), "qkv": np.zeros(3 * D, np.uint16), "q": np.zeros(D, np.uint16),
+            "K": bf(rng.standard_normal(S * D).astype(np.float32)),
+            "V": bf(rng.standard_normal(S * D).astype(np.float32))}
+    dts = {k: "bf16" for k in bufs}
+    dts["tab"] = "f32"
+    ops = [Op("rmsnorm", Ref("h"), (Ref("x"),), Ref("g"), n=D, dtype="bf16", rows=1, row_len=D,
+              eps=float(np.float32(1e-6))),
+           Op("gemv", Ref("qkv"), (Ref("h"),), Ref("W"), n=3 * D, dtype="bf16", dims=(3 * D, D)),
+           Op("rope", Ref("q"), (Ref("qkv", 0),), Ref("tab"), n=D, dtype="bf16", rows=H, row_len=hd,
+              dims=(H, hd)),
+           Op("rope", Ref("K", slot * D), (Ref("qkv", D),), Ref("tab"), n=D, dtype="bf16", rows=H,
+              row_len=hd, dims=(H, hd)),
+           Op("copy", Ref("V", slot * D), (Ref("qkv", 2 * D),), n=D, dtype="bf16")]
+    wl = Workload("norm_gemv_rope", bufs, dts, ops, outputs=["h", "qkv", "q", "K", "V"])
+    got = runner.run_resident(wl)
+    bad = oracle.local_check(wl, got, oracle.compare)
+    assert not bad, [(i, n, str(r)) for i, n, r in bad]
+    plain = runner.run_resident(wl, fusion=2)
+    for name in wl.outputs:
+        assert np.array_equal(got[name], plain[name]), name
+
+
+def test_decode_fusion_is_bit_identical():
+    """The decode's fused descriptors (RMSNORM -> GEMV -> SILU_MUL, RMSNORM ->
+    GEMV -> ROPE q, ROPE k, COPY v, GEMV -> residual ADD, ROW_SOFTMAX ->
+    ATTN_AV) store exactly the values the separate ops store (same sums in
+    the same order, same bf16 roundings)."""
     _need_gpu()
     say("decode 3 layers x 3 tokens, fusion on vs off")
     outs = {}
     for fusion in (1, 2):
         wl = workloads.gen_decode(seed=4, layers=3, tokens=3)
-        names = ["x", "h", "qkv", "gu", "act"] + [f"K{l}" for l in range(3)] + [f"V{l}" for l in range(3)]
+        names = (["x", "h", "qkv", "q", "scores", "probs", "attn", "o", "gu", "act", "down"] +
+                 [f"K{l}" for l in range(3)] + [f"V{l}" for l in range(3)])
         outs[fusion] = runner.run_resident(wl, outputs=names, fusion=fusion)
     for name, v in outs[1].items():
         assert np.array_equal(v, outs[2][name]), name

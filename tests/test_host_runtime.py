@@ -383,6 +383,45 @@ def test_norm_gemv_without_gate_and_refusals():
         assert c.published(0) == 3
 
 
+def _norm_gemv_rope_ops(H=14, hd=64, copy_off=None, k_out_overlaps_qkv=False):
+    D = H * hd
+    x, g, h, W, qkv, q, kc, vc, tab = (buf(i) for i in range(9))
+    kc = qkv + 2 * D if k_out_overlaps_qkv else kc
+    voff = 2 * D if copy_off is None else copy_off
+    ops = [make_op("rmsnorm", h, [x], aux=g, n=D, dtype="bf16", rows=1, row_len=D, eps=1e-6),
+           make_op("gemv", qkv, [h], aux=W, n=3 * D, dtype="bf16", dims=(3 * D, D)),
+           make_op("rope", q, [qkv], aux=tab, n=D, dtype="bf16", rows=H, row_len=hd),
+           make_op("rope", kc, [qkv + 2 * D], aux=tab, n=D, dtype="bf16", rows=H, row_len=hd),
+           make_op("copy", vc, [qkv + 2 * voff], n=D, dtype="bf16")]
+    return (gpuos.GpuosOp * 5)(*ops), (x, g, h, W, qkv, q, kc, vc, tab)
+
+
+def test_norm_gemv_rotary_fuses_five_ops():
+    ops, (x, g, h, W, qkv, q, kc, vc, tab) = _norm_gemv_rope_ops()
+    with ctx() as c:
+        c.submit(ops)
+        c.flush()
+        assert c.published(0) == 1
+        d = desc(c, 1)
+        assert d["opcode"] == 33 and d["user_ops"] == 5
+        ng = d["ng"]
+        assert (ng["q"], ng["k"], ng["v"], ng["tabq"], ng["tabk"], ng["hd"]) == (q, kc, vc, tab, tab, 64)
+        assert (ng["out"], ng["act"], ng["M"], ng["K"]) == (qkv, 0, 3 * 896, 896)
+        assert d["n"] == 3 * 896 and d["ntiles"] * d["tile"] >= 3 * 896 // 2
+
+
+def test_norm_gemv_rotary_refusals():
+    # a COPY of the wrong third, or a rotated k written over the GEMV output,
+    # leaves the rotary ops unfused (the norm and the GEMV still fuse)
+    for kw in (dict(copy_off=0), dict(k_out_overlaps_qkv=True)):
+        ops, _ = _norm_gemv_rope_ops(**kw)
+        with ctx() as c:
+            c.submit(ops)
+            c.flush()
+            assert c.published(0) == 4, kw
+            assert desc(c, 1)["user_ops"] == 2
+
+
 def test_norm_gemv_drops_unread_transient_norm_output():
     ops, _ = _norm_gemv_ops(transient_h=True)
     with ctx() as c:
