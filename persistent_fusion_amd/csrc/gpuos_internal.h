@@ -78,6 +78,10 @@ constexpr uint8_t DF_AUX_READY = 0x80;
 constexpr int kMaxDeps = 14;  // dependencies a descriptor carries (more: wait
                               // for the retire cursor instead)
 constexpr int kMaxFusedInputs = 4;
+// Copies of each slot's completion word.  The completing wave writes all of
+// them; a waiting wave polls the copy its number selects, so a descriptor
+// with many tiles is not waited on by thousands of polls of one address.
+constexpr uint32_t kDoneReplicas = 8;
 constexpr int kRings = 2;      // 0 = best effort (default), 1 = latency critical
 constexpr uint32_t kDescBytes = 256;
 // Largest byte extent of one operand.  Tile bodies address tensors through
@@ -255,7 +259,9 @@ struct KArgs {
   DevCtl* dctl;                   // device control block
   uint64_t* dends[kRings];        // device copy of ends[], 2 * ring_slots
                                   // entries indexed by (seq - 1) mod 2*slots
-  uint64_t* done_id[kRings];      // device: last completed sequence per slot
+  uint64_t* done_id[kRings];      // device: last completed sequence per slot,
+                                  // kDoneReplicas copies (copy k of slot s
+                                  // at k * slots + s)
   uint32_t* tiles_done[kRings];   // device: kSubCounters x ring_slots tile
                                   // counters, sub-counter s of slot at
                                   // [s * ring_slots + slot]

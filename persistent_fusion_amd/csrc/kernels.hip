@@ -54,6 +54,7 @@ struct Cached {
   lds_u32* slot;   // 64 dwords
   uint32_t deps_ok;
   lds_f32* scr;    // the wave's tile scratch (kWaveScratch floats)
+  uint32_t rep;    // which copy of the completion words this wave polls
   __device__ __forceinline__ SDesc desc() const { return SDesc{slot}; }
 };
 
@@ -190,7 +191,7 @@ __device__ __forceinline__ void wait_deps(const KArgs& a, const Cached& c) {
     const uint32_t delta = d(i < 8 ? 8 + i : 54 + (i - 8));
     if (delta) {
       const uint64_t dep = c.seq - delta;
-      const uint64_t* w = &a.done_id[RING][slot_of(dep, mask)];
+      const uint64_t* w = &a.done_id[RING][(uint64_t)c.rep * (mask + 1) + slot_of(dep, mask)];
       while (bcast64(ld_rlx_agent(w)) < dep) __builtin_amdgcn_s_sleep(1);
     }
   }
@@ -243,7 +244,8 @@ __device__ __forceinline__ void finish_tile(const KArgs& a, const Cached& c, uin
   if (complete) {
     // every tile's stores were acknowledged before its count: publish at once
     const uint64_t t_done = now_ticks();
-    st_rlx_agent(&a.done_id[RING][slot], c.seq);
+#pragma unroll
+    for (uint32_t k = 0; k < kDoneReplicas; ++k) st_rlx_agent(&a.done_id[RING][(uint64_t)k * cap + slot], c.seq);
     if (a.trace[RING]) {
       TraceRec* tr = &a.trace[RING][slot];
       st_rlx_agent(&tr->seq, c.seq);
@@ -381,7 +383,7 @@ __device__ __forceinline__ void service_lc(const KArgs& a, const AvailLine* line
 __device__ __forceinline__ void lc_loop(const KArgs& a, uint32_t w, lds_u32* slot1, lds_f32* scr) {
   const AvailLine* line0 = &a.dctl->avail[0][w % kReplicas];
   const AvailLine* line1 = &a.dctl->avail[1][w % kReplicas];
-  Cached c1{0, 0, 0, slot1, 0, scr};
+  Cached c1{0, 0, 0, slot1, 0, scr, w % kDoneReplicas};
   uint64_t seen = 0;
   for (;;) {
     service_lc(a, line1, c1, seen);
@@ -395,7 +397,7 @@ __device__ __forceinline__ void lc_loop(const KArgs& a, uint32_t w, lds_u32* slo
 // A best-effort wave: runs its round-robin share of the ring-0 tickets.
 __device__ __forceinline__ void worker_loop(const KArgs& a, uint32_t w, lds_u32* slot0, lds_f32* scr) {
   const AvailLine* line0 = &a.dctl->avail[0][w % kReplicas];
-  Cached c0{0, 0, 0, slot0, 0, scr};
+  Cached c0{0, 0, 0, slot0, 0, scr, w % kDoneReplicas};
   uint64_t avail = 0, avail_ops = 0, copied = 0;
   uint32_t idle = 0;
   // tickets are dealt round-robin: this wave owns those = w (mod workers),

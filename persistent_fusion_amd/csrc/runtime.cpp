@@ -670,9 +670,12 @@ void set_tiling(const gpuos_config& cfg, uint32_t workers, DevDesc& d) {
     }
     case GPUOS_OP_GEMV:
     case OP_GEMV_ADD: {
+      // at least 2 rows per tile: a short GEMV (batch-1 projections) then
+      // spends half as many waves, completion counts and dependency polls
+      // on the same work, which measured faster
       const uint32_t M = (uint32_t)d.p.aux[0];
       uint32_t r = ceil_div(M, std::max<uint32_t>(1, workers));
-      r = std::min<uint32_t>(std::max<uint32_t>(r, 1), 16);
+      r = std::min<uint32_t>(std::max<uint32_t>(r, 2), 16);
       d.tile = r;
       d.ntiles = ceil_div(M, r);
       break;
@@ -1651,7 +1654,7 @@ int gpuos_create(int device, const gpuos_config* cfg_in, gpuos_ctx** out) {
     for (int r = 0; r < kRings && !rc; ++r) {
       rc = dalloc((void**)&c->ddesc[r], (size_t)c->cap * sizeof(DevDesc));
       if (!rc) rc = dalloc((void**)&c->dends[r], (size_t)2 * c->cap * sizeof(uint64_t));
-      if (!rc) rc = dalloc((void**)&c->done_id[r], (size_t)c->cap * sizeof(uint64_t));
+      if (!rc) rc = dalloc((void**)&c->done_id[r], (size_t)c->cap * kDoneReplicas * sizeof(uint64_t));
       if (!rc) rc = dalloc((void**)&c->tiles_done[r], (size_t)kSubCounters * c->cap * sizeof(uint32_t));
       if (!rc) rc = dalloc((void**)&c->subs_done[r], (size_t)c->cap * sizeof(uint32_t));
       if (!rc && cfg.trace == 1) rc = dalloc((void**)&c->trace[r], (size_t)c->cap * sizeof(TraceRec));
@@ -1669,7 +1672,8 @@ int gpuos_create(int device, const gpuos_config* cfg_in, gpuos_ctx** out) {
       for (int r = 0; r < kRings && e == hipSuccess; ++r) {
         e = hipMemsetAsync(c->dends[r], 0, (size_t)2 * c->cap * sizeof(uint64_t), c->stream);
         if (e == hipSuccess) e = hipMemsetAsync(c->ddesc[r], 0, (size_t)c->cap * sizeof(DevDesc), c->stream);
-        if (e == hipSuccess) e = hipMemsetAsync(c->done_id[r], 0, (size_t)c->cap * 8, c->stream);
+        if (e == hipSuccess)
+          e = hipMemsetAsync(c->done_id[r], 0, (size_t)c->cap * kDoneReplicas * 8, c->stream);
         if (e == hipSuccess)
           e = hipMemsetAsync(c->tiles_done[r], 0, (size_t)kSubCounters * c->cap * 4, c->stream);
         if (e == hipSuccess) e = hipMemsetAsync(c->subs_done[r], 0, (size_t)c->cap * 4, c->stream);
