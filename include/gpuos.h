@@ -43,7 +43,7 @@
 extern "C" {
 #endif
 
-#define GPUOS_ABI_VERSION 1
+#define GPUOS_ABI_VERSION 2
 
 /* Status codes. */
 typedef enum gpuos_status {
@@ -124,10 +124,18 @@ typedef enum gpuos_opcode {
   GPUOS_OP_COUNT = 17
 } gpuos_opcode;
 
+/*
+ * Element types.  BF16 and F16 operands are widened exactly to fp32, computed
+ * in fp32 and rounded back with round-to-nearest-even.  F16 is accepted by
+ * COPY, ADD, MUL, SCALE, RELU, EXP, SILU_MUL, ROW_SUM, ROW_SOFTMAX, RMSNORM
+ * and ROPE.  I32 is accepted by COPY and GATHER (bit moves) and by ADD, MUL
+ * (two's-complement, wrapping modulo 2^32) and RELU (x > 0 ? x : 0).
+ */
 typedef enum gpuos_dtype {
   GPUOS_F32 = 0,
   GPUOS_BF16 = 1,
-  GPUOS_I32 = 2 /* COPY and GATHER only (bit moves) */
+  GPUOS_I32 = 2,
+  GPUOS_F16 = 3
 } gpuos_dtype;
 
 /* Op flags. */
@@ -289,6 +297,40 @@ int gpuos_create(int device, const gpuos_config* cfg, gpuos_ctx** out);
  */
 int gpuos_submit(gpuos_ctx* ctx, const gpuos_op* ops, uint32_t n,
                  uint64_t* ids_out);
+
+/*
+ * A strided or broadcast view of an elementwise op's operands (the "generic
+ * tensor abstraction" of arbitrary shapes, strides and broadcasting in the
+ * GPUOS page, section "The Paper").  With a view, element (i0, .., i{d-1})
+ * of the op's index space, shape[0] x .. x shape[ndim-1] (outermost first,
+ * product = n), is
+ *   out[sum_k i_k stride[0][k]] = f(in0[sum_k i_k stride[1][k]],
+ *                                   in1[sum_k i_k stride[2][k]])
+ * with strides in elements.  Input strides are >= 0 (0 broadcasts the input
+ * along that dimension); output strides are >= 0 and must address every
+ * element of the index space at a distinct position (checked).  src_len must
+ * be 0.  ndim = 0 means no view (the plain contiguous op).
+ */
+typedef struct gpuos_view {
+  uint32_t ndim;        /* 0..4 */
+  uint32_t _reserved;   /* must be 0 */
+  uint64_t shape[4];
+  int64_t stride[3][4]; /* [0] out, [1] in[0], [2] in[1] */
+} gpuos_view;
+
+/*
+ * gpuos_submit with views: views[i] (nullable array; NULL = no op has a
+ * view) describes op i's index space and strides.  Views are accepted by
+ * COPY, ADD, MUL, SCALE, RELU, EXP and SILU_MUL in every dtype those ops
+ * take; an op with a view is never fused.  The byte ranges used for hazard
+ * tracking cover each operand from its pointer to its largest offset.
+ * Errors: as gpuos_submit, plus EINVAL for a malformed view (ndim > 4, an
+ * extent product other than n, a negative stride, an output that addresses
+ * an element twice, an operand past 0xFFF00000 bytes, or an output that
+ * overlaps an input without being exactly that input under the same view).
+ */
+int gpuos_submit_views(gpuos_ctx* ctx, const gpuos_op* ops, const gpuos_view* views,
+                       uint32_t n, uint64_t* ids_out);
 
 /*
  * Runs the fusion pass over the staged ops, writes the resulting device

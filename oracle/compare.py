@@ -11,9 +11,10 @@ Matching rule:
   have the same class (NaN, +inf, -inf, finite) and finite values must satisfy
   ``|g - o| <= max(rtol * max(|o|, s), 2 * u)`` where ``s`` is the oracle's
   error scale for the element (sum of |terms| for sums and dot products),
-  ``rtol`` is 1e-5 for fp32 outputs and 1e-2 for bf16 outputs, and ``u`` is
-  the spacing of the output type's subnormal numbers (2**-149 for fp32,
-  2**-133 for bf16).  Below the normal range a format keeps a fixed absolute
+  ``rtol`` is 1e-5 for fp32 outputs, 1e-2 for bf16 and 2e-3 for fp16 (two
+  units in the last place of an 11-bit significand), and ``u`` is the
+  spacing of the output type's subnormal numbers (2**-149 for fp32, 2**-133
+  for bf16, 2**-24 for fp16).  Below the normal range a format keeps a fixed absolute
   spacing and ever fewer significant bits, so no relative bound is reachable
   there; a result within two subnormal steps of the exact value is accepted.
 """
@@ -27,9 +28,9 @@ import numpy as np
 
 from .interpreter import bf16_to_f32
 
-RTOL = {"f32": 1e-5, "bf16": 1e-2}
+RTOL = {"f32": 1e-5, "bf16": 1e-2, "f16": 2e-3}
 # spacing of the subnormal numbers of each output type
-SUBNORMAL_STEP = {"f32": 2.0 ** -149, "bf16": 2.0 ** -133}
+SUBNORMAL_STEP = {"f32": 2.0 ** -149, "bf16": 2.0 ** -133, "f16": 2.0 ** -24}
 
 
 @dataclass
@@ -82,8 +83,9 @@ def compare(got: np.ndarray, want: np.ndarray, dtype: str,
         if dtype == "i32":
             bad[ex] = got[ex] != want[ex]
         else:
-            g = got.view(np.uint16 if dtype == "bf16" else np.uint32)[ex]
-            w = want.view(np.uint16 if dtype == "bf16" else np.uint32)[ex]
+            bits = np.uint16 if dtype in ("bf16", "f16") else np.uint32
+            g = got.view(bits)[ex]
+            w = want.view(bits)[ex]
             gf = _as_f32(got[ex], dtype)
             wf = _as_f32(want[ex], dtype)
             both_nan = np.isnan(gf) & np.isnan(wf)

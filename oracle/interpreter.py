@@ -31,6 +31,18 @@ round-to-nearest-even narrowing to bf16):
   ``y_{i+h/2} = x_{i+h/2} c_i + x_i s_i``.
 * A data operand whose readable length is shorter than the op's extent is read
   cyclically (index ``k mod len``); a longer one is read as a prefix.
+* fp16 operands are widened exactly to fp32 and every fp16 result is the fp32
+  result rounded to fp16 with round-to-nearest-even (numpy's float32 ->
+  float16 conversion, which is that IEEE rounding).
+* int32 ADD and MUL are two's-complement and wrap modulo 2^32 (the exact
+  integer result reduced mod 2^32); int32 RELU is ``x > 0 ? x : 0``.
+* An elementwise op with a view (the generic tensor abstraction of arbitrary
+  shapes, strides and broadcasting in "GPUOS: A GPU Operating System
+  Primitive for Transparent Operation Fusion", section "The Paper") applies
+  the same per-element definition at every index (i0, .., i{d-1}) of its
+  shape, reading operand k at element ``sum_j i_j * stride[k][j]`` from the
+  operand's start and writing the output there; all inputs are read before
+  the output is written.
 
 ``run`` also returns, for every element written by a reduction or a
 transcendental, the error scale the tolerance test uses: the sum of absolute
@@ -79,13 +91,21 @@ def f32_to_bf16(x: np.ndarray) -> np.ndarray:
 def _to_f32(arr: np.ndarray, dtype: str) -> np.ndarray:
     if dtype == "bf16":
         return bf16_to_f32(arr)
-    return np.asarray(arr, dtype=np.float32)
+    return np.asarray(arr, dtype=np.float32)  # fp16 widens exactly
 
 
 def _store_from_f32(vals32: np.ndarray, dtype: str) -> np.ndarray:
     if dtype == "bf16":
         return f32_to_bf16(vals32)
+    if dtype == "f16":
+        with np.errstate(over="ignore"):
+            return np.asarray(vals32, dtype=np.float32).astype(np.float16)
     return np.asarray(vals32, dtype=np.float32)
+
+
+def _wrap_i32(v: np.ndarray) -> np.ndarray:
+    """The exact integer values reduced modulo 2^32, as int32."""
+    return (np.asarray(v, dtype=np.int64) & np.int64(0xFFFFFFFF)).astype(np.uint32).view(np.int32)
 
 
 def _store_from_f64(vals64: np.ndarray, dtype: str) -> np.ndarray:
@@ -129,6 +149,84 @@ def _write(bufs: Dict[str, np.ndarray], ref: Ref, vals: np.ndarray) -> None:
 
 
 # ----------------------------------------------------------------------------
+# elementwise values
+
+
+def _ew_values(k: str, dt: str, alpha: float, xr: np.ndarray, yr: Optional[np.ndarray]):
+    """Stored values of elementwise op ``k`` on raw operands xr (and yr), and
+    the error scale (None for the exact class)."""
+    if dt == "i32":
+        x = np.asarray(xr, dtype=np.int64)
+        if k == "add":
+            return _wrap_i32(x + np.asarray(yr, dtype=np.int64)), None
+        if k == "mul":
+            return _wrap_i32(x * np.asarray(yr, dtype=np.int64)), None
+        if k == "relu":
+            return np.where(x > 0, x, 0).astype(np.int32), None
+        raise OracleError(f"{k} is not defined for int32")
+    x = _to_f32(xr, dt)
+    y = _to_f32(yr, dt) if yr is not None else None
+    if k == "add":
+        r32 = x + y
+    elif k == "mul":
+        r32 = x * y
+    elif k == "scale":
+        r32 = np.float32(alpha) * x
+    elif k == "relu":
+        r32 = np.where(x > np.float32(0.0), x, np.float32(0.0)).astype(np.float32)
+    elif k == "exp":
+        with np.errstate(over="ignore"):
+            r64 = np.exp(x.astype(np.float64))
+        return _store_from_f64(r64, dt), np.abs(r64)
+    else:  # silu_mul: g / (1 + exp(-g)) * u in fp64
+        g = x.astype(np.float64)
+        u = y.astype(np.float64)
+        with np.errstate(over="ignore", invalid="ignore"):
+            r64 = g / (1.0 + np.exp(-g)) * u
+        return _store_from_f64(r64, dt), np.abs(r64)
+    return _store_from_f32(r32.astype(np.float32), dt), None
+
+
+def view_offsets(shape, strides) -> np.ndarray:
+    """Element offsets sum_j i_j * strides[j] of every index of ``shape``, in
+    row-major index order."""
+    idx = np.indices(tuple(shape), dtype=np.int64).reshape(len(shape), -1)
+    return (idx * np.asarray(strides, dtype=np.int64)[:, None]).sum(axis=0)
+
+
+def _apply_view(op: Op, bufs: Dict[str, np.ndarray]) -> Optional[np.ndarray]:
+    """An elementwise op over a view: op.view = (shape, out strides, in0
+    strides, in1 strides)."""
+    shape, so, s0, s1 = op.view
+    k = op.kind
+    if k not in ("copy", "add", "mul", "scale", "relu", "exp", "silu_mul"):
+        raise OracleError(f"views are not defined for {k}")
+    if int(np.prod(shape)) != op.n:
+        raise OracleError("view extents do not multiply to n")
+
+    def gather(ref: Ref, strides) -> np.ndarray:
+        off = ref.off + view_offsets(shape, strides)
+        if off.size and off.max() >= bufs[ref.buf].shape[0]:
+            raise OracleError(f"view of {ref} overruns its buffer")
+        return bufs[ref.buf][off].copy()
+
+    xr = gather(op.ins[0], s0)
+    if k == "copy":
+        vals, scale = xr, None
+    else:
+        yr = gather(op.ins[1], s1) if k in ("add", "mul", "silu_mul") else None
+        vals, scale = _ew_values(k, op.dtype, op.alpha, xr, yr)
+    out_off = op.out.off + view_offsets(shape, so)
+    dst = bufs[op.out.buf]
+    if out_off.size and out_off.max() >= dst.shape[0]:
+        raise OracleError("view output overruns its buffer")
+    if np.unique(out_off).size != out_off.size:
+        raise OracleError("view output addresses an element twice")
+    dst[out_off] = vals.astype(dst.dtype, copy=False)
+    return scale
+
+
+# ----------------------------------------------------------------------------
 # one op
 
 
@@ -139,6 +237,14 @@ def out_len(op: Op) -> int:
     if op.kind == "row_sum":
         return op.rows
     return op.n
+
+
+def out_positions(op: Op) -> np.ndarray:
+    """Element indices (in the output buffer) an op writes, in the order of
+    its results."""
+    if getattr(op, "view", None) is not None:
+        return op.out.off + view_offsets(op.view[0], op.view[1])
+    return np.arange(op.out.off, op.out.off + out_len(op), dtype=np.int64)
 
 
 def apply_op(op: Op, bufs: Dict[str, np.ndarray], dtypes: Dict[str, str]) -> Optional[np.ndarray]:
@@ -152,6 +258,9 @@ def apply_op(op: Op, bufs: Dict[str, np.ndarray], dtypes: Dict[str, str]) -> Opt
     n = op.n
     if k in ("nop", "spin"):
         return None
+
+    if getattr(op, "view", None) is not None:
+        return _apply_view(op, bufs)
 
     if k == "copy":
         _write(bufs, op.out, _read_cyclic(bufs, op.ins[0], op.src_len[0], n))
@@ -167,32 +276,11 @@ def apply_op(op: Op, bufs: Dict[str, np.ndarray], dtypes: Dict[str, str]) -> Opt
         return None
 
     if k in ("add", "mul", "scale", "relu", "exp", "silu_mul"):
-        x = _to_f32(_read_cyclic(bufs, op.ins[0], op.src_len[0], n), dt)
-        if k in ("add", "mul", "silu_mul"):
-            y = _to_f32(_read_cyclic(bufs, op.ins[1], op.src_len[1], n), dt)
-        if k == "add":
-            r32 = x + y
-        elif k == "mul":
-            r32 = x * y
-        elif k == "scale":
-            r32 = np.float32(op.alpha) * x
-        elif k == "relu":
-            r32 = np.where(x > np.float32(0.0), x, np.float32(0.0)).astype(np.float32)
-        elif k == "exp":
-            with np.errstate(over="ignore"):
-                r64 = np.exp(x.astype(np.float64))
-            vals = _store_from_f64(r64, dt)
-            _write(bufs, op.out, vals)
-            return np.abs(r64)
-        else:  # silu_mul: g / (1 + exp(-g)) * u in fp64
-            g = x.astype(np.float64)
-            u = y.astype(np.float64)
-            with np.errstate(over="ignore", invalid="ignore"):
-                r64 = g / (1.0 + np.exp(-g)) * u
-            _write(bufs, op.out, _store_from_f64(r64, dt))
-            return np.abs(r64)
-        _write(bufs, op.out, _store_from_f32(r32.astype(np.float32), dt))
-        return None
+        xr = _read_cyclic(bufs, op.ins[0], op.src_len[0], n)
+        yr = _read_cyclic(bufs, op.ins[1], op.src_len[1], n) if k in ("add", "mul", "silu_mul") else None
+        vals, scale = _ew_values(k, dt, op.alpha, xr, yr)
+        _write(bufs, op.out, vals)
+        return scale
 
     if k in ("row_sum", "row_softmax", "rmsnorm"):
         rows, L = op.rows, op.row_len
@@ -299,8 +387,7 @@ def run(wl: Workload, upto: Optional[int] = None, scales: bool = False,
         name = op.out.buf
         if name not in sc:
             sc[name] = np.full(bufs[name].shape[0], np.nan)
-        cnt = out_len(op)
-        sc[name][op.out.off:op.out.off + cnt] = np.nan if s is None else s
+        sc[name][out_positions(op)] = np.nan if s is None else s
     if scales:
         return bufs, sc
     return bufs
@@ -321,18 +408,17 @@ def local_check(wl: Workload, gpu: Dict[str, np.ndarray], compare_fn, only=None)
     state = {k: v.copy() for k, v in wl.buffers.items()}
     bad = []
     for i, op in enumerate(wl.ops):
-        cnt = out_len(op)
-        if cnt == 0:
+        if out_len(op) == 0:
             continue
-        name, off = op.out.buf, op.out.off
+        name, pos = op.out.buf, out_positions(op)
         if only is not None and i not in only:
-            state[name][off:off + cnt] = gpu[name][off:off + cnt]
+            state[name][pos] = gpu[name][pos]
             continue
         s = apply_op(op, state, wl.dtypes)
-        want = state[name][off:off + cnt].copy()
-        got = gpu[name][off:off + cnt]
+        want = state[name][pos].copy()
+        got = gpu[name][pos]
         r = compare_fn(got, want, wl.dtypes[name], s)
         if not r.ok:
             bad.append((i, name, r))
-        state[name][off:off + cnt] = got
+        state[name][pos] = got
     return bad

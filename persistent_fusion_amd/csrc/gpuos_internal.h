@@ -75,6 +75,9 @@ constexpr int kMaxSteps = 8;
 // (GEMV weights) has no queued writer, so the kernel may read it before the
 // op's dependencies have completed.
 constexpr uint8_t DF_AUX_READY = 0x80;
+// Descriptor flag set by the runtime: an elementwise op over a strided or
+// broadcast view (shape and strides in the descriptor's view fields).
+constexpr uint8_t DF_VIEW = 0x40;
 constexpr int kMaxDeps = 14;  // dependencies a descriptor carries (more: wait
                               // for the retire cursor instead)
 constexpr int kMaxFusedInputs = 4;
@@ -114,7 +117,11 @@ struct alignas(16) DevDesc {
       float alpha;          // 28
       float eps;            // 29
       int32_t aux[4];       // 30-33
-      uint8_t _pad[80];
+      // DF_VIEW: 4 dimensions, outermost first (leading extents of 1), and
+      // element strides of out, in0, in1 per dimension
+      uint32_t vshape[4];   // 34-37
+      int32_t vstride[3][4];  // 38-49
+      uint8_t _pad[16];
     } p;
     struct {
       uint64_t W;           // 18-19: GEMV weights [M x K] bf16
@@ -170,6 +177,8 @@ static_assert(offsetof(DevDesc, p.ptr) == 18 * 4, "ptr at dword 18");
 static_assert(offsetof(DevDesc, p.src_len) == 26 * 4, "src_len at dword 26");
 static_assert(offsetof(DevDesc, p.alpha) == 28 * 4, "alpha at dword 28");
 static_assert(offsetof(DevDesc, p.aux) == 30 * 4, "aux at dword 30");
+static_assert(offsetof(DevDesc, p.vshape) == 34 * 4 && offsetof(DevDesc, p.vstride) == 38 * 4,
+              "view fields at dwords 34-49");
 static_assert(offsetof(DevDesc, f.out) == 26 * 4, "fused out at dword 26");
 static_assert(offsetof(DevDesc, ng.M) == 30 * 4, "norm-GEMV M at dword 30");
 static_assert(offsetof(DevDesc, ng.q) == 34 * 4 && offsetof(DevDesc, ng.hd) == 44 * 4,

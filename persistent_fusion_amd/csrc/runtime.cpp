@@ -67,7 +67,7 @@ inline void cpu_relax() {
 #endif
 }
 
-uint32_t elem_size(uint32_t dt) { return dt == GPUOS_BF16 ? 2u : 4u; }
+uint32_t elem_size(uint32_t dt) { return dt == GPUOS_BF16 || dt == GPUOS_F16 ? 2u : 4u; }
 
 bool is_elementwise(uint32_t op) {
   switch (op) {
@@ -164,12 +164,27 @@ struct OpRanges {
   int nr = 0;
 };
 
+// An elementwise op's view after normalisation (gpuos_view): dimensions of
+// extent 1 dropped, adjacent dimensions merged wherever every operand's
+// strides allow, then padded to 4 with leading extents of 1.  on = 0: no view.
+struct ViewDesc {
+  uint32_t on = 0;
+  uint32_t shape[4] = {1, 1, 1, 1};
+  uint32_t stride[3][4] = {};  // elements: out, in0, in1
+  // largest element offset of operand k
+  uint64_t max_off(int k) const {
+    uint64_t m = 0;
+    for (int d = 0; d < 4; ++d) m += (uint64_t)(shape[d] - 1) * stride[k][d];
+    return m;
+  }
+};
+
 uint64_t src_extent(uint64_t src_len, uint64_t extent) {
   if (src_len == 0 || src_len >= extent) return extent;
   return src_len;
 }
 
-OpRanges op_ranges(const gpuos_op& o) {
+OpRanges op_ranges(const gpuos_op& o, const ViewDesc* v = nullptr) {
   OpRanges R;
   const uint64_t es = elem_size(o.dtype);
   auto rd = [&](const void* p, uint64_t bytes) {
@@ -179,6 +194,12 @@ OpRanges op_ranges(const gpuos_op& o) {
     if (p && bytes) R.w = Range{(uint64_t)p, (uint64_t)p + bytes};
   };
   const uint64_t n = o.n;
+  if (v && v->on) {  // each operand from its pointer to its largest offset
+    wr(o.out, (v->max_off(0) + 1) * es);
+    rd(o.in[0], (v->max_off(1) + 1) * es);
+    if (is_binary(o.opcode)) rd(o.in[1], (v->max_off(2) + 1) * es);
+    return R;
+  }
   switch (o.opcode) {
     case GPUOS_OP_COPY: case GPUOS_OP_ADD: case GPUOS_OP_MUL: case GPUOS_OP_SCALE:
     case GPUOS_OP_RELU: case GPUOS_OP_EXP: case GPUOS_OP_SILU_MUL:
@@ -244,10 +265,14 @@ bool overlaps(const Range& a, const Range& b) {
 int validate(const gpuos_op& o, uint32_t index) {
   const uint32_t op = o.opcode;
   if (op >= GPUOS_OP_COUNT) return fail(GPUOS_EINVAL, "op %u: unknown opcode %u", index, op);
-  if (o.dtype > GPUOS_I32) return fail(GPUOS_EINVAL, "op %u: unknown dtype %u", index, o.dtype);
+  if (o.dtype > GPUOS_F16) return fail(GPUOS_EINVAL, "op %u: unknown dtype %u", index, o.dtype);
   if (o.flags & ~0x7u) return fail(GPUOS_EINVAL, "op %u: unknown flag bits 0x%x", index, o.flags);
-  if (o.dtype == GPUOS_I32 && op != GPUOS_OP_COPY && op != GPUOS_OP_GATHER)
-    return fail(GPUOS_EINVAL, "op %u: int32 is only for COPY and GATHER", index);
+  if (o.dtype == GPUOS_I32 && op != GPUOS_OP_COPY && op != GPUOS_OP_GATHER && op != GPUOS_OP_ADD &&
+      op != GPUOS_OP_MUL && op != GPUOS_OP_RELU)
+    return fail(GPUOS_EINVAL, "op %u: int32 is only for COPY, GATHER, ADD, MUL and RELU", index);
+  if (o.dtype == GPUOS_F16 &&
+      (op == GPUOS_OP_GATHER || op == GPUOS_OP_GEMV || op == GPUOS_OP_ATTN_SCORE || op == GPUOS_OP_ATTN_AV))
+    return fail(GPUOS_EINVAL, "op %u: fp16 is not available for this opcode", index);
   const uint64_t es = elem_size(o.dtype);
   auto need = [&](const void* p, const char* what) -> int {
     if (!p) return fail(GPUOS_EINVAL, "op %u: %s pointer is null", index, what);
@@ -328,6 +353,95 @@ int validate(const gpuos_op& o, uint32_t index) {
   for (int q = 0; q < R.nr; ++q)
     if (R.r[q].hi - R.r[q].lo > kMaxExtentBytes)
       return fail(GPUOS_EINVAL, "op %u: an operand spans more than 4 GiB - 1 MiB", index);
+  return 0;
+}
+
+// Checks op `index`'s view and normalises it into `out` (out.on = 0 when the
+// view is plain contiguous indexing); see gpuos_view.
+int normalize_view(const gpuos_op& o, const gpuos_view& v, uint32_t index, ViewDesc& out) {
+  out = ViewDesc{};
+  if (v.ndim == 0) return 0;
+  const uint32_t op = o.opcode;
+  if (!is_elementwise(op) || op == GPUOS_OP_GATHER)
+    return fail(GPUOS_EINVAL, "op %u: views are only for COPY, ADD, MUL, SCALE, RELU, EXP, SILU_MUL", index);
+  if (v.ndim > 4 || v._reserved) return fail(GPUOS_EINVAL, "op %u: malformed view", index);
+  if (o.src_len[0] || o.src_len[1]) return fail(GPUOS_EINVAL, "op %u: an op with a view takes no src_len", index);
+  const bool bin = is_binary(op);
+  const int nk = bin ? 3 : 2;
+  struct Dim {
+    uint64_t ext;
+    int64_t st[3];
+  };
+  Dim dims[4];
+  int nd = 0;
+  uint64_t prod = 1;
+  for (uint32_t d = 0; d < v.ndim; ++d) {
+    const uint64_t ext = v.shape[d];
+    if (ext == 0 || ext > (1ull << 30)) return fail(GPUOS_EINVAL, "op %u: view extent %llu", index, (unsigned long long)ext);
+    prod *= ext;
+    if (prod > (1ull << 30)) return fail(GPUOS_EINVAL, "op %u: view extents exceed 2^30 elements", index);
+    for (int k = 0; k < nk; ++k)
+      if (v.stride[k][d] < 0 || v.stride[k][d] > 0x7fffffff)
+        return fail(GPUOS_EINVAL, "op %u: view stride out of range", index);
+    if (ext > 1) dims[nd++] = Dim{ext, {v.stride[0][d], v.stride[1][d], bin ? v.stride[2][d] : 0}};
+  }
+  if (prod != o.n)
+    return fail(GPUOS_EINVAL, "op %u: view extents multiply to %llu, not n = %u", index, (unsigned long long)prod, o.n);
+  // merge a dimension into the next inner one wherever every operand steps
+  // over the inner one contiguously
+  Dim m[4];
+  int nm = 0;
+  for (int d = nd - 1; d >= 0; --d) {
+    if (nm > 0) {
+      Dim& in = m[nm - 1];
+      bool ok = true;
+      for (int k = 0; k < 3; ++k) ok = ok && dims[d].st[k] == in.st[k] * (int64_t)in.ext;
+      if (ok) {
+        in.ext *= dims[d].ext;
+        continue;
+      }
+    }
+    m[nm++] = dims[d];  // m is innermost first
+  }
+  const uint64_t es = elem_size(o.dtype);
+  uint64_t maxoff[3] = {0, 0, 0};
+  for (int k = 0; k < nk; ++k) {
+    for (int i = 0; i < nm; ++i) maxoff[k] += (m[i].ext - 1) * (uint64_t)m[i].st[k];
+    if ((maxoff[k] + 1) * es > kMaxExtentBytes)
+      return fail(GPUOS_EINVAL, "op %u: a view operand spans more than 4 GiB - 1 MiB", index);
+  }
+  // the output must address each element once: ordered by stride, every
+  // stride must exceed the span of the smaller ones
+  {
+    int order[4];
+    for (int i = 0; i < nm; ++i) order[i] = i;
+    std::sort(order, order + nm, [&](int x, int y) { return m[x].st[0] < m[y].st[0]; });
+    uint64_t span = 0;
+    for (int i = 0; i < nm; ++i) {
+      const Dim& dm = m[order[i]];
+      if (dm.st[0] == 0 || (uint64_t)dm.st[0] <= span)
+        return fail(GPUOS_EINVAL, "op %u: the view's output addresses an element twice", index);
+      span += (dm.ext - 1) * (uint64_t)dm.st[0];
+    }
+  }
+  // an output overlapping an input must be that input under the same view
+  const Range ro{(uint64_t)o.out, (uint64_t)o.out + (maxoff[0] + 1) * es};
+  for (int k = 1; k < nk; ++k) {
+    const Range rk{(uint64_t)o.in[k - 1], (uint64_t)o.in[k - 1] + (maxoff[k] + 1) * es};
+    if (!overlaps(ro, rk)) continue;
+    bool same = o.in[k - 1] == o.out;
+    for (int i = 0; i < nm && same; ++i) same = m[i].st[k] == m[i].st[0];
+    if (!same) return fail(GPUOS_EINVAL, "op %u: the output overlaps input %d under a different view", index, k - 1);
+  }
+  bool plain = nm <= 1;
+  for (int i = 0; i < nm && plain; ++i)
+    for (int k = 0; k < nk; ++k) plain = plain && m[i].st[k] == 1;
+  if (plain) return 0;  // contiguous after all
+  out.on = 1;
+  for (int i = 0; i < nm; ++i) {  // innermost is dimension 3
+    out.shape[3 - i] = (uint32_t)m[i].ext;
+    for (int k = 0; k < 3; ++k) out.stride[k][3 - i] = (uint32_t)m[i].st[k];
+  }
   return 0;
 }
 
@@ -509,6 +623,7 @@ struct Staged {
   uint64_t id;
   uint32_t ring;
   DepVec deps;  // user ids
+  ViewDesc view;
 };
 
 // A device op after the fusion pass: one descriptor built from user ops
@@ -844,7 +959,7 @@ bool try_extend(const gpuos_op& o, ChainState& st, uint8_t& code, uint8_t& fl) {
 // Streams (non-temporal) elementwise, COPY and fused descriptors whose
 // operands total at least stream_min_kib.
 void mark_streaming(const gpuos_config& cfg, DevDesc& d) {
-  if (cfg.stream_min_kib == 0xFFFFFFFFu) return;
+  if (cfg.stream_min_kib == 0xFFFFFFFFu || (d.flags & DF_VIEW)) return;
   const uint64_t es = elem_size(d.dtype);
   uint64_t bytes = 0;
   if (d.opcode == OP_FUSED_EW) {
@@ -863,10 +978,26 @@ void mark_streaming(const gpuos_config& cfg, DevDesc& d) {
   if (bytes >= (uint64_t)cfg.stream_min_kib * 1024) d.flags |= GPUOS_FLAG_NONTEMPORAL;
 }
 
+// Adds an elementwise op's view to its descriptor: rows of shape[3]
+// elements, about 1,024 elements per tile, spread over the workers.
+void encode_view(const ViewDesc& v, uint32_t workers, DevDesc& d) {
+  d.flags = (uint8_t)((d.flags | DF_VIEW) & ~GPUOS_FLAG_NONTEMPORAL);
+  for (int j = 0; j < 4; ++j) {
+    d.p.vshape[j] = v.shape[j];
+    for (int k = 0; k < 3; ++k) d.p.vstride[k][j] = (int32_t)v.stride[k][j];
+  }
+  const uint64_t rows = (uint64_t)v.shape[0] * v.shape[1] * v.shape[2], L = v.shape[3];
+  uint64_t nt = std::max<uint64_t>(1, (rows * L + 1023) / 1024);
+  nt = std::min<uint64_t>(nt, std::max<uint32_t>(1, workers));
+  nt = std::min<uint64_t>(nt, rows);
+  d.tile = (uint32_t)((rows + nt - 1) / nt);
+  d.ntiles = (uint32_t)((rows + d.tile - 1) / d.tile);
+}
+
 // Is output range `w` of staged op `from` - 1 read by any op staged after it?
 bool read_later(gpuos_ctx* c, size_t from, const Range& w) {
   for (size_t k = from; k < c->staged.size(); ++k) {
-    const OpRanges R = op_ranges(c->staged[k].op);
+    const OpRanges R = op_ranges(c->staged[k].op, &c->staged[k].view);
     for (int q = 0; q < R.nr; ++q)
       if (overlaps(R.r[q], w)) return true;
   }
@@ -906,7 +1037,7 @@ uint32_t try_norm_gemv(gpuos_ctx* c, size_t i, size_t end, DevDesc& d) {
     const Staged& sc = c->staged[i + 2];
     const gpuos_op& C = sc.op;
     const uint32_t f = M / 2;
-    if (C.opcode == GPUOS_OP_SILU_MUL && C.dtype == GPUOS_BF16 && sc.ring == sa.ring &&
+    if (C.opcode == GPUOS_OP_SILU_MUL && C.dtype == GPUOS_BF16 && sc.ring == sa.ring && !sc.view.on &&
         M % 2 == 0 && C.n == f && (uint64_t)C.in[0] == y && (uint64_t)C.in[1] == y + 2ull * f &&
         (!C.src_len[0] || C.src_len[0] >= f) && (!C.src_len[1] || C.src_len[1] >= f)) {
       const Range ra{(uint64_t)C.out, (uint64_t)C.out + 2ull * f};
@@ -928,7 +1059,7 @@ uint32_t try_norm_gemv(gpuos_ctx* c, size_t i, size_t end, DevDesc& d) {
     const gpuos_op& Kr = c->staged[i + 3].op;
     const gpuos_op& Cv = c->staged[i + 4].op;
     bool ok = c->staged[i + 2].ring == sa.ring && c->staged[i + 3].ring == sa.ring &&
-              c->staged[i + 4].ring == sa.ring && Q.opcode == GPUOS_OP_ROPE &&
+              c->staged[i + 4].ring == sa.ring && !c->staged[i + 4].view.on && Q.opcode == GPUOS_OP_ROPE &&
               Kr.opcode == GPUOS_OP_ROPE && Cv.opcode == GPUOS_OP_COPY && Q.dtype == GPUOS_BF16 &&
               Kr.dtype == GPUOS_BF16 && Cv.dtype == GPUOS_BF16;
     const uint32_t H = Q.rows, h = Q.row_len, Dq = H * h;
@@ -1000,7 +1131,7 @@ uint32_t try_gemv_add(gpuos_ctx* c, size_t i, size_t end, DevDesc& d) {
   const Staged& sb = c->staged[i + 1];
   const gpuos_op& A = sa.op;
   const gpuos_op& B = sb.op;
-  if (A.opcode != GPUOS_OP_GEMV || B.opcode != GPUOS_OP_ADD || sa.ring != sb.ring) return 0;
+  if (A.opcode != GPUOS_OP_GEMV || B.opcode != GPUOS_OP_ADD || sa.ring != sb.ring || sb.view.on) return 0;
   if (A.dtype != B.dtype || (A.dtype != GPUOS_F32 && A.dtype != GPUOS_BF16)) return 0;
   const uint32_t M = (uint32_t)A.aux[0], K = (uint32_t)A.aux[1];
   if (B.n != M) return 0;
@@ -1111,9 +1242,10 @@ void plan_ops(gpuos_ctx* c, size_t begin, size_t end, std::vector<Planned>& plan
     // a chain needs a next op of the same ring, dtype and size that reads
     // this op's output
     bool chain_possible = false;
-    if (pl.count == 1 && fuse && j < end && fusable(s0.op)) {
+    if (pl.count == 1 && fuse && j < end && fusable(s0.op) && !s0.view.on) {
       const gpuos_op& nx = c->staged[j].op;
-      chain_possible = c->staged[j].ring == s0.ring && fusable(nx) && nx.dtype == s0.op.dtype &&
+      chain_possible = c->staged[j].ring == s0.ring && fusable(nx) && !c->staged[j].view.on &&
+                       nx.dtype == s0.op.dtype &&
                        nx.n == s0.op.n && (nx.in[0] == s0.op.out || nx.in[1] == s0.op.out);
     }
     if (chain_possible) {
@@ -1148,7 +1280,7 @@ void plan_ops(gpuos_ctx* c, size_t begin, size_t end, std::vector<Planned>& plan
         const uint32_t max_steps = std::min<uint32_t>(cfg.max_fuse, kMaxSteps);
         while (j < end && n_steps < max_steps) {
           const Staged& sj = c->staged[j];
-          if (sj.ring != s0.ring || !fusable(sj.op) || sj.op.dtype != o0.dtype ||
+          if (sj.ring != s0.ring || !fusable(sj.op) || sj.view.on || sj.op.dtype != o0.dtype ||
               sj.op.n != o0.n)
             break;
           ChainState trial = st;
@@ -1180,7 +1312,7 @@ void plan_ops(gpuos_ctx* c, size_t begin, size_t end, std::vector<Planned>& plan
             if (!keep) {
               const Range w{(uint64_t)os.out, (uint64_t)os.out + bytes};
               for (size_t k = j; k < c->staged.size() && !keep; ++k) {
-                const OpRanges R = op_ranges(c->staged[k].op);
+                const OpRanges R = op_ranges(c->staged[k].op, &c->staged[k].view);
                 for (int q = 0; q < R.nr; ++q)
                   if (overlaps(R.r[q], w)) keep = true;
               }
@@ -1197,6 +1329,7 @@ void plan_ops(gpuos_ctx* c, size_t begin, size_t end, std::vector<Planned>& plan
     }
     if (pl.count == 1) {
       encode_plain(s0.op, cfg, c->workers, pl.desc);
+      if (s0.view.on) encode_view(s0.view, c->workers, pl.desc);
       j = i + 1;
     }
     mark_streaming(cfg, pl.desc);
@@ -1717,16 +1850,22 @@ int gpuos_create(int device, const gpuos_config* cfg_in, gpuos_ctx** out) {
   return 0;
 }
 
-int gpuos_submit(gpuos_ctx* c, const gpuos_op* ops, uint32_t n, uint64_t* ids_out) {
+}  // extern "C"
+
+namespace {
+
+int submit_impl(gpuos_ctx* c, const gpuos_op* ops, const gpuos_view* views, uint32_t n, uint64_t* ids_out) {
   if (!c) return fail(GPUOS_EINVAL, "null context");
   if (c->stopped) return fail(GPUOS_ESTATE, "context is stopped");
   if (check_device_error(c)) return fail(GPUOS_ESTATE, "context is poisoned: %s", g_last_error.c_str());
   if (n && !ops) return fail(GPUOS_EINVAL, "ops is null");
   const uint64_t first = c->next_id;
   // validate everything before staging anything
+  std::vector<ViewDesc> vd(views ? n : 0);
   for (uint32_t i = 0; i < n; ++i) {
     int rc = validate(ops[i], i);
     if (rc) return rc;
+    if (views && (rc = normalize_view(ops[i], views[i], i, vd[i]))) return rc;
     for (int k = 0; k < 4; ++k) {
       const int64_t dv = ops[i].deps[k];
       if (dv > 0 && (uint64_t)dv >= first + i)
@@ -1757,6 +1896,7 @@ int gpuos_submit(gpuos_ctx* c, const gpuos_op* ops, uint32_t n, uint64_t* ids_ou
   for (uint32_t i = 0; i < n; ++i) {
     Staged& s = c->staged.emplace_back();
     s.op = ops[i];
+    if (views) s.view = vd[i];
     s.id = c->next_id++;
     s.ring = (ops[i].flags & GPUOS_FLAG_LC) ? 1 : 0;
     for (int k = 0; k < 4; ++k) {
@@ -1771,7 +1911,7 @@ int gpuos_submit(gpuos_ctx* c, const gpuos_op* ops, uint32_t n, uint64_t* ids_ou
     }
     if (c->cfg.auto_deps == 1) {
       const size_t before = s.deps.size();
-      const OpRanges R = op_ranges(ops[i]);
+      const OpRanges R = op_ranges(ops[i], &s.view);
       for (int q = 0; q < R.nr; ++q) {
         const size_t k0 = s.deps.size();
         c->hazards.access(R.r[q], s.id, false, s.deps, retired);
@@ -1798,6 +1938,19 @@ int gpuos_submit(gpuos_ctx* c, const gpuos_op* ops, uint32_t n, uint64_t* ids_ou
     c->hazards.prune(retired);
   }
   return 0;
+}
+
+}  // namespace
+
+extern "C" {
+
+int gpuos_submit(gpuos_ctx* c, const gpuos_op* ops, uint32_t n, uint64_t* ids_out) {
+  return submit_impl(c, ops, nullptr, n, ids_out);
+}
+
+int gpuos_submit_views(gpuos_ctx* c, const gpuos_op* ops, const gpuos_view* views, uint32_t n,
+                       uint64_t* ids_out) {
+  return submit_impl(c, ops, views, n, ids_out);
 }
 
 int gpuos_flush(gpuos_ctx* c) {

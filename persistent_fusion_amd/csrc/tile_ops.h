@@ -125,12 +125,82 @@ struct DTr<GPUOS_BF16, CPL, CPS> {
   __device__ static __forceinline__ float round(float v) { return bf2f(f2bf(v)); }
 };
 
+// fp16: widened exactly to fp32, narrowed with the hardware conversion
+// (round to nearest even, NaN stays NaN, subnormals kept).  Both directions
+// are kept opaque to the compiler's floating-point combines: it folds
+// "multiply in fp32, narrow to fp16" into a mixed-precision FMA with a +0
+// addend, which turns a -0 product into +0.  The widening is written out on
+// the bits; the narrowing is the conversion instruction itself.
+__device__ __forceinline__ float h2f(uint32_t b) {
+  const uint32_t sign = (b & 0x8000u) << 16, e = (b >> 10) & 0x1fu, m = b & 0x3ffu;
+  const uint32_t p = 31u - (uint32_t)__builtin_clz(m | 1u);  // leading bit of a subnormal
+  const uint32_t sub = ((p + 103u) << 23) | ((m << (23u - p)) & 0x7fffffu);
+  uint32_t bits = ((e + 112u) << 23) | (m << 13);  // normal
+  bits = e == 0x1fu ? 0x7f800000u | (m << 13) : bits;  // inf, NaN
+  bits = e == 0u ? (m ? sub : 0u) : bits;             // zero, subnormal
+  return __uint_as_float(sign | bits);
+}
+__device__ __forceinline__ uint32_t f2h(float v) {
+  uint32_t r;
+  asm("v_cvt_f16_f32 %0, %1" : "=v"(r) : "v"(v));
+  return r & 0xffffu;
+}
+__device__ __forceinline__ void unpack_f16x8(const u32x4& t, float (&w)[8]) {
+  w[0] = h2f(t.x & 0xffffu); w[1] = h2f(t.x >> 16);
+  w[2] = h2f(t.y & 0xffffu); w[3] = h2f(t.y >> 16);
+  w[4] = h2f(t.z & 0xffffu); w[5] = h2f(t.z >> 16);
+  w[6] = h2f(t.w & 0xffffu); w[7] = h2f(t.w >> 16);
+}
+__device__ __forceinline__ u32x4 pack_f16x8(const float (&x)[8]) {
+  u32x4 t;
+  t.x = f2h(x[0]) | (f2h(x[1]) << 16);
+  t.y = f2h(x[2]) | (f2h(x[3]) << 16);
+  t.z = f2h(x[4]) | (f2h(x[5]) << 16);
+  t.w = f2h(x[6]) | (f2h(x[7]) << 16);
+  return t;
+}
+
+template <int CPL, int CPS>
+struct DTr<GPUOS_F16, CPL, CPS> {
+  static constexpr int V = 8;
+  static constexpr int ES = 2;
+  __device__ static __forceinline__ float ld(rsrc_t r, uint32_t i) { return h2f(ld16<CPL>(r, 2u * i)); }
+  __device__ static __forceinline__ void st(rsrc_t r, uint32_t i, float v) {
+    st16<CPS>(r, 2u * i, (uint16_t)f2h(v));
+  }
+  __device__ static __forceinline__ void ldv(rsrc_t r, uint32_t i, float (&x)[8]) {
+    unpack_f16x8(ld128<CPL>(r, 2u * i), x);
+  }
+  __device__ static __forceinline__ void stv(rsrc_t r, uint32_t i, const float (&x)[8]) {
+    st128<CPS>(r, 2u * i, pack_f16x8(x));
+  }
+  __device__ static __forceinline__ void ldq(rsrc_t r, uint32_t q, float (&x)[8]) {
+    unpack_f16x8(ld128<CPL>(r, vec_off(q)), x);
+  }
+  __device__ static __forceinline__ void stq(rsrc_t r, uint32_t q, const float (&x)[8]) {
+    st128<CPS>(r, vec_off(q), pack_f16x8(x));
+  }
+  __device__ static __forceinline__ float round(float v) { return h2f(f2h(v)); }
+};
+
+// int32: the same 4-byte moves as fp32; values travel as bit patterns in
+// float registers and only ew_apply<OP, GPUOS_I32> interprets them.
+template <int CPL, int CPS>
+struct DTr<GPUOS_I32, CPL, CPS> : DTr<GPUOS_F32, CPL, CPS> {};
+
 // ---------------------------------------------------------------------------
 // elementwise semantics (one IEEE operation each; see gpuos.h)
 
-template <int OP>
+template <int OP, int DT = GPUOS_F32>
 __device__ __forceinline__ float ew_apply(float x, float y, float alpha) {
-  if constexpr (OP == GPUOS_OP_ADD) return x + y;
+  if constexpr (DT == GPUOS_I32) {  // two's-complement, wrapping
+    const uint32_t a = __float_as_uint(x), b = __float_as_uint(y);
+    if constexpr (OP == GPUOS_OP_ADD) return __uint_as_float(a + b);
+    else if constexpr (OP == GPUOS_OP_MUL) return __uint_as_float(a * b);
+    else return __uint_as_float((int32_t)a > 0 ? a : 0u);  // RELU
+  }
+  else if constexpr (OP == GPUOS_OP_COPY) return x;
+  else if constexpr (OP == GPUOS_OP_ADD) return x + y;
   else if constexpr (OP == GPUOS_OP_MUL) return x * y;
   else if constexpr (OP == GPUOS_OP_SCALE) return alpha * x;
   else if constexpr (OP == GPUOS_OP_RELU) return x > 0.0f ? x : 0.0f;
@@ -199,14 +269,14 @@ __device__ __forceinline__ void ew_tile(D d, uint32_t t) {
         const uint32_t q = (g * U + u) * 64 + lane;
         float r[V];
 #pragma unroll
-        for (int e = 0; e < V; ++e) r[e] = ew_apply<OP>(cx[u][e], cy[u][e], alpha);
+        for (int e = 0; e < V; ++e) r[e] = ew_apply<OP, DT>(cx[u][e], cy[u][e], alpha);
         T::stq(vo, q, r);
       }
     }
     if (t + 1 == ntiles) {
       for (uint32_t i = nv * V + lane; i < n; i += 64) {
         const float y = BIN ? T::ld(b, i) : 0.0f;
-        T::st(out, i, ew_apply<OP>(T::ld(a, i), y, alpha));
+        T::st(out, i, ew_apply<OP, DT>(T::ld(a, i), y, alpha));
       }
     }
     return;
@@ -214,7 +284,71 @@ __device__ __forceinline__ void ew_tile(D d, uint32_t t) {
   for (uint32_t i = t * 64 + lane; i < n; i += 64 * ntiles) {
     const float x = T::ld(a, ca ? i % ca : i);
     const float y = BIN ? T::ld(b, cb ? i % cb : i) : 0.0f;
-    T::st(out, i, ew_apply<OP>(x, y, alpha));
+    T::st(out, i, ew_apply<OP, DT>(x, y, alpha));
+  }
+}
+
+// Elementwise op over a strided or broadcast view (DF_VIEW).  The index space
+// is `rows` = shape[0] x shape[1] x shape[2] rows of shape[3] elements; tile t
+// takes `tile` rows from row t * tile, and the lanes split each row, four
+// elements per lane in flight.  Each operand's element offset is the dot
+// product of the index with its strides (an exact in-place op reads and
+// writes each element in the same lane).  COPY moves bits.
+template <int OP, int DT, int CPL, int CPS, class D>
+__device__ __forceinline__ void ew_view_tile(D d, uint32_t t) {
+  using T = DTr<DT, CPL, CPS>;
+  constexpr bool BIN = ew_binary<OP>();
+  constexpr int U = 4;
+  const uint32_t s1 = d(35), s2 = d(36), L = d(37);
+  const uint32_t rows = d(34) * s1 * s2, tile = d(7);
+  uint32_t st[3][4];
+#pragma unroll
+  for (int k = 0; k < 3; ++k)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) st[k][j] = d(38 + 4 * k + j);
+  const rsrc_t out = make_rsrc(d.q(18)), a = make_rsrc(d.q(20)), b = make_rsrc(d.q(22));
+  const float alpha = __uint_as_float(d(28));
+  const uint32_t r0 = t * tile;
+  const uint32_t r1 = r0 + tile < rows ? r0 + tile : rows;
+  const uint32_t lane = lane_id();
+  for (uint32_t r = r0; r < r1; ++r) {
+    const uint32_t i2 = r % s2, q = r / s2;
+    const uint32_t i1 = q % s1, i0 = q / s1;
+    uint32_t base[3];
+#pragma unroll
+    for (int k = 0; k < 3; ++k) base[k] = i0 * st[k][0] + i1 * st[k][1] + i2 * st[k][2];
+    for (uint32_t j0 = 0; j0 < L; j0 += 64 * U) {
+      float x[U], y[U];
+      uint32_t raw[U];
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        const uint32_t j = j0 + 64 * u + lane;
+        const bool ok = j < L;
+        const uint32_t oa = base[1] + j * st[1][3];
+        raw[u] = 0;
+        x[u] = 0.0f;
+        y[u] = 0.0f;
+        if (!ok) continue;  // no access past the row
+        if constexpr (OP == GPUOS_OP_COPY) {
+          raw[u] = T::ES == 2 ? (uint32_t)ld16<CPL>(a, 2u * oa) : ld32<CPL>(a, 4u * oa);
+        } else {
+          x[u] = T::ld(a, oa);
+          if constexpr (BIN) y[u] = T::ld(b, base[2] + j * st[2][3]);
+        }
+      }
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        const uint32_t j = j0 + 64 * u + lane;
+        if (j >= L) continue;
+        const uint32_t oo = base[0] + j * st[0][3];
+        if constexpr (OP == GPUOS_OP_COPY) {
+          if constexpr (T::ES == 2) st16<CPS>(out, 2u * oo, (uint16_t)raw[u]);
+          else st32<CPS>(out, 4u * oo, raw[u]);
+        } else {
+          T::st(out, oo, ew_apply<OP, DT>(x[u], y[u], alpha));
+        }
+      }
+    }
   }
 }
 
@@ -694,9 +828,9 @@ __device__ __forceinline__ void rope_tile(D d, uint32_t) {
       const uint32_t h = u / per_head, i0 = (u - h * per_head) * 8;
       const uint32_t e1 = h * hd + i0, e2 = e1 + half;
       float x1[8], x2[8], c[8], s[8];
-      if constexpr (DT == GPUOS_BF16) {
-        unpack_bf16x8(ld128<CPL>(in, 2u * e1), x1);
-        unpack_bf16x8(ld128<CPL>(in, 2u * e2), x2);
+      if constexpr (T::ES == 2) {
+        T::ldv(in, e1, x1);
+        T::ldv(in, e2, x2);
       } else {
 #pragma unroll
         for (int k = 0; k < 2; ++k) {
@@ -723,7 +857,7 @@ __device__ __forceinline__ void rope_tile(D d, uint32_t) {
         y1[k] = a1 - b1;
         y2[k] = a2 + b2;
       }
-      if constexpr (DT == GPUOS_BF16) {
+      if constexpr (T::ES == 2) {
         T::stv(out, e1, y1);
         T::stv(out, e2, y2);
       } else {
@@ -1339,36 +1473,63 @@ __device__ __forceinline__ void spin_tile(D d, uint32_t) {
 // opcode switch over the fixed op table (uniform per wave: a scalar branch,
 // no indirect call).  Returns a device error code, 0 on success.
 
+// One elementwise opcode in each dtype it takes (int32 only where INT).
+template <int OP, bool INT, int CPL, int CPS, class D>
+__device__ __forceinline__ void ew_any(uint32_t dt, D d, uint32_t t) {
+  if (dt == GPUOS_BF16) ew_tile<OP, GPUOS_BF16, CPL, CPS>(d, t);
+  else if (dt == GPUOS_F16) ew_tile<OP, GPUOS_F16, CPL, CPS>(d, t);
+  else if constexpr (INT) {
+    if (dt == GPUOS_I32) ew_tile<OP, GPUOS_I32, CPL, CPS>(d, t);
+    else ew_tile<OP, GPUOS_F32, CPL, CPS>(d, t);
+  } else ew_tile<OP, GPUOS_F32, CPL, CPS>(d, t);
+}
+
+template <int OP, bool INT, int CPL, int CPS, class D>
+__device__ __forceinline__ void ew_view_any(uint32_t dt, D d, uint32_t t) {
+  if (dt == GPUOS_BF16) ew_view_tile<OP, GPUOS_BF16, CPL, CPS>(d, t);
+  else if (dt == GPUOS_F16) ew_view_tile<OP, GPUOS_F16, CPL, CPS>(d, t);
+  else if constexpr (INT) {
+    if (dt == GPUOS_I32) ew_view_tile<OP, GPUOS_I32, CPL, CPS>(d, t);
+    else ew_view_tile<OP, GPUOS_F32, CPL, CPS>(d, t);
+  } else ew_view_tile<OP, GPUOS_F32, CPL, CPS>(d, t);
+}
+
+// Elementwise ops over a view (DF_VIEW).
+template <int CPL, int CPS, class D>
+__device__ __forceinline__ uint32_t exec_view(uint32_t op, uint32_t dt, D d, uint32_t t) {
+  switch (op) {
+    case GPUOS_OP_COPY:  // bits: the 2- or 4-byte move of any dtype
+      if (dt == GPUOS_BF16 || dt == GPUOS_F16) ew_view_tile<GPUOS_OP_COPY, GPUOS_BF16, CPL, CPS>(d, t);
+      else ew_view_tile<GPUOS_OP_COPY, GPUOS_F32, CPL, CPS>(d, t);
+      return 0;
+    case GPUOS_OP_ADD: ew_view_any<GPUOS_OP_ADD, true, CPL, CPS>(dt, d, t); return 0;
+    case GPUOS_OP_MUL: ew_view_any<GPUOS_OP_MUL, true, CPL, CPS>(dt, d, t); return 0;
+    case GPUOS_OP_RELU: ew_view_any<GPUOS_OP_RELU, true, CPL, CPS>(dt, d, t); return 0;
+    case GPUOS_OP_SCALE: ew_view_any<GPUOS_OP_SCALE, false, CPL, CPS>(dt, d, t); return 0;
+    case GPUOS_OP_EXP: ew_view_any<GPUOS_OP_EXP, false, CPL, CPS>(dt, d, t); return 0;
+    case GPUOS_OP_SILU_MUL: ew_view_any<GPUOS_OP_SILU_MUL, false, CPL, CPS>(dt, d, t); return 0;
+    default: return (uint32_t)DERR_BAD_OPCODE;
+  }
+}
+
 // Streaming ops (elementwise, copy, fused chains) under cache policies CPL /
 // CPS; returns false for any other opcode.
 template <int CPL, int CPS, class D>
-__device__ __forceinline__ bool exec_stream(uint32_t op, bool bf, D d, uint32_t t, uint32_t& err) {
-  constexpr int F = GPUOS_F32, B = GPUOS_BF16;
+__device__ __forceinline__ bool exec_stream(uint32_t op, uint32_t dt, D d, uint32_t t, uint32_t& err) {
   err = 0;
   switch (op) {
     case GPUOS_OP_COPY:
-      if (bf) copy_tile<2, CPL, CPS>(d, t); else copy_tile<4, CPL, CPS>(d, t);
+      if (dt == GPUOS_BF16 || dt == GPUOS_F16) copy_tile<2, CPL, CPS>(d, t); else copy_tile<4, CPL, CPS>(d, t);
       return true;
-    case GPUOS_OP_ADD:
-      if (bf) ew_tile<GPUOS_OP_ADD, B, CPL, CPS>(d, t); else ew_tile<GPUOS_OP_ADD, F, CPL, CPS>(d, t);
-      return true;
-    case GPUOS_OP_MUL:
-      if (bf) ew_tile<GPUOS_OP_MUL, B, CPL, CPS>(d, t); else ew_tile<GPUOS_OP_MUL, F, CPL, CPS>(d, t);
-      return true;
-    case GPUOS_OP_SCALE:
-      if (bf) ew_tile<GPUOS_OP_SCALE, B, CPL, CPS>(d, t); else ew_tile<GPUOS_OP_SCALE, F, CPL, CPS>(d, t);
-      return true;
-    case GPUOS_OP_RELU:
-      if (bf) ew_tile<GPUOS_OP_RELU, B, CPL, CPS>(d, t); else ew_tile<GPUOS_OP_RELU, F, CPL, CPS>(d, t);
-      return true;
-    case GPUOS_OP_EXP:
-      if (bf) ew_tile<GPUOS_OP_EXP, B, CPL, CPS>(d, t); else ew_tile<GPUOS_OP_EXP, F, CPL, CPS>(d, t);
-      return true;
-    case GPUOS_OP_SILU_MUL:
-      if (bf) ew_tile<GPUOS_OP_SILU_MUL, B, CPL, CPS>(d, t); else ew_tile<GPUOS_OP_SILU_MUL, F, CPL, CPS>(d, t);
-      return true;
-    case OP_FUSED_EW:  // fp32 chains only (the fusion pass leaves bf16 ops unfused)
-      if (bf) err = (uint32_t)DERR_BAD_OPCODE; else fused_tile<F, CPL, CPS>(d, t);
+    case GPUOS_OP_ADD: ew_any<GPUOS_OP_ADD, true, CPL, CPS>(dt, d, t); return true;
+    case GPUOS_OP_MUL: ew_any<GPUOS_OP_MUL, true, CPL, CPS>(dt, d, t); return true;
+    case GPUOS_OP_RELU: ew_any<GPUOS_OP_RELU, true, CPL, CPS>(dt, d, t); return true;
+    case GPUOS_OP_SCALE: ew_any<GPUOS_OP_SCALE, false, CPL, CPS>(dt, d, t); return true;
+    case GPUOS_OP_EXP: ew_any<GPUOS_OP_EXP, false, CPL, CPS>(dt, d, t); return true;
+    case GPUOS_OP_SILU_MUL: ew_any<GPUOS_OP_SILU_MUL, false, CPL, CPS>(dt, d, t); return true;
+    case OP_FUSED_EW:  // fp32 chains only (the fusion pass leaves other dtypes unfused)
+      if (dt != GPUOS_F32) err = (uint32_t)DERR_BAD_OPCODE;
+      else fused_tile<GPUOS_F32, CPL, CPS>(d, t);
       return true;
     default:
       return false;
@@ -1383,13 +1544,14 @@ template <int CPL, int CPS, class D>
 __device__ __forceinline__ uint32_t exec_tile(D d, uint32_t t, lds_f32* scr) {
   const uint32_t w0 = d(0);
   const uint32_t op = w0 & 0xffu, dt = (w0 >> 8) & 0xffu, fl = (w0 >> 16) & 0xffu;
-  const bool bf = dt == GPUOS_BF16;
-  constexpr int F = GPUOS_F32, B = GPUOS_BF16;
+  const bool bf = dt == GPUOS_BF16, hf = dt == GPUOS_F16;
+  constexpr int F = GPUOS_F32, B = GPUOS_BF16, H = GPUOS_F16;
   uint32_t err = 0;
+  if (fl & DF_VIEW) return exec_view<CPL, CPS>(op, dt, d, t);
   if (fl & GPUOS_FLAG_NONTEMPORAL) {
-    if (exec_stream<CPL | CP_NT, CPS | CP_NT>(op, bf, d, t, err)) return err;
+    if (exec_stream<CPL | CP_NT, CPS | CP_NT>(op, dt, d, t, err)) return err;
   } else {
-    if (exec_stream<CPL, CPS>(op, bf, d, t, err)) return err;
+    if (exec_stream<CPL, CPS>(op, dt, d, t, err)) return err;
   }
   switch (op) {
     case GPUOS_OP_NOP:
@@ -1397,17 +1559,24 @@ __device__ __forceinline__ uint32_t exec_tile(D d, uint32_t t, lds_f32* scr) {
     case GPUOS_OP_GATHER:
       return bf ? gather_tile<2, CPL, CPS>(d, t) : gather_tile<4, CPL, CPS>(d, t);
     case GPUOS_OP_ROW_SUM:
-      if (bf) row_tile<GPUOS_OP_ROW_SUM, B, CPL, CPS>(d, t); else row_tile<GPUOS_OP_ROW_SUM, F, CPL, CPS>(d, t);
+      if (bf) row_tile<GPUOS_OP_ROW_SUM, B, CPL, CPS>(d, t);
+      else if (hf) row_tile<GPUOS_OP_ROW_SUM, H, CPL, CPS>(d, t);
+      else row_tile<GPUOS_OP_ROW_SUM, F, CPL, CPS>(d, t);
       return 0;
     case GPUOS_OP_ROW_SOFTMAX:
       if (bf) row_tile<GPUOS_OP_ROW_SOFTMAX, B, CPL, CPS>(d, t);
+      else if (hf) row_tile<GPUOS_OP_ROW_SOFTMAX, H, CPL, CPS>(d, t);
       else row_tile<GPUOS_OP_ROW_SOFTMAX, F, CPL, CPS>(d, t);
       return 0;
     case GPUOS_OP_RMSNORM:
-      if (bf) row_tile<GPUOS_OP_RMSNORM, B, CPL, CPS>(d, t); else row_tile<GPUOS_OP_RMSNORM, F, CPL, CPS>(d, t);
+      if (bf) row_tile<GPUOS_OP_RMSNORM, B, CPL, CPS>(d, t);
+      else if (hf) row_tile<GPUOS_OP_RMSNORM, H, CPL, CPS>(d, t);
+      else row_tile<GPUOS_OP_RMSNORM, F, CPL, CPS>(d, t);
       return 0;
     case GPUOS_OP_ROPE:
-      if (bf) rope_tile<B, CPL, CPS>(d, t); else rope_tile<F, CPL, CPS>(d, t);
+      if (bf) rope_tile<B, CPL, CPS>(d, t);
+      else if (hf) rope_tile<H, CPL, CPS>(d, t);
+      else rope_tile<F, CPL, CPS>(d, t);
       return 0;
     case GPUOS_OP_GEMV:
       if (bf) gemv_tile<B, CPL, CPS>(d, t); else gemv_tile<F, CPL, CPS>(d, t);

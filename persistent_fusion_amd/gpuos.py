@@ -25,7 +25,7 @@ OPCODES = {
     "row_sum": 8, "row_softmax": 9, "rmsnorm": 10, "rope": 11, "gemv": 12,
     "attn_score": 13, "attn_av": 14, "silu_mul": 15, "spin": 16,
 }
-DTYPES = {"f32": 0, "bf16": 1, "i32": 2}
+DTYPES = {"f32": 0, "bf16": 1, "i32": 2, "f16": 3}
 ELEM_BYTES = {"f32": 4, "bf16": 2, "i32": 4}
 FLAG_TRANSIENT, FLAG_LC, FLAG_NONTEMPORAL = 0x1, 0x2, 0x4
 DEVICE_NONE = -1
@@ -62,6 +62,12 @@ class GpuosTraceRec(C.Structure):
                 ("first_ops", C.c_uint32)]
 
 
+class GpuosView(C.Structure):
+    _fields_ = [("ndim", C.c_uint32), ("_reserved", C.c_uint32), ("shape", C.c_uint64 * 4),
+                ("stride", (C.c_int64 * 4) * 3)]
+
+
+assert C.sizeof(GpuosView) == 136
 assert C.sizeof(GpuosOp) == 128
 assert C.sizeof(GpuosConfig) == 64
 assert C.sizeof(GpuosStats) == 128
@@ -71,7 +77,7 @@ assert C.sizeof(GpuosTraceRec) == 40
 EXPORTS = (
     "gpuos_abi_version", "gpuos_last_error", "gpuos_config_default", "gpuos_create",
     "gpuos_submit", "gpuos_flush", "gpuos_sync", "gpuos_query", "gpuos_get_stats",
-    "gpuos_trace_read", "gpuos_stop", "gpuos_destroy", "gpuos_baseline_run",
+    "gpuos_trace_read", "gpuos_stop", "gpuos_destroy", "gpuos_baseline_run", "gpuos_submit_views",
     "gpuos_graph_create", "gpuos_graph_launch", "gpuos_graph_destroy",
     "gpuos_debug_read_desc", "gpuos_debug_published", "gpuos_debug_seq_of", "gpuos_debug_retire",
 )
@@ -94,6 +100,8 @@ def lib() -> C.CDLL:
         "gpuos_config_default": (None, [C.POINTER(GpuosConfig)]),
         "gpuos_create": (C.c_int, [C.c_int, C.POINTER(GpuosConfig), C.POINTER(P)]),
         "gpuos_submit": (C.c_int, [P, C.POINTER(GpuosOp), C.c_uint32, C.POINTER(C.c_uint64)]),
+        "gpuos_submit_views": (C.c_int, [P, C.POINTER(GpuosOp), C.POINTER(GpuosView), C.c_uint32,
+                                         C.POINTER(C.c_uint64)]),
         "gpuos_flush": (C.c_int, [P]),
         "gpuos_sync": (C.c_int, [P, C.c_uint64, C.c_int64]),
         "gpuos_query": (C.c_int, [P, C.c_uint64]),
@@ -191,6 +199,32 @@ def encode_ops(ops, start: int, end: int, addr: Callable, id_of: Dict[int, int])
     return arr
 
 
+def make_view(shape: Sequence[int], strides: Sequence[Sequence[int]]) -> GpuosView:
+    """A gpuos_view: shape (outermost first) and element strides of out, in0,
+    in1 (a missing operand's strides are 0)."""
+    v = GpuosView()
+    v.ndim = len(shape)
+    for d, e in enumerate(shape):
+        v.shape[d] = int(e)
+    for k, st in enumerate(strides):
+        for d, x in enumerate(st):
+            v.stride[k][d] = int(x)
+    return v
+
+
+def encode_views(ops, start: int, end: int):
+    """GpuosView array for workload ops [start, end), or None if no op there
+    has a view (``Op.view`` = (shape, out strides, in0 strides, in1 strides))."""
+    if not any(getattr(ops[i], "view", None) for i in range(start, end)):
+        return None
+    arr = (GpuosView * (end - start))()
+    for k, i in enumerate(range(start, end)):
+        v = getattr(ops[i], "view", None)
+        if v:
+            arr[k] = make_view(v[0], v[1:])
+    return arr
+
+
 class Context:
     """One resident-kernel context (``gpuos_create`` ... ``gpuos_destroy``)."""
 
@@ -202,12 +236,16 @@ class Context:
         self.handle = h
         self.device = device
 
-    def submit(self, ops, n: Optional[int] = None) -> List[int]:
+    def submit(self, ops, n: Optional[int] = None, views=None) -> List[int]:
+        """Submits ops (and, optionally, a GpuosView array: gpuos_submit_views)."""
         if isinstance(ops, GpuosOp):
             ops = (GpuosOp * 1)(ops)
         n = len(ops) if n is None else n
         ids = (C.c_uint64 * max(n, 1))()
-        _check(self._lib.gpuos_submit(self.handle, ops, n, ids), "gpuos_submit")
+        if views is not None:
+            _check(self._lib.gpuos_submit_views(self.handle, ops, views, n, ids), "gpuos_submit_views")
+        else:
+            _check(self._lib.gpuos_submit(self.handle, ops, n, ids), "gpuos_submit")
         return list(ids[:n])
 
     def submit_noids(self, ops, n: int) -> None:
@@ -330,4 +368,5 @@ def decode_desc(raw: bytes) -> dict:
     # GEMV -> residual ADD descriptors
     d["ga"] = {"out": q(18), "x": q(20), "res": q(22), "W": q(24), "res_first": w[26],
                "M": w[30], "K": w[31], "sum": q(32)}
+    d["view"] = {"shape": list(w[34:38]), "stride": [list(w[38 + 4 * k:42 + 4 * k]) for k in range(3)]}
     return d

@@ -60,7 +60,7 @@ def submit_workload(ctx: gpuos.Context, wl: Workload, addr, groups=None, flush_e
     id_of = {}
     for gi, (g0, g1) in enumerate(groups or wl.groups):
         arr = encoded[gi] if encoded is not None else gpuos.encode_ops(wl.ops, g0, g1, addr, id_of)
-        got = ctx.submit(arr, g1 - g0)
+        got = ctx.submit(arr, g1 - g0, views=gpuos.encode_views(wl.ops, g0, g1))
         for k, i in enumerate(range(g0, g1)):
             ids[i] = got[k]
             id_of[i] = got[k]
@@ -141,7 +141,7 @@ def restore(tensors: Dict[str, "object"], wl: Workload, outputs: Iterable[str]) 
         t.copy_(torch.from_numpy(np.ascontiguousarray(host)))
     for name in poisonable(wl, outputs):
         t = tensors[name]
-        t.fill_(float("nan") if wl.dtypes[name] == "f32" else -1)
+        t.fill_(float("nan") if wl.dtypes[name] in ("f32", "f16") else -1)
 
 
 def capture_graph(wl: Workload, tensors, device: int = 0, fuse: bool = False) -> gpuos.Graph:

@@ -41,8 +41,8 @@ ALL_KINDS = (
     "attn_score", "attn_av", "silu_mul", "spin",
 )
 
-NP_DTYPE = {"f32": np.float32, "bf16": np.uint16, "i32": np.int32}
-ELEM_BYTES = {"f32": 4, "bf16": 2, "i32": 4}
+NP_DTYPE = {"f32": np.float32, "bf16": np.uint16, "i32": np.int32, "f16": np.float16}
+ELEM_BYTES = {"f32": 4, "bf16": 2, "i32": 4, "f16": 2}
 
 
 @dataclass(frozen=True)
@@ -63,7 +63,9 @@ class Op:
     ``dims`` holds the integer parameters (GEMV: M, K; attention: H, D, S;
     rotary: heads, head_dim; spin: nanoseconds).  ``deps`` are indices of
     earlier ops in the same workload that this op must wait for, beyond the
-    hazards the runtime derives from the byte ranges.
+    hazards the runtime derives from the byte ranges.  ``view`` (elementwise
+    ops only) is (shape, out strides, in0 strides, in1 strides), strides in
+    elements from each operand's start.
     """
 
     kind: str
@@ -81,6 +83,7 @@ class Op:
     deps: Tuple[int, ...] = ()
     transient: bool = False
     lc: bool = False
+    view: Optional[Tuple[Tuple[int, ...], ...]] = None
 
 
 @dataclass

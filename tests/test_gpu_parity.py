@@ -106,6 +106,129 @@ def test_elementwise_queue_small_ring_wraps():
 
 
 # ----------------------------------------------------------------------------
+# fp16, int32 and strided / broadcast views
+
+
+def _f16(rng, n, scale=1.0):
+    return (rng.standard_normal(n) * scale).astype(np.float32).astype(np.float16)
+
+
+@pytest.mark.parametrize("kind", ["copy", "add", "mul", "scale", "relu", "exp", "silu_mul"])
+def test_f16_elementwise(kind):
+    _need_gpu()
+    rng = np.random.default_rng(50)
+    for n, src in ((1, (0, 0)), (63, (0, 0)), (1000, (0, 0)), (4097, (0, 0)), (100_003, (0, 0)),
+                   (999, (37, 0))):
+        say(f"f16 {kind} n={n} src_len={src}")
+        a, b = _f16(rng, n), _f16(rng, n)
+        a[:5] = np.array([0.0, -0.0, 6e-8, -65504.0, np.inf], np.float16)[: min(5, n)]
+        bufs = {"a": a, "b": b, "y": np.zeros(n, np.float16)}
+        ins = (Ref("a"), Ref("b")) if kind in ("add", "mul", "silu_mul") else (Ref("a"),)
+        wl = Workload("f16", bufs, {"a": "f16", "b": "f16", "y": "f16"},
+                      [Op(kind, Ref("y"), ins, n=n, dtype="f16", alpha=0.75, src_len=src)],
+                      outputs=["y"])
+        check(wl, runner.run_resident(wl))
+
+
+@pytest.mark.parametrize("kind", ["row_sum", "row_softmax", "rmsnorm", "rope"])
+def test_f16_rows_and_rope(kind):
+    _need_gpu()
+    rng = np.random.default_rng(51)
+    for rows, L in ((3, 64), (5, 1000), (2, 4096), (7, 33)):
+        if kind == "rope" and L % 2:
+            continue
+        say(f"f16 {kind} rows={rows} L={L}")
+        n = rows * L
+        bufs = {"x": _f16(rng, n), "g": _f16(rng, L, 0.5), "tab": workloads.rope_table([11], L).reshape(-1),
+                "y": np.zeros(rows if kind == "row_sum" else n, np.float16)}
+        dts = {"x": "f16", "g": "f16", "tab": "f32", "y": "f16"}
+        aux = Ref("g") if kind == "rmsnorm" else Ref("tab") if kind == "rope" else None
+        op = Op(kind, Ref("y"), (Ref("x"),), aux, n=n, dtype="f16", rows=rows, row_len=L,
+                eps=float(np.float32(1e-6)), dims=(rows, L) if kind == "rope" else ())
+        wl = Workload("f16rows", bufs, dts, [op], outputs=["y"])
+        check(wl, runner.run_resident(wl))
+
+
+@pytest.mark.parametrize("kind", ["add", "mul", "relu", "copy"])
+def test_i32_elementwise_wraps(kind):
+    _need_gpu()
+    rng = np.random.default_rng(52)
+    for n in (1, 7, 4096, 65_537):
+        say(f"i32 {kind} n={n}")
+        a = rng.integers(-2 ** 31, 2 ** 31, n).astype(np.int32)
+        b = rng.integers(-2 ** 31, 2 ** 31, n).astype(np.int32)
+        a[:4] = np.array([2 ** 31 - 1, -2 ** 31, -1, 0], np.int32)[: min(4, n)]
+        bufs = {"a": a, "b": b, "y": np.zeros(n, np.int32)}
+        ins = (Ref("a"), Ref("b")) if kind in ("add", "mul") else (Ref("a"),)
+        wl = Workload("i32", bufs, {"a": "i32", "b": "i32", "y": "i32"},
+                      [Op(kind, Ref("y"), ins, n=n, dtype="i32")], outputs=["y"])
+        check(wl, runner.run_resident(wl))
+
+
+_VIEW_CASES = {
+    # name: (shape, out strides, in0 strides, in1 strides, in0 len, in1 len, out len)
+    "bias_add": ((37, 300), (300, 1), (300, 1), (0, 1), 37 * 300, 300, 37 * 300),
+    "row_scale": ((41, 129), (129, 1), (129, 1), (1, 0), 41 * 129, 41, 41 * 129),
+    "transpose": ((33, 70), (1, 33), (70, 1), (0, 0), 33 * 70, 0, 33 * 70),
+    "outer": ((50, 64), (64, 1), (1, 0), (0, 1), 50, 64, 50 * 64),
+    "strided_out": ((8, 100), (400, 2), (100, 1), (100, 1), 800, 800, 3200),
+    "scalar": ((5000,), (1,), (1,), (0,), 5000, 1, 5000),
+    "4d": ((3, 4, 5, 6), (120, 30, 6, 1), (1, 3, 12, 60), (0, 6, 0, 1), 360, 30, 360),
+    "long_rows": ((3, 5000), (5000, 1), (5000, 1), (0, 1), 15000, 5000, 15000),
+}
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16", "f16", "i32"])
+@pytest.mark.parametrize("case", sorted(_VIEW_CASES))
+def test_views(case, dtype):
+    _need_gpu()
+    shape, so, s0, s1, la, lb, lo = _VIEW_CASES[case]
+    rng = np.random.default_rng(53)
+    n = int(np.prod(shape))
+    kinds = ["add", "mul", "relu", "copy"] if dtype == "i32" else ["add", "mul", "scale", "relu",
+                                                                     "exp", "silu_mul", "copy"]
+    for kind in kinds:
+        binary = kind in ("add", "mul", "silu_mul")
+        if binary and lb == 0:
+            continue
+        say(f"view {case} {dtype} {kind}")
+
+        def draw(m):
+            if dtype == "i32":
+                return rng.integers(-2 ** 31, 2 ** 31, m).astype(np.int32)
+            v = rng.standard_normal(m).astype(np.float32)
+            return {"f32": v, "bf16": workloads.f32_to_bf16_trunc(v), "f16": v.astype(np.float16)}[dtype]
+
+        npdt = workloads.NP_DTYPE[dtype]
+        bufs = {"a": draw(la), "b": draw(max(lb, 1)), "y": np.zeros(lo, npdt)}
+        ins = (Ref("a"), Ref("b")) if binary else (Ref("a"),)
+        wl = Workload("view", bufs, {"a": dtype, "b": dtype, "y": dtype},
+                      [Op(kind, Ref("y"), ins, n=n, dtype=dtype, alpha=-1.25,
+                          view=(shape, so, s0, s1))], outputs=["y"])
+        check(wl, runner.run_resident(wl))
+
+
+def test_view_in_place_and_queue_with_hazards():
+    """A queue mixing viewed and plain ops over shared buffers: the hazards
+    derived from view ranges order it as submitted."""
+    _need_gpu()
+    say("views in a queue")
+    rng = np.random.default_rng(54)
+    R, Cn = 64, 96
+    bufs = {"x": rng.standard_normal(R * Cn).astype(np.float32),
+            "b": rng.standard_normal(Cn).astype(np.float32),
+            "s": rng.standard_normal(R).astype(np.float32),
+            "t": np.zeros(R * Cn, np.float32), "u": np.zeros(R * Cn, np.float32)}
+    ops = [Op("add", Ref("t"), (Ref("x"), Ref("b")), n=R * Cn, view=((R, Cn), (Cn, 1), (Cn, 1), (0, 1))),
+           Op("relu", Ref("t"), (Ref("t"),), n=R * Cn, view=((R, Cn), (Cn, 1), (Cn, 1), (0, 0))),
+           Op("copy", Ref("b"), (Ref("x", 5),), n=Cn),  # overwrites the broadcast row afterwards
+           Op("mul", Ref("u"), (Ref("t"), Ref("s")), n=R * Cn, view=((Cn, R), (1, Cn), (1, Cn), (0, 1))),
+           Op("add", Ref("x"), (Ref("x"), Ref("u")), n=R * Cn)]
+    wl = Workload("viewq", bufs, {k: "f32" for k in bufs}, ops, outputs=["x", "b", "t", "u"])
+    check(wl, runner.run_resident(wl))
+
+
+# ----------------------------------------------------------------------------
 # every opcode on ragged sizes
 
 

@@ -44,7 +44,7 @@ def test_library_exports_every_declared_symbol():
     missing = [s for s in sorted(declared) if not hasattr(lib, s)]
     assert not missing, missing
     assert set(gpuos.EXPORTS) == declared
-    assert lib.gpuos_abi_version() == 1
+    assert lib.gpuos_abi_version() == 2
 
 
 def test_fused_chain_becomes_one_descriptor():
@@ -271,7 +271,9 @@ def test_priority_ring_and_cross_ring_rules():
     (lambda: make_op("gemv", buf(0), [buf(1)], aux=buf(2), n=10, dims=(11, 4)), "GEMV"),
     (lambda: make_op("rope", buf(0), [buf(1)], aux=buf(2), n=21, rows=3, row_len=7), "ROPE"),
     (lambda: make_op("gather", buf(0), [buf(1)], aux=buf(2), n=10), "src_len"),
-    (lambda: make_op("relu", buf(0), [buf(1)], n=10, dtype="i32"), "int32"),
+    (lambda: make_op("exp", buf(0), [buf(1)], n=10, dtype="i32"), "int32"),
+    (lambda: make_op("scale", buf(0), [buf(1)], n=10, dtype="i32", alpha=2.0), "int32"),
+    (lambda: make_op("gemv", buf(0), [buf(1)], aux=buf(2), n=4, dtype="f16", dims=(4, 8)), "fp16"),
 ])
 def test_validation_errors_stage_nothing(op, msg):
     with ctx() as c:
@@ -525,6 +527,114 @@ def test_softmax_av_refusals():
         c.submit(ops)
         c.flush()
         assert c.published(0) == 2
+
+
+# ----------------------------------------------------------------------------
+# views (strided and broadcast operands) and the fp16 / int32 dtypes
+
+
+def _submit_views(c, ops, views):
+    arr = (gpuos.GpuosOp * len(ops))(*ops)
+    va = (gpuos.GpuosView * len(ops))(*views)
+    return c.submit(arr, len(ops), views=va)
+
+
+def test_views_are_normalised_into_the_descriptor():
+    R, Cn = 6, 40
+    x, b, y = buf(0), buf(1), buf(2)
+    add = make_op("add", y, [x, b], n=R * Cn)
+    with ctx() as c:
+        # contiguous indexing written as a view is the plain op
+        _submit_views(c, [add], [gpuos.make_view((R, Cn), [(Cn, 1), (Cn, 1), (Cn, 1)])])
+        # bias add: b broadcast over the rows
+        _submit_views(c, [add], [gpuos.make_view((R, Cn), [(Cn, 1), (Cn, 1), (0, 1)])])
+        # 3-D with the two inner dimensions contiguous for every operand: merged
+        _submit_views(c, [add], [gpuos.make_view((2, 3, Cn * 3 // 3 * R // 6), [(3 * Cn, Cn, 1), (3 * Cn, Cn, 1), (0, Cn, 1)])])
+        c.flush()
+        assert c.published(0) == 3
+        d1, d2, d3 = desc(c, 1), desc(c, 2), desc(c, 3)
+        assert not d1["flags"] & 0x40
+        assert d2["flags"] & 0x40
+        assert d2["view"]["shape"] == [1, 1, R, Cn]
+        assert d2["view"]["stride"] == [[0, 0, Cn, 1], [0, 0, Cn, 1], [0, 0, 0, 1]]
+        assert d2["ntiles"] * d2["tile"] >= R
+        assert d3["view"]["shape"] == [1, 1, 2, 3 * Cn]
+        assert d3["view"]["stride"] == [[0, 0, 3 * Cn, 1], [0, 0, 3 * Cn, 1], [0, 0, 0, 1]]
+
+
+@pytest.mark.parametrize("view,msg", [
+    (((4, 6), [(0, 1), (6, 1), (6, 1)]), "twice"),
+    (((4, 6), [(6, 1), (-6, 1), (6, 1)]), "stride"),
+    (((4, 5), [(5, 1), (5, 1), (5, 1)]), "multiply"),
+    (((4, 6), [(6, 1), (1, 4), (6, 1)]), None),  # a transposed read is fine
+])
+def test_view_validation(view, msg):
+    with ctx() as c:
+        op = make_op("add", buf(2), [buf(0), buf(1)], n=24)
+        if msg is None:
+            _submit_views(c, [op], [gpuos.make_view(*view)])
+            return
+        with pytest.raises(GpuosError) as e:
+            _submit_views(c, [op], [gpuos.make_view(*view)])
+        assert e.value.status == gpuos.EINVAL and msg in str(e.value)
+
+
+def test_view_rejections_for_ops_and_overlaps():
+    with ctx() as c:
+        # only elementwise ops take views
+        g = make_op("gemv", buf(0), [buf(1)], aux=buf(2), n=4, dims=(4, 8))
+        with pytest.raises(GpuosError):
+            _submit_views(c, [g], [gpuos.make_view((4,), [(1,), (1,), (0,)])])
+        # an output overlapping its input under another view would race
+        x = buf(0)
+        t = make_op("copy", x + 4, [x], n=24)
+        with pytest.raises(GpuosError) as e:
+            _submit_views(c, [t], [gpuos.make_view((4, 6), [(1, 4), (6, 1), (0, 0)])])
+        assert "overlaps" in str(e.value)
+        # ... but exactly in place is fine
+        r = make_op("relu", x, [x], n=24)
+        _submit_views(c, [r], [gpuos.make_view((4, 6), [(12, 2), (12, 2), (0, 0)])])
+        # src_len and a view do not mix
+        s = make_op("relu", buf(3), [buf(4)], n=24, src_len=(6, 0))
+        with pytest.raises(GpuosError):
+            _submit_views(c, [s], [gpuos.make_view((4, 6), [(6, 1), (0, 1), (0, 0)])])
+
+
+def test_view_ranges_drive_hazards_and_views_are_not_fused():
+    with ctx() as c:
+        x, b, y, z = buf(0), buf(1), buf(2), buf(3)
+        # y = x + b (b: 40 elements broadcast over 6 rows), then b is overwritten
+        add = make_op("add", y, [x, b], n=240)
+        wr = make_op("copy", b, [z], n=40)
+        far = make_op("copy", b + 4 * 40, [z], n=40)  # past the broadcast row: no hazard
+        arr = (gpuos.GpuosOp * 3)(add, wr, far)
+        va = (gpuos.GpuosView * 3)(gpuos.make_view((6, 40), [(40, 1), (40, 1), (0, 1)]),
+                                   gpuos.GpuosView(), gpuos.GpuosView())
+        c.submit(arr, 3, views=va)
+        c.flush()
+        assert c.published(0) == 3
+        assert desc(c, 2)["deps"][0] == 1
+        assert desc(c, 3)["deps"][0] == 0
+    # a viewed op next to a fusable fp32 op stays its own descriptor
+    with ctx() as c:
+        a, b, t, y = buf(0), buf(1), buf(2), buf(3)
+        ops = [make_op("mul", t, [a, b], n=64), make_op("relu", y, [t], n=64)]
+        views = [gpuos.GpuosView(), gpuos.make_view((8, 8), [(8, 1), (1, 8), (0, 0)])]
+        _submit_views(c, ops, views)
+        c.flush()
+        assert c.published(0) == 2
+
+
+def test_f16_and_i32_ops_are_accepted_and_not_fused():
+    with ctx() as c:
+        a, b, t, y = buf(0), buf(1), buf(2), buf(3)
+        ops = [make_op("add", t, [a, b], n=64, dtype="f16"), make_op("relu", y, [t], n=64, dtype="f16"),
+               make_op("mul", t, [a, b], n=64, dtype="i32"), make_op("relu", y, [t], n=64, dtype="i32"),
+               make_op("rmsnorm", y, [a], aux=b, n=64, dtype="f16", rows=1, row_len=64, eps=1e-6)]
+        c.submit((gpuos.GpuosOp * 5)(*ops))
+        c.flush()
+        assert c.published(0) == 5
+        assert [desc(c, s)["dtype"] for s in range(1, 6)] == [3, 3, 2, 2, 3]
 
 
 def test_graph_replay_poisons_only_buffers_written_whole_first():

@@ -38,7 +38,8 @@ def bits32(v) -> int:
 
 
 def wl_of(bufs, ops, dtypes=None):
-    dts = dtypes or {k: ("bf16" if v.dtype == np.uint16 else "i32" if v.dtype == np.int32 else "f32")
+    dts = dtypes or {k: ("bf16" if v.dtype == np.uint16 else "i32" if v.dtype == np.int32
+                         else "f16" if v.dtype == np.float16 else "f32")
                      for k, v in bufs.items()}
     return Workload("t", {k: np.asarray(v) for k, v in bufs.items()}, dts, ops)
 
@@ -615,6 +616,133 @@ def test_gather_and_copy():
     bufs["i"] = np.array([0, 10, 1, 1, 1], np.int32)
     with pytest.raises(oracle.OracleError):
         oracle.run(wl_of(bufs, [Op("gather", Ref("y"), (Ref("x"),), Ref("i"), n=5, src_len=(10, 0))]))
+
+
+# ----------------------------------------------------------------------------
+# fp16, int32 and views (the generic tensor abstraction of "GPUOS: A GPU
+# Operating System Primitive for Transparent Operation Fusion", section "The
+# Paper": arbitrary shapes, strides, dtypes, broadcasting)
+
+
+def _f16_neighbours_and_midpoints():
+    """Every finite positive fp16 value, and the exact midpoint between each
+    pair of neighbours (12 significant bits: exact in fp32)."""
+    bits = np.arange(0, 0x7C00, dtype=np.uint16)
+    vals = bits.view(np.float16).astype(np.float64)
+    mids = (vals[:-1] + vals[1:]) / 2.0
+    return bits, vals, mids
+
+
+def test_f16_rounding_is_round_to_nearest_even():
+    bits, vals, mids = _f16_neighbours_and_midpoints()
+    # exact values survive widening and narrowing
+    rt = oracle.run(wl_of({"x": bits.view(np.float16), "o": np.zeros(bits.size, np.float16)},
+                          [Op("relu", Ref("o"), (Ref("x"),), n=bits.size, dtype="f16")]))
+    assert np.array_equal(rt["o"].view(np.uint16), bits)  # relu of a non-negative value is the value
+    # ties go to the neighbour with an even last bit, others to the nearest
+    from oracle.interpreter import _store_from_f32
+    got = _store_from_f32(mids.astype(np.float32), "f16").view(np.uint16)
+    lo, hi = bits[:-1], bits[1:]
+    want = np.where(lo % 2 == 0, lo, hi)
+    assert np.array_equal(got, want)
+    quarter = (3 * vals[:-1] + vals[1:]) / 4.0  # closer to the lower neighbour
+    assert np.array_equal(_store_from_f32(quarter.astype(np.float32), "f16").view(np.uint16), lo)
+    # overflow: the largest finite fp16 is 65504; halfway to 2^16 and beyond is inf
+    big = _store_from_f32(np.array([65504.0, 65519.0, 65520.0, 1e6, -1e6], np.float32), "f16")
+    assert list(big[:2]) == [65504.0, 65504.0] and np.isinf(big[2:]).all()
+
+
+def test_f16_matches_torch_half():
+    torch = pytest.importorskip("torch")
+    rng = np.random.default_rng(40)
+    x = np.concatenate([rng.standard_normal(20000).astype(np.float32) * 100,
+                        rng.standard_normal(2000).astype(np.float32) * 1e-6])
+    from oracle.interpreter import _store_from_f32
+    want = torch.from_numpy(x).half().numpy()
+    assert np.array_equal(_store_from_f32(x, "f16").view(np.uint16), want.view(np.uint16))
+
+
+def test_f16_elementwise_is_fp32_then_rne():
+    torch = pytest.importorskip("torch")
+    rng = np.random.default_rng(41)
+    n = 257
+    a = rng.standard_normal(n).astype(np.float16)
+    b = rng.standard_normal(n).astype(np.float16)
+    bufs = {"a": a, "b": b, "y": np.zeros(n, np.float16), "z": np.zeros(n, np.float16)}
+    out = oracle.run(wl_of(bufs, [Op("mul", Ref("y"), (Ref("a"), Ref("b")), n=n, dtype="f16"),
+                                  Op("scale", Ref("z"), (Ref("a"),), n=n, dtype="f16", alpha=0.3)]))
+    ta, tb = torch.from_numpy(a).float(), torch.from_numpy(b).float()
+    assert np.array_equal(out["y"].view(np.uint16), (ta * tb).half().numpy().view(np.uint16))
+    sc = (torch.tensor(np.float32(0.3)) * ta).half().numpy()
+    assert np.array_equal(out["z"].view(np.uint16), sc.view(np.uint16))
+
+
+def test_int32_add_mul_wrap_and_relu():
+    rng = np.random.default_rng(42)
+    edge = [0, 1, -1, 2 ** 31 - 1, -2 ** 31, 2 ** 16, -2 ** 16, 46341, -46341]
+    a = np.array(edge + list(rng.integers(-2 ** 31, 2 ** 31, 200)), np.int64)
+    b = np.array(list(reversed(edge)) + list(rng.integers(-2 ** 31, 2 ** 31, 200)), np.int64)
+    n = a.size
+    bufs = {"a": a.astype(np.int32), "b": b.astype(np.int32), "s": np.zeros(n, np.int32),
+            "p": np.zeros(n, np.int32), "r": np.zeros(n, np.int32)}
+    out = oracle.run(wl_of(bufs, [Op("add", Ref("s"), (Ref("a"), Ref("b")), n=n, dtype="i32"),
+                                  Op("mul", Ref("p"), (Ref("a"), Ref("b")), n=n, dtype="i32"),
+                                  Op("relu", Ref("r"), (Ref("a"),), n=n, dtype="i32")]))
+
+    def wrap(v):  # Python integers are exact: reduce mod 2^32 into [-2^31, 2^31)
+        v %= 2 ** 32
+        return v - 2 ** 32 if v >= 2 ** 31 else v
+
+    for i in range(n):
+        x, y = int(a[i]), int(b[i])
+        assert int(out["s"][i]) == wrap(x + y)
+        assert int(out["p"][i]) == wrap(x * y)
+        assert int(out["r"][i]) == (x if x > 0 else 0)
+
+
+def test_view_broadcasts_match_numpy_broadcasting():
+    rng = np.random.default_rng(43)
+    R, Cn = 5, 7
+    x = rng.standard_normal(R * Cn).astype(np.float32)
+    row = rng.standard_normal(Cn).astype(np.float32)
+    col = rng.standard_normal(R).astype(np.float32)
+    bufs = {"x": x, "row": row, "col": col, "y1": np.zeros(R * Cn, np.float32),
+            "y2": np.zeros(R * Cn, np.float32), "y3": np.zeros(R * Cn, np.float32),
+            "y4": np.zeros(R * Cn, np.float32)}
+    ops = [
+        # bias add: [R, C] + [C]
+        Op("add", Ref("y1"), (Ref("x"), Ref("row")), n=R * Cn,
+           view=((R, Cn), (Cn, 1), (Cn, 1), (0, 1))),
+        # per-row scale: [R, C] * [R, 1]
+        Op("mul", Ref("y2"), (Ref("x"), Ref("col")), n=R * Cn,
+           view=((R, Cn), (Cn, 1), (Cn, 1), (1, 0))),
+        # transpose: out[j, i] = x[i, j]
+        Op("copy", Ref("y3"), (Ref("x"),), n=R * Cn, view=((R, Cn), (1, R), (Cn, 1), (0, 0))),
+        # outer product of two vectors
+        Op("mul", Ref("y4"), (Ref("col"), Ref("row")), n=R * Cn,
+           view=((R, Cn), (Cn, 1), (1, 0), (0, 1))),
+    ]
+    out = oracle.run(wl_of(bufs, ops))
+    X = x.reshape(R, Cn)
+    assert np.array_equal(out["y1"].reshape(R, Cn), X + row[None, :])
+    assert np.array_equal(out["y2"].reshape(R, Cn), X * col[:, None])
+    assert np.array_equal(out["y3"].reshape(Cn, R), X.T)
+    assert np.array_equal(out["y4"].reshape(R, Cn), col[:, None] * row[None, :])
+
+
+def test_view_strided_output_and_in_place():
+    x = np.arange(24, dtype=np.float32)
+    bufs = {"x": x.copy(), "y": np.full(48, -1.0, np.float32)}
+    ops = [Op("scale", Ref("y"), (Ref("x"),), n=24, alpha=2.0, view=((4, 6), (12, 2), (6, 1), (0, 0))),
+           Op("relu", Ref("x", 1), (Ref("x", 1),), n=4, view=((2, 2), (12, 1), (12, 1), (0, 0)))]
+    out = oracle.run(wl_of(bufs, ops))
+    y = out["y"].reshape(4, 12)
+    assert np.array_equal(y[:, 0::2], 2.0 * x.reshape(4, 6)) and np.all(y[:, 1::2] == -1.0)
+    assert np.array_equal(out["x"], x)  # relu of non-negative values in place leaves them
+    # an output addressing an element twice is rejected
+    with pytest.raises(oracle.OracleError):
+        oracle.run(wl_of({"x": x.copy(), "y": np.zeros(24, np.float32)},
+                         [Op("copy", Ref("y"), (Ref("x"),), n=24, view=((4, 6), (0, 1), (6, 1), (0, 0)))]))
 
 
 # ----------------------------------------------------------------------------
