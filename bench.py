@@ -500,6 +500,68 @@ def priority_leg(device=0, rounds=200):
     return res
 
 
+def torch_frontend_leg(device=0, reps=5, n_ops=1000, sizes=(4096, 1 << 20)):
+    """The same eager PyTorch program (n_ops elementwise ops on fp32 tensors
+    of each size in ``sizes``, each reading one or two earlier results) run
+    by PyTorch itself and under GpuosMode, which queues the ops into the
+    resident kernel; host wall time per program including the final
+    synchronisation that brings the result to the host."""
+    import numpy as np
+    import torch
+
+    from persistent_fusion_amd.torch_mode import GpuosMode
+
+    rng = np.random.default_rng(0)
+    prog = []
+    for i in range(n_ops):
+        kind = int(rng.integers(0, 4))
+        a, b = int(rng.integers(0, 2 + i)), int(rng.integers(0, 2 + i))
+        prog.append((kind, a, b, float(rng.uniform(-1, 1))))
+
+    def timed(fn):
+        fn()
+        torch.cuda.synchronize()
+        ts = []
+        for _ in range(reps):
+            t0 = time.perf_counter()
+            r = fn()
+            float(r)  # the result reaches the host
+            ts.append(time.perf_counter() - t0)
+        return sorted(ts)[len(ts) // 2], float(r)
+
+    res = {"workload": f"{n_ops} eager elementwise ops (add/mul/relu/scale by a Python float), fp32"}
+    mode = GpuosMode(device)
+    try:
+        for size in sizes:
+            torch.manual_seed(0)
+            base = [torch.rand(size, device=f"cuda:{device}") * 2 - 1 for _ in range(2)]
+
+            def run():
+                vals = list(base)
+                for kind, a, b, s in prog:
+                    x, y = vals[a], vals[b]
+                    vals.append(x + y if kind == 0 else x * y if kind == 1 else
+                                torch.relu(x) if kind == 2 else x * s)
+                return vals[-1].sum()
+
+            def in_mode():
+                with mode:
+                    return run()
+
+            eager_s, eager_r = timed(run)
+            mode_s, mode_r = timed(in_mode)
+            res[f"n{size}"] = {
+                "eager_pytorch_us_per_op": round(eager_s / n_ops * 1e6, 2),
+                "gpuos_mode_us_per_op": round(mode_s / n_ops * 1e6, 2),
+                "speedup_vs_eager_pytorch": round(eager_s / mode_s, 2),
+                "same_result": bool(abs(eager_r - mode_r) <= 1e-3 * max(1.0, abs(eager_r)))}
+            print(f"torch front end n={size}: {res[f'n{size}']}", file=sys.stderr, flush=True)
+            del base
+    finally:
+        mode.close()
+    return res
+
+
 def cpu_baseline_leg(budget_s=10.0, gpu_y=None):
     """The oracle, untuned, on a bounded sample of the same workload.
 
@@ -564,7 +626,7 @@ def main():
     ap.add_argument("--cpu-budget", type=float, default=10.0)
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--extra", default="",
-                    help="comma-separated extra legs: decode, dag, priority (or all)")
+                    help="comma-separated extra legs: decode, dag, priority, torch (or all)")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
         print("bench.py: this build measures one GPU only (the resident kernel runs on one "
@@ -578,12 +640,13 @@ def main():
     fc = fused_chain_leg(args.steps, args.warmup)
     q = queue_leg(args.queue_reps)
     cp = copy_leg()
-    extra_names = ("decode", "dag", "priority") if args.extra == "all" else \
+    extra_names = ("decode", "dag", "priority", "torch") if args.extra == "all" else \
         tuple(x for x in args.extra.split(",") if x)
     extra = {}
     for name in extra_names:
         log(f"bench: extra leg {name}")
-        extra[name] = {"decode": decode_leg, "dag": dag_leg, "priority": priority_leg}[name]()
+        extra[name] = {"decode": decode_leg, "dag": dag_leg, "priority": priority_leg,
+                       "torch": torch_frontend_leg}[name]()
     cpu, parity = (None, None) if args.no_cpu else cpu_baseline_leg(args.cpu_budget, fc["y"])
 
     steps = args.steps

@@ -430,6 +430,19 @@ int gpuos_graph_create(int device, const gpuos_op* ops, uint32_t n, int fuse, gp
 int gpuos_graph_launch(gpuos_graph* g, void* stream);
 int gpuos_graph_destroy(gpuos_graph* g);
 
+/*
+ * Gives the GPU back to other work: waits (up to timeout_ns, < 0 = forever)
+ * until every submitted op has completed, then lets the resident kernel leave
+ * at once instead of after idle_exit_ms, and returns once its launch has
+ * ended.  While the kernel is resident it holds the register files of every
+ * compute unit, so kernels launched by other code (PyTorch included) cannot
+ * start; the pages' critique of persistent kernels ("The Counter" on the
+ * GPUOS page) is exactly that.  The next gpuos_flush with work relaunches
+ * the kernel.  Returns 0 at once on a host-only or already parked context.
+ * Errors: ESTATE (stopped), ETIMEDOUT, EDEVICE.
+ */
+int gpuos_yield(gpuos_ctx* ctx, int64_t timeout_ns);
+
 /* ABI version of the loaded library (GPUOS_ABI_VERSION). */
 int gpuos_abi_version(void);
 

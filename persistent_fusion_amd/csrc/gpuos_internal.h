@@ -239,7 +239,9 @@ struct alignas(256) HostCtl {
                               // every published descriptor has retired
   uint64_t error;             // device: first error code (0 = none)
   uint64_t error_seq;         // device: (ring << 62) | sequence that raised it
-  uint64_t _p2[29];
+  uint64_t yield_req;         // host: nonzero asks a drained kernel to leave
+                              // at once, as after its idle period
+  uint64_t _p2[28];
 };
 
 // Per-descriptor trace record (device memory), one per ring slot.

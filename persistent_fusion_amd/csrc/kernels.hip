@@ -609,7 +609,13 @@ __device__ __forceinline__ void doorbell_loop(const KArgs& a) {
       release_workers(a, tiles0);
       return;
     }
-    if (drained && a.idle_exit_ticks && now_ticks() - last_work > a.idle_exit_ticks) {
+    bool yield = false;  // the host asks the kernel to give the GPU back now
+    if (drained) {
+      uint64_t y = 0;
+      if (lane_id() == 0) y = ld_rlx_sys(&a.hctl->yield_req);
+      yield = bcast64(y) != 0;
+    }
+    if (drained && (yield || (a.idle_exit_ticks && now_ticks() - last_work > a.idle_exit_ticks))) {
       // idle for too long: announce the exit, then look at the tails again.
       // The re-read cannot overtake the announcement on its way to host
       // memory, and the host reads the announcement after storing a tail, so

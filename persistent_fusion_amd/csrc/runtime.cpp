@@ -262,7 +262,7 @@ bool overlaps(const Range& a, const Range& b) {
 // ---------------------------------------------------------------------------
 // validation
 
-int validate(const gpuos_op& o, uint32_t index) {
+int validate(const gpuos_op& o, uint32_t index, bool has_view = false) {
   const uint32_t op = o.opcode;
   if (op >= GPUOS_OP_COUNT) return fail(GPUOS_EINVAL, "op %u: unknown opcode %u", index, op);
   if (o.dtype > GPUOS_F16) return fail(GPUOS_EINVAL, "op %u: unknown dtype %u", index, o.dtype);
@@ -353,6 +353,23 @@ int validate(const gpuos_op& o, uint32_t index) {
   for (int q = 0; q < R.nr; ++q)
     if (R.r[q].hi - R.r[q].lo > kMaxExtentBytes)
       return fail(GPUOS_EINVAL, "op %u: an operand spans more than 4 GiB - 1 MiB", index);
+  // In place: tiles run concurrently, so an output may overlap only a data
+  // input that is exactly it, read element for element (no cyclic reuse),
+  // and only in opcodes whose tiles read an element just where they write it.
+  // (A view's overlap rule is checked with the view.)
+  if (!has_view) {
+    const bool same_index = (is_elementwise(op) && op != GPUOS_OP_GATHER) || op == GPUOS_OP_ROW_SOFTMAX ||
+                            op == GPUOS_OP_RMSNORM || op == GPUOS_OP_ROPE;
+    // data inputs come first in op_ranges: in[0], then in[1] for binary ops
+    const int n_data = is_elementwise(op) && is_binary(op) ? 2 : 1;
+    for (int q = 0; q < R.nr; ++q) {
+      if (!overlaps(R.w, R.r[q])) continue;
+      const bool exact = R.r[q].lo == R.w.lo && R.r[q].hi == R.w.hi;
+      if (!(same_index && q < n_data && exact))
+        return fail(GPUOS_EINVAL, "op %u: the output overlaps an input without being that input "
+                    "read element for element", index);
+    }
+  }
   return 0;
 }
 
@@ -670,6 +687,8 @@ struct gpuos_ctx {
   bool poisoned = false;
   bool stopped = false;     // STOP published; no more submissions
   bool exited = false;      // resident kernel has exited
+  bool parked = false;      // the kernel left at gpuos_yield; the next flush
+  uint64_t park_tiles = 0;  // with work relaunches it from this ticket
   bool leaked = false;      // kernel did not exit: memory must not be freed
   bool timing = false;      // ev_start/ev_end bracket a launch not yet counted
   uint32_t epoch = 0;       // launches so far
@@ -1396,7 +1415,7 @@ int wait_kernel_end(gpuos_ctx* c, int64_t timeout_ns) {
 // after an idle period, waits for its launch to end and launches it again.
 // A kernel that ended without announcing an exit has failed.
 int keep_running(gpuos_ctx* c, bool query_stream) {
-  if (c->host_only || c->exited) return 0;
+  if (c->host_only || c->exited || c->parked) return 0;
   bool gone = load_acq(&c->hctl->exit_epoch) == c->epoch;
   if (!gone && load_acq(&c->hctl->exit_req) == c->epoch) {
     // the doorbell is deciding whether to leave: it either completes the exit
@@ -1533,6 +1552,11 @@ int publish_one(gpuos_ctx* c, Planned& pl) {
 int flush_impl(gpuos_ctx* c) {
   if (check_device_error(c)) return GPUOS_EDEVICE;
   if (c->staged.empty()) return 0;
+  if (c->parked) {  // relaunch first: publication may wait for ring space
+    const int rl = launch_kernel(c, c->park_tiles);
+    if (rl) return rl;
+    c->parked = false;
+  }
   ++c->st.flushes;
   std::vector<Planned>& plan = c->plan;
   plan.clear();
@@ -1863,7 +1887,7 @@ int submit_impl(gpuos_ctx* c, const gpuos_op* ops, const gpuos_view* views, uint
   // validate everything before staging anything
   std::vector<ViewDesc> vd(views ? n : 0);
   for (uint32_t i = 0; i < n; ++i) {
-    int rc = validate(ops[i], i);
+    int rc = validate(ops[i], i, views && views[i].ndim);
     if (rc) return rc;
     if (views && (rc = normalize_view(ops[i], views[i], i, vd[i]))) return rc;
     for (int k = 0; k < 4; ++k) {
@@ -1892,7 +1916,10 @@ int submit_impl(gpuos_ctx* c, const gpuos_op* ops, const gpuos_view* views, uint
     }
   }
   auto retired = [c](uint64_t id) { return id_retired(c, id); };
-  c->staged.reserve(c->staged.size() + n);
+  // geometric growth: reserving exactly size + n on every call would copy the
+  // whole staged list on each one-op submit
+  if (c->staged.size() + n > c->staged.capacity())
+    c->staged.reserve(std::max(2 * c->staged.capacity(), c->staged.size() + n));
   for (uint32_t i = 0; i < n; ++i) {
     Staged& s = c->staged.emplace_back();
     s.op = ops[i];
@@ -2028,6 +2055,11 @@ int gpuos_trace_read(gpuos_ctx* c, gpuos_trace_rec* out, uint32_t max, uint32_t*
 int gpuos_stop(gpuos_ctx* c, int64_t timeout_ns) {
   if (!c) return fail(GPUOS_EINVAL, "null context");
   if (c->host_only || c->exited) return 0;
+  if (c->parked && c->staged.empty()) {  // not running and nothing to run
+    c->stopped = true;
+    c->exited = true;
+    return check_device_error(c) ? GPUOS_EDEVICE : 0;
+  }
   if (c->leaked) return fail(GPUOS_ETIMEDOUT, "resident kernel did not exit");
   int rc = 0;
   if (!c->stopped) {
@@ -2049,6 +2081,39 @@ int gpuos_stop(gpuos_ctx* c, int64_t timeout_ns) {
   account_launch(c);
   if (check_device_error(c)) return GPUOS_EDEVICE;
   return rc;
+}
+
+int gpuos_yield(gpuos_ctx* c, int64_t timeout_ns) {
+  if (!c) return fail(GPUOS_EINVAL, "null context");
+  if (c->stopped) return fail(GPUOS_ESTATE, "context is stopped");
+  if (c->host_only || c->exited || c->parked) return 0;
+  int rc = flush_impl(c);
+  if (!rc) rc = sync_impl(c, 0, timeout_ns);
+  if (rc) return rc;
+  // the doorbell wave leaves once the queue is drained, with the same exit
+  // handshake as an idle exit; it may also have idled out already
+  std::atomic_thread_fence(std::memory_order_seq_cst);
+  store_rel(&c->hctl->yield_req, 1);
+  const auto t0 = std::chrono::steady_clock::now();
+  while (load_acq(&c->hctl->exit_epoch) != c->epoch) {
+    if (check_device_error(c)) {
+      store_rel(&c->hctl->yield_req, 0);
+      return GPUOS_EDEVICE;
+    }
+    if (timeout_ns >= 0 &&
+        std::chrono::steady_clock::now() - t0 > std::chrono::nanoseconds(timeout_ns)) {
+      store_rel(&c->hctl->yield_req, 0);
+      return fail(GPUOS_ETIMEDOUT, "yield: the resident kernel did not leave");
+    }
+    std::this_thread::sleep_for(std::chrono::microseconds(2));
+  }
+  store_rel(&c->hctl->yield_req, 0);
+  rc = wait_kernel_end(c, timeout_ns);
+  if (rc) return rc;
+  account_launch(c);
+  c->park_tiles = load_acq(&c->hctl->exit_tiles);
+  c->parked = true;
+  return 0;
 }
 
 int gpuos_destroy(gpuos_ctx* c, int64_t timeout_ns) {

@@ -14,6 +14,7 @@ from typing import Callable, Dict, Iterable, List, Optional, Sequence
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libgpuos.so")
+ABI_VERSION = 2  # GPUOS_ABI_VERSION of the header this binding follows
 
 # status codes
 OK, EINVAL, ENOMEM, EAGAIN, ETIMEDOUT, EDEVICE, ESTATE = 0, -1, -2, -3, -4, -5, -6
@@ -78,7 +79,7 @@ EXPORTS = (
     "gpuos_abi_version", "gpuos_last_error", "gpuos_config_default", "gpuos_create",
     "gpuos_submit", "gpuos_flush", "gpuos_sync", "gpuos_query", "gpuos_get_stats",
     "gpuos_trace_read", "gpuos_stop", "gpuos_destroy", "gpuos_baseline_run", "gpuos_submit_views",
-    "gpuos_graph_create", "gpuos_graph_launch", "gpuos_graph_destroy",
+    "gpuos_graph_create", "gpuos_graph_launch", "gpuos_graph_destroy", "gpuos_yield",
     "gpuos_debug_read_desc", "gpuos_debug_published", "gpuos_debug_seq_of", "gpuos_debug_retire",
 )
 
@@ -108,6 +109,7 @@ def lib() -> C.CDLL:
         "gpuos_get_stats": (C.c_int, [P, C.POINTER(GpuosStats)]),
         "gpuos_trace_read": (C.c_int, [P, C.POINTER(GpuosTraceRec), C.c_uint32, C.POINTER(C.c_uint32)]),
         "gpuos_stop": (C.c_int, [P, C.c_int64]),
+        "gpuos_yield": (C.c_int, [P, C.c_int64]),
         "gpuos_destroy": (C.c_int, [P, C.c_int64]),
         "gpuos_baseline_run": (C.c_int, [C.c_int, C.POINTER(GpuosOp), C.c_uint32, C.c_int, P]),
         "gpuos_graph_create": (C.c_int, [C.c_int, C.POINTER(GpuosOp), C.c_uint32, C.c_int, C.POINTER(P)]),
@@ -287,6 +289,10 @@ class Context:
 
     def retire(self, ring: int, upto: int) -> None:
         _check(self._lib.gpuos_debug_retire(self.handle, ring, upto), "gpuos_debug_retire")
+
+    def yield_gpu(self, timeout_s: float = 30.0) -> None:
+        """gpuos_yield: let the resident kernel leave once the queue is done."""
+        _check(self._lib.gpuos_yield(self.handle, int(timeout_s * 1e9)), "gpuos_yield")
 
     def stop(self, timeout_s: float = 30.0) -> None:
         _check(self._lib.gpuos_stop(self.handle, int(timeout_s * 1e9)), "gpuos_stop")

@@ -1,0 +1,414 @@
+"""PyTorch front end: eager elementwise ops batched into the resident queue.
+
+Idea (4) of "GPUOS: A GPU Operating System Primitive for Transparent
+Operation Fusion" (section "The Paper") is to intercept PyTorch's dispatch so
+that an unmodified eager program's small ops are batched into the persistent
+kernel's queue instead of being launched one by one.  :class:`GpuosMode` is
+that interception, as a ``TorchDispatchMode``:
+
+* An elementwise op on CUDA tensors of the mode's device (``add``, ``mul``
+  by a tensor or a scalar, ``relu``, ``exp``, ``clone``, and the in-place
+  ``add_``, ``mul_``, ``relu_``), in fp32, bf16, fp16 or (add, mul, relu)
+  int32, with broadcastable shapes of at most 4 non-trivial dimensions, is
+  not run: its output tensor is allocated (torch supplies memory only) and
+  the op is queued as a gpuos op with a view (strides from the broadcast),
+  and the output tensor is returned at once.
+* An op that only makes a new view of existing memory (``t``, ``view``,
+  ``expand``, ``slice`` and the like) runs at once: it touches no element.
+* Any other op, and leaving the mode, first flushes and waits for the queued
+  ops and lets the resident kernel leave (``gpuos_yield``: while it is
+  resident it holds every compute unit's registers, so no PyTorch kernel
+  could start), then runs in PyTorch.  So every value PyTorch code can
+  observe is final, and the ordering among queued ops comes from the
+  runtime's hazard tracking.  The next queued op relaunches the kernel.
+* Before the first queued op after PyTorch work, the current stream is
+  synchronised, so the queue never reads a tensor a PyTorch kernel is still
+  writing.  Every tensor a queued op touches is kept alive until the wait,
+  so the caching allocator cannot hand its memory to another tensor first.
+
+The decision whether and how to queue an op (:func:`plan_op`) only looks at
+tensor metadata and is testable without a GPU.
+"""
+
+from __future__ import annotations
+
+from typing import Optional, Sequence
+
+from . import gpuos
+
+_DTYPES = {}  # torch dtype -> gpuos dtype name (filled lazily: torch is optional at import)
+
+
+def _dtype_name(t) -> Optional[str]:
+    import torch
+
+    if not _DTYPES:
+        _DTYPES.update({torch.float32: "f32", torch.bfloat16: "bf16", torch.float16: "f16",
+                        torch.int32: "i32"})
+    return _DTYPES.get(t.dtype)
+
+
+_TABLE: dict = {}
+
+
+def _ops():
+    if _TABLE:
+        return _TABLE
+    import torch
+
+    a = torch.ops.aten
+    _TABLE.update({
+        a.add.Tensor: ("add", False), a.mul.Tensor: ("mul", False), a.mul.Scalar: ("scale", False),
+        a.relu.default: ("relu", False), a.exp.default: ("exp", False),
+        a.clone.default: ("copy", False),
+        a.add_.Tensor: ("add", True), a.mul_.Tensor: ("mul", True), a.relu_.default: ("relu", True),
+    })
+    return _TABLE
+
+
+_META: set = set()
+
+
+def _metadata_ops():
+    """aten ops that only make a new view of existing memory: they read and
+    write no element, so they run at once, with no wait for the queue."""
+    if _META:
+        return _META
+    import torch
+
+    a = torch.ops.aten
+    for name, overloads in (("t", ("default",)), ("transpose", ("int",)), ("permute", ("default",)),
+                            ("view", ("default",)), ("_unsafe_view", ("default",)),
+                            ("expand", ("default",)), ("slice", ("Tensor",)), ("select", ("int",)),
+                            ("unsqueeze", ("default",)), ("squeeze", ("default", "dim", "dims")),
+                            ("as_strided", ("default",)), ("detach", ("default",)),
+                            ("alias", ("default",)), ("split", ("Tensor",)), ("unbind", ("int",)),
+                            ("diagonal", ("default",))):
+        op = getattr(a, name, None)
+        for ov in overloads:
+            f = getattr(op, ov, None) if op is not None else None
+            if f is not None:
+                _META.add(f)
+    return _META
+
+
+def _broadcast(shapes):
+    """The broadcast shape of ``shapes`` (numpy's rule), or None."""
+    nd = max(len(s) for s in shapes)
+    out = [1] * nd
+    for s in shapes:
+        for i, e in enumerate(s):
+            d = nd - len(s) + i
+            if e != 1:
+                if out[d] != 1 and out[d] != e:
+                    return None
+                out[d] = e
+    return out
+
+
+def _strides_over(t, shape):
+    """Element strides of tensor ``t`` read over the broadcast ``shape``
+    (0 along every broadcast dimension)."""
+    off = len(shape) - t.dim()
+    st = [0] * len(shape)
+    ts = t.stride()
+    for i, e in enumerate(t.shape):
+        if e != 1:
+            st[off + i] = ts[i]
+    return st
+
+
+def _squeeze(shape: Sequence[int], strides: Sequence[Sequence[int]]):
+    """Drops extent-1 dimensions (their strides never matter)."""
+    keep = [d for d, e in enumerate(shape) if e != 1]
+    return [shape[d] for d in keep], [[st[d] for d in keep] for st in strides]
+
+
+def plan_op(func, args, kwargs, device):
+    """How an aten call on tensors of ``device`` (a torch.device) would be
+    queued: None if it is not interceptable, else (kind, dtype name, alpha,
+    out shape, in-place, inputs, view shape, view strides [out, in0, in1]).
+    Pure metadata: no GPU work."""
+    import torch
+
+    table = _ops()
+    if func not in table:
+        return None
+    kind, inplace = table[func]
+    kwargs = kwargs or {}
+    if kind == "add" and kwargs.get("alpha", 1) != 1:
+        return None
+    if kind == "copy" and kwargs.get("memory_format", None) not in (None, torch.preserve_format):
+        return None
+    extra = set(kwargs) - {"alpha", "memory_format"}
+    if extra:
+        return None
+    alpha = 0.0
+    if kind == "scale":
+        x, s = args[0], args[1]
+        if not isinstance(s, (int, float)) or isinstance(s, bool):
+            return None
+        alpha, tens = float(s), [x]
+    elif kind == "mul" and len(args) == 2 and type(args[1]) in (int, float):
+        # ``x * 0.5`` reaches the dispatcher as mul.Tensor with a Python number
+        if not isinstance(args[0], torch.Tensor):
+            return None
+        kind, alpha, tens = "scale", float(args[1]), [args[0]]
+    elif kind in ("add", "mul"):
+        if len(args) != 2 or not all(isinstance(a, torch.Tensor) for a in args):
+            return None
+        tens = list(args)
+        # a Python number multiplying a tensor arrives wrapped as a 0-dim CPU
+        # tensor: that is SCALE
+        if kind == "mul" and args[1].dim() == 0 and args[1].device.type == "cpu" and \
+                args[0].device == device and args[1].dtype in (torch.float32, torch.float64):
+            if args[0].dtype not in (torch.float32, torch.bfloat16, torch.float16):
+                return None
+            kind, alpha, tens = "scale", float(args[1].item()), [args[0]]
+    else:
+        if len(args) != 1:
+            return None
+        tens = [args[0]]
+    dev = device
+    dt = _dtype_name(tens[0])
+    if dt is None:
+        return None
+    for t in tens:
+        if t.device != dev or t.dtype != tens[0].dtype or t.requires_grad:
+            return None
+    if dt == "i32" and kind not in ("add", "mul", "relu", "copy"):
+        return None
+    if any(t.numel() == 0 for t in tens):
+        return None
+    shape = _broadcast([t.shape for t in tens])
+    if shape is None:
+        return None
+    shape = tuple(shape)
+    n = 1
+    for e in shape:
+        n *= e
+    if n > (1 << 30):
+        return None
+    if inplace and tuple(tens[0].shape) != shape:
+        return None
+    # strides of each operand over the output's index space (0 = broadcast)
+    out_strides = []
+    if inplace:
+        out_strides = list(tens[0].stride())
+    else:
+        acc = 1
+        for e in reversed(shape):
+            out_strides.append(acc)
+            acc *= e
+        out_strides.reverse()
+    ins = [_strides_over(t, shape) for t in tens]
+    if any(s < 0 for st in [out_strides] + ins for s in st):
+        return None
+    if inplace:
+        # the runtime takes an in-place output only over itself under the same
+        # view, and never one that names an element twice
+        o = tens[0]
+        if any(st == 0 and e > 1 for st, e in zip(out_strides, shape)):
+            return None
+        for t, st in zip(tens[1:], ins[1:]):
+            if t.untyped_storage().data_ptr() == o.untyped_storage().data_ptr() and \
+                    (t.data_ptr() != o.data_ptr() or st != out_strides):
+                return None
+    while len(ins) < 2:
+        ins.append([0] * len(shape))
+    vshape, vstr = _squeeze(list(shape), [out_strides] + ins)
+    if len(vshape) > 4:
+        return None
+    if not vshape:  # a single element
+        vshape, vstr = [1], [[1], [1 if len(tens) > 0 else 0], [1 if len(tens) > 1 else 0]]
+    return kind, dt, alpha, shape, inplace, tens, vshape, vstr
+
+
+class GpuosMode:
+    """Context manager: ``with GpuosMode(): ...`` runs the block's eligible
+    elementwise ops through one resident gpuos context (see the module
+    docstring).  ``stats`` counts queued and passed-through ops.
+
+    Queued ops are written into a preallocated gpuos_op / gpuos_view batch
+    and handed to ``gpuos_submit_views`` and flushed ``batch`` at a time (and
+    before any wait), so an error the runtime finds in an op surfaces at that
+    call, and the device works on one batch while Python fills the next."""
+
+    def __init__(self, device: int = 0, batch: int = 64, **cfg):
+        from torch.utils._python_dispatch import TorchDispatchMode
+
+        outer = self
+
+        class _Mode(TorchDispatchMode):
+            def __torch_dispatch__(self, func, types, args=(), kwargs=None):
+                return outer._dispatch(func, args, kwargs)
+
+        import torch
+
+        self._mode = _Mode()
+        self.device = device
+        self._torch_device = torch.device("cuda", device)
+        self.ctx = gpuos.Context(device, **cfg)
+        self._batch = max(1, batch)
+        self._ops = (gpuos.GpuosOp * self._batch)()
+        self._views = (gpuos.GpuosView * self._batch)()
+        self._k = 0         # ops in the batch
+        self._unsynced = False  # flushed ops not yet waited for
+        self._keep: list = []
+        self._torch_dirty = True
+        self._table = _ops()
+        self._meta = _metadata_ops()
+        self._opcode = {k: gpuos.OPCODES[k] for k in ("add", "mul", "scale", "relu", "exp", "copy")}
+        self._dtype = {torch.float32: gpuos.DTYPES["f32"], torch.bfloat16: gpuos.DTYPES["bf16"],
+                       torch.float16: gpuos.DTYPES["f16"], torch.int32: gpuos.DTYPES["i32"]}
+        self._i32 = torch.int32
+        self._empty_like = torch.empty_like
+        self._empty = torch.empty
+        self._tensor = torch.Tensor
+        self.stats = {"queued": 0, "metadata": 0, "passed_through": 0, "syncs": 0}
+
+    # ------------------------------------------------------------------
+    def _submit_batch(self) -> None:
+        k = self._k
+        if not k:
+            return
+        self._k = 0
+        lib = self.ctx._lib
+        rc = lib.gpuos_submit_views(self.ctx.handle, self._ops, self._views, k, None)
+        if rc < 0:
+            raise gpuos.GpuosError(rc, "gpuos_submit_views")
+        # published at once, so the device runs this batch while Python queues
+        # the next
+        self.ctx.flush()
+        self._unsynced = True
+
+    def sync(self) -> None:
+        """Makes every queued op's result final."""
+        self._submit_batch()
+        if self._unsynced:
+            self.ctx.sync(0, 120.0)
+            self.stats["syncs"] += 1
+            self._unsynced = False
+        self._keep.clear()
+
+    def _fast(self, func, args, kwargs):
+        """(kind, dtype code, alpha, in-place, inputs) for the common case:
+        contiguous operands of one shape and dtype on the mode's device, or
+        None (then :func:`plan_op` decides)."""
+        if kwargs:
+            return None
+        ent = self._table.get(func)
+        if ent is None:
+            return None
+        kind, inplace = ent
+        x = args[0]
+        if type(x) is not self._tensor or x.get_device() != self.device or \
+                x.requires_grad or not x.is_contiguous():
+            return None
+        dt = self._dtype.get(x.dtype)
+        if dt is None:
+            return None
+        alpha = 0.0
+        if kind == "mul" and type(args[1]) in (float, int):
+            kind = "scale"
+        if kind == "scale":
+            s = args[1]
+            if type(s) is not float and type(s) is not int:
+                return None
+            alpha, tens = float(s), (x,)
+        elif kind in ("add", "mul"):
+            y = args[1]
+            if type(y) is not self._tensor or y.get_device() != self.device or \
+                    y.requires_grad or not y.is_contiguous() or y.dtype != x.dtype or y.shape != x.shape:
+                return None
+            if inplace and y.data_ptr() != x.data_ptr() and \
+                    y.untyped_storage().data_ptr() == x.untyped_storage().data_ptr():
+                return None  # in place over a shifted part of itself
+            tens = (x, y)
+        else:
+            tens = (x,)
+        if x.dtype == self._i32 and kind not in ("add", "mul", "relu", "copy"):
+            return None
+        n = x.numel()
+        if n == 0 or n > (1 << 30):
+            return None
+        return kind, dt, alpha, inplace, tens
+
+    def _queue(self, kind, dt, alpha, out, tens, vshape=None, vstr=None) -> None:
+        k = self._k
+        o = self._ops[k]
+        o.opcode = self._opcode[kind]
+        o.dtype = dt
+        o.n = out.numel()
+        o.out = out.data_ptr()
+        o.in_[0] = tens[0].data_ptr()
+        o.in_[1] = tens[1].data_ptr() if len(tens) > 1 else None
+        o.alpha = alpha
+        v = self._views[k]
+        if vshape is None:
+            v.ndim = 0
+        else:
+            v.ndim = len(vshape)
+            for d, e in enumerate(vshape):
+                v.shape[d] = e
+            for j in range(3):
+                st = vstr[j]
+                for d in range(len(vshape)):
+                    v.stride[j][d] = st[d]
+        self._keep.extend(tens)
+        self._keep.append(out)
+        self._k = k + 1
+        if self._k == self._batch:
+            self._submit_batch()
+
+    def _dispatch(self, func, args, kwargs):
+        fast = self._fast(func, args, kwargs)
+        if fast is not None:
+            kind, dt, alpha, inplace, tens = fast
+            if self._torch_dirty:
+                self._sync_torch()
+            out = tens[0] if inplace else self._empty_like(tens[0])
+            self._queue(kind, dt, alpha, out, tens)
+            self.stats["queued"] += 1
+            return out
+        if func in self._meta:
+            self.stats["metadata"] += 1
+            return func(*args, **(kwargs or {}))
+        plan = plan_op(func, args, kwargs, self._torch_device)
+        if plan is None:
+            # the queue finishes and the resident kernel gives the GPU back
+            # (while it is resident no other kernel can start)
+            self.sync()
+            self.ctx.yield_gpu()
+            self.stats["passed_through"] += 1
+            self._torch_dirty = True
+            return func(*args, **(kwargs or {}))
+        kind, dt, alpha, shape, inplace, tens, vshape, vstr = plan
+        if self._torch_dirty:
+            self._sync_torch()
+        out = tens[0] if inplace else self._empty(shape, dtype=tens[0].dtype, device=tens[0].device)
+        self._queue(kind, gpuos.DTYPES[dt], alpha, out, tens, vshape, vstr)
+        self.stats["queued"] += 1
+        return out
+
+    def _sync_torch(self) -> None:
+        import torch
+
+        torch.cuda.current_stream(self.device).synchronize()
+        self._torch_dirty = False
+
+    # ------------------------------------------------------------------
+    def __enter__(self):
+        self._mode.__enter__()
+        return self
+
+    def __exit__(self, *exc):
+        try:
+            self.sync()
+            self.ctx.yield_gpu()
+        finally:
+            self._mode.__exit__(*exc)
+        return False
+
+    def close(self) -> None:
+        self.ctx.destroy()

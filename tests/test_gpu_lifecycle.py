@@ -126,3 +126,40 @@ def test_never_idle_exit():
         ctx.destroy()
     assert st["launches"] == 1
     _check_queue(wl, t)
+
+
+def test_yield_gives_the_gpu_back_and_the_next_flush_relaunches():
+    """gpuos_yield: once the queue is done the kernel leaves at once (a
+    PyTorch kernel launched next runs without waiting for the idle period),
+    and the next flush relaunches it without losing or repeating an op."""
+    import torch
+
+    say("lifecycle: yield")
+    wl = workloads.gen_elementwise_queue(seed=5)
+    t = runner.to_device(wl)
+    addr = runner.addr_fn(t, wl)
+    x = torch.randn(1024, device="cuda")
+    ctx = gpuos.Context(0, idle_exit_ms=60000)  # no idle exit: only yield ends a launch
+    try:
+        id_of = {}
+        n = len(wl.ops)
+        waits = []
+        for k in range(4):
+            _submit_range(ctx, wl, addr, k * n // 4, (k + 1) * n // 4, id_of)
+            ctx.flush()
+            ctx.yield_gpu()
+            ctx.yield_gpu()  # parked: returns at once
+            t0 = time.perf_counter()
+            y = x * 2.0  # a torch kernel while the context is parked
+            torch.cuda.synchronize()
+            waits.append(time.perf_counter() - t0)
+            assert torch.equal(y, x * 2.0)
+        ctx.sync(0, 30.0)
+        ctx.stop()
+        st = ctx.stats()
+    finally:
+        ctx.destroy()
+    say(f"launches {st['launches']}, torch waits {[round(w * 1e3, 2) for w in waits]} ms")
+    assert st["launches"] == 4
+    assert max(waits) < 1.0  # far below the 60 s idle period
+    _check_queue(wl, t)

@@ -1,0 +1,114 @@
+"""GPU: the PyTorch front end (eager elementwise ops queued into the resident
+kernel).  Results are compared with the same program run by PyTorch itself:
+bit for bit for ops with exactly rounded results (add, mul, scale, relu,
+copy; torch rounds them the same way), within the exp tolerance otherwise."""
+
+import numpy as np
+import pytest
+
+from persistent_fusion_amd import gpuos
+
+pytestmark = pytest.mark.gpu
+
+
+def _need_gpu():
+    import torch
+
+    assert torch.cuda.is_available(), "GPU tests need a GPU"
+    gpuos.lib()
+
+
+def say(msg):
+    print(msg, flush=True)
+
+
+def _program(torch, x, b, s, dtype):
+    """A small eager program: broadcasts, in-place ops, a transpose, a scalar."""
+    y = x * b                # [R, C] * [C]
+    y = y + x                # plain
+    y.relu_()                # in place
+    z = y.t() * s            # transposed [C, R] * [R]
+    z = z * 0.5              # scalar -> SCALE
+    w = z.clone()
+    w.add_(z)
+    if dtype != torch.int32:
+        e = (w * 0.01).exp()
+    else:
+        e = w
+    return y, z, w, e
+
+
+@pytest.mark.parametrize("dtype_name", ["float32", "bfloat16", "float16", "int32"])
+def test_mode_matches_eager(dtype_name):
+    _need_gpu()
+    import torch
+
+    from persistent_fusion_amd.torch_mode import GpuosMode
+
+    say(f"torch mode {dtype_name}")
+    dtype = getattr(torch, dtype_name)
+    g = torch.Generator(device="cpu").manual_seed(60)
+    R, Cn = 37, 300
+
+    def draw(*shape):
+        if dtype == torch.int32:
+            return torch.randint(-1000, 1000, shape, generator=g, dtype=torch.int32).cuda()
+        return torch.randn(*shape, generator=g).to(dtype).cuda()
+
+    x, b, s = draw(R, Cn), draw(Cn), draw(R)
+    want = _program(torch, x, b, s if dtype != torch.int32 else s, dtype) if dtype != torch.int32 else None
+    if dtype == torch.int32:
+        # torch's int32 mul by 0.5 promotes to float; the program keeps ints
+        def prog(x, b, s):
+            y = x * b
+            y = y + x
+            y.relu_()
+            z = y.t() * s
+            w = z.clone()
+            w.add_(z)
+            return y, z, w
+        want = prog(x, b, s)
+    mode = GpuosMode(0)
+    try:
+        with mode:
+            got = prog(x, b, s) if dtype == torch.int32 else _program(torch, x, b, s, dtype)
+    finally:
+        mode.close()
+    # every op is queued (the transpose only makes a view): nothing waits
+    assert mode.stats["queued"] >= 6 and mode.stats["passed_through"] == 0, mode.stats
+    assert mode.stats["metadata"] >= 1, mode.stats
+    for k, (gt, wt) in enumerate(zip(got, want)):
+        if k == 3 and dtype != torch.int32:  # exp: within the tolerance class
+            rt = {torch.float32: 1e-5, torch.bfloat16: 1e-2, torch.float16: 2e-3}[dtype]
+            assert torch.allclose(gt.float(), wt.float(), rtol=rt, atol=0), k
+        else:
+            assert torch.equal(gt, wt), k
+
+
+def test_mode_orders_around_torch_ops_and_keeps_memory():
+    """PyTorch ops between queued ops see final values; temporaries freed by
+    Python stay allocated until the queue has run."""
+    _need_gpu()
+    import torch
+
+    from persistent_fusion_amd.torch_mode import GpuosMode
+
+    say("torch mode with torch ops in between")
+    torch.manual_seed(61)
+    a = torch.randn(64, 64, device="cuda")
+    want_t = a
+    for _ in range(20):
+        want_t = torch.relu(want_t * 0.9 + a)
+        want_t = want_t @ a * 0.01  # a matmul: not intercepted
+    mode = GpuosMode(0)
+    try:
+        with mode:
+            t = a
+            for _ in range(20):
+                t = torch.relu(t * 0.9 + a)
+                t = t @ a * 0.01
+            got = t.clone()
+    finally:
+        mode.close()
+    assert mode.stats["queued"] > 40 and mode.stats["syncs"] >= 20
+    assert torch.equal(got, want_t)

@@ -44,7 +44,7 @@ def test_library_exports_every_declared_symbol():
     missing = [s for s in sorted(declared) if not hasattr(lib, s)]
     assert not missing, missing
     assert set(gpuos.EXPORTS) == declared
-    assert lib.gpuos_abi_version() == 2
+    assert lib.gpuos_abi_version() == 2 == gpuos.ABI_VERSION
 
 
 def test_fused_chain_becomes_one_descriptor():
@@ -274,6 +274,13 @@ def test_priority_ring_and_cross_ring_rules():
     (lambda: make_op("exp", buf(0), [buf(1)], n=10, dtype="i32"), "int32"),
     (lambda: make_op("scale", buf(0), [buf(1)], n=10, dtype="i32", alpha=2.0), "int32"),
     (lambda: make_op("gemv", buf(0), [buf(1)], aux=buf(2), n=4, dtype="f16", dims=(4, 8)), "fp16"),
+    # in place over a shifted copy of itself, cyclically, or where tiles read
+    # beyond the elements they write
+    (lambda: make_op("add", buf(0), [buf(0) + 4, buf(1)], n=10), "overlaps"),
+    (lambda: make_op("relu", buf(0), [buf(0)], n=10, src_len=(4, 0)), "overlaps"),
+    (lambda: make_op("row_sum", buf(0), [buf(0)], n=64, rows=2, row_len=32), "overlaps"),
+    (lambda: make_op("gemv", buf(0), [buf(0)], aux=buf(2), n=4, dims=(4, 4)), "overlaps"),
+    (lambda: make_op("rmsnorm", buf(0), [buf(1)], aux=buf(0), n=64, rows=2, row_len=32), "overlaps"),
 ])
 def test_validation_errors_stage_nothing(op, msg):
     with ctx() as c:
@@ -651,3 +658,14 @@ def test_graph_replay_poisons_only_buffers_written_whole_first():
     assert runner.poisonable(wl, wl.outputs) == []
     wl = workloads.gen_fused_chain(seed=5, n=1000)
     assert runner.poisonable(wl, ["y"]) == ["y"]
+
+
+def test_exact_in_place_ops_are_accepted():
+    with ctx() as c:
+        arr = (gpuos.GpuosOp * 4)(
+            make_op("add", buf(0), [buf(0), buf(1)], n=10),
+            make_op("relu", buf(0), [buf(0)], n=10, src_len=(12, 0)),
+            make_op("row_softmax", buf(2), [buf(2)], n=64, rows=2, row_len=32),
+            make_op("rope", buf(3), [buf(3)], aux=buf(4), n=64, rows=2, row_len=32),
+        )
+        c.submit(arr)

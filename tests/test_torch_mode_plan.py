@@ -1,0 +1,92 @@
+"""Host logic of the PyTorch front end: which aten calls are queued, and the
+views they become (metadata only, CPU tensors)."""
+
+import pytest
+
+torch = pytest.importorskip("torch")
+
+from persistent_fusion_amd.torch_mode import plan_op  # noqa: E402
+
+A = torch.ops.aten
+CPU = torch.device("cpu")
+_B = torch.zeros(8)
+_S = torch.zeros(4, 4)
+
+
+def test_broadcast_add_becomes_a_view():
+    x = torch.zeros(6, 40)
+    b = torch.zeros(40)
+    kind, dt, alpha, shape, inplace, tens, vshape, vstr = plan_op(A.add.Tensor, (x, b), {}, CPU)
+    assert (kind, dt, shape, inplace) == ("add", "f32", (6, 40), False)
+    assert vshape == [6, 40]
+    assert vstr == [[40, 1], [40, 1], [0, 1]]
+
+
+def test_scalar_mul_is_scale_and_transposed_input_keeps_strides():
+    x = torch.zeros(8, 5).t()  # (5, 8), strides (1, 5)
+    kind, dt, alpha, shape, inplace, tens, vshape, vstr = plan_op(A.mul.Scalar, (x, 2.5), {}, CPU)
+    assert (kind, alpha, shape) == ("scale", 2.5, (5, 8))
+    assert vstr[0] == [8, 1] and vstr[1] == [1, 5] and vstr[2] == [0, 0]
+
+
+def test_in_place_and_unit_dimensions():
+    x = torch.zeros(3, 1, 7, dtype=torch.float16)
+    y = torch.zeros(1, 1, 7, dtype=torch.float16)
+    kind, dt, alpha, shape, inplace, tens, vshape, vstr = plan_op(A.add_.Tensor, (x, y), {}, CPU)
+    assert (kind, dt, inplace, shape) == ("add", "f16", True, (3, 1, 7))
+    assert vshape == [3, 7] and vstr == [[7, 1], [7, 1], [0, 1]]
+
+
+@pytest.mark.parametrize("call", [
+    lambda: (A.add.Tensor, (torch.zeros(4), torch.zeros(4)), {"alpha": 2}),          # alpha
+    lambda: (A.add.Tensor, (torch.zeros(4), torch.zeros(4, dtype=torch.float64)), {}),  # mixed dtypes
+    lambda: (A.add.Tensor, (torch.zeros(4, dtype=torch.float64), torch.zeros(4, dtype=torch.float64)), {}),
+    lambda: (A.exp.default, (torch.zeros(4, dtype=torch.int32),), {}),                # exp on int32
+    lambda: (A.mm.default, (torch.zeros(2, 2), torch.zeros(2, 2)), {}),               # not elementwise
+    lambda: (A.add.Tensor, (torch.zeros(2, 2, 2, 2, 2), torch.zeros(2, 2, 2, 2, 2)), {}),  # 5-D
+    lambda: (A.add.Tensor, (torch.zeros(0), torch.zeros(0)), {}),                     # empty
+    lambda: (A.add_.Tensor, (torch.zeros(4), torch.zeros(3, 4)), {}),                 # in-place broadcast of self
+    lambda: (A.add_.Tensor, (_B[:4], _B[1:5]), {}),                                   # in place over a shifted self
+    lambda: (A.add_.Tensor, (_S, _S.t()), {}),                                        # in place over a transposed self
+    lambda: (A.relu_.default, (torch.zeros(1, 4).expand(3, 4),), {}),                 # output names elements twice
+])
+def test_not_intercepted(call):
+    func, args, kwargs = call()
+    assert plan_op(func, args, kwargs, CPU) is None
+
+
+def test_other_device_is_not_intercepted():
+    x = torch.zeros(4)
+    assert plan_op(A.relu.default, (x,), {}, torch.device("cuda", 0)) is None
+
+
+def test_python_scalar_multiplier_is_scale():
+    x = torch.zeros(10)
+    kind, dt, alpha, shape, inplace, tens, vshape, vstr = plan_op(A.mul.Tensor, (x, torch.tensor(0.25)), {}, CPU)
+    assert (kind, alpha, shape) == ("scale", 0.25, (10,))
+
+
+def test_in_place_over_itself_is_intercepted():
+    x = torch.zeros(4, 4)
+    plan = plan_op(A.add_.Tensor, (x, x), {}, CPU)
+    assert plan is not None and plan[4] is True
+
+
+def test_python_number_in_mul_tensor_is_scale():
+    # ``x * 0.5`` reaches the dispatcher as mul.Tensor(x, 0.5)
+    x = torch.zeros(6)
+    kind, dt, alpha, shape, inplace, tens, vshape, vstr = plan_op(A.mul.Tensor, (x, 0.5), {}, CPU)
+    assert (kind, alpha, inplace, len(tens)) == ("scale", 0.5, False, 1)
+    kind, dt, alpha, shape, inplace, tens, vshape, vstr = plan_op(A.mul_.Tensor, (x, 3), {}, CPU)
+    assert (kind, alpha, inplace) == ("scale", 3.0, True)
+    assert plan_op(A.mul.Tensor, (torch.zeros(6, dtype=torch.int32), 2), {}, CPU) is None
+
+
+def test_metadata_only_ops_are_listed():
+    from persistent_fusion_amd.torch_mode import _metadata_ops
+
+    meta = _metadata_ops()
+    for f in (A.t.default, A.view.default, A.expand.default, A.slice.Tensor, A.transpose.int):
+        assert f in meta
+    for f in (A.add.Tensor, A.clone.default, A.sum.default, A.mm.default, A._to_copy.default):
+        assert f not in meta
