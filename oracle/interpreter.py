@@ -43,6 +43,17 @@ round-to-nearest-even narrowing to bf16):
   shape, reading operand k at element ``sum_j i_j * stride[k][j]`` from the
   operand's start and writing the output there; all inputs are read before
   the output is written.
+* A PROGRAM op (an operator defined while the persistent kernel runs:
+  runtime operator injection in "GPUOS: A GPU Operating System Primitive for
+  Transparent Operation Fusion", section "The Paper") runs its register
+  program at every element, one instruction at a time: registers r0..r7 hold
+  fp32 values (the op's inputs widened exactly in r0..n_inputs-1, +0 in the
+  rest), r8..r15 the program's constants; each instruction stores one fp32
+  result rounded to nearest even (division too; no fused multiply-add); MIN
+  and MAX return NaN for a NaN operand and order -0 below +0 (IEEE 754-2019
+  minimum / maximum); EXP is exp evaluated in fp64 and rounded to fp32.  The
+  result register is rounded once to the op's dtype.  A program with EXP is
+  in the tolerance class, with |result| as the error scale; otherwise exact.
 
 ``run`` also returns, for every element written by a reduction or a
 transcendental, the error scale the tolerance test uses: the sum of absolute
@@ -187,6 +198,77 @@ def _ew_values(k: str, dt: str, alpha: float, xr: np.ndarray, yr: Optional[np.nd
     return _store_from_f32(r32.astype(np.float32), dt), None
 
 
+def _bits(x: np.ndarray) -> np.ndarray:
+    return np.ascontiguousarray(x, dtype=np.float32).view(np.uint32)
+
+
+def _from_bits(u: np.ndarray) -> np.ndarray:
+    return np.ascontiguousarray(u, dtype=np.uint32).view(np.float32)
+
+
+def _p_min(a: np.ndarray, b: np.ndarray, smaller: bool) -> np.ndarray:
+    """IEEE 754-2019 minimum (smaller=True) / maximum: NaN if either operand
+    is NaN; of two equal values (+0 and -0 included) minimum takes the one
+    with the sign bit set, maximum the one without."""
+    lt, gt = (a < b, a > b) if smaller else (a > b, a < b)
+    eq_bits = (_bits(a) | _bits(b)) if smaller else (_bits(a) & _bits(b))
+    r = np.where(lt, a, np.where(gt, b, _from_bits(eq_bits)))
+    return np.where(np.isnan(a) | np.isnan(b), np.float32(np.nan), r).astype(np.float32)
+
+
+def _program_values(prog, dt: str, raws):
+    """Stored values of a PROGRAM op on its raw inputs, and the error scale
+    (None unless the program uses EXP)."""
+    n = raws[0].shape[0]
+    regs = [np.zeros(n, np.float32) for _ in range(8)]
+    for j, r in enumerate(raws):
+        regs[j] = _to_f32(r, dt).astype(np.float32)
+    consts = [np.float32(c) for c in prog.consts] + [np.float32(0.0)] * (8 - len(prog.consts))
+
+    def reg(i: int) -> np.ndarray:
+        return regs[i] if i < 8 else np.full(n, consts[i - 8], np.float32)
+
+    uses_exp = False
+    with np.errstate(all="ignore"):
+        for ins in prog.insns:
+            name, dst, src = ins[0], ins[1], ins[2:]
+            a = reg(src[0])
+            b = reg(src[1]) if len(src) > 1 else None
+            c = reg(src[2]) if len(src) > 2 else None
+            if name == "mov":
+                y = a.copy()
+            elif name == "add":
+                y = a + b
+            elif name == "sub":
+                y = a - b
+            elif name == "mul":
+                y = a * b
+            elif name == "div":
+                y = a / b
+            elif name == "min":
+                y = _p_min(a, b, True)
+            elif name == "max":
+                y = _p_min(a, b, False)
+            elif name == "neg":
+                y = _from_bits(_bits(a) ^ np.uint32(0x80000000))
+            elif name == "abs":
+                y = _from_bits(_bits(a) & np.uint32(0x7FFFFFFF))
+            elif name == "relu":
+                y = np.where(a > np.float32(0.0), a, np.float32(0.0))
+            elif name == "exp":
+                y = np.exp(a.astype(np.float64)).astype(np.float32)
+                uses_exp = True
+            elif name == "lt":
+                y = np.where(a < b, np.float32(1.0), np.float32(0.0))
+            elif name == "sel":
+                y = np.where(a != np.float32(0.0), b, c)
+            else:
+                raise OracleError(f"unknown program instruction {name}")
+            regs[dst] = np.asarray(y, dtype=np.float32)
+    res = reg(prog.result)
+    return _store_from_f32(res, dt), (np.abs(res.astype(np.float64)) if uses_exp else None)
+
+
 def view_offsets(shape, strides) -> np.ndarray:
     """Element offsets sum_j i_j * strides[j] of every index of ``shape``, in
     row-major index order."""
@@ -274,6 +356,13 @@ def apply_op(op: Op, bufs: Dict[str, np.ndarray], dtypes: Dict[str, str]) -> Opt
         src = _read(bufs, op.ins[0], src_n)
         _write(bufs, op.out, src[idx])
         return None
+
+    if k == "program":
+        if len(op.ins) != op.prog.n_inputs:
+            raise OracleError("program op with a wrong number of inputs")
+        vals, scale = _program_values(op.prog, dt, [_read(bufs, r, n) for r in op.ins])
+        _write(bufs, op.out, vals)
+        return scale
 
     if k in ("add", "mul", "scale", "relu", "exp", "silu_mul"):
         xr = _read_cyclic(bufs, op.ins[0], op.src_len[0], n)

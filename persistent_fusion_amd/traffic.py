@@ -46,6 +46,8 @@ def op_bytes(op: Op, scalar_bufs: Set[str] = frozenset()) -> int:
         return 2 * S * H * D + 4 * H * S + eb * H * D
     if k == "gather":
         return (eb + 4) * n + eb * n
+    if k == "program":
+        return eb * n * (len(op.ins) + 1)
     return 0
 
 

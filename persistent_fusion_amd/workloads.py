@@ -38,11 +38,26 @@ ROW_OPS = ("row_sum", "row_softmax", "rmsnorm")
 ALL_KINDS = (
     "nop", "copy", "gather", "add", "mul", "scale", "relu", "exp",
     "row_sum", "row_softmax", "rmsnorm", "rope", "gemv",
-    "attn_score", "attn_av", "silu_mul", "spin",
+    "attn_score", "attn_av", "silu_mul", "spin", "program",
 )
 
 NP_DTYPE = {"f32": np.float32, "bf16": np.uint16, "i32": np.int32, "f16": np.float16}
 ELEM_BYTES = {"f32": 4, "bf16": 2, "i32": 4, "f16": 2}
+
+
+@dataclass(frozen=True)
+class Program:
+    """The body of an op defined at run time: register instructions
+    ``(name, dst, *sources)`` (names as in gpuos_program: mov, add, sub, mul,
+    div, min, max, neg, abs, relu, exp, lt, sel), the number of data inputs
+    (registers 0..n_inputs-1), the result register and the constants held in
+    registers 8..15.  Data only: the oracle and the runtime each give it its
+    meaning."""
+
+    insns: Tuple[Tuple, ...]
+    n_inputs: int
+    result: int
+    consts: Tuple[float, ...] = ()
 
 
 @dataclass(frozen=True)
@@ -65,7 +80,8 @@ class Op:
     earlier ops in the same workload that this op must wait for, beyond the
     hazards the runtime derives from the byte ranges.  ``view`` (elementwise
     ops only) is (shape, out strides, in0 strides, in1 strides), strides in
-    elements from each operand's start.
+    elements from each operand's start.  A ``program`` op reads ``ins``
+    (one to three data operands) and runs ``prog``.
     """
 
     kind: str
@@ -84,6 +100,7 @@ class Op:
     transient: bool = False
     lc: bool = False
     view: Optional[Tuple[Tuple[int, ...], ...]] = None
+    prog: Optional[Program] = None
 
 
 @dataclass

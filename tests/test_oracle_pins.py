@@ -833,3 +833,181 @@ def test_small_decode_runs_and_feeds_back():
     # token t wrote its cache slot t
     assert not np.array_equal(out["K0"][:896], wl.buffers["K0"][:896])
     assert np.array_equal(out["K0"][2 * 896:], wl.buffers["K0"][2 * 896:])
+
+
+# ----------------------------------------------------------------------------
+# PROGRAM ops (operators defined at run time)
+
+from persistent_fusion_amd.workloads import Program  # noqa: E402
+
+NAN = float("nan")
+INF = float("inf")
+
+
+def _run_prog(prog, ins, dt="f32"):
+    """Runs one PROGRAM op over the given input columns; returns (out, scale)."""
+    npdt = {"f32": np.float32, "f16": np.float16}[dt]
+    n = len(ins[0])
+    bufs = {f"i{j}": np.asarray(c, npdt) for j, c in enumerate(ins)}
+    bufs["y"] = np.zeros(n, npdt)
+    op = Op("program", Ref("y"), tuple(Ref(f"i{j}") for j in range(len(ins))), n=n, dtype=dt, prog=prog)
+    wl = wl_of(bufs, [op])
+    out, scales = oracle.run(wl, scales=True)
+    return out["y"], scales.get("y")
+
+
+def _exact(scale) -> bool:
+    """Every element in the exact class (no error scale)."""
+    return scale is None or bool(np.all(np.isnan(scale)))
+
+
+def _one(name, *srcs_vals):
+    """A one-instruction program name(r0, r1, r2) over single values."""
+    k = len(srcs_vals)
+    prog = Program(((name, 3) + tuple(range(k)),), n_inputs=k, result=3)
+    y, _ = _run_prog(prog, [[v] for v in srcs_vals])
+    return float(y[0])
+
+
+@pytest.mark.parametrize("name,args,want", [
+    ("add", (1.5, 2.25), 3.75),
+    ("sub", (5.0, 3.0), 2.0),                 # operand order: a - b
+    ("sub", (3.0, 5.0), -2.0),
+    ("mul", (3.0, -0.5), -1.5),
+    ("div", (1.0, 3.0), struct.unpack("<f", bytes.fromhex("abaaaa3e"))[0]),  # 0x3EAAAAAB
+    ("div", (7.0, 2.0), 3.5),
+    ("div", (1.0, 0.0), INF),
+    ("div", (-1.0, 0.0), -INF),
+    ("div", (0.0, 0.0), NAN),
+    ("min", (2.0, 3.0), 2.0),
+    ("min", (3.0, 2.0), 2.0),
+    ("max", (2.0, 3.0), 3.0),
+    ("min", (1.0, NAN), NAN),
+    ("min", (NAN, 1.0), NAN),
+    ("max", (NAN, 1.0), NAN),
+    ("min", (-INF, 1.0), -INF),
+    ("relu", (-2.0,), 0.0),
+    ("relu", (2.0,), 2.0),
+    ("relu", (NAN,), 0.0),
+    ("exp", (0.0,), 1.0),
+    ("exp", (1.0,), f32(math.e)),
+    ("exp", (-INF,), 0.0),
+    ("exp", (100.0,), INF),
+    ("lt", (1.0, 2.0), 1.0),
+    ("lt", (2.0, 1.0), 0.0),
+    ("lt", (1.0, 1.0), 0.0),
+    ("lt", (NAN, 1.0), 0.0),
+    ("sel", (0.0, 5.0, 7.0), 7.0),
+    ("sel", (2.0, 5.0, 7.0), 5.0),
+    ("sel", (NAN, 5.0, 7.0), 5.0),             # NaN != 0
+    ("mov", (-3.25,), -3.25),
+    ("abs", (-INF,), INF),
+    ("neg", (2.5,), -2.5),
+])
+def test_program_instruction_values(name, args, want):
+    got = _one(name, *args)
+    if math.isnan(want):
+        assert math.isnan(got)
+    else:
+        assert bits32(got) == bits32(want), (name, args, got, want)
+
+
+def test_program_signed_zero_rules():
+    pz, nz = 0.0, -0.0
+    assert bits32(_one("min", pz, nz)) == 0x80000000 and bits32(_one("min", nz, pz)) == 0x80000000
+    assert bits32(_one("max", pz, nz)) == 0 and bits32(_one("max", nz, pz)) == 0
+    assert bits32(_one("neg", pz)) == 0x80000000
+    assert bits32(_one("abs", nz)) == 0
+    assert bits32(_one("relu", nz)) == 0
+    assert bits32(_one("sel", nz, 5.0, 7.0)) == bits32(7.0)   # -0 == 0
+    nan_neg = _one("neg", NAN)
+    assert math.isnan(nan_neg) and bits32(nan_neg) >> 31 == 1  # the sign of a NaN flips too
+
+
+def test_program_arithmetic_is_correctly_rounded_fp32():
+    # Python's double result rounded to fp32 is the correctly rounded fp32
+    # result of +, -, *, / on fp32 operands (53 >= 2 * 24 + 2: the double
+    # rounding is innocuous), an evaluation independent of numpy's float32 ops
+    rng = np.random.default_rng(70)
+    a = (rng.standard_normal(3000) * np.exp2(rng.integers(-30, 30, 3000))).astype(np.float32)
+    b = (rng.standard_normal(3000) * np.exp2(rng.integers(-30, 30, 3000))).astype(np.float32)
+    for name, fn in (("add", lambda x, y: x + y), ("sub", lambda x, y: x - y),
+                     ("mul", lambda x, y: x * y), ("div", lambda x, y: x / y)):
+        prog = Program(((name, 3, 0, 1),), n_inputs=2, result=3)
+        y, scale = _run_prog(prog, [a, b])
+        assert _exact(scale)
+        want = np.array([f32(fn(float(x), float(z))) for x, z in zip(a, b)], np.float32)
+        assert np.array_equal(y.view(np.uint32), want.view(np.uint32)), name
+
+
+def test_program_registers_start_at_plus_zero_and_constants():
+    # r5 is never written: it reads +0, so -0 + r5 = +0
+    prog = Program((("add", 3, 0, 5),), n_inputs=1, result=3)
+    y, _ = _run_prog(prog, [[-0.0, 2.0, NAN]])
+    assert bits32(y[0]) == 0 and y[1] == 2.0 and math.isnan(y[2])
+    # constants sit in r8..r15; the result may be any register
+    prog = Program((("mul", 3, 0, 9), ("add", 4, 3, 15)), n_inputs=1, result=4,
+                   consts=(0, 2.5, 0, 0, 0, 0, 0, -1.0))
+    y, _ = _run_prog(prog, [[2.0, -4.0]])
+    assert list(y) == [4.0, -11.0]
+    prog = Program((("mov", 1, 0),), n_inputs=1, result=10, consts=(0, 0, 7.5))
+    y, _ = _run_prog(prog, [[1.0, 2.0]])
+    assert list(y) == [7.5, 7.5]
+    # a later instruction sees an earlier one's result; inputs can be overwritten
+    prog = Program((("mul", 0, 0, 0), ("mul", 0, 0, 0), ("sub", 2, 0, 1)), n_inputs=2, result=2)
+    y, _ = _run_prog(prog, [[3.0], [1.0]])
+    assert y[0] == 80.0  # 3^4 - 1
+
+
+def test_program_output_is_rounded_once_to_the_dtype():
+    # fp16: 1 + 2^-11 is a tie that rounds to 1.0, but the program keeps fp32
+    # registers: (1 + 2^-11) + 2^-11 = 1 + 2^-10 is then stored exactly
+    prog = Program((("add", 3, 0, 1), ("add", 3, 3, 1)), n_inputs=2, result=3)
+    y, _ = _run_prog(prog, [[1.0], [2.0 ** -11]], dt="f16")
+    assert y.dtype == np.float16 and float(y[0]) == 1.0 + 2.0 ** -10
+    prog = Program((("add", 3, 0, 1),), n_inputs=2, result=3)
+    y, _ = _run_prog(prog, [[1.0], [2.0 ** -11]], dt="f16")
+    assert float(y[0]) == 1.0  # a single add: the tie goes to even
+
+
+def test_program_matches_the_builtin_ops():
+    rng = np.random.default_rng(71)
+    n = 777
+    a, x, b = (rng.uniform(-2, 2, n).astype(np.float32) for _ in range(3))
+    # relu(a*x + b) as three built-in ops vs one program
+    bufs = {"a": a, "x": x, "b": b, "t": np.zeros(n, np.float32), "y": np.zeros(n, np.float32)}
+    ops = [Op("mul", Ref("t"), (Ref("a"), Ref("x")), n=n), Op("add", Ref("t"), (Ref("t"), Ref("b")), n=n),
+           Op("relu", Ref("y"), (Ref("t"),), n=n)]
+    want = oracle.run(wl_of(bufs, ops))["y"]
+    prog = Program((("mul", 3, 0, 1), ("add", 3, 3, 2), ("relu", 3, 3)), n_inputs=3, result=3)
+    got, scale = _run_prog(prog, [a, x, b])
+    assert _exact(scale) and np.array_equal(got.view(np.uint32), want.view(np.uint32))
+    # scaling by a constant register is SCALE
+    prog = Program((("mul", 3, 8, 0),), n_inputs=1, result=3, consts=(0.3,))
+    got, _ = _run_prog(prog, [x])
+    bufs = {"x": x, "y": np.zeros(n, np.float32)}
+    want = oracle.run(wl_of(bufs, [Op("scale", Ref("y"), (Ref("x"),), n=n, alpha=0.3)]))["y"]
+    assert np.array_equal(got.view(np.uint32), want.view(np.uint32))
+    # g / (1 + exp(-g)) * u, step by step in fp32, is SILU_MUL within its tolerance
+    prog = Program((("neg", 3, 0), ("exp", 3, 3), ("add", 3, 3, 8), ("div", 3, 0, 3), ("mul", 3, 3, 1)),
+                   n_inputs=2, result=3, consts=(1.0,))
+    got, scale = _run_prog(prog, [a, x])
+    assert not _exact(scale)
+    bufs = {"g": a, "u": x, "y": np.zeros(n, np.float32)}
+    want = oracle.run(wl_of(bufs, [Op("silu_mul", Ref("y"), (Ref("g"), Ref("u")), n=n)]))["y"]
+    assert compare(got, want, "f32", np.abs(want.astype(np.float64))).ok
+
+
+def test_program_ops_write_only_their_output_and_read_every_input():
+    rng = np.random.default_rng(72)
+    n = 50
+    p, q, r = (rng.uniform(-1, 1, n).astype(np.float32) for _ in range(3))
+    prog = Program((("sel", 3, 0, 1, 2),), n_inputs=3, result=3)
+    bufs = {"p": np.where(p > 0, p, 0).astype(np.float32), "q": q, "r": r,
+            "y": np.full(n + 3, 9.0, np.float32)}
+    op = Op("program", Ref("y", 1), (Ref("p"), Ref("q"), Ref("r")), n=n, prog=prog)
+    out = oracle.run(wl_of(bufs, [op]))
+    y = out["y"]
+    assert y[0] == 9.0 and y[-1] == 9.0 and y[-2] == 9.0
+    assert np.array_equal(y[1:n + 1], np.where(bufs["p"] != 0, q, r))
+    assert traffic.op_bytes(op) == 4 * n * 4
