@@ -562,6 +562,55 @@ def torch_frontend_leg(device=0, reps=5, n_ops=1000, sizes=(4096, 1 << 20)):
     return res
 
 
+def program_leg(device=0, steps=200, warmup=100):
+    """The fused chain y = relu(a*x + b) at 16,777,216 fp32 elements computed
+    by one op defined at run time (a 3-instruction register program) instead
+    of the built-in fused descriptor: one resident launch, the same rotating
+    replicas and passes as the headline, 16 algorithmic bytes per element.
+    The built-in fused chain is timed the same way in the same process."""
+    import numpy as np
+    import torch
+
+    from persistent_fusion_amd import gpuos, runner, workloads
+
+    ys = {}
+    out = {"workload": "relu(a*x+b), 16,777,216 fp32 elements, 3-instruction program vs built-in "
+                       "fused chain, 4 rotating replicas"}
+    for label, wl in (("program", workloads.gen_program_chain(seed=0, n=N_ELEMS)),
+                      ("builtin_fused", workloads.gen_fused_chain(seed=0, n=N_ELEMS))):
+        reps = [runner.to_device(wl, device) for _ in range(REPLICAS)]
+        ctx = gpuos.Context(device, trace=1)
+        try:
+            pids = gpuos.define_programs(ctx, wl.ops)
+            arrs = [gpuos.encode_ops(wl.ops, 0, len(wl.ops), runner.addr_fn(t, wl), {}, pids) for t in reps]
+            torch.cuda.synchronize()
+            for k in range(warmup):
+                ctx.submit_noids(arrs[k % REPLICAS], len(wl.ops))
+                ctx.flush()
+            ctx.sync(0, 60.0)
+            t0 = time.perf_counter()
+            for k in range(steps):
+                ctx.submit_noids(arrs[(warmup + k) % REPLICAS], len(wl.ops))
+                ctx.flush()
+            ctx.sync(0, 120.0)
+            wall = time.perf_counter() - t0
+            tr = ctx.trace()
+        finally:
+            ctx.destroy()
+        op_code = gpuos.OPCODES["program"] if label == "program" else 32
+        recs = sorted((r for r in tr if r["opcode"] == op_code), key=lambda r: r["seq"])[-steps:]
+        per_pass = sorted((r["t_done"] - r["t_claim"]) * 1e-8 for r in recs)
+        out[label] = {"gb_per_s": round(steps * 16 * N_ELEMS / wall / 1e9, 1),
+                      "median_pass_device_us": round(per_pass[len(per_pass) // 2] * 1e6, 2) if per_pass else None}
+        log(f"bench: program leg {label}: {out[label]}")
+        ys[label] = reps[(warmup + steps - 1) % REPLICAS]["y"].cpu().numpy()
+        del reps
+    out["program_vs_builtin"] = round(out["program"]["gb_per_s"] / out["builtin_fused"]["gb_per_s"], 3)
+    out["bit_identical"] = bool(np.array_equal(ys["program"].view(np.uint32),
+                                               ys["builtin_fused"].view(np.uint32)))
+    return out
+
+
 def cpu_baseline_leg(budget_s=10.0, gpu_y=None):
     """The oracle, untuned, on a bounded sample of the same workload.
 
@@ -626,7 +675,7 @@ def main():
     ap.add_argument("--cpu-budget", type=float, default=10.0)
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--extra", default="",
-                    help="comma-separated extra legs: decode, dag, priority, torch (or all)")
+                    help="comma-separated extra legs: decode, dag, priority, torch, program (or all)")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
         print("bench.py: this build measures one GPU only (the resident kernel runs on one "
@@ -640,13 +689,13 @@ def main():
     fc = fused_chain_leg(args.steps, args.warmup)
     q = queue_leg(args.queue_reps)
     cp = copy_leg()
-    extra_names = ("decode", "dag", "priority", "torch") if args.extra == "all" else \
+    extra_names = ("decode", "dag", "priority", "torch", "program") if args.extra == "all" else \
         tuple(x for x in args.extra.split(",") if x)
     extra = {}
     for name in extra_names:
         log(f"bench: extra leg {name}")
         extra[name] = {"decode": decode_leg, "dag": dag_leg, "priority": priority_leg,
-                       "torch": torch_frontend_leg}[name]()
+                       "torch": torch_frontend_leg, "program": program_leg}[name]()
     cpu, parity = (None, None) if args.no_cpu else cpu_baseline_leg(args.cpu_budget, fc["y"])
 
     steps = args.steps

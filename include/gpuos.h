@@ -43,7 +43,7 @@
 extern "C" {
 #endif
 
-#define GPUOS_ABI_VERSION 2
+#define GPUOS_ABI_VERSION 3
 
 /* Status codes. */
 typedef enum gpuos_status {
@@ -96,12 +96,18 @@ typedef enum gpuos_status {
  *  SILU_MUL     out[k] = g[k] / (1 + exp(-g[k])) * u[k], g = in0, u = in1.
  *  SPIN         debug op: the claiming wave spins for aux[0] nanoseconds
  *               (bounded to 10 ms) and completes; used to test time-outs.
+ *  PROGRAM      an op defined at run time (gpuos_program_define): out[k] =
+ *               P(in0[k], in1[k], in2[k]) for the register program P whose
+ *               id is aux[0]; in[j] is given for j < P.n_inputs and null
+ *               otherwise (in[2] is a data input here).  dtype F32, BF16 or
+ *               F16 for every operand; src_len must be 0.
  *
  * Ops whose result is rounded once from an exact formula (COPY, GATHER, ADD,
  * MUL, SCALE, RELU, ROPE) give bit-identical results however the queue is
  * scheduled or fused.  Reductions and transcendentals (EXP, ROW_SUM,
  * ROW_SOFTMAX, RMSNORM, GEMV, ATTN_*, SILU_MUL) accumulate in fp32 and match
- * an exact evaluation to within rounding.
+ * an exact evaluation to within rounding.  A PROGRAM op is bit-reproducible
+ * like the first group unless its program uses EXP.
  */
 typedef enum gpuos_opcode {
   GPUOS_OP_NOP = 0,
@@ -121,7 +127,8 @@ typedef enum gpuos_opcode {
   GPUOS_OP_ATTN_AV = 14,
   GPUOS_OP_SILU_MUL = 15,
   GPUOS_OP_SPIN = 16,
-  GPUOS_OP_COUNT = 17
+  GPUOS_OP_PROGRAM = 17,
+  GPUOS_OP_COUNT = 18
 } gpuos_opcode;
 
 /*
@@ -407,10 +414,92 @@ const char* gpuos_last_error(void);
  * ("Under the hood": blocks of different kernels on one stream never
  * overlap).  With fuse = 1 the fusion pass runs first and each fused chain is
  * one launch (a stand-alone fused kernel).  Does not synchronise.
- * deps are ignored.  Errors: EINVAL, EDEVICE.
+ * deps are ignored; PROGRAM ops are refused (their bodies belong to a
+ * context).  Errors: EINVAL, EDEVICE.
  */
 int gpuos_baseline_run(int device, const gpuos_op* ops, uint32_t n, int fuse,
                        void* stream);
+
+/*
+ * Ops defined at run time ("GPUOS: A GPU Operating System Primitive for
+ * Transparent Operation Fusion", section "The Paper": operators injected into
+ * the running persistent kernel and updated safely while it runs).  An op
+ * body is a register program of up to GPUOS_PROG_MAX_INSNS instructions that
+ * the resident kernel interprets per element; defining or updating one needs
+ * no compilation and no relaunch.
+ *
+ * Registers hold fp32 values.  r0..r7 are per element: r0..r(n_inputs-1)
+ * start as the op's inputs in0[k], in1[k], in2[k] (widened exactly from
+ * BF16 / F16), the rest as +0.  r8..r15 are the constants consts[0..7].
+ * Instructions run in order; each writes register dst (0..7) with one fp32
+ * result rounded to nearest even (no fused multiply-add).  The op's output is
+ * register `result` (0..15), rounded once to the op's dtype.  Operand fields
+ * an instruction does not use, and every reserved field, must be 0.
+ *
+ *  MOV  a        EXP  exp(a) (within the EXP op's tolerance)
+ *  ADD  a + b    NEG  -a (sign flip)        LT   a < b ? 1 : 0
+ *  SUB  a - b    ABS  |a| (sign cleared)    SEL  a != 0 ? b : c (NaN != 0)
+ *  MUL  a * b    RELU a > 0 ? a : +0
+ *  DIV  a / b (correctly rounded)
+ *  MIN  the smaller of a, b; MAX the larger: a NaN operand gives NaN, and -0
+ *       counts as smaller than +0 (IEEE 754-2019 minimum / maximum).
+ *
+ * An op's body is fixed when the op is submitted: gpuos_program_update
+ * changes the body of ops submitted after it and never of ops already
+ * submitted, whether or not they have started.
+ */
+#define GPUOS_PROG_MAX_INSNS 16
+#define GPUOS_PROG_MAX_PROGRAMS 4096
+
+typedef enum gpuos_pop {
+  GPUOS_P_MOV = 0,
+  GPUOS_P_ADD = 1,
+  GPUOS_P_SUB = 2,
+  GPUOS_P_MUL = 3,
+  GPUOS_P_DIV = 4,
+  GPUOS_P_MIN = 5,
+  GPUOS_P_MAX = 6,
+  GPUOS_P_NEG = 7,
+  GPUOS_P_ABS = 8,
+  GPUOS_P_RELU = 9,
+  GPUOS_P_EXP = 10,
+  GPUOS_P_LT = 11,
+  GPUOS_P_SEL = 12,
+  GPUOS_P_COUNT = 13
+} gpuos_pop;
+
+typedef struct gpuos_insn {
+  uint8_t op;        /* gpuos_pop */
+  uint8_t dst;       /* 0..7 */
+  uint8_t a, b, c;   /* source registers 0..15 (b for binary ops and LT,
+                        b and c for SEL) */
+  uint8_t _reserved[3];
+} gpuos_insn;        /* 8 bytes */
+
+typedef struct gpuos_program {
+  uint32_t n_insns;   /* 1..GPUOS_PROG_MAX_INSNS */
+  uint32_t n_inputs;  /* 1..3 */
+  uint32_t result;    /* register holding the output, 0..15 */
+  uint32_t _reserved;
+  float consts[8];    /* registers 8..15 */
+  gpuos_insn insns[GPUOS_PROG_MAX_INSNS];
+} gpuos_program;      /* 176 bytes */
+
+/*
+ * Defines a program on the context and returns its id (0, 1, 2, ... in
+ * definition order) in *id_out; PROGRAM ops name it in aux[0].  The program
+ * is copied.  Errors: EINVAL for a null argument, an instruction or register
+ * out of range, a nonzero reserved field, or more than
+ * GPUOS_PROG_MAX_PROGRAMS programs; ESTATE on a stopped context.
+ */
+int gpuos_program_define(gpuos_ctx* ctx, const gpuos_program* prog, uint32_t* id_out);
+
+/*
+ * Replaces the body of program `id` for ops submitted from now on (see
+ * above).  Errors: EINVAL for an unknown id or a malformed program (as
+ * gpuos_program_define); ESTATE on a stopped context.
+ */
+int gpuos_program_update(gpuos_ctx* ctx, uint32_t id, const gpuos_program* prog);
 
 /*
  * Graph-replay comparator ("Launch Overhead and Fusion", section "Graph

@@ -157,6 +157,13 @@ struct alignas(16) DevDesc {
       uint8_t _pad[80];
     } ga;
     struct {
+      uint64_t ptr[4];      // 18-25: out, in0, in1, in2
+      uint32_t meta;        // 26: n_insns | result << 8 | n_inputs << 16
+      uint32_t ins[16];     // 27-42: op | dst << 5 | a << 8 | b << 12 | c << 16
+      float k[8];           // 43-50: registers 8..15
+      uint8_t _pad[12];
+    } pg;                   // GPUOS_OP_PROGRAM: the op's body, by value
+    struct {
       uint64_t in[4];       // 18-25: in[0] = chain input, in[1..3] operands
       uint64_t out[8];      // 26-41: output pointer of step s (FSF_STORE)
       uint8_t step_op[8];   // 42-43
@@ -186,6 +193,9 @@ static_assert(offsetof(DevDesc, ng.q) == 34 * 4 && offsetof(DevDesc, ng.hd) == 4
 static_assert(offsetof(DevDesc, ga.W) == 24 * 4 && offsetof(DevDesc, ga.M) == 30 * 4 &&
                   offsetof(DevDesc, ga.sum) == 32 * 4,
               "GEMV-ADD keeps the GEMV fields where a GEMV descriptor has them");
+static_assert(offsetof(DevDesc, pg.meta) == 26 * 4 && offsetof(DevDesc, pg.ins) == 27 * 4 &&
+                  offsetof(DevDesc, pg.k) == 43 * 4,
+              "program fields at dwords 26-50");
 static_assert(offsetof(DevDesc, f.step_op) == 42 * 4, "step_op at dword 42");
 static_assert(offsetof(DevDesc, f.step_fl) == 44 * 4, "step_fl at dword 44");
 static_assert(offsetof(DevDesc, f.fscal) == 46 * 4, "fscal at dword 46");

@@ -179,6 +179,72 @@ struct ViewDesc {
   }
 };
 
+// A PROGRAM op's body as its descriptor carries it (dwords 26-50; see the
+// pg layout): meta = n_insns | result << 8 | n_inputs << 16 | zero mask << 24,
+// where the zero mask lists the per-element registers r0..r7 the program
+// reads before writing (they start at +0).
+struct ProgCode {
+  uint32_t meta = 0;
+  uint32_t ins[GPUOS_PROG_MAX_INSNS] = {};
+  float k[8] = {};
+  uint32_t n_inputs() const { return (meta >> 16) & 3u; }
+};
+
+// Arity of a program instruction: registers it reads.
+int pop_arity(uint32_t op) {
+  switch (op) {
+    case GPUOS_P_ADD: case GPUOS_P_SUB: case GPUOS_P_MUL: case GPUOS_P_DIV:
+    case GPUOS_P_MIN: case GPUOS_P_MAX: case GPUOS_P_LT:
+      return 2;
+    case GPUOS_P_SEL:
+      return 3;
+    default:
+      return 1;
+  }
+}
+
+int check_program(const gpuos_program* p, ProgCode& out) {
+  if (!p) return fail(GPUOS_EINVAL, "program is null");
+  if (p->n_insns < 1 || p->n_insns > GPUOS_PROG_MAX_INSNS)
+    return fail(GPUOS_EINVAL, "program: n_insns %u outside 1..%d", p->n_insns, GPUOS_PROG_MAX_INSNS);
+  if (p->n_inputs < 1 || p->n_inputs > 3) return fail(GPUOS_EINVAL, "program: n_inputs %u outside 1..3", p->n_inputs);
+  if (p->result > 15) return fail(GPUOS_EINVAL, "program: result register %u > 15", p->result);
+  if (p->_reserved) return fail(GPUOS_EINVAL, "program: reserved field is not 0");
+  out = ProgCode{};
+  uint32_t written = (1u << p->n_inputs) - 1, zmask = 0;
+  auto reads = [&](uint32_t r) {
+    if (r < 8 && !(written & (1u << r))) zmask |= 1u << r;
+  };
+  for (uint32_t s = 0; s < p->n_insns; ++s) {
+    const gpuos_insn& in = p->insns[s];
+    if (in.op >= GPUOS_P_COUNT) return fail(GPUOS_EINVAL, "program: instruction %u: unknown op %u", s, in.op);
+    if (in.dst > 7) return fail(GPUOS_EINVAL, "program: instruction %u: destination r%u is not 0..7", s, in.dst);
+    const int ar = pop_arity(in.op);
+    const uint8_t src[3] = {in.a, in.b, in.c};
+    for (int j = 0; j < 3; ++j) {
+      if (j < ar && src[j] > 15)
+        return fail(GPUOS_EINVAL, "program: instruction %u: source register %u > 15", s, src[j]);
+      if (j >= ar && src[j])
+        return fail(GPUOS_EINVAL, "program: instruction %u: unused operand field is not 0", s);
+    }
+    if (in._reserved[0] || in._reserved[1] || in._reserved[2])
+      return fail(GPUOS_EINVAL, "program: instruction %u: reserved field is not 0", s);
+    for (int j = 0; j < ar; ++j) reads(src[j]);
+    written |= 1u << in.dst;
+    out.ins[s] = in.op | (uint32_t)in.dst << 5 | (uint32_t)in.a << 8 | (uint32_t)in.b << 12 |
+                 (uint32_t)in.c << 16;
+  }
+  for (uint32_t s = p->n_insns; s < GPUOS_PROG_MAX_INSNS; ++s) {
+    const gpuos_insn& in = p->insns[s];
+    if (in.op || in.dst || in.a || in.b || in.c || in._reserved[0] || in._reserved[1] || in._reserved[2])
+      return fail(GPUOS_EINVAL, "program: instruction slot %u past n_insns is not 0", s);
+  }
+  reads(p->result);
+  for (int j = 0; j < 8; ++j) out.k[j] = p->consts[j];
+  out.meta = p->n_insns | p->result << 8 | p->n_inputs << 16 | zmask << 24;
+  return 0;
+}
+
 uint64_t src_extent(uint64_t src_len, uint64_t extent) {
   if (src_len == 0 || src_len >= extent) return extent;
   return src_len;
@@ -211,6 +277,10 @@ OpRanges op_ranges(const gpuos_op& o, const ViewDesc* v = nullptr) {
       wr(o.out, n * es);
       rd(o.in[0], o.src_len[0] * es);
       rd(o.in[2], n * 4);
+      break;
+    case GPUOS_OP_PROGRAM:  // data inputs in[0..n_inputs)
+      wr(o.out, n * es);
+      for (int j = 0; j < 3; ++j) rd(o.in[j], n * es);
       break;
     case GPUOS_OP_ROW_SUM:
       wr(o.out, (uint64_t)o.rows * es);
@@ -316,6 +386,11 @@ int validate(const gpuos_op& o, uint32_t index, bool has_view = false) {
         if (!(o.eps >= 0.0f)) return fail(GPUOS_EINVAL, "op %u: eps must be >= 0", index);
       }
       break;
+    case GPUOS_OP_PROGRAM:
+      if (o.src_len[0] || o.src_len[1]) return fail(GPUOS_EINVAL, "op %u: a PROGRAM op takes no src_len", index);
+      if (o.aux[0] < 0) return fail(GPUOS_EINVAL, "op %u: negative program id", index);
+      if ((rc = align(o.in[1], es, "in[1]")) || (rc = align(o.in[2], es, "in[2]"))) return rc;
+      break;
     case GPUOS_OP_ROPE:
       if (o.rows == 0 || o.row_len == 0 || (o.row_len & 1) ||
           (uint64_t)o.rows * o.row_len != o.n)
@@ -359,9 +434,10 @@ int validate(const gpuos_op& o, uint32_t index, bool has_view = false) {
   // (A view's overlap rule is checked with the view.)
   if (!has_view) {
     const bool same_index = (is_elementwise(op) && op != GPUOS_OP_GATHER) || op == GPUOS_OP_ROW_SOFTMAX ||
-                            op == GPUOS_OP_RMSNORM || op == GPUOS_OP_ROPE;
+                            op == GPUOS_OP_RMSNORM || op == GPUOS_OP_ROPE || op == GPUOS_OP_PROGRAM;
     // data inputs come first in op_ranges: in[0], then in[1] for binary ops
-    const int n_data = is_elementwise(op) && is_binary(op) ? 2 : 1;
+    // (every read of a PROGRAM op is a data input)
+    const int n_data = op == GPUOS_OP_PROGRAM ? R.nr : is_elementwise(op) && is_binary(op) ? 2 : 1;
     for (int q = 0; q < R.nr; ++q) {
       if (!overlaps(R.w, R.r[q])) continue;
       const bool exact = R.r[q].lo == R.w.lo && R.r[q].hi == R.w.hi;
@@ -641,6 +717,7 @@ struct Staged {
   uint32_t ring;
   DepVec deps;  // user ids
   ViewDesc view;
+  ProgCode prog;  // PROGRAM ops: the body as of submission
 };
 
 // A device op after the fusion pass: one descriptor built from user ops
@@ -683,6 +760,7 @@ struct gpuos_ctx {
   uint64_t pub_tiles[kRings] = {0, 0};
   uint64_t tail_written[kRings] = {0, 0};
   HazardMap hazards;
+  std::vector<ProgCode> programs;  // gpuos_program_define / _update
   uint64_t since_prune = 0;
   bool poisoned = false;
   bool stopped = false;     // STOP published; no more submissions
@@ -975,8 +1053,16 @@ bool try_extend(const gpuos_op& o, ChainState& st, uint8_t& code, uint8_t& fl) {
   return true;
 }
 
-// Streams (non-temporal) elementwise, COPY and fused descriptors whose
-// operands total at least stream_min_kib.
+// Puts a PROGRAM op's body into its descriptor (over the plain op's
+// src_len, scalar and aux fields, which such an op does not use).
+void encode_program(const ProgCode& pc, DevDesc& d) {
+  d.pg.meta = pc.meta;
+  for (int s = 0; s < GPUOS_PROG_MAX_INSNS; ++s) d.pg.ins[s] = pc.ins[s];
+  for (int j = 0; j < 8; ++j) d.pg.k[j] = pc.k[j];
+}
+
+// Streams (non-temporal) elementwise, COPY, fused and PROGRAM descriptors
+// whose operands total at least stream_min_kib.
 void mark_streaming(const gpuos_config& cfg, DevDesc& d) {
   if (cfg.stream_min_kib == 0xFFFFFFFFu || (d.flags & DF_VIEW)) return;
   const uint64_t es = elem_size(d.dtype);
@@ -986,6 +1072,8 @@ void mark_streaming(const gpuos_config& cfg, DevDesc& d) {
     for (int i = 0; i < 4; ++i) k += d.f.in[i] != 0;
     for (int i = 0; i < kMaxSteps; ++i) k += d.f.out[i] != 0;
     bytes = (uint64_t)k * d.n * es;
+  } else if (d.opcode == GPUOS_OP_PROGRAM) {
+    bytes = (uint64_t)(1 + ((d.pg.meta >> 16) & 3u)) * d.n * es;
   } else if (is_elementwise(d.opcode) && d.opcode != GPUOS_OP_GATHER) {
     const uint64_t ext = (uint64_t)d.n * es;
     const uint64_t l0 = d.p.src_len[0] ? std::min<uint64_t>(d.p.src_len[0], d.n) * es : ext;
@@ -1349,6 +1437,7 @@ void plan_ops(gpuos_ctx* c, size_t begin, size_t end, std::vector<Planned>& plan
     if (pl.count == 1) {
       encode_plain(s0.op, cfg, c->workers, pl.desc);
       if (s0.view.on) encode_view(s0.view, c->workers, pl.desc);
+      if (s0.op.opcode == GPUOS_OP_PROGRAM) encode_program(s0.prog, pl.desc);
       j = i + 1;
     }
     mark_streaming(cfg, pl.desc);
@@ -1889,6 +1978,15 @@ int submit_impl(gpuos_ctx* c, const gpuos_op* ops, const gpuos_view* views, uint
   for (uint32_t i = 0; i < n; ++i) {
     int rc = validate(ops[i], i, views && views[i].ndim);
     if (rc) return rc;
+    if (ops[i].opcode == GPUOS_OP_PROGRAM) {
+      const uint32_t pid = (uint32_t)ops[i].aux[0];
+      if (pid >= c->programs.size()) return fail(GPUOS_EINVAL, "op %u: unknown program %u", i, pid);
+      const uint32_t nin = c->programs[pid].n_inputs();
+      for (uint32_t j = 0; j < 3; ++j)
+        if ((j < nin) != (ops[i].in[j] != nullptr))
+          return fail(GPUOS_EINVAL, "op %u: program %u reads %u inputs: in[%u] must be %s", i, pid, nin, j,
+                      j < nin ? "given" : "null");
+    }
     if (views && (rc = normalize_view(ops[i], views[i], i, vd[i]))) return rc;
     for (int k = 0; k < 4; ++k) {
       const int64_t dv = ops[i].deps[k];
@@ -1926,6 +2024,7 @@ int submit_impl(gpuos_ctx* c, const gpuos_op* ops, const gpuos_view* views, uint
     if (views) s.view = vd[i];
     s.id = c->next_id++;
     s.ring = (ops[i].flags & GPUOS_FLAG_LC) ? 1 : 0;
+    if (ops[i].opcode == GPUOS_OP_PROGRAM) s.prog = c->programs[(uint32_t)ops[i].aux[0]];
     for (int k = 0; k < 4; ++k) {
       const int64_t dv = ops[i].deps[k];
       if (dv > 0) {
@@ -2083,6 +2182,31 @@ int gpuos_stop(gpuos_ctx* c, int64_t timeout_ns) {
   return rc;
 }
 
+int gpuos_program_define(gpuos_ctx* c, const gpuos_program* prog, uint32_t* id_out) {
+  if (!c || !id_out) return fail(GPUOS_EINVAL, "null argument");
+  if (c->stopped) return fail(GPUOS_ESTATE, "context is stopped");
+  if (c->programs.size() >= GPUOS_PROG_MAX_PROGRAMS)
+    return fail(GPUOS_EINVAL, "more than %d programs", GPUOS_PROG_MAX_PROGRAMS);
+  ProgCode pc;
+  const int rc = check_program(prog, pc);
+  if (rc) return rc;
+  *id_out = (uint32_t)c->programs.size();
+  c->programs.push_back(pc);
+  return 0;
+}
+
+int gpuos_program_update(gpuos_ctx* c, uint32_t id, const gpuos_program* prog) {
+  if (!c) return fail(GPUOS_EINVAL, "null context");
+  if (c->stopped) return fail(GPUOS_ESTATE, "context is stopped");
+  if (id >= c->programs.size()) return fail(GPUOS_EINVAL, "unknown program %u", id);
+  ProgCode pc;
+  const int rc = check_program(prog, pc);
+  if (rc) return rc;
+  // staged and published ops keep the body they were submitted with
+  c->programs[id] = pc;
+  return 0;
+}
+
 int gpuos_yield(gpuos_ctx* c, int64_t timeout_ns) {
   if (!c) return fail(GPUOS_EINVAL, "null context");
   if (c->stopped) return fail(GPUOS_ESTATE, "context is stopped");
@@ -2147,6 +2271,8 @@ int per_op_prepare(int device, const gpuos_op* ops, uint32_t n, uint32_t* cus) {
   for (uint32_t i = 0; i < n; ++i) {
     int rc = validate(ops[i], i);
     if (rc) return rc;
+    if (ops[i].opcode == GPUOS_OP_PROGRAM)
+      return fail(GPUOS_EINVAL, "op %u: PROGRAM ops run only in a context (their bodies belong to it)", i);
   }
   static thread_local int cached_dev = -2;
   static thread_local uint32_t cached_cus = 0;

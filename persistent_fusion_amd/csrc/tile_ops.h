@@ -288,6 +288,207 @@ __device__ __forceinline__ void ew_tile(D d, uint32_t t) {
   }
 }
 
+// ---------------------------------------------------------------------------
+// PROGRAM ops: a register program defined at run time (gpuos_program in
+// gpuos.h), carried by value in the descriptor (dword 26: n_insns | result
+// << 8 | n_inputs << 16 | zero-init mask << 24; dwords 27-42: instructions
+// op | dst << 5 | a << 8 | b << 12 | c << 16; dwords 43-50: constants).  The
+// program is uniform across the wave, so each instruction is a few scalar
+// branches and one 4-wide vector operation per lane.  Registers r0..r7 are
+// eight separate vector values (never an indexed array, which the compiler
+// would have to place in scratch memory); r8..r15 are uniform constants.
+
+typedef float pvec __attribute__((ext_vector_type(4)));
+
+struct PRegs {
+  pvec r0, r1, r2, r3, r4, r5, r6, r7;
+};
+
+// IEEE 754-2019 minimum / maximum: NaN if either operand is NaN, -0 < +0.
+__device__ __forceinline__ float prog_min(float a, float b) {
+  if (a != a || b != b) return a + b;
+  if (a < b) return a;
+  if (b < a) return b;
+  return __uint_as_float(__float_as_uint(a) | __float_as_uint(b));  // equal: -0 wins
+}
+__device__ __forceinline__ float prog_max(float a, float b) {
+  if (a != a || b != b) return a + b;
+  if (a > b) return a;
+  if (b > a) return b;
+  return __uint_as_float(__float_as_uint(a) & __float_as_uint(b));  // equal: +0 wins
+}
+
+template <class D>
+__device__ __forceinline__ pvec prog_src(D d, const PRegs& R, uint32_t i) {
+  switch (i) {
+    case 0: return R.r0;
+    case 1: return R.r1;
+    case 2: return R.r2;
+    case 3: return R.r3;
+    case 4: return R.r4;
+    case 5: return R.r5;
+    case 6: return R.r6;
+    case 7: return R.r7;
+    default: return pvec(__uint_as_float(d(43 + (int)(i & 7u))));
+  }
+}
+
+__device__ __forceinline__ void prog_dst(PRegs& R, uint32_t i, pvec y) {
+  switch (i) {
+    case 0: R.r0 = y; break;
+    case 1: R.r1 = y; break;
+    case 2: R.r2 = y; break;
+    case 3: R.r3 = y; break;
+    case 4: R.r4 = y; break;
+    case 5: R.r5 = y; break;
+    case 6: R.r6 = y; break;
+    default: R.r7 = y; break;
+  }
+}
+
+// Runs the descriptor's program on R; returns the result register.
+template <class D>
+__device__ __forceinline__ pvec prog_run(D d, PRegs& R) {
+  const uint32_t meta = d(26), ni = meta & 31u;
+  for (uint32_t s = 0; s < ni; ++s) {
+    const uint32_t w = d(27 + (int)s);
+    const uint32_t op = w & 31u;
+    const pvec a = prog_src(d, R, (w >> 8) & 15u);
+    pvec b = a, c = a, y;
+    if (op == GPUOS_P_ADD || op == GPUOS_P_SUB || op == GPUOS_P_MUL || op == GPUOS_P_DIV ||
+        op == GPUOS_P_MIN || op == GPUOS_P_MAX || op == GPUOS_P_LT || op == GPUOS_P_SEL)
+      b = prog_src(d, R, (w >> 12) & 15u);
+    if (op == GPUOS_P_SEL) c = prog_src(d, R, (w >> 16) & 15u);
+    switch (op) {
+      case GPUOS_P_ADD: y = a + b; break;
+      case GPUOS_P_SUB: y = a - b; break;
+      case GPUOS_P_MUL: y = a * b; break;
+      case GPUOS_P_DIV: y = a / b; break;
+#define GPUOS_PEW(code, expr) \
+      case code: _Pragma("unroll") for (int e = 0; e < 4; ++e) y[e] = (expr); break;
+      GPUOS_PEW(GPUOS_P_MIN, prog_min(a[e], b[e]))
+      GPUOS_PEW(GPUOS_P_MAX, prog_max(a[e], b[e]))
+      GPUOS_PEW(GPUOS_P_NEG, __uint_as_float(__float_as_uint(a[e]) ^ 0x80000000u))
+      GPUOS_PEW(GPUOS_P_ABS, __uint_as_float(__float_as_uint(a[e]) & 0x7fffffffu))
+      GPUOS_PEW(GPUOS_P_RELU, a[e] > 0.0f ? a[e] : 0.0f)
+      GPUOS_PEW(GPUOS_P_EXP, expf(a[e]))
+      GPUOS_PEW(GPUOS_P_LT, a[e] < b[e] ? 1.0f : 0.0f)
+      GPUOS_PEW(GPUOS_P_SEL, a[e] != 0.0f ? b[e] : c[e])
+#undef GPUOS_PEW
+      default: y = a; break;  // MOV
+    }
+    prog_dst(R, (w >> 5) & 7u, y);
+  }
+  return prog_src(d, R, (meta >> 8) & 15u);
+}
+
+// A group's registers: the inputs in r0..r(nin-1), then +0 in every register
+// the program reads before writing (mask in meta bits 24-31; never an input
+// register).  The others keep the previous group's values, which the program
+// overwrites before reading.
+__device__ __forceinline__ void prog_init(PRegs& R, uint32_t nin, uint32_t zmask, pvec x0, pvec x1,
+                                          pvec x2) {
+  const pvec z = pvec(0.0f);
+  R.r0 = x0;
+  if (nin >= 2) R.r1 = x1; else if (zmask & 2u) R.r1 = z;
+  if (nin >= 3) R.r2 = x2; else if (zmask & 4u) R.r2 = z;
+  if (zmask & 8u) R.r3 = z;
+  if (zmask & 16u) R.r4 = z;
+  if (zmask & 32u) R.r5 = z;
+  if (zmask & 64u) R.r6 = z;
+  if (zmask & 128u) R.r7 = z;
+}
+
+// Tiles as ew_tile with one row per group: whole 16-byte vectors form rows of
+// 64 (one per lane), tile t takes rows t, t + T, ...; the next row's inputs
+// are requested before the current one is computed.  A 16-byte vector holds
+// 4 fp32 or 8 16-bit elements: the program runs once or twice per vector, on
+// 4 elements at a time.  The n % V leftover elements belong to the last
+// tile; misaligned operands use per-element accesses.
+template <int DT, int CPL, int CPS, class D>
+__device__ __forceinline__ void prog_tile(D d, uint32_t t) {
+  using T = DTr<DT, CPL, CPS>;
+  constexpr int V = T::V;
+  constexpr int H = V / 4;  // program passes per vector
+  const uint32_t n = d(1), ntiles = d(6), meta = d(26);
+  const uint32_t nin = (meta >> 16) & 3u, zmask = meta >> 24;
+  const uint64_t po = d.q(18), p0 = d.q(20), p1 = nin >= 2 ? d.q(22) : 0, p2 = nin >= 3 ? d.q(24) : 0;
+  const uint32_t lane = lane_id();
+  PRegs R;
+  R.r0 = R.r1 = R.r2 = R.r3 = R.r4 = R.r5 = R.r6 = R.r7 = pvec(0.0f);
+  const bool fast = aligned16(po) && aligned16(p0) && aligned16(p1) && aligned16(p2);
+  if (fast) {
+    const uint32_t nv = n / V, nrows = (nv + 63) / 64;
+    const rsrc_t vo = make_rsrc_n(po, nv * 16u), v0 = make_rsrc_n(p0, nv * 16u),
+                 v1 = make_rsrc_n(p1, nv * 16u), v2 = make_rsrc_n(p2, nv * 16u);
+    float x0[V], x1[V], x2[V];
+#pragma unroll
+    for (int e = 0; e < V; ++e) x1[e] = x2[e] = 0.0f;
+    auto load = [&](uint32_t g) {
+      const uint32_t q = g * 64 + lane;
+      T::ldq(v0, q, x0);
+      if (nin >= 2) T::ldq(v1, q, x1);
+      if (nin >= 3) T::ldq(v2, q, x2);
+    };
+    if (t < nrows) load(t);
+    for (uint32_t g = t; g < nrows; g += ntiles) {
+      pvec c0[H], c1[H], c2[H];
+#pragma unroll
+      for (int h = 0; h < H; ++h)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          c0[h][e] = x0[4 * h + e];
+          c1[h][e] = x1[4 * h + e];
+          c2[h][e] = x2[4 * h + e];
+        }
+      if (g + ntiles < nrows) load(g + ntiles);
+      float w[V];
+#pragma unroll
+      for (int h = 0; h < H; ++h) {
+        prog_init(R, nin, zmask, c0[h], c1[h], c2[h]);
+        const pvec o = prog_run(d, R);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) w[4 * h + e] = o[e];
+      }
+      T::stq(vo, g * 64 + lane, w);
+    }
+    if (t + 1 == ntiles && nv * V < n) {  // fewer than V leftover elements
+      const uint32_t nb = n * (uint32_t)T::ES;  // bounded: lanes past n read 0
+      const rsrc_t so = make_rsrc_n(po, nb), s0 = make_rsrc_n(p0, nb), s1 = make_rsrc_n(p1, nb),
+                   s2 = make_rsrc_n(p2, nb);
+      const uint32_t i = nv * V + lane;
+      pvec y0 = pvec(0.0f), y1 = pvec(0.0f), y2 = pvec(0.0f);
+      y0[0] = T::ld(s0, i);
+      if (nin >= 2) y1[0] = T::ld(s1, i);
+      if (nin >= 3) y2[0] = T::ld(s2, i);
+      prog_init(R, nin, zmask, y0, y1, y2);
+      const pvec o = prog_run(d, R);
+      if (i < n) T::st(so, i, o[0]);
+    }
+    return;
+  }
+  const uint32_t nb = n * (uint32_t)T::ES;  // bounded: lanes past n read 0
+  const rsrc_t so = make_rsrc_n(po, nb), s0 = make_rsrc_n(p0, nb), s1 = make_rsrc_n(p1, nb),
+               s2 = make_rsrc_n(p2, nb);
+  for (uint64_t base = (uint64_t)t * 256u; base < n; base += (uint64_t)256u * ntiles) {
+    pvec y0, y1 = pvec(0.0f), y2 = pvec(0.0f);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const uint32_t i = (uint32_t)base + (uint32_t)e * 64 + lane;
+      y0[e] = T::ld(s0, i);
+      if (nin >= 2) y1[e] = T::ld(s1, i);
+      if (nin >= 3) y2[e] = T::ld(s2, i);
+    }
+    prog_init(R, nin, zmask, y0, y1, y2);
+    const pvec o = prog_run(d, R);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const uint32_t i = (uint32_t)base + (uint32_t)e * 64 + lane;
+      if (i < n) T::st(so, i, o[e]);
+    }
+  }
+}
+
 // Elementwise op over a strided or broadcast view (DF_VIEW).  The index space
 // is `rows` = shape[0] x shape[1] x shape[2] rows of shape[3] elements; tile t
 // takes `tile` rows from row t * tile, and the lanes split each row, four
@@ -1527,6 +1728,11 @@ __device__ __forceinline__ bool exec_stream(uint32_t op, uint32_t dt, D d, uint3
     case GPUOS_OP_SCALE: ew_any<GPUOS_OP_SCALE, false, CPL, CPS>(dt, d, t); return true;
     case GPUOS_OP_EXP: ew_any<GPUOS_OP_EXP, false, CPL, CPS>(dt, d, t); return true;
     case GPUOS_OP_SILU_MUL: ew_any<GPUOS_OP_SILU_MUL, false, CPL, CPS>(dt, d, t); return true;
+    case GPUOS_OP_PROGRAM:
+      if (dt == GPUOS_BF16) prog_tile<GPUOS_BF16, CPL, CPS>(d, t);
+      else if (dt == GPUOS_F16) prog_tile<GPUOS_F16, CPL, CPS>(d, t);
+      else prog_tile<GPUOS_F32, CPL, CPS>(d, t);
+      return true;
     case OP_FUSED_EW:  // fp32 chains only (the fusion pass leaves other dtypes unfused)
       if (dt != GPUOS_F32) err = (uint32_t)DERR_BAD_OPCODE;
       else fused_tile<GPUOS_F32, CPL, CPS>(d, t);

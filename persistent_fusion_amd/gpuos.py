@@ -14,7 +14,7 @@ from typing import Callable, Dict, Iterable, List, Optional, Sequence
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libgpuos.so")
-ABI_VERSION = 2  # GPUOS_ABI_VERSION of the header this binding follows
+ABI_VERSION = 3  # GPUOS_ABI_VERSION of the header this binding follows
 
 # status codes
 OK, EINVAL, ENOMEM, EAGAIN, ETIMEDOUT, EDEVICE, ESTATE = 0, -1, -2, -3, -4, -5, -6
@@ -24,8 +24,14 @@ STATUS_NAMES = {0: "OK", -1: "EINVAL", -2: "ENOMEM", -3: "EAGAIN", -4: "ETIMEDOU
 OPCODES = {
     "nop": 0, "copy": 1, "gather": 2, "add": 3, "mul": 4, "scale": 5, "relu": 6, "exp": 7,
     "row_sum": 8, "row_softmax": 9, "rmsnorm": 10, "rope": 11, "gemv": 12,
-    "attn_score": 13, "attn_av": 14, "silu_mul": 15, "spin": 16,
+    "attn_score": 13, "attn_av": 14, "silu_mul": 15, "spin": 16, "program": 17,
 }
+# instructions of a gpuos_program
+POPS = {"mov": 0, "add": 1, "sub": 2, "mul": 3, "div": 4, "min": 5, "max": 6, "neg": 7,
+        "abs": 8, "relu": 9, "exp": 10, "lt": 11, "sel": 12}
+POP_ARITY = {k: (3 if k == "sel" else 2 if k in ("add", "sub", "mul", "div", "min", "max", "lt") else 1)
+             for k in POPS}
+PROG_MAX_INSNS = 16
 DTYPES = {"f32": 0, "bf16": 1, "i32": 2, "f16": 3}
 ELEM_BYTES = {"f32": 4, "bf16": 2, "i32": 4}
 FLAG_TRANSIENT, FLAG_LC, FLAG_NONTEMPORAL = 0x1, 0x2, 0x4
@@ -68,6 +74,19 @@ class GpuosView(C.Structure):
                 ("stride", (C.c_int64 * 4) * 3)]
 
 
+class GpuosInsn(C.Structure):
+    _fields_ = [("op", C.c_uint8), ("dst", C.c_uint8), ("a", C.c_uint8), ("b", C.c_uint8),
+                ("c", C.c_uint8), ("_reserved", C.c_uint8 * 3)]
+
+
+class GpuosProgram(C.Structure):
+    _fields_ = [("n_insns", C.c_uint32), ("n_inputs", C.c_uint32), ("result", C.c_uint32),
+                ("_reserved", C.c_uint32), ("consts", C.c_float * 8),
+                ("insns", GpuosInsn * 16)]
+
+
+assert C.sizeof(GpuosInsn) == 8
+assert C.sizeof(GpuosProgram) == 176
 assert C.sizeof(GpuosView) == 136
 assert C.sizeof(GpuosOp) == 128
 assert C.sizeof(GpuosConfig) == 64
@@ -80,6 +99,7 @@ EXPORTS = (
     "gpuos_submit", "gpuos_flush", "gpuos_sync", "gpuos_query", "gpuos_get_stats",
     "gpuos_trace_read", "gpuos_stop", "gpuos_destroy", "gpuos_baseline_run", "gpuos_submit_views",
     "gpuos_graph_create", "gpuos_graph_launch", "gpuos_graph_destroy", "gpuos_yield",
+    "gpuos_program_define", "gpuos_program_update",
     "gpuos_debug_read_desc", "gpuos_debug_published", "gpuos_debug_seq_of", "gpuos_debug_retire",
 )
 
@@ -110,6 +130,8 @@ def lib() -> C.CDLL:
         "gpuos_trace_read": (C.c_int, [P, C.POINTER(GpuosTraceRec), C.c_uint32, C.POINTER(C.c_uint32)]),
         "gpuos_stop": (C.c_int, [P, C.c_int64]),
         "gpuos_yield": (C.c_int, [P, C.c_int64]),
+        "gpuos_program_define": (C.c_int, [P, C.POINTER(GpuosProgram), C.POINTER(C.c_uint32)]),
+        "gpuos_program_update": (C.c_int, [P, C.c_uint32, C.POINTER(GpuosProgram)]),
         "gpuos_destroy": (C.c_int, [P, C.c_int64]),
         "gpuos_baseline_run": (C.c_int, [C.c_int, C.POINTER(GpuosOp), C.c_uint32, C.c_int, P]),
         "gpuos_graph_create": (C.c_int, [C.c_int, C.POINTER(GpuosOp), C.c_uint32, C.c_int, C.POINTER(P)]),
@@ -174,13 +196,15 @@ def make_op(kind: str, out: int, ins: Sequence[int] = (), aux: int = 0, n: int =
     return o
 
 
-def encode_ops(ops, start: int, end: int, addr: Callable, id_of: Dict[int, int]):
+def encode_ops(ops, start: int, end: int, addr: Callable, id_of: Dict[int, int],
+               prog_ids: Optional[Dict] = None):
     """Encodes workload ops [start, end) as a gpuos_op array.
 
     ``addr(ref, dtype)`` returns the device address of a workload ``Ref``;
     ``id_of`` maps earlier op indices to the ids gpuos_submit returned.  A
     dependency inside [start, end) becomes a relative one (negative), an
-    earlier one an absolute id.
+    earlier one an absolute id.  ``prog_ids`` maps the ``Program`` of each
+    program op to its id in the context (``define_programs``).
     """
     arr = (GpuosOp * (end - start))()
     for k, i in enumerate(range(start, end)):
@@ -194,11 +218,48 @@ def encode_ops(ops, start: int, end: int, addr: Callable, id_of: Dict[int, int])
         aux_dt = {"rmsnorm": op.dtype, "rope": "f32", "gather": "i32"}.get(op.kind, "bf16")
         out_dt = "f32" if op.kind == "attn_score" else op.dtype
         flags = (FLAG_TRANSIENT if op.transient else 0) | (FLAG_LC if op.lc else 0)
+        if op.kind == "program":  # up to three data inputs; in[2] is one of them
+            ins = [addr(r, op.dtype) for r in op.ins]
+            arr[k] = make_op("program", addr(op.out, op.dtype), ins[:2], ins[2] if len(ins) > 2 else 0,
+                             n=op.n, dtype=op.dtype, dims=(prog_ids[op.prog],), deps=deps,
+                             flags=flags)
+            continue
         arr[k] = make_op(op.kind, addr(op.out, out_dt), [addr(r, in_dt) for r in op.ins],
                          addr(op.aux, aux_dt) if op.aux is not None else 0, n=op.n,
                          dtype=op.dtype, rows=op.rows, row_len=op.row_len, src_len=op.src_len,
                          alpha=op.alpha, eps=op.eps, dims=op.dims, deps=deps, flags=flags)
     return arr
+
+
+def make_program(insns: Sequence[Sequence], n_inputs: int, result: int,
+                 consts: Sequence[float] = ()) -> GpuosProgram:
+    """A gpuos_program from (op name, dst, *sources) tuples, e.g.
+    ``[("mul", 3, 0, 1), ("add", 3, 3, 2), ("relu", 3, 3)]``."""
+    p = GpuosProgram()
+    p.n_insns, p.n_inputs, p.result = len(insns), n_inputs, result
+    for j, v in enumerate(consts):
+        p.consts[j] = float(v)
+    for s, ins in enumerate(insns):
+        op, dst, *src = ins
+        p.insns[s].op, p.insns[s].dst = POPS[op], dst
+        for j, r in enumerate(src):
+            setattr(p.insns[s], "abc"[j], r)
+    return p
+
+
+def program_of(prog) -> GpuosProgram:
+    """The gpuos_program of a workload ``Program``."""
+    return make_program(prog.insns, prog.n_inputs, prog.result, prog.consts)
+
+
+def define_programs(ctx: "Context", ops) -> Dict:
+    """Defines every distinct ``Program`` of the program ops in ``ops`` on
+    the context, in order of first use; returns Program -> id."""
+    ids: Dict = {}
+    for op in ops:
+        if op.kind == "program" and op.prog not in ids:
+            ids[op.prog] = ctx.program_define(program_of(op.prog))
+    return ids
 
 
 def make_view(shape: Sequence[int], strides: Sequence[Sequence[int]]) -> GpuosView:
@@ -290,6 +351,17 @@ class Context:
     def retire(self, ring: int, upto: int) -> None:
         _check(self._lib.gpuos_debug_retire(self.handle, ring, upto), "gpuos_debug_retire")
 
+    def program_define(self, prog: GpuosProgram) -> int:
+        """gpuos_program_define: returns the program id (aux[0] of PROGRAM ops)."""
+        pid = C.c_uint32()
+        _check(self._lib.gpuos_program_define(self.handle, C.byref(prog), C.byref(pid)),
+               "gpuos_program_define")
+        return pid.value
+
+    def program_update(self, pid: int, prog: GpuosProgram) -> None:
+        """gpuos_program_update: ops submitted from now on run the new body."""
+        _check(self._lib.gpuos_program_update(self.handle, pid, C.byref(prog)), "gpuos_program_update")
+
     def yield_gpu(self, timeout_s: float = 30.0) -> None:
         """gpuos_yield: let the resident kernel leave once the queue is done."""
         _check(self._lib.gpuos_yield(self.handle, int(timeout_s * 1e9)), "gpuos_yield")
@@ -375,4 +447,8 @@ def decode_desc(raw: bytes) -> dict:
     d["ga"] = {"out": q(18), "x": q(20), "res": q(22), "W": q(24), "res_first": w[26],
                "M": w[30], "K": w[31], "sum": q(32)}
     d["view"] = {"shape": list(w[34:38]), "stride": [list(w[38 + 4 * k:42 + 4 * k]) for k in range(3)]}
+    # PROGRAM descriptors
+    d["pg"] = {"n_insns": w[26] & 31, "result": (w[26] >> 8) & 15, "n_inputs": (w[26] >> 16) & 3,
+               "zero_mask": w[26] >> 24, "ins": list(w[27:43]),
+               "consts": list(struct.unpack("<8f", raw[43 * 4:51 * 4]))}
     return d

@@ -58,8 +58,10 @@ def submit_workload(ctx: gpuos.Context, wl: Workload, addr, groups=None, flush_e
     """Submits every group of the workload (flushing after each); returns the ids."""
     ids: List[int] = [0] * len(wl.ops)
     id_of = {}
+    prog_ids = gpuos.define_programs(ctx, wl.ops) if encoded is None else None
     for gi, (g0, g1) in enumerate(groups or wl.groups):
-        arr = encoded[gi] if encoded is not None else gpuos.encode_ops(wl.ops, g0, g1, addr, id_of)
+        arr = encoded[gi] if encoded is not None else \
+            gpuos.encode_ops(wl.ops, g0, g1, addr, id_of, prog_ids)
         got = ctx.submit(arr, g1 - g0, views=gpuos.encode_views(wl.ops, g0, g1))
         for k, i in enumerate(range(g0, g1)):
             ids[i] = got[k]

@@ -219,6 +219,21 @@ def gen_fused_chain(seed: int = 0, n: int = 16_777_216) -> Workload:
                     meta={"n": n, "fused_bytes": 16 * n, "unfused_bytes": 32 * n})
 
 
+# relu(a*x + b) as a register program: r3 = r0 * r1; r3 = r3 + r2; r3 = relu(r3)
+RELU_AXB = Program((("mul", 3, 0, 1), ("add", 3, 3, 2), ("relu", 3, 3)), n_inputs=3, result=3)
+
+
+def gen_program_chain(seed: int = 0, n: int = 16_777_216) -> Workload:
+    """The fused chain's inputs and result, y = relu(a*x + b), computed by
+    one op defined at run time (PROGRAM, inputs a, x, b) instead of the
+    built-in MUL, ADD, RELU."""
+    base = gen_fused_chain(seed, n)
+    bufs = {k: base.buffers[k] for k in ("x", "a", "b", "y")}
+    ops = [Op("program", Ref("y"), (Ref("a"), Ref("x"), Ref("b")), n=n, prog=RELU_AXB)]
+    return Workload("program_chain", bufs, {k: "f32" for k in bufs}, ops, outputs=["y"],
+                    meta={"n": n, "fused_bytes": 16 * n})
+
+
 # ----------------------------------------------------------------------------
 # Batch-1 decode step of a small decoder
 

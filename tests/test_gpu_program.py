@@ -1,0 +1,176 @@
+"""GPU: ops defined at run time (register programs interpreted by the resident
+kernel) against the oracle.  Programs without EXP are bit-exact; with EXP the
+tolerance class applies.  Also: a program updated while ops that use it are
+queued, in-place programs, misaligned operands, and the fused chain computed
+by one program at full size."""
+
+import numpy as np
+import pytest
+
+import oracle
+from persistent_fusion_amd import gpuos, runner, workloads
+from persistent_fusion_amd.workloads import Op, Program, Ref, Workload
+
+pytestmark = pytest.mark.gpu
+
+
+def _need_gpu():
+    import torch
+
+    assert torch.cuda.is_available(), "GPU tests need a GPU"
+    gpuos.lib()
+
+
+def say(msg):
+    print(msg, flush=True)
+
+
+def check(wl, got, outputs=None):
+    want, scales = oracle.run(wl, scales=True)
+    for name in outputs or wl.outputs:
+        r = oracle.compare(got[name], want[name], wl.dtypes[name], scales.get(name))
+        assert r.ok, f"{wl.name}/{name}: {r}"
+
+
+def _specials(rng, n):
+    """Random values with NaN, +-0, +-inf, subnormals, ties and huge/tiny
+    magnitudes spread through them."""
+    v = (rng.standard_normal(n) * np.exp2(rng.integers(-20, 20, n))).astype(np.float32)
+    sp = np.array([np.nan, 0.0, -0.0, np.inf, -np.inf, 1e-45, -1e-45, 1.17e-38, 3.0e38, -3.0e38,
+                   1.0, -1.0, 0.5, 2.0], np.float32)
+    idx = rng.choice(n, size=min(n, 4 * len(sp)), replace=False)
+    v[idx] = np.resize(sp, idx.size)
+    return v
+
+
+# every instruction once, each in its own one-instruction program, plus
+# programs that chain them
+SINGLE = [(name, 3) + tuple(range(gpuos.POP_ARITY[name])) for name in gpuos.POPS]
+CHAINS = [
+    Program((("mul", 3, 0, 1), ("add", 3, 3, 2), ("relu", 3, 3)), 3, 3),
+    Program((("sub", 3, 0, 1), ("div", 4, 3, 2), ("max", 5, 4, 8), ("min", 5, 5, 9), ("abs", 6, 5),
+             ("neg", 6, 6), ("lt", 7, 6, 0), ("sel", 3, 7, 4, 5)), 3, 3, consts=(-4.0, 4.0)),
+    Program((("neg", 3, 0), ("exp", 3, 3), ("add", 3, 3, 8), ("div", 3, 0, 3), ("mul", 3, 3, 1)),
+            2, 3, consts=(1.0,)),                                   # x * sigmoid(x) * u
+    Program((("add", 4, 0, 5), ("mul", 4, 4, 9), ("mov", 1, 4)), 1, 1, consts=(0.0, -0.75)),  # r5 = +0
+]
+
+
+def _program_workload(progs, n, dtype, seed, misalign=False, in_place=False):
+    rng = np.random.default_rng(seed)
+    npdt = workloads.NP_DTYPE[dtype]
+    off = 1 if misalign else 0
+    bufs, dts, ops = {}, {}, []
+    for k, prog in enumerate(progs):
+        ins = []
+        for j in range(prog.n_inputs):
+            name = f"p{k}_{j}"
+            v = _specials(rng, n + off)
+            if dtype == "bf16":
+                v = oracle.f32_to_bf16(v)
+            bufs[name] = v.astype(npdt) if dtype != "bf16" else v
+            dts[name] = dtype
+            ins.append(Ref(name, off))
+        out = ins[0] if in_place else Ref(f"y{k}", off)
+        if not in_place:
+            bufs[f"y{k}"] = np.zeros(n + off, npdt)
+            dts[f"y{k}"] = dtype
+        ops.append(Op("program", out, tuple(ins), n=n, dtype=dtype, prog=prog))
+    outs = sorted({op.out.buf for op in ops})
+    return Workload("programs", bufs, dts, ops, outputs=outs)
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16", "f16"])
+@pytest.mark.parametrize("n", [1, 5, 64 * 8 + 3, 20_011])
+def test_every_instruction_and_chain(dtype, n):
+    _need_gpu()
+    say(f"programs dtype={dtype} n={n}")
+    progs = [Program((ins,), len(ins) - 2, 3) for ins in SINGLE] + CHAINS
+    wl = _program_workload(progs, n, dtype, seed=80 + n)
+    got = runner.run_resident(wl)
+    check(wl, got)
+
+
+@pytest.mark.parametrize("misalign,in_place", [(True, False), (False, True), (True, True)])
+def test_misaligned_and_in_place(misalign, in_place):
+    _need_gpu()
+    say(f"programs misalign={misalign} in_place={in_place}")
+    wl = _program_workload(CHAINS, 100_003, "f32", seed=90, misalign=misalign, in_place=in_place)
+    got = runner.run_resident(wl)
+    check(wl, got)
+
+
+def test_update_while_queued():
+    """Ops keep the body they were submitted with: a program redefined
+    between two submissions gives the old result to the first ops and the
+    new one to the later ops, with one flush for all of them."""
+    _need_gpu()
+    import torch
+
+    say("program update while queued")
+    rng = np.random.default_rng(91)
+    n, per = 4096, 100
+    v1 = Program((("mul", 3, 0, 1), ("add", 3, 3, 8)), 2, 3, consts=(0.5,))
+    v2 = Program((("sub", 3, 0, 1), ("relu", 3, 3), ("mul", 3, 3, 8)), 2, 3, consts=(3.0,))
+    x = rng.uniform(-1, 1, (2 * per, n)).astype(np.float32)
+    w = rng.uniform(-1, 1, (2 * per, n)).astype(np.float32)
+    tx, tw = torch.from_numpy(x).cuda(), torch.from_numpy(w).cuda()
+    ty = torch.full((2 * per, n), float("nan"), device="cuda")
+    ctx = gpuos.Context(0)
+    try:
+        pid = ctx.program_define(gpuos.program_of(v1))
+        def ops(rows):
+            arr = (gpuos.GpuosOp * len(rows))()
+            for k, r in enumerate(rows):
+                arr[k] = gpuos.make_op("program", ty[r].data_ptr(), [tx[r].data_ptr(), tw[r].data_ptr()],
+                                       n=n, dims=(pid,))
+            return arr
+        ctx.submit(ops(range(per)))
+        ctx.program_update(pid, gpuos.program_of(v2))
+        ctx.submit(ops(range(per, 2 * per)))
+        ctx.sync(0, 30.0)
+    finally:
+        ctx.destroy()
+    got = ty.cpu().numpy()
+    for rows, prog in ((range(per), v1), (range(per, 2 * per), v2)):
+        bufs = {"x": x[list(rows)].reshape(-1), "w": w[list(rows)].reshape(-1),
+                "y": np.zeros(len(rows) * n, np.float32)}
+        wl = Workload("upd", bufs, {k: "f32" for k in bufs},
+                      [Op("program", Ref("y"), (Ref("x"), Ref("w")), n=len(rows) * n, prog=prog)])
+        want = oracle.run(wl)["y"]
+        assert np.array_equal(got[list(rows)].reshape(-1).view(np.uint32), want.view(np.uint32))
+
+
+def test_programs_in_a_queue_with_builtin_ops():
+    """Program ops reading and feeding built-in ops: hazards order them."""
+    _need_gpu()
+    say("programs mixed with built-in ops")
+    rng = np.random.default_rng(92)
+    n = 30_000
+    bufs = {k: rng.uniform(-2, 2, n).astype(np.float32) for k in ("a", "b", "c")}
+    for k in ("t", "u", "v", "y"):
+        bufs[k] = np.zeros(n, np.float32)
+    sq = Program((("mul", 3, 0, 0), ("sub", 3, 3, 1)), 2, 3)        # a*a - b
+    mx = Program((("max", 3, 0, 1), ("min", 3, 3, 2)), 3, 3)         # clamp(max(u, v), c)
+    ops = [
+        Op("relu", Ref("t"), (Ref("a"),), n=n),
+        Op("program", Ref("u"), (Ref("t"), Ref("b")), n=n, prog=sq),
+        Op("exp", Ref("v"), (Ref("c"),), n=n),
+        Op("program", Ref("y"), (Ref("u"), Ref("v"), Ref("c")), n=n, prog=mx),
+        Op("program", Ref("t"), (Ref("y"), Ref("a")), n=n, prog=sq),   # rewrites t after its readers
+    ]
+    wl = Workload("mixed", bufs, {k: "f32" for k in bufs}, ops, outputs=["t", "u", "v", "y"])
+    got = runner.run_resident(wl)
+    check(wl, got)
+
+
+def test_program_chain_full_size_equals_the_fused_chain():
+    """relu(a*x + b) at 16M elements as one program: bit-identical to the
+    built-in fused chain and to the oracle."""
+    _need_gpu()
+    say("program chain 16M")
+    wl = workloads.gen_program_chain(seed=0)
+    got = runner.run_resident(wl, outputs=["y"])
+    check(wl, got, ["y"])
+    ref = runner.run_resident(workloads.gen_fused_chain(seed=0), outputs=["y"])
+    assert np.array_equal(got["y"].view(np.uint32), ref["y"].view(np.uint32))

@@ -44,7 +44,7 @@ def test_library_exports_every_declared_symbol():
     missing = [s for s in sorted(declared) if not hasattr(lib, s)]
     assert not missing, missing
     assert set(gpuos.EXPORTS) == declared
-    assert lib.gpuos_abi_version() == 2 == gpuos.ABI_VERSION
+    assert lib.gpuos_abi_version() == 3 == gpuos.ABI_VERSION
 
 
 def test_fused_chain_becomes_one_descriptor():
@@ -669,3 +669,126 @@ def test_exact_in_place_ops_are_accepted():
             make_op("rope", buf(3), [buf(3)], aux=buf(4), n=64, rows=2, row_len=32),
         )
         c.submit(arr)
+
+
+# ----------------------------------------------------------------------------
+# ops defined at run time (register programs)
+
+P = gpuos.make_program
+
+
+def _with(p, **fields):
+    for k, v in fields.items():
+        setattr(p, k, v)
+    return p
+
+
+def _prog_op(pid, n=1000, nin=3, out=0, dtype="f32", **kw):
+    ins = [buf(1 + j) for j in range(nin)]
+    return make_op("program", buf(out), ins[:2], ins[2] if nin > 2 else 0, n=n, dtype=dtype,
+                   dims=(pid,), **kw)
+
+
+def test_program_define_encodes_the_body_into_the_descriptor():
+    with ctx() as c:
+        p0 = c.program_define(P([("mul", 3, 0, 1), ("add", 3, 3, 2), ("relu", 3, 3)], 3, 3))
+        # reads r5 and r6 before writing them: they start at +0 (zero mask)
+        p1 = c.program_define(P([("add", 4, 0, 5), ("sel", 7, 4, 6, 9)], 1, 7, consts=(0.0, 2.5)))
+        assert (p0, p1) == (0, 1)
+        c.submit((gpuos.GpuosOp * 2)(_prog_op(p0), _prog_op(p1, nin=1, out=5)))
+        c.flush()
+        d0, d1 = desc(c, 1), desc(c, 2)
+        assert d0["opcode"] == gpuos.OPCODES["program"] and d0["ntiles"] >= 1
+        assert d0["pg"]["n_insns"] == 3 and d0["pg"]["result"] == 3 and d0["pg"]["n_inputs"] == 3
+        assert d0["pg"]["zero_mask"] == 0
+        assert d0["pg"]["ins"][:3] == [3 | 3 << 5 | 0 << 8 | 1 << 12, 1 | 3 << 5 | 3 << 8 | 2 << 12,
+                                       9 | 3 << 5 | 3 << 8]
+        assert d0["ptr"][:4] == [buf(0), buf(1), buf(2), buf(3)]
+        assert d1["pg"]["zero_mask"] == (1 << 5) | (1 << 6)
+        assert d1["pg"]["ins"][1] == 12 | 7 << 5 | 4 << 8 | 6 << 12 | 9 << 16
+        assert d1["pg"]["consts"][1] == 2.5
+
+
+def test_program_update_changes_only_later_ops():
+    with ctx() as c:
+        pid = c.program_define(P([("add", 3, 0, 1)], 2, 3))
+        c.submit((gpuos.GpuosOp * 1)(_prog_op(pid, nin=2)))
+        c.program_update(pid, P([("sub", 3, 0, 1), ("neg", 3, 3)], 2, 3))
+        c.submit((gpuos.GpuosOp * 1)(_prog_op(pid, nin=2, out=6)))
+        c.flush()
+        a, b = desc(c, 1)["pg"], desc(c, 2)["pg"]
+        assert a["n_insns"] == 1 and a["ins"][0] & 31 == gpuos.POPS["add"]
+        assert b["n_insns"] == 2 and b["ins"][0] & 31 == gpuos.POPS["sub"]
+
+
+@pytest.mark.parametrize("make,msg", [
+    (lambda: P([("add", 3, 0, 1)], 0, 3), "n_inputs"),
+    (lambda: P([("add", 3, 0, 1)], 4, 3), "n_inputs"),
+    (lambda: P([], 1, 0), "n_insns"),
+    (lambda: _with(P([("mov", 1, 0)] * 16, 1, 1), n_insns=17), "n_insns"),
+    (lambda: P([("mov", 8, 0)], 1, 8), "destination"),
+    (lambda: P([("add", 3, 0, 16)], 1, 3), "source register"),
+    (lambda: P([("relu", 3, 0, 1)], 1, 3), "unused operand"),
+    (lambda: P([("mov", 3, 0)], 1, 16), "result"),
+])
+def test_program_define_rejects_malformed_bodies(make, msg):
+    with ctx() as c:
+        with pytest.raises(GpuosError) as e:
+            c.program_define(make())
+        assert e.value.status == gpuos.EINVAL and msg in str(e.value)
+    with ctx() as c:
+        p = P([("mov", 3, 0)], 1, 3)
+        p.insns[0].op = gpuos.POPS["sel"] + 1  # unknown instruction
+        with pytest.raises(GpuosError, match="unknown op"):
+            c.program_define(p)
+        p = P([("mov", 3, 0)], 1, 3)
+        p.insns[5].a = 1  # a slot past n_insns
+        with pytest.raises(GpuosError, match="past n_insns"):
+            c.program_define(p)
+        p = P([("mov", 3, 0)], 1, 3)
+        p.insns[0]._reserved[1] = 1
+        with pytest.raises(GpuosError, match="reserved"):
+            c.program_define(p)
+        with pytest.raises(GpuosError, match="unknown program"):
+            c.program_update(3, P([("mov", 3, 0)], 1, 3))
+
+
+def test_program_op_validation():
+    with ctx() as c:
+        pid = c.program_define(P([("mul", 3, 0, 1)], 2, 3))
+        bad = [
+            (_prog_op(pid + 1, nin=2), "unknown program"),
+            (_prog_op(pid, nin=1), "in[1] must be given"),
+            (_prog_op(pid, nin=3), "in[2] must be null"),
+            (_prog_op(pid, nin=2, dtype="i32"), "int32 is only for"),
+            (_prog_op(pid, nin=2, src_len=(10, 0)), "src_len"),
+            (make_op("program", buf(1), [buf(1) + 8, buf(2)], n=100, dims=(pid,)), "overlaps"),
+        ]
+        for op, msg in bad:
+            with pytest.raises(GpuosError) as e:
+                c.submit((gpuos.GpuosOp * 1)(op))
+            assert e.value.status == gpuos.EINVAL and msg in str(e.value), msg
+        with pytest.raises(GpuosError, match="views are only"):
+            c.submit((gpuos.GpuosOp * 1)(_prog_op(pid, nin=2, n=6)),
+                     views=(gpuos.GpuosView * 1)(gpuos.make_view([2, 3], [[3, 1], [3, 1], [3, 1]])))
+        # in place over its own input, element for element, is fine
+        c.submit((gpuos.GpuosOp * 1)(make_op("program", buf(1), [buf(1), buf(2)], n=100, dims=(pid,))))
+    with pytest.raises(GpuosError, match="only in a context"):
+        gpuos.baseline_run(0, (gpuos.GpuosOp * 1)(_prog_op(0, nin=2)), 1)
+
+
+def test_program_ops_get_hazards_and_are_not_fused():
+    with ctx() as c:
+        pid = c.program_define(P([("max", 3, 0, 1), ("min", 3, 3, 2)], 3, 3))
+        n = 4096
+        arr = (gpuos.GpuosOp * 4)(
+            make_op("relu", buf(3), [buf(9)], n=n),                 # writes the program's in[2]
+            make_op("program", buf(4), [buf(1), buf(2)], buf(3), n=n, dims=(pid,)),
+            make_op("relu", buf(5), [buf(4)], n=n),                 # reads the program's output
+            make_op("relu", buf(6), [buf(5)], n=n),                 # fuses with the one before
+        )
+        c.submit(arr)
+        c.flush()
+        assert c.published(0) == 3
+        assert desc(c, 2)["opcode"] == gpuos.OPCODES["program"] and desc(c, 2)["deps"][0] == 1
+        assert desc(c, 3)["deps"][0] == 2
