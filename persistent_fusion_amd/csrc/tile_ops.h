@@ -318,8 +318,8 @@ __device__ __forceinline__ float prog_max(float a, float b) {
   return __uint_as_float(__float_as_uint(a) & __float_as_uint(b));  // equal: +0 wins
 }
 
-template <class D>
-__device__ __forceinline__ pvec prog_src(D d, const PRegs& R, uint32_t i) {
+// Source register i: r0..r7, or constant i - 8 (lane 16 + (i - 8) of pw).
+__device__ __forceinline__ pvec prog_src(uint32_t pw, const PRegs& R, uint32_t i) {
   switch (i) {
     case 0: return R.r0;
     case 1: return R.r1;
@@ -329,7 +329,7 @@ __device__ __forceinline__ pvec prog_src(D d, const PRegs& R, uint32_t i) {
     case 5: return R.r5;
     case 6: return R.r6;
     case 7: return R.r7;
-    default: return pvec(__uint_as_float(d(43 + (int)(i & 7u))));
+    default: return pvec(__uint_as_float((uint32_t)__builtin_amdgcn_readlane((int)pw, 16 + (int)(i & 7u))));
   }
 }
 
@@ -346,19 +346,23 @@ __device__ __forceinline__ void prog_dst(PRegs& R, uint32_t i, pvec y) {
   }
 }
 
-// Runs the descriptor's program on R; returns the result register.
-template <class D>
-__device__ __forceinline__ pvec prog_run(D d, PRegs& R) {
-  const uint32_t meta = d(26), ni = meta & 31u;
+// Instructions that read b (binary ops and LT) and c (SEL).
+constexpr uint32_t kPReadsB = (1u << GPUOS_P_ADD) | (1u << GPUOS_P_SUB) | (1u << GPUOS_P_MUL) |
+                              (1u << GPUOS_P_DIV) | (1u << GPUOS_P_MIN) | (1u << GPUOS_P_MAX) |
+                              (1u << GPUOS_P_LT) | (1u << GPUOS_P_SEL);
+
+// Runs the program on R and returns the result register.  pw holds the
+// program in lanes: lane s < 16 instruction s, lane 16 + j constant j (read
+// with readlane: it was loaded while every lane was active).
+__device__ __forceinline__ pvec prog_run(uint32_t pw, uint32_t meta, PRegs& R) {
+  const uint32_t ni = meta & 31u;
   for (uint32_t s = 0; s < ni; ++s) {
-    const uint32_t w = d(27 + (int)s);
+    const uint32_t w = (uint32_t)__builtin_amdgcn_readlane((int)pw, (int)s);
     const uint32_t op = w & 31u;
-    const pvec a = prog_src(d, R, (w >> 8) & 15u);
+    const pvec a = prog_src(pw, R, (w >> 8) & 15u);
     pvec b = a, c = a, y;
-    if (op == GPUOS_P_ADD || op == GPUOS_P_SUB || op == GPUOS_P_MUL || op == GPUOS_P_DIV ||
-        op == GPUOS_P_MIN || op == GPUOS_P_MAX || op == GPUOS_P_LT || op == GPUOS_P_SEL)
-      b = prog_src(d, R, (w >> 12) & 15u);
-    if (op == GPUOS_P_SEL) c = prog_src(d, R, (w >> 16) & 15u);
+    if ((kPReadsB >> op) & 1u) b = prog_src(pw, R, (w >> 12) & 15u);
+    if (op == GPUOS_P_SEL) c = prog_src(pw, R, (w >> 16) & 15u);
     switch (op) {
       case GPUOS_P_ADD: y = a + b; break;
       case GPUOS_P_SUB: y = a - b; break;
@@ -379,12 +383,12 @@ __device__ __forceinline__ pvec prog_run(D d, PRegs& R) {
     }
     prog_dst(R, (w >> 5) & 7u, y);
   }
-  return prog_src(d, R, (meta >> 8) & 15u);
+  return prog_src(pw, R, (meta >> 8) & 15u);
 }
 
-// A group's registers: the inputs in r0..r(nin-1), then +0 in every register
+// A pass's registers: the inputs in r0..r(nin-1), then +0 in every register
 // the program reads before writing (mask in meta bits 24-31; never an input
-// register).  The others keep the previous group's values, which the program
+// register).  The others keep the previous pass's values, which the program
 // overwrites before reading.
 __device__ __forceinline__ void prog_init(PRegs& R, uint32_t nin, uint32_t zmask, pvec x0, pvec x1,
                                           pvec x2) {
@@ -399,58 +403,77 @@ __device__ __forceinline__ void prog_init(PRegs& R, uint32_t nin, uint32_t zmask
   if (zmask & 128u) R.r7 = z;
 }
 
-// Tiles as ew_tile with one row per group: whole 16-byte vectors form rows of
-// 64 (one per lane), tile t takes rows t, t + T, ...; the next row's inputs
-// are requested before the current one is computed.  A 16-byte vector holds
-// 4 fp32 or 8 16-bit elements: the program runs once or twice per vector, on
-// 4 elements at a time.  The n % V leftover elements belong to the last
-// tile; misaligned operands use per-element accesses.
-template <int DT, int CPL, int CPS, class D>
-__device__ __forceinline__ void prog_tile(D d, uint32_t t) {
+// Tiles as ew_tile: whole 16-byte vectors form rows of 64 (one per lane), U
+// adjacent rows a group of 8 elements per lane (2 rows of fp32, 1 of 16-bit
+// types), tile t takes groups t, t + T, ...  The program runs on 4 elements
+// at a time; as soon as a pass has copied the last of a row's inputs into
+// its registers, the same row of the tile's next group is requested, so
+// about a group's 3U vectors per lane stay in flight.  The copies complete
+// before that request (a copy the compiler sank into the program's register
+// switch would wait for the newer loads too: the vector-memory counter is in
+// order), and the loads are unconditional, past the end they fall outside
+// the bounded resources and return 0, which keeps the counter's waits exact.
+// The n % V leftover elements belong to the last tile; misaligned operands
+// use per-element accesses.
+template <int DT, int CPL, int CPS>
+__device__ __forceinline__ void prog_tile(SDesc d, uint32_t t) {
   using T = DTr<DT, CPL, CPS>;
   constexpr int V = T::V;
-  constexpr int H = V / 4;  // program passes per vector
+  constexpr int G = 8;      // elements per lane per group
+  constexpr int U = G / V;  // rows per group
+  constexpr int P = G / 4;  // program passes per group (4 elements each)
   const uint32_t n = d(1), ntiles = d(6), meta = d(26);
   const uint32_t nin = (meta >> 16) & 3u, zmask = meta >> 24;
   const uint64_t po = d.q(18), p0 = d.q(20), p1 = nin >= 2 ? d.q(22) : 0, p2 = nin >= 3 ? d.q(24) : 0;
   const uint32_t lane = lane_id();
+  // instructions (dwords 27-42) in lanes 0-15, constants (43-50) in lanes 16-23
+  const uint32_t pw = d.p[27 + (lane & 31u)];
   PRegs R;
   R.r0 = R.r1 = R.r2 = R.r3 = R.r4 = R.r5 = R.r6 = R.r7 = pvec(0.0f);
   const bool fast = aligned16(po) && aligned16(p0) && aligned16(p1) && aligned16(p2);
   if (fast) {
-    const uint32_t nv = n / V, nrows = (nv + 63) / 64;
+    const uint32_t nv = n / V, nrows = (nv + 63) / 64, ngroups = (nrows + U - 1) / U;
     const rsrc_t vo = make_rsrc_n(po, nv * 16u), v0 = make_rsrc_n(p0, nv * 16u),
                  v1 = make_rsrc_n(p1, nv * 16u), v2 = make_rsrc_n(p2, nv * 16u);
-    float x0[V], x1[V], x2[V];
-#pragma unroll
-    for (int e = 0; e < V; ++e) x1[e] = x2[e] = 0.0f;
-    auto load = [&](uint32_t g) {
-      const uint32_t q = g * 64 + lane;
-      T::ldq(v0, q, x0);
-      if (nin >= 2) T::ldq(v1, q, x1);
-      if (nin >= 3) T::ldq(v2, q, x2);
+    float x0[U][V], x1[U][V], x2[U][V];
+    auto load_row = [&](uint32_t g, int u) {
+      // past the end: clamped to a vector out of every range (loads give 0)
+      const uint64_t q64 = ((uint64_t)g * U + u) * 64 + lane;
+      const uint32_t q = q64 < 0x0FFF0000u ? (uint32_t)q64 : 0x0FFF0000u;
+      T::ldq(v0, q, x0[u]);
+      T::ldq(v1, q, x1[u]);
+      T::ldq(v2, q, x2[u]);
     };
-    if (t < nrows) load(t);
-    for (uint32_t g = t; g < nrows; g += ntiles) {
-      pvec c0[H], c1[H], c2[H];
+    if (t < ngroups) {
 #pragma unroll
-      for (int h = 0; h < H; ++h)
+      for (int u = 0; u < U; ++u) load_row(t, u);
+    }
+    for (uint32_t g = t; g < ngroups; g += ntiles) {
+      float w[G];
+#pragma unroll
+      for (int k = 0; k < P; ++k) {
+        const int u = 4 * k / V, e0 = 4 * k % V;  // row and first element of pass k
+        pvec a0, a1, a2;
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
-          c0[h][e] = x0[4 * h + e];
-          c1[h][e] = x1[4 * h + e];
-          c2[h][e] = x2[4 * h + e];
+          a0[e] = x0[u][e0 + e];
+          a1[e] = x1[u][e0 + e];
+          a2[e] = x2[u][e0 + e];
         }
-      if (g + ntiles < nrows) load(g + ntiles);
-      float w[V];
+        asm volatile("" : "+v"(a0), "+v"(a1), "+v"(a2));
+        if (e0 + 4 == V) load_row(g + ntiles, u);  // row u fully taken
+        prog_init(R, nin, zmask, a0, a1, a2);
+        const pvec o = prog_run(pw, meta, R);
 #pragma unroll
-      for (int h = 0; h < H; ++h) {
-        prog_init(R, nin, zmask, c0[h], c1[h], c2[h]);
-        const pvec o = prog_run(d, R);
-#pragma unroll
-        for (int e = 0; e < 4; ++e) w[4 * h + e] = o[e];
+        for (int e = 0; e < 4; ++e) w[4 * k + e] = o[e];
       }
-      T::stq(vo, g * 64 + lane, w);
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        float wr[V];
+#pragma unroll
+        for (int e = 0; e < V; ++e) wr[e] = w[u * V + e];
+        T::stq(vo, (g * U + u) * 64 + lane, wr);
+      }
     }
     if (t + 1 == ntiles && nv * V < n) {  // fewer than V leftover elements
       const uint32_t nb = n * (uint32_t)T::ES;  // bounded: lanes past n read 0
@@ -462,7 +485,7 @@ __device__ __forceinline__ void prog_tile(D d, uint32_t t) {
       if (nin >= 2) y1[0] = T::ld(s1, i);
       if (nin >= 3) y2[0] = T::ld(s2, i);
       prog_init(R, nin, zmask, y0, y1, y2);
-      const pvec o = prog_run(d, R);
+      const pvec o = prog_run(pw, meta, R);
       if (i < n) T::st(so, i, o[0]);
     }
     return;
@@ -480,7 +503,7 @@ __device__ __forceinline__ void prog_tile(D d, uint32_t t) {
       if (nin >= 3) y2[e] = T::ld(s2, i);
     }
     prog_init(R, nin, zmask, y0, y1, y2);
-    const pvec o = prog_run(d, R);
+    const pvec o = prog_run(pw, meta, R);
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
       const uint32_t i = (uint32_t)base + (uint32_t)e * 64 + lane;

@@ -32,6 +32,7 @@ POPS = {"mov": 0, "add": 1, "sub": 2, "mul": 3, "div": 4, "min": 5, "max": 6, "n
 POP_ARITY = {k: (3 if k == "sel" else 2 if k in ("add", "sub", "mul", "div", "min", "max", "lt") else 1)
              for k in POPS}
 PROG_MAX_INSNS = 16
+PROG_MAX_PROGRAMS = 4096  # programs per context
 DTYPES = {"f32": 0, "bf16": 1, "i32": 2, "f16": 3}
 ELEM_BYTES = {"f32": 4, "bf16": 2, "i32": 4}
 FLAG_TRANSIENT, FLAG_LC, FLAG_NONTEMPORAL = 0x1, 0x2, 0x4

@@ -13,6 +13,12 @@ that interception, as a ``TorchDispatchMode``:
   not run: its output tensor is allocated (torch supplies memory only) and
   the op is queued as a gpuos op with a view (strides from the broadcast),
   and the output tensor is returned at once.
+* ``sub`` and ``div`` of two tensors, ``add``, ``sub`` and ``rsub`` with a
+  Python number, ``neg`` and ``abs`` have no built-in opcode: over
+  contiguous operands of one shape (fp32, bf16, fp16) each becomes an op
+  defined at run time (a one-instruction register program, defined once per
+  body and constant in the mode's context), the pages' runtime operator
+  injection for the intercepted ops.
 * An op that only makes a new view of existing memory (``t``, ``view``,
   ``expand``, ``slice`` and the like) runs at once: it touches no element.
 * Any other op, and leaving the mode, first flushes and waits for the queued
@@ -64,6 +70,55 @@ def _ops():
         a.add_.Tensor: ("add", True), a.mul_.Tensor: ("mul", True), a.relu_.default: ("relu", True),
     })
     return _TABLE
+
+
+_PTABLE: dict = {}
+
+
+def _program_ops():
+    """aten ops with no built-in opcode that run as programs defined at run
+    time: func -> (name, in place).  See :func:`program_plan`."""
+    if _PTABLE:
+        return _PTABLE
+    import torch
+
+    a = torch.ops.aten
+    _PTABLE.update({
+        a.sub.Tensor: ("sub", False), a.sub_.Tensor: ("sub", True),
+        a.div.Tensor: ("div", False), a.div_.Tensor: ("div", True),
+        a.rsub.Scalar: ("rsub", False), a.add.Tensor: ("add", False),
+        a.neg.default: ("neg", False), a.abs.default: ("abs", False),
+    })
+    return _PTABLE
+
+
+def program_plan(name, args, kwargs):
+    """The register program for an aten op of :func:`_program_ops`: (body
+    key, constants, tensor operands), or None.  The key is (instructions,
+    inputs) with the result in r3; constants sit in r8.. .  Tensor-tensor
+    ``sub`` and ``div``, tensor-number ``add``, ``sub`` and ``rsub``, and
+    ``neg``, ``abs``.  Division by a number is left to PyTorch (it may use a
+    reciprocal, which would not give the same bits)."""
+    kwargs = kwargs or {}
+    if set(kwargs) - {"alpha"} or kwargs.get("alpha", 1) != 1:
+        return None
+    num = (int, float)
+    if name in ("neg", "abs"):
+        return ((((name, 3, 0),), 1), (), (args[0],)) if len(args) == 1 else None
+    if len(args) != 2:
+        return None
+    x, y = args
+    if type(y) in num:
+        if name == "add":
+            return (((("add", 3, 0, 8),), 1), (float(y),), (x,))
+        if name == "sub":
+            return (((("sub", 3, 0, 8),), 1), (float(y),), (x,))
+        if name == "rsub":
+            return (((("sub", 3, 8, 0),), 1), (float(y),), (x,))
+        return None
+    if name in ("sub", "div"):
+        return ((((name, 3, 0, 1),), 2), (), (x, y))
+    return None
 
 
 _META: set = set()
@@ -257,15 +312,17 @@ class GpuosMode:
         self._keep: list = []
         self._torch_dirty = True
         self._table = _ops()
+        self._ptable = _program_ops()
+        self._pids: dict = {}  # (body key, constants) -> program id
         self._meta = _metadata_ops()
-        self._opcode = {k: gpuos.OPCODES[k] for k in ("add", "mul", "scale", "relu", "exp", "copy")}
+        self._opcode = {k: gpuos.OPCODES[k] for k in ("add", "mul", "scale", "relu", "exp", "copy", "program")}
         self._dtype = {torch.float32: gpuos.DTYPES["f32"], torch.bfloat16: gpuos.DTYPES["bf16"],
                        torch.float16: gpuos.DTYPES["f16"], torch.int32: gpuos.DTYPES["i32"]}
         self._i32 = torch.int32
         self._empty_like = torch.empty_like
         self._empty = torch.empty
         self._tensor = torch.Tensor
-        self.stats = {"queued": 0, "metadata": 0, "passed_through": 0, "syncs": 0}
+        self.stats = {"queued": 0, "programs": 0, "metadata": 0, "passed_through": 0, "syncs": 0}
 
     # ------------------------------------------------------------------
     def _submit_batch(self) -> None:
@@ -344,6 +401,7 @@ class GpuosMode:
         o.in_[0] = tens[0].data_ptr()
         o.in_[1] = tens[1].data_ptr() if len(tens) > 1 else None
         o.alpha = alpha
+        o.aux[0] = 0
         v = self._views[k]
         if vshape is None:
             v.ndim = 0
@@ -371,6 +429,10 @@ class GpuosMode:
             self._queue(kind, dt, alpha, out, tens)
             self.stats["queued"] += 1
             return out
+        if func in self._ptable:
+            done = self._try_program(func, args, kwargs)
+            if done is not None:
+                return done
         if func in self._meta:
             self.stats["metadata"] += 1
             return func(*args, **(kwargs or {}))
@@ -389,6 +451,56 @@ class GpuosMode:
         out = tens[0] if inplace else self._empty(shape, dtype=tens[0].dtype, device=tens[0].device)
         self._queue(kind, gpuos.DTYPES[dt], alpha, out, tens, vshape, vstr)
         self.stats["queued"] += 1
+        return out
+
+    def _try_program(self, func, args, kwargs):
+        """Queues an op of :func:`_program_ops` as a PROGRAM op over contiguous
+        operands of one shape and a float dtype; None if it does not apply."""
+        name, inplace = self._ptable[func]
+        plan = program_plan(name, args, kwargs)
+        if plan is None:
+            return None
+        key, consts, tens = plan
+        x = tens[0]
+        for t in tens:
+            if type(t) is not self._tensor or t.get_device() != self.device or t.requires_grad or \
+                    not t.is_contiguous() or t.dtype != x.dtype or t.shape != x.shape:
+                return None
+        dt = self._dtype.get(x.dtype)
+        n = x.numel()
+        if dt is None or x.dtype == self._i32 or n == 0 or n > (1 << 30):
+            return None
+        if inplace and len(tens) > 1 and tens[1].data_ptr() != x.data_ptr() and \
+                tens[1].untyped_storage().data_ptr() == x.untyped_storage().data_ptr():
+            return None
+        pid = self._pids.get((key, consts))
+        if pid is None:
+            if len(self._pids) >= gpuos.PROG_MAX_PROGRAMS - 1:
+                return None  # every program id is taken: PyTorch runs it
+            insns, nin = key
+            pid = self.ctx.program_define(gpuos.make_program(insns, nin, 3, consts))
+            self._pids[(key, consts)] = pid
+        if self._torch_dirty:
+            self._sync_torch()
+        out = x if inplace else self._empty_like(x)
+        k = self._k
+        o = self._ops[k]
+        o.opcode = self._opcode["program"]
+        o.dtype = dt
+        o.n = n
+        o.out = out.data_ptr()
+        o.in_[0] = x.data_ptr()
+        o.in_[1] = tens[1].data_ptr() if len(tens) > 1 else None
+        o.alpha = 0.0
+        o.aux[0] = pid
+        self._views[k].ndim = 0
+        self._keep.extend(tens)
+        self._keep.append(out)
+        self._k = k + 1
+        self.stats["queued"] += 1
+        self.stats["programs"] += 1
+        if self._k == self._batch:
+            self._submit_batch()
         return out
 
     def _sync_torch(self) -> None:

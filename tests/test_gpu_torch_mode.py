@@ -112,3 +112,44 @@ def test_mode_orders_around_torch_ops_and_keeps_memory():
         mode.close()
     assert mode.stats["queued"] > 40 and mode.stats["syncs"] >= 20
     assert torch.equal(got, want_t)
+
+
+@pytest.mark.parametrize("dtype_name", ["float32", "bfloat16", "float16"])
+def test_ops_without_an_opcode_run_as_programs(dtype_name):
+    """sub, div, neg, abs and number add/sub/rsub become programs defined at
+    run time; their results are PyTorch's, bit for bit."""
+    _need_gpu()
+    import torch
+
+    from persistent_fusion_amd.torch_mode import GpuosMode
+
+    say(f"torch mode programs {dtype_name}")
+    dtype = getattr(torch, dtype_name)
+    g = torch.Generator(device="cpu").manual_seed(62)
+    x = torch.randn(5000, generator=g).to(dtype).cuda()
+    y = (torch.rand(5000, generator=g) + 0.5).to(dtype).cuda()
+
+    def prog(x, y):
+        a = x - y
+        b = a / y
+        c = -b
+        d = c.abs()
+        e = d + 1.25
+        f = e - 3
+        h = 1 - f
+        h.sub_(x)
+        h.div_(y)
+        return a, b, c, d, e, f, h
+
+    want = prog(x, y)
+    mode = GpuosMode(0)
+    try:
+        with mode:
+            got = prog(x, y)
+            got2 = prog(x, y)  # the same bodies and constants again: no new programs
+    finally:
+        mode.close()
+    assert mode.stats["programs"] == 18 and mode.stats["passed_through"] == 0, mode.stats
+    assert len(mode._pids) == 7, mode._pids  # sub, div, neg, abs, +1.25, -3, 1-x
+    for k, (gt, g2, wt) in enumerate(zip(got, got2, want)):
+        assert torch.equal(gt, wt) and torch.equal(g2, wt), k

@@ -90,3 +90,21 @@ def test_metadata_only_ops_are_listed():
         assert f in meta
     for f in (A.add.Tensor, A.clone.default, A.sum.default, A.mm.default, A._to_copy.default):
         assert f not in meta
+
+
+def test_program_plans_for_ops_without_an_opcode():
+    from persistent_fusion_amd.torch_mode import _program_ops, program_plan
+
+    x, y = torch.zeros(4), torch.ones(4)
+    assert program_plan("sub", (x, y), {}) == (((("sub", 3, 0, 1),), 2), (), (x, y))
+    assert program_plan("div", (x, y), {}) == (((("div", 3, 0, 1),), 2), (), (x, y))
+    assert program_plan("add", (x, 2), {})[:2] == (((("add", 3, 0, 8),), 1), (2.0,))
+    assert program_plan("sub", (x, 0.5), {})[:2] == (((("sub", 3, 0, 8),), 1), (0.5,))
+    assert program_plan("rsub", (x, 1), {})[:2] == (((("sub", 3, 8, 0),), 1), (1.0,))  # 1 - x
+    assert program_plan("neg", (x,), {})[:2] == (((("neg", 3, 0),), 1), ())
+    assert program_plan("abs", (x,), {})[:2] == (((("abs", 3, 0),), 1), ())
+    assert program_plan("div", (x, 2.0), {}) is None        # may be a reciprocal multiply in torch
+    assert program_plan("add", (x, y), {}) is None          # a built-in ADD
+    assert program_plan("sub", (x, y), {"alpha": 2}) is None
+    table = _program_ops()
+    assert table[A.sub_.Tensor] == ("sub", True) and table[A.rsub.Scalar] == ("rsub", False)
