@@ -174,3 +174,27 @@ def test_program_chain_full_size_equals_the_fused_chain():
     check(wl, got, ["y"])
     ref = runner.run_resident(workloads.gen_fused_chain(seed=0), outputs=["y"])
     assert np.array_equal(got["y"].view(np.uint32), ref["y"].view(np.uint32))
+
+
+def test_programs_in_the_priority_ring():
+    """Latency-critical PROGRAM ops (claimed from the priority ring) between
+    best-effort built-in ops: every output matches the oracle."""
+    _need_gpu()
+    say("programs in the priority ring")
+    rng = np.random.default_rng(93)
+    n = 8192
+    bufs = {}
+    ops = []
+    clamp = Program((("max", 3, 0, 8), ("min", 3, 3, 9), ("mul", 3, 3, 1)), 2, 3, consts=(-0.5, 0.5))
+    for k in range(40):
+        for nm in (f"a{k}", f"b{k}"):
+            bufs[nm] = rng.uniform(-1, 1, n).astype(np.float32)
+        bufs[f"y{k}"] = np.zeros(n, np.float32)
+        if k % 4 == 0:
+            ops.append(Op("program", Ref(f"y{k}"), (Ref(f"a{k}"), Ref(f"b{k}")), n=n, prog=clamp, lc=True))
+        else:
+            ops.append(Op("mul", Ref(f"y{k}"), (Ref(f"a{k}"), Ref(f"b{k}")), n=n))
+    wl = Workload("lc-programs", bufs, {k: "f32" for k in bufs}, ops,
+                  outputs=[f"y{k}" for k in range(40)])
+    got = runner.run_resident(wl, priority=1)
+    check(wl, got)
