@@ -2153,7 +2153,11 @@ int gpuos_trace_read(gpuos_ctx* c, gpuos_trace_rec* out, uint32_t max, uint32_t*
 
 int gpuos_stop(gpuos_ctx* c, int64_t timeout_ns) {
   if (!c) return fail(GPUOS_EINVAL, "null context");
-  if (c->host_only || c->exited) return 0;
+  if (c->host_only) {  // nothing runs; the context still stops accepting work
+    c->stopped = true;
+    return 0;
+  }
+  if (c->exited) return 0;
   if (c->parked && c->staged.empty()) {  // not running and nothing to run
     c->stopped = true;
     c->exited = true;

@@ -792,3 +792,16 @@ def test_program_ops_get_hazards_and_are_not_fused():
         assert c.published(0) == 3
         assert desc(c, 2)["opcode"] == gpuos.OPCODES["program"] and desc(c, 2)["deps"][0] == 1
         assert desc(c, 3)["deps"][0] == 2
+
+
+def test_yield_and_program_calls_follow_the_context_state():
+    with ctx() as c:
+        c.yield_gpu()  # nothing resident on a host-only context: returns at once
+        pid = c.program_define(P([("mov", 3, 0)], 1, 3))
+        c.stop()
+        for call in (lambda: c.yield_gpu(), lambda: c.program_define(P([("mov", 3, 0)], 1, 3)),
+                     lambda: c.program_update(pid, P([("neg", 3, 0)], 1, 3)),
+                     lambda: c.submit((gpuos.GpuosOp * 1)(_prog_op(pid, nin=1)))):
+            with pytest.raises(GpuosError) as e:
+                call()
+            assert e.value.status == gpuos.ESTATE
