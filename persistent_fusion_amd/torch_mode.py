@@ -391,7 +391,9 @@ class GpuosMode:
             return None
         return kind, dt, alpha, inplace, tens
 
-    def _queue(self, kind, dt, alpha, out, tens, vshape=None, vstr=None) -> None:
+    def _queue(self, kind, dt, alpha, out, tens, vshape=None, vstr=None, pid=0) -> None:
+        """Writes one op (and its view, or none) into the next batch slot.
+        Every field a slot's earlier op may have set is written again."""
         k = self._k
         o = self._ops[k]
         o.opcode = self._opcode[kind]
@@ -401,7 +403,7 @@ class GpuosMode:
         o.in_[0] = tens[0].data_ptr()
         o.in_[1] = tens[1].data_ptr() if len(tens) > 1 else None
         o.alpha = alpha
-        o.aux[0] = 0
+        o.aux[0] = pid  # the program id of a PROGRAM op, else 0
         v = self._views[k]
         if vshape is None:
             v.ndim = 0
@@ -483,24 +485,9 @@ class GpuosMode:
         if self._torch_dirty:
             self._sync_torch()
         out = x if inplace else self._empty_like(x)
-        k = self._k
-        o = self._ops[k]
-        o.opcode = self._opcode["program"]
-        o.dtype = dt
-        o.n = n
-        o.out = out.data_ptr()
-        o.in_[0] = x.data_ptr()
-        o.in_[1] = tens[1].data_ptr() if len(tens) > 1 else None
-        o.alpha = 0.0
-        o.aux[0] = pid
-        self._views[k].ndim = 0
-        self._keep.extend(tens)
-        self._keep.append(out)
-        self._k = k + 1
+        self._queue("program", dt, 0.0, out, tens, pid=pid)
         self.stats["queued"] += 1
         self.stats["programs"] += 1
-        if self._k == self._batch:
-            self._submit_batch()
         return out
 
     def _sync_torch(self) -> None:
