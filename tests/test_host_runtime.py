@@ -805,3 +805,17 @@ def test_yield_and_program_calls_follow_the_context_state():
             with pytest.raises(GpuosError) as e:
                 call()
             assert e.value.status == gpuos.ESTATE
+
+
+def test_extent_limits():
+    # an operand spans at most 0xFFF00000 bytes, and n is at most 2^30
+    with ctx() as c:
+        n32 = 0xFFF00000 // 4
+        c.submit((gpuos.GpuosOp * 1)(make_op("add", buf(0), [buf(64), buf(128)], n=n32)))
+        with pytest.raises(GpuosError, match="spans more than"):
+            c.submit((gpuos.GpuosOp * 1)(make_op("add", buf(0), [buf(64), buf(128)], n=n32 + 1)))
+        c.submit((gpuos.GpuosOp * 1)(make_op("add", buf(200), [buf(240), buf(280)], n=1 << 30,
+                                             dtype="bf16")))
+        with pytest.raises(GpuosError, match="2\\^30"):
+            c.submit((gpuos.GpuosOp * 1)(make_op("add", buf(200), [buf(240), buf(280)], n=(1 << 30) + 1,
+                                                 dtype="bf16")))
