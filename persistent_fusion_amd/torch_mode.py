@@ -21,6 +21,8 @@ that interception, as a ``TorchDispatchMode``:
   injection for the intercepted ops.
 * An op that only makes a new view of existing memory (``t``, ``view``,
   ``expand``, ``slice`` and the like) runs at once: it touches no element.
+* An op none of whose arguments is a CUDA tensor or names a CUDA device
+  runs at once: it can neither read a queued result nor start a GPU kernel.
 * Any other op, and leaving the mode, first flushes and waits for the queued
   ops and lets the resident kernel leave (``gpuos_yield``: while it is
   resident it holds every compute unit's registers, so no PyTorch kernel
@@ -119,6 +121,24 @@ def program_plan(name, args, kwargs):
     if name in ("sub", "div"):
         return ((((name, 3, 0, 1),), 2), (), (x, y))
     return None
+
+
+def _touches_cuda(args, kwargs) -> bool:
+    """Whether any argument is a CUDA tensor or names a CUDA device (then the
+    op may read queued results or start a GPU kernel)."""
+    import torch
+    from torch.utils._pytree import tree_leaves
+
+    for leaf in tree_leaves((args, kwargs or {})):
+        if isinstance(leaf, torch.Tensor):
+            if leaf.is_cuda:
+                return True
+        elif isinstance(leaf, torch.device):
+            if leaf.type == "cuda":
+                return True
+        elif isinstance(leaf, str) and leaf.startswith("cuda"):
+            return True
+    return False
 
 
 _META: set = set()
@@ -287,9 +307,11 @@ class GpuosMode:
     Queued ops are written into a preallocated gpuos_op / gpuos_view batch
     and handed to ``gpuos_submit_views`` and flushed ``batch`` at a time (and
     before any wait), so an error the runtime finds in an op surfaces at that
-    call, and the device works on one batch while Python fills the next."""
+    call, and the device works on one batch while Python fills the next.
+    Queued ops keep their tensors referenced until the next wait; once
+    ``max_kept`` are held, a batch submission also waits for the queue."""
 
-    def __init__(self, device: int = 0, batch: int = 64, **cfg):
+    def __init__(self, device: int = 0, batch: int = 64, max_kept: int = 1 << 16, **cfg):
         from torch.utils._python_dispatch import TorchDispatchMode
 
         outer = self
@@ -305,6 +327,7 @@ class GpuosMode:
         self._torch_device = torch.device("cuda", device)
         self.ctx = gpuos.Context(device, **cfg)
         self._batch = max(1, batch)
+        self.max_kept = max_kept
         self._ops = (gpuos.GpuosOp * self._batch)()
         self._views = (gpuos.GpuosView * self._batch)()
         self._k = 0         # ops in the batch
@@ -322,7 +345,8 @@ class GpuosMode:
         self._empty_like = torch.empty_like
         self._empty = torch.empty
         self._tensor = torch.Tensor
-        self.stats = {"queued": 0, "programs": 0, "metadata": 0, "passed_through": 0, "syncs": 0}
+        self.stats = {"queued": 0, "programs": 0, "metadata": 0, "host_ops": 0, "passed_through": 0,
+                      "syncs": 0}
 
     # ------------------------------------------------------------------
     def _submit_batch(self) -> None:
@@ -338,6 +362,9 @@ class GpuosMode:
         # the next
         self.ctx.flush()
         self._unsynced = True
+        if len(self._keep) >= self.max_kept:
+            # the tensors of queued ops stay referenced until a wait: bound them
+            self.sync()
 
     def sync(self) -> None:
         """Makes every queued op's result final."""
@@ -440,6 +467,10 @@ class GpuosMode:
             return func(*args, **(kwargs or {}))
         plan = plan_op(func, args, kwargs, self._torch_device)
         if plan is None:
+            if not _touches_cuda(args, kwargs):
+                # a host-only op cannot observe the queue or start a GPU kernel
+                self.stats["host_ops"] += 1
+                return func(*args, **(kwargs or {}))
             # the queue finishes and the resident kernel gives the GPU back
             # (while it is resident no other kernel can start)
             self.sync()

@@ -153,3 +153,38 @@ def test_ops_without_an_opcode_run_as_programs(dtype_name):
     assert len(mode._pids) == 7, mode._pids  # sub, div, neg, abs, +1.25, -3, 1-x
     for k, (gt, g2, wt) in enumerate(zip(got, got2, want)):
         assert torch.equal(gt, wt) and torch.equal(g2, wt), k
+
+
+def test_host_ops_do_not_wait_and_kept_tensors_are_bounded():
+    """CPU-only ops inside the mode neither wait for the queue nor make the
+    resident kernel leave; a long run of queued ops waits for the queue
+    whenever max_kept tensors are held, and the results stay PyTorch's."""
+    _need_gpu()
+    import torch
+
+    from persistent_fusion_amd.torch_mode import GpuosMode
+
+    say("torch mode host ops and kept bound")
+    torch.manual_seed(63)
+    x = torch.randn(4096, device="cuda")
+    mode = GpuosMode(0, batch=16, max_kept=200)
+    try:
+        with mode:
+            y = x * 0.5
+            c = torch.arange(10) * 3          # host only
+            d = c + 1
+            t = y
+            for _ in range(300):
+                t = t * 0.999 + x
+            launches_inside = mode.ctx.stats()["launches"]
+        got_y, got_t = y.clone(), t.clone()
+    finally:
+        mode.close()
+    want_t = x * 0.5
+    for _ in range(300):
+        want_t = want_t * 0.999 + x
+    assert mode.stats["host_ops"] >= 2 and mode.stats["passed_through"] == 0, mode.stats
+    assert launches_inside == 1  # no yield happened for the host ops
+    assert mode.stats["syncs"] >= 3  # the kept-tensor bound forced waits
+    assert torch.equal(d, torch.arange(10) * 3 + 1)
+    assert torch.equal(got_y, x * 0.5) and torch.equal(got_t, want_t)

@@ -108,3 +108,14 @@ def test_program_plans_for_ops_without_an_opcode():
     assert program_plan("sub", (x, y), {"alpha": 2}) is None
     table = _program_ops()
     assert table[A.sub_.Tensor] == ("sub", True) and table[A.rsub.Scalar] == ("rsub", False)
+
+
+def test_host_only_arguments_are_recognised():
+    from persistent_fusion_amd.torch_mode import _touches_cuda
+
+    x = torch.zeros(3)
+    assert not _touches_cuda((x, 2.0), {})
+    assert not _touches_cuda(([x, x],), {"dim": 0})
+    assert _touches_cuda((), {"device": torch.device("cuda", 0)})
+    assert _touches_cuda((), {"device": "cuda:0"})
+    assert not _touches_cuda((), {"device": torch.device("cpu")})
