@@ -262,7 +262,9 @@ typedef struct gpuos_stats {
   uint64_t launches;           /* resident kernel launches (1 + relaunches
                                   after idle exits) */
   uint64_t lc_waves;           /* waves serving the latency-critical ring */
-  uint64_t reserved[1];
+  uint64_t programs_lowered;   /* PROGRAM ops run as a built-in op or fused
+                                  micro-program (their body is a chain the
+                                  fused tile expresses; fusion on) */
 } gpuos_stats;
 
 /* Per-descriptor device timing, recorded when config.trace == 1. */
@@ -447,6 +449,13 @@ int gpuos_baseline_run(int device, const gpuos_op* ops, uint32_t n, int fuse,
  * An op's body is fixed when the op is submitted: gpuos_program_update
  * changes the body of ops submitted after it and never of ops already
  * submitted, whether or not they have started.
+ *
+ * With fusion on, an fp32 PROGRAM op whose body is a chain over one
+ * accumulator (each instruction reads the previous result, first an input,
+ * and at most an unchanged input, the result itself or, for MUL, a
+ * constant; ADD, MUL, RELU, EXP, MOV only) runs as the built-in op or fused
+ * micro-program doing the same fp32 operations: the same result, at the
+ * built-in ops' speed.  Other programs are interpreted.
  */
 #define GPUOS_PROG_MAX_INSNS 16
 #define GPUOS_PROG_MAX_PROGRAMS 4096

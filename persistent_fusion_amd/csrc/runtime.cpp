@@ -1325,6 +1325,128 @@ uint32_t try_softmax_av(gpuos_ctx* c, size_t i, size_t end, DevDesc& d) {
   return 2;
 }
 
+// A PROGRAM op whose body is a chain over one accumulator, in fp32, can run as
+// the built-in op or fused micro-program that performs the same fp32
+// operations in the same order: each instruction reads the accumulator (the
+// previous instruction's result, first an input register) and at most an
+// unwritten input register, the accumulator again, or, for MUL, a constant
+// (then a SCALE step), and the result is the last accumulator.  ADD and MUL
+// are commutative in IEEE arithmetic, so acc + x and x + acc are the same
+// result.  This is the operators compiled at run time of the pages, for the
+// programs the fused tile can express; any other program is interpreted.
+bool program_as_builtin(const Staged& st, const gpuos_config& cfg, uint32_t workers, DevDesc& d) {
+  const gpuos_op& o = st.op;
+  if (o.dtype != GPUOS_F32) return false;
+  const ProgCode& pc = st.prog;
+  const uint32_t ni = pc.meta & 31u, res = (pc.meta >> 8) & 15u, nin = pc.n_inputs();
+  if (ni > (uint32_t)kMaxSteps) return false;
+  const uint64_t inp[3] = {(uint64_t)o.in[0], (uint64_t)o.in[1], (uint64_t)o.in[2]};
+  uint32_t written = 0;
+  int acc = -1;
+  uint64_t chain_in = 0, operands[3] = {0, 0, 0};
+  int nops = 0;
+  uint8_t codes[kMaxSteps], fls[kMaxSteps];
+  float scal[kMaxSteps];
+  uint32_t opnd_reg[kMaxSteps];
+  auto is_input = [&](uint32_t r) { return r < nin && !(written & (1u << r)); };
+  for (uint32_t s = 0; s < ni; ++s) {
+    const uint32_t w = pc.ins[s], op = w & 31u, dst = (w >> 5) & 7u;
+    uint32_t a = (w >> 8) & 15u, b = (w >> 12) & 15u;
+    const bool binary = op == GPUOS_P_ADD || op == GPUOS_P_MUL;
+    if (acc < 0) {  // the chain starts from an input register
+      if (!is_input(a)) {
+        if (!binary || !is_input(b)) return false;
+        std::swap(a, b);
+      }
+      chain_in = inp[a];
+      acc = (int)a;
+    }
+    uint8_t code = 0, fl = 0;
+    float k = 0.0f;
+    opnd_reg[s] = 0;
+    switch (op) {
+      case GPUOS_P_MOV: case GPUOS_P_RELU: case GPUOS_P_EXP:
+        if ((int)a != acc) return false;
+        code = op == GPUOS_P_MOV ? FS_COPY : op == GPUOS_P_RELU ? FS_RELU : FS_EXP;
+        break;
+      case GPUOS_P_ADD: case GPUOS_P_MUL: {
+        uint32_t other;
+        if ((int)a == acc) other = b;
+        else if ((int)b == acc) other = a;
+        else return false;
+        code = op == GPUOS_P_ADD ? FS_ADD : FS_MUL;
+        if ((int)other == acc) {
+          fl = FSF_SELF;
+        } else if (is_input(other)) {
+          int slot = 0;
+          for (int q = 0; q < nops; ++q)
+            if (operands[q] == inp[other]) slot = q + 1;
+          if (!slot) {
+            if (nops == 3) return false;
+            operands[nops++] = inp[other];
+            slot = nops;
+          }
+          fl = (uint8_t)(FSF_OPERAND | (slot << 4));
+          opnd_reg[s] = other;
+        } else if (other >= 8 && op == GPUOS_P_MUL) {
+          code = FS_SCALE;
+          k = pc.k[other - 8];
+        } else {
+          return false;
+        }
+        break;
+      }
+      default:
+        return false;
+    }
+    codes[s] = code;
+    fls[s] = fl;
+    scal[s] = k;
+    written |= 1u << dst;
+    acc = (int)dst;
+  }
+  if ((int)res != acc) return false;
+  if (ni == 1) {  // one step: the plain built-in op
+    gpuos_op po;
+    memset(&po, 0, sizeof po);
+    po.dtype = GPUOS_F32;
+    po.flags = o.flags;
+    po.n = o.n;
+    po.out = o.out;
+    po.in[0] = (const void*)chain_in;
+    switch (codes[0]) {
+      case FS_ADD: case FS_MUL:
+        po.opcode = codes[0] == FS_ADD ? GPUOS_OP_ADD : GPUOS_OP_MUL;
+        po.in[1] = (fls[0] & FSF_SELF) ? (const void*)chain_in : (const void*)inp[opnd_reg[0]];
+        break;
+      case FS_SCALE: po.opcode = GPUOS_OP_SCALE; po.alpha = scal[0]; break;
+      case FS_RELU: po.opcode = GPUOS_OP_RELU; break;
+      case FS_EXP: po.opcode = GPUOS_OP_EXP; break;
+      default: po.opcode = GPUOS_OP_COPY; break;
+    }
+    encode_plain(po, cfg, workers, d);
+    return true;
+  }
+  memset(&d, 0, sizeof d);
+  d.opcode = OP_FUSED_EW;
+  d.dtype = GPUOS_F32;
+  d.flags = (uint8_t)(o.flags & GPUOS_FLAG_NONTEMPORAL);
+  d.n = o.n;
+  d.nsteps = (uint8_t)ni;
+  d.f.in[0] = chain_in;
+  for (int q = 0; q < 3; ++q) d.f.in[q + 1] = operands[q];
+  for (uint32_t s = 0; s < ni; ++s) {
+    d.f.step_op[s] = codes[s];
+    d.f.fscal[s] = scal[s];
+    d.f.step_fl[s] = fls[s];
+  }
+  d.f.out[ni - 1] = (uint64_t)o.out;
+  d.f.step_fl[ni - 1] = (uint8_t)(fls[ni - 1] | FSF_STORE);
+  d.user_ops = 1;
+  set_tiling(cfg, workers, d);
+  return true;
+}
+
 void plan_ops(gpuos_ctx* c, size_t begin, size_t end, std::vector<Planned>& plan) {
   const gpuos_config& cfg = c->cfg;
   const bool fuse = cfg.fusion == 1;
@@ -1435,9 +1557,13 @@ void plan_ops(gpuos_ctx* c, size_t begin, size_t end, std::vector<Planned>& plan
       }
     }
     if (pl.count == 1) {
-      encode_plain(s0.op, cfg, c->workers, pl.desc);
-      if (s0.view.on) encode_view(s0.view, c->workers, pl.desc);
-      if (s0.op.opcode == GPUOS_OP_PROGRAM) encode_program(s0.prog, pl.desc);
+      if (s0.op.opcode == GPUOS_OP_PROGRAM && fuse && program_as_builtin(s0, cfg, c->workers, pl.desc)) {
+        ++c->st.programs_lowered;
+      } else {
+        encode_plain(s0.op, cfg, c->workers, pl.desc);
+        if (s0.view.on) encode_view(s0.view, c->workers, pl.desc);
+        if (s0.op.opcode == GPUOS_OP_PROGRAM) encode_program(s0.prog, pl.desc);
+      }
       j = i + 1;
     }
     mark_streaming(cfg, pl.desc);

@@ -60,8 +60,7 @@ class GpuosStats(C.Structure):
     _fields_ = [(name, C.c_uint64) for name in (
         "ops_submitted", "ops_fused", "descs_published", "descs_completed", "flushes",
         "ring_full_waits", "deps_explicit", "deps_auto", "device_error", "error_desc",
-        "worker_waves", "compute_units", "kernel_ns", "launches", "lc_waves")] + [
-            ("reserved", C.c_uint64 * 1)]
+        "worker_waves", "compute_units", "kernel_ns", "launches", "lc_waves", "programs_lowered")]
 
 
 class GpuosTraceRec(C.Structure):

@@ -80,14 +80,17 @@ def _program_workload(progs, n, dtype, seed, misalign=False, in_place=False):
     return Workload("programs", bufs, dts, ops, outputs=outs)
 
 
+@pytest.mark.parametrize("fusion", [1, 2])
 @pytest.mark.parametrize("dtype", ["f32", "bf16", "f16"])
 @pytest.mark.parametrize("n", [1, 5, 64 * 8 + 3, 20_011])
-def test_every_instruction_and_chain(dtype, n):
+def test_every_instruction_and_chain(dtype, n, fusion):
+    """fusion 2: every program interpreted; fusion 1: fp32 chains lowered to
+    built-in descriptors (the rest interpreted)."""
     _need_gpu()
-    say(f"programs dtype={dtype} n={n}")
+    say(f"programs dtype={dtype} n={n} fusion={fusion}")
     progs = [Program((ins,), len(ins) - 2, 3) for ins in SINGLE] + CHAINS
     wl = _program_workload(progs, n, dtype, seed=80 + n)
-    got = runner.run_resident(wl)
+    got = runner.run_resident(wl, fusion=fusion)
     check(wl, got)
 
 
@@ -96,8 +99,9 @@ def test_misaligned_and_in_place(misalign, in_place):
     _need_gpu()
     say(f"programs misalign={misalign} in_place={in_place}")
     wl = _program_workload(CHAINS, 100_003, "f32", seed=90, misalign=misalign, in_place=in_place)
-    got = runner.run_resident(wl)
-    check(wl, got)
+    for fusion in (1, 2):
+        got = runner.run_resident(wl, fusion=fusion)
+        check(wl, got)
 
 
 def test_update_while_queued():
@@ -165,15 +169,17 @@ def test_programs_in_a_queue_with_builtin_ops():
 
 
 def test_program_chain_full_size_equals_the_fused_chain():
-    """relu(a*x + b) at 16M elements as one program: bit-identical to the
-    built-in fused chain and to the oracle."""
+    """relu(a*x + b) at 16M elements as one program, interpreted (fusion
+    off) and lowered to the fused micro-program (fusion on): bit-identical
+    to the built-in fused chain and to the oracle."""
     _need_gpu()
     say("program chain 16M")
     wl = workloads.gen_program_chain(seed=0)
-    got = runner.run_resident(wl, outputs=["y"])
-    check(wl, got, ["y"])
     ref = runner.run_resident(workloads.gen_fused_chain(seed=0), outputs=["y"])
-    assert np.array_equal(got["y"].view(np.uint32), ref["y"].view(np.uint32))
+    for fusion in (2, 1):
+        got = runner.run_resident(wl, outputs=["y"], fusion=fusion)
+        check(wl, got, ["y"])
+        assert np.array_equal(got["y"].view(np.uint32), ref["y"].view(np.uint32)), fusion
 
 
 def test_programs_in_the_priority_ring():

@@ -690,7 +690,7 @@ def _prog_op(pid, n=1000, nin=3, out=0, dtype="f32", **kw):
 
 
 def test_program_define_encodes_the_body_into_the_descriptor():
-    with ctx() as c:
+    with ctx(fusion=2) as c:  # fusion off: no chain is lowered to a built-in descriptor
         p0 = c.program_define(P([("mul", 3, 0, 1), ("add", 3, 3, 2), ("relu", 3, 3)], 3, 3))
         # reads r5 and r6 before writing them: they start at +0 (zero mask)
         p1 = c.program_define(P([("add", 4, 0, 5), ("sel", 7, 4, 6, 9)], 1, 7, consts=(0.0, 2.5)))
@@ -710,7 +710,7 @@ def test_program_define_encodes_the_body_into_the_descriptor():
 
 
 def test_program_update_changes_only_later_ops():
-    with ctx() as c:
+    with ctx(fusion=2) as c:
         pid = c.program_define(P([("add", 3, 0, 1)], 2, 3))
         c.submit((gpuos.GpuosOp * 1)(_prog_op(pid, nin=2)))
         c.program_update(pid, P([("sub", 3, 0, 1), ("neg", 3, 3)], 2, 3))
@@ -819,3 +819,39 @@ def test_extent_limits():
         with pytest.raises(GpuosError, match="2\\^30"):
             c.submit((gpuos.GpuosOp * 1)(make_op("add", buf(200), [buf(240), buf(280)], n=(1 << 30) + 1,
                                                  dtype="bf16")))
+
+
+def test_chain_programs_lower_to_builtin_descriptors():
+    FUSED = 32
+    with ctx() as c:
+        relu_axb = c.program_define(P([("mul", 3, 0, 1), ("add", 3, 3, 2), ("relu", 3, 3)], 3, 3))
+        one_add = c.program_define(P([("add", 3, 1, 0)], 2, 3))            # x1 + x0: commutative
+        scale = c.program_define(P([("mul", 4, 8, 0)], 1, 4, consts=(2.5,)))
+        square_exp = c.program_define(P([("mul", 3, 0, 0), ("exp", 3, 3)], 1, 3))
+        interp = [
+            c.program_define(P([("sub", 3, 0, 1)], 2, 3)),                  # no SUB step
+            c.program_define(P([("add", 3, 0, 8)], 1, 3, consts=(1.0,))),   # ADD of a constant
+            c.program_define(P([("mul", 3, 0, 1), ("add", 4, 0, 1)], 2, 4)),  # the accumulator is dropped
+            c.program_define(P([("add", 3, 0, 5)], 1, 3)),                  # reads an unset register
+        ]
+        ops = [_prog_op(relu_axb, out=0), _prog_op(one_add, nin=2, out=5), _prog_op(scale, nin=1, out=6),
+               _prog_op(square_exp, nin=1, out=7)]
+        ops += [_prog_op(p, nin=2 if k in (0, 2) else 1, out=8 + k) for k, p in enumerate(interp)]
+        ops.append(_prog_op(relu_axb, out=12, dtype="bf16"))                # fp32 only
+        c.submit((gpuos.GpuosOp * len(ops))(*ops))
+        c.flush()
+        d = [desc(c, s) for s in range(1, len(ops) + 1)]
+        assert d[0]["opcode"] == FUSED and d[0]["nsteps"] == 3
+        assert d[0]["step_op"][:3] == [2, 1, 4]                 # MUL, ADD, RELU
+        assert d[0]["ptr"][0] == buf(1)                         # the chain starts from in[0]
+        assert d[1]["opcode"] == gpuos.OPCODES["add"] and d[1]["ptr"][1:3] == [buf(2), buf(1)]
+        assert d[2]["opcode"] == gpuos.OPCODES["scale"] and d[2]["alpha"] == 2.5
+        assert d[3]["opcode"] == FUSED and d[3]["step_fl"][0] & 0x2  # acc * acc
+        for k in range(4, len(ops)):
+            assert d[k]["opcode"] == gpuos.OPCODES["program"], k
+        assert c.stats()["programs_lowered"] == 4
+    with ctx(fusion=2) as c:  # fusion off: every program is interpreted
+        pid = c.program_define(P([("mul", 3, 0, 1), ("add", 3, 3, 2), ("relu", 3, 3)], 3, 3))
+        c.submit((gpuos.GpuosOp * 1)(_prog_op(pid)))
+        c.flush()
+        assert desc(c, 1)["opcode"] == gpuos.OPCODES["program"]
