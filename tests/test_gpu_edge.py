@@ -6,7 +6,9 @@
   the two rings, honoured by the host before publishing);
 * empty submissions and syncs with nothing pending;
 * a strictly dependent chain of 3,000 ops (every op reads the previous
-  op's output), so every descriptor waits on its predecessor.
+  op's output), so every descriptor waits on its predecessor;
+* a GATHER index out of range, which the kernel's own bound check turns
+  into the device error word (no out-of-range access is made).
 """
 
 import numpy as np
@@ -123,3 +125,35 @@ def test_dependent_chain_of_3000_ops():
     for fusion in (1, 2):
         got = runner.run_resident(wl, fusion=fusion)
         check(wl, got)
+
+
+def test_gather_index_out_of_range_poisons_the_context():
+    """The kernel checks every GATHER index against src_len before reading:
+    an index out of range sets the device error word (no access is made),
+    the context reports EDEVICE and refuses work, the kernel still stops
+    normally, and a new context on the same GPU runs correctly."""
+    _need_gpu()
+    import torch
+
+    say("edge: gather index out of range")
+    x = torch.arange(100, dtype=torch.float32, device="cuda")
+    idx = torch.tensor([0, 5, 100, 7], dtype=torch.int32, device="cuda")  # 100 is past src_len
+    y = torch.full((4,), -1.0, device="cuda")
+    op = gpuos.make_op("gather", y.data_ptr(), [x.data_ptr()], idx.data_ptr(), n=4, src_len=(100, 0))
+    ctx = gpuos.Context(0)
+    with pytest.raises(gpuos.GpuosError) as e:
+        ctx.submit(op)
+        ctx.sync(0, 10.0)
+    assert e.value.status == gpuos.EDEVICE
+    assert ctx.stats()["device_error"] == 2  # the gather-range code
+    with pytest.raises(gpuos.GpuosError):
+        ctx.submit(op)
+    with pytest.raises(gpuos.GpuosError) as e:
+        ctx.destroy()
+    assert e.value.status == gpuos.EDEVICE
+    assert y.cpu().tolist() == [0.0, 5.0, -1.0, 7.0]  # in-range elements gathered, the bad one untouched
+    rng = np.random.default_rng(103)
+    bufs = {"a": rng.uniform(-1, 1, 5000).astype(np.float32), "b": np.zeros(5000, np.float32)}
+    wl = Workload("after-error", bufs, {"a": "f32", "b": "f32"}, [Op("relu", Ref("b"), (Ref("a"),), n=5000)],
+                  outputs=["b"])
+    check(wl, runner.run_resident(wl))
