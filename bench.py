@@ -323,6 +323,13 @@ def decode_leg(device=0, reps=3):
     descs_per_run = ctx.stats()["descs_published"] // (reps + 1)
     last_run = sorted(tr, key=lambda x: x["seq"])[-descs_per_run:]
     gaps = handoff_gaps(ctx, last_run)
+    # median claim-to-completion time of each descriptor kind in the last run
+    names = {v: k for k, v in gpuos.OPCODES.items()}
+    names.update({32: "fused_ew", 33: "norm_gemv", 34: "gemv_add", 35: "softmax_av"})
+    by_op = {}
+    for x in last_run:
+        by_op.setdefault(names.get(x["opcode"], str(x["opcode"])), []).append((x["t_done"] - x["t_claim"]) * 1e-2)
+    busy_by_op = {k: round(sorted(v)[len(v) // 2], 2) for k, v in sorted(by_op.items())}
     ctx.destroy()
     torch.cuda.synchronize()
     per_op = []
@@ -363,6 +370,7 @@ def decode_leg(device=0, reps=3):
             "graph_capture_and_instantiate_ms": round(graph["graph_replay"][1] * 1e3, 1),
             "per_op_launch_us_per_op": round(best_b / ops * 1e6, 2),
             "resident_trace_last_run": gaps,
+            "resident_busy_us_by_descriptor": busy_by_op,
             "bytes_per_token": byt // tokens}
 
 
