@@ -510,8 +510,9 @@ def priority_leg(device=0, rounds=200):
 
 def torch_frontend_leg(device=0, reps=5, n_ops=1000, sizes=(4096, 1 << 20)):
     """The same eager PyTorch program (n_ops elementwise ops on fp32 tensors
-    of each size in ``sizes``, each reading one or two earlier results) run
-    by PyTorch itself and under GpuosMode, which queues the ops into the
+    of each size in ``sizes``, each reading one or two earlier results: add,
+    mul, relu, scale, and sub and neg, which have no built-in opcode) run by
+    PyTorch itself and under GpuosMode, which queues the ops into the
     resident kernel; host wall time per program including the final
     synchronisation that brings the result to the host."""
     import numpy as np
@@ -522,7 +523,7 @@ def torch_frontend_leg(device=0, reps=5, n_ops=1000, sizes=(4096, 1 << 20)):
     rng = np.random.default_rng(0)
     prog = []
     for i in range(n_ops):
-        kind = int(rng.integers(0, 4))
+        kind = int(rng.integers(0, 6))
         a, b = int(rng.integers(0, 2 + i)), int(rng.integers(0, 2 + i))
         prog.append((kind, a, b, float(rng.uniform(-1, 1))))
 
@@ -537,7 +538,8 @@ def torch_frontend_leg(device=0, reps=5, n_ops=1000, sizes=(4096, 1 << 20)):
             ts.append(time.perf_counter() - t0)
         return sorted(ts)[len(ts) // 2], float(r)
 
-    res = {"workload": f"{n_ops} eager elementwise ops (add/mul/relu/scale by a Python float), fp32"}
+    res = {"workload": f"{n_ops} eager elementwise ops (add/mul/relu/scale by a Python float, and sub/neg, "
+                       "which the mode runs as programs defined at run time), fp32"}
     mode = GpuosMode(device)
     try:
         for size in sizes:
@@ -549,7 +551,8 @@ def torch_frontend_leg(device=0, reps=5, n_ops=1000, sizes=(4096, 1 << 20)):
                 for kind, a, b, s in prog:
                     x, y = vals[a], vals[b]
                     vals.append(x + y if kind == 0 else x * y if kind == 1 else
-                                torch.relu(x) if kind == 2 else x * s)
+                                torch.relu(x) if kind == 2 else x * s if kind == 3 else
+                                x - y if kind == 4 else -x)
                 return vals[-1].sum()
 
             def in_mode():
