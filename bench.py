@@ -573,6 +573,69 @@ def torch_frontend_leg(device=0, reps=5, n_ops=1000, sizes=(4096, 1 << 20)):
     return res
 
 
+def views_leg(device=0, steps=100, warmup=30, R=4096, C=4096):
+    """Elementwise ops over strided and broadcast views: fp32 [R x C], 4
+    rotating replicas, one resident launch per case, host wall time over
+    `steps` passes.  Cases: a bias add y = x + b[None, :] (reads x and a
+    C-element bias, writes y), a row scale y = x * s[:, None], a transposed
+    copy y = x.T (reads x down its columns), and the contiguous y = x + z
+    for reference.  GB/s counts each operand's bytes once."""
+    import torch
+
+    from persistent_fusion_amd import gpuos
+
+    n = R * C
+    E = 4
+    out = {"workload": f"views over fp32 [{R} x {C}], 4 rotating replicas"}
+    cases = {
+        "bias_add": ("add", [[C, 1], [C, 1], [0, 1]], (n + C + n) * E),
+        "row_scale": ("mul", [[C, 1], [C, 1], [1, 0]], (n + R + n) * E),
+        "transpose_copy": ("copy", [[C, 1], [1, R], [0, 0]], 2 * n * E),
+        "contiguous_add": ("add", None, 3 * n * E),
+    }
+    for name, (kind, strides, byt) in cases.items():
+        reps = []
+        for r in range(REPLICAS):
+            x = torch.rand(n, device=f"cuda:{device}")
+            second = torch.rand(n if name == "contiguous_add" else max(R, C), device=f"cuda:{device}")
+            y = torch.empty(n, device=f"cuda:{device}")
+            ins = [x.data_ptr()] + ([] if kind == "copy" else [second.data_ptr()])
+            op = gpuos.make_op(kind, y.data_ptr(), ins, n=n)
+            view = gpuos.make_view([R, C], strides) if strides else None
+            reps.append((x, second, y, (gpuos.GpuosOp * 1)(op),
+                         (gpuos.GpuosView * 1)(view) if view is not None else None))
+        torch.cuda.synchronize()
+        ctx = gpuos.Context(device)
+        try:
+            def one(k):
+                _, _, _, arr, varr = reps[k % REPLICAS]
+                ctx.submit(arr, 1, views=varr)
+                ctx.flush()
+            for k in range(warmup):
+                one(k)
+            ctx.sync(0, 60.0)
+            t0 = time.perf_counter()
+            for k in range(steps):
+                one(warmup + k)
+            ctx.sync(0, 120.0)
+            wall = time.perf_counter() - t0
+        finally:
+            ctx.destroy()
+        # spot check of the last pass against PyTorch on the same tensors
+        x, second, y, _, _ = reps[(warmup + steps - 1) % REPLICAS]
+        X = x.view(R, C)
+        want = {"bias_add": lambda: X + second[:C][None, :], "row_scale": lambda: X * second[:R][:, None],
+                "transpose_copy": lambda: X.t().contiguous().view(R, C) if R == C else None,
+                "contiguous_add": lambda: X + second.view(R, C)}[name]()
+        gbs = steps * byt / wall / 1e9
+        out[name] = {"gb_per_s": round(gbs, 1), "frac_of_hbm_peak": round(gbs / HBM_PEAK_GBS, 4),
+                     "same_as_torch": bool(want is None or torch.equal(y.view(R, C), want))}
+        log(f"bench: views leg {name}: {out[name]}")
+        del reps
+        torch.cuda.empty_cache()
+    return out
+
+
 def program_leg(device=0, steps=200, warmup=100):
     """The fused chain y = relu(a*x + b) at 16,777,216 fp32 elements computed
     by one op defined at run time (a 3-instruction register program) instead
@@ -691,7 +754,7 @@ def main():
     ap.add_argument("--cpu-budget", type=float, default=10.0)
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--extra", default="",
-                    help="comma-separated extra legs: decode, dag, priority, torch, program (or all)")
+                    help="comma-separated extra legs: decode, dag, priority, torch, program, views (or all)")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
         print("bench.py: this build measures one GPU only (the resident kernel runs on one "
@@ -705,13 +768,13 @@ def main():
     fc = fused_chain_leg(args.steps, args.warmup)
     q = queue_leg(args.queue_reps)
     cp = copy_leg()
-    extra_names = ("decode", "dag", "priority", "torch", "program") if args.extra == "all" else \
+    extra_names = ("decode", "dag", "priority", "torch", "program", "views") if args.extra == "all" else \
         tuple(x for x in args.extra.split(",") if x)
     extra = {}
     for name in extra_names:
         log(f"bench: extra leg {name}")
         extra[name] = {"decode": decode_leg, "dag": dag_leg, "priority": priority_leg,
-                       "torch": torch_frontend_leg, "program": program_leg}[name]()
+                       "torch": torch_frontend_leg, "program": program_leg, "views": views_leg}[name]()
     cpu, parity = (None, None) if args.no_cpu else cpu_baseline_leg(args.cpu_budget, fc["y"])
 
     steps = args.steps

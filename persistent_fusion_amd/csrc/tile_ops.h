@@ -535,6 +535,74 @@ __device__ __forceinline__ void ew_view_tile(D d, uint32_t t) {
   const uint32_t r0 = t * tile;
   const uint32_t r1 = r0 + tile < rows ? r0 + tile : rows;
   const uint32_t lane = lane_id();
+  // Rows that are contiguous in the output and contiguous or broadcast (one
+  // value per row) in every input, with 16-byte aligned row starts, move
+  // 16-byte vectors: V elements per lane per access, UV vectors in flight.
+  constexpr int V = T::V;
+  constexpr int UV = DT == GPUOS_F32 || DT == GPUOS_I32 ? 4 : 2;
+  // An operand read as vectors (inner stride 1) needs 16-byte aligned row
+  // starts; a broadcast one (inner stride 0) is read one element per row.
+  // COPY moves raw 16-byte words, so its input must be contiguous too.
+  bool vec = st[0][3] == 1 && st[1][3] <= 1 && (OP != GPUOS_OP_COPY || st[1][3] == 1) &&
+             (!BIN || st[2][3] <= 1) && L % V == 0;
+  const uint64_t ptr[3] = {d.q(18), d.q(20), d.q(22)};
+#pragma unroll
+  for (int k = 0; k < 3; ++k) {
+    if (k == 2 && !BIN) continue;
+    if (st[k][3] != 1) continue;
+    vec = vec && aligned16(ptr[k]);
+#pragma unroll
+    for (int j = 0; j < 3; ++j) vec = vec && (st[k][j] * (uint32_t)T::ES) % 16u == 0;
+  }
+  if (vec) {
+    const uint32_t nv = L / V;
+    for (uint32_t r = r0; r < r1; ++r) {
+      const uint32_t i2 = r % s2, q = r / s2;
+      const uint32_t i1 = q % s1, i0 = q / s1;
+      uint32_t base[3];
+#pragma unroll
+      for (int k = 0; k < 3; ++k) base[k] = i0 * st[k][0] + i1 * st[k][1] + i2 * st[k][2];
+      // a broadcast input (inner stride 0) has one value per row
+      const float xa = st[1][3] == 0 && OP != GPUOS_OP_COPY ? T::ld(a, base[1]) : 0.0f;
+      const float yb = BIN && st[2][3] == 0 ? T::ld(b, base[2]) : 0.0f;
+      for (uint32_t q0 = 0; q0 < nv; q0 += 64 * UV) {
+        if constexpr (OP == GPUOS_OP_COPY) {  // bits, 16 bytes at a time
+          u32x4 w[UV];
+#pragma unroll
+          for (int u = 0; u < UV; ++u) {
+            const uint32_t qv = q0 + 64 * u + lane;
+            if (qv < nv) w[u] = ld128<CPL>(a, T::ES * (base[1] + qv * V));
+          }
+#pragma unroll
+          for (int u = 0; u < UV; ++u) {
+            const uint32_t qv = q0 + 64 * u + lane;
+            if (qv < nv) st128<CPS>(out, T::ES * (base[0] + qv * V), w[u]);
+          }
+        } else {
+          float x[UV][V], y[UV][V];
+#pragma unroll
+          for (int u = 0; u < UV; ++u) {
+            const uint32_t qv = q0 + 64 * u + lane;
+#pragma unroll
+            for (int e = 0; e < V; ++e) x[u][e] = xa, y[u][e] = yb;
+            if (qv >= nv) continue;
+            if (st[1][3]) T::ldv(a, base[1] + qv * V, x[u]);
+            if (BIN && st[2][3]) T::ldv(b, base[2] + qv * V, y[u]);
+          }
+#pragma unroll
+          for (int u = 0; u < UV; ++u) {
+            const uint32_t qv = q0 + 64 * u + lane;
+            if (qv >= nv) continue;
+            float rr[V];
+#pragma unroll
+            for (int e = 0; e < V; ++e) rr[e] = ew_apply<OP, DT>(x[u][e], y[u][e], alpha);
+            T::stv(out, base[0] + qv * V, rr);
+          }
+        }
+      }
+    }
+    return;
+  }
   for (uint32_t r = r0; r < r1; ++r) {
     const uint32_t i2 = r % s2, q = r / s2;
     const uint32_t i1 = q % s1, i0 = q / s1;
