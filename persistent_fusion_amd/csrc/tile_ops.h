@@ -539,7 +539,7 @@ __device__ __forceinline__ void ew_view_tile(D d, uint32_t t) {
   // value per row) in every input, with 16-byte aligned row starts, move
   // 16-byte vectors: V elements per lane per access, UV vectors in flight.
   constexpr int V = T::V;
-  constexpr int UV = DT == GPUOS_F32 || DT == GPUOS_I32 ? 4 : 2;
+  constexpr int UV = DT == GPUOS_F32 || DT == GPUOS_I32 ? 8 : 4;
   // An operand read as vectors (inner stride 1) needs 16-byte aligned row
   // starts; a broadcast one (inner stride 0) is read one element per row.
   // COPY moves raw 16-byte words, so its input must be contiguous too.
