@@ -537,9 +537,10 @@ __device__ __forceinline__ void ew_view_tile(D d, uint32_t t) {
   const uint32_t lane = lane_id();
   // Rows that are contiguous in the output and contiguous or broadcast (one
   // value per row) in every input, with 16-byte aligned row starts, move
-  // 16-byte vectors: V elements per lane per access, UV vectors in flight.
+  // 16-byte vectors: V elements per lane per access, UV vectors per chunk,
+  // the next chunk in flight while one is computed.
   constexpr int V = T::V;
-  constexpr int UV = DT == GPUOS_F32 || DT == GPUOS_I32 ? 8 : 4;
+  constexpr int UV = DT == GPUOS_F32 || DT == GPUOS_I32 ? 4 : 2;
   // An operand read as vectors (inner stride 1) needs 16-byte aligned row
   // starts; a broadcast one (inner stride 0) is read one element per row.
   // COPY moves raw 16-byte words, so its input must be contiguous too.
@@ -555,50 +556,95 @@ __device__ __forceinline__ void ew_view_tile(D d, uint32_t t) {
     for (int j = 0; j < 3; ++j) vec = vec && (st[k][j] * (uint32_t)T::ES) % 16u == 0;
   }
   if (vec) {
-    const uint32_t nv = L / V;
-    for (uint32_t r = r0; r < r1; ++r) {
+    // the tile's rows cut into chunks of 64 x UV vectors, one flat sequence;
+    // after chunk c's stores, chunk c + 1's inputs are copied out (behind an
+    // asm barrier) and chunk c + 2 is requested, so the copies wait for loads
+    // only and a chunk is in flight while one is computed
+    const uint32_t nv = L / V, cpr = (nv + 64 * UV - 1) / (64 * UV), nchunks = (r1 - r0) * cpr;
+    auto row_base = [&](uint32_t c, int k) {
+      const uint32_t r = r0 + c / cpr;
       const uint32_t i2 = r % s2, q = r / s2;
       const uint32_t i1 = q % s1, i0 = q / s1;
-      uint32_t base[3];
+      return i0 * st[k][0] + i1 * st[k][1] + i2 * st[k][2];
+    };
+    if constexpr (OP == GPUOS_OP_COPY) {  // bits, 16 bytes at a time
+      u32x4 w[UV];
+      auto load = [&](uint32_t c) {
+        const uint32_t ba = row_base(c, 1), q0 = (c % cpr) * 64 * UV;
 #pragma unroll
-      for (int k = 0; k < 3; ++k) base[k] = i0 * st[k][0] + i1 * st[k][1] + i2 * st[k][2];
-      // a broadcast input (inner stride 0) has one value per row
-      const float xa = st[1][3] == 0 && OP != GPUOS_OP_COPY ? T::ld(a, base[1]) : 0.0f;
-      const float yb = BIN && st[2][3] == 0 ? T::ld(b, base[2]) : 0.0f;
-      for (uint32_t q0 = 0; q0 < nv; q0 += 64 * UV) {
-        if constexpr (OP == GPUOS_OP_COPY) {  // bits, 16 bytes at a time
-          u32x4 w[UV];
+        for (int u = 0; u < UV; ++u) {
+          const uint32_t qv = q0 + 64 * u + lane;
+          if (qv < nv) w[u] = ld128<CPL>(a, T::ES * (ba + qv * V));
+        }
+      };
+      u32x4 cw[UV];
+      auto take_then_load = [&](uint32_t next) {
 #pragma unroll
-          for (int u = 0; u < UV; ++u) {
-            const uint32_t qv = q0 + 64 * u + lane;
-            if (qv < nv) w[u] = ld128<CPL>(a, T::ES * (base[1] + qv * V));
-          }
+        for (int u = 0; u < UV; ++u) {
+          cw[u] = w[u];
+          asm volatile("" : "+v"(cw[u]));
+        }
+        if (next < nchunks) load(next);
+      };
+      if (nchunks) {
+        load(0);
+        take_then_load(1);
+      }
+      for (uint32_t c = 0; c < nchunks; ++c) {
+        const uint32_t bo = row_base(c, 0), q0 = (c % cpr) * 64 * UV;
 #pragma unroll
-          for (int u = 0; u < UV; ++u) {
-            const uint32_t qv = q0 + 64 * u + lane;
-            if (qv < nv) st128<CPS>(out, T::ES * (base[0] + qv * V), w[u]);
-          }
-        } else {
-          float x[UV][V], y[UV][V];
+        for (int u = 0; u < UV; ++u) {
+          const uint32_t qv = q0 + 64 * u + lane;
+          if (qv < nv) st128<CPS>(out, T::ES * (bo + qv * V), cw[u]);
+        }
+        if (c + 1 < nchunks) take_then_load(c + 2);
+      }
+    } else {
+      float x[UV][V], y[UV][V];
+      auto load = [&](uint32_t c) {
+        const uint32_t ba = row_base(c, 1), bb = row_base(c, 2), q0 = (c % cpr) * 64 * UV;
+        // a broadcast input (inner stride 0) has one value per row
+        const float xa = st[1][3] == 0 ? T::ld(a, ba) : 0.0f;
+        const float yb = BIN && st[2][3] == 0 ? T::ld(b, bb) : 0.0f;
 #pragma unroll
-          for (int u = 0; u < UV; ++u) {
-            const uint32_t qv = q0 + 64 * u + lane;
+        for (int u = 0; u < UV; ++u) {
+          const uint32_t qv = q0 + 64 * u + lane;
 #pragma unroll
-            for (int e = 0; e < V; ++e) x[u][e] = xa, y[u][e] = yb;
-            if (qv >= nv) continue;
-            if (st[1][3]) T::ldv(a, base[1] + qv * V, x[u]);
-            if (BIN && st[2][3]) T::ldv(b, base[2] + qv * V, y[u]);
-          }
+          for (int e = 0; e < V; ++e) x[u][e] = xa, y[u][e] = yb;
+          if (qv >= nv) continue;
+          if (st[1][3]) T::ldv(a, ba + qv * V, x[u]);
+          if (BIN && st[2][3]) T::ldv(b, bb + qv * V, y[u]);
+        }
+      };
+      float cx[UV][V], cy[UV][V];
+      auto take_then_load = [&](uint32_t next) {
 #pragma unroll
-          for (int u = 0; u < UV; ++u) {
-            const uint32_t qv = q0 + 64 * u + lane;
-            if (qv >= nv) continue;
-            float rr[V];
+        for (int u = 0; u < UV; ++u) {
 #pragma unroll
-            for (int e = 0; e < V; ++e) rr[e] = ew_apply<OP, DT>(x[u][e], y[u][e], alpha);
-            T::stv(out, base[0] + qv * V, rr);
+          for (int e = 0; e < V; ++e) {
+            cx[u][e] = x[u][e];
+            cy[u][e] = y[u][e];
+            asm volatile("" : "+v"(cx[u][e]), "+v"(cy[u][e]));
           }
         }
+        if (next < nchunks) load(next);
+      };
+      if (nchunks) {
+        load(0);
+        take_then_load(1);
+      }
+      for (uint32_t c = 0; c < nchunks; ++c) {
+        const uint32_t bo = row_base(c, 0), q0 = (c % cpr) * 64 * UV;
+#pragma unroll
+        for (int u = 0; u < UV; ++u) {
+          const uint32_t qv = q0 + 64 * u + lane;
+          if (qv >= nv) continue;
+          float rr[V];
+#pragma unroll
+          for (int e = 0; e < V; ++e) rr[e] = ew_apply<OP, DT>(cx[u][e], cy[u][e], alpha);
+          T::stv(out, bo + qv * V, rr);
+        }
+        if (c + 1 < nchunks) take_then_load(c + 2);
       }
     }
     return;
