@@ -78,6 +78,12 @@ constexpr uint8_t DF_AUX_READY = 0x80;
 // Descriptor flag set by the runtime: an elementwise op over a strided or
 // broadcast view (shape and strides in the descriptor's view fields).
 constexpr uint8_t DF_VIEW = 0x40;
+// Descriptor flag set by the runtime with DF_VIEW: a COPY whose view is a
+// 2-D transpose (output rows contiguous, the input contiguous down the output's
+// columns).  Tiles are blocks of kTBlockBytes / element size rows (one 128-byte
+// line of each input column) by kTCols columns, row blocks outer.
+constexpr uint8_t DF_VIEW_T = 0x20;
+constexpr uint32_t kTBlockBytes = 128, kTCols = 128;
 constexpr int kMaxDeps = 14;  // dependencies a descriptor carries (more: wait
                               // for the retire cursor instead)
 constexpr int kMaxFusedInputs = 4;

@@ -512,6 +512,75 @@ __device__ __forceinline__ void prog_tile(SDesc d, uint32_t t) {
   }
 }
 
+// COPY over a transposed view (DF_VIEW_T): out[r][c] = in[c * si + r] for
+// rows r < R and columns c < L, the output's rows contiguous with row stride
+// so.  Tile t is a block of K = 128 / ES rows (one 128-byte line of each input
+// column) by 128 columns.  A lane holds P = 4 / ES adjacent columns per step
+// (one for fp32, two for 16-bit types), two steps for fp32: it reads each of
+// its columns' K elements with eight 16-byte loads (all issued before the
+// first store, line by line so the first rows arrive first) and then writes
+// row by row 4-byte words, so each store instruction writes 256 consecutive
+// output bytes.  Bottom-edge blocks, misaligned input columns and 16-bit
+// outputs whose pairs are not 4-byte aligned move element by element.
+template <int ES, int CPL, int CPS>
+__device__ __forceinline__ void copy_transposed_tile(SDesc d, uint32_t t) {
+  constexpr uint32_t K = kTBlockBytes / ES, P = 4 / ES, CS = 2 / P;
+  constexpr uint32_t W = kTBlockBytes / 16;  // 16-byte loads per column
+  const uint32_t R = d(34) * d(35) * d(36), L = d(37);
+  const uint32_t so = d(38 + 2), si = d(42 + 3);
+  const uint32_t ncb = (L + kTCols - 1) / kTCols;
+  const uint32_t r0 = (t / ncb) * K, c0 = (t % ncb) * kTCols;
+  const uint64_t pout = d.q(18), pin = d.q(20);
+  const rsrc_t out = make_rsrc(pout), in = make_rsrc(pin);
+  const uint32_t lane = lane_id();
+  const bool vec = r0 + K <= R && aligned16(pin) && (si * ES) % 16u == 0 &&
+                   (ES == 4 || ((pout & 3u) == 0 && so % 2u == 0));
+  if (vec) {
+    u32x4 w[CS][P][W];
+#pragma unroll
+    for (uint32_t v = 0; v < W; ++v)
+#pragma unroll
+      for (uint32_t k = 0; k < CS; ++k)
+#pragma unroll
+        for (uint32_t j = 0; j < P; ++j) {
+          // columns past the edge read the last column (stores skip them)
+          const uint32_t c = min(c0 + 64 * P * k + P * lane + j, L - 1);
+          w[k][j][v] = ld128<CPL>(in, ES * (c * si + r0) + 16u * v);
+        }
+    auto word = [&](uint32_t k, uint32_t j, uint32_t m) {  // the dword holding element m
+      const uint32_t q = (m * ES) / 4, v = q / 4, e = q % 4;
+      const u32x4 x = w[k][j][v];
+      return e == 0 ? x.x : e == 1 ? x.y : e == 2 ? x.z : x.w;
+    };
+#pragma unroll
+    for (uint32_t m = 0; m < K; ++m)
+#pragma unroll
+      for (uint32_t k = 0; k < CS; ++k) {
+        const uint32_t c = c0 + 64 * P * k + P * lane;
+        const uint32_t o = ES * ((r0 + m) * so + c);
+        if constexpr (ES == 4) {
+          if (c < L) st32<CPS>(out, o, word(k, 0, m));
+        } else {
+          const uint32_t sh = 16 * (m % 2);
+          const uint32_t lo = (word(k, 0, m) >> sh) & 0xffffu, hi = (word(k, 1, m) >> sh) & 0xffffu;
+          if (c + 1 < L) st32<CPS>(out, o, lo | (hi << 16));
+          else if (c < L) st16<CPS>(out, o, (uint16_t)lo);
+        }
+      }
+    return;
+  }
+  for (uint32_t k = 0; k < CS; ++k)
+    for (uint32_t j = 0; j < P; ++j) {
+      const uint32_t c = c0 + 64 * P * k + P * lane + j;
+      if (c >= L) continue;
+      for (uint32_t m = 0; m < K && r0 + m < R; ++m) {
+        const uint32_t e = c * si + r0 + m, o = ES * ((r0 + m) * so + c);
+        if constexpr (ES == 2) st16<CPS>(out, o, ld16<CPL>(in, 2u * e));
+        else st32<CPS>(out, o, ld32<CPL>(in, 4u * e));
+      }
+    }
+}
+
 // Elementwise op over a strided or broadcast view (DF_VIEW).  The index space
 // is `rows` = shape[0] x shape[1] x shape[2] rows of shape[3] elements; tile t
 // takes `tile` rows from row t * tile, and the lanes split each row, four
@@ -1837,8 +1906,14 @@ template <int CPL, int CPS, class D>
 __device__ __forceinline__ uint32_t exec_view(uint32_t op, uint32_t dt, D d, uint32_t t) {
   switch (op) {
     case GPUOS_OP_COPY:  // bits: the 2- or 4-byte move of any dtype
-      if (dt == GPUOS_BF16 || dt == GPUOS_F16) ew_view_tile<GPUOS_OP_COPY, GPUOS_BF16, CPL, CPS>(d, t);
-      else ew_view_tile<GPUOS_OP_COPY, GPUOS_F32, CPL, CPS>(d, t);
+      if ((d(0) >> 16) & DF_VIEW_T) {
+        if (dt == GPUOS_BF16 || dt == GPUOS_F16) copy_transposed_tile<2, CPL, CPS>(d, t);
+        else copy_transposed_tile<4, CPL, CPS>(d, t);
+      } else if (dt == GPUOS_BF16 || dt == GPUOS_F16) {
+        ew_view_tile<GPUOS_OP_COPY, GPUOS_BF16, CPL, CPS>(d, t);
+      } else {
+        ew_view_tile<GPUOS_OP_COPY, GPUOS_F32, CPL, CPS>(d, t);
+      }
       return 0;
     case GPUOS_OP_ADD: ew_view_any<GPUOS_OP_ADD, true, CPL, CPS>(dt, d, t); return 0;
     case GPUOS_OP_MUL: ew_view_any<GPUOS_OP_MUL, true, CPL, CPS>(dt, d, t); return 0;

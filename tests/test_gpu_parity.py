@@ -170,6 +170,12 @@ _VIEW_CASES = {
     "bias_add": ((37, 300), (300, 1), (300, 1), (0, 1), 37 * 300, 300, 37 * 300),
     "row_scale": ((41, 129), (129, 1), (129, 1), (1, 0), 41 * 129, 41, 41 * 129),
     "transpose": ((33, 70), (1, 33), (70, 1), (0, 0), 33 * 70, 0, 33 * 70),
+    # COPY of these two takes the transposed-block path: ragged row and column
+    # blocks, a padded even output row stride (16-bit pairs stored as words, the
+    # odd last column alone), input columns 16-byte aligned
+    "transpose_read": ((328, 257), (260, 1), (1, 328), (0, 0), 328 * 257, 0, 328 * 260),
+    # odd strides: misaligned input columns and output pairs, element by element
+    "transpose_read_odd": ((70, 33), (33, 1), (1, 70), (0, 0), 70 * 33, 0, 70 * 33),
     "outer": ((50, 64), (64, 1), (1, 0), (0, 1), 50, 64, 50 * 64),
     "strided_out": ((8, 100), (400, 2), (100, 1), (100, 1), 800, 800, 3200),
     "scalar": ((5000,), (1,), (1,), (0,), 5000, 1, 5000),
