@@ -578,22 +578,28 @@ def views_leg(device=0, steps=100, warmup=30, R=4096, C=4096):
     rotating replicas, one resident launch per case, host wall time over
     `steps` passes.  Cases: a bias add y = x + b[None, :] (reads x and a
     C-element bias, writes y), a row scale y = x * s[:, None], a transposed
-    copy y = x.T (reads x down its columns), and the contiguous y = x + z
-    for reference.  GB/s counts each operand's bytes once."""
+    copy y = x.T (reads x down its columns), a batched transposed copy
+    y[b] = x[b].T of 16 [2048 x 512] blocks (the same bytes), and the
+    contiguous y = x + z for reference.  GB/s counts each operand's bytes
+    once."""
     import torch
 
     from persistent_fusion_amd import gpuos
 
     n = R * C
     E = 4
+    BR, BC = 512, 2048  # the batched transpose's output block: [n / (BR * BC), BR, BC]
+    assert n % (BR * BC) == 0
     out = {"workload": f"views over fp32 [{R} x {C}], 4 rotating replicas"}
     cases = {
         "bias_add": ("add", [[C, 1], [C, 1], [0, 1]], (n + C + n) * E),
         "row_scale": ("mul", [[C, 1], [C, 1], [1, 0]], (n + R + n) * E),
         "transpose_copy": ("copy", [[C, 1], [1, R], [0, 0]], 2 * n * E),
+        "batched_transpose_copy": ("copy", [[BR * BC, BC, 1], [BR * BC, 1, BR], [0, 0, 0]], 2 * n * E),
         "contiguous_add": ("add", None, 3 * n * E),
     }
     for name, (kind, strides, byt) in cases.items():
+        shape = [n // (BR * BC), BR, BC] if name.startswith("batched") else [R, C]
         reps = []
         for r in range(REPLICAS):
             x = torch.rand(n, device=f"cuda:{device}")
@@ -601,7 +607,7 @@ def views_leg(device=0, steps=100, warmup=30, R=4096, C=4096):
             y = torch.empty(n, device=f"cuda:{device}")
             ins = [x.data_ptr()] + ([] if kind == "copy" else [second.data_ptr()])
             op = gpuos.make_op(kind, y.data_ptr(), ins, n=n)
-            view = gpuos.make_view([R, C], strides) if strides else None
+            view = gpuos.make_view(shape, strides) if strides else None
             reps.append((x, second, y, (gpuos.GpuosOp * 1)(op),
                          (gpuos.GpuosView * 1)(view) if view is not None else None))
         torch.cuda.synchronize()
@@ -626,6 +632,7 @@ def views_leg(device=0, steps=100, warmup=30, R=4096, C=4096):
         X = x.view(R, C)
         want = {"bias_add": lambda: X + second[:C][None, :], "row_scale": lambda: X * second[:R][:, None],
                 "transpose_copy": lambda: X.t().contiguous().view(R, C) if R == C else None,
+                "batched_transpose_copy": lambda: x.view(-1, BC, BR).transpose(1, 2).contiguous().view(R, C),
                 "contiguous_add": lambda: X + second.view(R, C)}[name]()
         gbs = steps * byt / wall / 1e9
         out[name] = {"gb_per_s": round(gbs, 1), "frac_of_hbm_peak": round(gbs / HBM_PEAK_GBS, 4),

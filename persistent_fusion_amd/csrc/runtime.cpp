@@ -1094,13 +1094,14 @@ void encode_view(const ViewDesc& v, uint32_t workers, DevDesc& d) {
     for (int k = 0; k < 3; ++k) d.p.vstride[k][j] = (int32_t)v.stride[k][j];
   }
   const uint64_t rows = (uint64_t)v.shape[0] * v.shape[1] * v.shape[2], L = v.shape[3];
-  // a 2-D transposing COPY: blocks of 128 / element size rows by kTCols columns
-  if (d.opcode == GPUOS_OP_COPY && v.shape[0] == 1 && v.shape[1] == 1 && v.stride[0][3] == 1 &&
-      v.stride[1][2] == 1 && v.stride[1][3] > 1) {
-    const uint64_t K = kTBlockBytes / elem_size(d.dtype);
+  // a (batched) 2-D transposing COPY: per batch, blocks of 128 / element
+  // size rows by kTCols columns
+  if (d.opcode == GPUOS_OP_COPY && v.shape[0] == 1 && v.stride[0][3] == 1 && v.stride[1][2] == 1 &&
+      v.stride[1][3] > 1) {
+    const uint64_t K = kTBlockBytes / elem_size(d.dtype), R = v.shape[2];
     d.flags |= DF_VIEW_T;
     d.tile = (uint32_t)K;
-    d.ntiles = (uint32_t)(((rows + K - 1) / K) * ((L + kTCols - 1) / kTCols));
+    d.ntiles = (uint32_t)(v.shape[1] * ((R + K - 1) / K) * ((L + kTCols - 1) / kTCols));
     return;
   }
   uint64_t nt = std::max<uint64_t>(1, (rows * L + 1023) / 1024);

@@ -512,9 +512,9 @@ __device__ __forceinline__ void prog_tile(SDesc d, uint32_t t) {
   }
 }
 
-// COPY over a transposed view (DF_VIEW_T): out[r][c] = in[c * si + r] for
-// rows r < R and columns c < L, the output's rows contiguous with row stride
-// so.  Tile t is a block of K = 128 / ES rows (one 128-byte line of each input
+// COPY over a transposed view (DF_VIEW_T): out[b][r][c] = in[b][c * si + r]
+// for batches b < shape[1] (strides d(39), d(43)), rows r < R and columns
+// c < L, the output's rows contiguous with row stride so.  Tile t is a block of K = 128 / ES rows (one 128-byte line of each input
 // column) by 128 columns.  A lane holds P = 4 / ES adjacent columns per step
 // (one for fp32, two for 16-bit types), two steps for fp32: it reads each of
 // its columns' K elements with eight 16-byte loads (all issued before the
@@ -526,11 +526,20 @@ template <int ES, int CPL, int CPS>
 __device__ __forceinline__ void copy_transposed_tile(SDesc d, uint32_t t) {
   constexpr uint32_t K = kTBlockBytes / ES, P = 4 / ES, CS = 2 / P;
   constexpr uint32_t W = kTBlockBytes / 16;  // 16-byte loads per column
-  const uint32_t R = d(34) * d(35) * d(36), L = d(37);
+  const uint32_t R = d(36), L = d(37);
   const uint32_t so = d(38 + 2), si = d(42 + 3);
-  const uint32_t ncb = (L + kTCols - 1) / kTCols;
-  const uint32_t r0 = (t / ncb) * K, c0 = (t % ncb) * kTCols;
-  const uint64_t pout = d.q(18), pin = d.q(20);
+  const uint32_t ncb = (L + kTCols - 1) / kTCols, nb = ((R + K - 1) / K) * ncb;
+  // batch and block within it; the tile index is the same in every lane, and
+  // saying so keeps the batch's base addresses (buffer resources) scalar
+  uint32_t tb = t;
+  uint64_t pout = d.q(18), pin = d.q(20);
+  if (d(35) > 1) {
+    const uint32_t tu = __builtin_amdgcn_readfirstlane(t), bi = tu / nb;
+    tb = tu - bi * nb;
+    pout += (uint64_t)ES * bi * d(38 + 1);
+    pin += (uint64_t)ES * bi * d(42 + 1);
+  }
+  const uint32_t r0 = (tb / ncb) * K, c0 = (tb % ncb) * kTCols;
   const rsrc_t out = make_rsrc(pout), in = make_rsrc(pin);
   const uint32_t lane = lane_id();
   const bool vec = r0 + K <= R && aligned16(pin) && (si * ES) % 16u == 0 &&

@@ -174,6 +174,9 @@ _VIEW_CASES = {
     # blocks, a padded even output row stride (16-bit pairs stored as words, the
     # odd last column alone), input columns 16-byte aligned
     "transpose_read": ((328, 257), (260, 1), (1, 328), (0, 0), 328 * 257, 0, 328 * 260),
+    # batched: x.transpose(1, 2) of a contiguous [3, 136, 72] input, copied out
+    "transpose_read_batched": ((3, 72, 136), (72 * 136, 136, 1), (72 * 136, 1, 72), (0, 0, 0),
+                               3 * 72 * 136, 0, 3 * 72 * 136),
     # odd strides: misaligned input columns and output pairs, element by element
     "transpose_read_odd": ((70, 33), (33, 1), (1, 70), (0, 0), 70 * 33, 0, 70 * 33),
     "outer": ((50, 64), (64, 1), (1, 0), (0, 1), 50, 64, 50 * 64),
