@@ -569,6 +569,34 @@ def test_views_are_normalised_into_the_descriptor():
         assert d3["view"]["stride"] == [[0, 0, 3 * Cn, 1], [0, 0, 3 * Cn, 1], [0, 0, 0, 1]]
 
 
+def test_transposed_copies_are_tiled_in_blocks():
+    """A COPY whose (batched) 2-D view reads the input down the output's
+    columns is flagged 0x20 and tiled per batch into blocks of one 128-byte
+    line per input column (32 fp32 or 64 16-bit rows) by 128 columns; other
+    ops over the same view, and views whose input rows are not contiguous,
+    keep the row tiling."""
+    x, y = buf(0), buf(1)
+    R, L = 300, 257
+    T = [(L, 1), (1, R), (0, 0)]
+    with ctx() as c:
+        _submit_views(c, [make_op("copy", y, [x], n=R * L)], [gpuos.make_view((R, L), T)])
+        _submit_views(c, [make_op("copy", y, [x], n=R * L, dtype="bf16")], [gpuos.make_view((R, L), T)])
+        _submit_views(c, [make_op("copy", y, [x], n=3 * R * L)],
+                      [gpuos.make_view((3, R, L), [(R * L, L, 1), (R * L, 1, R), (0, 0, 0)])])
+        _submit_views(c, [make_op("relu", y, [x], n=R * L)], [gpuos.make_view((R, L), T)])
+        _submit_views(c, [make_op("copy", y, [x], n=R * L)], [gpuos.make_view((R, L), [(L, 1), (2, 2 * R), (0, 0)])])
+        c.flush()
+        assert c.published(0) == 5
+        f32, bf16, batched, relu, strided = (desc(c, k) for k in range(1, 6))
+        for d, rows_per_block, batches in ((f32, 32, 1), (bf16, 64, 1), (batched, 32, 3)):
+            assert d["flags"] & 0x40 and d["flags"] & 0x20
+            assert d["tile"] == rows_per_block
+            assert d["ntiles"] == batches * -(-R // rows_per_block) * -(-L // 128)
+        assert batched["view"]["shape"] == [1, 3, R, L]
+        for d in (relu, strided):
+            assert d["flags"] & 0x40 and not d["flags"] & 0x20
+
+
 @pytest.mark.parametrize("view,msg", [
     (((4, 6), [(0, 1), (6, 1), (6, 1)]), "twice"),
     (((4, 6), [(6, 1), (-6, 1), (6, 1)]), "stride"),
