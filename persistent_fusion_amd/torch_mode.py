@@ -213,7 +213,12 @@ def plan_op(func, args, kwargs, device):
     kwargs = kwargs or {}
     if kind == "add" and kwargs.get("alpha", 1) != 1:
         return None
-    if kind == "copy" and kwargs.get("memory_format", None) not in (None, torch.preserve_format):
+    # the output is contiguous: that is clone's result under contiguous_format,
+    # and under preserve_format only for a contiguous input (PyTorch keeps a
+    # strided input's layout there)
+    fmt = kwargs.get("memory_format", None)
+    if kind == "copy" and (fmt not in (None, torch.preserve_format, torch.contiguous_format) or
+                           (fmt != torch.contiguous_format and not args[0].is_contiguous())):
         return None
     extra = set(kwargs) - {"alpha", "memory_format"}
     if extra:

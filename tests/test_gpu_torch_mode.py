@@ -188,3 +188,34 @@ def test_host_ops_do_not_wait_and_kept_tensors_are_bounded():
     assert mode.stats["syncs"] >= 3  # the kept-tensor bound forced waits
     assert torch.equal(d, torch.arange(10) * 3 + 1)
     assert torch.equal(got_y, x * 0.5) and torch.equal(got_t, want_t)
+
+
+@pytest.mark.parametrize("dtype_name", ["float32", "bfloat16"])
+def test_contiguous_transposes_are_queued(dtype_name):
+    """x.t().contiguous() and a batched x.transpose(1, 2).contiguous() are
+    queued as transposed COPYs (ragged blocks included) and equal PyTorch's
+    results bit for bit; a default clone of a transpose, which keeps the
+    strided layout, passes through and keeps it."""
+    _need_gpu()
+    import torch
+
+    from persistent_fusion_amd.torch_mode import GpuosMode
+
+    dtype = getattr(torch, dtype_name)
+    say(f"torch mode: contiguous transposes {dtype_name}")
+    g = torch.Generator(device="cuda").manual_seed(7)
+    x = torch.randn(300, 257, generator=g, device="cuda").to(dtype)
+    xb = torch.randn(3, 136, 72, generator=g, device="cuda").to(dtype)
+    mode = GpuosMode(0)
+    try:
+        with mode:
+            t2 = x.t().contiguous()
+            t3 = xb.transpose(1, 2).contiguous()
+            queued = mode.stats["queued"]
+            kept = x.t().clone()
+    finally:
+        mode.close()
+    assert queued == 2 and mode.stats["passed_through"] == 1, mode.stats
+    assert t2.is_contiguous() and torch.equal(t2, x.t().contiguous())
+    assert t3.is_contiguous() and torch.equal(t3, xb.transpose(1, 2).contiguous())
+    assert kept.stride() == x.t().stride() and torch.equal(kept, x.t())

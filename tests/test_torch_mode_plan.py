@@ -49,6 +49,8 @@ def test_in_place_and_unit_dimensions():
     lambda: (A.add_.Tensor, (_B[:4], _B[1:5]), {}),                                   # in place over a shifted self
     lambda: (A.add_.Tensor, (_S, _S.t()), {}),                                        # in place over a transposed self
     lambda: (A.relu_.default, (torch.zeros(1, 4).expand(3, 4),), {}),                 # output names elements twice
+    lambda: (A.clone.default, (torch.zeros(3, 4).t(),), {}),                          # clone keeps a strided layout
+    lambda: (A.clone.default, (torch.zeros(3, 4),), {"memory_format": torch.channels_last}),
 ])
 def test_not_intercepted(call):
     func, args, kwargs = call()
@@ -119,3 +121,13 @@ def test_host_only_arguments_are_recognised():
     assert _touches_cuda((), {"device": torch.device("cuda", 0)})
     assert _touches_cuda((), {"device": "cuda:0"})
     assert not _touches_cuda((), {"device": torch.device("cpu")})
+
+
+def test_contiguous_clone_of_a_transpose_is_a_transposed_copy():
+    """x.t().contiguous() reaches the dispatcher as clone(contiguous_format):
+    a COPY whose view reads the input down the output's columns."""
+    x = torch.zeros(3, 5)
+    kind, dt, alpha, shape, inplace, tens, vshape, vstr = plan_op(
+        A.clone.default, (x.t(),), {"memory_format": torch.contiguous_format}, CPU)
+    assert (kind, dt, shape, inplace) == ("copy", "f32", (5, 3), False)
+    assert vshape == [5, 3] and vstr[0] == [3, 1] and vstr[1] == [1, 5]
