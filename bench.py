@@ -1,16 +1,22 @@
 #!/usr/bin/env python3
-"""Benchmark: the fused chain y = relu(a*x + b) on 16,777,216-element fp32
-vectors through the resident kernel, beside one kernel launch per op, a
-stand-alone fused kernel, the 1,000-op elementwise queue (ops/s vs per-op
-launches) and the CPU oracle.
+"""Benchmark of the persistent small-op kernel on one MI355X.
 
-A step is one pass of the whole path over one batch: gpuos_submit of the
-three descriptors, gpuos_flush (fusion pass, ring publication, doorbell), the
-resident kernel's claim/dispatch/completion, and (once, after the last step)
-gpuos_sync.  Four independent replicas of x, a, b, y (1 GiB) rotate across
-steps so the 256 MB infinity cache cannot serve a pass from the previous one.
-The warm-up and timed passes run in one launch of the resident kernel, whose
-duration (HIP events on its stream) gives the roofline's achieved bandwidth.
+The headline is the fused chain y = relu(a*x + b) on 16,777,216-element fp32
+vectors through the resident kernel.  A step is one pass of the whole path
+over one batch: gpuos_submit of the three descriptors, gpuos_flush (fusion
+pass, ring publication, doorbell), the resident kernel's claim, dispatch and
+completion, and (once, after the last step) gpuos_sync.  Four independent
+replicas of x, a, b, y (1 GiB) rotate across steps so the 256 MB infinity
+cache cannot serve a pass from the previous one.  The warm-up and timed passes
+run in one launch of the resident kernel, whose duration (HIP events on its
+stream) gives the roofline's achieved bandwidth.  Beside it: one kernel launch
+per op, a stand-alone fused kernel, graph replay, a plain copy kernel.
+
+The same line carries the other small-op streams (`configs`): the 1,000-op
+elementwise queue, the 24-layer decode, the 100,000-op dynamic DAG and the
+two-priority mix, each with ops/s, GB/s, its roofline fraction, the per-op
+launch comparator and the CPU oracle (untuned, one thread pinned to one core)
+on a bounded sample.
 
 Prints one JSON line (rank 0).  Only one GPU is supported.
 """
@@ -20,6 +26,7 @@ from __future__ import annotations
 import argparse
 import json
 import os
+import subprocess
 import sys
 import time
 
@@ -39,8 +46,10 @@ def log(msg):
     print(msg, file=sys.stderr, flush=True)
 
 
-def fused_chain_leg(steps, warmup, device=0):
-    """One resident launch: `warmup` passes, then `steps` timed passes."""
+def fused_chain_leg(steps, warmup, device=0, warm_s=0.5):
+    """One resident launch: warm-up passes (at least `warmup`, and at least
+    `warm_s` seconds of them, so that the GPU's clocks and memory system are
+    at their sustained state), then `steps` timed passes."""
     import torch
 
     from persistent_fusion_amd import gpuos, runner, traffic, workloads
@@ -59,15 +68,24 @@ def fused_chain_leg(steps, warmup, device=0):
 
     # the launch covers the warm-up passes and the timed passes; the HIP events
     # recorded around it on its stream give the kernel's duration
-    log(f"bench: fused chain, one resident launch: {warmup} warm-up + {steps} timed passes")
     ctx = gpuos.Context(device, trace=1)
-    for k in range(warmup):
-        ctx.submit_noids(arrs[k % REPLICAS], 3)
-        ctx.flush()
-    ctx.sync(0, 60.0)
+    # warm-up: `warmup` passes, continued in rounds of 64 until warm_s
+    # seconds have passed (each round is waited for, so the host does not run
+    # ahead of the device by more than a round)
+    w0 = time.perf_counter()
+    k = 0
+    while k < warmup or time.perf_counter() - w0 < warm_s:
+        for _ in range(warmup if k == 0 and warmup else 64):
+            ctx.submit_noids(arrs[k % REPLICAS], 3)
+            ctx.flush()
+            k += 1
+        ctx.sync(0, 60.0)
+    warm_passes = k
+    log(f"bench: fused chain, one resident launch: {warm_passes} warm-up passes "
+        f"({time.perf_counter() - w0:.2f} s) + {steps} timed passes")
     t0 = time.perf_counter()
     for k in range(steps):
-        ctx.submit_noids(arrs[(warmup + k) % REPLICAS], 3)
+        ctx.submit_noids(arrs[(warm_passes + k) % REPLICAS], 3)
         ctx.flush()
     ctx.sync(0, 120.0)
     t1 = time.perf_counter()
@@ -88,7 +106,7 @@ def fused_chain_leg(steps, warmup, device=0):
     per_pass_dev = sorted((r["t_done"] - r["t_claim"]) * 1e-8 for r in fused)
 
     # output of the last pass (checked against the oracle in the CPU leg)
-    y = reps[(warmup + steps - 1) % REPLICAS]["y"].cpu().numpy()
+    y = reps[(warm_passes + steps - 1) % REPLICAS]["y"].cpu().numpy()
 
     # per-op launches (3 kernels per pass) and one stand-alone fused kernel
     stream = torch.cuda.current_stream(device)
@@ -135,7 +153,7 @@ def fused_chain_leg(steps, warmup, device=0):
     del reps
     torch.cuda.empty_cache()
     return {
-        "wall_s": wall, "kernel_s": kernel_s, "dev_span_s": dev_span, "y": y,
+        "wall_s": wall, "kernel_s": kernel_s, "dev_span_s": dev_span, "y": y, "warmup_passes": warm_passes,
         "fused_bytes": fused_bytes, "unfused_bytes": unfused_bytes,
         "per_pass_dev_us": per_pass_dev[len(per_pass_dev) // 2] * 1e6 if per_pass_dev else None,
         "stats": st, "baselines": res,
@@ -221,7 +239,9 @@ def queue_leg(reps_n, device=0):
             "resident_trace": gaps,
             "resident_us_per_queue_median": round(med * 1e6, 1),
             "per_op_launch_us_per_queue_median": round(bmed * 1e6, 1),
-            "effective_gb_per_s": round(wl.meta["bytes"] / med / 1e9, 1)}
+            "effective_gb_per_s": round(wl.meta["bytes"] / med / 1e9, 1),
+            "roofline": {"bound": "latency (16 MB working set, cache-resident)",
+                         "frac_of_hbm_peak": _frac(wl.meta["bytes"] / med / 1e9)}}
 
 
 class _NoIds(dict):
@@ -371,7 +391,9 @@ def decode_leg(device=0, reps=3):
             "per_op_launch_us_per_op": round(best_b / ops * 1e6, 2),
             "resident_trace_last_run": gaps,
             "resident_busy_us_by_descriptor": busy_by_op,
-            "bytes_per_token": byt // tokens}
+            "bytes_per_token": byt // tokens,
+            "roofline": {"bound": "hbm (weights and KV cache stream every token)",
+                         "frac_of_hbm_peak": _frac(byt / best / 1e9)}}
 
 
 def dag_leg(device=0, reps=2):
@@ -422,7 +444,9 @@ def dag_leg(device=0, reps=2):
             "resident_gb_per_s": round(wl.meta["bytes"] / best / 1e9, 1),
             "per_op_launch_ops_per_s": round(n / best_b),
             "per_op_launch_gb_per_s": round(wl.meta["bytes"] / best_b / 1e9, 1),
-            "speedup_vs_per_op_launch": round(best_b / best, 2)}
+            "speedup_vs_per_op_launch": round(best_b / best, 2),
+            "roofline": {"bound": "hbm and dependency latency",
+                         "frac_of_hbm_peak": _frac(wl.meta["bytes"] / best / 1e9)}}
 
 
 def priority_leg(device=0, rounds=200):
@@ -505,6 +529,9 @@ def priority_leg(device=0, rounds=200):
     torch.cuda.empty_cache()
     res["workload"] = (f"{rounds} rounds of one fp32[67,108,864] best-effort op and ten "
                        "bf16[4096] latency-critical ops (closed loop)")
+    res["ops"] = len(wl.ops)
+    res["roofline"] = {"bound": "hbm (best-effort ops); latency (latency-critical ops)",
+                       "frac_of_hbm_peak": _frac(res["priority_ring"]["aggregate_gb_per_s"])}
     return res
 
 
@@ -697,32 +724,160 @@ def program_leg(device=0, steps=200, warmup=100):
     return out
 
 
-def cpu_baseline_leg(budget_s=10.0, gpu_y=None):
-    """The oracle, untuned, on a bounded sample of the same workload.
+# ---------------------------------------------------------------------------
+# CPU baseline: the oracle, untuned, single-threaded, pinned to one core, in a
+# child process (so that BLAS is limited to one thread before numpy loads and
+# the pinning does not touch the GPU process).
 
-    The first oracle pass also checks the GPU's output of the last timed pass
-    bit for bit."""
+
+def _cpu_info():
+    model = None
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    return {"nproc": os.cpu_count(), "usable_cores": len(os.sched_getaffinity(0)), "cpu_model": model}
+
+
+def _oracle_sample(cfg, budget_s):
+    """Runs the oracle on a bounded sample of config `cfg` in this process;
+    returns the measured sample."""
+    import numpy as np
+
     import oracle
     from persistent_fusion_amd import traffic, workloads
 
-    wl = workloads.gen_fused_chain(seed=0, n=N_ELEMS)
-    fused_bytes = traffic.fused_chain_bytes(wl.ops)
-    passes = 0
-    first = None
-    t0 = time.perf_counter()
-    while True:
-        out = oracle.run(wl)
-        if first is None:
-            first = out["y"]
-        passes += 1
+    np.seterr(all="ignore")
+    t_end = None
+
+    def over(t0):
+        return time.perf_counter() - t0 >= budget_s
+
+    if cfg == "fused_chain":
+        wl = workloads.gen_fused_chain(seed=0, n=N_ELEMS)
+        fb = traffic.fused_chain_bytes(wl.ops)
+        n, t0 = 0, time.perf_counter()
+        while True:
+            out = oracle.run(wl)
+            n += 1
+            if over(t0) or n >= 200:
+                break
         el = time.perf_counter() - t0
-        if el >= budget_s or passes >= 200:
-            break
-    parity = oracle.compare(gpu_y, first, "f32").ok if gpu_y is not None else None
-    return {"value": round(passes * fused_bytes / el / 1e9, 3), "unit": "GB/s", "cores": 1,
-            "kind": "oracle",
-            "sample": f"{passes} passes of the 16,777,216-element relu(a*x+b) chain, op by op "
-                      f"(3 numpy passes each), {el:.1f} s, single thread"}, parity
+        return {"value": round(n * fb / el / 1e9, 3), "unit": "GB/s",
+                "sample": f"{n} passes of the 16,777,216-element relu(a*x+b) chain, op by op (3 numpy "
+                          f"passes each), {el:.1f} s", "_y": out["y"]}
+    if cfg == "elementwise_queue":
+        wl = workloads.gen_elementwise_queue(seed=0)
+        n, t0 = 0, time.perf_counter()
+        while True:
+            oracle.run(wl)
+            n += 1
+            if over(t0):
+                break
+        el = time.perf_counter() - t0
+        return {"value": round(n * len(wl.ops) / el), "unit": "ops/s",
+                "gb_per_s": round(n * wl.meta["bytes"] / el / 1e9, 3),
+                "sample": f"{n} whole 1,000-op queues, {el:.1f} s"}
+    if cfg == "decode":
+        wl = workloads.gen_decode(seed=0)
+        per = wl.meta["ops_per_token"]
+        byt = wl.meta["weight_bytes"] + wl.meta["kv_bytes"]
+        cache = oracle.WeightCache.for_workload(wl)
+        bufs, n, t0 = None, 0, time.perf_counter()
+        while n < wl.meta["tokens"]:
+            bufs = oracle.run(wl, upto=(n + 1) * per, buffers=bufs, start=n * per, wcache=cache)
+            n += 1
+            if over(t0):
+                break
+        el = time.perf_counter() - t0
+        return {"value": round(n / el, 3), "unit": "tok/s", "ops_per_s": round(n * per / el),
+                "gb_per_s": round(n * byt / el / 1e9, 3),
+                "sample": f"the first {n} tokens of the 64-token decode ({n * per} ops, weights widened "
+                          f"to fp64 once and reused), {el:.1f} s"}
+    if cfg == "dynamic_dag":
+        wl = workloads.gen_dynamic_dag(seed=0)
+        ob = wl.meta["out_len"]
+        bufs, n, byt, t0 = None, 0, 0, time.perf_counter()
+        step = 250
+        while n < len(wl.ops):
+            bufs = oracle.run(wl, upto=n + step, buffers=bufs, start=n)
+            for i in range(n, min(n + step, len(wl.ops))):
+                op = wl.ops[i]
+                byt += 4 * (op.n * len(op.ins) + ob[i])
+            n = min(n + step, len(wl.ops))
+            if over(t0):
+                break
+        el = time.perf_counter() - t0
+        return {"value": round(n / el), "unit": "ops/s", "gb_per_s": round(byt / el / 1e9, 3),
+                "sample": f"the first {n} of the 100,000 ops, {el:.1f} s"}
+    if cfg == "priority_mix":
+        wl = workloads.gen_priority_mix(seed=0)
+        per = 1 + wl.meta["lc_per_round"]
+        bufs, n, byt, t0 = None, 0, 0, time.perf_counter()
+        while n < wl.meta["rounds"]:
+            bufs = oracle.run(wl, upto=(n + 1) * per, buffers=bufs, start=n * per)
+            byt += sum(traffic.op_bytes(op) for op in wl.ops[n * per:(n + 1) * per])
+            n += 1
+            if over(t0):
+                break
+        el = time.perf_counter() - t0
+        return {"value": round(byt / el / 1e9, 3), "unit": "GB/s", "ops_per_s": round(n * per / el),
+                "sample": f"the first {n} of the 200 rounds ({n} best-effort and {n * (per - 1)} "
+                          f"latency-critical ops), {el:.1f} s"}
+    raise ValueError(cfg)
+
+
+def cpu_child_main(cfg, budget_s, core, y_path):
+    """Entry of the child process: pin, run the sample, print one JSON line."""
+    os.sched_setaffinity(0, {core})
+    res = _oracle_sample(cfg, budget_s)
+    y = res.pop("_y", None)
+    if y is not None and y_path:
+        import numpy as np
+
+        np.save(y_path, y)
+    print(json.dumps(res), flush=True)
+
+
+def cpu_baseline(cfg, budget_s, gpu_y=None):
+    """The oracle on a bounded sample of config `cfg`, in a child process
+    pinned to one core with one BLAS / OpenMP thread."""
+    import tempfile
+
+    core = sorted(os.sched_getaffinity(0))[0]
+    env = dict(os.environ)
+    for k in ("OMP_NUM_THREADS", "OPENBLAS_NUM_THREADS", "MKL_NUM_THREADS", "BLIS_NUM_THREADS",
+              "NUMEXPR_NUM_THREADS", "VECLIB_MAXIMUM_THREADS"):
+        env[k] = "1"
+    y_path = None
+    if gpu_y is not None:
+        fd, y_path = tempfile.mkstemp(suffix=".npy")
+        os.close(fd)
+    try:
+        r = subprocess.run([sys.executable, os.path.abspath(__file__), "--cpu-child", cfg,
+                            "--cpu-budget", str(budget_s), "--cpu-core", str(core),
+                            "--cpu-y", y_path or ""],
+                           env=env, capture_output=True, text=True, timeout=max(300, 10 * budget_s))
+        if r.returncode != 0:
+            raise RuntimeError(f"oracle child for {cfg} failed:\n{r.stderr[-2000:]}")
+        res = json.loads(r.stdout.strip().splitlines()[-1])
+        parity = None
+        if gpu_y is not None:
+            import numpy as np
+
+            import oracle
+
+            parity = oracle.compare(gpu_y, np.load(y_path), "f32").ok
+    finally:
+        if y_path:
+            os.unlink(y_path)
+    res.update({"cores": 1, "kind": "oracle", "threads": 1, "pinned_core": core, **_cpu_info()})
+    res["sample"] += ", one thread pinned to one core"
+    return res, parity
 
 
 def traffic_per_launch(passes):
@@ -752,17 +907,33 @@ def traffic_per_launch(passes):
         return None
 
 
+def _frac(gbs):
+    return round(gbs / HBM_PEAK_GBS, 4)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=1000)
-    ap.add_argument("--warmup", type=int, default=500)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--device-warmup-s", type=float, default=0.5,
+                    help="the fused chain's warm-up continues until this many seconds have passed")
     ap.add_argument("--queue-reps", type=int, default=50)
-    ap.add_argument("--cpu-budget", type=float, default=10.0)
+    ap.add_argument("--cpu-budget", type=float, default=10.0,
+                    help="seconds of oracle work for the headline's CPU baseline (other configs: "
+                         "proportionally less)")
     ap.add_argument("--no-cpu", action="store_true")
+    ap.add_argument("--configs", default="all",
+                    help="comma-separated configs besides the headline: queue, decode, dag, priority (or all)")
     ap.add_argument("--extra", default="",
-                    help="comma-separated extra legs: decode, dag, priority, torch, program, views (or all)")
+                    help="comma-separated extra legs: torch, program, views (or all)")
+    ap.add_argument("--cpu-child", default="", help=argparse.SUPPRESS)
+    ap.add_argument("--cpu-core", type=int, default=0, help=argparse.SUPPRESS)
+    ap.add_argument("--cpu-y", default="", help=argparse.SUPPRESS)
     args = ap.parse_args()
+    if args.cpu_child:
+        cpu_child_main(args.cpu_child, args.cpu_budget, args.cpu_core, args.cpu_y)
+        return
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
         print("bench.py: this build measures one GPU only (the resident kernel runs on one "
               "device; --gpus must be 1)", file=sys.stderr)
@@ -772,23 +943,47 @@ def main():
 
     assert torch.cuda.is_available(), "bench.py needs a GPU"
     torch.cuda.synchronize()
-    fc = fused_chain_leg(args.steps, args.warmup)
-    q = queue_leg(args.queue_reps)
+    fc = fused_chain_leg(args.steps, args.warmup, warm_s=args.device_warmup_s)
     cp = copy_leg()
-    extra_names = ("decode", "dag", "priority", "torch", "program", "views") if args.extra == "all" else \
+    names = ("queue", "decode", "dag", "priority") if args.configs == "all" else \
+        tuple(x for x in args.configs.split(",") if x)
+    cfgs = {}
+    for name in names:
+        log(f"bench: config {name}")
+        if name == "queue":
+            cfgs["C1_elementwise_queue_1000x4096"] = queue_leg(args.queue_reps)
+        elif name == "decode":
+            cfgs["C3_decode_24_layers_64_tokens"] = decode_leg()
+        elif name == "dag":
+            cfgs["C4_dynamic_dag_100000_ops"] = dag_leg()
+        elif name == "priority":
+            cfgs["C5_priority_mix_200_rounds"] = priority_leg()
+        else:
+            raise SystemExit(f"unknown config {name}")
+    extra_names = ("torch", "program", "views") if args.extra == "all" else \
         tuple(x for x in args.extra.split(",") if x)
     extra = {}
     for name in extra_names:
         log(f"bench: extra leg {name}")
-        extra[name] = {"decode": decode_leg, "dag": dag_leg, "priority": priority_leg,
-                       "torch": torch_frontend_leg, "program": program_leg, "views": views_leg}[name]()
-    cpu, parity = (None, None) if args.no_cpu else cpu_baseline_leg(args.cpu_budget, fc["y"])
+        extra[name] = {"torch": torch_frontend_leg, "program": program_leg, "views": views_leg}[name]()
+    cpu, parity = None, None
+    if not args.no_cpu:
+        log("bench: CPU oracle baselines")
+        cpu, parity = cpu_baseline("fused_chain", args.cpu_budget, fc["y"])
+        share = {"C1_elementwise_queue_1000x4096": ("elementwise_queue", 0.3),
+                 "C3_decode_24_layers_64_tokens": ("decode", 1.5),
+                 "C4_dynamic_dag_100000_ops": ("dynamic_dag", 0.8),
+                 "C5_priority_mix_200_rounds": ("priority_mix", 0.8)}
+        for key, res in cfgs.items():
+            which, f = share[key]
+            res["cpu_baseline"], _ = cpu_baseline(which, max(2.0, f * args.cpu_budget))
 
     steps = args.steps
     value = steps * fc["fused_bytes"] / fc["wall_s"] / 1e9
-    launch_bytes = (args.warmup + steps) * fc["fused_bytes"]
+    passes = fc["warmup_passes"] + steps
+    launch_bytes = passes * fc["fused_bytes"]
     achieved = launch_bytes / fc["kernel_s"] / 1e9
-    tr = traffic_per_launch(args.warmup + steps)
+    tr = traffic_per_launch(passes)
     line = {
         "metric": METRIC,
         "value": round(value, 1),
@@ -808,7 +1003,12 @@ def main():
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
                      "traffic": tr,
-                     "kernel": "gpuos_resident", "passes_per_launch": args.warmup + steps,
+                     "traffic_source": (f"profiles/gpuos_resident_fused_chain_16M_traffic.md: calibrated "
+                                        f"FETCH_SIZE + WRITE_SIZE per pass x {passes} passes (counters "
+                                        f"taken in a separate run of the same kernel sources)")
+                     if tr is not None else None,
+                     "kernel": "gpuos_resident", "passes_per_launch": passes,
+                     "device_warmup_passes": fc["warmup_passes"],
                      "bytes_per_launch": launch_bytes,
                      "launch_s_hip_events": round(fc["kernel_s"], 6)},
         "ops_per_s": round(3 * steps / fc["wall_s"]),
@@ -820,8 +1020,8 @@ def main():
         "standalone_fused_kernel": fc["baselines"]["standalone_fused_kernel"],
         "graph_replay": fc["baselines"]["graph_replay"],
         "graph_replay_fused": fc["baselines"]["graph_replay_fused"],
-        "elementwise_queue_1000x4096": q,
         "plain_copy_kernel": cp,
+        "configs": cfgs,
         **({"extra_configs": extra} if extra else {}),
         "cpu_baseline": cpu,
     }

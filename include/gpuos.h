@@ -43,7 +43,7 @@
 extern "C" {
 #endif
 
-#define GPUOS_ABI_VERSION 3
+#define GPUOS_ABI_VERSION 4
 
 /* Status codes. */
 typedef enum gpuos_status {
@@ -152,9 +152,17 @@ typedef enum gpuos_dtype {
                                        store is elided and its contents are
                                        left undefined */
 #define GPUOS_FLAG_LC 0x2u          /* latency-critical: goes to the priority
-                                       ring, whose work is claimed before any
-                                       best-effort tile; LC ops may depend
-                                       only on LC ops */
+                                       ring, served by reserved waves that
+                                       never run best-effort tiles.  An
+                                       explicit dependency between an LC op
+                                       and a best-effort op is rejected
+                                       (EINVAL).  A byte-range hazard
+                                       between them is honoured on the
+                                       host: gpuos_flush waits, before
+                                       publishing the dependent op, until
+                                       the op it depends on has completed,
+                                       which can block the flush for as
+                                       long as that op runs */
 #define GPUOS_FLAG_NONTEMPORAL 0x4u /* stream the op's operands: loads and
                                        stores are marked non-temporal so
                                        their cache lines are evicted first.
@@ -238,7 +246,18 @@ typedef struct gpuos_config {
                              per XCD).  They never run best-effort tiles, so
                              a latency-critical op waits for no best-effort
                              tile */
-  uint32_t reserved[3];
+  uint32_t tile_counts;   /* debug: count how many times each of the first
+                             tile_counts tiles (tickets) of each ring runs,
+                             in device memory that gpuos_debug_tile_counts
+                             reads back (every count must be exactly 1);
+                             0 = off (default) */
+  uint32_t jitter;        /* debug: before running a tile, its wave waits a
+                             pseudo-random 0..jitter steps of about 0.1 us
+                             drawn from a hash of the tile's ticket, so tiles
+                             start and finish in another order; results of
+                             exact-class ops must not change.  0 = off
+                             (default), at most 1000 */
+  uint32_t reserved;
 } gpuos_config;
 
 /* Counters returned by gpuos_get_stats. */
@@ -287,9 +306,17 @@ void gpuos_config_default(gpuos_config* cfg);
  * Creates a context on HIP device `device`: allocates the descriptor rings
  * (pinned host memory), the scheduler state (device memory) and launches the
  * resident kernel on a library-owned non-blocking stream ("The Paper": one
- * long-lived kernel instead of one launch per op).  cfg may be NULL for the
- * defaults.  *out receives the context (NULL on failure).
- * Errors: EINVAL (bad device or config), ENOMEM, EDEVICE (HIP failure).
+ * long-lived kernel instead of one launch per op).  The grid is sized to the
+ * kernel's occupancy (waves_per_cu on every compute unit), and the kernel
+ * takes no work before every one of its waves is running: each wave checks
+ * in at start, and the call returns only once the whole grid has (a worker
+ * waits only for tiles held by other waves, so a partly resident grid could
+ * wait forever; "The Counter" on the GPUOS page notes the kernel holds the
+ * GPU).  cfg may be NULL for the defaults.  *out receives the context (NULL
+ * on failure).
+ * Errors: EINVAL (bad device or config), ENOMEM, EDEVICE (HIP failure, or the
+ * grid did not become resident within 10 s, for example because another
+ * kernel holds compute units).
  */
 int gpuos_create(int device, const gpuos_config* cfg, gpuos_ctx** out);
 
@@ -344,10 +371,16 @@ int gpuos_submit_views(gpuos_ctx* ctx, const gpuos_op* ops, const gpuos_view* vi
 /*
  * Runs the fusion pass over the staged ops, writes the resulting device
  * descriptors into the ring and rings the doorbell (a release store of the
- * ring tail the resident kernel polls).  Returns without waiting for the ops
- * to run, like a kernel launch.  If the ring is full it waits for space when
- * block_on_full = 1, else returns EAGAIN with the unpublished ops still
- * staged.  Errors: EDEVICE (context poisoned), EAGAIN.
+ * ring tail the resident kernel polls).  This is the user-space form of the
+ * last steps of a launch in "Kernel Launch and Host-Device Interaction"
+ * (section "The launch path": the command packet is written into a ring and
+ * a doorbell write tells the GPU to fetch it), paid once per flush instead of
+ * once per op.  Returns without waiting for the ops to run, like a kernel
+ * launch.  If the ring is full it waits for space when block_on_full = 1,
+ * else returns EAGAIN with the unpublished ops still staged.  A staged op that
+ * has a byte-range hazard on an op of the other ring makes the flush wait on
+ * the host for that op (see GPUOS_FLAG_LC).
+ * Errors: EDEVICE (context poisoned), EAGAIN.
  */
 int gpuos_flush(gpuos_ctx* ctx);
 
@@ -369,7 +402,17 @@ int gpuos_sync(gpuos_ctx* ctx, uint64_t upto, int64_t timeout_ns);
  */
 int gpuos_query(gpuos_ctx* ctx, uint64_t id);
 
-/* Copies the context's counters into *out. */
+/*
+ * Copies the context's counters into *out (host memory, written during the
+ * call only).  The counters are what "gpuopt-runtime 0.1.0" (section "What it
+ * does") keeps for its replay path, recast for a work queue: how many ops were
+ * accepted, fused and completed, how often publication waited, and how long
+ * the resident kernel ran (HIP events, the timing method of "Kernel Launch and
+ * Host-Device Interaction", section "CUDA events for timing").  Works on any
+ * context, also a stopped or poisoned one.  Errors: EINVAL (null argument).
+ * Named gpuos_get_stats rather than gpuos_stats because gpuos_stats is the
+ * struct's name.
+ */
 int gpuos_get_stats(gpuos_ctx* ctx, gpuos_stats* out);
 
 /*
@@ -393,10 +436,14 @@ int gpuos_trace_read(gpuos_ctx* ctx, gpuos_trace_rec* out, uint32_t max,
 int gpuos_stop(gpuos_ctx* ctx, int64_t timeout_ns);
 
 /*
- * Drains every submitted op (or abandons unflushed ones when the context is
- * poisoned), tells the resident kernel to exit, waits for it (bounded by
- * timeout_ns, < 0 = forever) and frees all library memory.  The context
- * pointer is invalid afterwards, also when an error is returned.
+ * Ends a context: drains every submitted op (or abandons unflushed ones when
+ * the context is poisoned), tells the resident kernel to exit, waits for it
+ * (bounded by timeout_ns, < 0 = forever) and frees all library memory.  The
+ * long-lived worker kernel of "GPUOS: A GPU Operating System Primitive for
+ * Transparent Operation Fusion" (section "The Paper") holds its compute units
+ * until told to stop; this is that stop, with a bound so that a wedged kernel
+ * cannot hang the caller.  The context pointer is invalid afterwards, also
+ * when an error is returned.
  * Errors: ETIMEDOUT (kernel did not exit; its memory is then leaked, not
  * freed under it), EDEVICE.
  */
@@ -405,7 +452,12 @@ int gpuos_destroy(gpuos_ctx* ctx, int64_t timeout_ns);
 /*
  * Message describing the last failing call made by this thread (on any
  * context); "" if none.  The pointer stays valid until the thread's next
- * failing call.
+ * failing call.  Errors are reported where the caller waits, as in "Kernel
+ * Launch and Host-Device Interaction" (section "Synchronization primitives":
+ * an asynchronous call returns at once and a failure surfaces at the next
+ * synchronising call); the status code says that a call failed and this
+ * message says why.  It is thread-local rather than per context because some
+ * failures (gpuos_create, gpuos_baseline_run) have no context.
  */
 const char* gpuos_last_error(void);
 

@@ -44,6 +44,20 @@ int gpuos_debug_seq_of(gpuos_ctx* ctx, uint64_t id, int* ring_out, uint64_t* seq
  */
 int gpuos_debug_retire(gpuos_ctx* ctx, int ring, uint64_t upto);
 
+/*
+ * Copies the execution counts of tickets [0, n) of `ring` into out (n
+ * uint32 entries, caller owned), for a context created with
+ * config.tile_counts >= n.  Ticket i is the i-th tile published to the ring
+ * (descriptor s owns the tickets from the sum of the tile counts of the
+ * descriptors before it); each count is the number of times a wave ran that
+ * tile, which the scheduler's claim rule makes exactly 1 ("LithOS", section
+ * 5.4, Algorithm 1: non-overlapping block ranges, so every block runs once).
+ * Call after gpuos_sync; reads device memory while the kernel may run.
+ * Errors: EINVAL (bad argument, n above tile_counts), ESTATE (counting off
+ * or host-only context), EDEVICE.
+ */
+int gpuos_debug_tile_counts(gpuos_ctx* ctx, int ring, uint32_t* out, uint32_t n);
+
 #ifdef __cplusplus
 }
 #endif

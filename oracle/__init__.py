@@ -12,9 +12,10 @@ pinned only through its individual ops) and GPUOS's own scheduling semantics
 (the pages give none beyond "run the queued ops").
 """
 
-from .interpreter import (EXACT_KINDS, TOL_KINDS, OracleError, apply_op, bf16_to_f32,
-                          f32_to_bf16, local_check, out_len, run)
-from .compare import RTOL, Mismatch, compare
+from .interpreter import (EXACT_KINDS, TOL_KINDS, OracleError, WeightCache, apply_op,
+                          bf16_to_f32, f32_to_bf16, local_check, out_len, run)
+from .compare import RTOL, EndToEnd, Mismatch, compare, end_to_end
 
-__all__ = ["EXACT_KINDS", "TOL_KINDS", "OracleError", "apply_op", "bf16_to_f32",
-           "f32_to_bf16", "local_check", "out_len", "run", "RTOL", "Mismatch", "compare"]
+__all__ = ["EXACT_KINDS", "TOL_KINDS", "OracleError", "WeightCache", "apply_op", "bf16_to_f32",
+           "f32_to_bf16", "local_check", "out_len", "run", "RTOL", "EndToEnd", "Mismatch",
+           "compare", "end_to_end"]

@@ -113,3 +113,55 @@ def compare(got: np.ndarray, want: np.ndarray, dtype: str,
         return Mismatch(cnt, total, i, float(_as_f32(got[i:i + 1], dtype)[0]),
                         float(_as_f32(want[i:i + 1], dtype)[0]), worst)
     return Mismatch(0, total, worst_rel=worst)
+
+
+@dataclass
+class EndToEnd:
+    """Outcome of an end-to-end comparison of a final buffer.
+
+    ``count`` elements lie outside the bound, ``bit_equal`` are bit-identical
+    (any NaN matching any NaN), ``rel_l2`` is ||g - o||_2 / ||o||_2 over the
+    elements finite on both sides and ``max_rel`` the largest |g - o| / |o|
+    there (0 where both are 0)."""
+
+    count: int
+    total: int
+    bit_equal: int
+    rel_l2: float
+    max_rel: float
+
+    @property
+    def fraction(self) -> float:
+        return self.count / self.total if self.total else 0.0
+
+    def __str__(self) -> str:
+        return (f"{self.count}/{self.total} outside the bound ({self.fraction:.3%}), "
+                f"{self.bit_equal} bit-identical, rel L2 {self.rel_l2:.3g}, max rel {self.max_rel:.3g}")
+
+
+def end_to_end(got: np.ndarray, want: np.ndarray, dtype: str, rtol: Optional[float] = None) -> EndToEnd:
+    """Compares a final buffer of a long queue with the oracle's run of the
+    same queue.  Every element, whichever op wrote it last, must satisfy the
+    relative bound of its type, ``|g - o| <= rtol * |o|`` (two subnormal steps
+    near zero) with the same class (NaN, +inf, -inf, finite): along a chain of
+    ops, the rounding differences that tolerance-class ops are allowed reach
+    the later exact ops too, so the exact-class bit test does not apply to
+    them.  The caller states how many elements may fall outside the bound."""
+    got = np.asarray(got)
+    want = np.asarray(want)
+    m = compare(got, want, dtype, np.zeros(got.shape[0]), rtol)
+    gf = _as_f32(got, dtype).astype(np.float64)
+    wf = _as_f32(want, dtype).astype(np.float64)
+    if dtype == "i32":
+        same = got == want
+    else:
+        bits = np.uint16 if dtype in ("bf16", "f16") else np.uint32
+        same = (got.view(bits) == want.view(bits)) | (np.isnan(gf) & np.isnan(wf))
+    fin = np.isfinite(gf) & np.isfinite(wf)
+    diff = np.abs(gf[fin] - wf[fin])
+    ref = np.abs(wf[fin])
+    norm = float(np.sqrt(np.sum(ref * ref)))
+    rel_l2 = float(np.sqrt(np.sum(diff * diff))) / norm if norm > 0 else float(np.any(diff > 0))
+    with np.errstate(invalid="ignore", divide="ignore"):
+        rel = np.where(ref > 0, diff / np.where(ref > 0, ref, 1.0), np.where(diff > 0, np.inf, 0.0))
+    return EndToEnd(m.count, m.total, int(same.sum()), rel_l2, float(rel.max()) if rel.size else 0.0)

@@ -58,6 +58,20 @@ round-to-nearest-even narrowing to bf16):
 ``run`` also returns, for every element written by a reduction or a
 transcendental, the error scale the tolerance test uses: the sum of absolute
 values of the terms for sums and dot products, ``|result|`` otherwise.
+
+Accumulation type.  ``acc="f64"`` (the default, and the oracle's definition)
+evaluates the tolerance-class ops as stated above.  ``acc="f32"`` evaluates
+the same formulas with fp32 accumulation instead (numpy float32 sums, float32
+BLAS products, float32 exp) and rounds the same way: a second implementation
+inside the same tolerance, which lets a test measure how far two correct
+evaluations of a long dependent chain drift apart through rounding alone.
+
+Weight matrices.  A GEMV widens its bf16 weight matrix to fp64 on every call.
+``run`` and ``local_check`` keep the widened matrix (and its absolute values,
+for the error scale) of a GEMV whose weights sit in a buffer that no op of
+the workload writes, and reuse it for every later GEMV over the same
+weights.  The arithmetic is unchanged: the cached arrays are exactly the ones
+the GEMV would compute again.
 """
 
 from __future__ import annotations
@@ -163,7 +177,14 @@ def _write(bufs: Dict[str, np.ndarray], ref: Ref, vals: np.ndarray) -> None:
 # elementwise values
 
 
-def _ew_values(k: str, dt: str, alpha: float, xr: np.ndarray, yr: Optional[np.ndarray]):
+def _acc_type(acc: str):
+    if acc not in ("f64", "f32"):
+        raise ValueError(f"accumulation type {acc!r}")
+    return np.float64 if acc == "f64" else np.float32
+
+
+def _ew_values(k: str, dt: str, alpha: float, xr: np.ndarray, yr: Optional[np.ndarray],
+               acc: str = "f64"):
     """Stored values of elementwise op ``k`` on raw operands xr (and yr), and
     the error scale (None for the exact class)."""
     if dt == "i32":
@@ -186,15 +207,17 @@ def _ew_values(k: str, dt: str, alpha: float, xr: np.ndarray, yr: Optional[np.nd
     elif k == "relu":
         r32 = np.where(x > np.float32(0.0), x, np.float32(0.0)).astype(np.float32)
     elif k == "exp":
+        F = _acc_type(acc)
         with np.errstate(over="ignore"):
-            r64 = np.exp(x.astype(np.float64))
-        return _store_from_f64(r64, dt), np.abs(r64)
+            r64 = np.exp(x.astype(F))
+        return _store_from_f64(r64, dt), np.abs(r64.astype(np.float64))
     else:  # silu_mul: g / (1 + exp(-g)) * u in fp64
-        g = x.astype(np.float64)
-        u = y.astype(np.float64)
+        F = _acc_type(acc)
+        g = x.astype(F)
+        u = y.astype(F)
         with np.errstate(over="ignore", invalid="ignore"):
-            r64 = g / (1.0 + np.exp(-g)) * u
-        return _store_from_f64(r64, dt), np.abs(r64)
+            r64 = g / (F(1.0) + np.exp(-g)) * u
+        return _store_from_f64(r64, dt), np.abs(r64.astype(np.float64))
     return _store_from_f32(r32.astype(np.float32), dt), None
 
 
@@ -329,15 +352,45 @@ def out_positions(op: Op) -> np.ndarray:
     return np.arange(op.out.off, op.out.off + out_len(op), dtype=np.int64)
 
 
-def apply_op(op: Op, bufs: Dict[str, np.ndarray], dtypes: Dict[str, str]) -> Optional[np.ndarray]:
+class WeightCache:
+    """Widened weight matrices of GEMVs over buffers that no op writes
+    (``frozen``): (buffer, offset, M, K) -> (W, |W|) in fp64."""
+
+    def __init__(self, frozen):
+        self.frozen = frozenset(frozen)
+        self.mats: Dict[tuple, Tuple[np.ndarray, np.ndarray]] = {}
+
+    @staticmethod
+    def for_workload(wl: Workload) -> "WeightCache":
+        written = {op.out.buf for op in wl.ops}
+        return WeightCache(set(wl.buffers) - written)
+
+
+def _gemv_weights(bufs: Dict[str, np.ndarray], ref: Ref, M: int, K: int,
+                  cache: Optional[WeightCache], acc: str = "f64") -> Tuple[np.ndarray, np.ndarray]:
+    key = (ref.buf, ref.off, M, K, acc)
+    if cache is not None and key in cache.mats:
+        return cache.mats[key]
+    W = bf16_to_f32(_read(bufs, ref, M * K)).astype(_acc_type(acc)).reshape(M, K)
+    absW = np.abs(W)
+    if cache is not None and ref.buf in cache.frozen:
+        cache.mats[key] = (W, absW)
+    return W, absW
+
+
+def apply_op(op: Op, bufs: Dict[str, np.ndarray], dtypes: Dict[str, str],
+             wcache: Optional[WeightCache] = None, acc: str = "f64") -> Optional[np.ndarray]:
     """Executes one op on ``bufs`` in place.
 
     Returns the error-scale array of the elements written (tolerance class),
-    or None for ops whose result is exact.
+    or None for ops whose result is exact.  ``wcache`` (optional) keeps the
+    widened weights of GEMVs over buffers no op writes; ``acc`` is the
+    accumulation type of the tolerance-class ops (see the module docstring).
     """
     k = op.kind
     dt = op.dtype
     n = op.n
+    F = _acc_type(acc)
     if k in ("nop", "spin"):
         return None
 
@@ -367,7 +420,7 @@ def apply_op(op: Op, bufs: Dict[str, np.ndarray], dtypes: Dict[str, str]) -> Opt
     if k in ("add", "mul", "scale", "relu", "exp", "silu_mul"):
         xr = _read_cyclic(bufs, op.ins[0], op.src_len[0], n)
         yr = _read_cyclic(bufs, op.ins[1], op.src_len[1], n) if k in ("add", "mul", "silu_mul") else None
-        vals, scale = _ew_values(k, dt, op.alpha, xr, yr)
+        vals, scale = _ew_values(k, dt, op.alpha, xr, yr, acc)
         _write(bufs, op.out, vals)
         return scale
 
@@ -375,25 +428,25 @@ def apply_op(op: Op, bufs: Dict[str, np.ndarray], dtypes: Dict[str, str]) -> Opt
         rows, L = op.rows, op.row_len
         if rows * L != n:
             raise OracleError("row op with n != rows * row_len")
-        x64 = _to_f32(_read_cyclic(bufs, op.ins[0], op.src_len[0], n), dt).astype(np.float64)
+        x64 = _to_f32(_read_cyclic(bufs, op.ins[0], op.src_len[0], n), dt).astype(F)
         x64 = x64.reshape(rows, L)
         if k == "row_sum":
             s = x64.sum(axis=1)
             _write(bufs, op.out, _store_from_f64(s, dt))
-            return np.abs(x64).sum(axis=1)
+            return np.abs(x64.astype(np.float64)).sum(axis=1)
         if k == "row_softmax":
             m = x64.max(axis=1, keepdims=True)  # NaN propagates through max
             with np.errstate(invalid="ignore", over="ignore"):
                 e = np.exp(x64 - m)
                 y = e / e.sum(axis=1, keepdims=True)
             _write(bufs, op.out, _store_from_f64(y.reshape(-1), dt))
-            return np.abs(y).reshape(-1)
-        g = _to_f32(_read(bufs, op.aux, L), dt).astype(np.float64)
-        ms = (x64 * x64).sum(axis=1) / L
-        inv = 1.0 / np.sqrt(ms + float(np.float32(op.eps)))
+            return np.abs(y.astype(np.float64)).reshape(-1)
+        g = _to_f32(_read(bufs, op.aux, L), dt).astype(F)
+        ms = (x64 * x64).sum(axis=1) / F(L)
+        inv = F(1.0) / np.sqrt(ms + F(np.float32(op.eps)))
         y = x64 * inv[:, None] * g[None, :]
         _write(bufs, op.out, _store_from_f64(y.reshape(-1), dt))
-        return np.abs(y).reshape(-1)
+        return np.abs(y.astype(np.float64)).reshape(-1)
 
     if k == "rope":
         heads, hd = op.rows, op.row_len
@@ -414,20 +467,20 @@ def apply_op(op: Op, bufs: Dict[str, np.ndarray], dtypes: Dict[str, str]) -> Opt
         M, K = op.dims[0], op.dims[1]
         if M != n:
             raise OracleError("gemv needs n == M")
-        W = bf16_to_f32(_read(bufs, op.aux, M * K)).astype(np.float64).reshape(M, K)
-        x = _to_f32(_read(bufs, op.ins[0], K), dt).astype(np.float64)
+        W, absW = _gemv_weights(bufs, op.aux, M, K, wcache, acc)
+        x = _to_f32(_read(bufs, op.ins[0], K), dt).astype(F)
         y = W @ x
         _write(bufs, op.out, _store_from_f64(y, dt))
-        return np.abs(W) @ np.abs(x)
+        return (absW @ np.abs(x)).astype(np.float64)
 
     if k == "attn_score":
         H, Dh, S = op.dims[0], op.dims[1], op.dims[2]
         if H * S != n:
             raise OracleError("attn_score needs n == H * S")
-        q = _to_f32(_read(bufs, op.ins[0], H * Dh), dt).astype(np.float64).reshape(H, Dh)
-        Kc = bf16_to_f32(_read(bufs, op.aux, S * H * Dh)).astype(np.float64).reshape(S, H, Dh)
-        a = float(np.float32(op.alpha))
-        sc = np.empty((H, S))
+        q = _to_f32(_read(bufs, op.ins[0], H * Dh), dt).astype(F).reshape(H, Dh)
+        Kc = bf16_to_f32(_read(bufs, op.aux, S * H * Dh)).astype(F).reshape(S, H, Dh)
+        a = F(np.float32(op.alpha))
+        sc = np.empty((H, S), F)
         scale = np.empty((H, S))
         for h in range(H):
             sc[h] = a * (Kc[:, h, :] @ q[h])
@@ -439,9 +492,9 @@ def apply_op(op: Op, bufs: Dict[str, np.ndarray], dtypes: Dict[str, str]) -> Opt
         H, Dh, S = op.dims[0], op.dims[1], op.dims[2]
         if H * Dh != n:
             raise OracleError("attn_av needs n == H * D")
-        p = _read(bufs, op.ins[0], H * S).astype(np.float64).reshape(H, S)
-        Vc = bf16_to_f32(_read(bufs, op.aux, S * H * Dh)).astype(np.float64).reshape(S, H, Dh)
-        o = np.empty((H, Dh))
+        p = _read(bufs, op.ins[0], H * S).astype(F).reshape(H, S)
+        Vc = bf16_to_f32(_read(bufs, op.aux, S * H * Dh)).astype(F).reshape(S, H, Dh)
+        o = np.empty((H, Dh), F)
         scale = np.empty((H, Dh))
         for h in range(H):
             o[h] = Vc[:, h, :].T @ p[h]
@@ -457,20 +510,27 @@ def apply_op(op: Op, bufs: Dict[str, np.ndarray], dtypes: Dict[str, str]) -> Opt
 
 
 def run(wl: Workload, upto: Optional[int] = None, scales: bool = False,
-        buffers: Optional[Dict[str, np.ndarray]] = None):
-    """Runs ops [0, upto) of the workload in submission order.
+        buffers: Optional[Dict[str, np.ndarray]] = None, start: int = 0,
+        wcache: Optional[WeightCache] = None, acc: str = "f64"):
+    """Runs ops [start, upto) of the workload in submission order, from the
+    workload's initial buffers or from ``buffers`` (the state after ops
+    [0, start), for a run taken in pieces).
 
     Returns the final buffers (copies; the workload is not modified).  With
     ``scales=True`` also returns ``{buffer: scale array or None}``: for every
     buffer, an fp64 array of error scales where the last writer of an element
-    was a tolerance-class op, NaN where it was an exact op or the initial
-    contents.
+    in the run was a tolerance-class op, NaN where it was an exact op or the
+    initial contents.  ``wcache`` (optional) carries widened weights from one
+    piece of a run to the next.  ``acc`` is the accumulation type of the
+    tolerance-class ops ("f64", the definition, or "f32"; see the module
+    docstring).
     """
     bufs = {k: v.copy() for k, v in (buffers or wl.buffers).items()}
     sc: Dict[str, np.ndarray] = {}
-    ops = wl.ops if upto is None else wl.ops[:upto]
+    ops = wl.ops[start:] if upto is None else wl.ops[start:upto]
+    cache = wcache if wcache is not None else WeightCache.for_workload(wl)
     for op in ops:
-        s = apply_op(op, bufs, wl.dtypes)
+        s = apply_op(op, bufs, wl.dtypes, cache, acc)
         if not scales or op.kind in ("nop", "spin"):
             continue
         name = op.out.buf
@@ -496,6 +556,7 @@ def local_check(wl: Workload, gpu: Dict[str, np.ndarray], compare_fn, only=None)
     """
     state = {k: v.copy() for k, v in wl.buffers.items()}
     bad = []
+    cache = WeightCache.for_workload(wl)
     for i, op in enumerate(wl.ops):
         if out_len(op) == 0:
             continue
@@ -503,7 +564,7 @@ def local_check(wl: Workload, gpu: Dict[str, np.ndarray], compare_fn, only=None)
         if only is not None and i not in only:
             state[name][pos] = gpu[name][pos]
             continue
-        s = apply_op(op, state, wl.dtypes)
+        s = apply_op(op, state, wl.dtypes, cache)
         want = state[name][pos].copy()
         got = gpu[name][pos]
         r = compare_fn(got, want, wl.dtypes[name], s)

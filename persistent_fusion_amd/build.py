@@ -10,14 +10,16 @@ import sys
 HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libgpuos.so")
-SOURCES = ["kernels.hip", "runtime.cpp"]
+# Each kernel is its own translation unit; the units compile in parallel and
+# are linked into one shared library.
+SOURCES = ["kernels.hip", "single_kernel.hip", "runtime.cpp"]
+OBJDIR = os.path.join(os.path.dirname(HERE), "_build")
 
 FLAGS = [
     "--offload-arch=gfx950",
     "-O3",
     "-std=c++17",
     "-fPIC",
-    "-shared",
     # exact-class ops must be single IEEE operations: no a*b+c contraction
     "-ffp-contract=off",
     # keep fp32 subnormals (no flush to zero)
@@ -55,19 +57,40 @@ def kernel_resources(stderr: str) -> dict:
     return res
 
 
-def build(verbose: bool = False) -> str:
-    tmp = LIB + ".tmp"
-    cmd = [hipcc(), *FLAGS, "-Rpass-analysis=kernel-resource-usage", "-o", tmp] + \
-        [os.path.join(CSRC, s) for s in SOURCES]
-    if verbose:
-        print(" ".join(cmd), flush=True)
-    r = subprocess.run(cmd, cwd=CSRC, capture_output=True, text=True)
-    errs = [l for l in r.stderr.splitlines()
+def _filter(stderr: str):
+    return [l for l in stderr.splitlines()
             if "packed-fp32-ops" not in l and "kernel-resource-usage" not in l and l.strip()
             and not l.strip().startswith(("|", "^")) and not l[:8].strip().isdigit()]
-    if r.returncode != 0:
+
+
+def build(verbose: bool = False, only=None) -> str:
+    """Compiles every source (or, with `only`, just those sources, linking
+    them with the objects already in _build/) and links libgpuos.so."""
+    os.makedirs(OBJDIR, exist_ok=True)
+    jobs = []
+    for src in SOURCES:
+        obj = os.path.join(OBJDIR, os.path.splitext(src)[0] + ".o")
+        if only is not None and src not in only:
+            if not os.path.exists(obj):
+                raise RuntimeError(f"{obj} is missing: build everything first")
+            jobs.append((src, obj, None))
+            continue
+        cmd = [hipcc(), *FLAGS, "-c", "-Rpass-analysis=kernel-resource-usage", "-o", obj,
+               os.path.join(CSRC, src)]
+        if verbose:
+            print(" ".join(cmd), flush=True)
+        jobs.append((src, obj, subprocess.Popen(cmd, cwd=CSRC, stdout=subprocess.PIPE,
+                                                stderr=subprocess.PIPE, text=True)))
+    res, errs = {}, []
+    for src, obj, p in jobs:
+        if p is None:
+            continue
+        _, err = p.communicate()
+        if p.returncode != 0:
+            errs.append(f"{src}:\n" + "\n".join(_filter(err)))
+        res.update(kernel_resources(err))
+    if errs:
         raise RuntimeError("hipcc failed:\n" + "\n".join(errs))
-    res = kernel_resources(r.stderr)
     for name, k in res.items():
         if "gpuos_resident" not in name and "gpuos_single" not in name:
             continue
@@ -80,6 +103,12 @@ def build(verbose: bool = False) -> str:
             raise RuntimeError(f"{name}: {k.get('VGPRs')} VGPRs, {waves} waves/SIMD, "
                                f"{scratch} B scratch: below {MIN_WAVES_PER_SIMD} waves/SIMD "
                                "or using scratch")
+    tmp = LIB + ".tmp"
+    link = [hipcc(), "--offload-arch=gfx950", "-shared", "-fPIC", "-o", tmp] + \
+        [obj for _, obj, _ in jobs]
+    r = subprocess.run(link, cwd=CSRC, capture_output=True, text=True)
+    if r.returncode != 0:
+        raise RuntimeError("link failed:\n" + r.stderr)
     os.replace(tmp, LIB)
     return LIB
 

@@ -70,12 +70,45 @@ __device__ __forceinline__ uint32_t f2bf(float f) {
 }
 
 // ---------------------------------------------------------------------------
-// Wave reductions (butterfly over all 64 lanes; every lane gets the result).
+// Wave reductions with DPP.  Within a row of 16 lanes, four DPP steps
+// combine each lane with a partner (quad_perm [1,0,3,2], then [2,3,0,1], then
+// row_half_mirror, then row_mirror); every combine pairs lanes symmetrically,
+// so all 16 lanes of a row end with the same value.  The four row values are
+// then read into scalar registers (v_readlane) and combined as
+// (r0 + r1) + (r2 + r3), so the wave-wide result is uniform.  DPP moves data
+// between lanes inside the VALU instruction, without the LDS crossbar a
+// ds_bpermute shuffle takes.  Every lane of the wave must be active.
+
+template <int CTRL>
+__device__ __forceinline__ float dpp_f(float v) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, 0xF, 0xF, false));
+}
+enum : int {
+  DPP_QUAD_1032 = 0xB1,     // quad_perm [1,0,3,2]: lane i <-> i ^ 1
+  DPP_QUAD_2301 = 0x4E,     // quad_perm [2,3,0,1]: lane i <-> i ^ 2
+  DPP_ROW_HALF_MIRROR = 0x141,  // lane i <-> 7 - i within each 8 lanes
+  DPP_ROW_MIRROR = 0x140,   // lane i <-> 15 - i within each 16 lanes
+};
+
+__device__ __forceinline__ float lane_f(float v, int l) {
+  return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), l));
+}
+
+// Sum over aligned groups of G lanes (G a power of two, 2..16): every lane
+// receives its group's sum.
+template <int G>
+__device__ __forceinline__ float row_group_sum(float v) {
+  static_assert(G >= 2 && G <= 16 && (G & (G - 1)) == 0, "groups of 2..16 lanes");
+  v += dpp_f<DPP_QUAD_1032>(v);
+  if constexpr (G >= 4) v += dpp_f<DPP_QUAD_2301>(v);
+  if constexpr (G >= 8) v += dpp_f<DPP_ROW_HALF_MIRROR>(v);
+  if constexpr (G >= 16) v += dpp_f<DPP_ROW_MIRROR>(v);
+  return v;
+}
 
 __device__ __forceinline__ float wave_sum(float v) {
-#pragma unroll
-  for (int m = 32; m >= 1; m >>= 1) v += __shfl_xor(v, m, 64);
-  return v;
+  v = row_group_sum<16>(v);
+  return (lane_f(v, 0) + lane_f(v, 16)) + (lane_f(v, 32) + lane_f(v, 48));
 }
 
 __device__ __forceinline__ float nan_max(float a, float b) {
@@ -84,18 +117,30 @@ __device__ __forceinline__ float nan_max(float a, float b) {
   return a > b ? a : b;
 }
 
+// NaN-propagating maximum over the wave, uniform in every lane.
 __device__ __forceinline__ float wave_max_nan(float v) {
-#pragma unroll
-  for (int m = 32; m >= 1; m >>= 1) v = nan_max(v, __shfl_xor(v, m, 64));
-  return v;
+  v = nan_max(v, dpp_f<DPP_QUAD_1032>(v));
+  v = nan_max(v, dpp_f<DPP_QUAD_2301>(v));
+  v = nan_max(v, dpp_f<DPP_ROW_HALF_MIRROR>(v));
+  v = nan_max(v, dpp_f<DPP_ROW_MIRROR>(v));
+  return nan_max(nan_max(lane_f(v, 0), lane_f(v, 16)), nan_max(lane_f(v, 32), lane_f(v, 48)));
 }
 
-// Sum over aligned groups of G consecutive lanes (G a power of two <= 64).
+// Sum over aligned groups of G consecutive lanes (G a power of two <= 64);
+// every lane receives its group's sum.
 template <int G>
 __device__ __forceinline__ float group_sum(float v) {
-#pragma unroll
-  for (int m = G / 2; m >= 1; m >>= 1) v += __shfl_xor(v, m, 64);
-  return v;
+  if constexpr (G == 1) {
+    return v;
+  } else if constexpr (G <= 16) {
+    return row_group_sum<G>(v);
+  } else if constexpr (G == 32) {
+    v = row_group_sum<16>(v);
+    const float lo = lane_f(v, 0) + lane_f(v, 16), hi = lane_f(v, 32) + lane_f(v, 48);
+    return lane_id() < 32 ? lo : hi;
+  } else {
+    return wave_sum(v);
+  }
 }
 
 __device__ __forceinline__ bool aligned16(uint64_t p) { return (p & 15u) == 0; }

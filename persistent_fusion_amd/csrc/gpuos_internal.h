@@ -235,7 +235,15 @@ struct alignas(256) AvailLine {
 struct alignas(256) DevCtl {
   DevRing ring[kRings];
   AvailLine avail[kRings][kReplicas];
+  uint64_t arrived;     // waves that have started, summed over all launches:
+                        // launch e of a grid of W waves is complete at e * W
+  uint64_t _pa[31];
+  // debug options (read only when KArgs::debug is nonzero)
+  uint32_t* tile_exec[kRings];  // executions of ticket i of each ring, i < n
+  uint64_t tile_exec_n;
+  uint64_t _pd[29];
 };
+constexpr uint32_t kDebugCount = 1u;
 
 // Host-visible control block (pinned host memory, fine-grained).
 struct alignas(256) HostCtl {
@@ -250,7 +258,9 @@ struct alignas(256) HostCtl {
                               // after idling (0 = cancelled); between this
                               // store and the exit, the doorbell re-reads
                               // the tails and cancels if any moved
-  uint64_t _p1[26];
+  uint64_t resident_epoch;    // device: epoch of the last launch whose waves
+                              // have all started (before any work is taken)
+  uint64_t _p1[25];
   uint64_t stop_req;          // host: nonzero asks the kernel to exit once
                               // every published descriptor has retired
   uint64_t error;             // device: first error code (0 = none)
@@ -300,7 +310,9 @@ struct KArgs {
   uint32_t lc_waves;              // waves reserved for the latency-critical
                                   // ring (0 = no priority ring)
   uint32_t epoch;                 // launch number of this context, from 1
-  uint32_t _pad;
+  uint32_t debug;                 // 0, or the debug options of DevCtl::dbg
+                                  // (bit 0: count tile executions; bits
+                                  // 16-31: jitter steps)
   uint64_t ticket_base;           // ring-0 tickets below this ran in earlier
                                   // launches
   uint64_t idle_exit_ticks;       // exit after this long (100 MHz ticks) with

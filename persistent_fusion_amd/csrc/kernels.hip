@@ -1,4 +1,6 @@
-// Resident scheduler kernel and per-op comparator kernel (gfx950).
+// Resident scheduler kernel (gfx950).  The per-op comparator kernel is in
+// single_kernel.hip: each kernel is its own translation unit so that the two
+// large, fully inlined kernels compile in parallel.
 //
 // The resident kernel is the persistent worker of "GPUOS: A GPU Operating
 // System Primitive for Transparent Operation Fusion" (section "The Paper"):
@@ -208,11 +210,17 @@ __device__ __forceinline__ void wait_deps(const KArgs& a, const Cached& c) {
 // device-coherent write-through stores, so waiting for their acknowledgement
 // makes them visible on every XCD before the count moves (no L2 writeback).
 template <int RING>
-__device__ __forceinline__ void finish_tile(const KArgs& a, const Cached& c, uint32_t tile) {
+__device__ __forceinline__ void finish_tile(const KArgs& a, const Cached& c, uint32_t tile,
+                                            uint64_t ticket) {
   const uint32_t slot = slot_of(c.seq, a.cap_mask);
   const uint32_t cap = a.cap_mask + 1;
   const SDesc d = c.desc();
   const uint32_t ntiles = d(6);
+  if ((a.debug & kDebugCount) && lane_id() == 0) {
+    uint32_t* cnt = a.dctl->tile_exec[RING];
+    if (ticket < a.dctl->tile_exec_n)
+      __hip_atomic_fetch_add(&cnt[ticket], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  }
   if constexpr (kReleaseWriteback) fence_rel_agent();
   wait_mem();
   if (lane_id() != 0) return;
@@ -256,10 +264,23 @@ __device__ __forceinline__ void finish_tile(const KArgs& a, const Cached& c, uin
   }
 }
 
+// Debug schedule jitter: waits a pseudo-random 0..max steps of s_sleep 4
+// (256 clocks, about 0.1 us), the count drawn from a hash of the ticket
+// (splitmix64 finaliser), so that tiles start and finish in another order.
+__device__ __forceinline__ void jitter_wait(uint64_t ticket, uint32_t max) {
+  uint64_t h = ticket + 0x9E3779B97F4A7C15ull;
+  h = (h ^ (h >> 30)) * 0xBF58476D1CE4E5B9ull;
+  h = (h ^ (h >> 27)) * 0x94D049BB133111EBull;
+  h ^= h >> 31;
+  const uint32_t n = (uint32_t)(h % ((uint64_t)max + 1));
+  for (uint32_t i = 0; i < n; ++i) __builtin_amdgcn_s_sleep(4);
+}
+
 template <int RING>
 __device__ __forceinline__ void run_ticket(const KArgs& a, uint64_t ticket, Cached& c) {
   const uint32_t tile = (uint32_t)(ticket - c.start);
   const SDesc d = c.desc();
+  if (a.debug >> 16) jitter_wait(ticket, a.debug >> 16);
   auto claimed = [&]() {
     if (a.trace[RING] && tile == 0 && lane_id() == 0)
       st_rlx_agent(&a.trace[RING][slot_of(c.seq, a.cap_mask)].t_claim, now_ticks());
@@ -288,7 +309,7 @@ __device__ __forceinline__ void run_ticket(const KArgs& a, uint64_t ticket, Cach
         gemv_tile<GPUOS_F32, kResidentLoadCP, kResidentStoreCP>(d, tile, ready, true);
       else
         report_error(a, RING, c.seq, DERR_BAD_OPCODE);
-      finish_tile<RING>(a, c, tile);
+      finish_tile<RING>(a, c, tile, ticket);
       return;
     }
     wait_deps<RING>(a, c);
@@ -297,7 +318,7 @@ __device__ __forceinline__ void run_ticket(const KArgs& a, uint64_t ticket, Cach
   claimed();
   const uint32_t err = exec_tile<kResidentLoadCP, kResidentStoreCP>(d, tile, c.scr);
   if (err) report_error(a, RING, c.seq, err);
-  finish_tile<RING>(a, c, tile);
+  finish_tile<RING>(a, c, tile, ticket);
 }
 
 // Maps a runnable ticket to its descriptor (refreshing the cache if needed).
@@ -562,7 +583,37 @@ __device__ __forceinline__ void release_workers(const KArgs& a, uint64_t tiles0)
   wait_mem();
 }
 
+// Co-residency check: every wave of the grid counts itself in at start, and
+// the doorbell wave publishes no work before the whole grid has arrived.  A
+// worker only ever waits for tiles with smaller tickets, which resident waves
+// hold, so once every wave is resident each wait ends; a grid that cannot be
+// resident at once (another kernel holding compute units) takes no work, and
+// the host sees no resident_epoch for this launch.  A stop request ends the
+// wait.  Returns false when stopped before the grid was complete.
+__device__ __forceinline__ bool await_grid(const KArgs& a) {
+  const uint64_t want = (uint64_t)a.epoch * gridDim.x * 4u;
+  for (;;) {
+    uint64_t got = 0, stop = 0;
+    if (lane_id() == 0) {
+      got = ld_rlx_agent(&a.dctl->arrived);
+      stop = ld_rlx_sys(&a.hctl->stop_req);
+    }
+    if (bcast64(got) >= want) break;
+    if (bcast64(stop)) return false;
+    __builtin_amdgcn_s_sleep(8);
+  }
+  if (lane_id() == 0) st_rel_sys(&a.hctl->resident_epoch, (uint64_t)a.epoch);
+  return true;
+}
+
 __device__ __forceinline__ void doorbell_loop(const KArgs& a) {
+  if (!await_grid(a)) {
+    // stopped before the grid was resident: release whatever waves run
+    uint64_t t0 = 0;
+    if (lane_id() == 0) t0 = ld_rlx_agent(&a.dctl->avail[0][0].avail_tiles);
+    release_workers(a, bcast64(t0));
+    return;
+  }
   // resume from what earlier launches published and retired
   uint64_t avail0 = 0, avail1 = 0, ret0 = 0, ret1 = 0, tiles0 = 0, tiles1 = 0, cp0 = 0, cp1 = 0;
   if (lane_id() == 0) {
@@ -644,7 +695,8 @@ __device__ __forceinline__ void doorbell_loop(const KArgs& a) {
   }
 }
 
-__global__ __launch_bounds__(256) void gpuos_resident(KArgs a) {
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2)))
+void gpuos_resident(KArgs a) {
   // one descriptor slot per wave and ring, and each wave's tile scratch
   __shared__ uint32_t sdesc[4][2][64];
   __shared__ float sscr[4][kWaveScratch];
@@ -655,6 +707,8 @@ __global__ __launch_bounds__(256) void gpuos_resident(KArgs a) {
   // up to 8) serve the latency-critical ring; the rest run best-effort tiles.
   const uint32_t wib = threadIdx.x / 64;
   const uint32_t num = wib * gridDim.x + blockIdx.x;
+  if (lane_id() == 0)
+    __hip_atomic_fetch_add(&a.dctl->arrived, (uint64_t)1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   if (num == 0)
     doorbell_loop(a);
   else if (num - 1 < a.lc_waves)
@@ -663,38 +717,8 @@ __global__ __launch_bounds__(256) void gpuos_resident(KArgs a) {
     worker_loop(a, num - 1 - a.lc_waves, (lds_u32*)&sdesc[wib][0][0], (lds_f32*)&sscr[wib][0]);
 }
 
-// ---------------------------------------------------------------------------
-// per-op comparator: one launch per descriptor, every wave runs tiles
-// wave, wave + waves, ... of that descriptor.
-
-__global__ __launch_bounds__(256) void gpuos_single(DevDesc d, uint32_t* err) {
-  const uint32_t wave = (blockIdx.x * blockDim.x + threadIdx.x) / 64;
-  const uint32_t waves = gridDim.x * blockDim.x / 64;
-  // the descriptor goes to this wave's LDS slot, as in the resident kernel
-  __shared__ uint32_t sdesc[4][64];
-  __shared__ float sscr[4][kWaveScratch];
-  lds_u32* slot = (lds_u32*)&sdesc[threadIdx.x / 64][0];
-  lds_f32* scr = (lds_f32*)&sscr[threadIdx.x / 64][0];
-  slot[lane_id()] = reinterpret_cast<const uint32_t*>(&d)[lane_id()];
-  const SDesc v{slot};
-  const uint32_t ntiles = v(6);
-  for (uint32_t t = wave; t < ntiles; t += waves) {
-    const uint32_t e = exec_tile<CP_DEFAULT, CP_DEFAULT>(v, t, scr);
-    if (e && lane_id() == 0 && err) *err = e;
-  }
-}
-
 hipError_t launch_resident(const KArgs& a, uint32_t blocks, hipStream_t s) {
   hipLaunchKernelGGL(gpuos_resident, dim3(blocks), dim3(256), 0, s, a);
-  return hipGetLastError();
-}
-
-hipError_t launch_single(const DevDesc& d, uint32_t* err, hipStream_t s) {
-  uint32_t waves = d.ntiles;
-  uint32_t blocks = (waves + 3) / 4;
-  if (blocks > 16384) blocks = 16384;
-  if (blocks == 0) blocks = 1;
-  hipLaunchKernelGGL(gpuos_single, dim3(blocks), dim3(256), 0, s, d, err);
   return hipGetLastError();
 }
 

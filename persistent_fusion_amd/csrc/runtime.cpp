@@ -749,6 +749,7 @@ struct gpuos_ctx {
   uint32_t* tiles_done[kRings] = {nullptr, nullptr};
   uint32_t* subs_done[kRings] = {nullptr, nullptr};
   TraceRec* trace[kRings] = {nullptr, nullptr};
+  uint32_t* tile_exec[kRings] = {nullptr, nullptr};
 
   // host bookkeeping
   uint64_t next_id = 1;
@@ -1636,6 +1637,33 @@ int wait_kernel_end(gpuos_ctx* c, int64_t timeout_ns) {
   }
 }
 
+// Waits until every wave of the launch just made has started (the doorbell
+// wave publishes resident_epoch once the grid has checked in).  If that does
+// not happen within 10 s, the kernel is told to stop (it leaves without
+// taking work) and the context fails.
+int wait_resident(gpuos_ctx* c) {
+  const auto t0 = std::chrono::steady_clock::now();
+  while (load_acq(&c->hctl->resident_epoch) != c->epoch) {
+    const hipError_t e = hipStreamQuery(c->stream);
+    if (e != hipErrorNotReady) {
+      c->poisoned = true;
+      c->exited = true;
+      return fail(GPUOS_EDEVICE, "resident kernel ended before its grid was resident: %s",
+                  hipGetErrorString(e));
+    }
+    if (std::chrono::steady_clock::now() - t0 > std::chrono::seconds(10)) {
+      c->poisoned = true;
+      store_rel(&c->hctl->stop_req, 1);
+      if (wait_kernel_end(c, 2ll * 1000 * 1000 * 1000) == 0) c->exited = true;
+      else c->leaked = true;  // still running: its memory must not be freed
+      return fail(GPUOS_EDEVICE, "the resident grid of %u waves did not become resident within 10 s "
+                  "(another kernel may hold compute units)", c->blocks * 4);
+    }
+    std::this_thread::sleep_for(std::chrono::microseconds(20));
+  }
+  return 0;
+}
+
 // Called from every host wait and after every flush: if the kernel has left
 // after an idle period, waits for its launch to end and launches it again.
 // A kernel that ended without announcing an exit has failed.
@@ -1839,6 +1867,7 @@ void free_all(gpuos_ctx* c) {
       (void)hipFree(c->tiles_done[r]);
       (void)hipFree(c->subs_done[r]);
       (void)hipFree(c->trace[r]);
+      (void)hipFree(c->tile_exec[r]);
     }
     if (c->ev_start) (void)hipEventDestroy(c->ev_start);
     if (c->ev_end) (void)hipEventDestroy(c->ev_end);
@@ -1868,6 +1897,10 @@ int apply_config(const gpuos_config* in, gpuos_config& out) {
   if (in->idle_exit_ms) out.idle_exit_ms = in->idle_exit_ms;
   if (in->stream_min_kib) out.stream_min_kib = in->stream_min_kib;
   if (in->lc_waves) out.lc_waves = in->lc_waves;
+  out.tile_counts = in->tile_counts;
+  out.jitter = in->jitter;
+  if (in->reserved) return fail(GPUOS_EINVAL, "reserved config field must be 0");
+  if (out.jitter > 1000) return fail(GPUOS_EINVAL, "jitter must be at most 1000");
   const uint32_t rs = out.ring_slots;
   if (rs < 64 || rs > (1u << 18) || (rs & (rs - 1)))
     return fail(GPUOS_EINVAL, "ring_slots must be a power of two in [64, 2^18]");
@@ -2040,17 +2073,21 @@ int gpuos_create(int device, const gpuos_config* cfg_in, gpuos_ctx** out) {
       if (!rc) rc = dalloc((void**)&c->tiles_done[r], (size_t)kSubCounters * c->cap * sizeof(uint32_t));
       if (!rc) rc = dalloc((void**)&c->subs_done[r], (size_t)c->cap * sizeof(uint32_t));
       if (!rc && cfg.trace == 1) rc = dalloc((void**)&c->trace[r], (size_t)c->cap * sizeof(TraceRec));
+      if (!rc && cfg.tile_counts) rc = dalloc((void**)&c->tile_exec[r], (size_t)cfg.tile_counts * 4);
     }
     hipError_t e = hipSuccess;
     if (!rc) e = hipStreamCreateWithFlags(&c->stream, hipStreamNonBlocking);
     if (!rc && e == hipSuccess) {
       // control block: zeros, except that no wave may stop yet
-      auto* img = new DevCtl();
+      static_assert(sizeof(DevCtl) <= 16384, "control block image fits the stack");
+      DevCtl img_storage;
+      DevCtl* img = &img_storage;
       memset(img, 0, sizeof *img);
       for (int r = 0; r < kRings; ++r)
         for (uint32_t k = 0; k < kReplicas; ++k) img->avail[r][k].stop_ticket = ~0ull;  // epoch 0
+      for (int r = 0; r < kRings; ++r) img->tile_exec[r] = c->tile_exec[r];
+      img->tile_exec_n = cfg.tile_counts;
       e = hipMemcpy(c->dctl, img, sizeof(DevCtl), hipMemcpyHostToDevice);
-      delete img;
       for (int r = 0; r < kRings && e == hipSuccess; ++r) {
         e = hipMemsetAsync(c->dends[r], 0, (size_t)2 * c->cap * sizeof(uint64_t), c->stream);
         if (e == hipSuccess) e = hipMemsetAsync(c->ddesc[r], 0, (size_t)c->cap * sizeof(DevDesc), c->stream);
@@ -2061,6 +2098,8 @@ int gpuos_create(int device, const gpuos_config* cfg_in, gpuos_ctx** out) {
         if (e == hipSuccess) e = hipMemsetAsync(c->subs_done[r], 0, (size_t)c->cap * 4, c->stream);
         if (e == hipSuccess && c->trace[r])
           e = hipMemsetAsync(c->trace[r], 0, (size_t)c->cap * sizeof(TraceRec), c->stream);
+        if (e == hipSuccess && c->tile_exec[r])
+          e = hipMemsetAsync(c->tile_exec[r], 0, (size_t)cfg.tile_counts * 4, c->stream);
       }
     }
     if (!rc && e == hipSuccess) {
@@ -2075,6 +2114,7 @@ int gpuos_create(int device, const gpuos_config* cfg_in, gpuos_ctx** out) {
         a.subs_done[r] = c->subs_done[r];
         a.trace[r] = c->trace[r];
       }
+      a.debug = (cfg.tile_counts ? kDebugCount : 0u) | (cfg.jitter << 16);
       a.hctl = (HostCtl*)dev_ptr(c->hctl);
       a.dctl = c->dctl;
       a.cap_mask = c->cap - 1;
@@ -2086,9 +2126,11 @@ int gpuos_create(int device, const gpuos_config* cfg_in, gpuos_ctx** out) {
       e = hipEventCreate(&c->ev_start);
       if (e == hipSuccess) e = hipEventCreate(&c->ev_end);
       if (e == hipSuccess) rc = launch_kernel(c, 0);
+      if (!rc && e == hipSuccess) rc = wait_resident(c);
     }
     if (!rc && e != hipSuccess) rc = fail(GPUOS_EDEVICE, "create: %s", hipGetErrorString(e));
     if (rc) {
+      if (c->leaked) return rc;  // the kernel still runs on this memory
       if (c->stream) (void)hipStreamSynchronize(c->stream);
       free_all(c);
       delete c;
@@ -2547,6 +2589,19 @@ int gpuos_debug_seq_of(gpuos_ctx* c, uint64_t id, int* ring_out, uint64_t* seq_o
   if (!v) return fail(GPUOS_EAGAIN, "id still staged");
   *ring_out = (int)(v >> 63);
   *seq_out = v & ((1ull << 63) - 1);
+  return 0;
+}
+
+int gpuos_debug_tile_counts(gpuos_ctx* c, int ring, uint32_t* out, uint32_t n) {
+  if (!c || !out || ring < 0 || ring >= kRings) return fail(GPUOS_EINVAL, "bad argument");
+  if (c->host_only || !c->tile_exec[ring]) return fail(GPUOS_ESTATE, "tile counting is off");
+  if (n > c->cfg.tile_counts) return fail(GPUOS_EINVAL, "n above config.tile_counts");
+  hipStream_t s = nullptr;
+  hipError_t e = hipStreamCreateWithFlags(&s, hipStreamNonBlocking);
+  if (e == hipSuccess) e = hipMemcpyAsync(out, c->tile_exec[ring], (size_t)n * 4, hipMemcpyDeviceToHost, s);
+  if (e == hipSuccess) e = hipStreamSynchronize(s);
+  if (s) (void)hipStreamDestroy(s);
+  if (e != hipSuccess) return fail(GPUOS_EDEVICE, "tile count copy: %s", hipGetErrorString(e));
   return 0;
 }
 

@@ -14,7 +14,7 @@ from typing import Callable, Dict, Iterable, List, Optional, Sequence
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libgpuos.so")
-ABI_VERSION = 3  # GPUOS_ABI_VERSION of the header this binding follows
+ABI_VERSION = 4  # GPUOS_ABI_VERSION of the header this binding follows
 
 # status codes
 OK, EINVAL, ENOMEM, EAGAIN, ETIMEDOUT, EDEVICE, ESTATE = 0, -1, -2, -3, -4, -5, -6
@@ -53,7 +53,7 @@ class GpuosConfig(C.Structure):
     _fields_ = [(name, C.c_uint32) for name in (
         "ring_slots", "waves_per_cu", "tile_elems", "be_tile_elems", "fusion", "auto_deps",
         "trace", "block_on_full", "max_fuse", "priority", "idle_exit_ms", "stream_min_kib",
-        "lc_waves")] + [("reserved", C.c_uint32 * 3)]
+        "lc_waves", "tile_counts", "jitter", "reserved")]
 
 
 class GpuosStats(C.Structure):
@@ -101,6 +101,7 @@ EXPORTS = (
     "gpuos_graph_create", "gpuos_graph_launch", "gpuos_graph_destroy", "gpuos_yield",
     "gpuos_program_define", "gpuos_program_update",
     "gpuos_debug_read_desc", "gpuos_debug_published", "gpuos_debug_seq_of", "gpuos_debug_retire",
+    "gpuos_debug_tile_counts",
 )
 
 _lib = None
@@ -141,6 +142,7 @@ def lib() -> C.CDLL:
         "gpuos_debug_published": (C.c_uint64, [P, C.c_int]),
         "gpuos_debug_seq_of": (C.c_int, [P, C.c_uint64, C.POINTER(C.c_int), C.POINTER(C.c_uint64)]),
         "gpuos_debug_retire": (C.c_int, [P, C.c_int, C.c_uint64]),
+        "gpuos_debug_tile_counts": (C.c_int, [P, C.c_int, C.POINTER(C.c_uint32), C.c_uint32]),
     }
     for name, (res, args) in sig.items():
         fn = getattr(L, name)
@@ -288,6 +290,7 @@ def encode_views(ops, start: int, end: int):
     return arr
 
 
+
 class Context:
     """One resident-kernel context (``gpuos_create`` ... ``gpuos_destroy``)."""
 
@@ -350,6 +353,21 @@ class Context:
 
     def retire(self, ring: int, upto: int) -> None:
         _check(self._lib.gpuos_debug_retire(self.handle, ring, upto), "gpuos_debug_retire")
+
+    def tile_counts(self, ring: int, n: int) -> List[int]:
+        """gpuos_debug_tile_counts: executions of tickets [0, n) of `ring`."""
+        buf = (C.c_uint32 * max(n, 1))()
+        _check(self._lib.gpuos_debug_tile_counts(self.handle, ring, buf, n), "gpuos_debug_tile_counts")
+        return list(buf[:n])
+
+    def tickets(self, ring: int = 0) -> int:
+        """Tickets (tiles) published to `ring` so far: the first ticket after
+        its last published descriptor."""
+        last = self.published(ring)
+        if not last:
+            return 0
+        d = decode_desc(self.read_desc(ring, last))
+        return d["tstart"] + d["ntiles"]
 
     def program_define(self, prog: GpuosProgram) -> int:
         """gpuos_program_define: returns the program id (aux[0] of PROGRAM ops)."""

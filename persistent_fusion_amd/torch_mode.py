@@ -199,10 +199,50 @@ def _squeeze(shape: Sequence[int], strides: Sequence[Sequence[int]]):
     return [shape[d] for d in keep], [[st[d] for d in keep] for st in strides]
 
 
+def _dense_strides(shape, strides) -> bool:
+    """Whether a tensor of ``shape`` with element ``strides`` addresses a
+    dense block of prod(shape) elements, each once (a permuted contiguous
+    layout)."""
+    dims = sorted((st, e) for st, e in zip(strides, shape) if e != 1)
+    acc = 1
+    for st, e in dims:
+        if st != acc:
+            return False
+        acc *= e
+    return True
+
+
+def eager_out_strides(func, args, kwargs, device):
+    """The strides PyTorch itself gives the output of an out-of-place call:
+    the same call on meta tensors (same shapes, strides and dtypes as the
+    arguments on ``device``), which runs PyTorch's own layout rule and touches
+    no element.  None if the call fails on meta tensors or its output is not
+    a dense permuted layout."""
+    import torch
+    from torch.utils._pytree import tree_map
+
+    def meta(a):
+        if isinstance(a, torch.Tensor) and a.device == device:
+            return torch.empty_strided(a.shape, a.stride(), dtype=a.dtype, device="meta")
+        return a
+
+    try:
+        r = func(*tree_map(meta, tuple(args)), **tree_map(meta, dict(kwargs or {})))
+    except Exception:  # an argument combination the meta kernels refuse
+        return None
+    if not isinstance(r, torch.Tensor) or not _dense_strides(r.shape, r.stride()):
+        return None
+    return tuple(r.stride())
+
+
 def plan_op(func, args, kwargs, device):
     """How an aten call on tensors of ``device`` (a torch.device) would be
     queued: None if it is not interceptable, else (kind, dtype name, alpha,
-    out shape, in-place, inputs, view shape, view strides [out, in0, in1]).
+    out shape, in-place, inputs, view shape, view strides [out, in0, in1],
+    full-rank output strides).
+    An out-of-place op's output gets the strides PyTorch would give it
+    (:func:`eager_out_strides`): a dense input's layout is kept, as eager
+    PyTorch keeps it, so later view ops behave the same in the mode.
     Pure metadata: no GPU work."""
     import torch
 
@@ -213,12 +253,8 @@ def plan_op(func, args, kwargs, device):
     kwargs = kwargs or {}
     if kind == "add" and kwargs.get("alpha", 1) != 1:
         return None
-    # the output is contiguous: that is clone's result under contiguous_format,
-    # and under preserve_format only for a contiguous input (PyTorch keeps a
-    # strided input's layout there)
     fmt = kwargs.get("memory_format", None)
-    if kind == "copy" and (fmt not in (None, torch.preserve_format, torch.contiguous_format) or
-                           (fmt != torch.contiguous_format and not args[0].is_contiguous())):
+    if kind == "copy" and fmt not in (None, torch.preserve_format, torch.contiguous_format):
         return None
     extra = set(kwargs) - {"alpha", "memory_format"}
     if extra:
@@ -272,15 +308,13 @@ def plan_op(func, args, kwargs, device):
     if inplace and tuple(tens[0].shape) != shape:
         return None
     # strides of each operand over the output's index space (0 = broadcast)
-    out_strides = []
     if inplace:
         out_strides = list(tens[0].stride())
     else:
-        acc = 1
-        for e in reversed(shape):
-            out_strides.append(acc)
-            acc *= e
-        out_strides.reverse()
+        st = eager_out_strides(func, args, kwargs, dev)
+        if st is None or len(st) != len(shape):
+            return None
+        out_strides = list(st)
     ins = [_strides_over(t, shape) for t in tens]
     if any(s < 0 for st in [out_strides] + ins for s in st):
         return None
@@ -301,7 +335,7 @@ def plan_op(func, args, kwargs, device):
         return None
     if not vshape:  # a single element
         vshape, vstr = [1], [[1], [1 if len(tens) > 0 else 0], [1 if len(tens) > 1 else 0]]
-    return kind, dt, alpha, shape, inplace, tens, vshape, vstr
+    return kind, dt, alpha, shape, inplace, tens, vshape, vstr, tuple(out_strides)
 
 
 class GpuosMode:
@@ -348,7 +382,7 @@ class GpuosMode:
                        torch.float16: gpuos.DTYPES["f16"], torch.int32: gpuos.DTYPES["i32"]}
         self._i32 = torch.int32
         self._empty_like = torch.empty_like
-        self._empty = torch.empty
+        self._empty_strided = torch.empty_strided
         self._tensor = torch.Tensor
         self.stats = {"queued": 0, "programs": 0, "metadata": 0, "host_ops": 0, "passed_through": 0,
                       "syncs": 0}
@@ -483,10 +517,11 @@ class GpuosMode:
             self.stats["passed_through"] += 1
             self._torch_dirty = True
             return func(*args, **(kwargs or {}))
-        kind, dt, alpha, shape, inplace, tens, vshape, vstr = plan
+        kind, dt, alpha, shape, inplace, tens, vshape, vstr, ostr = plan
         if self._torch_dirty:
             self._sync_torch()
-        out = tens[0] if inplace else self._empty(shape, dtype=tens[0].dtype, device=tens[0].device)
+        out = tens[0] if inplace else self._empty_strided(shape, ostr, dtype=tens[0].dtype,
+                                                           device=tens[0].device)
         self._queue(kind, gpuos.DTYPES[dt], alpha, out, tens, vshape, vstr)
         self.stats["queued"] += 1
         return out

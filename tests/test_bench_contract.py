@@ -15,19 +15,48 @@ sys.path.insert(0, ROOT)
 import bench  # noqa: E402
 
 
-def test_traffic_is_reported_for_the_profiled_kernel_only(tmp_path, monkeypatch):
-    per_launch = bench.traffic_per_launch(1500)
-    assert isinstance(per_launch, int) and per_launch > 1500 * 268_435_456  # at least the algorithmic bytes
-    # the same profile against different kernel sources: no traffic
+def _fake_tree(tmp_path, sha, per_pass="268563935"):
+    """A tree holding the kernel sources and a traffic profile that records
+    the kernel-source hash `sha`."""
     fake = tmp_path / "persistent_fusion_amd" / "csrc"
     fake.mkdir(parents=True)
     for name in bench.KERNEL_SOURCES:
         shutil.copy(os.path.join(ROOT, "persistent_fusion_amd", "csrc", name), fake / name)
-    (fake / bench.KERNEL_SOURCES[0]).write_text((fake / bench.KERNEL_SOURCES[0]).read_text() + "\n// edited\n")
     (tmp_path / "profiles").mkdir()
-    shutil.copy(os.path.join(ROOT, "profiles", "gpuos_resident_fused_chain_16M_traffic.md"), tmp_path / "profiles")
+    (tmp_path / "profiles" / "gpuos_resident_fused_chain_16M_traffic.md").write_text(
+        f"# traffic\n\n- kernel_sources_sha256: `{sha}`\n- hbm_bytes_per_pass: `{per_pass}`\n")
+    return fake
+
+
+def _sources_sha():
+    import hashlib
+
+    h = hashlib.sha256()
+    for name in bench.KERNEL_SOURCES:
+        with open(os.path.join(ROOT, "persistent_fusion_amd", "csrc", name), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()
+
+
+def test_traffic_is_reported_for_the_profiled_kernel_only(tmp_path, monkeypatch):
+    fake = _fake_tree(tmp_path, _sources_sha())
     monkeypatch.setattr(bench, "ROOT", str(tmp_path))
+    assert bench.traffic_per_launch(1500) == 1500 * 268_563_935
+    # the same profile against edited kernel sources: no traffic
+    (fake / bench.KERNEL_SOURCES[0]).write_text((fake / bench.KERNEL_SOURCES[0]).read_text() + "\n// edited\n")
     assert bench.traffic_per_launch(1500) is None
+
+
+def test_committed_profile_is_read_when_current():
+    """The committed counter summary is used exactly when it records the
+    hash of the kernel sources in the tree."""
+    path = os.path.join(ROOT, "profiles", "gpuos_resident_fused_chain_16M_traffic.md")
+    text = open(path).read()
+    per_launch = bench.traffic_per_launch(1500)
+    if _sources_sha() in text:
+        assert isinstance(per_launch, int) and per_launch > 1500 * 268_435_456
+    else:
+        assert per_launch is None
 
 
 def test_more_than_one_gpu_is_refused():

@@ -194,8 +194,8 @@ def test_host_ops_do_not_wait_and_kept_tensors_are_bounded():
 def test_contiguous_transposes_are_queued(dtype_name):
     """x.t().contiguous() and a batched x.transpose(1, 2).contiguous() are
     queued as transposed COPYs (ragged blocks included) and equal PyTorch's
-    results bit for bit; a default clone of a transpose, which keeps the
-    strided layout, passes through and keeps it."""
+    results bit for bit; a default clone of a transpose keeps the
+    transposed layout, as in PyTorch."""
     _need_gpu()
     import torch
 
@@ -215,7 +215,98 @@ def test_contiguous_transposes_are_queued(dtype_name):
             kept = x.t().clone()
     finally:
         mode.close()
-    assert queued == 2 and mode.stats["passed_through"] == 1, mode.stats
+    assert queued == 2 and mode.stats["queued"] == 3 and mode.stats["passed_through"] == 0, mode.stats
     assert t2.is_contiguous() and torch.equal(t2, x.t().contiguous())
     assert t3.is_contiguous() and torch.equal(t3, xb.transpose(1, 2).contiguous())
     assert kept.stride() == x.t().stride() and torch.equal(kept, x.t())
+
+
+@pytest.mark.parametrize("dtype_name", ["float32", "bfloat16", "float16"])
+def test_mode_queue_matches_the_oracle(dtype_name):
+    """Every op the mode queued, replayed by the oracle on the same initial
+    storages, gives the device's final storages element by element (bit for
+    bit for the exact-class ops, within the tolerance for exp)."""
+    _need_gpu()
+    import torch
+
+    import oracle
+    from torch_record import RecordingMode, final_storages, snapshot, to_workload
+
+    say(f"torch mode against the oracle {dtype_name}")
+    dtype = getattr(torch, dtype_name)
+    g = torch.Generator(device="cpu").manual_seed(64)
+    R, Cn = 45, 260
+    x = torch.randn(R, Cn, generator=g).to(dtype).cuda()
+    b = torch.randn(Cn, generator=g).to(dtype).cuda()
+    s = torch.randn(R, generator=g).to(dtype).cuda()
+    w = (torch.rand(R, Cn, generator=g) + 0.5).to(dtype).cuda()
+    init = snapshot([x, b, s, w])
+    mode = RecordingMode(0)
+    try:
+        with mode:
+            y = x * b                 # broadcast along rows
+            y = y + x
+            y.relu_()
+            z = y.t() * s             # transposed input, broadcast; keeps the layout
+            z = z * 0.5
+            c = z.clone()             # a dense transposed clone
+            c.add_(z)
+            d = x - w                 # programs defined at run time
+            d = d / w
+            d = -d
+            e = (d * 0.05).exp()
+            f = x.t().contiguous()    # transposed COPY
+            h = f * 2.0 + 1.25
+    finally:
+        mode.close()
+    assert mode.stats["passed_through"] == 0, mode.stats
+    wl = to_workload(mode.record, init)
+    say(f"  {len(wl.ops)} queued ops over {len(wl.buffers)} storages")
+    assert len(wl.ops) == mode.stats["queued"]
+    got = final_storages(wl)
+    want, scales = oracle.run(wl, scales=True)
+    for name in wl.buffers:
+        r = oracle.compare(got[name], want[name], wl.dtypes[name], scales.get(name))
+        assert r.ok, f"{name}: {r}"
+    # the outputs have PyTorch's layouts
+    assert z.stride() == (y.t() * s).stride() and c.stride() == z.stride()
+
+
+def test_mode_outputs_keep_eager_layouts():
+    """Out-of-place results have the strides eager PyTorch gives them, so a
+    view taken of them afterwards works the same inside the mode."""
+    _need_gpu()
+    import torch
+
+    from persistent_fusion_amd.torch_mode import GpuosMode
+
+    say("torch mode output layouts")
+    g = torch.Generator(device="cpu").manual_seed(65)
+    x = torch.randn(33, 70, generator=g).cuda()
+    m = torch.randn(70, 33, generator=g).cuda()
+    v = torch.randn(33, generator=g).cuda()
+    cube = torch.randn(4, 6, 9, generator=g).cuda()
+
+    def prog():
+        a = torch.relu(x.t())          # (70, 33) with strides (1, 70)
+        flat = a.t().reshape(-1)       # a view only because a kept its layout
+        b = x.t() + m                  # mixed layouts
+        c = m * v                      # broadcast, contiguous
+        d = x.t() * v                  # broadcast, transposed
+        e = cube.permute(2, 0, 1).exp()
+        return a, flat, b, c, d, e
+
+    want = prog()
+    mode = GpuosMode(0)
+    try:
+        with mode:
+            got = prog()
+    finally:
+        mode.close()
+    assert mode.stats["passed_through"] == 0, mode.stats
+    for k, (gt, wt) in enumerate(zip(got, want)):
+        assert gt.stride() == wt.stride(), (k, gt.stride(), wt.stride())
+        if k == 5:
+            assert torch.allclose(gt, wt, rtol=1e-5, atol=0), k
+        else:
+            assert torch.equal(gt, wt), k

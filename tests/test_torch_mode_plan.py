@@ -16,7 +16,7 @@ _S = torch.zeros(4, 4)
 def test_broadcast_add_becomes_a_view():
     x = torch.zeros(6, 40)
     b = torch.zeros(40)
-    kind, dt, alpha, shape, inplace, tens, vshape, vstr = plan_op(A.add.Tensor, (x, b), {}, CPU)
+    kind, dt, alpha, shape, inplace, tens, vshape, vstr, _ = plan_op(A.add.Tensor, (x, b), {}, CPU)
     assert (kind, dt, shape, inplace) == ("add", "f32", (6, 40), False)
     assert vshape == [6, 40]
     assert vstr == [[40, 1], [40, 1], [0, 1]]
@@ -24,15 +24,17 @@ def test_broadcast_add_becomes_a_view():
 
 def test_scalar_mul_is_scale_and_transposed_input_keeps_strides():
     x = torch.zeros(8, 5).t()  # (5, 8), strides (1, 5)
-    kind, dt, alpha, shape, inplace, tens, vshape, vstr = plan_op(A.mul.Scalar, (x, 2.5), {}, CPU)
+    kind, dt, alpha, shape, inplace, tens, vshape, vstr, _ = plan_op(A.mul.Scalar, (x, 2.5), {}, CPU)
     assert (kind, alpha, shape) == ("scale", 2.5, (5, 8))
-    assert vstr[0] == [8, 1] and vstr[1] == [1, 5] and vstr[2] == [0, 0]
+    # the output keeps the transposed layout, as eager PyTorch's does
+    assert vstr[0] == [1, 5] and vstr[1] == [1, 5] and vstr[2] == [0, 0]
+    assert list((x * 2.5).stride()) == vstr[0]
 
 
 def test_in_place_and_unit_dimensions():
     x = torch.zeros(3, 1, 7, dtype=torch.float16)
     y = torch.zeros(1, 1, 7, dtype=torch.float16)
-    kind, dt, alpha, shape, inplace, tens, vshape, vstr = plan_op(A.add_.Tensor, (x, y), {}, CPU)
+    kind, dt, alpha, shape, inplace, tens, vshape, vstr, _ = plan_op(A.add_.Tensor, (x, y), {}, CPU)
     assert (kind, dt, inplace, shape) == ("add", "f16", True, (3, 1, 7))
     assert vshape == [3, 7] and vstr == [[7, 1], [7, 1], [0, 1]]
 
@@ -49,7 +51,6 @@ def test_in_place_and_unit_dimensions():
     lambda: (A.add_.Tensor, (_B[:4], _B[1:5]), {}),                                   # in place over a shifted self
     lambda: (A.add_.Tensor, (_S, _S.t()), {}),                                        # in place over a transposed self
     lambda: (A.relu_.default, (torch.zeros(1, 4).expand(3, 4),), {}),                 # output names elements twice
-    lambda: (A.clone.default, (torch.zeros(3, 4).t(),), {}),                          # clone keeps a strided layout
     lambda: (A.clone.default, (torch.zeros(3, 4),), {"memory_format": torch.channels_last}),
 ])
 def test_not_intercepted(call):
@@ -64,7 +65,7 @@ def test_other_device_is_not_intercepted():
 
 def test_python_scalar_multiplier_is_scale():
     x = torch.zeros(10)
-    kind, dt, alpha, shape, inplace, tens, vshape, vstr = plan_op(A.mul.Tensor, (x, torch.tensor(0.25)), {}, CPU)
+    kind, dt, alpha, shape, inplace, tens, vshape, vstr, _ = plan_op(A.mul.Tensor, (x, torch.tensor(0.25)), {}, CPU)
     assert (kind, alpha, shape) == ("scale", 0.25, (10,))
 
 
@@ -77,9 +78,9 @@ def test_in_place_over_itself_is_intercepted():
 def test_python_number_in_mul_tensor_is_scale():
     # ``x * 0.5`` reaches the dispatcher as mul.Tensor(x, 0.5)
     x = torch.zeros(6)
-    kind, dt, alpha, shape, inplace, tens, vshape, vstr = plan_op(A.mul.Tensor, (x, 0.5), {}, CPU)
+    kind, dt, alpha, shape, inplace, tens, vshape, vstr, _ = plan_op(A.mul.Tensor, (x, 0.5), {}, CPU)
     assert (kind, alpha, inplace, len(tens)) == ("scale", 0.5, False, 1)
-    kind, dt, alpha, shape, inplace, tens, vshape, vstr = plan_op(A.mul_.Tensor, (x, 3), {}, CPU)
+    kind, dt, alpha, shape, inplace, tens, vshape, vstr, _ = plan_op(A.mul_.Tensor, (x, 3), {}, CPU)
     assert (kind, alpha, inplace) == ("scale", 3.0, True)
     assert plan_op(A.mul.Tensor, (torch.zeros(6, dtype=torch.int32), 2), {}, CPU) is None
 
@@ -127,7 +128,38 @@ def test_contiguous_clone_of_a_transpose_is_a_transposed_copy():
     """x.t().contiguous() reaches the dispatcher as clone(contiguous_format):
     a COPY whose view reads the input down the output's columns."""
     x = torch.zeros(3, 5)
-    kind, dt, alpha, shape, inplace, tens, vshape, vstr = plan_op(
+    kind, dt, alpha, shape, inplace, tens, vshape, vstr, _ = plan_op(
         A.clone.default, (x.t(),), {"memory_format": torch.contiguous_format}, CPU)
     assert (kind, dt, shape, inplace) == ("copy", "f32", (5, 3), False)
     assert vshape == [5, 3] and vstr[0] == [3, 1] and vstr[1] == [1, 5]
+
+
+def _layouts():
+    base = torch.zeros(6, 10)
+    cube = torch.zeros(3, 4, 5)
+    return [
+        (A.relu.default, (base.t(),), {}),
+        (A.exp.default, (cube.permute(2, 0, 1),), {}),
+        (A.add.Tensor, (base.t(), base.t()), {}),
+        (A.add.Tensor, (base.t(), torch.zeros(10, 6)), {}),     # mixed layouts
+        (A.add.Tensor, (torch.zeros(10, 6), base.t()), {}),
+        (A.mul.Tensor, (base.t(), torch.zeros(6)), {}),        # broadcast + transposed
+        (A.mul.Tensor, (torch.zeros(6), base.t()), {}),
+        (A.add.Tensor, (cube.transpose(0, 2), cube.transpose(0, 2)), {}),
+        (A.clone.default, (base.t(),), {}),                     # preserve_format keeps it
+        (A.clone.default, (base.t(),), {"memory_format": torch.contiguous_format}),
+        (A.clone.default, (cube[:, ::2],), {}),                 # not dense: contiguous
+        (A.mul.Tensor, (base.t(), 0.25), {}),
+    ]
+
+
+@pytest.mark.parametrize("case", range(len(_layouts())))
+def test_output_layout_is_eagers(case):
+    """Every queued out-of-place op's output has the strides eager PyTorch
+    gives it, so views taken of it later (.view, .t()) behave the same."""
+    func, args, kwargs = _layouts()[case]
+    plan = plan_op(func, args, kwargs, CPU)
+    assert plan is not None
+    want = func(*args, **kwargs)
+    assert plan[8] == tuple(want.stride()), (plan[8], want.stride())
+    assert plan[3] == tuple(want.shape)
