@@ -321,6 +321,34 @@ void gpuos_config_default(gpuos_config* cfg);
 int gpuos_create(int device, const gpuos_config* cfg, gpuos_ctx** out);
 
 /*
+ * gpuos_create for callers that cannot allocate memory (code that must not
+ * call hipMalloc or hipHostMalloc: serving loops, harnesses that forbid it).
+ * The context's device scheduler state (control block, device descriptor
+ * ring, ticket ends, completion words, tile counters) lives in a static
+ * device array the library holds on each device until the process ends
+ * (8 MiB: at most GPUOS_STATIC_MAX_SLOTS ring slots per ring), and its pinned
+ * rings live in host_ws, which the caller owns: host_ws_bytes >=
+ * GPUOS_STATIC_HOST_BYTES(cfg->ring_slots), 256-byte aligned, from
+ * hipHostMalloc with hipHostMallocMapped | hipHostMallocCoherent, untouched
+ * by the caller until gpuos_destroy returns.  The call makes no device or
+ * pinned allocation (host bookkeeping uses the C++ heap; the stream and the
+ * two timing events are created as in gpuos_create).  Every other entry point
+ * works on the context as on one from gpuos_create.
+ * One static context per device at a time: they would share the device's
+ * array, and calls on two of them would race; the second create returns
+ * ESTATE.  A new static context clears what must start at zero.
+ * Errors: EINVAL (ring_slots above GPUOS_STATIC_MAX_SLOTS, trace or
+ * tile_counts requested, a workspace too small, misaligned or not pinned
+ * that way, a bad device or config), ESTATE (a static context is alive on
+ * the device), EDEVICE.
+ */
+#define GPUOS_STATIC_MAX_SLOTS 4096u
+#define GPUOS_STATIC_HOST_BYTES(slots) \
+  (768u + 2u * ((size_t)(slots) * 256u + (((size_t)(slots) * 8u + 255u) / 256u) * 256u))
+int gpuos_create_static(int device, const gpuos_config* cfg, void* host_ws, size_t host_ws_bytes,
+                        gpuos_ctx** out);
+
+/*
  * Validates and copies n ops into the context's staging area; the caller's
  * array may be reused on return.  ids_out (nullable, n entries) receives the
  * ids assigned to the ops: consecutive, monotone, starting at 1 for a new

@@ -12,7 +12,7 @@ CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libgpuos.so")
 # Each kernel is its own translation unit; the units compile in parallel and
 # are linked into one shared library.
-SOURCES = ["kernels.hip", "single_kernel.hip", "runtime.cpp"]
+SOURCES = ["kernels.hip", "single_kernel.hip", "static_scratch.hip", "runtime.cpp"]
 OBJDIR = os.path.join(os.path.dirname(HERE), "_build")
 
 FLAGS = [

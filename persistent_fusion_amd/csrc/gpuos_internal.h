@@ -286,6 +286,34 @@ enum : uint64_t {
   DERR_DESC_CHECK = 3,
 };
 
+// Host bytes of the pinned rings of a context with `slots` slots per ring:
+// control block, then per ring the descriptor ring and its ends.
+inline size_t align256(size_t b) { return (b + 255) / 256 * 256; }
+inline size_t static_host_bytes(uint32_t slots) {
+  return align256(sizeof(HostCtl)) +
+         kRings * (align256((size_t)slots * kDescBytes) + align256((size_t)slots * 8));
+}
+
+// Device scratch of gpuos_create_static: one array per device, sized for
+// kStaticMaxSlots ring slots per ring.
+constexpr size_t kStaticScratchBytes = 8u << 20;
+constexpr uint32_t kStaticMaxSlots = 4096;
+constexpr int kMaxStaticDevices = 64;
+// Device bytes of a context's scheduler state with `slots` slots per ring:
+// control block, then per ring the descriptor ring, ends, completion words,
+// tile counters and their second level.
+inline size_t static_device_bytes(uint32_t slots) {
+  size_t b = align256(sizeof(DevCtl));
+  for (int r = 0; r < kRings; ++r) {
+    b += align256((size_t)slots * kDescBytes);
+    b += align256((size_t)2 * slots * 8);
+    b += align256((size_t)slots * kDoneReplicas * 8);
+    b += align256((size_t)kSubCounters * slots * 4);
+    b += align256((size_t)slots * 4);
+  }
+  return b;
+}
+
 // Everything the resident kernel needs, passed by value.
 struct KArgs {
   const DevDesc* hdesc[kRings];   // pinned host ring (device-visible address)

@@ -18,4 +18,10 @@ hipError_t launch_single(const DevDesc& d, uint32_t* err, hipStream_t s);
 // The resident kernel's function handle (for occupancy queries).
 const void* resident_kernel();
 
+// Address on `device` of the file-scope device scratch array of
+// static_scratch.hip (kStaticScratchBytes), taken once per device with that
+// device current (hipGetSymbolAddress); the error of that first call is
+// returned on every later one.
+hipError_t static_scratch(int device, void** ptr);
+
 }  // namespace gpuos

@@ -750,6 +750,8 @@ struct gpuos_ctx {
   uint32_t* subs_done[kRings] = {nullptr, nullptr};
   TraceRec* trace[kRings] = {nullptr, nullptr};
   uint32_t* tile_exec[kRings] = {nullptr, nullptr};
+  bool static_mem = false;  // rings in the caller's workspace and the static
+                            // device scratch (gpuos_create_static): not freed
 
   // host bookkeeping
   uint64_t next_id = 1;
@@ -1852,7 +1854,18 @@ void free_host(gpuos_ctx* c, void* p) {
     (void)hipHostFree(p);
 }
 
+// One static-scratch context per device at a time (they share the array).
+std::atomic<bool> g_static_busy[kMaxStaticDevices];
+
 void free_all(gpuos_ctx* c) {
+  if (c->static_mem) {
+    // the rings live in the caller's workspace and the static scratch
+    if (c->ev_start) (void)hipEventDestroy(c->ev_start);
+    if (c->ev_end) (void)hipEventDestroy(c->ev_end);
+    if (c->stream) (void)hipStreamDestroy(c->stream);
+    g_static_busy[c->device].store(false, std::memory_order_release);
+    return;
+  }
   free_host(c, c->hctl);
   for (int r = 0; r < kRings; ++r) {
     free_host(c, c->hdesc[r]);
@@ -1968,6 +1981,15 @@ int sync_impl(gpuos_ctx* c, uint64_t upto, int64_t timeout_ns) {
   return 0;
 }
 
+// Memory a static context is built in (gpuos_create_static).
+struct StaticMem {
+  void* host;                // the caller's pinned workspace (host address)
+  void* dev;                 // the device's static scratch
+  bool handed_over = false;  // the context now owns the device's busy flag
+};
+
+int create_impl(int device, const gpuos_config* cfg_in, StaticMem* sm, gpuos_ctx** out);
+
 }  // namespace
 
 // ===========================================================================
@@ -1998,6 +2020,55 @@ void gpuos_config_default(gpuos_config* cfg) {
 }
 
 int gpuos_create(int device, const gpuos_config* cfg_in, gpuos_ctx** out) {
+  return create_impl(device, cfg_in, nullptr, out);
+}
+
+int gpuos_create_static(int device, const gpuos_config* cfg_in, void* host_ws, size_t host_ws_bytes,
+                        gpuos_ctx** out) {
+  if (!out) return fail(GPUOS_EINVAL, "out is null");
+  *out = nullptr;
+  gpuos_config cfg;
+  int rc = apply_config(cfg_in, cfg);
+  if (rc) return rc;
+  if (device < 0 || device >= kMaxStaticDevices)
+    return fail(GPUOS_EINVAL, "device %d: static contexts exist for devices 0..%d", device,
+                kMaxStaticDevices - 1);
+  if (cfg.ring_slots > kStaticMaxSlots)
+    return fail(GPUOS_EINVAL, "ring_slots %u: a static context holds at most %u slots per ring "
+                "(%zu bytes of static device scratch)", cfg.ring_slots, kStaticMaxSlots,
+                kStaticScratchBytes);
+  if (cfg.trace == 1 || cfg.tile_counts)
+    return fail(GPUOS_EINVAL, "trace and tile_counts need allocations: not available in a static context");
+  const size_t need = static_host_bytes(cfg.ring_slots);
+  if (!host_ws || ((uintptr_t)host_ws & 255) || host_ws_bytes < need)
+    return fail(GPUOS_EINVAL, "host workspace: need %zu bytes, 256-byte aligned (got %zu at %p)", need,
+                host_ws_bytes, host_ws);
+  unsigned int flags = 0;
+  if (hipHostGetFlags(&flags, host_ws) != hipSuccess ||
+      (flags & (hipHostMallocMapped | hipHostMallocCoherent)) != (hipHostMallocMapped | hipHostMallocCoherent))
+    return fail(GPUOS_EINVAL, "host workspace must come from hipHostMalloc with hipHostMallocMapped | "
+                "hipHostMallocCoherent (flags %#x)", flags);
+  bool expect = false;
+  if (!g_static_busy[device].compare_exchange_strong(expect, true, std::memory_order_acq_rel))
+    return fail(GPUOS_ESTATE, "device %d already has a live static context: contexts on one device "
+                "share its static scratch", device);
+  void* dev = nullptr;
+  const hipError_t e = static_scratch(device, &dev);
+  if (e != hipSuccess || !dev) {
+    g_static_busy[device].store(false, std::memory_order_release);
+    return fail(GPUOS_EDEVICE, "static scratch of device %d: %s", device, hipGetErrorString(e));
+  }
+  StaticMem sm{host_ws, dev};
+  rc = create_impl(device, &cfg, &sm, out);
+  if (rc && !*out && !sm.handed_over) g_static_busy[device].store(false, std::memory_order_release);
+  return rc;
+}
+
+}  // extern "C"
+
+namespace {
+
+int create_impl(int device, const gpuos_config* cfg_in, StaticMem* sm, gpuos_ctx** out) {
   if (!out) return fail(GPUOS_EINVAL, "out is null");
   *out = nullptr;
   gpuos_config cfg;
@@ -2049,10 +2120,27 @@ int gpuos_create(int device, const gpuos_config* cfg_in, gpuos_ctx** out) {
   c->st.lc_waves = c->lc_waves;
   c->st.compute_units = c->cus;
 
-  rc = alloc_host(c, (void**)&c->hctl, sizeof(HostCtl));
-  for (int r = 0; r < kRings && !rc; ++r) {
-    rc = alloc_host(c, (void**)&c->hdesc[r], (size_t)c->cap * sizeof(DevDesc));
-    if (!rc) rc = alloc_host(c, (void**)&c->hends[r], (size_t)c->cap * sizeof(uint64_t));
+  if (sm) {
+    // carve the caller's pinned workspace and the static device scratch in
+    // the order static_host_bytes / static_device_bytes count them
+    c->static_mem = true;
+    sm->handed_over = true;  // from here on free_all releases the device
+    uint8_t* h = static_cast<uint8_t*>(sm->host);
+    memset(h, 0, static_host_bytes(c->cap));
+    c->hctl = reinterpret_cast<HostCtl*>(h);
+    h += align256(sizeof(HostCtl));
+    for (int r = 0; r < kRings; ++r) {
+      c->hdesc[r] = reinterpret_cast<DevDesc*>(h);
+      h += align256((size_t)c->cap * kDescBytes);
+      c->hends[r] = reinterpret_cast<uint64_t*>(h);
+      h += align256((size_t)c->cap * 8);
+    }
+  } else {
+    rc = alloc_host(c, (void**)&c->hctl, sizeof(HostCtl));
+    for (int r = 0; r < kRings && !rc; ++r) {
+      rc = alloc_host(c, (void**)&c->hdesc[r], (size_t)c->cap * sizeof(DevDesc));
+      if (!rc) rc = alloc_host(c, (void**)&c->hends[r], (size_t)c->cap * sizeof(uint64_t));
+    }
   }
   if (rc) {
     free_all(c);
@@ -2060,7 +2148,13 @@ int gpuos_create(int device, const gpuos_config* cfg_in, gpuos_ctx** out) {
     return rc;
   }
   if (!c->host_only) {
+    uint8_t* carve = sm ? static_cast<uint8_t*>(sm->dev) : nullptr;
     auto dalloc = [&](void** p, size_t bytes) -> int {
+      if (carve) {  // static scratch: consecutive 256-byte aligned pieces
+        *p = carve;
+        carve += align256(bytes);
+        return 0;
+      }
       hipError_t e = hipMalloc(p, bytes);
       if (e != hipSuccess) return fail(GPUOS_ENOMEM, "hipMalloc(%zu): %s", bytes, hipGetErrorString(e));
       return 0;
@@ -2141,7 +2235,7 @@ int gpuos_create(int device, const gpuos_config* cfg_in, gpuos_ctx** out) {
   return 0;
 }
 
-}  // extern "C"
+}  // namespace
 
 namespace {
 

@@ -101,7 +101,7 @@ EXPORTS = (
     "gpuos_graph_create", "gpuos_graph_launch", "gpuos_graph_destroy", "gpuos_yield",
     "gpuos_program_define", "gpuos_program_update",
     "gpuos_debug_read_desc", "gpuos_debug_published", "gpuos_debug_seq_of", "gpuos_debug_retire",
-    "gpuos_debug_tile_counts",
+    "gpuos_debug_tile_counts", "gpuos_create_static",
 )
 
 _lib = None
@@ -121,6 +121,7 @@ def lib() -> C.CDLL:
         "gpuos_last_error": (C.c_char_p, []),
         "gpuos_config_default": (None, [C.POINTER(GpuosConfig)]),
         "gpuos_create": (C.c_int, [C.c_int, C.POINTER(GpuosConfig), C.POINTER(P)]),
+        "gpuos_create_static": (C.c_int, [C.c_int, C.POINTER(GpuosConfig), P, C.c_size_t, C.POINTER(P)]),
         "gpuos_submit": (C.c_int, [P, C.POINTER(GpuosOp), C.c_uint32, C.POINTER(C.c_uint64)]),
         "gpuos_submit_views": (C.c_int, [P, C.POINTER(GpuosOp), C.POINTER(GpuosView), C.c_uint32,
                                          C.POINTER(C.c_uint64)]),
@@ -290,15 +291,28 @@ def encode_views(ops, start: int, end: int):
     return arr
 
 
+STATIC_MAX_SLOTS = 4096  # GPUOS_STATIC_MAX_SLOTS
+
+
+def static_host_bytes(slots: int) -> int:
+    """GPUOS_STATIC_HOST_BYTES(slots): the pinned workspace a static context needs."""
+    return 768 + 2 * (slots * 256 + (slots * 8 + 255) // 256 * 256)
+
 
 class Context:
-    """One resident-kernel context (``gpuos_create`` ... ``gpuos_destroy``)."""
+    """One resident-kernel context (``gpuos_create`` ... ``gpuos_destroy``).
+    With ``host_ws`` (the address of a pinned workspace of ``host_ws_bytes``
+    bytes) the context is made by ``gpuos_create_static`` instead."""
 
-    def __init__(self, device: int = 0, **cfg):
+    def __init__(self, device: int = 0, host_ws: Optional[int] = None, host_ws_bytes: int = 0, **cfg):
         self._lib = lib()
         self._cfg = config(**cfg)
         h = C.c_void_p()
-        _check(self._lib.gpuos_create(device, C.byref(self._cfg), C.byref(h)), "gpuos_create")
+        if host_ws is None:
+            _check(self._lib.gpuos_create(device, C.byref(self._cfg), C.byref(h)), "gpuos_create")
+        else:
+            _check(self._lib.gpuos_create_static(device, C.byref(self._cfg), host_ws, host_ws_bytes,
+                                                 C.byref(h)), "gpuos_create_static")
         self.handle = h
         self.device = device
 
