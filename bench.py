@@ -69,17 +69,22 @@ def fused_chain_leg(steps, warmup, device=0, warm_s=0.5):
     # the launch covers the warm-up passes and the timed passes; the HIP events
     # recorded around it on its stream give the kernel's duration
     ctx = gpuos.Context(device, trace=1)
-    # warm-up: `warmup` passes, continued in rounds of 64 until warm_s
-    # seconds have passed (each round is waited for, so the host does not run
-    # ahead of the device by more than a round)
+    # warm-up: at least `warmup` passes and warm_s seconds of them, submitted
+    # back to back; the host stays at most 128 passes ahead of the device (it
+    # waits for pass k - 128 before submitting pass k), so the device never
+    # idles and the host never queues seconds of work.  Then the queue drains.
     w0 = time.perf_counter()
     k = 0
+    last = []
     while k < warmup or time.perf_counter() - w0 < warm_s:
-        for _ in range(warmup if k == 0 and warmup else 64):
-            ctx.submit_noids(arrs[k % REPLICAS], 3)
-            ctx.flush()
-            k += 1
-        ctx.sync(0, 60.0)
+        if len(last) >= 128:
+            oid = last.pop(0)
+            while not ctx.query(oid):
+                pass
+        last.append(ctx.submit(arrs[k % REPLICAS], 3)[-1])
+        ctx.flush()
+        k += 1
+    ctx.sync(0, 60.0)
     warm_passes = k
     log(f"bench: fused chain, one resident launch: {warm_passes} warm-up passes "
         f"({time.perf_counter() - w0:.2f} s) + {steps} timed passes")

@@ -344,7 +344,8 @@ int gpuos_create(int device, const gpuos_config* cfg, gpuos_ctx** out);
  */
 #define GPUOS_STATIC_MAX_SLOTS 4096u
 #define GPUOS_STATIC_HOST_BYTES(slots) \
-  (768u + 2u * ((size_t)(slots) * 256u + (((size_t)(slots) * 8u + 255u) / 256u) * 256u))
+  (768u + 2u * ((size_t)(slots) * 256u + (((size_t)(slots) * 8u + 255u) / 256u) * 256u) + \
+   (((size_t)(slots) * 8u + 255u) / 256u) * 256u)
 int gpuos_create_static(int device, const gpuos_config* cfg, void* host_ws, size_t host_ws_bytes,
                         gpuos_ctx** out);
 

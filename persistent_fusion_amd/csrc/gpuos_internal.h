@@ -241,7 +241,11 @@ struct alignas(256) DevCtl {
   // debug options (read only when KArgs::debug is nonzero)
   uint32_t* tile_exec[kRings];  // executions of ticket i of each ring, i < n
   uint64_t tile_exec_n;
-  uint64_t _pd[29];
+  // latency-critical ring: the wave that completes descriptor s stores s into
+  // hdone_lc[slot] (pinned host memory), so that the host sees an LC op done
+  // without waiting for the in-order retire of the doorbell wave
+  uint64_t* hdone_lc;
+  uint64_t _pd[28];
 };
 constexpr uint32_t kDebugCount = 1u;
 
@@ -287,11 +291,13 @@ enum : uint64_t {
 };
 
 // Host bytes of the pinned rings of a context with `slots` slots per ring:
-// control block, then per ring the descriptor ring and its ends.
+// control block, then per ring the descriptor ring and its ends, then the
+// latency-critical ring's completion words.
 inline size_t align256(size_t b) { return (b + 255) / 256 * 256; }
 inline size_t static_host_bytes(uint32_t slots) {
   return align256(sizeof(HostCtl)) +
-         kRings * (align256((size_t)slots * kDescBytes) + align256((size_t)slots * 8));
+         kRings * (align256((size_t)slots * kDescBytes) + align256((size_t)slots * 8)) +
+         align256((size_t)slots * 8);
 }
 
 // Device scratch of gpuos_create_static: one array per device, sized for

@@ -254,6 +254,7 @@ __device__ __forceinline__ void finish_tile(const KArgs& a, const Cached& c, uin
     const uint64_t t_done = now_ticks();
 #pragma unroll
     for (uint32_t k = 0; k < kDoneReplicas; ++k) st_rlx_agent(&a.done_id[RING][(uint64_t)k * cap + slot], c.seq);
+    if constexpr (RING == 1) st_rlx_sys(&a.dctl->hdone_lc[slot], c.seq);
     if (a.trace[RING]) {
       TraceRec* tr = &a.trace[RING][slot];
       st_rlx_agent(&tr->seq, c.seq);
@@ -376,8 +377,16 @@ __device__ __forceinline__ void service_lc(const KArgs& a, const AvailLine* line
     if (lane_id() == 0) av = ld_rlx_agent(&line->avail_tiles);
     av = bcast64(av);
     if (av == seen) return;
-    uint64_t nxt = 0;
-    if (lane_id() == 0) nxt = ld_rlx_agent(&R->next);
+    // after avail_tiles has returned: the claim cursor, and avail_ops (stored
+    // before avail_tiles, so it covers every descriptor below av) and the
+    // copied frontier, all in one round trip
+    uint64_t nxt = 0, ops = 0, copied = 0;
+    if (lane_id() == 0) {
+      wait_mem();
+      nxt = ld_rlx_agent(&R->next);
+      ops = ld_rlx_agent(&line->avail_ops);
+      copied = ld_rlx_agent(&line->copied_ops);
+    }
     nxt = bcast64(nxt);
     if (nxt >= av) {
       seen = av;
@@ -392,9 +401,7 @@ __device__ __forceinline__ void service_lc(const KArgs& a, const AvailLine* line
                : 0u;
     }
     if (!bcast(ok)) continue;
-    uint64_t tiles, ops, copied;
-    read_avail(line, tiles, ops, copied);
-    map_ticket<1>(a, nxt, ops, copied, line, c);
+    map_ticket<1>(a, nxt, bcast64(ops), bcast64(copied), line, c);
     run_ticket<1>(a, nxt, c);
   }
 }

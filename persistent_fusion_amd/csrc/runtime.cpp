@@ -741,6 +741,7 @@ struct gpuos_ctx {
   HostCtl* hctl = nullptr;
   DevDesc* hdesc[kRings] = {nullptr, nullptr};
   uint64_t* hends[kRings] = {nullptr, nullptr};
+  uint64_t* hdone_lc = nullptr;  // latency-critical completions by slot
   // device memory
   DevCtl* dctl = nullptr;
   DevDesc* ddesc[kRings] = {nullptr, nullptr};
@@ -750,6 +751,8 @@ struct gpuos_ctx {
   uint32_t* subs_done[kRings] = {nullptr, nullptr};
   TraceRec* trace[kRings] = {nullptr, nullptr};
   uint32_t* tile_exec[kRings] = {nullptr, nullptr};
+  bool spread_big = false;  // per-op launches: big elementwise ops take every
+                            // wave (each op is then the only kernel running)
   bool static_mem = false;  // rings in the caller's workspace and the static
                             // device scratch (gpuos_create_static): not freed
 
@@ -804,7 +807,12 @@ bool id_retired(gpuos_ctx* c, uint64_t id) {
   if (idx >= c->idseq.size()) return false;
   const uint64_t v = c->idseq[idx];
   if (!v) return false;
-  return (v & ((1ull << 63) - 1)) <= completed_of(c, (uint32_t)(v >> 63));
+  const uint64_t seq = v & ((1ull << 63) - 1);
+  const uint32_t ring = (uint32_t)(v >> 63);
+  if (seq <= completed_of(c, ring)) return true;
+  // a latency-critical descriptor is seen done by its own completion word
+  // before the in-order retire cursor passes it
+  return ring == 1 && c->hdone_lc && load_acq(&c->hdone_lc[(seq - 1) & (c->cap - 1)]) == seq;
 }
 
 void prune_ids(gpuos_ctx* c) {
@@ -842,15 +850,21 @@ uint32_t ceil_div(uint64_t a, uint64_t b) { return (uint32_t)((a + b - 1) / b); 
 
 // Elementwise tile: cfg.tile_elems, or be_tile_elems for ops of 2^24
 // elements or more.  Large ops are cut into whole rounds over the worker
-// waves (every wave gets the same number of tiles) and an op big enough to
-// give every wave 1024 elements is spread over all of them.  Tiles stay a
-// multiple of 64 elements so every tile starts 16-byte aligned.
-uint32_t ew_tile_elems(const gpuos_config& cfg, uint32_t workers, uint64_t n) {
-  uint64_t tile = n >= (1ull << 24) ? cfg.be_tile_elems : cfg.tile_elems;
+// waves (every wave gets the same number of tiles).  An op below 2^24
+// elements that is big enough to give every wave 1024 elements is spread over
+// all of them; an op of 2^24 or more with fewer be_tile_elems tiles than
+// waves keeps its tiles in the resident kernel (several such ops then run side
+// by side on different waves, each tile streaming longer between its
+// completion counts) and is spread like the others with `spread` (one launch
+// per op, where the op is the only kernel running).  Tiles stay a multiple of
+// 64 elements so every tile starts 16-byte aligned.
+uint32_t ew_tile_elems(const gpuos_config& cfg, uint32_t workers, uint64_t n, bool spread = false) {
+  const bool big = n >= (1ull << 24);
+  uint64_t tile = big ? cfg.be_tile_elems : cfg.tile_elems;
   uint64_t nt = (n + tile - 1) / tile;
   if (workers) {
     if (nt < workers) {
-      if (n >= (uint64_t)workers * 1024) nt = workers;
+      if ((!big || spread) && n >= (uint64_t)workers * 1024) nt = workers;
     } else {
       nt = (nt + workers - 1) / workers * workers;
     }
@@ -861,7 +875,7 @@ uint32_t ew_tile_elems(const gpuos_config& cfg, uint32_t workers, uint64_t n) {
   return (uint32_t)tile;
 }
 
-void set_tiling(const gpuos_config& cfg, uint32_t workers, DevDesc& d) {
+void set_tiling(const gpuos_config& cfg, uint32_t workers, DevDesc& d, bool spread = false) {
   switch (d.opcode) {
     case GPUOS_OP_NOP: case GPUOS_OP_SPIN: case GPUOS_OP_ROPE:
       d.tile = 1;
@@ -919,14 +933,15 @@ void set_tiling(const gpuos_config& cfg, uint32_t workers, DevDesc& d) {
       break;
     }
     default: {  // elementwise and fused
-      d.tile = ew_tile_elems(cfg, workers, d.n);
+      d.tile = ew_tile_elems(cfg, workers, d.n, spread);
       d.ntiles = ceil_div(d.n, d.tile);
       break;
     }
   }
 }
 
-void encode_plain(const gpuos_op& o, const gpuos_config& cfg, uint32_t workers, DevDesc& d) {
+void encode_plain(const gpuos_op& o, const gpuos_config& cfg, uint32_t workers, DevDesc& d,
+                  bool spread = false) {
   memset(&d, 0, sizeof d);
   d.opcode = (uint8_t)o.opcode;
   d.dtype = o.dtype;
@@ -954,7 +969,7 @@ void encode_plain(const gpuos_op& o, const gpuos_config& cfg, uint32_t workers, 
     d.row_len = o.row_len;
   }
   d.user_ops = 1;
-  set_tiling(cfg, workers, d);
+  set_tiling(cfg, workers, d, spread);
 }
 
 // ---------------------------------------------------------------------------
@@ -1347,7 +1362,8 @@ uint32_t try_softmax_av(gpuos_ctx* c, size_t i, size_t end, DevDesc& d) {
 // are commutative in IEEE arithmetic, so acc + x and x + acc are the same
 // result.  This is the operators compiled at run time of the pages, for the
 // programs the fused tile can express; any other program is interpreted.
-bool program_as_builtin(const Staged& st, const gpuos_config& cfg, uint32_t workers, DevDesc& d) {
+bool program_as_builtin(const Staged& st, const gpuos_config& cfg, uint32_t workers, DevDesc& d,
+                        bool spread = false) {
   const gpuos_op& o = st.op;
   if (o.dtype != GPUOS_F32) return false;
   const ProgCode& pc = st.prog;
@@ -1437,7 +1453,7 @@ bool program_as_builtin(const Staged& st, const gpuos_config& cfg, uint32_t work
       case FS_EXP: po.opcode = GPUOS_OP_EXP; break;
       default: po.opcode = GPUOS_OP_COPY; break;
     }
-    encode_plain(po, cfg, workers, d);
+    encode_plain(po, cfg, workers, d, spread);
     return true;
   }
   memset(&d, 0, sizeof d);
@@ -1456,7 +1472,7 @@ bool program_as_builtin(const Staged& st, const gpuos_config& cfg, uint32_t work
   d.f.out[ni - 1] = (uint64_t)o.out;
   d.f.step_fl[ni - 1] = (uint8_t)(fls[ni - 1] | FSF_STORE);
   d.user_ops = 1;
-  set_tiling(cfg, workers, d);
+  set_tiling(cfg, workers, d, spread);
   return true;
 }
 
@@ -1563,17 +1579,17 @@ void plan_ops(gpuos_ctx* c, size_t begin, size_t end, std::vector<Planned>& plan
             d.f.step_fl[s] = (uint8_t)(fls[s] | (keep ? FSF_STORE : 0));
           }
           d.user_ops = n_steps;
-          set_tiling(cfg, c->workers, d);
+          set_tiling(cfg, c->workers, d, c->spread_big);
           pl.count = n_steps;
           c->st.ops_fused += n_steps - 1;
         }
       }
     }
     if (pl.count == 1) {
-      if (s0.op.opcode == GPUOS_OP_PROGRAM && fuse && program_as_builtin(s0, cfg, c->workers, pl.desc)) {
+      if (s0.op.opcode == GPUOS_OP_PROGRAM && fuse && program_as_builtin(s0, cfg, c->workers, pl.desc, c->spread_big)) {
         ++c->st.programs_lowered;
       } else {
-        encode_plain(s0.op, cfg, c->workers, pl.desc);
+        encode_plain(s0.op, cfg, c->workers, pl.desc, c->spread_big);
         if (s0.view.on) encode_view(s0.view, c->workers, pl.desc);
         if (s0.op.opcode == GPUOS_OP_PROGRAM) encode_program(s0.prog, pl.desc);
       }
@@ -1867,6 +1883,7 @@ void free_all(gpuos_ctx* c) {
     return;
   }
   free_host(c, c->hctl);
+  free_host(c, c->hdone_lc);
   for (int r = 0; r < kRings; ++r) {
     free_host(c, c->hdesc[r]);
     free_host(c, c->hends[r]);
@@ -2135,12 +2152,14 @@ int create_impl(int device, const gpuos_config* cfg_in, StaticMem* sm, gpuos_ctx
       c->hends[r] = reinterpret_cast<uint64_t*>(h);
       h += align256((size_t)c->cap * 8);
     }
+    c->hdone_lc = reinterpret_cast<uint64_t*>(h);
   } else {
     rc = alloc_host(c, (void**)&c->hctl, sizeof(HostCtl));
     for (int r = 0; r < kRings && !rc; ++r) {
       rc = alloc_host(c, (void**)&c->hdesc[r], (size_t)c->cap * sizeof(DevDesc));
       if (!rc) rc = alloc_host(c, (void**)&c->hends[r], (size_t)c->cap * sizeof(uint64_t));
     }
+    if (!rc) rc = alloc_host(c, (void**)&c->hdone_lc, (size_t)c->cap * sizeof(uint64_t));
   }
   if (rc) {
     free_all(c);
@@ -2181,6 +2200,7 @@ int create_impl(int device, const gpuos_config* cfg_in, StaticMem* sm, gpuos_ctx
         for (uint32_t k = 0; k < kReplicas; ++k) img->avail[r][k].stop_ticket = ~0ull;  // epoch 0
       for (int r = 0; r < kRings; ++r) img->tile_exec[r] = c->tile_exec[r];
       img->tile_exec_n = cfg.tile_counts;
+      img->hdone_lc = (uint64_t*)dev_ptr(c->hdone_lc);
       e = hipMemcpy(c->dctl, img, sizeof(DevCtl), hipMemcpyHostToDevice);
       for (int r = 0; r < kRings && e == hipSuccess; ++r) {
         e = hipMemsetAsync(c->dends[r], 0, (size_t)2 * c->cap * sizeof(uint64_t), c->stream);
@@ -2571,10 +2591,11 @@ int issue_per_op(const gpuos_op* ops, uint32_t n, int fuse, uint32_t cus, hipStr
   gpuos_config_default(&tmp.cfg);
   tmp.cfg.fusion = fuse ? 1 : 2;
   tmp.workers = cus * 16;
+  tmp.spread_big = true;
   if (!fuse) {
     DevDesc d;
     for (uint32_t i = 0; i < n; ++i) {
-      encode_plain(ops[i], tmp.cfg, tmp.workers, d);
+      encode_plain(ops[i], tmp.cfg, tmp.workers, d, true);
       mark_streaming(tmp.cfg, d);
       if (ops[i].opcode == GPUOS_OP_NOP) continue;
       HIP_TRY(launch_single(d, nullptr, s));

@@ -296,7 +296,7 @@ STATIC_MAX_SLOTS = 4096  # GPUOS_STATIC_MAX_SLOTS
 
 def static_host_bytes(slots: int) -> int:
     """GPUOS_STATIC_HOST_BYTES(slots): the pinned workspace a static context needs."""
-    return 768 + 2 * (slots * 256 + (slots * 8 + 255) // 256 * 256)
+    return 768 + 2 * (slots * 256 + (slots * 8 + 255) // 256 * 256) + (slots * 8 + 255) // 256 * 256
 
 
 class Context:
