@@ -680,9 +680,10 @@ def program_leg(device=0, steps=200, warmup=100):
     by one op defined at run time (a 3-instruction register program) instead
     of the built-in fused descriptor: one resident launch, the same rotating
     replicas and passes as the headline, 16 algorithmic bytes per element.
-    The program runs interpreted (fusion off) and lowered to the fused
-    micro-program (fusion on, the default); the built-in fused chain is timed
-    the same way in the same process."""
+    The program runs interpreted (fusion off), compiled at run time into the
+    kernel variant (gpuos_program_compile, fusion off) and lowered to the
+    fused micro-program (fusion on, the default); the built-in fused chain is
+    timed the same way in the same process."""
     import numpy as np
     import torch
 
@@ -690,14 +691,19 @@ def program_leg(device=0, steps=200, warmup=100):
 
     ys = {}
     out = {"workload": "relu(a*x+b), 16,777,216 fp32 elements, 3-instruction program (interpreted; "
-                       "lowered) vs built-in fused chain, 4 rotating replicas"}
+                       "compiled at run time; lowered) vs built-in fused chain, 4 rotating replicas"}
     prog_wl = workloads.gen_program_chain(seed=0, n=N_ELEMS)
-    for label, wl, fusion in (("program", prog_wl, 2), ("program_lowered", prog_wl, 1),
+    for label, wl, fusion in (("program", prog_wl, 2), ("program_compiled", prog_wl, 2),
+                              ("program_lowered", prog_wl, 1),
                               ("builtin_fused", workloads.gen_fused_chain(seed=0, n=N_ELEMS), 1)):
         reps = [runner.to_device(wl, device) for _ in range(REPLICAS)]
         ctx = gpuos.Context(device, trace=1, fusion=fusion)
         try:
             pids = gpuos.define_programs(ctx, wl.ops)
+            if label == "program_compiled":
+                t0 = time.perf_counter()
+                ctx.program_compile(dtypes=["f32"])
+                out["compile_s"] = round(time.perf_counter() - t0, 2)
             arrs = [gpuos.encode_ops(wl.ops, 0, len(wl.ops), runner.addr_fn(t, wl), {}, pids) for t in reps]
             torch.cuda.synchronize()
             for k in range(warmup):
@@ -713,7 +719,7 @@ def program_leg(device=0, steps=200, warmup=100):
             tr = ctx.trace()
         finally:
             ctx.destroy()
-        op_code = gpuos.OPCODES["program"] if label == "program" else 32  # 32: fused chain
+        op_code = gpuos.OPCODES["program"] if label in ("program", "program_compiled") else 32  # 32: fused
         recs = sorted((r for r in tr if r["opcode"] == op_code), key=lambda r: r["seq"])[-steps:]
         per_pass = sorted((r["t_done"] - r["t_claim"]) * 1e-8 for r in recs)
         out[label] = {"gb_per_s": round(steps * 16 * N_ELEMS / wall / 1e9, 1),
@@ -722,10 +728,12 @@ def program_leg(device=0, steps=200, warmup=100):
         ys[label] = reps[(warmup + steps - 1) % REPLICAS]["y"].cpu().numpy()
         del reps
     out["program_vs_builtin"] = round(out["program"]["gb_per_s"] / out["builtin_fused"]["gb_per_s"], 3)
+    out["program_compiled_vs_builtin"] = round(out["program_compiled"]["gb_per_s"] /
+                                               out["builtin_fused"]["gb_per_s"], 3)
     out["program_lowered_vs_builtin"] = round(out["program_lowered"]["gb_per_s"] /
                                               out["builtin_fused"]["gb_per_s"], 3)
     out["bit_identical"] = bool(all(np.array_equal(ys[k].view(np.uint32), ys["builtin_fused"].view(np.uint32))
-                                    for k in ("program", "program_lowered")))
+                                    for k in ("program", "program_compiled", "program_lowered")))
     return out
 
 

@@ -43,7 +43,7 @@
 extern "C" {
 #endif
 
-#define GPUOS_ABI_VERSION 4
+#define GPUOS_ABI_VERSION 5
 
 /* Status codes. */
 typedef enum gpuos_status {
@@ -54,7 +54,8 @@ typedef enum gpuos_status {
   GPUOS_ETIMEDOUT = -4, /* gpuos_sync gave up before the ops completed */
   GPUOS_EDEVICE = -5,   /* HIP error, or the device raised its error word;
                            the context is poisoned and must be destroyed */
-  GPUOS_ESTATE = -6     /* call not allowed in the context's current state */
+  GPUOS_ESTATE = -6,    /* call not allowed in the context's current state */
+  GPUOS_ECOMPILE = -7   /* run-time compilation failed (gpuos_program_compile) */
 } gpuos_status;
 
 /*
@@ -284,6 +285,10 @@ typedef struct gpuos_stats {
   uint64_t programs_lowered;   /* PROGRAM ops run as a built-in op or fused
                                   micro-program (their body is a chain the
                                   fused tile expresses; fusion on) */
+  uint64_t programs_compiled;  /* PROGRAM ops published with a compiled body
+                                  (gpuos_program_compile) */
+  uint64_t kernel_switches;    /* hand-overs of the queue between the built-in
+                                  kernel and the compiled variant */
 } gpuos_stats;
 
 /* Per-descriptor device timing, recorded when config.trace == 1. */
@@ -540,6 +545,7 @@ int gpuos_baseline_run(int device, const gpuos_op* ops, uint32_t n, int fuse,
  */
 #define GPUOS_PROG_MAX_INSNS 16
 #define GPUOS_PROG_MAX_PROGRAMS 4096
+#define GPUOS_PROG_MAX_COMPILED 256  /* distinct bodies in one compile */
 
 typedef enum gpuos_pop {
   GPUOS_P_MOV = 0,
@@ -590,6 +596,49 @@ int gpuos_program_define(gpuos_ctx* ctx, const gpuos_program* prog, uint32_t* id
  * gpuos_program_define); ESTATE on a stopped context.
  */
 int gpuos_program_update(gpuos_ctx* ctx, uint32_t id, const gpuos_program* prog);
+
+/*
+ * Compiled program bodies ("GPUOS: A GPU Operating System Primitive for
+ * Transparent Operation Fusion", section "The Paper": operators compiled at
+ * run time and installed into the running persistent kernel, with two slots
+ * so that an operator can be replaced while the kernel runs).
+ *
+ * gpuos_program_compile writes the current bodies of programs ids[0, n_ids)
+ * (ids = NULL: every program defined so far) as straight-line code, builds
+ * with hipRTC a variant of the resident kernel whose op table holds them,
+ * and loads it on the context's device.  The call blocks for the compile
+ * (seconds) and leaves the queue alone: the running kernel goes on.  It
+ * allocates device memory for the code (refused on a static context).
+ *
+ * Two kernels can then serve the queue.  The built-in kernel runs every op
+ * (PROGRAM ops interpreted).  The compiled variant runs PROGRAM ops whose
+ * body, as of their submission, is one it compiled (in a dtype of `dtypes`),
+ * and the fp32 streaming ops: NOP, COPY of 4-byte elements, ADD, MUL, RELU,
+ * SCALE, EXP, SILU_MUL and fused chains of them, without views.  At a flush,
+ * the context hands the queue to the compiled variant before a PROGRAM op
+ * with a compiled body when every descriptor left in that flush can run
+ * there, and back to the built-in kernel before a descriptor that cannot.  A
+ * hand-over waits until every published op has completed, lets the running
+ * kernel leave as gpuos_yield does, and launches the other kernel on the same
+ * rings, so such a flush blocks for that drain.  A new compile's variant
+ * replaces the previous one at the next hand-over (the previous one stays
+ * loaded while it runs: two slots).  Which kernel runs an op never changes
+ * its result: a compiled body performs the interpreter's fp32 operations in
+ * the same order, each rounded to nearest even.
+ *
+ * dtypes: a mask of 1u << GPUOS_F32, 1u << GPUOS_BF16, 1u << GPUOS_F16 to
+ * compile the bodies for (0 = all three).  log: if not NULL, receives the
+ * compiler's messages, NUL-terminated and cut to log_bytes (empty when there
+ * are none).  On a host-only context (GPUOS_DEVICE_NONE) the variant is
+ * compiled for gfx950 and not loaded; flushes then count hand-overs without
+ * running anything.
+ * Errors: EINVAL (null context, an unknown id, no program to compile, more
+ * than GPUOS_PROG_MAX_COMPILED distinct bodies, a bad mask); ESTATE (stopped or static context); ECOMPILE (hipRTC failed, or the
+ * variant would not fit the resident grid: see log and gpuos_last_error);
+ * EDEVICE (loading the module failed).
+ */
+int gpuos_program_compile(gpuos_ctx* ctx, const uint32_t* ids, uint32_t n_ids, uint32_t dtypes,
+                          char* log, size_t log_bytes);
 
 /*
  * Graph-replay comparator ("Launch Overhead and Fusion", section "Graph

@@ -58,6 +58,14 @@ int gpuos_debug_retire(gpuos_ctx* ctx, int ring, uint64_t upto);
  */
 int gpuos_debug_tile_counts(gpuos_ctx* ctx, int ring, uint32_t* out, uint32_t n);
 
+/*
+ * The program-body source that the last gpuos_program_compile call wrote
+ * (the generated gpuos_rtc_bodies.h): copies it, NUL-terminated and cut to
+ * n bytes, into buf (may be NULL) and returns its length plus 1 (1 if there
+ * has been no compile, 0 for a null context).
+ */
+size_t gpuos_debug_rtc_source(gpuos_ctx* ctx, char* buf, size_t n);
+
 #ifdef __cplusplus
 }
 #endif

@@ -13,12 +13,20 @@
 // a worker: it claims tiles with an atomic ticket, maps the ticket to its
 // descriptor, waits for the descriptor's dependencies, runs the tile through
 // the opcode switch and counts it done.
+//
+// The same source also builds the run-time compiled variant of the kernel
+// (GPUOS_RTC_VARIANT, compiled with hipRTC): its opcode switch is the one in
+// rtc_exec.h, which adds program bodies compiled to straight-line code.
 #include <hip/hip_runtime.h>
 
 #include "device_common.h"
 #include "gpuos_internal.h"
-#include "kernels.h"
 #include "tile_ops.h"
+#ifdef GPUOS_RTC_VARIANT
+#include "rtc_exec.h"
+#else
+#include "kernels.h"
+#endif
 
 namespace gpuos {
 
@@ -287,6 +295,7 @@ __device__ __forceinline__ void run_ticket(const KArgs& a, uint64_t ticket, Cach
       st_rlx_agent(&a.trace[RING][slot_of(c.seq, a.cap_mask)].t_claim, now_ticks());
   };
   if (!c.deps_ok) {
+#ifndef GPUOS_RTC_VARIANT
     const uint32_t w0 = d(0);
     const uint32_t op = w0 & 0xffu;
     if ((op == GPUOS_OP_GEMV || op == OP_NORM_GEMV || op == OP_GEMV_ADD) &&
@@ -313,11 +322,16 @@ __device__ __forceinline__ void run_ticket(const KArgs& a, uint64_t ticket, Cach
       finish_tile<RING>(a, c, tile, ticket);
       return;
     }
+#endif
     wait_deps<RING>(a, c);
     c.deps_ok = 1;
   }
   claimed();
+#ifdef GPUOS_RTC_VARIANT
+  const uint32_t err = exec_rtc<kResidentLoadCP, kResidentStoreCP>(d, tile);
+#else
   const uint32_t err = exec_tile<kResidentLoadCP, kResidentStoreCP>(d, tile, c.scr);
+#endif
   if (err) report_error(a, RING, c.seq, err);
   finish_tile<RING>(a, c, tile, ticket);
 }
@@ -702,8 +716,7 @@ __device__ __forceinline__ void doorbell_loop(const KArgs& a) {
   }
 }
 
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2)))
-void gpuos_resident(KArgs a) {
+__device__ __forceinline__ void resident_main(const KArgs& a) {
   // one descriptor slot per wave and ring, and each wave's tile scratch
   __shared__ uint32_t sdesc[4][2][64];
   __shared__ float sscr[4][kWaveScratch];
@@ -724,6 +737,22 @@ void gpuos_resident(KArgs a) {
     worker_loop(a, num - 1 - a.lc_waves, (lds_u32*)&sdesc[wib][0][0], (lds_f32*)&sscr[wib][0]);
 }
 
+}  // namespace gpuos
+
+#ifdef GPUOS_RTC_VARIANT
+// Entry point of the compiled variant, found by name in the loaded module.
+extern "C" __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2)))
+void gpuos_resident_rtc(gpuos::KArgs a) {
+  gpuos::resident_main(a);
+}
+#else
+namespace gpuos {
+
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2)))
+void gpuos_resident(KArgs a) {
+  resident_main(a);
+}
+
 hipError_t launch_resident(const KArgs& a, uint32_t blocks, hipStream_t s) {
   hipLaunchKernelGGL(gpuos_resident, dim3(blocks), dim3(256), 0, s, a);
   return hipGetLastError();
@@ -732,3 +761,4 @@ hipError_t launch_resident(const KArgs& a, uint32_t blocks, hipStream_t s) {
 const void* resident_kernel() { return reinterpret_cast<const void*>(&gpuos_resident); }
 
 }  // namespace gpuos
+#endif

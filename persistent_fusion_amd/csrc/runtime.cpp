@@ -11,6 +11,7 @@
 // is what lets the device read the ring directly (same page, section "Memory
 // transfers").
 #include <hip/hip_runtime.h>
+#include <hip/hiprtc.h>
 
 #include <algorithm>
 #include <atomic>
@@ -21,6 +22,7 @@
 #include <cstring>
 #include <deque>
 #include <map>
+#include <memory>
 #include <mutex>
 #include <string>
 #include <thread>
@@ -32,6 +34,14 @@
 #include "kernels.h"
 
 using namespace gpuos;
+
+namespace gpuos {
+// Sources of the compiled kernel variant, embedded at build time under the
+// names their #include lines use (rtc_sources.cpp, generated).
+extern const char* const kRtcSourceNames[];
+extern const char* const kRtcSourceTexts[];
+extern const unsigned kRtcSourceCount;
+}  // namespace gpuos
 
 namespace {
 
@@ -189,6 +199,7 @@ struct ProgCode {
   float k[8] = {};
   uint32_t n_inputs() const { return (meta >> 16) & 3u; }
 };
+static_assert(sizeof(ProgCode) == 100, "a body's bytes are its identity: no padding");
 
 // Arity of a program instruction: registers it reads.
 int pop_arity(uint32_t op) {
@@ -711,6 +722,23 @@ class HazardMap {
 // ---------------------------------------------------------------------------
 // context
 
+// A loaded compiled kernel variant (gpuos_program_compile): its module, the
+// kernel, and the index of each compiled body by the body's bytes.
+struct RtcModule {
+  hipModule_t mod = nullptr;
+  hipFunction_t fn = nullptr;
+  std::map<std::string, uint32_t> index;
+  uint32_t dtypes = 0;
+  bool leak = false;  // a launch of it may still run: never unloaded
+  ~RtcModule() {
+    if (mod && !leak) (void)hipModuleUnload(mod);
+  }
+};
+
+std::string body_key(const ProgCode& pc) {
+  return std::string(reinterpret_cast<const char*>(&pc), sizeof pc);
+}
+
 struct Staged {
   gpuos_op op;
   uint64_t id;
@@ -762,6 +790,7 @@ struct gpuos_ctx {
   std::deque<uint64_t> idseq;      // (ring << 63) | seq, 0 = staged
   std::vector<Staged> staged;
   std::vector<Planned> plan;       // fusion pass output, reused across flushes
+  std::vector<uint8_t> tail_ok;    // plan[i..] all runnable by the compiled variant
   uint64_t pub_seq[kRings] = {0, 0};
   uint64_t pub_tiles[kRings] = {0, 0};
   uint64_t tail_written[kRings] = {0, 0};
@@ -776,6 +805,13 @@ struct gpuos_ctx {
   bool leaked = false;      // kernel did not exit: memory must not be freed
   bool timing = false;      // ev_start/ev_end bracket a launch not yet counted
   uint32_t epoch = 0;       // launches so far
+  // compiled kernel variants: the latest compile, and the one the running
+  // kernel was launched from (null while the built-in kernel runs).  A
+  // variant is unloaded once neither holds it.
+  std::shared_ptr<RtcModule> rtc_new, rtc_run;
+  bool on_rtc = false;      // the launched kernel is rtc_run's
+  std::string arch = "gfx950";  // the device's target name for hipRTC
+  std::string rtc_source;   // body source of the last compile
   KArgs kargs{};
   hipEvent_t ev_start = nullptr, ev_end = nullptr;
   gpuos_stats st{};
@@ -1591,7 +1627,15 @@ void plan_ops(gpuos_ctx* c, size_t begin, size_t end, std::vector<Planned>& plan
       } else {
         encode_plain(s0.op, cfg, c->workers, pl.desc, c->spread_big);
         if (s0.view.on) encode_view(s0.view, c->workers, pl.desc);
-        if (s0.op.opcode == GPUOS_OP_PROGRAM) encode_program(s0.prog, pl.desc);
+        if (s0.op.opcode == GPUOS_OP_PROGRAM) {
+          encode_program(s0.prog, pl.desc);
+          // the latest compiled variant's body for it, if any
+          const RtcModule* m = c->rtc_new.get();
+          if (m && ((m->dtypes >> pl.desc.dtype) & 1u)) {
+            const auto it = m->index.find(body_key(s0.prog));
+            if (it != m->index.end()) pl.desc.pg.body = it->second + 1;
+          }
+        }
       }
       j = i + 1;
     }
@@ -1613,7 +1657,14 @@ int launch_kernel(gpuos_ctx* c, uint64_t base) {
   c->kargs.epoch = ++c->epoch;
   c->kargs.ticket_base = base;
   hipError_t e = hipEventRecord(c->ev_start, c->stream);
-  if (e == hipSuccess) e = launch_resident(c->kargs, c->blocks, c->stream);
+  if (e == hipSuccess) {
+    if (c->on_rtc) {
+      void* args[] = {&c->kargs};
+      e = hipModuleLaunchKernel(c->rtc_run->fn, c->blocks, 1, 1, 256, 1, 1, 0, c->stream, args, nullptr);
+    } else {
+      e = launch_resident(c->kargs, c->blocks, c->stream);
+    }
+  }
   if (e == hipSuccess) e = hipEventRecord(c->ev_end, c->stream);
   if (e != hipSuccess) {
     c->poisoned = true;
@@ -1820,24 +1871,137 @@ int publish_one(gpuos_ctx* c, Planned& pl) {
   return 0;
 }
 
+// Can the compiled kernel variant run descriptor d?  (Its op table: PROGRAM
+// ops with a compiled body, NOP, 4-byte COPY, fp32 elementwise ops and fused
+// fp32 chains, no views.)
+bool rtc_runnable(const DevDesc& d) {
+  if (d.flags & DF_VIEW) return false;
+  switch (d.opcode) {
+    case GPUOS_OP_PROGRAM:
+      return d.pg.body != 0;
+    case GPUOS_OP_NOP:
+      return true;
+    case GPUOS_OP_COPY:
+      return d.dtype == GPUOS_F32 || d.dtype == GPUOS_I32;
+    case GPUOS_OP_ADD: case GPUOS_OP_MUL: case GPUOS_OP_RELU: case GPUOS_OP_SCALE:
+    case GPUOS_OP_EXP: case GPUOS_OP_SILU_MUL: case OP_FUSED_EW:
+      return d.dtype == GPUOS_F32;
+    default:
+      return false;
+  }
+}
+
+// The resident kernel leaves once the queue is drained (the doorbell wave
+// runs the same exit handshake as an idle exit; it may also have idled out
+// already) and the context is parked: the next launch starts at park_tiles.
+int park_kernel(gpuos_ctx* c, int64_t timeout_ns) {
+  std::atomic_thread_fence(std::memory_order_seq_cst);
+  store_rel(&c->hctl->yield_req, 1);
+  const auto t0 = std::chrono::steady_clock::now();
+  while (load_acq(&c->hctl->exit_epoch) != c->epoch) {
+    if (check_device_error(c)) {
+      store_rel(&c->hctl->yield_req, 0);
+      return GPUOS_EDEVICE;
+    }
+    if (timeout_ns >= 0 &&
+        std::chrono::steady_clock::now() - t0 > std::chrono::nanoseconds(timeout_ns)) {
+      store_rel(&c->hctl->yield_req, 0);
+      return fail(GPUOS_ETIMEDOUT, "the resident kernel did not leave");
+    }
+    std::this_thread::sleep_for(std::chrono::microseconds(2));
+  }
+  store_rel(&c->hctl->yield_req, 0);
+  const int rc = wait_kernel_end(c, timeout_ns);
+  if (rc) return rc;
+  account_launch(c);
+  c->park_tiles = load_acq(&c->hctl->exit_tiles);
+  c->parked = true;
+  return 0;
+}
+
+// Hands the queue to the compiled variant rtc_new (to_rtc) or to the
+// built-in kernel, at a drain point: every published op completes, the
+// running kernel leaves, and the other kernel is launched on the same rings
+// from the ticket where the first one stopped.  The variant the previous
+// kernel ran is released here unless it is also the latest compile.
+constexpr int64_t kSwitchTimeoutNs = 60ll * 1000 * 1000 * 1000;
+int sync_impl(gpuos_ctx* c, uint64_t upto, int64_t timeout_ns);
+
+int switch_kernel(gpuos_ctx* c, bool to_rtc) {
+  ++c->st.kernel_switches;
+  if (c->host_only) {  // nothing runs: the hand-over is only counted
+    c->on_rtc = to_rtc;
+    c->rtc_run = to_rtc ? c->rtc_new : nullptr;
+    return 0;
+  }
+  if (!c->parked) {
+    int rc = sync_impl(c, 0, kSwitchTimeoutNs);
+    if (!rc) rc = park_kernel(c, kSwitchTimeoutNs);
+    if (rc) return rc;
+  }
+  c->on_rtc = to_rtc;
+  c->rtc_run = to_rtc ? c->rtc_new : nullptr;
+  const int rc = launch_kernel(c, c->park_tiles);
+  if (!rc) c->parked = false;
+  return rc;
+}
+
 int flush_impl(gpuos_ctx* c) {
   if (check_device_error(c)) return GPUOS_EDEVICE;
   if (c->staged.empty()) return 0;
-  if (c->parked) {  // relaunch first: publication may wait for ring space
-    const int rl = launch_kernel(c, c->park_tiles);
-    if (rl) return rl;
-    c->parked = false;
-  }
   ++c->st.flushes;
   std::vector<Planned>& plan = c->plan;
   plan.clear();
   plan.reserve(c->staged.size());
   plan_ops(c, 0, c->staged.size(), plan);
-  size_t done_ops = 0;
+  // Kernel hand-overs: to the compiled variant before a PROGRAM op with a
+  // compiled body if it can run every descriptor left in this flush; back to
+  // the built-in kernel before one it cannot run; from an older variant to
+  // the latest before a body only the latest holds.
+  const bool variants = c->rtc_new || c->on_rtc;
+  std::vector<uint8_t>& tail_ok = c->tail_ok;
+  if (variants) {
+    tail_ok.assign(plan.size() + 1, 1);
+    for (size_t i = plan.size(); i-- > 0;) tail_ok[i] = tail_ok[i + 1] && rtc_runnable(plan[i].desc);
+  }
+  auto wanted = [&](size_t i) -> int {  // -1 = stay, 0 = built-in, 1 = latest variant
+    const DevDesc& d = plan[i].desc;
+    const bool compiled = d.opcode == GPUOS_OP_PROGRAM && d.pg.body != 0;
+    if (c->on_rtc) {
+      if (!rtc_runnable(d)) return 0;
+      return compiled && c->rtc_run != c->rtc_new ? 1 : -1;
+    }
+    return compiled && tail_ok[i] ? 1 : -1;
+  };
   int rc = 0;
-  for (Planned& pl : plan) {
+  if (c->parked) {  // relaunch first: publication may wait for ring space
+    if (variants && !plan.empty()) {
+      const int w = wanted(0);
+      if (w >= 0) {
+        ++c->st.kernel_switches;
+        c->on_rtc = w == 1;
+        c->rtc_run = c->on_rtc ? c->rtc_new : nullptr;
+      }
+    }
+    rc = launch_kernel(c, c->park_tiles);
+    if (rc) return rc;
+    c->parked = false;
+  }
+  size_t done_ops = 0;
+  for (size_t i = 0; i < plan.size(); ++i) {
+    Planned& pl = plan[i];
+    if (variants) {
+      const int w = wanted(i);
+      if (w >= 0) {
+        publish_tail(c, 0);
+        publish_tail(c, 1);
+        rc = switch_kernel(c, w == 1);
+        if (rc) break;
+      }
+    }
     rc = publish_one(c, pl);
     if (rc) break;
+    if (pl.desc.opcode == GPUOS_OP_PROGRAM && pl.desc.pg.body) ++c->st.programs_compiled;
     done_ops += pl.count;
   }
   publish_tail(c, 0);
@@ -1998,6 +2162,124 @@ int sync_impl(gpuos_ctx* c, uint64_t upto, int64_t timeout_ns) {
   return 0;
 }
 
+// ---------------------------------------------------------------------------
+// compiled kernel variant (gpuos_program_compile)
+
+// Source register r of a body: r0..r7 are variables, r8..r15 the program's
+// constants, written as their exact bits.
+std::string rtc_reg(const ProgCode& pc, uint32_t r) {
+  if (r < 8) return "r" + std::to_string(r);
+  uint32_t bits;
+  memcpy(&bits, &pc.k[r - 8], 4);
+  char buf[64];
+  snprintf(buf, sizeof buf, "pvec(__uint_as_float(0x%08xu))", bits);
+  return buf;
+}
+
+// Program pc as straight-line code: a functor over 4-element vectors with
+// one statement per instruction, each the interpreter's operation for it
+// (the pv_* helpers are the interpreter's own).  r0..r2 arrive as the
+// inputs (+0 past n_inputs); r3..r7 start at +0, as registers the program
+// reads before writing do in the interpreter.
+void emit_body(std::string& s, uint32_t k, const ProgCode& pc) {
+  s += "struct RtcBody" + std::to_string(k) + " {\n";
+  s += "  __device__ __forceinline__ pvec operator()(pvec r0, pvec r1, pvec r2) const {\n";
+  s += "    [[maybe_unused]] pvec r3 = pvec(0.0f), r4 = r3, r5 = r3, r6 = r3, r7 = r3;\n";
+  const uint32_t ni = pc.meta & 31u;
+  for (uint32_t i = 0; i < ni; ++i) {
+    const uint32_t w = pc.ins[i];
+    const uint32_t op = w & 31u, dst = (w >> 5) & 7u;
+    const std::string a = rtc_reg(pc, (w >> 8) & 15u), b = rtc_reg(pc, (w >> 12) & 15u),
+                      cc = rtc_reg(pc, (w >> 16) & 15u);
+    std::string e;
+    switch (op) {
+      case GPUOS_P_ADD: e = a + " + " + b; break;
+      case GPUOS_P_SUB: e = a + " - " + b; break;
+      case GPUOS_P_MUL: e = a + " * " + b; break;
+      case GPUOS_P_DIV: e = a + " / " + b; break;
+      case GPUOS_P_MIN: e = "pv_min(" + a + ", " + b + ")"; break;
+      case GPUOS_P_MAX: e = "pv_max(" + a + ", " + b + ")"; break;
+      case GPUOS_P_NEG: e = "pv_neg(" + a + ")"; break;
+      case GPUOS_P_ABS: e = "pv_abs(" + a + ")"; break;
+      case GPUOS_P_RELU: e = "pv_relu(" + a + ")"; break;
+      case GPUOS_P_EXP: e = "pv_exp(" + a + ")"; break;
+      case GPUOS_P_LT: e = "pv_lt(" + a + ", " + b + ")"; break;
+      case GPUOS_P_SEL: e = "pv_sel(" + a + ", " + b + ", " + cc + ")"; break;
+      default: e = a; break;  // MOV
+    }
+    s += "    r" + std::to_string(dst) + " = " + e + ";\n";
+  }
+  s += "    return " + rtc_reg(pc, (pc.meta >> 8) & 15u) + ";\n  }\n};\n";
+}
+
+const char kRtcMain[] = "#define GPUOS_RTC_VARIANT 1\n#include \"kernels.hip\"\n";
+// hipRTC has no hip/hip_runtime.h (its device API is built in) and no
+// stddef.h: these stand in for them.
+const char kRtcHipRuntime[] = "#pragma once\n";
+const char kRtcStddef[] =
+    "#pragma once\ntypedef decltype(sizeof(0)) size_t;\n#define offsetof(t, m) __builtin_offsetof(t, m)\n";
+
+// Compiles the variant with `bodies` as gpuos_rtc_bodies.h for target
+// `arch`; the code object goes to `code`, the compiler's messages to `log`.
+int rtc_compile(const std::string& arch, const std::string& bodies, std::vector<char>& code,
+                std::string& log) {
+  std::vector<const char*> names, texts;
+  for (unsigned i = 0; i < kRtcSourceCount; ++i) {
+    names.push_back(kRtcSourceNames[i]);
+    texts.push_back(kRtcSourceTexts[i]);
+  }
+  names.push_back("hip/hip_runtime.h");
+  texts.push_back(kRtcHipRuntime);
+  names.push_back("stddef.h");
+  texts.push_back(kRtcStddef);
+  names.push_back("gpuos_rtc_bodies.h");
+  texts.push_back(bodies.c_str());
+  hiprtcProgram prog;
+  hiprtcResult r = hiprtcCreateProgram(&prog, kRtcMain, "gpuos_resident_rtc.hip", (int)names.size(),
+                                       texts.data(), names.data());
+  if (r != HIPRTC_SUCCESS) return fail(GPUOS_ECOMPILE, "hiprtcCreateProgram: %s", hiprtcGetErrorString(r));
+  // the flags the library's own kernels are built with
+  const std::string target = "--offload-arch=" + arch;
+  const char* opts[] = {target.c_str(), "-O3", "-std=c++17", "-ffp-contract=off",
+                        "-fno-gpu-flush-denormals-to-zero", "-Xclang", "-target-feature", "-Xclang",
+                        "-packed-fp32-ops"};
+  r = hiprtcCompileProgram(prog, (int)(sizeof opts / sizeof opts[0]), opts);
+  size_t n = 0;
+  if (hiprtcGetProgramLogSize(prog, &n) == HIPRTC_SUCCESS && n > 1) {
+    log.assign(n, '\0');
+    if (hiprtcGetProgramLog(prog, &log[0]) != HIPRTC_SUCCESS) log.clear();
+    while (!log.empty() && log.back() == '\0') log.pop_back();
+  }
+  if (r == HIPRTC_SUCCESS) {
+    n = 0;
+    r = hiprtcGetCodeSize(prog, &n);
+    if (r == HIPRTC_SUCCESS && n) {
+      code.resize(n);
+      r = hiprtcGetCode(prog, code.data());
+    }
+  }
+  (void)hiprtcDestroyProgram(&prog);
+  if (r != HIPRTC_SUCCESS || code.empty())
+    return fail(GPUOS_ECOMPILE, "hipRTC compile failed: %s", hiprtcGetErrorString(r));
+  return 0;
+}
+
+// Loads a compiled variant and checks that it fits the context's resident
+// grid (the built-in kernel's blocks per CU) without scratch memory.
+int rtc_load(gpuos_ctx* c, const std::vector<char>& code, RtcModule& m) {
+  HIP_TRY(hipSetDevice(c->device));
+  HIP_TRY(hipModuleLoadData(&m.mod, code.data()));
+  HIP_TRY(hipModuleGetFunction(&m.fn, m.mod, "gpuos_resident_rtc"));
+  int scratch = 0, nb = 0;
+  HIP_TRY(hipFuncGetAttribute(&scratch, HIP_FUNC_ATTRIBUTE_LOCAL_SIZE_BYTES, m.fn));
+  HIP_TRY(hipModuleOccupancyMaxActiveBlocksPerMultiprocessor(&nb, m.fn, 256, 0));
+  const uint32_t bpc = c->blocks / c->cus;
+  if (scratch != 0 || (uint32_t)nb < bpc)
+    return fail(GPUOS_ECOMPILE, "compiled variant fits %d blocks per CU (%u needed) and uses %d B of scratch",
+                nb, bpc, scratch);
+  return 0;
+}
+
 // Memory a static context is built in (gpuos_create_static).
 struct StaticMem {
   void* host;                // the caller's pinned workspace (host address)
@@ -2110,6 +2392,7 @@ int create_impl(int device, const gpuos_config* cfg_in, StaticMem* sm, gpuos_ctx
       return fail(GPUOS_EDEVICE, "device %d: %s", device, hipGetErrorString(e));
     }
     c->cus = (uint32_t)prop.multiProcessorCount;
+    c->arch = prop.gcnArchName;
     int nb = 0;
     e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&nb, resident_kernel(), 256, 0);
     if (e != hipSuccess || nb <= 0) {
@@ -2503,6 +2786,63 @@ int gpuos_program_update(gpuos_ctx* c, uint32_t id, const gpuos_program* prog) {
   return 0;
 }
 
+int gpuos_program_compile(gpuos_ctx* c, const uint32_t* ids, uint32_t n_ids, uint32_t dtypes,
+                          char* log, size_t log_bytes) {
+  if (log && log_bytes) log[0] = '\0';
+  if (!c) return fail(GPUOS_EINVAL, "null context");
+  if (c->stopped) return fail(GPUOS_ESTATE, "context is stopped");
+  if (c->static_mem) return fail(GPUOS_ESTATE, "a static context allocates nothing: it cannot load compiled code");
+  const uint32_t all = (1u << GPUOS_F32) | (1u << GPUOS_BF16) | (1u << GPUOS_F16);
+  if (dtypes == 0) dtypes = all;
+  if (dtypes & ~all) return fail(GPUOS_EINVAL, "dtypes mask 0x%x has bits other than F32, BF16, F16", dtypes);
+  std::vector<uint32_t> list;
+  if (ids) {
+    for (uint32_t i = 0; i < n_ids; ++i) {
+      if (ids[i] >= c->programs.size()) return fail(GPUOS_EINVAL, "unknown program %u", ids[i]);
+      list.push_back(ids[i]);
+    }
+  } else {
+    for (uint32_t i = 0; i < (uint32_t)c->programs.size(); ++i) list.push_back(i);
+  }
+  if (list.empty()) return fail(GPUOS_EINVAL, "no program to compile");
+  auto m = std::make_shared<RtcModule>();
+  m->dtypes = dtypes;
+  std::string bodies = "// Program bodies of one gpuos_program_compile call (generated).\n#pragma once\n";
+  char buf[96];
+  snprintf(buf, sizeof buf, "#define GPUOS_RTC_DTYPES 0x%xu\n", dtypes);
+  bodies += buf;
+  bodies += "namespace gpuos {\n";
+  std::string cases;
+  for (uint32_t id : list) {
+    const ProgCode& pc = c->programs[id];
+    const std::string key = body_key(pc);
+    if (m->index.count(key)) continue;
+    const uint32_t k = (uint32_t)m->index.size();
+    if (k == GPUOS_PROG_MAX_COMPILED)
+      return fail(GPUOS_EINVAL, "more than %d distinct bodies in one compile", GPUOS_PROG_MAX_COMPILED);
+    m->index.emplace(key, k);
+    emit_body(bodies, k, pc);
+    cases += " X(" + std::to_string(k) + ")";
+  }
+  bodies += "}  // namespace gpuos\n#define GPUOS_RTC_BODIES(X)" + cases + "\n";
+  c->rtc_source = bodies;
+  std::vector<char> code;
+  std::string clog;
+  int rc = rtc_compile(c->host_only ? std::string("gfx950") : c->arch, bodies, code, clog);
+  if (log && log_bytes) {
+    const size_t k = std::min(clog.size(), log_bytes - 1);
+    memcpy(log, clog.data(), k);
+    log[k] = '\0';
+  }
+  if (rc) return rc;
+  if (!c->host_only) {
+    rc = rtc_load(c, code, *m);
+    if (rc) return rc;
+  }
+  c->rtc_new = std::move(m);  // the previous compile stays loaded while a kernel runs it
+  return 0;
+}
+
 int gpuos_yield(gpuos_ctx* c, int64_t timeout_ns) {
   if (!c) return fail(GPUOS_EINVAL, "null context");
   if (c->stopped) return fail(GPUOS_ESTATE, "context is stopped");
@@ -2510,30 +2850,7 @@ int gpuos_yield(gpuos_ctx* c, int64_t timeout_ns) {
   int rc = flush_impl(c);
   if (!rc) rc = sync_impl(c, 0, timeout_ns);
   if (rc) return rc;
-  // the doorbell wave leaves once the queue is drained, with the same exit
-  // handshake as an idle exit; it may also have idled out already
-  std::atomic_thread_fence(std::memory_order_seq_cst);
-  store_rel(&c->hctl->yield_req, 1);
-  const auto t0 = std::chrono::steady_clock::now();
-  while (load_acq(&c->hctl->exit_epoch) != c->epoch) {
-    if (check_device_error(c)) {
-      store_rel(&c->hctl->yield_req, 0);
-      return GPUOS_EDEVICE;
-    }
-    if (timeout_ns >= 0 &&
-        std::chrono::steady_clock::now() - t0 > std::chrono::nanoseconds(timeout_ns)) {
-      store_rel(&c->hctl->yield_req, 0);
-      return fail(GPUOS_ETIMEDOUT, "yield: the resident kernel did not leave");
-    }
-    std::this_thread::sleep_for(std::chrono::microseconds(2));
-  }
-  store_rel(&c->hctl->yield_req, 0);
-  rc = wait_kernel_end(c, timeout_ns);
-  if (rc) return rc;
-  account_launch(c);
-  c->park_tiles = load_acq(&c->hctl->exit_tiles);
-  c->parked = true;
-  return 0;
+  return park_kernel(c, timeout_ns);
 }
 
 int gpuos_destroy(gpuos_ctx* c, int64_t timeout_ns) {
@@ -2542,7 +2859,8 @@ int gpuos_destroy(gpuos_ctx* c, int64_t timeout_ns) {
   if (!c->host_only) {
     rc = gpuos_stop(c, timeout_ns);
     if (c->leaked) {
-      // never free memory a running kernel may still touch
+      // never free memory (or unload code) a running kernel may still touch
+      if (c->rtc_run) c->rtc_run->leak = true;
       rc = fail(GPUOS_ETIMEDOUT, "resident kernel did not exit; its memory is leaked");
       delete c;
       return rc;
@@ -2705,6 +3023,16 @@ int gpuos_debug_seq_of(gpuos_ctx* c, uint64_t id, int* ring_out, uint64_t* seq_o
   *ring_out = (int)(v >> 63);
   *seq_out = v & ((1ull << 63) - 1);
   return 0;
+}
+
+size_t gpuos_debug_rtc_source(gpuos_ctx* c, char* buf, size_t n) {
+  if (!c) return 0;
+  if (buf && n) {
+    const size_t k = std::min(c->rtc_source.size(), n - 1);
+    memcpy(buf, c->rtc_source.data(), k);
+    buf[k] = '\0';
+  }
+  return c->rtc_source.size() + 1;
 }
 
 int gpuos_debug_tile_counts(gpuos_ctx* c, int ring, uint32_t* out, uint32_t n) {

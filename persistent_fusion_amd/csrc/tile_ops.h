@@ -346,6 +346,57 @@ __device__ __forceinline__ void prog_dst(PRegs& R, uint32_t i, pvec y) {
   }
 }
 
+// The instructions' per-element operations on 4-element vectors; the
+// interpreter and compiled program bodies both use them.
+__device__ __forceinline__ pvec pv_min(pvec a, pvec b) {
+  pvec y;
+#pragma unroll
+  for (int e = 0; e < 4; ++e) y[e] = prog_min(a[e], b[e]);
+  return y;
+}
+__device__ __forceinline__ pvec pv_max(pvec a, pvec b) {
+  pvec y;
+#pragma unroll
+  for (int e = 0; e < 4; ++e) y[e] = prog_max(a[e], b[e]);
+  return y;
+}
+__device__ __forceinline__ pvec pv_neg(pvec a) {
+  pvec y;
+#pragma unroll
+  for (int e = 0; e < 4; ++e) y[e] = __uint_as_float(__float_as_uint(a[e]) ^ 0x80000000u);
+  return y;
+}
+__device__ __forceinline__ pvec pv_abs(pvec a) {
+  pvec y;
+#pragma unroll
+  for (int e = 0; e < 4; ++e) y[e] = __uint_as_float(__float_as_uint(a[e]) & 0x7fffffffu);
+  return y;
+}
+__device__ __forceinline__ pvec pv_relu(pvec a) {
+  pvec y;
+#pragma unroll
+  for (int e = 0; e < 4; ++e) y[e] = a[e] > 0.0f ? a[e] : 0.0f;
+  return y;
+}
+__device__ __forceinline__ pvec pv_exp(pvec a) {
+  pvec y;
+#pragma unroll
+  for (int e = 0; e < 4; ++e) y[e] = expf(a[e]);
+  return y;
+}
+__device__ __forceinline__ pvec pv_lt(pvec a, pvec b) {
+  pvec y;
+#pragma unroll
+  for (int e = 0; e < 4; ++e) y[e] = a[e] < b[e] ? 1.0f : 0.0f;
+  return y;
+}
+__device__ __forceinline__ pvec pv_sel(pvec a, pvec b, pvec c) {
+  pvec y;
+#pragma unroll
+  for (int e = 0; e < 4; ++e) y[e] = a[e] != 0.0f ? b[e] : c[e];
+  return y;
+}
+
 // Instructions that read b (binary ops and LT) and c (SEL).
 constexpr uint32_t kPReadsB = (1u << GPUOS_P_ADD) | (1u << GPUOS_P_SUB) | (1u << GPUOS_P_MUL) |
                               (1u << GPUOS_P_DIV) | (1u << GPUOS_P_MIN) | (1u << GPUOS_P_MAX) |
@@ -368,17 +419,14 @@ __device__ __forceinline__ pvec prog_run(uint32_t pw, uint32_t meta, PRegs& R) {
       case GPUOS_P_SUB: y = a - b; break;
       case GPUOS_P_MUL: y = a * b; break;
       case GPUOS_P_DIV: y = a / b; break;
-#define GPUOS_PEW(code, expr) \
-      case code: _Pragma("unroll") for (int e = 0; e < 4; ++e) y[e] = (expr); break;
-      GPUOS_PEW(GPUOS_P_MIN, prog_min(a[e], b[e]))
-      GPUOS_PEW(GPUOS_P_MAX, prog_max(a[e], b[e]))
-      GPUOS_PEW(GPUOS_P_NEG, __uint_as_float(__float_as_uint(a[e]) ^ 0x80000000u))
-      GPUOS_PEW(GPUOS_P_ABS, __uint_as_float(__float_as_uint(a[e]) & 0x7fffffffu))
-      GPUOS_PEW(GPUOS_P_RELU, a[e] > 0.0f ? a[e] : 0.0f)
-      GPUOS_PEW(GPUOS_P_EXP, expf(a[e]))
-      GPUOS_PEW(GPUOS_P_LT, a[e] < b[e] ? 1.0f : 0.0f)
-      GPUOS_PEW(GPUOS_P_SEL, a[e] != 0.0f ? b[e] : c[e])
-#undef GPUOS_PEW
+      case GPUOS_P_MIN: y = pv_min(a, b); break;
+      case GPUOS_P_MAX: y = pv_max(a, b); break;
+      case GPUOS_P_NEG: y = pv_neg(a); break;
+      case GPUOS_P_ABS: y = pv_abs(a); break;
+      case GPUOS_P_RELU: y = pv_relu(a); break;
+      case GPUOS_P_EXP: y = pv_exp(a); break;
+      case GPUOS_P_LT: y = pv_lt(a, b); break;
+      case GPUOS_P_SEL: y = pv_sel(a, b, c); break;
       default: y = a; break;  // MOV
     }
     prog_dst(R, (w >> 5) & 7u, y);
@@ -415,21 +463,19 @@ __device__ __forceinline__ void prog_init(PRegs& R, uint32_t nin, uint32_t zmask
 // the bounded resources and return 0, which keeps the counter's waits exact.
 // The n % V leftover elements belong to the last tile; misaligned operands
 // use per-element accesses.
-template <int DT, int CPL, int CPS>
-__device__ __forceinline__ void prog_tile(SDesc d, uint32_t t) {
+// `body(x0, x1, x2)` computes 4 elements' results from their inputs (inputs
+// past n_inputs are +0): the interpreter below, or a compiled program body.
+template <int DT, int CPL, int CPS, class Body>
+__device__ __forceinline__ void prog_each(SDesc d, uint32_t t, Body& body) {
   using T = DTr<DT, CPL, CPS>;
   constexpr int V = T::V;
   constexpr int G = 8;      // elements per lane per group
   constexpr int U = G / V;  // rows per group
   constexpr int P = G / 4;  // program passes per group (4 elements each)
   const uint32_t n = d(1), ntiles = d(6), meta = d(26);
-  const uint32_t nin = (meta >> 16) & 3u, zmask = meta >> 24;
+  const uint32_t nin = (meta >> 16) & 3u;
   const uint64_t po = d.q(18), p0 = d.q(20), p1 = nin >= 2 ? d.q(22) : 0, p2 = nin >= 3 ? d.q(24) : 0;
   const uint32_t lane = lane_id();
-  // instructions (dwords 27-42) in lanes 0-15, constants (43-50) in lanes 16-23
-  const uint32_t pw = d.p[27 + (lane & 31u)];
-  PRegs R;
-  R.r0 = R.r1 = R.r2 = R.r3 = R.r4 = R.r5 = R.r6 = R.r7 = pvec(0.0f);
   const bool fast = aligned16(po) && aligned16(p0) && aligned16(p1) && aligned16(p2);
   if (fast) {
     const uint32_t nv = n / V, nrows = (nv + 63) / 64, ngroups = (nrows + U - 1) / U;
@@ -462,8 +508,7 @@ __device__ __forceinline__ void prog_tile(SDesc d, uint32_t t) {
         }
         asm volatile("" : "+v"(a0), "+v"(a1), "+v"(a2));
         if (e0 + 4 == V) load_row(g + ntiles, u);  // row u fully taken
-        prog_init(R, nin, zmask, a0, a1, a2);
-        const pvec o = prog_run(pw, meta, R);
+        const pvec o = body(a0, a1, a2);
 #pragma unroll
         for (int e = 0; e < 4; ++e) w[4 * k + e] = o[e];
       }
@@ -484,8 +529,7 @@ __device__ __forceinline__ void prog_tile(SDesc d, uint32_t t) {
       y0[0] = T::ld(s0, i);
       if (nin >= 2) y1[0] = T::ld(s1, i);
       if (nin >= 3) y2[0] = T::ld(s2, i);
-      prog_init(R, nin, zmask, y0, y1, y2);
-      const pvec o = prog_run(pw, meta, R);
+      const pvec o = body(y0, y1, y2);
       if (i < n) T::st(so, i, o[0]);
     }
     return;
@@ -502,14 +546,29 @@ __device__ __forceinline__ void prog_tile(SDesc d, uint32_t t) {
       if (nin >= 2) y1[e] = T::ld(s1, i);
       if (nin >= 3) y2[e] = T::ld(s2, i);
     }
-    prog_init(R, nin, zmask, y0, y1, y2);
-    const pvec o = prog_run(pw, meta, R);
+    const pvec o = body(y0, y1, y2);
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
       const uint32_t i = (uint32_t)base + (uint32_t)e * 64 + lane;
       if (i < n) T::st(so, i, o[e]);
     }
   }
+}
+
+// A PROGRAM op interpreted: the program rides in the descriptor.
+template <int DT, int CPL, int CPS>
+__device__ __forceinline__ void prog_tile(SDesc d, uint32_t t) {
+  const uint32_t meta = d(26);
+  const uint32_t nin = (meta >> 16) & 3u, zmask = meta >> 24;
+  // instructions (dwords 27-42) in lanes 0-15, constants (43-50) in lanes 16-23
+  const uint32_t pw = d.p[27 + (lane_id() & 31u)];
+  PRegs R;
+  R.r0 = R.r1 = R.r2 = R.r3 = R.r4 = R.r5 = R.r6 = R.r7 = pvec(0.0f);
+  auto run = [&](pvec x0, pvec x1, pvec x2) {
+    prog_init(R, nin, zmask, x0, x1, x2);
+    return prog_run(pw, meta, R);
+  };
+  prog_each<DT, CPL, CPS>(d, t, run);
 }
 
 // COPY over a transposed view (DF_VIEW_T): out[b][r][c] = in[b][c * si + r]

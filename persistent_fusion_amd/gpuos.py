@@ -14,12 +14,12 @@ from typing import Callable, Dict, Iterable, List, Optional, Sequence
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libgpuos.so")
-ABI_VERSION = 4  # GPUOS_ABI_VERSION of the header this binding follows
+ABI_VERSION = 5  # GPUOS_ABI_VERSION of the header this binding follows
 
 # status codes
-OK, EINVAL, ENOMEM, EAGAIN, ETIMEDOUT, EDEVICE, ESTATE = 0, -1, -2, -3, -4, -5, -6
+OK, EINVAL, ENOMEM, EAGAIN, ETIMEDOUT, EDEVICE, ESTATE, ECOMPILE = 0, -1, -2, -3, -4, -5, -6, -7
 STATUS_NAMES = {0: "OK", -1: "EINVAL", -2: "ENOMEM", -3: "EAGAIN", -4: "ETIMEDOUT",
-                -5: "EDEVICE", -6: "ESTATE"}
+                -5: "EDEVICE", -6: "ESTATE", -7: "ECOMPILE"}
 
 OPCODES = {
     "nop": 0, "copy": 1, "gather": 2, "add": 3, "mul": 4, "scale": 5, "relu": 6, "exp": 7,
@@ -60,7 +60,8 @@ class GpuosStats(C.Structure):
     _fields_ = [(name, C.c_uint64) for name in (
         "ops_submitted", "ops_fused", "descs_published", "descs_completed", "flushes",
         "ring_full_waits", "deps_explicit", "deps_auto", "device_error", "error_desc",
-        "worker_waves", "compute_units", "kernel_ns", "launches", "lc_waves", "programs_lowered")]
+        "worker_waves", "compute_units", "kernel_ns", "launches", "lc_waves", "programs_lowered",
+        "programs_compiled", "kernel_switches")]
 
 
 class GpuosTraceRec(C.Structure):
@@ -90,7 +91,7 @@ assert C.sizeof(GpuosProgram) == 176
 assert C.sizeof(GpuosView) == 136
 assert C.sizeof(GpuosOp) == 128
 assert C.sizeof(GpuosConfig) == 64
-assert C.sizeof(GpuosStats) == 128
+assert C.sizeof(GpuosStats) == 144
 assert C.sizeof(GpuosTraceRec) == 40
 
 # Every symbol declared in include/gpuos.h and include/gpuos_debug.h.
@@ -99,9 +100,9 @@ EXPORTS = (
     "gpuos_submit", "gpuos_flush", "gpuos_sync", "gpuos_query", "gpuos_get_stats",
     "gpuos_trace_read", "gpuos_stop", "gpuos_destroy", "gpuos_baseline_run", "gpuos_submit_views",
     "gpuos_graph_create", "gpuos_graph_launch", "gpuos_graph_destroy", "gpuos_yield",
-    "gpuos_program_define", "gpuos_program_update",
+    "gpuos_program_define", "gpuos_program_update", "gpuos_program_compile",
     "gpuos_debug_read_desc", "gpuos_debug_published", "gpuos_debug_seq_of", "gpuos_debug_retire",
-    "gpuos_debug_tile_counts", "gpuos_create_static",
+    "gpuos_debug_tile_counts", "gpuos_create_static", "gpuos_debug_rtc_source",
 )
 
 _lib = None
@@ -134,6 +135,8 @@ def lib() -> C.CDLL:
         "gpuos_yield": (C.c_int, [P, C.c_int64]),
         "gpuos_program_define": (C.c_int, [P, C.POINTER(GpuosProgram), C.POINTER(C.c_uint32)]),
         "gpuos_program_update": (C.c_int, [P, C.c_uint32, C.POINTER(GpuosProgram)]),
+        "gpuos_program_compile": (C.c_int, [P, C.POINTER(C.c_uint32), C.c_uint32, C.c_uint32,
+                                            C.c_char_p, C.c_size_t]),
         "gpuos_destroy": (C.c_int, [P, C.c_int64]),
         "gpuos_baseline_run": (C.c_int, [C.c_int, C.POINTER(GpuosOp), C.c_uint32, C.c_int, P]),
         "gpuos_graph_create": (C.c_int, [C.c_int, C.POINTER(GpuosOp), C.c_uint32, C.c_int, C.POINTER(P)]),
@@ -144,6 +147,7 @@ def lib() -> C.CDLL:
         "gpuos_debug_seq_of": (C.c_int, [P, C.c_uint64, C.POINTER(C.c_int), C.POINTER(C.c_uint64)]),
         "gpuos_debug_retire": (C.c_int, [P, C.c_int, C.c_uint64]),
         "gpuos_debug_tile_counts": (C.c_int, [P, C.c_int, C.POINTER(C.c_uint32), C.c_uint32]),
+        "gpuos_debug_rtc_source": (C.c_size_t, [P, C.c_char_p, C.c_size_t]),
     }
     for name, (res, args) in sig.items():
         fn = getattr(L, name)
@@ -394,6 +398,29 @@ class Context:
         """gpuos_program_update: ops submitted from now on run the new body."""
         _check(self._lib.gpuos_program_update(self.handle, pid, C.byref(prog)), "gpuos_program_update")
 
+    def program_compile(self, ids: Optional[Sequence[int]] = None, dtypes: Sequence[str] = ()) -> str:
+        """gpuos_program_compile: builds the kernel variant holding the current
+        bodies of programs `ids` (None = all) for `dtypes` (empty = all float
+        types); returns the compiler's log."""
+        mask = 0
+        for dt in dtypes:
+            mask |= 1 << DTYPES[dt]
+        arr = None if ids is None else (C.c_uint32 * max(1, len(ids)))(*ids)
+        buf = C.create_string_buffer(1 << 16)
+        rc = self._lib.gpuos_program_compile(self.handle, arr, 0 if ids is None else len(ids), mask,
+                                             buf, len(buf))
+        log = buf.value.decode(errors="replace")
+        if rc < 0:
+            raise GpuosError(rc, "gpuos_program_compile" + (f" (log: {log[:2000]})" if log else ""))
+        return log
+
+    def rtc_source(self) -> str:
+        """The body source written by the last program_compile."""
+        n = self._lib.gpuos_debug_rtc_source(self.handle, None, 0)
+        buf = C.create_string_buffer(max(1, n))
+        self._lib.gpuos_debug_rtc_source(self.handle, buf, len(buf))
+        return buf.value.decode()
+
     def yield_gpu(self, timeout_s: float = 30.0) -> None:
         """gpuos_yield: let the resident kernel leave once the queue is done."""
         _check(self._lib.gpuos_yield(self.handle, int(timeout_s * 1e9)), "gpuos_yield")
@@ -482,5 +509,5 @@ def decode_desc(raw: bytes) -> dict:
     # PROGRAM descriptors
     d["pg"] = {"n_insns": w[26] & 31, "result": (w[26] >> 8) & 15, "n_inputs": (w[26] >> 16) & 3,
                "zero_mask": w[26] >> 24, "ins": list(w[27:43]),
-               "consts": list(struct.unpack("<8f", raw[43 * 4:51 * 4]))}
+               "consts": list(struct.unpack("<8f", raw[43 * 4:51 * 4])), "body": w[51]}
     return d

@@ -54,11 +54,15 @@ def addr_fn(tensors: Dict[str, "object"], wl: Workload):
 
 
 def submit_workload(ctx: gpuos.Context, wl: Workload, addr, groups=None, flush_each: bool = True,
-                    encoded=None) -> List[int]:
-    """Submits every group of the workload (flushing after each); returns the ids."""
+                    encoded=None, compile_programs: bool = False) -> List[int]:
+    """Submits every group of the workload (flushing after each); returns the
+    ids.  With compile_programs, the workload's programs are compiled
+    (gpuos_program_compile) before the first submission."""
     ids: List[int] = [0] * len(wl.ops)
     id_of = {}
     prog_ids = gpuos.define_programs(ctx, wl.ops) if encoded is None else None
+    if compile_programs and prog_ids:
+        ctx.program_compile()
     for gi, (g0, g1) in enumerate(groups or wl.groups):
         arr = encoded[gi] if encoded is not None else \
             gpuos.encode_ops(wl.ops, g0, g1, addr, id_of, prog_ids)
@@ -72,14 +76,18 @@ def submit_workload(ctx: gpuos.Context, wl: Workload, addr, groups=None, flush_e
 
 
 def run_resident(wl: Workload, device: int = 0, outputs: Optional[Iterable[str]] = None,
-                 tensors=None, timeout_s: float = 60.0, **cfg) -> Dict[str, np.ndarray]:
-    """Runs the workload on a fresh resident context and returns the outputs."""
+                 tensors=None, timeout_s: float = 60.0, compile_programs: bool = False,
+                 stats: Optional[dict] = None, **cfg) -> Dict[str, np.ndarray]:
+    """Runs the workload on a fresh resident context and returns the outputs
+    (the context's final counters go into `stats` if given)."""
     tensors = tensors if tensors is not None else to_device(wl, device)
     addr = addr_fn(tensors, wl)
     ctx = gpuos.Context(device, **cfg)
     try:
-        submit_workload(ctx, wl, addr)
+        submit_workload(ctx, wl, addr, compile_programs=compile_programs)
         ctx.sync(0, timeout_s)
+        if stats is not None:
+            stats.update(ctx.stats())
     finally:
         ctx.destroy()
     return download(tensors, wl, outputs or wl.outputs)

@@ -38,13 +38,13 @@ def test_library_exports_every_declared_symbol():
     declared = set()
     for h in ("gpuos.h", "gpuos_debug.h"):
         text = open(os.path.join(ROOT, "include", h)).read()
-        declared |= set(re.findall(r"^(?:int|void|uint64_t|const char\*)\s+(gpuos_[a-z_]+)\(",
+        declared |= set(re.findall(r"^(?:int|void|uint64_t|size_t|const char\*)\s+(gpuos_[a-z_]+)\(",
                                    text, re.M))
     lib = gpuos.lib()
     missing = [s for s in sorted(declared) if not hasattr(lib, s)]
     assert not missing, missing
     assert set(gpuos.EXPORTS) == declared
-    assert lib.gpuos_abi_version() == 4 == gpuos.ABI_VERSION
+    assert lib.gpuos_abi_version() == 5 == gpuos.ABI_VERSION
 
 
 def test_fused_chain_becomes_one_descriptor():
