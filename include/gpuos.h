@@ -218,9 +218,8 @@ typedef struct gpuos_config {
                              in [4, 32]; default 8 */
   uint32_t tile_elems;    /* elementwise tile in elements, multiple of 256;
                              default 1024 (one memory round trip per wave) */
-  uint32_t be_tile_elems; /* tile for ops of 1<<24 elements or more (bounds
-                             how long a priority op waits for a free wave);
-                             default 16384 */
+  uint32_t be_tile_elems; /* tile for ops of 1<<24 elements or more, multiple
+                             of 256 in [256, 1<<22]; default 32768 */
   uint32_t fusion;        /* 1 = merge adjacent elementwise ops (default),
                              2 = off */
   uint32_t auto_deps;     /* 1 = add hazard dependencies (default), 2 = off */

@@ -888,12 +888,15 @@ uint32_t ceil_div(uint64_t a, uint64_t b) { return (uint32_t)((a + b - 1) / b); 
 // elements or more.  Large ops are cut into whole rounds over the worker
 // waves (every wave gets the same number of tiles).  An op below 2^24
 // elements that is big enough to give every wave 1024 elements is spread over
-// all of them; an op of 2^24 or more with fewer be_tile_elems tiles than
-// waves keeps its tiles in the resident kernel (several such ops then run side
-// by side on different waves, each tile streaming longer between its
-// completion counts) and is spread like the others with `spread` (one launch
-// per op, where the op is the only kernel running).  Tiles stay a multiple of
-// 64 elements so every tile starts 16-byte aligned.
+// all of them.  An op of 2^24 or more with fewer be_tile_elems tiles than
+// waves keeps its larger tiles in the resident kernel (several such ops then
+// run side by side on different waves, each tile streaming longer between
+// its completion counts), with the tile count cut to a whole fraction of a
+// round: k = ceil(workers / tiles) such ops fill one round, so consecutive
+// ops leave no wave a tile more than the others (tiles are dealt
+// round-robin); with `spread` (one launch per op, where the op is the only
+// kernel running) it is spread like the others.  Tiles stay a multiple of 64
+// elements so every tile starts 16-byte aligned.
 uint32_t ew_tile_elems(const gpuos_config& cfg, uint32_t workers, uint64_t n, bool spread = false) {
   const bool big = n >= (1ull << 24);
   uint64_t tile = big ? cfg.be_tile_elems : cfg.tile_elems;
@@ -901,6 +904,7 @@ uint32_t ew_tile_elems(const gpuos_config& cfg, uint32_t workers, uint64_t n, bo
   if (workers) {
     if (nt < workers) {
       if ((!big || spread) && n >= (uint64_t)workers * 1024) nt = workers;
+      else if (big) nt = workers / ((workers + nt - 1) / nt);
     } else {
       nt = (nt + workers - 1) / workers * workers;
     }
@@ -2306,7 +2310,7 @@ void gpuos_config_default(gpuos_config* cfg) {
   cfg->ring_slots = 65536;
   cfg->waves_per_cu = 8;
   cfg->tile_elems = 1024;
-  cfg->be_tile_elems = 16384;
+  cfg->be_tile_elems = 32768;
   cfg->fusion = 1;
   cfg->auto_deps = 1;
   cfg->trace = 2;
