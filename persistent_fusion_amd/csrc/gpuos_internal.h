@@ -215,7 +215,7 @@ static_assert(offsetof(DevDesc, check) == 63 * 4, "check word is dword 63");
 // Device-side scheduler state (device memory).  Hot words sit on their own
 // 256-byte lines.
 struct alignas(256) DevRing {
-  uint64_t next;        // latency-critical ring: next ticket to claim (CAS)
+  uint64_t next;        // latency-critical ring: descriptors claimed (CAS)
   uint64_t _p0[31];
   uint64_t retired;     // in-order retire cursor
   uint64_t _p1[31];

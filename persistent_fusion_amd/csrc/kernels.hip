@@ -380,32 +380,32 @@ __device__ __forceinline__ void read_avail(const AvailLine* l, uint64_t& tiles, 
   copied = bcast64(k);
 }
 
-// Latency-critical ring: served only by the reserved waves, which claim its
-// tiles with compare-and-swap (a wave never holds a priority ticket with no
-// work behind it).  Drains the ring; `seen` is the published count at which
-// this wave last found it empty.
-__device__ __forceinline__ void service_lc(const KArgs& a, const AvailLine* line, Cached& c, uint64_t& seen) {
+// Latency-critical ring: served only by the reserved waves, which take its
+// descriptors straight from the host: a wave reads the host's ring tail
+// (pinned memory) and the claim cursor in one round trip, claims the next
+// descriptor with one compare-and-swap, reading it from the pinned host ring
+// in the same round trip (its slot does not change before it retires), and
+// runs all its tiles
+// itself (the host plans small latency-critical ops as one tile).  The
+// doorbell wave still publishes and retires the ring in order, but is not on
+// this path.  Drains the ring.
+__device__ __forceinline__ void service_lc(const KArgs& a, Cached& c) {
   DevRing* R = &a.dctl->ring[1];
   for (;;) {
-    uint64_t av = 0;
-    if (lane_id() == 0) av = ld_rlx_agent(&line->avail_tiles);
-    av = bcast64(av);
-    if (av == seen) return;
-    // after avail_tiles has returned: the claim cursor, and avail_ops (stored
-    // before avail_tiles, so it covers every descriptor below av) and the
-    // copied frontier, all in one round trip
-    uint64_t nxt = 0, ops = 0, copied = 0;
+    uint64_t tail = 0, nxt = 0;
     if (lane_id() == 0) {
-      wait_mem();
+      tail = ld_rlx_sys(&a.hctl->tail[1]);
       nxt = ld_rlx_agent(&R->next);
-      ops = ld_rlx_agent(&line->avail_ops);
-      copied = ld_rlx_agent(&line->copied_ops);
     }
+    tail = bcast64(tail);
     nxt = bcast64(nxt);
-    if (nxt >= av) {
-      seen = av;
-      return;
-    }
+    if (nxt >= tail) return;
+    // the descriptor is read in the same round trip as the claim (the host
+    // stored it before the tail this wave has read); it is used only if the
+    // claim succeeds
+    const uint64_t seq = nxt + 1;
+    const rsrc_t r = make_rsrc(reinterpret_cast<uint64_t>(&a.hdesc[1][slot_of(seq, a.cap_mask)]));
+    const uint32_t dw = ld32<CP_SYSTEM>(r, 4u * lane_id());
     uint32_t ok = 0;
     if (lane_id() == 0) {
       uint64_t expect = nxt;
@@ -415,20 +415,32 @@ __device__ __forceinline__ void service_lc(const KArgs& a, const AvailLine* line
                : 0u;
     }
     if (!bcast(ok)) continue;
-    map_ticket<1>(a, nxt, bcast64(ops), bcast64(copied), line, c);
-    run_ticket<1>(a, nxt, c);
+    const VDesc f{dw};
+    if (f.q(4) != seq || f(63) != ((uint32_t)seq ^ kDescMagic)) report_error(a, 1, seq, DERR_DESC_CHECK);
+    install_desc(c, seq, dw);
+    for (uint64_t t = c.start; t < c.end; ++t) run_ticket<1>(a, t, c);
   }
 }
 
 // A reserved wave: serves the latency-critical ring until the launch ends
-// (at which point every published descriptor has retired).
+// (at which point every published descriptor has retired).  It takes no
+// descriptor before the whole grid has checked in.
 __device__ __forceinline__ void lc_loop(const KArgs& a, uint32_t w, lds_u32* slot1, lds_f32* scr) {
   const AvailLine* line0 = &a.dctl->avail[0][w % kReplicas];
-  const AvailLine* line1 = &a.dctl->avail[1][w % kReplicas];
   Cached c1{0, 0, 0, slot1, 0, scr, w % kDoneReplicas};
-  uint64_t seen = 0;
+  const uint64_t want = (uint64_t)a.epoch * gridDim.x * 4u;
   for (;;) {
-    service_lc(a, line1, c1, seen);
+    uint64_t got = 0, se = 0;
+    if (lane_id() == 0) {
+      got = ld_rlx_agent(&a.dctl->arrived);
+      se = ld_rlx_agent(&line0->stop_epoch);
+    }
+    if (bcast64(got) >= want) break;
+    if (bcast64(se) == a.epoch) return;
+    __builtin_amdgcn_s_sleep(8);
+  }
+  for (;;) {
+    service_lc(a, c1);
     uint64_t se = 0;
     if (lane_id() == 0) se = ld_rlx_agent(&line0->stop_epoch);
     if (bcast64(se) == a.epoch) return;

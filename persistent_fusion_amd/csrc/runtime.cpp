@@ -1119,6 +1119,22 @@ void encode_program(const ProgCode& pc, DevDesc& d) {
   for (int j = 0; j < 8; ++j) d.pg.k[j] = pc.k[j];
 }
 
+// A latency-critical op is run by the one reserved wave that claims its
+// descriptor, tile after tile; a small elementwise, COPY, fused or PROGRAM
+// op (plain layout, up to 2^16 elements) becomes a single tile, which that
+// wave streams with its loads pipelined and completes without a counter.
+constexpr uint32_t kLcOneTileElems = 1u << 16;
+
+void one_tile_if_small(DevDesc& d) {
+  if (d.flags & DF_VIEW) return;
+  const bool stream = d.opcode == OP_FUSED_EW || d.opcode == GPUOS_OP_PROGRAM ||
+                      (is_elementwise(d.opcode) && d.opcode != GPUOS_OP_GATHER);
+  if (stream && d.n <= kLcOneTileElems) {
+    d.tile = d.n;
+    d.ntiles = 1;
+  }
+}
+
 // Streams (non-temporal) elementwise, COPY, fused and PROGRAM descriptors
 // whose operands total at least stream_min_kib.
 void mark_streaming(const gpuos_config& cfg, DevDesc& d) {
@@ -1644,6 +1660,7 @@ void plan_ops(gpuos_ctx* c, size_t begin, size_t end, std::vector<Planned>& plan
       j = i + 1;
     }
     mark_streaming(cfg, pl.desc);
+    if (pl.ring == 1) one_tile_if_small(pl.desc);
     // dependencies: union of the members' deps that point outside the group
     const uint64_t gfirst = c->staged[i].id, glast = c->staged[i + pl.count - 1].id;
     for (uint32_t k = 0; k < pl.count; ++k)

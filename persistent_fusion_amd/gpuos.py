@@ -319,12 +319,20 @@ class Context:
                                                  C.byref(h)), "gpuos_create_static")
         self.handle = h
         self.device = device
+        self._submit = self._lib.gpuos_submit
+        self._query = self._lib.gpuos_query
+        self._id1 = (C.c_uint64 * 1)()
 
     def submit(self, ops, n: Optional[int] = None, views=None) -> List[int]:
         """Submits ops (and, optionally, a GpuosView array: gpuos_submit_views)."""
         if isinstance(ops, GpuosOp):
             ops = (GpuosOp * 1)(ops)
         n = len(ops) if n is None else n
+        if n == 1 and views is None:  # one op: no per-call id array
+            rc = self._submit(self.handle, ops, 1, self._id1)
+            if rc < 0:
+                raise GpuosError(rc, "gpuos_submit")
+            return [self._id1[0]]
         ids = (C.c_uint64 * max(n, 1))()
         if views is not None:
             _check(self._lib.gpuos_submit_views(self.handle, ops, views, n, ids), "gpuos_submit_views")
@@ -343,7 +351,10 @@ class Context:
         _check(self._lib.gpuos_sync(self.handle, upto, t), "gpuos_sync")
 
     def query(self, op_id: int) -> bool:
-        return _check(self._lib.gpuos_query(self.handle, op_id), "gpuos_query") == 1
+        rc = self._query(self.handle, op_id)
+        if rc < 0:
+            raise GpuosError(rc, "gpuos_query")
+        return rc == 1
 
     def stats(self) -> dict:
         s = GpuosStats()
