@@ -483,8 +483,7 @@ def priority_leg(device=0, rounds=200):
             if prio == 2:
                 a[0].flags &= ~gpuos.FLAG_LC
             s0 = time.perf_counter()
-            oid = ctx.submit(a, 1)[0]
-            ctx.flush()
+            oid = ctx.submit(a, 1, flush=True)[0]
             while not ctx.query(oid):
                 pass
             lat.append(time.perf_counter() - s0)

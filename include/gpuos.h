@@ -43,7 +43,7 @@
 extern "C" {
 #endif
 
-#define GPUOS_ABI_VERSION 5
+#define GPUOS_ABI_VERSION 6
 
 /* Status codes. */
 typedef enum gpuos_status {
@@ -416,6 +416,14 @@ int gpuos_submit_views(gpuos_ctx* ctx, const gpuos_op* ops, const gpuos_view* vi
  * Errors: EDEVICE (context poisoned), EAGAIN.
  */
 int gpuos_flush(gpuos_ctx* ctx);
+
+/*
+ * gpuos_submit followed by gpuos_flush in one call, for callers whose ops
+ * must start at once (a latency-critical op submitted alone): the same
+ * validation, ids and errors as gpuos_submit, then the flush's.  If the submit
+ * fails nothing is flushed; if the flush fails the ops stay staged.
+ */
+int gpuos_submit_flush(gpuos_ctx* ctx, const gpuos_op* ops, uint32_t n, uint64_t* ids_out);
 
 /*
  * Flushes, then blocks until every op with id <= upto has completed

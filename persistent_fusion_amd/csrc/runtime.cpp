@@ -2681,6 +2681,12 @@ int gpuos_flush(gpuos_ctx* c) {
   return flush_impl(c);
 }
 
+int gpuos_submit_flush(gpuos_ctx* c, const gpuos_op* ops, uint32_t n, uint64_t* ids_out) {
+  const int rc = submit_impl(c, ops, nullptr, n, ids_out);
+  if (rc) return rc;
+  return gpuos_flush(c);
+}
+
 int gpuos_sync(gpuos_ctx* c, uint64_t upto, int64_t timeout_ns) {
   if (!c) return fail(GPUOS_EINVAL, "null context");
   if (c->exited) return check_device_error(c) ? GPUOS_EDEVICE : 0;

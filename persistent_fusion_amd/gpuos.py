@@ -14,7 +14,7 @@ from typing import Callable, Dict, Iterable, List, Optional, Sequence
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libgpuos.so")
-ABI_VERSION = 5  # GPUOS_ABI_VERSION of the header this binding follows
+ABI_VERSION = 6  # GPUOS_ABI_VERSION of the header this binding follows
 
 # status codes
 OK, EINVAL, ENOMEM, EAGAIN, ETIMEDOUT, EDEVICE, ESTATE, ECOMPILE = 0, -1, -2, -3, -4, -5, -6, -7
@@ -97,7 +97,7 @@ assert C.sizeof(GpuosTraceRec) == 40
 # Every symbol declared in include/gpuos.h and include/gpuos_debug.h.
 EXPORTS = (
     "gpuos_abi_version", "gpuos_last_error", "gpuos_config_default", "gpuos_create",
-    "gpuos_submit", "gpuos_flush", "gpuos_sync", "gpuos_query", "gpuos_get_stats",
+    "gpuos_submit", "gpuos_flush", "gpuos_submit_flush", "gpuos_sync", "gpuos_query", "gpuos_get_stats",
     "gpuos_trace_read", "gpuos_stop", "gpuos_destroy", "gpuos_baseline_run", "gpuos_submit_views",
     "gpuos_graph_create", "gpuos_graph_launch", "gpuos_graph_destroy", "gpuos_yield",
     "gpuos_program_define", "gpuos_program_update", "gpuos_program_compile",
@@ -127,6 +127,7 @@ def lib() -> C.CDLL:
         "gpuos_submit_views": (C.c_int, [P, C.POINTER(GpuosOp), C.POINTER(GpuosView), C.c_uint32,
                                          C.POINTER(C.c_uint64)]),
         "gpuos_flush": (C.c_int, [P]),
+        "gpuos_submit_flush": (C.c_int, [P, C.POINTER(GpuosOp), C.c_uint32, C.POINTER(C.c_uint64)]),
         "gpuos_sync": (C.c_int, [P, C.c_uint64, C.c_int64]),
         "gpuos_query": (C.c_int, [P, C.c_uint64]),
         "gpuos_get_stats": (C.c_int, [P, C.POINTER(GpuosStats)]),
@@ -320,24 +321,32 @@ class Context:
         self.handle = h
         self.device = device
         self._submit = self._lib.gpuos_submit
+        self._submit_flush = self._lib.gpuos_submit_flush
         self._query = self._lib.gpuos_query
         self._id1 = (C.c_uint64 * 1)()
 
-    def submit(self, ops, n: Optional[int] = None, views=None) -> List[int]:
-        """Submits ops (and, optionally, a GpuosView array: gpuos_submit_views)."""
+    def submit(self, ops, n: Optional[int] = None, views=None, flush: bool = False) -> List[int]:
+        """Submits ops (and, optionally, a GpuosView array: gpuos_submit_views);
+        with flush, also flushes in the same call (gpuos_submit_flush)."""
         if isinstance(ops, GpuosOp):
             ops = (GpuosOp * 1)(ops)
         n = len(ops) if n is None else n
         if n == 1 and views is None:  # one op: no per-call id array
-            rc = self._submit(self.handle, ops, 1, self._id1)
+            rc = (self._submit_flush if flush else self._submit)(self.handle, ops, 1, self._id1)
             if rc < 0:
-                raise GpuosError(rc, "gpuos_submit")
+                raise GpuosError(rc, "gpuos_submit_flush" if flush else "gpuos_submit")
             return [self._id1[0]]
+        if flush and views is None:
+            ids = (C.c_uint64 * max(n, 1))()
+            _check(self._submit_flush(self.handle, ops, n, ids), "gpuos_submit_flush")
+            return list(ids[:n])
         ids = (C.c_uint64 * max(n, 1))()
         if views is not None:
             _check(self._lib.gpuos_submit_views(self.handle, ops, views, n, ids), "gpuos_submit_views")
         else:
             _check(self._lib.gpuos_submit(self.handle, ops, n, ids), "gpuos_submit")
+        if flush:
+            self.flush()
         return list(ids[:n])
 
     def submit_noids(self, ops, n: int) -> None:

@@ -44,7 +44,7 @@ def test_library_exports_every_declared_symbol():
     missing = [s for s in sorted(declared) if not hasattr(lib, s)]
     assert not missing, missing
     assert set(gpuos.EXPORTS) == declared
-    assert lib.gpuos_abi_version() == 5 == gpuos.ABI_VERSION
+    assert lib.gpuos_abi_version() == 6 == gpuos.ABI_VERSION
 
 
 def test_fused_chain_becomes_one_descriptor():
@@ -883,3 +883,20 @@ def test_chain_programs_lower_to_builtin_descriptors():
         c.submit((gpuos.GpuosOp * 1)(_prog_op(pid)))
         c.flush()
         assert desc(c, 1)["opcode"] == gpuos.OPCODES["program"]
+
+
+def test_submit_flush_publishes_in_the_same_call():
+    """gpuos_submit_flush: the ids of gpuos_submit, and the ops published as
+    by gpuos_flush; a failed submit publishes nothing."""
+    with ctx() as c:
+        a, b, y = buf(0), buf(1), buf(2)
+        ids = c.submit(make_op("add", y, [a, b], n=4096), flush=True)
+        assert ids == [1] and c.published(0) == 1
+        two = (gpuos.GpuosOp * 2)(make_op("relu", buf(3), [buf(6)], n=4096, flags=gpuos.FLAG_LC),
+                                  make_op("mul", buf(4), [a, b], n=4096))
+        assert c.submit(two, flush=True) == [2, 3]
+        assert c.published(0) == 2 and c.published(1) == 1
+        bad = (gpuos.GpuosOp * 1)(make_op("add", buf(5), [a, b], n=0))
+        with pytest.raises(GpuosError, match="EINVAL"):
+            c.submit(bad, flush=True)
+        assert c.published(0) == 2 and c.published(1) == 1
