@@ -177,6 +177,13 @@ _VIEW_CASES = {
     # batched: x.transpose(1, 2) of a contiguous [3, 136, 72] input, copied out
     "transpose_read_batched": ((3, 72, 136), (72 * 136, 136, 1), (72 * 136, 1, 72), (0, 0, 0),
                                3 * 72 * 136, 0, 3 * 72 * 136),
+    # batched with ragged batch strides (one element past the batch's size, in
+    # and out): the first batch's input columns are 16-byte aligned and the
+    # others' are not, and the output's 16-bit pairs shift between batches, so
+    # the batches of one descriptor take different paths
+    "transpose_read_batched_ragged": ((3, 72, 136), (72 * 136 + 1, 136, 1), (72 * 136 + 1, 1, 72),
+                                      (0, 0, 0), 2 * (72 * 136 + 1) + 72 * 136, 0,
+                                      2 * (72 * 136 + 1) + 72 * 136),
     # odd strides: misaligned input columns and output pairs, element by element
     "transpose_read_odd": ((70, 33), (33, 1), (1, 70), (0, 0), 70 * 33, 0, 70 * 33),
     "outer": ((50, 64), (64, 1), (1, 0), (0, 1), 50, 64, 50 * 64),
