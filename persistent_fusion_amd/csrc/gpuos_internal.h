@@ -274,8 +274,17 @@ struct alignas(256) HostCtl {
   uint64_t error_seq;         // device: (ring << 62) | sequence that raised it
   uint64_t yield_req;         // host: nonzero asks a drained kernel to leave
                               // at once, as after its idle period
-  uint64_t _p2[28];
+  uint64_t _p2[4];
+  uint64_t lc_tail;           // host: tail[1] again, on a 64-byte line of its
+                              // own: the reserved waves poll it, so the line
+                              // the host writes at every flush and the
+                              // doorbell polls is not also read by them
+  uint64_t _p3[23];
 };
+static_assert(sizeof(HostCtl) == 768, "host control block is three 256-byte groups");
+static_assert(offsetof(HostCtl, lc_tail) % 64 == 0 && offsetof(HostCtl, lc_tail) / 64 != 0 &&
+                  offsetof(HostCtl, lc_tail) / 64 != offsetof(HostCtl, stop_req) / 64,
+              "the latency-critical tail has a 64-byte line of its own");
 
 // Per-descriptor trace record (device memory), one per ring slot.
 struct TraceRec {

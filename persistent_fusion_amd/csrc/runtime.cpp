@@ -1805,6 +1805,7 @@ int wait_ring_space(gpuos_ctx* c, uint32_t ring, uint64_t seq) {
   // make what is already written visible so the device can drain it
   if (c->tail_written[ring] != c->pub_seq[ring]) {
     store_rel(&c->hctl->tail[ring], c->pub_seq[ring]);
+    if (ring == 1) store_rel(&c->hctl->lc_tail, c->pub_seq[1]);
     c->tail_written[ring] = c->pub_seq[ring];
   }
   uint32_t spins = 0;
@@ -1827,6 +1828,7 @@ void publish_tail(gpuos_ctx* c, uint32_t ring) {
   if (c->tail_written[ring] == c->pub_seq[ring]) return;
   std::atomic_thread_fence(std::memory_order_release);
   store_rel(&c->hctl->tail[ring], c->pub_seq[ring]);
+  if (ring == 1) store_rel(&c->hctl->lc_tail, c->pub_seq[1]);
   c->tail_written[ring] = c->pub_seq[ring];
 }
 
