@@ -243,10 +243,30 @@ def queue_leg(reps_n, device=0):
             "per_op_launch_us_per_op": round(bmed / n_ops * 1e6, 2),
             "resident_trace": gaps,
             "resident_us_per_queue_median": round(med * 1e6, 1),
+            "resident_us_per_queue_p10_p90": [round(_pct(times, 0.1) * 1e6, 1), round(_pct(times, 0.9) * 1e6, 1)],
             "per_op_launch_us_per_queue_median": round(bmed * 1e6, 1),
+            "per_op_launch_us_per_queue_p10_p90": [round(_pct(btimes, 0.1) * 1e6, 1),
+                                                   round(_pct(btimes, 0.9) * 1e6, 1)],
             "effective_gb_per_s": round(wl.meta["bytes"] / med / 1e9, 1),
             "roofline": {"bound": "latency (16 MB working set, cache-resident)",
                          "frac_of_hbm_peak": _frac(wl.meta["bytes"] / med / 1e9)}}
+
+
+def _pct(xs, q):
+    """The q-quantile of xs (nearest rank)."""
+    v = sorted(xs)
+    return v[min(len(v) - 1, int(q * len(v)))]
+
+
+def launch_rate_leg(device=0, n=10000):
+    """The pages' launch-overhead measurement, in C++ HIP: an empty kernel
+    launched n times back to back (host time per launch), and n times each
+    followed by a stream synchronize (time per launch-and-wait round trip)."""
+    from persistent_fusion_amd import gpuos
+
+    a, s = gpuos.launch_overhead(device, n)
+    return {"kernel": "empty kernel, one wave", "launches": n,
+            "us_per_launch_back_to_back": round(a, 2), "us_per_launch_and_sync": round(s, 2)}
 
 
 class _NoIds(dict):
@@ -957,6 +977,7 @@ def main():
     torch.cuda.synchronize()
     fc = fused_chain_leg(args.steps, args.warmup, warm_s=args.device_warmup_s)
     cp = copy_leg()
+    lr = launch_rate_leg()
     names = ("queue", "decode", "dag", "priority") if args.configs == "all" else \
         tuple(x for x in args.configs.split(",") if x)
     cfgs = {}
@@ -1033,6 +1054,7 @@ def main():
         "graph_replay": fc["baselines"]["graph_replay"],
         "graph_replay_fused": fc["baselines"]["graph_replay_fused"],
         "plain_copy_kernel": cp,
+        "launch_overhead": lr,
         "configs": cfgs,
         **({"extra_configs": extra} if extra else {}),
         "cpu_baseline": cpu,

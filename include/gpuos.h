@@ -43,7 +43,7 @@
 extern "C" {
 #endif
 
-#define GPUOS_ABI_VERSION 6
+#define GPUOS_ABI_VERSION 7
 
 /* Status codes. */
 typedef enum gpuos_status {
@@ -664,6 +664,18 @@ typedef struct gpuos_graph gpuos_graph;
 int gpuos_graph_create(int device, const gpuos_op* ops, uint32_t n, int fuse, gpuos_graph** out);
 int gpuos_graph_launch(gpuos_graph* g, void* stream);
 int gpuos_graph_destroy(gpuos_graph* g);
+
+/*
+ * Launch-rate measurement ("Kernel Launch and Host-Device Interaction",
+ * section "The launch path": each launch writes a packet into a queue and
+ * rings a doorbell, a few microseconds per launch).  On device `device`, an
+ * empty kernel (one workgroup of one wave) is launched n times back to back
+ * on a new stream and then waited for once (*async_us: host time per launch),
+ * then n times each followed by hipStreamSynchronize (*sync_us: time per
+ * launch-and-wait round trip); both from std::chrono::steady_clock, after 100
+ * untimed launches.  Errors: EINVAL (n = 0 or a null output), EDEVICE.
+ */
+int gpuos_launch_overhead(int device, uint32_t n, double* async_us, double* sync_us);
 
 /*
  * Gives the GPU back to other work: waits (up to timeout_ns, < 0 = forever)

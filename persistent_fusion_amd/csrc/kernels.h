@@ -15,6 +15,9 @@ hipError_t launch_resident(const KArgs& a, uint32_t blocks, hipStream_t s);
 // (device memory, nullable) receives a device error code if a tile fails.
 hipError_t launch_single(const DevDesc& d, uint32_t* err, hipStream_t s);
 
+// Launches an empty kernel (one wave) on stream s.
+hipError_t launch_empty(hipStream_t s);
+
 // The resident kernel's function handle (for occupancy queries).
 const void* resident_kernel();
 

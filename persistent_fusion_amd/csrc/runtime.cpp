@@ -3028,6 +3028,36 @@ int gpuos_graph_destroy(gpuos_graph* g) {
   return rc;
 }
 
+int gpuos_launch_overhead(int device, uint32_t n, double* async_us, double* sync_us) {
+  if (n == 0 || !async_us || !sync_us) return fail(GPUOS_EINVAL, "launch_overhead: n = 0 or a null output");
+  HIP_TRY(hipSetDevice(device));
+  hipStream_t s = nullptr;
+  HIP_TRY(hipStreamCreateWithFlags(&s, hipStreamNonBlocking));
+  int rc = 0;
+  auto run = [&]() -> int {
+    for (int i = 0; i < 100; ++i)
+      if (launch_empty(s) != hipSuccess) return fail(GPUOS_EDEVICE, "empty kernel launch failed");
+    if (hipStreamSynchronize(s) != hipSuccess) return fail(GPUOS_EDEVICE, "stream synchronize failed");
+    auto t0 = std::chrono::steady_clock::now();
+    for (uint32_t i = 0; i < n; ++i)
+      if (launch_empty(s) != hipSuccess) return fail(GPUOS_EDEVICE, "empty kernel launch failed");
+    if (hipStreamSynchronize(s) != hipSuccess) return fail(GPUOS_EDEVICE, "stream synchronize failed");
+    auto t1 = std::chrono::steady_clock::now();
+    *async_us = std::chrono::duration<double, std::micro>(t1 - t0).count() / n;
+    t0 = std::chrono::steady_clock::now();
+    for (uint32_t i = 0; i < n; ++i) {
+      if (launch_empty(s) != hipSuccess) return fail(GPUOS_EDEVICE, "empty kernel launch failed");
+      if (hipStreamSynchronize(s) != hipSuccess) return fail(GPUOS_EDEVICE, "stream synchronize failed");
+    }
+    t1 = std::chrono::steady_clock::now();
+    *sync_us = std::chrono::duration<double, std::micro>(t1 - t0).count() / n;
+    return 0;
+  };
+  rc = run();
+  (void)hipStreamDestroy(s);
+  return rc;
+}
+
 // ---------------------------------------------------------------------------
 // debug hooks
 

@@ -37,4 +37,13 @@ hipError_t launch_single(const DevDesc& d, uint32_t* err, hipStream_t s) {
   return hipGetLastError();
 }
 
+// An empty kernel: one workgroup of one wave that does nothing, so that a
+// launch measures the launch path alone.
+__global__ __launch_bounds__(64) void gpuos_empty() {}
+
+hipError_t launch_empty(hipStream_t s) {
+  hipLaunchKernelGGL(gpuos_empty, dim3(1), dim3(64), 0, s);
+  return hipGetLastError();
+}
+
 }  // namespace gpuos

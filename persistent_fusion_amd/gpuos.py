@@ -14,7 +14,7 @@ from typing import Callable, Dict, Iterable, List, Optional, Sequence
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libgpuos.so")
-ABI_VERSION = 6  # GPUOS_ABI_VERSION of the header this binding follows
+ABI_VERSION = 7  # GPUOS_ABI_VERSION of the header this binding follows
 
 # status codes
 OK, EINVAL, ENOMEM, EAGAIN, ETIMEDOUT, EDEVICE, ESTATE, ECOMPILE = 0, -1, -2, -3, -4, -5, -6, -7
@@ -100,6 +100,7 @@ EXPORTS = (
     "gpuos_submit", "gpuos_flush", "gpuos_submit_flush", "gpuos_sync", "gpuos_query", "gpuos_get_stats",
     "gpuos_trace_read", "gpuos_stop", "gpuos_destroy", "gpuos_baseline_run", "gpuos_submit_views",
     "gpuos_graph_create", "gpuos_graph_launch", "gpuos_graph_destroy", "gpuos_yield",
+    "gpuos_launch_overhead",
     "gpuos_program_define", "gpuos_program_update", "gpuos_program_compile",
     "gpuos_debug_read_desc", "gpuos_debug_published", "gpuos_debug_seq_of", "gpuos_debug_retire",
     "gpuos_debug_tile_counts", "gpuos_create_static", "gpuos_debug_rtc_source",
@@ -143,6 +144,7 @@ def lib() -> C.CDLL:
         "gpuos_graph_create": (C.c_int, [C.c_int, C.POINTER(GpuosOp), C.c_uint32, C.c_int, C.POINTER(P)]),
         "gpuos_graph_launch": (C.c_int, [P, P]),
         "gpuos_graph_destroy": (C.c_int, [P]),
+        "gpuos_launch_overhead": (C.c_int, [C.c_int, C.c_uint32, C.POINTER(C.c_double), C.POINTER(C.c_double)]),
         "gpuos_debug_read_desc": (C.c_int, [P, C.c_int, C.c_uint64, P]),
         "gpuos_debug_published": (C.c_uint64, [P, C.c_int]),
         "gpuos_debug_seq_of": (C.c_int, [P, C.c_uint64, C.POINTER(C.c_int), C.POINTER(C.c_uint64)]),
@@ -459,6 +461,14 @@ class Context:
     def __exit__(self, *exc):
         self.destroy()
         return False
+
+
+def launch_overhead(device: int, n: int = 10000):
+    """gpuos_launch_overhead: (host us per back-to-back empty-kernel launch,
+    us per launch followed by a stream synchronize)."""
+    a, s = C.c_double(), C.c_double()
+    _check(lib().gpuos_launch_overhead(device, n, C.byref(a), C.byref(s)), "gpuos_launch_overhead")
+    return a.value, s.value
 
 
 def baseline_run(device: int, ops, n: Optional[int] = None, fuse: bool = False,

@@ -44,7 +44,7 @@ def test_library_exports_every_declared_symbol():
     missing = [s for s in sorted(declared) if not hasattr(lib, s)]
     assert not missing, missing
     assert set(gpuos.EXPORTS) == declared
-    assert lib.gpuos_abi_version() == 6 == gpuos.ABI_VERSION
+    assert lib.gpuos_abi_version() == 7 == gpuos.ABI_VERSION
 
 
 def test_fused_chain_becomes_one_descriptor():
