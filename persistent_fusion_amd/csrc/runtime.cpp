@@ -23,6 +23,7 @@
 #include <deque>
 #include <map>
 #include <memory>
+#include <unordered_map>
 #include <mutex>
 #include <string>
 #include <thread>
@@ -557,6 +558,9 @@ int normalize_view(const gpuos_op& o, const gpuos_view& v, uint32_t index, ViewD
 // written (inputs uploaded before the queue) go to merged read spans, so
 // reading many different prefixes of one buffer costs no segments.  A write
 // depends on the writers and readers of every segment and span it overlaps.
+// An index from each segment's first byte to the segment serves the common
+// accesses, which start exactly at a segment (reading or rewriting a whole
+// earlier output), without a search of the ordered map.
 
 typedef SmallVec<uint64_t, 4> Readers;
 
@@ -588,10 +592,12 @@ class HazardMap {
       WSeg& sg = it->second;
       if (sg.writer && retired(sg.writer)) sg.writer = 0;
       sg.readers.remove_if(retired);
-      if (!sg.writer && sg.readers.empty())
+      if (!sg.writer && sg.readers.empty()) {
+        wi_.erase(it->first);
         it = w_.erase(it);
-      else
+      } else {
         ++it;
+      }
     }
     for (auto it = r_.begin(); it != r_.end();) {
       it->second.readers.remove_if(retired);
@@ -605,6 +611,7 @@ class HazardMap {
   size_t size() const { return w_.size() + r_.size(); }
   void clear() {
     w_.clear();
+    wi_.clear();
     r_.clear();
   }
 
@@ -630,6 +637,13 @@ class HazardMap {
 
   template <class Retired>
   void do_read(const Range& rg, uint64_t id, DepVec& deps, Retired retired) {
+    const auto f = wi_.find(rg.lo);
+    if (f != wi_.end() && f->second->second.hi >= rg.hi) {  // inside one segment
+      WSeg& sg = f->second->second;
+      if (sg.writer && !retired(sg.writer)) deps.push_back(sg.writer);
+      add_reader(sg.readers, id, retired);
+      return;
+    }
     uint64_t cur = rg.lo;
     bool gap = false;
     for (auto it = first_overlap(w_, rg.lo); it != w_.end() && it->first < rg.hi; ++it) {
@@ -678,10 +692,10 @@ class HazardMap {
       else
         ++it;
     }
-    auto it = w_.lower_bound(rg.lo);
-    if (it != w_.end() && it->first == rg.lo && it->second.hi == rg.hi) {
+    const auto f = wi_.find(rg.lo);
+    if (f != wi_.end() && f->second->second.hi == rg.hi) {
       // exactly one segment (segments never overlap)
-      WSeg& sg = it->second;
+      WSeg& sg = f->second->second;
       collect(sg, deps, retired);
       sg.writer = id;
       sg.readers.clear();
@@ -691,8 +705,11 @@ class HazardMap {
       collect(j->second, deps, retired);
     split(rg.lo);
     split(rg.hi);
-    w_.erase(w_.lower_bound(rg.lo), w_.lower_bound(rg.hi));
-    w_.emplace(rg.lo, WSeg{rg.hi, id, {}});
+    for (auto j = w_.lower_bound(rg.lo); j != w_.end() && j->first < rg.hi;) {
+      wi_.erase(j->first);
+      j = w_.erase(j);
+    }
+    wi_[rg.lo] = w_.emplace(rg.lo, WSeg{rg.hi, id, {}}).first;
   }
 
   template <class Retired>
@@ -709,11 +726,12 @@ class HazardMap {
     if (it->first < x && x < it->second.hi) {
       WSeg tail = it->second;
       it->second.hi = x;
-      w_.emplace(x, std::move(tail));
+      wi_[x] = w_.emplace(x, std::move(tail)).first;
     }
   }
 
   std::map<uint64_t, WSeg> w_;
+  std::unordered_map<uint64_t, std::map<uint64_t, WSeg>::iterator> wi_;  // first byte -> segment
   std::map<uint64_t, RSpan> r_;
 };
 
