@@ -322,23 +322,44 @@ def handoff_gaps(ctx, recs):
     """Idle gaps between dependent ops inside the resident kernel, from its
     trace (100 MHz timestamps): for every descriptor whose dependencies are all
     in `recs`, the time from the last dependency's completion to the claim of
-    the descriptor's first tile; and each descriptor's own claim-to-done time."""
+    the descriptor's first tile, and whether that tile's wave was already
+    polling when the dependency completed; and each descriptor's own
+    claim-to-done time, split at the completing wave's last store issue and
+    its acknowledgement (work, store acknowledgement, completion count)."""
     from persistent_fusion_amd import gpuos
 
     by_seq = {r["seq"]: r for r in recs if r["ring"] == 0}
-    gaps, busy = [], []
+    gaps, busy, waiting = [], [], 0
     for seq, r in by_seq.items():
         busy.append((r["t_done"] - r["t_claim"]) * 1e-2)
         deps = [x for x in gpuos.decode_desc(ctx.read_desc(0, seq))["deps"] if x]
         if not deps or any(x not in by_seq for x in deps):
             continue
-        gaps.append((r["t_claim"] - max(by_seq[x]["t_done"] for x in deps)) * 1e-2)
+        last_done = max(by_seq[x]["t_done"] for x in deps)
+        gaps.append((r["t_claim"] - last_done) * 1e-2)
+        waiting += 0 < r["t_wait"] <= last_done
     gaps.sort()
     busy.sort()
     pick = lambda v, q: round(v[min(len(v) - 1, int(q * len(v)))], 2) if v else None
     return {"descriptors": len(by_seq), "with_deps": len(gaps),
             "handoff_us_p50": pick(gaps, 0.5), "handoff_us_p90": pick(gaps, 0.9),
+            "first_tile_polling_at_dep_done_frac": round(waiting / len(gaps), 3) if gaps else None,
             "busy_us_p50": pick(busy, 0.5), "busy_us_p90": pick(busy, 0.9)}
+
+
+def critical_path_split(recs, names):
+    """Median split of each descriptor kind's claim-to-done time (µs): work up
+    to the completing wave's last store issue, that store's acknowledgement,
+    and the completion count (tile counter atomics)."""
+    by_op = {}
+    for x in recs:
+        if not (x["t_claim"] <= x["t_end"] <= x["t_ack"] <= x["t_done"]):
+            continue
+        by_op.setdefault(names.get(x["opcode"], str(x["opcode"])), []).append(
+            ((x["t_end"] - x["t_claim"]) * 1e-2, (x["t_ack"] - x["t_end"]) * 1e-2, (x["t_done"] - x["t_ack"]) * 1e-2))
+    med = lambda v: round(sorted(v)[len(v) // 2], 2)
+    return {k: {"work_us": med([w for w, _, _ in v]), "store_ack_us": med([a for _, a, _ in v]),
+                "count_us": med([c for _, _, c in v]), "n": len(v)} for k, v in sorted(by_op.items())}
 
 
 def decode_leg(device=0, reps=3):
@@ -375,6 +396,7 @@ def decode_leg(device=0, reps=3):
     for x in last_run:
         by_op.setdefault(names.get(x["opcode"], str(x["opcode"])), []).append((x["t_done"] - x["t_claim"]) * 1e-2)
     busy_by_op = {k: round(sorted(v)[len(v) // 2], 2) for k, v in sorted(by_op.items())}
+    split = critical_path_split(last_run, names)
     ctx.destroy()
     torch.cuda.synchronize()
     per_op = []
@@ -416,6 +438,7 @@ def decode_leg(device=0, reps=3):
             "per_op_launch_us_per_op": round(best_b / ops * 1e6, 2),
             "resident_trace_last_run": gaps,
             "resident_busy_us_by_descriptor": busy_by_op,
+            "resident_critical_path_us_by_descriptor": split,
             "bytes_per_token": byt // tokens,
             "roofline": {"bound": "hbm (weights and KV cache stream every token)",
                          "frac_of_hbm_peak": _frac(byt / best / 1e9)}}

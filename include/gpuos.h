@@ -43,7 +43,7 @@
 extern "C" {
 #endif
 
-#define GPUOS_ABI_VERSION 7
+#define GPUOS_ABI_VERSION 8
 
 /* Status codes. */
 typedef enum gpuos_status {
@@ -290,15 +290,22 @@ typedef struct gpuos_stats {
                                   kernel and the compiled variant */
 } gpuos_stats;
 
-/* Per-descriptor device timing, recorded when config.trace == 1. */
+/* Per-descriptor device timing, recorded when config.trace == 1.  Times are
+ * s_memrealtime ticks (100 MHz).  They split a descriptor's critical path:
+ * t_wait..t_claim is the first tile's dependency poll, t_claim..t_end its
+ * work up to the completing wave's last store, t_end..t_ack that wave's
+ * store acknowledgement, t_ack..t_done the completion count. */
 typedef struct gpuos_trace_rec {
   uint64_t seq;       /* device descriptor sequence (1-based, per ring) */
-  uint64_t t_claim;   /* s_memrealtime at the first tile's start */
-  uint64_t t_done;    /* s_memrealtime when the last tile finished */
+  uint64_t t_claim;   /* the first tile's dependencies are met */
+  uint64_t t_done;    /* the last tile is counted (done_id follows) */
   uint32_t opcode;    /* opcode executed (FUSED_EW = 32) */
   uint32_t ntiles;
   uint32_t ring;      /* 0 = best-effort ring, 1 = latency-critical ring */
   uint32_t first_ops; /* user ops folded into this descriptor */
+  uint64_t t_wait;    /* the first tile's wave starts its dependency poll */
+  uint64_t t_end;     /* the completing wave's tile has issued its stores */
+  uint64_t t_ack;     /* those stores are acknowledged */
 } gpuos_trace_rec;
 
 typedef struct gpuos_ctx gpuos_ctx;

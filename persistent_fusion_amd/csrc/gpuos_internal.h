@@ -289,10 +289,13 @@ static_assert(offsetof(HostCtl, lc_tail) % 64 == 0 && offsetof(HostCtl, lc_tail)
 // Per-descriptor trace record (device memory), one per ring slot.
 struct TraceRec {
   uint64_t seq;
-  uint64_t t_claim;
-  uint64_t t_done;
+  uint64_t t_claim;  // first tile: dependencies met
+  uint64_t t_done;   // completing wave: counted last, done_id about to be stored
   uint32_t opcode;
   uint32_t ntiles;
+  uint64_t t_wait;   // first tile: its wave starts waiting on the dependencies
+  uint64_t t_end;    // completing wave: its tile's stores issued
+  uint64_t t_ack;    // completing wave: those stores acknowledged
 };
 
 // Device error codes (HostCtl::error).

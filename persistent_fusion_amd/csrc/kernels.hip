@@ -230,7 +230,10 @@ __device__ __forceinline__ void finish_tile(const KArgs& a, const Cached& c, uin
       __hip_atomic_fetch_add(&cnt[ticket], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   }
   if constexpr (kReleaseWriteback) fence_rel_agent();
+  const bool traced = a.trace[RING] != nullptr;
+  const uint64_t t_end = traced ? now_ticks() : 0;
   wait_mem();
+  const uint64_t t_ack = traced ? now_ticks() : 0;
   if (lane_id() != 0) return;
   bool complete;
   const uint32_t S = ntiles <= kTilesPerSub ? 1u
@@ -263,10 +266,12 @@ __device__ __forceinline__ void finish_tile(const KArgs& a, const Cached& c, uin
 #pragma unroll
     for (uint32_t k = 0; k < kDoneReplicas; ++k) st_rlx_agent(&a.done_id[RING][(uint64_t)k * cap + slot], c.seq);
     if constexpr (RING == 1) st_rlx_sys(&a.dctl->hdone_lc[slot], c.seq);
-    if (a.trace[RING]) {
+    if (traced) {
       TraceRec* tr = &a.trace[RING][slot];
       st_rlx_agent(&tr->seq, c.seq);
       st_rlx_agent(&tr->t_done, t_done);
+      st_rlx_agent(&tr->t_end, t_end);
+      st_rlx_agent(&tr->t_ack, t_ack);
       st_rlx_agent(&tr->opcode, d(0) & 0xffu);
       st_rlx_agent(&tr->ntiles, ntiles);
     }
@@ -290,10 +295,11 @@ __device__ __forceinline__ void run_ticket(const KArgs& a, uint64_t ticket, Cach
   const uint32_t tile = (uint32_t)(ticket - c.start);
   const SDesc d = c.desc();
   if (a.debug >> 16) jitter_wait(ticket, a.debug >> 16);
-  auto claimed = [&]() {
+  auto stamp = [&](uint64_t TraceRec::*field) {
     if (a.trace[RING] && tile == 0 && lane_id() == 0)
-      st_rlx_agent(&a.trace[RING][slot_of(c.seq, a.cap_mask)].t_claim, now_ticks());
+      st_rlx_agent(&(a.trace[RING][slot_of(c.seq, a.cap_mask)].*field), now_ticks());
   };
+  auto claimed = [&]() { stamp(&TraceRec::t_claim); };
   if (!c.deps_ok) {
 #ifndef GPUOS_RTC_VARIANT
     const uint32_t w0 = d(0);
@@ -302,6 +308,7 @@ __device__ __forceinline__ void run_ticket(const KArgs& a, uint64_t ticket, Cach
         ((w0 >> 16) & DF_AUX_READY)) {
       // the weights are final: start streaming them, then wait for x
       auto ready = [&]() {
+        stamp(&TraceRec::t_wait);
         wait_deps<RING>(a, c);
         c.deps_ok = 1;
         claimed();
@@ -323,6 +330,7 @@ __device__ __forceinline__ void run_ticket(const KArgs& a, uint64_t ticket, Cach
       return;
     }
 #endif
+    stamp(&TraceRec::t_wait);
     wait_deps<RING>(a, c);
     c.deps_ok = 1;
   }

@@ -812,6 +812,9 @@ struct gpuos_ctx {
   uint64_t pub_seq[kRings] = {0, 0};
   uint64_t pub_tiles[kRings] = {0, 0};
   uint64_t tail_written[kRings] = {0, 0};
+  // per ring slot of descriptor s: a k such that descriptors 1..k of the
+  // ring have all completed whenever s starts (publish_one)
+  std::vector<uint64_t> done_prefix[kRings];
   HazardMap hazards;
   std::vector<ProgCode> programs;  // gpuos_program_define / _update
   uint64_t since_prune = 0;
@@ -1886,6 +1889,19 @@ int publish_one(gpuos_ctx* c, Planned& pl) {
     dseq.push_back(s);
   }
   dseq.sort_unique();
+  // Dependencies implied by another are dropped, so waves poll fewer
+  // completion words.  A descriptor's prefix k says that descriptors 1..k of
+  // its ring have all completed whenever it starts: those the host saw
+  // retired before publishing it, its dependencies and, through them, theirs.
+  // A dependency at or below another dependency's prefix completed before
+  // that one started, so waiting for the latter covers it: its stores were
+  // acknowledged before its completion was counted.
+  std::vector<uint64_t>& prefix = c->done_prefix[ring];
+  uint64_t pre = completed_of(c, ring);
+  for (uint64_t s : dseq) pre = std::max(pre, prefix[(s - 1) & (c->cap - 1)]);
+  dseq.remove_if([pre](uint64_t s) { return s <= pre; });
+  for (uint64_t s : dseq)
+    if (s == pre + 1) pre = s;  // ascending: consecutive dependencies extend it
   if (dseq.size() <= (size_t)kMaxDeps) {
     // seq - dep fits 32 bits: a live dependency is less than a ring behind
     for (size_t k = 0; k < dseq.size(); ++k) {
@@ -1897,7 +1913,9 @@ int publish_one(gpuos_ctx* c, Planned& pl) {
     }
   } else {
     d.wait_retired = dseq.back();  // retire order covers every dependency
+    pre = dseq.back();
   }
+  prefix[(seq - 1) & (c->cap - 1)] = pre;
   DevDesc* slot = &c->hdesc[ring][(seq - 1) & (c->cap - 1)];
   memcpy(slot, &d, sizeof d);
   c->hends[ring][(seq - 1) & (c->cap - 1)] = c->pub_tiles[ring] + d.ntiles;
@@ -2417,6 +2435,7 @@ int create_impl(int device, const gpuos_config* cfg_in, StaticMem* sm, gpuos_ctx
   auto* c = new gpuos_ctx();
   c->cfg = cfg;
   c->cap = cfg.ring_slots;
+  for (int r = 0; r < kRings; ++r) c->done_prefix[r].assign(c->cap, 0);
   c->device = device;
   c->host_only = device == GPUOS_DEVICE_NONE;
   if (!c->host_only) {
@@ -2758,6 +2777,9 @@ int gpuos_trace_read(gpuos_ctx* c, gpuos_trace_rec* out, uint32_t max, uint32_t*
       o.seq = sq;
       o.t_claim = t.t_claim;
       o.t_done = t.t_done;
+      o.t_wait = t.t_wait;
+      o.t_end = t.t_end;
+      o.t_ack = t.t_ack;
       o.opcode = t.opcode;
       o.ntiles = t.ntiles;
       o.ring = (uint32_t)r;

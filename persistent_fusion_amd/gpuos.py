@@ -14,7 +14,7 @@ from typing import Callable, Dict, Iterable, List, Optional, Sequence
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libgpuos.so")
-ABI_VERSION = 7  # GPUOS_ABI_VERSION of the header this binding follows
+ABI_VERSION = 8  # GPUOS_ABI_VERSION of the header this binding follows
 
 # status codes
 OK, EINVAL, ENOMEM, EAGAIN, ETIMEDOUT, EDEVICE, ESTATE, ECOMPILE = 0, -1, -2, -3, -4, -5, -6, -7
@@ -67,7 +67,8 @@ class GpuosStats(C.Structure):
 class GpuosTraceRec(C.Structure):
     _fields_ = [("seq", C.c_uint64), ("t_claim", C.c_uint64), ("t_done", C.c_uint64),
                 ("opcode", C.c_uint32), ("ntiles", C.c_uint32), ("ring", C.c_uint32),
-                ("first_ops", C.c_uint32)]
+                ("first_ops", C.c_uint32), ("t_wait", C.c_uint64), ("t_end", C.c_uint64),
+                ("t_ack", C.c_uint64)]
 
 
 class GpuosView(C.Structure):
@@ -92,7 +93,7 @@ assert C.sizeof(GpuosView) == 136
 assert C.sizeof(GpuosOp) == 128
 assert C.sizeof(GpuosConfig) == 64
 assert C.sizeof(GpuosStats) == 144
-assert C.sizeof(GpuosTraceRec) == 40
+assert C.sizeof(GpuosTraceRec) == 64
 
 # Every symbol declared in include/gpuos.h and include/gpuos_debug.h.
 EXPORTS = (

@@ -14,6 +14,11 @@
   to the run without jitter, and match the oracle.
 * The grid checks in: gpuos_create returns only once every wave of the
   resident grid has started; the relaunch after a yield checks in again.
+* Dependencies in time: with config.trace the kernel stamps each descriptor
+  (one global 100 MHz clock); on a 2-layer decode, whose descriptors chain
+  through their dependencies, every descriptor's first tile starts after the
+  completion stamp of each dependency, and each record's stamps are in order
+  (poll start, claim, completion; last store issued, acknowledged, counted).
 """
 
 import numpy as np
@@ -142,3 +147,31 @@ def test_relaunch_after_yield_checks_in_again():
     want = oracle.run(wl)
     for name in wl.outputs:
         assert oracle.compare(got[name], want[name], "f32").ok, name
+
+
+def test_trace_orders_every_dependency_in_time():
+    _need_gpu()
+    say("trace: dependencies in time, 2-layer decode")
+    wl = workloads.gen_decode(seed=5, layers=2, tokens=3, distinct=True)
+    tensors = runner.to_device(wl, 0)
+    addr = runner.addr_fn(tensors, wl)
+    ctx = gpuos.Context(0, trace=1)
+    try:
+        runner.submit_workload(ctx, wl, addr)
+        ctx.sync(0, 60.0)
+        recs = {r["seq"]: r for r in ctx.trace(1 << 16) if r["ring"] == 0}
+        n = ctx.published(0)
+        assert sorted(recs) == list(range(1, n + 1)), "a completed descriptor has no trace record"
+        checked = 0
+        for seq, r in recs.items():
+            assert 0 < r["t_wait"] <= r["t_claim"] <= r["t_done"], (seq, r)
+            assert 0 < r["t_end"] <= r["t_ack"] <= r["t_done"], (seq, r)
+            for dep in (x for x in gpuos.decode_desc(ctx.read_desc(0, seq))["deps"] if x):
+                assert r["t_claim"] > recs[dep]["t_done"], (seq, dep)
+                checked += 1
+        say(f"  {n} descriptors, {checked} dependencies")
+        assert checked >= n // 2
+    finally:
+        ctx.destroy()
+    bad = oracle.local_check(wl, runner.download(tensors, wl, wl.outputs), oracle.compare)
+    assert not bad, f"{len(bad)} ops differ, first: {bad[:3]}"

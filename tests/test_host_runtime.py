@@ -44,7 +44,7 @@ def test_library_exports_every_declared_symbol():
     missing = [s for s in sorted(declared) if not hasattr(lib, s)]
     assert not missing, missing
     assert set(gpuos.EXPORTS) == declared
-    assert lib.gpuos_abi_version() == 7 == gpuos.ABI_VERSION
+    assert lib.gpuos_abi_version() == 8 == gpuos.ABI_VERSION
 
 
 def test_fused_chain_becomes_one_descriptor():
@@ -332,11 +332,50 @@ def test_elementwise_queue_encoding_matches_workload():
         c.submit(arr)
         c.flush()
         assert c.published(0) == 50
+        got = []
         for i, op in enumerate(wl.ops):
             d = desc(c, i + 1)
             assert d["ptr"][0] == base[op.out.buf]
-            got = sorted(x for x in d["deps"] if x)
-            assert got == sorted({j + 1 for j in op.deps})
+            got.append({x - 1 for x in d["deps"] if x})
+    # a published dependency implied by another is dropped: each op keeps a
+    # subset of its dependencies with the same transitive closure
+    want = [set(op.deps) for op in wl.ops]
+    assert all(g <= w for g, w in zip(got, want))
+    assert _closure(got) == _closure(want)
+
+
+def _closure(preds):
+    reach = []
+    for p in preds:
+        r = set(p)
+        for j in p:
+            r |= reach[j]
+        reach.append(r)
+    return reach
+
+
+def test_implied_dependencies_are_dropped():
+    # a chain 1 <- 2 <- 3 where 3 also reads 1's output: 3 waits for 2 only;
+    # 4 reads 1's and 3's outputs: 3 covers 1
+    A, B, C_, D = (buf(i) for i in range(4))
+    ops = (gpuos.GpuosOp * 4)(
+        make_op("relu", B, [A], n=1024),            # 1
+        make_op("exp", C_, [B], n=1024),            # 2: RAW on 1
+        make_op("add", D, [C_, B], n=1024),         # 3: RAW on 2 and 1
+        make_op("add", A + 8192, [B, D], n=1024),   # 4: RAW on 1 and 3
+    )
+    with ctx(fusion=2) as c:
+        c.submit(ops)
+        c.flush()
+        deps = [sorted(x for x in desc(c, s)["deps"] if x) for s in (1, 2, 3, 4)]
+    assert deps == [[], [1], [2], [3]]
+    ops[1].deps[0] = -1                       # explicit: 2 after 1
+    ops[2].deps[0], ops[2].deps[1] = -1, -2   # 3 after 2 and after 1
+    with ctx(fusion=2, auto_deps=2) as c:     # explicit dependencies are pruned too
+        c.submit(ops)
+        c.flush()
+        deps = [sorted(x for x in desc(c, s)["deps"] if x) for s in (1, 2, 3, 4)]
+    assert deps == [[], [1], [2], []]
 
 
 # ----------------------------------------------------------------------------
