@@ -1016,6 +1016,22 @@ def main():
             cfgs["C5_priority_mix_200_rounds"] = priority_leg()
         else:
             raise SystemExit(f"unknown config {name}")
+    c3 = cfgs.get("C3_decode_24_layers_64_tokens")
+    if c3 and c3.get("resident_device_span_ms"):
+        # the pages' launch-cost model with this GPU's figures: every op of a
+        # token launched on its own, each costing the measured host time of a
+        # back-to-back launch, on top of the resident kernel's device time
+        from persistent_fusion_amd import traffic
+
+        per_tok = c3["ops"] // c3["tokens"]
+        comp = c3["resident_device_span_ms"] * 1e-3 / c3["tokens"]
+        m = traffic.launch_model(per_tok, lr["us_per_launch_back_to_back"] * 1e-6, comp)
+        c3["launch_model"] = {
+            "launches_per_token": per_tok, "us_per_launch": lr["us_per_launch_back_to_back"],
+            "compute_us_per_token": round(comp * 1e6, 1),
+            "modelled_per_op_launch_us_per_token": round(m["total_s"] * 1e6, 1),
+            "measured_per_op_launch_us_per_token": round(1e6 / c3["per_op_launch_tok_per_s"], 1),
+            "launch_share": round(m["share"], 3)}
     extra_names = ("torch", "program", "views") if args.extra == "all" else \
         tuple(x for x in args.extra.split(",") if x)
     extra = {}

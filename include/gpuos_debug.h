@@ -45,6 +45,30 @@ int gpuos_debug_seq_of(gpuos_ctx* ctx, uint64_t id, int* ring_out, uint64_t* seq
 int gpuos_debug_retire(gpuos_ctx* ctx, int ring, uint64_t upto);
 
 /*
+ * Host consumer: a thread that plays the resident kernel on a host-only
+ * context, for tests of the host runtime under concurrency (back-pressure on
+ * a full ring, ring wraparound, the order dependencies impose).  After
+ * gpuos_debug_consumer_attach, a full ring or a pending cross-ring dependency
+ * blocks the producer until the consumer retires enough (30 s at most, then
+ * ETIMEDOUT) instead of failing with EAGAIN, and gpuos_sync waits for the
+ * consumer.  The three consumer calls may run on another thread, concurrently
+ * with the producer's calls, and touch only what the device would:
+ *  - gpuos_debug_consumer_tail: the ring's published tail (acquire load; 0
+ *    for a device context or a bad argument);
+ *  - gpuos_debug_consumer_read: copies the 256-byte descriptor of sequence
+ *    seq from its ring slot into out (caller owned), after checking the
+ *    slot's sequence and check words (EINVAL if the slot holds another
+ *    sequence); seq must be at or below the tail, and not yet retired;
+ *  - gpuos_debug_consumer_retire: advances the ring's in-order retire cursor
+ *    to upto (release store; EINVAL beyond the published tail).
+ * Errors: ESTATE on a device context.  One consumer thread per context.
+ */
+int gpuos_debug_consumer_attach(gpuos_ctx* ctx);
+uint64_t gpuos_debug_consumer_tail(gpuos_ctx* ctx, int ring);
+int gpuos_debug_consumer_read(gpuos_ctx* ctx, int ring, uint64_t seq, void* out);
+int gpuos_debug_consumer_retire(gpuos_ctx* ctx, int ring, uint64_t upto);
+
+/*
  * Copies the execution counts of tickets [0, n) of `ring` into out (n
  * uint32 entries, caller owned), for a context created with
  * config.tile_counts >= n.  Ticket i is the i-th tile published to the ring

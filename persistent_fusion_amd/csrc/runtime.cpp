@@ -819,6 +819,8 @@ struct gpuos_ctx {
   std::vector<ProgCode> programs;  // gpuos_program_define / _update
   uint64_t since_prune = 0;
   bool poisoned = false;
+  bool consumer = false;    // host-only: another thread plays the device
+                            // (gpuos_debug_consumer_attach), so waits block
   bool stopped = false;     // STOP published; no more submissions
   bool exited = false;      // resident kernel has exited
   bool parked = false;      // the kernel left at gpuos_yield; the next flush
@@ -1820,7 +1822,7 @@ int keep_running(gpuos_ctx* c, bool query_stream) {
 // Waits until ring slot for `seq` is free; returns 0, EAGAIN or EDEVICE.
 int wait_ring_space(gpuos_ctx* c, uint32_t ring, uint64_t seq) {
   if (seq <= (uint64_t)c->cap || seq - c->cap <= completed_of(c, ring)) return 0;
-  if (c->host_only || c->cfg.block_on_full == 2)
+  if ((c->host_only && !c->consumer) || c->cfg.block_on_full == 2)
     return fail(GPUOS_EAGAIN, "ring %u full (%u slots)", ring, c->cap);
   ++c->st.ring_full_waits;
   // make what is already written visible so the device can drain it
@@ -1830,8 +1832,11 @@ int wait_ring_space(gpuos_ctx* c, uint32_t ring, uint64_t seq) {
     c->tail_written[ring] = c->pub_seq[ring];
   }
   uint32_t spins = 0;
+  const auto t0 = std::chrono::steady_clock::now();
   while (seq - c->cap > completed_of(c, ring)) {
     if (check_device_error(c)) return GPUOS_EDEVICE;
+    if (c->host_only && std::chrono::steady_clock::now() - t0 > std::chrono::seconds(30))
+      return fail(GPUOS_ETIMEDOUT, "ring %u full: the consumer retired nothing for 30 s", ring);
     if (++spins > 256) {
       std::this_thread::yield();
       if ((spins & 1023) == 0) {
@@ -1877,7 +1882,7 @@ int publish_one(gpuos_ctx* c, Planned& pl) {
       uint32_t spins = 0;
       while (s > completed_of(c, dring)) {
         if (check_device_error(c)) return GPUOS_EDEVICE;
-        if (c->host_only) return fail(GPUOS_EAGAIN, "cross-ring dependency pending");
+        if (c->host_only && !c->consumer) return fail(GPUOS_EAGAIN, "cross-ring dependency pending");
         if ((++spins & 1023) == 0) {
           const int rc2 = keep_running(c, (spins & 0xffff) == 0);
           if (rc2) return rc2;
@@ -2195,7 +2200,8 @@ int sync_impl(gpuos_ctx* c, uint64_t upto, int64_t timeout_ns) {
   for (int r = 0; r < kRings; ++r) {
     while (completed_of(c, r) < target[r]) {
       if (check_device_error(c)) return GPUOS_EDEVICE;
-      if (c->host_only) return fail(GPUOS_ETIMEDOUT, "host-only context: ops never complete");
+      if (c->host_only && !c->consumer)
+        return fail(GPUOS_ETIMEDOUT, "host-only context: ops never complete");
       ++spins;
       if (spins < 2048) {
         cpu_relax();
@@ -3144,6 +3150,40 @@ int gpuos_debug_tile_counts(gpuos_ctx* c, int ring, uint32_t* out, uint32_t n) {
   if (e == hipSuccess) e = hipStreamSynchronize(s);
   if (s) (void)hipStreamDestroy(s);
   if (e != hipSuccess) return fail(GPUOS_EDEVICE, "tile count copy: %s", hipGetErrorString(e));
+  return 0;
+}
+
+int gpuos_debug_consumer_attach(gpuos_ctx* c) {
+  if (!c) return fail(GPUOS_EINVAL, "bad argument");
+  if (!c->host_only) return fail(GPUOS_ESTATE, "only host-only contexts take a host consumer");
+  c->consumer = true;
+  return 0;
+}
+
+// The consumer side touches only what the device would: the published tails,
+// the ring slots and the retire cursors, never the producer's own fields.
+uint64_t gpuos_debug_consumer_tail(gpuos_ctx* c, int ring) {
+  if (!c || !c->host_only || ring < 0 || ring >= kRings) return 0;
+  return load_acq(&c->hctl->tail[ring]);
+}
+
+int gpuos_debug_consumer_read(gpuos_ctx* c, int ring, uint64_t seq, void* out) {
+  if (!c || !out || ring < 0 || ring >= kRings || seq == 0) return fail(GPUOS_EINVAL, "bad argument");
+  if (!c->host_only) return fail(GPUOS_ESTATE, "only host-only contexts take a host consumer");
+  const DevDesc* d = &c->hdesc[ring][(seq - 1) & (c->cap - 1)];
+  if (d->seq != seq || d->check != ((uint32_t)seq ^ kDescMagic))
+    return fail(GPUOS_EINVAL, "slot of sequence %llu holds sequence %llu",
+                (unsigned long long)seq, (unsigned long long)d->seq);
+  memcpy(out, d, sizeof(DevDesc));
+  return 0;
+}
+
+int gpuos_debug_consumer_retire(gpuos_ctx* c, int ring, uint64_t upto) {
+  if (!c || ring < 0 || ring >= kRings) return fail(GPUOS_EINVAL, "bad argument");
+  if (!c->host_only) return fail(GPUOS_ESTATE, "only host-only contexts take a host consumer");
+  if (upto > load_acq(&c->hctl->tail[ring]))
+    return fail(GPUOS_EINVAL, "retire beyond the published tail");
+  if (upto > load_acq(&c->hctl->completed[ring])) store_rel(&c->hctl->completed[ring], upto);
   return 0;
 }
 

@@ -105,6 +105,8 @@ EXPORTS = (
     "gpuos_program_define", "gpuos_program_update", "gpuos_program_compile",
     "gpuos_debug_read_desc", "gpuos_debug_published", "gpuos_debug_seq_of", "gpuos_debug_retire",
     "gpuos_debug_tile_counts", "gpuos_create_static", "gpuos_debug_rtc_source",
+    "gpuos_debug_consumer_attach", "gpuos_debug_consumer_tail", "gpuos_debug_consumer_read",
+    "gpuos_debug_consumer_retire",
 )
 
 _lib = None
@@ -150,6 +152,10 @@ def lib() -> C.CDLL:
         "gpuos_debug_published": (C.c_uint64, [P, C.c_int]),
         "gpuos_debug_seq_of": (C.c_int, [P, C.c_uint64, C.POINTER(C.c_int), C.POINTER(C.c_uint64)]),
         "gpuos_debug_retire": (C.c_int, [P, C.c_int, C.c_uint64]),
+        "gpuos_debug_consumer_attach": (C.c_int, [P]),
+        "gpuos_debug_consumer_tail": (C.c_uint64, [P, C.c_int]),
+        "gpuos_debug_consumer_read": (C.c_int, [P, C.c_int, C.c_uint64, P]),
+        "gpuos_debug_consumer_retire": (C.c_int, [P, C.c_int, C.c_uint64]),
         "gpuos_debug_tile_counts": (C.c_int, [P, C.c_int, C.POINTER(C.c_uint32), C.c_uint32]),
         "gpuos_debug_rtc_source": (C.c_size_t, [P, C.c_char_p, C.c_size_t]),
     }

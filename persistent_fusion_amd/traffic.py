@@ -68,3 +68,18 @@ def fused_chain_bytes(ops: Sequence[Op], scalar_bufs: Set[str] = frozenset()) ->
     n = ops[0].n
     outs = {op.out.buf for op in ops if not op.transient}
     return eb * n * (len(inputs) + len(outs))
+
+
+def launch_model(launches: int, per_launch_s: float, compute_s: float) -> dict:
+    """Host launch cost against device work for one step ("Launch Overhead and
+    Fusion", section "Code": a decode step issues a fixed number of launches,
+    each costing a fixed host time, on top of its compute).  Launches are
+    issued one after another on one host thread, so their cost adds to the
+    compute instead of overlapping it; the share is the launches' part of the
+    total."""
+    if launches < 0 or per_launch_s < 0 or compute_s < 0:
+        raise ValueError("launch model: negative input")
+    overhead = launches * per_launch_s
+    total = overhead + compute_s
+    return {"overhead_s": overhead, "total_s": total,
+            "share": overhead / total if total > 0 else 0.0}

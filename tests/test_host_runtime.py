@@ -999,3 +999,36 @@ def test_random_overlaps_every_conflict_is_ordered(seed):
             conflict = overlap(wi, wj) or any(overlap(r, wj) for r in ri) or any(overlap(wi, r) for r in rj)
             if conflict:
                 assert j in reach[i], f"op {i} is not ordered after op {j}"
+
+
+def test_consumer_calls_on_a_host_only_context():
+    """The host-consumer entry points: the tail follows flushes, a slot is read
+    only under its own sequence, retiring is bounded by the tail, and with a
+    consumer attached a wait that nobody serves times out instead of failing
+    at once."""
+    lib = gpuos.lib()
+    raw = (gpuos.C.c_uint8 * 256)()
+    with ctx(ring_slots=64) as c:
+        h = c.handle
+        assert lib.gpuos_debug_consumer_tail(h, 0) == 0
+        c.submit((gpuos.GpuosOp * 2)(make_op("add", buf(2), [buf(0), buf(1)], n=256),
+                                     make_op("relu", buf(3), [buf(2)], n=256)))
+        assert lib.gpuos_debug_consumer_tail(h, 0) == 0  # staged, not yet published
+        c.flush()
+        tail = lib.gpuos_debug_consumer_tail(h, 0)
+        assert tail == c.published(0) >= 1
+        assert lib.gpuos_debug_consumer_read(h, 0, 1, raw) == 0
+        assert bytes(raw) == bytes(c.read_desc(0, 1))
+        assert lib.gpuos_debug_consumer_read(h, 0, tail + 1, raw) == gpuos.EINVAL
+        assert lib.gpuos_debug_consumer_read(h, 2, 1, raw) == gpuos.EINVAL
+        assert lib.gpuos_debug_consumer_retire(h, 0, tail + 1) == gpuos.EINVAL
+        # without a consumer, a sync on a host-only context fails at once
+        with pytest.raises(GpuosError) as e:
+            c.sync(0, 5.0)
+        assert e.value.status == gpuos.ETIMEDOUT
+        assert lib.gpuos_debug_consumer_attach(h) == 0
+        with pytest.raises(GpuosError) as e:
+            c.sync(0, 0.05)
+        assert e.value.status == gpuos.ETIMEDOUT
+        assert lib.gpuos_debug_consumer_retire(h, 0, tail) == 0
+        c.sync(0, 1.0)

@@ -105,6 +105,31 @@ def test_golden_traffic_model_page_bytes():
     assert traffic.fused_chain_bytes(wl.ops) == wl.meta["fused_bytes"] // wl.meta["n"] * 4096
 
 
+def test_golden_launch_model_page_figures():
+    """The launch-cost model reproduces the figures the page prints for its
+    decode step, at the page's rounding."""
+    vals = {}
+    with open(os.path.join(GOLDEN, "launch_model.txt")) as f:
+        for line in f:
+            t = line.split()
+            if t and not t[0].startswith("#"):
+                vals[t[0]] = [float(v) for v in t[1:]]
+    launches, per_us, compute_ms = vals["inputs"]
+    m = traffic.launch_model(int(launches), per_us * 1e-6, compute_ms * 1e-3)
+    ov_ms, tot_ms, pct = vals["printed"]
+    assert f"{m['overhead_s'] * 1e3:.1f}" == f"{ov_ms:.1f}"
+    assert f"{m['total_s'] * 1e3:.1f}" == f"{tot_ms:.1f}"
+    assert f"{100 * m['share']:.0f}" == f"{pct:.0f}"
+    # invariants: no launches cost nothing; doubling the work per launch (a
+    # larger batch under the same launches) lowers the share
+    assert traffic.launch_model(0, 1e-5, 1e-3)["share"] == 0.0
+    a = traffic.launch_model(400, 1e-5, 2e-3)["share"]
+    b = traffic.launch_model(400, 1e-5, 4e-3)["share"]
+    assert b < a
+    with pytest.raises(ValueError):
+        traffic.launch_model(-1, 1e-5, 1e-3)
+
+
 # ----------------------------------------------------------------------------
 # closed forms on constants
 
