@@ -114,6 +114,7 @@ def fused_chain_leg(steps, warmup, device=0, warm_s=0.5):
     y = reps[(warm_passes + steps - 1) % REPLICAS]["y"].cpu().numpy()
 
     # per-op launches (3 kernels per pass) and one stand-alone fused kernel
+    log("bench: fused chain baselines (per-op launches, stand-alone fused kernel, graph replay)")
     stream = torch.cuda.current_stream(device)
     res = {}
     for label, fuse in (("per_op_launch", False), ("standalone_fused_kernel", True)):
@@ -978,6 +979,9 @@ def main():
                     help="seconds of oracle work for the headline's CPU baseline (other configs: "
                          "proportionally less)")
     ap.add_argument("--no-cpu", action="store_true")
+    ap.add_argument("--no-launch-rate", action="store_true",
+                    help="leave out the launch-rate measurement (20,000 empty-kernel launches), e.g. "
+                         "under a profiler that serialises every dispatch")
     ap.add_argument("--configs", default="all",
                     help="comma-separated configs besides the headline: queue, decode, dag, priority (or all)")
     ap.add_argument("--extra", default="",
@@ -999,8 +1003,12 @@ def main():
     assert torch.cuda.is_available(), "bench.py needs a GPU"
     torch.cuda.synchronize()
     fc = fused_chain_leg(args.steps, args.warmup, warm_s=args.device_warmup_s)
+    log("bench: copy kernel reference")
     cp = copy_leg()
-    lr = launch_rate_leg()
+    lr = None
+    if not args.no_launch_rate:
+        log("bench: launch rate (empty kernel)")
+        lr = launch_rate_leg()
     names = ("queue", "decode", "dag", "priority") if args.configs == "all" else \
         tuple(x for x in args.configs.split(",") if x)
     cfgs = {}
@@ -1017,7 +1025,7 @@ def main():
         else:
             raise SystemExit(f"unknown config {name}")
     c3 = cfgs.get("C3_decode_24_layers_64_tokens")
-    if c3 and c3.get("resident_device_span_ms"):
+    if c3 and c3.get("resident_device_span_ms") and lr:
         # the pages' launch-cost model with this GPU's figures: every op of a
         # token launched on its own, each costing the measured host time of a
         # back-to-back launch, on top of the resident kernel's device time
