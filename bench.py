@@ -479,6 +479,30 @@ def dag_leg(device=0, reps=2):
             times.append(time.perf_counter() - t0)
     ctx.destroy()
     torch.cuda.synchronize()
+    # one more pass with the in-kernel trace on (not timed): hand-off gaps of
+    # the last 65,536 descriptors, and whether the wave holding each one's
+    # first tile was already waiting when its last dependency completed (a
+    # wave still busy with earlier tickets arrives late)
+    ctx = gpuos.Context(device, trace=1)
+    for arr, k in passes[0]:
+        ctx.submit_noids(arr, k)
+        ctx.flush()
+    ctx.sync(0, 300.0)
+    tr = ctx.trace(1 << 16)
+    gaps = handoff_gaps(ctx, tr)
+    late = []
+    by_seq = {r["seq"]: r for r in tr if r["ring"] == 0}
+    for seq, r in by_seq.items():
+        deps = [x for x in gpuos.decode_desc(ctx.read_desc(0, seq))["deps"] if x]
+        if deps and all(x in by_seq for x in deps):
+            last_done = max(by_seq[x]["t_done"] for x in deps)
+            if r["t_wait"] > last_done:
+                late.append((r["t_wait"] - last_done) * 1e-2)
+    late.sort()
+    gaps["late_first_wave_us_p50"] = round(late[len(late) // 2], 2) if late else None
+    gaps["late_first_wave_us_p90"] = round(late[int(0.9 * len(late))], 2) if late else None
+    ctx.destroy()
+    torch.cuda.synchronize()
     # per-op launches: stream order covers every dependency
     enc_b = [gpuos.encode_ops(wl.ops, g0, g1, addr, _NoIds()) for g0, g1 in wl.groups]
     sizes = [g1 - g0 for g0, g1 in wl.groups]
@@ -494,6 +518,7 @@ def dag_leg(device=0, reps=2):
             "per_op_launch_ops_per_s": round(n / best_b),
             "per_op_launch_gb_per_s": round(wl.meta["bytes"] / best_b / 1e9, 1),
             "speedup_vs_per_op_launch": round(best_b / best, 2),
+            "resident_trace": gaps,
             "roofline": {"bound": "hbm and dependency latency",
                          "frac_of_hbm_peak": _frac(wl.meta["bytes"] / best / 1e9)}}
 

@@ -43,7 +43,7 @@
 extern "C" {
 #endif
 
-#define GPUOS_ABI_VERSION 8
+#define GPUOS_ABI_VERSION 9
 
 /* Status codes. */
 typedef enum gpuos_status {
@@ -209,7 +209,12 @@ typedef struct gpuos_op {
 
 /*
  * Context configuration.  gpuos_config_default() fills the defaults; zero in
- * a field of a config passed to gpuos_create also selects the default.
+ * a field of a config passed to gpuos_create also selects the default.  The
+ * environment can replace a default when a context is created: GPUOS_<FIELD>
+ * (the field's name in capitals, e.g. GPUOS_FUSION=2 or GPUOS_RING_SLOTS=
+ * 0x1000) sets that field wherever the caller's config leaves it zero; a value
+ * that is not a 32-bit unsigned number fails gpuos_create with EINVAL, and
+ * the result is validated like the caller's own fields.
  */
 typedef struct gpuos_config {
   uint32_t ring_slots;    /* descriptors per ring, power of two in
@@ -257,7 +262,7 @@ typedef struct gpuos_config {
                              start and finish in another order; results of
                              exact-class ops must not change.  0 = off
                              (default), at most 1000 */
-  uint32_t reserved;
+  uint32_t reserved;      /* must be 0 */
 } gpuos_config;
 
 /* Counters returned by gpuos_get_stats. */

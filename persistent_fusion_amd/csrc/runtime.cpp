@@ -2139,25 +2139,52 @@ void* dev_ptr(void* host) {
   return d;
 }
 
+// Environment overrides of the defaults: GPUOS_<FIELD> (the field's name in
+// capitals, a decimal or 0x-prefixed value) replaces the default of that
+// field; a nonzero field in the caller's config still wins.  A malformed
+// value is an error, so that a typo is not silently ignored.
+int env_defaults(gpuos_config& out) {
+  struct F { const char* name; uint32_t* field; };
+  const F fields[] = {
+      {"GPUOS_RING_SLOTS", &out.ring_slots}, {"GPUOS_WAVES_PER_CU", &out.waves_per_cu},
+      {"GPUOS_TILE_ELEMS", &out.tile_elems}, {"GPUOS_BE_TILE_ELEMS", &out.be_tile_elems},
+      {"GPUOS_FUSION", &out.fusion}, {"GPUOS_AUTO_DEPS", &out.auto_deps}, {"GPUOS_TRACE", &out.trace},
+      {"GPUOS_BLOCK_ON_FULL", &out.block_on_full}, {"GPUOS_MAX_FUSE", &out.max_fuse},
+      {"GPUOS_PRIORITY", &out.priority}, {"GPUOS_IDLE_EXIT_MS", &out.idle_exit_ms},
+      {"GPUOS_STREAM_MIN_KIB", &out.stream_min_kib}, {"GPUOS_LC_WAVES", &out.lc_waves},
+      {"GPUOS_TILE_COUNTS", &out.tile_counts}, {"GPUOS_JITTER", &out.jitter}};
+  for (const F& f : fields) {
+    const char* v = getenv(f.name);
+    if (!v || !*v) continue;
+    char* end = nullptr;
+    const unsigned long long x = strtoull(v, &end, 0);
+    if (*end || x > 0xFFFFFFFFull) return fail(GPUOS_EINVAL, "%s=%s is not a 32-bit unsigned number", f.name, v);
+    *f.field = (uint32_t)x;
+  }
+  return 0;
+}
+
 int apply_config(const gpuos_config* in, gpuos_config& out) {
   gpuos_config_default(&out);
-  if (!in) return 0;
-  if (in->ring_slots) out.ring_slots = in->ring_slots;
-  if (in->waves_per_cu) out.waves_per_cu = in->waves_per_cu;
-  if (in->tile_elems) out.tile_elems = in->tile_elems;
-  if (in->be_tile_elems) out.be_tile_elems = in->be_tile_elems;
-  if (in->fusion) out.fusion = in->fusion;
-  if (in->auto_deps) out.auto_deps = in->auto_deps;
-  if (in->trace) out.trace = in->trace;
-  if (in->block_on_full) out.block_on_full = in->block_on_full;
-  if (in->max_fuse) out.max_fuse = in->max_fuse;
-  if (in->priority) out.priority = in->priority;
-  if (in->idle_exit_ms) out.idle_exit_ms = in->idle_exit_ms;
-  if (in->stream_min_kib) out.stream_min_kib = in->stream_min_kib;
-  if (in->lc_waves) out.lc_waves = in->lc_waves;
-  out.tile_counts = in->tile_counts;
-  out.jitter = in->jitter;
-  if (in->reserved) return fail(GPUOS_EINVAL, "reserved config field must be 0");
+  if (int rc = env_defaults(out)) return rc;
+  if (in) {
+    if (in->ring_slots) out.ring_slots = in->ring_slots;
+    if (in->waves_per_cu) out.waves_per_cu = in->waves_per_cu;
+    if (in->tile_elems) out.tile_elems = in->tile_elems;
+    if (in->be_tile_elems) out.be_tile_elems = in->be_tile_elems;
+    if (in->fusion) out.fusion = in->fusion;
+    if (in->auto_deps) out.auto_deps = in->auto_deps;
+    if (in->trace) out.trace = in->trace;
+    if (in->block_on_full) out.block_on_full = in->block_on_full;
+    if (in->max_fuse) out.max_fuse = in->max_fuse;
+    if (in->priority) out.priority = in->priority;
+    if (in->idle_exit_ms) out.idle_exit_ms = in->idle_exit_ms;
+    if (in->stream_min_kib) out.stream_min_kib = in->stream_min_kib;
+    if (in->lc_waves) out.lc_waves = in->lc_waves;
+    if (in->tile_counts) out.tile_counts = in->tile_counts;
+    if (in->jitter) out.jitter = in->jitter;
+    if (in->reserved) return fail(GPUOS_EINVAL, "reserved config field must be 0");
+  }
   if (out.jitter > 1000) return fail(GPUOS_EINVAL, "jitter must be at most 1000");
   const uint32_t rs = out.ring_slots;
   if (rs < 64 || rs > (1u << 18) || (rs & (rs - 1)))

@@ -14,7 +14,7 @@ from typing import Callable, Dict, Iterable, List, Optional, Sequence
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libgpuos.so")
-ABI_VERSION = 8  # GPUOS_ABI_VERSION of the header this binding follows
+ABI_VERSION = 9  # GPUOS_ABI_VERSION of the header this binding follows
 
 # status codes
 OK, EINVAL, ENOMEM, EAGAIN, ETIMEDOUT, EDEVICE, ESTATE, ECOMPILE = 0, -1, -2, -3, -4, -5, -6, -7
@@ -181,8 +181,9 @@ def _check(rc: int, where: str) -> int:
 
 
 def config(**kw) -> GpuosConfig:
+    """A config with the given fields set and every other field zero, which
+    selects the library's default (or a GPUOS_<FIELD> environment override)."""
     cfg = GpuosConfig()
-    lib().gpuos_config_default(C.byref(cfg))
     for k, v in kw.items():
         if not hasattr(cfg, k):
             raise TypeError(f"unknown config field {k}")

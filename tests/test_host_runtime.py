@@ -44,7 +44,7 @@ def test_library_exports_every_declared_symbol():
     missing = [s for s in sorted(declared) if not hasattr(lib, s)]
     assert not missing, missing
     assert set(gpuos.EXPORTS) == declared
-    assert lib.gpuos_abi_version() == 8 == gpuos.ABI_VERSION
+    assert lib.gpuos_abi_version() == 9 == gpuos.ABI_VERSION
 
 
 def test_fused_chain_becomes_one_descriptor():
@@ -1032,3 +1032,50 @@ def test_consumer_calls_on_a_host_only_context():
         assert e.value.status == gpuos.ETIMEDOUT
         assert lib.gpuos_debug_consumer_retire(h, 0, tail) == 0
         c.sync(0, 1.0)
+
+
+def test_environment_overrides_config_defaults(monkeypatch):
+    """GPUOS_<FIELD> replaces a default; the caller's nonzero field wins; a
+    malformed or out-of-range value fails the create."""
+    op = make_op("relu", buf(1), [buf(0)], n=256)
+
+    def fill(c):
+        k = 0
+        while True:
+            try:
+                c.submit((gpuos.GpuosOp * 1)(op))
+                c.flush()
+            except GpuosError as e:
+                assert e.status == gpuos.EAGAIN
+                return k
+            k += 1
+
+    monkeypatch.setenv("GPUOS_RING_SLOTS", "0x40")
+    with Context(DEVICE_NONE) as c:
+        assert fill(c) == 64  # the ring holds 64 descriptors, none retire
+    with Context(DEVICE_NONE, ring_slots=128) as c:
+        assert fill(c) == 128
+    monkeypatch.setenv("GPUOS_RING_SLOTS", "48")  # not a power of two
+    with pytest.raises(GpuosError, match="ring_slots"):
+        Context(DEVICE_NONE)
+    monkeypatch.setenv("GPUOS_RING_SLOTS", "64k")
+    with pytest.raises(GpuosError, match="GPUOS_RING_SLOTS"):
+        Context(DEVICE_NONE)
+    monkeypatch.delenv("GPUOS_RING_SLOTS")
+    monkeypatch.setenv("GPUOS_FUSION", "3")  # switch fields take 1 or 2
+    with pytest.raises(GpuosError, match="switch fields"):
+        Context(DEVICE_NONE)
+    monkeypatch.setenv("GPUOS_FUSION", "2")
+    with Context(DEVICE_NONE) as c:  # fusion off: the chain stays three descriptors
+        c.submit((gpuos.GpuosOp * 3)(make_op("mul", buf(2), [buf(0), buf(1)], n=256),
+                                     make_op("add", buf(3), [buf(2), buf(1)], n=256),
+                                     make_op("relu", buf(4), [buf(3)], n=256)))
+        c.flush()
+        assert c.published(0) == 3
+    monkeypatch.delenv("GPUOS_FUSION")
+    with Context(DEVICE_NONE) as c:
+        c.submit((gpuos.GpuosOp * 3)(make_op("mul", buf(2), [buf(0), buf(1)], n=256),
+                                     make_op("add", buf(3), [buf(2), buf(1)], n=256),
+                                     make_op("relu", buf(4), [buf(3)], n=256)))
+        c.flush()
+        assert c.published(0) == 1
