@@ -1019,7 +1019,7 @@ def main():
         cpu_child_main(args.cpu_child, args.cpu_budget, args.cpu_core, args.cpu_y)
         return
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
-        print("bench.py: this build measures one GPU only (the resident kernel runs on one "
+        print("bench.py measures one GPU only (the resident kernel runs on one "
               "device; --gpus must be 1)", file=sys.stderr)
         sys.exit(2)
 

@@ -10,7 +10,7 @@ hazards across the two rings are waited for on the host.  The buffers' final
 contents must equal the oracle's program-order run of the same queue, element
 for element (int32 ADD / MUL / COPY are exact).
 
-The runtime and the driver are compiled from source with g++ under
+The runtime and the C++ test program are compiled from source with g++ under
 AddressSanitizer + UndefinedBehaviorSanitizer, and under ThreadSanitizer (the
 consumer shares the ring, the tails and the retire cursors with the producer).
 They are linked with the library's kernel objects, which a host-only context
