@@ -20,7 +20,6 @@
 #include <cstdio>
 #include <cstdlib>
 #include <cstring>
-#include <deque>
 #include <map>
 #include <memory>
 #include <unordered_map>
@@ -178,6 +177,37 @@ struct OpRanges {
 // An elementwise op's view after normalisation (gpuos_view): dimensions of
 // extent 1 dropped, adjacent dimensions merged wherever every operand's
 // strides allow, then padded to 4 with leading extents of 1.  on = 0: no view.
+// A FIFO of 64-bit words with O(1) indexing: one power-of-two array used as
+// a ring (the id -> sequence map is indexed on every dependency check, where
+// std::deque's two-level lookup showed).
+class WordFifo {
+ public:
+  size_t size() const { return n_; }
+  bool empty() const { return n_ == 0; }
+  uint64_t& operator[](size_t i) { return a_[(head_ + i) & (a_.size() - 1)]; }
+  uint64_t operator[](size_t i) const { return a_[(head_ + i) & (a_.size() - 1)]; }
+  uint64_t front() const { return a_[head_]; }
+  void pop_front() {
+    head_ = (head_ + 1) & (a_.size() - 1);
+    --n_;
+  }
+  void push_back(uint64_t v) {
+    if (n_ == a_.size()) grow();
+    a_[(head_ + n_) & (a_.size() - 1)] = v;
+    ++n_;
+  }
+
+ private:
+  void grow() {
+    std::vector<uint64_t> b(a_.empty() ? 1024 : 2 * a_.size());
+    for (size_t i = 0; i < n_; ++i) b[i] = (*this)[i];
+    a_.swap(b);
+    head_ = 0;
+  }
+  std::vector<uint64_t> a_;
+  size_t head_ = 0, n_ = 0;
+};
+
 struct ViewDesc {
   uint32_t on = 0;
   uint32_t shape[4] = {1, 1, 1, 1};
@@ -805,7 +835,7 @@ struct gpuos_ctx {
   // host bookkeeping
   uint64_t next_id = 1;
   uint64_t id_base = 1;            // ids below are retired and forgotten
-  std::deque<uint64_t> idseq;      // (ring << 63) | seq, 0 = staged
+  WordFifo idseq;                  // (ring << 63) | seq, 0 = staged
   std::vector<Staged> staged;
   std::vector<Planned> plan;       // fusion pass output, reused across flushes
   std::vector<uint8_t> tail_ok;    // plan[i..] all runnable by the compiled variant

@@ -90,6 +90,14 @@ void consumer(gpuos_ctx* ctx, uint32_t cap, uint64_t seed, Counters* cnt) {
   uint64_t retired[gpuos::kRings] = {0, 0};
   uint64_t seen[gpuos::kRings] = {0, 0};
   uint32_t idle = 0;
+  // let the producer fill the ring first, so that it has to wait for ring
+  // space at least once whatever the two threads' speeds (after 200 ms the
+  // consumer starts anyway: the producer may be waiting on the host for a
+  // cross-ring dependency, which only this thread can end)
+  const auto t0 = std::chrono::steady_clock::now();
+  while (!producer_done.load() && gpuos_debug_consumer_tail(ctx, 0) < cap &&
+         std::chrono::steady_clock::now() - t0 < std::chrono::milliseconds(200))
+    std::this_thread::sleep_for(std::chrono::microseconds(100));
   for (;;) {
     bool progress = false;
     for (int r = 0; r < gpuos::kRings; ++r) {
